@@ -1,0 +1,484 @@
+"""Plain CPU reference ("oracle") for the OSCAR INT2-history decode path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import this module.  The HIP library never does, and this module imports nothing
+from it: the two share no code.  Every function here is slow, vectorised numpy written to be
+checked against the pages by eye; floating point is fp64 except where a float decides an integer
+code (see ``quantize``), where the oracle takes the decision in the precision the kernels use
+(fp32), on values first computed in fp64.
+
+Sources (web pages on OSCAR; cited by the short keys below):
+  [W1] "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化" (66bd.net, article 13430)
+  [W3] the repost of the same write-up on m.kljzs.com (untitled page; it keeps the evaluation part)
+  [P]  "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization",
+       ModelScope paper page of arXiv 2605.17757 (Chinese summary "摘要" and "Abstract")
+
+What the path computes, in the pages' terms:
+  * the KV pool of a sequence has three segments: a BF16 attention sink of 64 tokens, a rotated
+    INT2 history, and a BF16 window of the 256 most recent tokens ([W1] §OSCAR 的设计);
+  * a history key or value x is stored as the codes of x' = x R with R = U · Hadamard ·
+    bit-reversal, one R per layer and head for keys and one for values ([W1] §OSCAR 的设计), after
+    clipping to a calibrated threshold and asymmetric INT2 quantisation with a scale and a zero
+    point, four 2-bit codes to a byte ([W1] §OSCAR 的设计; [P] 摘要);
+  * a new token goes into the recent window; the oldest recent token is then rotated, clipped,
+    quantised, packed and moved into the history ([W1] §OSCAR 的设计);
+  * decode attention treats the BF16 segments and the INT2 segment separately and combines the two
+    with an online-softmax merge; the result is ordinary softmax attention over the whole cache
+    ([W1] §OSCAR 的设计).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  R1  x' = x R for a row vector x (U first, then the Hadamard, then the permutation).
+  R2  Hadamard in Sylvester order, scaled by 1/sqrt(d); bit-reversal reverses the log2(d)-bit
+      channel index, P[i, j] = 1 iff i = rev(j).
+  R3  clip is symmetric, |x'| <= c, per (layer, KV head, K|V), applied after rotation.
+  R4  groups run along the rotated channels of one token: channels [m g, (m+1) g).
+  R5  zero point = group minimum, scale = (max - min) / 3; both stored as fp16 (round to nearest
+      even); codes use the stored fp16 values: code = clamp(rint((x'' - z) / s), 0, 3) with ties to
+      even; a group whose fp16 scale is 0 stores all-zero codes.
+  R6  the float steps that decide codes (rotated value to fp32, clip, min/max, range, /3, fp16
+      rounding, (x - z)/s) run in IEEE fp32, the kernels' precision; the rotation itself is fp64.
+  R7  pack order: code of element 4b+i sits in bits [2i, 2i+1] of byte b (LSB first).
+  R8  page layout (one block per page and KV head, 64 tokens): key codes packed along channels,
+      value codes packed along tokens, then key meta and value meta as fp16 (scale, zero) pairs.
+  R9  order within a decode step: append the new token, demote the token that leaves the recent
+      window, then attend; the recent window holds the last min(256, L-64) tokens.
+  R10 attention: scores scaled by 1/sqrt(d), no mask, query head i uses KV head i // G.
+  R11 calibration: U_k = eigenvectors of the summed Q^T Q of the KV head's query heads; U_v =
+      eigenvectors of (S V)^T (S V) with S = softmax(Q K^T / sqrt(d)) ([W1] §OSCAR 的设计 names the
+      two covariances); eigenvectors in descending eigenvalue order, each column's largest-magnitude
+      entry made positive; clip = a percentile of |x R|.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------------------------
+# geometry
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    """Cache geometry.  The pages fix sink = 64 and recent = 256 ([W1] §OSCAR 的设计); page = 64
+    tokens is this build's paged-KV block.  Smaller values serve brute-force tests."""
+
+    head_dim: int = 128
+    group: int = 128
+    page: int = 64
+    sink: int = 64
+    recent: int = 256
+
+    @property
+    def n_groups(self) -> int:
+        return self.head_dim // self.group
+
+    # byte offsets inside one (page, KV head) block (reading R8)
+    @property
+    def k_codes_off(self) -> int:
+        return 0
+
+    @property
+    def v_codes_off(self) -> int:
+        return self.page * self.head_dim // 4
+
+    @property
+    def k_meta_off(self) -> int:
+        return self.v_codes_off + self.head_dim * self.page // 4
+
+    @property
+    def v_meta_off(self) -> int:
+        return self.k_meta_off + self.page * self.n_groups * 4
+
+    @property
+    def block_bytes(self) -> int:
+        return self.v_meta_off + self.page * self.n_groups * 4
+
+
+# ----------------------------------------------------------------------------------------------
+# rotation R = U · Hadamard · bit-reversal   ([W1] §OSCAR 的设计; [W3] same design paragraph)
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order d (a power of two): H[i, j] = (-1)^popcount(i & j)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("order must be a power of two")
+    idx = np.arange(d)
+    both = np.bitwise_and.outer(idx, idx)
+    parity = np.zeros_like(both)
+    while both.any():
+        parity ^= both & 1
+        both = both >> 1
+    return np.where(parity == 0, 1.0, -1.0)
+
+
+def bit_reverse(j, d: int):
+    """Reverse the log2(d) low bits of channel index j (reading R2)."""
+    nbits = int(round(math.log2(d)))
+    j = np.asarray(j)
+    out = np.zeros_like(j)
+    for b in range(nbits):
+        out = out | (((j >> b) & 1) << (nbits - 1 - b))
+    return out
+
+
+def bit_reversal_matrix(d: int) -> np.ndarray:
+    """Permutation matrix P with P[i, j] = 1 iff i = rev(j), so (x P)_j = x_rev(j)."""
+    p = np.zeros((d, d))
+    j = np.arange(d)
+    p[bit_reverse(j, d), j] = 1.0
+    return p
+
+
+def rotation_matrix(u) -> np.ndarray:
+    """R = U (H / sqrt(d)) P in fp64, from the fp32 U the kernels receive (reading R1, R2)."""
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    return u @ (hadamard(d) / math.sqrt(d)) @ bit_reversal_matrix(d)
+
+
+# ----------------------------------------------------------------------------------------------
+# quantisation ([W1] §OSCAR 的设计: clip, asymmetric scale / zero point, 4 codes per byte)
+
+def rotate(x, u) -> np.ndarray:
+    """x' = x R in fp64 (reading R1).  x: (..., d)."""
+    return np.asarray(x, dtype=np.float64) @ rotation_matrix(u)
+
+
+def unrotate(xr, u) -> np.ndarray:
+    """x = x' R^T in fp64: R is orthogonal, so this undoes ``rotate``."""
+    return np.asarray(xr, dtype=np.float64) @ rotation_matrix(u).T
+
+
+def rotate_to_fp32(x, u) -> np.ndarray:
+    """x' = x R computed in fp64 and rounded once to fp32 (reading R6).  x: (..., d)."""
+    return rotate(x, u).astype(np.float32)
+
+
+def quantize(xr, clip, group: int):
+    """Clip and quantise rotated vectors xr (..., d) (fp32) group by group (readings R3-R6).
+
+    Returns (codes uint8 (..., d), scale fp16 (..., d/g), zero fp16 (..., d/g), pre) where
+    ``pre`` holds the values just before each rounding step, for acceptance windows:
+    pre["t"] fp32 (..., d) is (x'' - z) / s before rint, pre["s"] fp32 is (max-min)/3 before the
+    fp16 rounding and pre["z"] fp32 is the group minimum.
+    """
+    x = np.asarray(xr, dtype=np.float32)
+    c = np.float32(clip)
+    xc = np.minimum(np.maximum(x, -c), c)
+    d = x.shape[-1]
+    xg = xc.reshape(x.shape[:-1] + (d // group, group))
+    mn = xg.min(axis=-1)
+    mx = xg.max(axis=-1)
+    s32 = (mx - mn) / np.float32(3.0)
+    s16 = s32.astype(np.float16)
+    z16 = mn.astype(np.float16)
+    sf = s16.astype(np.float32)[..., None]
+    zf = z16.astype(np.float32)[..., None]
+    safe = np.where(sf == 0, np.float32(1.0), sf)
+    t = (xg - zf) / safe
+    codes = np.clip(np.rint(t), 0, 3)
+    codes = np.where(sf == 0, 0, codes).astype(np.uint8).reshape(x.shape)
+    pre = {"t": np.where(sf == 0, np.float32(0), t).reshape(x.shape), "s": s32, "z": mn}
+    return codes, s16, z16, pre
+
+
+def dequantize(codes, scale, zero, group: int) -> np.ndarray:
+    """Rotated-space values s * code + z in fp64, (..., d)."""
+    c = np.asarray(codes, dtype=np.float64)
+    d = c.shape[-1]
+    cg = c.reshape(c.shape[:-1] + (d // group, group))
+    s = np.asarray(scale, dtype=np.float64)[..., None]
+    z = np.asarray(zero, dtype=np.float64)[..., None]
+    return (s * cg + z).reshape(c.shape)
+
+
+def encode(x, u, clip, group: int):
+    """Rotate, clip and quantise vectors x (..., d): the demotion step on values."""
+    return quantize(rotate_to_fp32(x, u), clip, group)
+
+
+# ----------------------------------------------------------------------------------------------
+# packing (4 codes per byte; reading R7)
+
+def pack_codes(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    n = c.shape[-1]
+    c4 = c.reshape(c.shape[:-1] + (n // 4, 4))
+    return (c4[..., 0] | (c4[..., 1] << 2) | (c4[..., 2] << 4) | (c4[..., 3] << 6)).astype(np.uint8)
+
+
+def unpack_codes(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    parts = [(p >> (2 * i)) & 3 for i in range(4)]
+    return np.stack(parts, axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * 4,)).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------------------------
+# paged pool (reading R8)
+
+def new_pool(num_pages: int, num_kv_heads: int, geom: Geometry) -> np.ndarray:
+    return np.zeros((num_pages, num_kv_heads, geom.block_bytes), dtype=np.uint8)
+
+
+def _meta_bytes(scale16, zero16) -> np.ndarray:
+    """(n, G) fp16 scale and zero -> (n, G*4) bytes: per group the scale's two bytes, then the
+    zero's, little endian."""
+    s = np.asarray(scale16, dtype=np.float16).view(np.uint16)
+    z = np.asarray(zero16, dtype=np.float16).view(np.uint16)
+    pair = np.stack([s, z], axis=-1).astype("<u2")
+    return pair.reshape(pair.shape[0], -1).view(np.uint8).reshape(pair.shape[0], -1)
+
+
+def store_history(pool, table_row, hist_idx, head, kq, vq, geom: Geometry):
+    """Write encoded tokens into the pool.
+
+    hist_idx (n,) history indices; kq / vq = (codes (n,d), scale (n,G), zero (n,G)).  Token with
+    history index t lives in page table_row[t // page], slot t % page.
+    """
+    hist_idx = np.asarray(hist_idx)
+    kc, ks, kz = kq
+    vc, vs, vz = vq
+    d, pg = geom.head_dim, geom.page
+    kmeta = _meta_bytes(ks, kz)
+    vmeta = _meta_bytes(vs, vz)
+    kpacked = pack_codes(kc)
+    msz = geom.n_groups * 4
+    for n, t in enumerate(hist_idx):
+        blk = pool[table_row[t // pg], head]
+        slot = int(t % pg)
+        blk[geom.k_codes_off + slot * d // 4: geom.k_codes_off + (slot + 1) * d // 4] = kpacked[n]
+        # value codes: channel j's codes for the page's tokens are packed along tokens
+        byte = geom.v_codes_off + np.arange(d) * (pg // 4) + slot // 4
+        shift = 2 * (slot % 4)
+        blk[byte] = (blk[byte] & np.uint8(~(3 << shift) & 0xFF)) | (vc[n].astype(np.uint8) << shift)
+        blk[geom.k_meta_off + slot * msz: geom.k_meta_off + (slot + 1) * msz] = kmeta[n]
+        blk[geom.v_meta_off + slot * msz: geom.v_meta_off + (slot + 1) * msz] = vmeta[n]
+
+
+def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
+    """Read history tokens [0, n_hist) of one sequence and KV head back from the pool.
+
+    Returns ((k codes, k scale, k zero), (v codes, v scale, v zero)) with codes (n, d) and
+    scale / zero fp16 (n, G)."""
+    d, pg, ng = geom.head_dim, geom.page, geom.n_groups
+    kc = np.zeros((n_hist, d), np.uint8)
+    vc = np.zeros((n_hist, d), np.uint8)
+    ks = np.zeros((n_hist, ng), np.float16)
+    kz = np.zeros_like(ks)
+    vs = np.zeros_like(ks)
+    vz = np.zeros_like(ks)
+    msz = ng * 4
+    for t in range(n_hist):
+        blk = pool[table_row[t // pg], head]
+        slot = t % pg
+        kc[t] = unpack_codes(blk[geom.k_codes_off + slot * d // 4:
+                                 geom.k_codes_off + (slot + 1) * d // 4])
+        byte = geom.v_codes_off + np.arange(d) * (pg // 4) + slot // 4
+        vc[t] = (blk[byte] >> (2 * (slot % 4))) & 3
+        km = blk[geom.k_meta_off + slot * msz: geom.k_meta_off + (slot + 1) * msz]
+        vm = blk[geom.v_meta_off + slot * msz: geom.v_meta_off + (slot + 1) * msz]
+        km = km.view("<f2").reshape(ng, 2)
+        vm = vm.view("<f2").reshape(ng, 2)
+        ks[t], kz[t] = km[:, 0], km[:, 1]
+        vs[t], vz[t] = vm[:, 0], vm[:, 1]
+    return (kc, ks, kz), (vc, vs, vz)
+
+
+# ----------------------------------------------------------------------------------------------
+# the demotion step and the decode-step write ([W1] §OSCAR 的设计; reading R9)
+
+def demote(pool, page_table, u_k, u_v, clip_k, clip_v, k_src, v_src, hist_start,
+           geom: Geometry):
+    """Encode tokens k_src / v_src (B, n, Hkv, d) and store them at history indices
+    hist_start[b] + i.  Modifies ``pool`` in place."""
+    k_src = np.asarray(k_src, dtype=np.float64)
+    v_src = np.asarray(v_src, dtype=np.float64)
+    bsz, n, hkv, _ = k_src.shape
+    for b in range(bsz):
+        idx = int(hist_start[b]) + np.arange(n)
+        for h in range(hkv):
+            kq = encode(k_src[b, :, h], u_k[h], clip_k[h], geom.group)[:3]
+            vq = encode(v_src[b, :, h], u_v[h], clip_v[h], geom.group)[:3]
+            store_history(pool, page_table[b], idx, h, kq, vq, geom)
+
+
+def append(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_k, clip_v,
+           k_new, v_new, seq_slot, seq_lens, geom: Geometry):
+    """One decode-step write (reading R9).  seq_lens[b] is the length before the append, i.e. the
+    position P of the new token.  P < sink: the token goes to the sink.  Otherwise it goes to
+    recent-window ring slot P % recent, and when P >= sink + recent the token it replaces
+    (position P - recent) is first demoted to history index P - sink - recent.  Modifies the
+    arrays in place."""
+    for b in range(len(seq_lens)):
+        pos = int(seq_lens[b])
+        slot = int(seq_slot[b])
+        if pos < geom.sink:
+            sink_k[slot, :, pos] = k_new[b]
+            sink_v[slot, :, pos] = v_new[b]
+            continue
+        r = pos % geom.recent
+        if pos >= geom.sink + geom.recent:
+            old_k = np.asarray(recent_k[slot, :, r], dtype=np.float64)[None, None]
+            old_v = np.asarray(recent_v[slot, :, r], dtype=np.float64)[None, None]
+            demote(pool, page_table[b:b + 1], u_k, u_v, clip_k, clip_v, old_k, old_v,
+                   [pos - geom.sink - geom.recent], geom)
+        recent_k[slot, :, r] = k_new[b]
+        recent_v[slot, :, r] = v_new[b]
+
+
+# ----------------------------------------------------------------------------------------------
+# decode attention ([W1] §OSCAR 的设计; readings R9, R10)
+
+def segment_lengths(length: int, geom: Geometry):
+    """(sink tokens, history tokens, recent tokens) of a context of ``length`` tokens."""
+    n_sink = min(length, geom.sink)
+    n_recent = min(geom.recent, max(0, length - geom.sink))
+    n_hist = max(0, length - geom.sink - geom.recent)
+    return n_sink, n_hist, n_recent
+
+
+def recent_slots(length: int, geom: Geometry) -> np.ndarray:
+    """Ring slots of the recent window: positions max(sink, L - recent) .. L-1, modulo recent."""
+    start = max(geom.sink, length - geom.recent)
+    return np.arange(start, length) % geom.recent
+
+
+def gather_cache(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, slot, b, kv,
+                 length: int, geom: Geometry):
+    """All cached keys and values of one (sequence, KV head) in fp64, unrotated: sink tokens,
+    then history tokens dequantised in rotated space and mapped back by R^T, then recent tokens."""
+    n_sink, n_hist, _ = segment_lengths(length, geom)
+    ks = [np.asarray(sink_k[slot, kv, :n_sink], dtype=np.float64)]
+    vs = [np.asarray(sink_v[slot, kv, :n_sink], dtype=np.float64)]
+    if n_hist:
+        (kc, kS, kZ), (vc, vS, vZ) = load_history(pool, page_table[b], n_hist, kv, geom)
+        ks.append(unrotate(dequantize(kc, kS, kZ, geom.group), u_k[kv]))
+        vs.append(unrotate(dequantize(vc, vS, vZ, geom.group), u_v[kv]))
+    rs = recent_slots(length, geom)
+    ks.append(np.asarray(recent_k[slot, kv, rs], dtype=np.float64))
+    vs.append(np.asarray(recent_v[slot, kv, rs], dtype=np.float64))
+    return np.concatenate(ks, 0), np.concatenate(vs, 0)
+
+
+def attend(q, keys, values, sm_scale: float):
+    """Softmax attention of one query over keys/values (n, d), fp64.  Returns (out (d,), lse)."""
+    s = (np.asarray(keys, np.float64) @ np.asarray(q, np.float64)) * sm_scale
+    m = s.max()
+    w = np.exp(s - m)
+    tot = w.sum()
+    return (w @ np.asarray(values, np.float64)) / tot, m + math.log(tot)
+
+
+def decode_attention(pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot, seq_lens,
+                     q, u_k, u_v, geom: Geometry, sm_scale=None, heads=None):
+    """Decode attention of q (B, Hq, d) over each sequence's three-segment cache.
+
+    Returns (out fp64 (B, Hq, d), lse fp64 (B, Hq)); ``heads`` optionally restricts the work to a
+    list of (b, q_head) pairs (other rows stay NaN)."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, d = q.shape
+    hkv = np.asarray(u_k).shape[0]
+    gqa = hq // hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    out = np.full((bsz, hq, d), np.nan)
+    lse = np.full((bsz, hq), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(bsz) for h in range(hq)]
+    cache = {}
+    for b, h in todo:
+        kv = h // gqa
+        if (b, kv) not in cache:
+            cache = {(b, kv): gather_cache(pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                                           u_k, u_v, int(seq_slot[b]), b, kv, int(seq_lens[b]),
+                                           geom)}
+        keys, values = cache[(b, kv)]
+        out[b, h], lse[b, h] = attend(q[b, h], keys, values, sm_scale)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------------------
+# online-softmax partials and their merge ([W1] §OSCAR 的设计: BF16 and INT2 parts are combined by
+# an online-softmax merge)
+
+def softmax_partial(q, keys, values, sm_scale: float):
+    """(m, l, acc) of one segment: m = max score, l = sum exp(s - m), acc = sum exp(s - m) v."""
+    s = (np.asarray(keys, np.float64) @ np.asarray(q, np.float64)) * sm_scale
+    if s.size == 0:
+        return -np.inf, 0.0, np.zeros(np.asarray(values).shape[-1])
+    m = s.max()
+    w = np.exp(s - m)
+    return m, w.sum(), w @ np.asarray(values, np.float64)
+
+
+def merge_partials(parts):
+    """Merge (m, l, acc) partials of disjoint segments into one (m, l, acc)."""
+    m = max(p[0] for p in parts)
+    if m == -np.inf:
+        return m, 0.0, np.zeros_like(parts[0][2])
+    l = sum(p[1] * math.exp(p[0] - m) for p in parts if p[1] > 0)
+    acc = sum(p[2] * math.exp(p[0] - m) for p in parts if p[1] > 0)
+    return m, l, acc
+
+
+# ----------------------------------------------------------------------------------------------
+# offline calibration ([W1] §OSCAR 的设计 and figure 2, left side; [P] 摘要; reading R11)
+
+def _sorted_eigenvectors(c: np.ndarray) -> np.ndarray:
+    w, v = np.linalg.eigh(c)
+    order = np.argsort(w)[::-1]
+    v = v[:, order]
+    pick = np.argmax(np.abs(v), axis=0)
+    sign = np.sign(v[pick, np.arange(v.shape[1])])
+    return v * sign[None, :]
+
+
+def key_covariance(q_cal) -> np.ndarray:
+    """Q^T Q over calibration queries q_cal (n, d) (all query heads of one KV head stacked)."""
+    q = np.asarray(q_cal, dtype=np.float64)
+    return q.T @ q
+
+
+def value_covariance(q_cal, keys, values, sm_scale: float, chunk: int = 512) -> np.ndarray:
+    """(S V)^T (S V) with S = softmax(Q K^T * sm_scale) row-wise, over calibration queries."""
+    q = np.asarray(q_cal, dtype=np.float64)
+    k = np.asarray(keys, dtype=np.float64)
+    v = np.asarray(values, dtype=np.float64)
+    c = np.zeros((v.shape[1], v.shape[1]))
+    for i in range(0, q.shape[0], chunk):
+        s = (q[i:i + chunk] @ k.T) * sm_scale
+        s = np.exp(s - s.max(axis=1, keepdims=True))
+        s /= s.sum(axis=1, keepdims=True)
+        sv = s @ v
+        c += sv.T @ sv
+    return c
+
+
+def key_rotation(q_cal) -> np.ndarray:
+    return _sorted_eigenvectors(key_covariance(q_cal))
+
+
+def value_rotation(q_cal, keys, values, sm_scale: float) -> np.ndarray:
+    return _sorted_eigenvectors(value_covariance(q_cal, keys, values, sm_scale))
+
+
+def clip_threshold(x, u, percentile: float = 99.9) -> float:
+    """Percentile (linear interpolation) of |x R| over all tokens and channels of x (n, d)."""
+    return float(np.percentile(np.abs(rotate(x, u)), percentile))
+
+
+# ----------------------------------------------------------------------------------------------
+# byte accounting ([W3] evaluation: effective bits per KV element and the ~8x memory claim)
+
+def history_bytes_per_token_head(head_dim: int, group: int) -> int:
+    """Key codes + value codes + fp16 (scale, zero) per group for keys and values."""
+    return 2 * head_dim // 4 + 2 * (head_dim // group) * 4
+
+
+def effective_bits_per_element(length: int, head_dim: int, group: int, sink: int = 64,
+                               recent: int = 256) -> float:
+    """Average stored bits per K/V element of a context: BF16 sink and recent, INT2 history."""
+    bf16 = min(length, sink + recent)
+    hist = max(0, length - sink - recent)
+    bits = bf16 * 16.0 + hist * history_bytes_per_token_head(head_dim, group) * 8 / (2 * head_dim)
+    return bits / length
