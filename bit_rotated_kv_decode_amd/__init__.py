@@ -1,0 +1,250 @@
+"""OSCAR INT2-history decode path for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``liboscar.so`` (C ABI declared in ``include/oscar.h``): this module only
+marshals arguments; every step of the path runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current stream.  There is no CPU fallback: if the library is not built or
+a call fails, an ``OscarError`` is raised.
+
+The entry points follow the OSCAR write-up "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化"
+(section OSCAR 的设计): ``append`` writes a decode step's new token into the BF16 recent window
+and demotes the token it displaces into the rotated INT2 history, ``demote`` encodes a run of
+tokens into the history, and ``decode_attn`` runs decode attention over the BF16 sink, the INT2
+history and the BF16 recent window with an online-softmax merge.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
+    "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "check_page_table",
+    "demote", "append", "decode_attn", "Cache", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
+    "RECENT_TOKENS",
+]
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+SINK_TOKENS = 64
+RECENT_TOKENS = 256
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "liboscar.so")
+
+
+class OscarError(RuntimeError):
+    """A liboscar call returned an error status, or the library is missing."""
+
+
+class Layout(ctypes.Structure):
+    """Mirror of ``oscar_layout`` (include/oscar.h)."""
+
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "head_dim", "group_size", "num_q_heads", "num_kv_heads", "page_tokens", "sink_tokens",
+        "recent_tokens", "num_pages", "max_seqs", "max_pages_per_seq")]
+
+    def __repr__(self):
+        return "Layout(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_LP = ctypes.POINTER(Layout)
+
+_SIGNATURES = {
+    "oscar_abi_version": (ctypes.c_uint32, []),
+    "oscar_status_string": (ctypes.c_char_p, [_i32]),
+    "oscar_last_error": (ctypes.c_char_p, []),
+    "oscar_layout_check": (_i32, [_LP]),
+    "oscar_page_block_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_page_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_pool_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_sink_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_recent_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_decode_workspace_bytes": (ctypes.c_size_t, [_LP, _i32, _i32]),
+    "oscar_check_page_table": (_i32, [_LP, _vp, _vp, _i32, _i32]),
+    "oscar_demote": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
+                            _i32, _i32, _vp]),
+    "oscar_append": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _i32, _vp]),
+    "oscar_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _i32, _i32,
+                                 _vp]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liboscar.so from this package directory (raises OscarError if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OscarError(f"{LIB_PATH} is not built: run bit_rotated_kv_decode_amd.build.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise OscarError(f"{what}: {L.oscar_status_string(status).decode()} ({status}): "
+                         f"{L.oscar_last_error().decode()}")
+
+
+def make_layout(num_q_heads: int, num_kv_heads: int, num_pages: int, max_seqs: int,
+                max_pages_per_seq: int, group_size: int = 128, head_dim: int = HEAD_DIM) -> Layout:
+    lay = Layout(head_dim, group_size, num_q_heads, num_kv_heads, PAGE_TOKENS, SINK_TOKENS,
+                 RECENT_TOKENS, num_pages, max_seqs, max_pages_per_seq)
+    _check(lib().oscar_layout_check(ctypes.byref(lay)), "layout")
+    return lay
+
+
+def page_block_bytes(lay: Layout) -> int:
+    return lib().oscar_page_block_bytes(ctypes.byref(lay))
+
+
+def page_bytes(lay: Layout) -> int:
+    return lib().oscar_page_bytes(ctypes.byref(lay))
+
+
+def pool_bytes(lay: Layout) -> int:
+    return lib().oscar_pool_bytes(ctypes.byref(lay))
+
+
+def sink_bytes(lay: Layout) -> int:
+    return lib().oscar_sink_bytes(ctypes.byref(lay))
+
+
+def recent_bytes(lay: Layout) -> int:
+    return lib().oscar_recent_bytes(ctypes.byref(lay))
+
+
+def decode_workspace_bytes(lay: Layout, batch: int, max_seq_len: int) -> int:
+    return lib().oscar_decode_workspace_bytes(ctypes.byref(lay), batch, max_seq_len)
+
+
+def check_page_table(lay: Layout, page_table, seq_lens, extra_tokens: int = 0) -> None:
+    """Validate a host copy of a page table (int32 [B, max_pages_per_seq]) and lengths."""
+    pt = torch.as_tensor(page_table, dtype=torch.int32).cpu().contiguous()
+    sl = torch.as_tensor(seq_lens, dtype=torch.int32).cpu().contiguous()
+    if pt.dim() != 2 or pt.shape[1] != lay.max_pages_per_seq or pt.shape[0] != sl.numel():
+        raise OscarError("page table must be [batch, max_pages_per_seq] with one length per row")
+    _check(lib().oscar_check_page_table(ctypes.byref(lay), pt.data_ptr(), sl.data_ptr(),
+                                        sl.numel(), extra_tokens), "check_page_table")
+
+
+# ----------------------------------------------------------------------------------------------
+# argument marshalling helpers
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be on a GPU device")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _contig(t: torch.Tensor, name: str, dtype) -> int:
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    return _dev(t, name, dtype)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def demote(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, u_k: torch.Tensor,
+           u_v: torch.Tensor, clip_k: torch.Tensor, clip_v: torch.Tensor, k_src: torch.Tensor,
+           v_src: torch.Tensor, hist_start: torch.Tensor) -> None:
+    """Encode k_src / v_src (bf16 [B, n, Hkv, 128], unit stride on the last axis, the same
+    strides for both) into history indices hist_start[b] + i (oscar_demote)."""
+    if k_src.dim() != 4 or k_src.shape != v_src.shape or k_src.stride() != v_src.stride():
+        raise TypeError("k_src / v_src must be [B, n, Hkv, 128] with identical strides")
+    if k_src.stride(3) != 1 or k_src.shape[3] != HEAD_DIM or k_src.shape[2] != lay.num_kv_heads:
+        raise TypeError("k_src last axis must be contiguous head_dim; axis 2 the KV heads")
+    bsz, n = k_src.shape[0], k_src.shape[1]
+    _check(lib().oscar_demote(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(u_k, "u_k", torch.float32),
+        _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
+        _contig(clip_v, "clip_v", torch.float32), _dev(k_src, "k_src", torch.bfloat16),
+        _dev(v_src, "v_src", torch.bfloat16), k_src.stride(0), k_src.stride(1), k_src.stride(2),
+        _contig(hist_start, "hist_start", torch.int32), bsz, n, _stream()), "demote")
+
+
+def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_k,
+           clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot: torch.Tensor,
+           seq_lens: torch.Tensor) -> None:
+    """Decode-step write of k_new / v_new (bf16 [B, Hkv, 128]) at positions seq_lens[b]
+    (oscar_append); the caller advances seq_lens afterwards."""
+    bsz = seq_lens.numel()
+    if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
+        raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
+    _check(lib().oscar_append(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
+        _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
+        _contig(clip_v, "clip_v", torch.float32), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_lens, "seq_lens", torch.int32), bsz, _stream()), "append")
+
+
+def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                seq_lens, q: torch.Tensor, u_k, u_v, out: torch.Tensor, workspace: torch.Tensor,
+                max_seq_len: int, lse: Optional[torch.Tensor] = None,
+                sm_scale: float = 0.0) -> None:
+    """Decode attention of q (bf16 [B, Hq, 128]) into out (fp32 [B, Hq, 128]) and optionally
+    lse (fp32 [B, Hq]) (oscar_decode_attn).  workspace: uint8 tensor of at least
+    decode_workspace_bytes(lay, B, max_seq_len) bytes."""
+    bsz = seq_lens.numel()
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _check(lib().oscar_decode_attn(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_lens, "seq_lens", torch.int32), _contig(q, "q", torch.bfloat16),
+        _contig(u_k, "u_k", torch.float32), _contig(u_v, "u_v", torch.float32), float(sm_scale),
+        _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        _stream()), "decode_attn")
+
+
+@dataclasses.dataclass
+class Cache:
+    """Device buffers of one layer's three-segment cache, allocated with torch."""
+
+    layout: Layout
+    pool: torch.Tensor       # uint8 [num_pages, page_bytes]
+    sink_k: torch.Tensor     # bf16 [max_seqs, Hkv, 64, 128]
+    sink_v: torch.Tensor
+    recent_k: torch.Tensor   # bf16 [max_seqs, Hkv, 256, 128]
+    recent_v: torch.Tensor
+
+    @classmethod
+    def allocate(cls, lay: Layout, device="cuda", zero: bool = True) -> "Cache":
+        mk = torch.zeros if zero else torch.empty
+        pool = mk((max(lay.num_pages, 1), page_bytes(lay)), dtype=torch.uint8, device=device)
+        seg = lambda n: mk((max(lay.max_seqs, 1), lay.num_kv_heads, n, HEAD_DIM),
+                           dtype=torch.bfloat16, device=device)
+        return cls(lay, pool, seg(SINK_TOKENS), seg(SINK_TOKENS), seg(RECENT_TOKENS),
+                   seg(RECENT_TOKENS))

@@ -1,0 +1,265 @@
+// Demotion of keys / values into the rotated INT2 history, and the decode-step append.
+//
+// The steps follow the OSCAR write-up "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化",
+// section OSCAR 的设计: the token leaving the BF16 recent window is rotated by R = U * Hadamard *
+// bit-reversal, clipped, quantised with a per-group scale and zero point and packed four 2-bit
+// codes to a byte.  One 64-lane wave encodes one (token, KV head, K|V) vector: lane l owns rotated
+// channels l and l + 64.  The rotation runs in fp64 (x U as a matrix-vector product, the Hadamard
+// as cross-lane butterflies), the rotated vector is rounded once to fp32 and every step that
+// decides a code (clip, group min / max, (max - min) / 3, fp16 rounding, (x - z) / s, rint) runs
+// in IEEE fp32.
+#include "device_common.h"
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+constexpr int kWaves = 4;
+
+struct LaneCodes {
+  uint32_t c0, c1;     // codes of channels lane and lane + 64
+  uint32_t meta[2];    // per group: fp16 scale in bits 0..15, fp16 zero in bits 16..31
+};
+
+// Clip and quantise the rotated channels (lane, lane + 64) of one vector; all lanes of the wave
+// must call this together (the group min / max are wave reductions).
+__device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float clip,
+                                                   int n_groups) {
+  float x0 = static_cast<float>(r0);
+  float x1 = static_cast<float>(r1);
+  x0 = fminf(fmaxf(x0, -clip), clip);
+  x1 = fminf(fmaxf(x1, -clip), clip);
+  float mn[2], mx[2];
+  if (n_groups == 1) {
+    mn[0] = mn[1] = dev::wave_min(fminf(x0, x1));
+    mx[0] = mx[1] = dev::wave_max(fmaxf(x0, x1));
+  } else {
+    // group 0 = channels 0..63 (slot 0 of every lane), group 1 = channels 64..127 (slot 1)
+    mn[0] = dev::wave_min(x0);
+    mx[0] = dev::wave_max(x0);
+    mn[1] = dev::wave_min(x1);
+    mx[1] = dev::wave_max(x1);
+  }
+  LaneCodes out;
+  float sf[2], zf[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float s32 = (mx[m] - mn[m]) / 3.0f;
+    const __half s16 = __float2half_rn(s32);
+    const __half z16 = __float2half_rn(mn[m]);
+    sf[m] = __half2float(s16);
+    zf[m] = __half2float(z16);
+    out.meta[m] = static_cast<uint32_t>(__half_as_ushort(s16)) |
+                  (static_cast<uint32_t>(__half_as_ushort(z16)) << 16);
+  }
+  auto code = [](float x, float s, float z) -> uint32_t {
+    if (s == 0.0f) return 0u;
+    const float t = rintf((x - z) / s);
+    return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
+  };
+  out.c0 = code(x0, sf[0], zf[0]);
+  out.c1 = code(x1, sf[1], zf[1]);
+  return out;
+}
+
+__device__ __forceinline__ uint8_t* page_block(uint8_t* pool, const int32_t* page_table,
+                                               int max_pages_per_seq, int b, int hist_idx, int hkv,
+                                               int h, int blk_bytes) {
+  const int page = page_table[static_cast<int64_t>(b) * max_pages_per_seq + hist_idx / kPage];
+  return pool + (static_cast<int64_t>(page) * hkv + h) * blk_bytes;
+}
+
+// Key codes are packed along channels: dword w of a token row holds channels 16w..16w+15.
+__device__ __forceinline__ void store_key_row(uint8_t* blk, int slot, uint32_t c0, uint32_t c1) {
+  const int lane = dev::lane_id();
+  uint32_t v0 = c0 << (2 * (lane & 15));
+  uint32_t v1 = c1 << (2 * (lane & 15));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    v0 |= __shfl_xor(v0, m);
+    v1 |= __shfl_xor(v1, m);
+  }
+  if ((lane & 15) == 0) {
+    uint32_t* row = reinterpret_cast<uint32_t*>(blk + kKCodesOff + slot * (kHeadDim / 4));
+    row[lane >> 4] = v0;
+    row[4 + (lane >> 4)] = v1;
+  }
+}
+
+__device__ __forceinline__ void store_meta(uint8_t* blk, int meta_off, int slot, int n_groups,
+                                           const LaneCodes& q) {
+  if (dev::lane_id() == 0) {
+    uint32_t* m = reinterpret_cast<uint32_t*>(blk + meta_off) + slot * n_groups;
+    for (int g = 0; g < n_groups; ++g) m[g] = q.meta[g];
+  }
+}
+
+// Replace the bits under `mask` of a pool dword that other waves may update concurrently.
+__device__ __forceinline__ void merge_bits(uint32_t* p, uint32_t mask, uint32_t bits) {
+  uint32_t old = *p;
+  while (true) {
+    const uint32_t want = (old & ~mask) | bits;
+    const uint32_t prev = atomicCAS(p, old, want);
+    if (prev == old) break;
+    old = prev;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Bulk demotion.  A wave encodes the tokens of one 16-slot run of a page (history indices
+// [16k, 16k + 16) that the call covers) for one (sequence, KV head, K|V).  The 16 slots share the
+// value-code dwords, which a full run writes with plain stores; a partly covered run merges its
+// bits with compare-and-swap.
+constexpr int kRun = 16;
+
+__global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_seq) {
+  __shared__ float xs[kWaves][kRun * kHeadDim];
+  const int wave = threadIdx.x >> 6;
+  const int lane = dev::lane_id();
+  int64_t wid = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int tensor = static_cast<int>(wid % 2);
+  wid /= 2;
+  const int h = static_cast<int>(wid % a.hkv);
+  wid /= a.hkv;
+  const int run = static_cast<int>(wid % runs_per_seq);
+  const int b = static_cast<int>(wid / runs_per_seq);
+  if (b >= a.batch) return;
+
+  const int hs = a.hist_start[b];
+  const int first = (hs / kRun + run) * kRun;   // first history index of this run
+  const int lo = max(first, hs);
+  const int hi = min(first + kRun, hs + a.n_tokens);
+  if (lo >= hi) return;
+
+  const uint16_t* src = tensor == 0 ? a.k_src : a.v_src;
+  float* x = xs[wave];
+  for (int t = 0; t < kRun; ++t) {
+    const int idx = first + t;
+    float v0 = 0.0f, v1 = 0.0f;
+    if (idx >= lo && idx < hi) {
+      const uint16_t* row = src + b * a.stride_b + static_cast<int64_t>(idx - hs) * a.stride_t +
+                            static_cast<int64_t>(h) * a.stride_h;
+      v0 = dev::bf16_to_f32(row[lane]);
+      v1 = dev::bf16_to_f32(row[lane + 64]);
+    }
+    x[t * kHeadDim + lane] = v0;
+    x[t * kHeadDim + lane + 64] = v1;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  const float* u = (tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim;
+  const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+  double r[kRun][2];
+  dev::rotate_fp64<kRun>(x, u, r);
+
+  const int blk_bytes = block_bytes(a.n_groups);
+  uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, first, a.hkv, h,
+                            blk_bytes);
+  const int slot0 = first % kPage;
+  const int meta_off = tensor == 0 ? kKMetaOff : v_meta_off(a.n_groups);
+  uint32_t vword0 = 0, vword1 = 0, vmask = 0;
+#pragma unroll
+  for (int t = 0; t < kRun; ++t) {
+    const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups);
+    const int idx = first + t;
+    if (idx < lo || idx >= hi) continue;
+    if (tensor == 0) {
+      store_key_row(blk, slot0 + t, q.c0, q.c1);
+    } else {
+      vword0 |= q.c0 << (2 * t);
+      vword1 |= q.c1 << (2 * t);
+      vmask |= 3u << (2 * t);
+    }
+    store_meta(blk, meta_off, slot0 + t, a.n_groups, q);
+  }
+  if (tensor == 1) {
+    // value codes of channel j for this run: dword (j * 4 + slot0 / 16) of the value region
+    uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
+    const int dw = slot0 / kRun;
+    if (vmask == 0xFFFFFFFFu) {
+      vc[lane * 4 + dw] = vword0;
+      vc[(lane + 64) * 4 + dw] = vword1;
+    } else {
+      merge_bits(&vc[lane * 4 + dw], vmask, vword0);
+      merge_bits(&vc[(lane + 64) * 4 + dw], vmask, vword1);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-step append: block = 2 waves for one (sequence, KV head); wave 0 keys, wave 1 values.
+__global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
+  __shared__ float xs[2][kHeadDim];
+  const int tensor = threadIdx.x >> 6;
+  const int lane = dev::lane_id();
+  const int h = blockIdx.x % a.hkv;
+  const int b = blockIdx.x / a.hkv;
+  const int pos = a.seq_lens[b];
+  const int64_t slot = a.seq_slot[b];
+  const uint16_t* nw = (tensor == 0 ? a.k_new : a.v_new) +
+                       (static_cast<int64_t>(b) * a.hkv + h) * kHeadDim;
+  const uint16_t n0 = nw[lane];
+  const uint16_t n1 = nw[lane + 64];
+  if (pos < kSink) {
+    uint16_t* row = (tensor == 0 ? a.sink_k : a.sink_v) +
+                    ((slot * a.hkv + h) * kSink + pos) * kHeadDim;
+    row[lane] = n0;
+    row[lane + 64] = n1;
+    return;
+  }
+  uint16_t* ring = (tensor == 0 ? a.recent_k : a.recent_v) +
+                   ((slot * a.hkv + h) * kRecent + pos % kRecent) * kHeadDim;
+  if (pos >= kSink + kRecent) {
+    float* x = xs[tensor];
+    x[lane] = dev::bf16_to_f32(ring[lane]);
+    x[lane + 64] = dev::bf16_to_f32(ring[lane + 64]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const float* u = (tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim;
+    const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+    double r[1][2];
+    dev::rotate_fp64<1>(x, u, r);
+    const LaneCodes q = quantize_lane(r[0][0], r[0][1], clip, a.n_groups);
+    const int idx = pos - kSink - kRecent;
+    const int blk_bytes = block_bytes(a.n_groups);
+    uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
+                              blk_bytes);
+    const int slot_in_page = idx % kPage;
+    if (tensor == 0) {
+      store_key_row(blk, slot_in_page, q.c0, q.c1);
+      store_meta(blk, kKMetaOff, slot_in_page, a.n_groups, q);
+    } else {
+      uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
+      const int dw = slot_in_page / 16;
+      const int sh = 2 * (slot_in_page % 16);
+      merge_bits(&vc[lane * 4 + dw], 3u << sh, q.c0 << sh);
+      merge_bits(&vc[(lane + 64) * 4 + dw], 3u << sh, q.c1 << sh);
+      store_meta(blk, v_meta_off(a.n_groups), slot_in_page, a.n_groups, q);
+    }
+  }
+  // the old row has been read (its values were consumed above); overwrite it with the new token
+  ring[lane] = n0;
+  ring[lane + 64] = n1;
+}
+
+}  // namespace
+
+hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.n_tokens == 0) return hipSuccess;
+  const int runs_per_seq = (a.n_tokens + kRun - 1) / kRun + 1;
+  const int64_t waves = static_cast<int64_t>(a.batch) * runs_per_seq * a.hkv * 2;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(demote_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a,
+                     runs_per_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(a.batch * a.hkv)), dim3(128), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

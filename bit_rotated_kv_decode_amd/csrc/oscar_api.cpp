@@ -1,0 +1,332 @@
+// C-ABI entry points of liboscar: argument validation (host only, before any HIP call), work
+// planning and kernel launches.  See include/oscar.h for the contract of every function.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_map>
+
+#include "oscar.h"
+#include "oscar_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+oscar_status fail(oscar_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+oscar_status ok() {
+  g_last_error.clear();
+  return OSCAR_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+oscar_status check_layout(const oscar_layout* l) {
+  if (l == nullptr) return fail(OSCAR_ERR_NULL, "layout is NULL");
+  if (l->head_dim != oscar::kHeadDim)
+    return fail(OSCAR_ERR_SHAPE, "head_dim %d unsupported (must be 128)", l->head_dim);
+  if (l->group_size != 128 && l->group_size != 64)
+    return fail(OSCAR_ERR_SHAPE, "group_size %d unsupported (must be 64 or 128)", l->group_size);
+  if (l->num_q_heads <= 0 || l->num_kv_heads <= 0 || l->num_q_heads % l->num_kv_heads != 0)
+    return fail(OSCAR_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                l->num_q_heads, l->num_kv_heads);
+  const int gqa = l->num_q_heads / l->num_kv_heads;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8)
+    return fail(OSCAR_ERR_SHAPE, "query heads per KV head %d unsupported (1, 2, 4 or 8)", gqa);
+  if (l->page_tokens != oscar::kPage || l->sink_tokens != oscar::kSink ||
+      l->recent_tokens != oscar::kRecent)
+    return fail(OSCAR_ERR_SHAPE, "page/sink/recent tokens must be 64/64/256 (got %d/%d/%d)",
+                l->page_tokens, l->sink_tokens, l->recent_tokens);
+  if (l->num_pages < 0 || l->max_seqs < 0 || l->max_pages_per_seq < 0)
+    return fail(OSCAR_ERR_SHAPE, "negative num_pages / max_seqs / max_pages_per_seq");
+  return OSCAR_OK;
+}
+
+int n_groups(const oscar_layout* l) { return oscar::kHeadDim / l->group_size; }
+
+oscar_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(OSCAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+namespace oscar {
+
+Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
+  Plan p;
+  p.batch = batch;
+  p.hq = lay.num_q_heads;
+  p.hkv = lay.num_kv_heads;
+  p.gqa = p.hq / p.hkv;
+  p.n_groups = kHeadDim / lay.group_size;
+  const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
+  p.max_pages = (n_hist + kPage - 1) / kPage;
+  // Aim for about 1024 work items (four per compute unit) with at least one page per wave.
+  const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
+  p.pages_per_split = static_cast<int>(std::max<long long>(4, (items + 1023) / 1024));
+  p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t rows = static_cast<size_t>(batch) * p.hq;
+  size_t off = 0;
+  p.off_qrot = off;
+  off = al(off + rows * kHeadDim * 4);
+  p.off_sigma = off;
+  off = al(off + rows * 2 * 4);
+  p.off_int2_ml = off;
+  off = al(off + rows * std::max(p.num_splits, 1) * 2 * 4);
+  p.off_int2_acc = off;
+  off = al(off + rows * std::max(p.num_splits, 1) * kHeadDim * 4);
+  p.off_bf16_ml = off;
+  off = al(off + rows * kBf16Chunks * 2 * 4);
+  p.off_bf16_acc = off;
+  off = al(off + rows * kBf16Chunks * kHeadDim * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace oscar
+
+extern "C" {
+
+uint32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
+
+const char* oscar_status_string(oscar_status s) {
+  switch (s) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_ERR_NULL: return "null pointer";
+    case OSCAR_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case OSCAR_ERR_ALIGN: return "misaligned pointer or stride";
+    case OSCAR_ERR_RANGE: return "value out of range";
+    case OSCAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case OSCAR_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* oscar_last_error(void) { return g_last_error.c_str(); }
+
+oscar_status oscar_layout_check(const oscar_layout* layout) {
+  const oscar_status st = check_layout(layout);
+  return st == OSCAR_OK ? ok() : st;
+}
+
+size_t oscar_page_block_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(oscar::block_bytes(n_groups(l)));
+}
+
+size_t oscar_page_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(oscar::block_bytes(n_groups(l))) * l->num_kv_heads;
+}
+
+size_t oscar_pool_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return oscar_page_bytes(l) * static_cast<size_t>(l->num_pages);
+}
+
+size_t oscar_sink_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(l->max_seqs) * l->num_kv_heads * oscar::kSink * oscar::kHeadDim * 2;
+}
+
+size_t oscar_recent_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(l->max_seqs) * l->num_kv_heads * oscar::kRecent * oscar::kHeadDim *
+         2;
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_layout* l, int32_t batch, int32_t max_seq_len) {
+  if (check_layout(l) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
+  return oscar::make_plan(*l, batch, max_seq_len).total;
+}
+
+oscar_status oscar_check_page_table(const oscar_layout* l, const int32_t* table,
+                                    const int32_t* seq_lens, int32_t batch, int32_t extra) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || extra < 0) return fail(OSCAR_ERR_RANGE, "negative batch or extra_tokens");
+  if (batch > 0 && (table == nullptr || seq_lens == nullptr))
+    return fail(OSCAR_ERR_NULL, "page table or seq_lens is NULL");
+  // page id -> (sequence, logical page) of its first user
+  std::unordered_map<int32_t, std::pair<int32_t, int32_t>> owner;
+  for (int32_t b = 0; b < batch; ++b) {
+    const long long len = static_cast<long long>(seq_lens[b]) + extra;
+    if (seq_lens[b] < 0) return fail(OSCAR_ERR_RANGE, "seq_lens[%d] = %d < 0", b, seq_lens[b]);
+    const long long hist = std::max(0LL, len - oscar::kSink - oscar::kRecent);
+    const long long pages = (hist + oscar::kPage - 1) / oscar::kPage;
+    if (pages > l->max_pages_per_seq)
+      return fail(OSCAR_ERR_RANGE, "sequence %d needs %lld pages > max_pages_per_seq %d", b,
+                  pages, l->max_pages_per_seq);
+    const int32_t* row = table + static_cast<size_t>(b) * l->max_pages_per_seq;
+    for (int32_t p = 0; p < pages; ++p) {
+      const int32_t id = row[p];
+      if (id < 0 || id >= l->num_pages)
+        return fail(OSCAR_ERR_RANGE, "page_table[%d][%d] = %d outside [0, %d)", b, p, id,
+                    l->num_pages);
+      auto it = owner.find(id);
+      if (it == owner.end()) {
+        owner.emplace(id, std::make_pair(b, p));
+        continue;
+      }
+      const int32_t ob = it->second.first, op = it->second.second;
+      if (ob == b || op != p)
+        return fail(OSCAR_ERR_RANGE, "page %d used by (%d,%d) and (%d,%d)", id, ob, op, b, p);
+      const int32_t* orow = table + static_cast<size_t>(ob) * l->max_pages_per_seq;
+      for (int32_t q = 0; q <= p; ++q)
+        if (orow[q] != row[q])
+          return fail(OSCAR_ERR_RANGE, "shared page %d of sequences %d and %d is not part of a "
+                      "common prefix", id, ob, b);
+    }
+  }
+  return ok();
+}
+
+oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page_table,
+                          const float* u_k, const float* u_v, const float* clip_k,
+                          const float* clip_v, const void* k_src, const void* v_src,
+                          int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                          const int32_t* hist_start, int32_t batch, int32_t n_tokens,
+                          void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || n_tokens < 0) return fail(OSCAR_ERR_RANGE, "negative batch or n_tokens");
+  if (batch == 0 || n_tokens == 0) return ok();
+  if (!pool || !page_table || !u_k || !u_v || !clip_k || !clip_v || !k_src || !v_src ||
+      !hist_start)
+    return fail(OSCAR_ERR_NULL, "oscar_demote: a required pointer is NULL");
+  if (stride_b < 0 || stride_t < 0 || stride_h < 0)
+    return fail(OSCAR_ERR_RANGE, "negative source stride");
+  if (!aligned(pool, 16)) return fail(OSCAR_ERR_ALIGN, "pool must be 16-byte aligned");
+  if (!aligned(k_src, 2) || !aligned(v_src, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
+      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(page_table, 4) ||
+      !aligned(hist_start, 4))
+    return fail(OSCAR_ERR_ALIGN, "oscar_demote: misaligned pointer");
+  oscar::DemoteArgs a;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.hkv = l->num_kv_heads;
+  a.n_groups = n_groups(l);
+  a.u_k = u_k;
+  a.u_v = u_v;
+  a.clip_k = clip_k;
+  a.clip_v = clip_v;
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.stride_b = stride_b;
+  a.stride_t = stride_t;
+  a.stride_h = stride_h;
+  a.hist_start = hist_start;
+  a.batch = batch;
+  a.n_tokens = n_tokens;
+  return hip_status(oscar::launch_demote(a, static_cast<hipStream_t>(stream)), "oscar_demote");
+}
+
+oscar_status oscar_append(const oscar_layout* l, void* pool, const int32_t* page_table,
+                          void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                          const float* u_k, const float* u_v, const float* clip_k,
+                          const float* clip_v, const void* k_new, const void* v_new,
+                          const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
+                          void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (batch == 0) return ok();
+  if (l->max_seqs == 0) return fail(OSCAR_ERR_SHAPE, "layout has no sequence slots");
+  if (!pool || !page_table || !sink_k || !sink_v || !recent_k || !recent_v || !u_k || !u_v ||
+      !clip_k || !clip_v || !k_new || !v_new || !seq_slot || !seq_lens)
+    return fail(OSCAR_ERR_NULL, "oscar_append: a required pointer is NULL");
+  if (!aligned(pool, 16) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
+      !aligned(recent_k, 16) || !aligned(recent_v, 16))
+    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
+      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(seq_slot, 4) ||
+      !aligned(seq_lens, 4) || !aligned(page_table, 4))
+    return fail(OSCAR_ERR_ALIGN, "oscar_append: misaligned pointer");
+  oscar::AppendArgs a;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.hkv = l->num_kv_heads;
+  a.n_groups = n_groups(l);
+  a.sink_k = static_cast<uint16_t*>(sink_k);
+  a.sink_v = static_cast<uint16_t*>(sink_v);
+  a.recent_k = static_cast<uint16_t*>(recent_k);
+  a.recent_v = static_cast<uint16_t*>(recent_v);
+  a.u_k = u_k;
+  a.u_v = u_v;
+  a.clip_k = clip_k;
+  a.clip_v = clip_v;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seq_slot = seq_slot;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  return hip_status(oscar::launch_append(a, static_cast<hipStream_t>(stream)), "oscar_append");
+}
+
+oscar_status oscar_decode_attn(const oscar_layout* l, const void* pool, const int32_t* page_table,
+                               const void* sink_k, const void* sink_v, const void* recent_k,
+                               const void* recent_v, const int32_t* seq_slot,
+                               const int32_t* seq_lens, const void* q, const float* u_k,
+                               const float* u_v, float sm_scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int32_t batch,
+                               int32_t max_seq_len, void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (batch == 0) return ok();
+  if (max_seq_len < 1) return fail(OSCAR_ERR_RANGE, "max_seq_len %d < 1", max_seq_len);
+  const oscar::Plan plan = oscar::make_plan(*l, batch, max_seq_len);
+  if (plan.max_pages > l->max_pages_per_seq)
+    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
+                max_seq_len, plan.max_pages, l->max_pages_per_seq);
+  if ((plan.max_pages > 0 && (!pool || !page_table)) || !sink_k || !sink_v || !recent_k ||
+      !recent_v || !seq_slot || !seq_lens || !q || !u_k || !u_v || !out)
+    return fail(OSCAR_ERR_NULL, "oscar_decode_attn: a required pointer is NULL");
+  if (workspace == nullptr || workspace_bytes < plan.total)
+    return fail(OSCAR_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes,
+                plan.total);
+  if (!aligned(workspace, 256)) return fail(OSCAR_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((pool && !aligned(pool, 16)) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
+      !aligned(recent_k, 16) || !aligned(recent_v, 16))
+    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
+  if (!aligned(q, 4) || !aligned(u_k, 4) || !aligned(u_v, 4) || !aligned(out, 4) ||
+      (lse && !aligned(lse, 4)) || !aligned(seq_slot, 4) || !aligned(seq_lens, 4) ||
+      (page_table && !aligned(page_table, 4)))
+    return fail(OSCAR_ERR_ALIGN, "oscar_decode_attn: misaligned pointer");
+  oscar::DecodeArgs a;
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.sink_k = static_cast<const uint16_t*>(sink_k);
+  a.sink_v = static_cast<const uint16_t*>(sink_v);
+  a.recent_k = static_cast<const uint16_t*>(recent_k);
+  a.recent_v = static_cast<const uint16_t*>(recent_v);
+  a.seq_slot = seq_slot;
+  a.seq_lens = seq_lens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.u_k = u_k;
+  a.u_v = u_v;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : 0.08838834764831845f;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = static_cast<uint8_t*>(workspace);
+  return hip_status(oscar::launch_decode(a, plan, static_cast<hipStream_t>(stream)),
+                    "oscar_decode_attn");
+}
+
+}  // extern "C"

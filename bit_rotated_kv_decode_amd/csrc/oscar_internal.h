@@ -1,0 +1,105 @@
+// Internal interface between the C-ABI host layer (oscar_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 64;
+constexpr int kSink = 64;
+constexpr int kRecent = 256;
+constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the BF16 segments
+constexpr int kMaxGqa = 16;
+
+// Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
+constexpr int kKCodesOff = 0;
+constexpr int kVCodesOff = kPage * kHeadDim / 4;              // 2048
+constexpr int kKMetaOff = kVCodesOff + kHeadDim * kPage / 4;  // 4096
+__host__ __device__ inline int v_meta_off(int n_groups) { return kKMetaOff + kPage * n_groups * 4; }
+__host__ __device__ inline int block_bytes(int n_groups) { return v_meta_off(n_groups) + kPage * n_groups * 4; }
+
+// Work plan of one decode-attention call, and the carve-up of its workspace.
+struct Plan {
+  int batch = 0, hq = 0, hkv = 0, gqa = 0, n_groups = 0;
+  int max_pages = 0;         // history pages of the longest sequence
+  int pages_per_split = 1;   // history pages per INT2 work item
+  int num_splits = 0;        // work items per (sequence, KV head)
+  size_t off_qrot = 0;       // fp32 [B][Hq][128] rotated queries
+  size_t off_sigma = 0;      // fp32 [B][Hq][G] per-group sums of the rotated query
+  size_t off_int2_ml = 0;    // fp32 [B][Hq][S][2] (m, l) of INT2 partials (log2 domain)
+  size_t off_int2_acc = 0;   // fp32 [B][Hq][S][128] rotated-space accumulators
+  size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]
+  size_t off_bf16_acc = 0;   // fp32 [B][Hq][5][128]
+  size_t total = 0;
+};
+
+Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len);
+
+struct DemoteArgs {
+  uint8_t* pool;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+  int hkv;
+  int n_groups;
+  const float* u_k;
+  const float* u_v;
+  const float* clip_k;
+  const float* clip_v;
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t stride_b, stride_t, stride_h;
+  const int32_t* hist_start;
+  int batch;
+  int n_tokens;
+};
+
+struct AppendArgs {
+  uint8_t* pool;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+  int hkv;
+  int n_groups;
+  uint16_t* sink_k;
+  uint16_t* sink_v;
+  uint16_t* recent_k;
+  uint16_t* recent_v;
+  const float* u_k;
+  const float* u_v;
+  const float* clip_k;
+  const float* clip_v;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* seq_slot;
+  const int32_t* seq_lens;
+  int batch;
+};
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  const uint16_t* recent_k;
+  const uint16_t* recent_v;
+  const int32_t* seq_slot;
+  const int32_t* seq_lens;
+  const uint16_t* q;
+  const float* u_k;
+  const float* u_v;
+  float sm_scale;
+  float* out;
+  float* lse;
+  uint8_t* workspace;
+};
+
+hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream);
+
+}  // namespace oscar

@@ -1,0 +1,204 @@
+/*
+ * oscar.h -- C ABI of the OSCAR INT2-history decode library for AMD Instinct MI355X (gfx950).
+ *
+ * OSCAR keeps each sequence's KV cache in three segments: a BF16 attention sink of 64 tokens, a
+ * history stored as rotated INT2 codes, and a BF16 window of the 256 most recent tokens.  A
+ * history key (value) x is stored as the 2-bit group codes of x' = clip(x R_k) (x R_v), where
+ * R = U * Hadamard * bit-reversal is fixed per layer and KV head.  Decode attention runs over the
+ * BF16 segments and the INT2 segment separately and merges the two with an online softmax.
+ *
+ * Sources (web pages on OSCAR), cited by key:
+ *   [W1] "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化" (66bd.net article 13430),
+ *        section "OSCAR 的设计" -- the rotation R = U * Hadamard * bit-reversal per layer and
+ *        head, calibrated clipping, the three-segment pool (64 | INT2 | 256), demotion of the
+ *        oldest recent token by a fused rotate / clip / quantise / pack step, 4 two-bit codes per
+ *        byte, INT2 decode with scale / zero-point dequantisation and float accumulation, a
+ *        separate BF16 sink / recent pass, an online-softmax merge, paged-KV compatibility.
+ *   [P]  "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization",
+ *        ModelScope paper page of arXiv 2605.17757, "摘要" and "Abstract" -- an INT2 attention
+ *        kernel that stays compatible with paged KV caches and fused decode pipelines.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All buffers are caller-owned device memory (allocated by the caller, e.g. through PyTorch).
+ *    The library never allocates, frees or synchronises; it keeps no state between calls and is
+ *    safe to call from several host threads on different streams.
+ *  - Every compute call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *  - All argument checks that can be made on the host run before any HIP call; on failure the
+ *    call returns a negative status and touches no device memory.  A kernel launch failure
+ *    returns OSCAR_ERR_HIP.  oscar_last_error() gives a message for the calling thread.
+ *  - Values that live in device memory (page ids, lengths, history positions) are trusted; a
+ *    host copy can be checked with oscar_check_page_table().
+ *  - bf16 = IEEE binary32 truncated to its upper 16 bits (round-to-nearest-even when produced);
+ *    fp16 = IEEE binary16.  Multi-byte values are little endian.
+ *
+ * Pool layout (per layer)
+ * -----------------------
+ *  INT2 pool: num_pages pages; a page holds 64 consecutive history tokens of one sequence for
+ *  every KV head: pool bytes [page][kv_head][block], block = oscar_page_block_bytes().  A block
+ *  (d = 128 channels, g = group_size, G = d / g groups) is:
+ *      offset 0                 key codes    [64 tokens][d/4 bytes]   packed along channels:
+ *                               code of channel 4b+i in bits [2i, 2i+1] of byte b of the row
+ *      offset 64*d/4 (2048)     value codes  [d channels][64/4 bytes] packed along tokens:
+ *                               code of token-slot 4b+i in bits [2i, 2i+1] of byte b of the row
+ *      offset 4096              key meta     [64 tokens][G][fp16 scale, fp16 zero]
+ *      offset 4096 + 64*G*4     value meta   [64 tokens][G][fp16 scale, fp16 zero]
+ *  (4,608 bytes per block at g = 128, i.e. 72 bytes per token and KV head; 5,120 at g = 64.)
+ *  Codes are of the rotated, clipped vector in rotated-channel order; the value of element j of
+ *  token t in group m = j / g is  scale[t][m] * code[t][j] + zero[t][m]  (rotated space).
+ *  History index h of a sequence (h = position - 64) lives in page page_table[b][h / 64],
+ *  slot h % 64.  Prefix sharing is expressed by page-table aliasing only; the caller must not
+ *  demote into a page that other sequences alias (copy-on-write is the caller's job).
+ *
+ *  BF16 sink:   [max_seqs][num_kv_heads][64][d]  bf16, token at position p < 64 in row p.
+ *  BF16 recent: [max_seqs][num_kv_heads][256][d] bf16 ring, token at position p >= 64 in row
+ *               p % 256.  A sequence of length L caches positions 0 .. min(L,64)-1 in the sink,
+ *               history indices 0 .. L-321 in the pool (when L > 320) and positions
+ *               max(64, L-256) .. L-1 in the recent ring.
+ *
+ * Rotation inputs: U_k, U_v fp32 [num_kv_heads][d][d] row-major (U[h][i][j] is row i, column j);
+ * x' = x U H P / sqrt(d) for a row vector x, with H the Sylvester Hadamard matrix and P the
+ * bit-reversal permutation of the 7-bit channel index.  clip_k, clip_v fp32 [num_kv_heads]
+ * (finite, > 0, <= 65504).
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_ABI_VERSION 1u
+
+typedef int32_t oscar_status;
+
+#define OSCAR_OK              0
+#define OSCAR_ERR_NULL       -1   /* a required pointer is NULL */
+#define OSCAR_ERR_SHAPE      -2   /* unsupported or inconsistent sizes */
+#define OSCAR_ERR_ALIGN      -3   /* a pointer or stride is not suitably aligned */
+#define OSCAR_ERR_RANGE      -4   /* a value is out of range (page id, length, count) */
+#define OSCAR_ERR_WORKSPACE  -5   /* workspace missing or smaller than required */
+#define OSCAR_ERR_HIP        -6   /* the HIP runtime reported an error */
+
+/* Geometry of one layer's cache.  The GPU kernels support exactly: head_dim 128, group_size 128
+ * or 64, page_tokens 64, sink_tokens 64, recent_tokens 256 ([W1] OSCAR 的设计 fixes the 64 / 256
+ * segment sizes), num_q_heads a multiple of num_kv_heads with a quotient (GQA group) of 1, 2, 4 or 8. */
+typedef struct oscar_layout {
+  int32_t head_dim;           /* d */
+  int32_t group_size;         /* g: channels per (scale, zero) group */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv */
+  int32_t page_tokens;        /* history tokens per page */
+  int32_t sink_tokens;        /* BF16 sink tokens */
+  int32_t recent_tokens;      /* BF16 recent-window tokens */
+  int32_t num_pages;          /* physical pages in the INT2 pool */
+  int32_t max_seqs;           /* sequence slots in the BF16 sink / recent arrays */
+  int32_t max_pages_per_seq;  /* row stride of the page table */
+} oscar_layout;
+
+/* Library ABI version (OSCAR_ABI_VERSION of the build). */
+uint32_t oscar_abi_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* oscar_status_string(oscar_status status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* oscar_last_error(void);
+
+/* OSCAR_OK if the layout is supported by the kernels, else OSCAR_ERR_NULL / OSCAR_ERR_SHAPE. */
+oscar_status oscar_layout_check(const oscar_layout* layout);
+
+/* Size queries; each returns 0 for an unsupported layout. */
+size_t oscar_page_block_bytes(const oscar_layout* layout);   /* one (page, KV head) block */
+size_t oscar_page_bytes(const oscar_layout* layout);         /* one page, all KV heads */
+size_t oscar_pool_bytes(const oscar_layout* layout);         /* num_pages pages */
+size_t oscar_sink_bytes(const oscar_layout* layout);         /* keys or values: one array */
+size_t oscar_recent_bytes(const oscar_layout* layout);       /* keys or values: one array */
+
+/* Device workspace oscar_decode_attn needs for `batch` sequences of at most `max_seq_len`
+ * tokens (0 for invalid arguments). */
+size_t oscar_decode_workspace_bytes(const oscar_layout* layout, int32_t batch,
+                                    int32_t max_seq_len);
+
+/* Host-side check of a host copy of a page table and sequence lengths: every page that a
+ * sequence of length seq_lens[b] + extra_tokens uses must be in [0, num_pages), fit in
+ * max_pages_per_seq, and no two sequences may share a page beyond the pages they share from
+ * position 0 (shared pages must be a common prefix of both rows).  Touches no device memory. */
+oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* host_page_table,
+                                    const int32_t* host_seq_lens, int32_t batch,
+                                    int32_t extra_tokens);
+
+/* Demotion into the INT2 history ([W1] OSCAR 的设计: the oldest recent tokens are rotated,
+ * clipped, quantised and packed into the history; four 2-bit codes per byte).
+ *
+ * For every sequence b < batch, token i < n_tokens and KV head h, the key vector
+ *   k = k_src[b * stride_b + i * stride_t + h * stride_h + (0..d-1)]  (bf16 elements)
+ * (and likewise the value vector from v_src) is encoded and written to history index
+ * hist_start[b] + i of sequence b:
+ *   1. x' = x U H P / sqrt(d) computed in fp64, then rounded to fp32;
+ *   2. x'' = min(max(x', -clip), clip)  (fp32);
+ *   3. per group m of g rotated channels: mn = min, mx = max; scale = fp16((mx - mn) / 3),
+ *      zero = fp16(mn) (fp32 arithmetic, round-to-nearest-even);
+ *   4. code_j = min(max(rint((x''_j - zero) / scale), 0), 3) in fp32 with ties to even, or 0 for
+ *      every j of a group whose fp16 scale is 0;
+ *   5. codes and meta are stored in the block layout described above.
+ * pool: oscar_pool_bytes(layout) bytes, 16-byte aligned.  page_table: int32
+ * [batch][max_pages_per_seq].  U_k / U_v / clip_k / clip_v as described above.  hist_start:
+ * int32 [batch].  Strides are in bf16 elements, >= 0; k_src / v_src 2-byte aligned.  The call
+ * must not run concurrently with a decode over the same pages (stream order suffices).
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE (negative batch or n_tokens) / HIP. */
+oscar_status oscar_demote(const oscar_layout* layout, void* pool, const int32_t* page_table,
+                          const float* u_k, const float* u_v, const float* clip_k,
+                          const float* clip_v, const void* k_src, const void* v_src,
+                          int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                          const int32_t* hist_start, int32_t batch, int32_t n_tokens,
+                          void* stream);
+
+/* One decode-step write ([W1] OSCAR 的设计: a new token first enters the recent window; the
+ * oldest recent token is then demoted into the history).
+ *
+ * For each b < batch with P = seq_lens[b] (the length before this token, i.e. its position) and
+ * s = seq_slot[b]: if P < 64 the new key / value (k_new / v_new, bf16 [batch][Hkv][d]) go to
+ * sink row P of slot s.  Otherwise they go to recent ring row P % 256 of slot s, and when
+ * P >= 320 the token held in that row (position P - 256) is first demoted (as oscar_demote) to
+ * history index P - 320.  The caller advances seq_lens afterwards.  sink / recent arrays as in
+ * the layout above; seq_slot, seq_lens int32 [batch] device arrays.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / HIP. */
+oscar_status oscar_append(const oscar_layout* layout, void* pool, const int32_t* page_table,
+                          void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                          const float* u_k, const float* u_v, const float* clip_k,
+                          const float* clip_v, const void* k_new, const void* v_new,
+                          const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
+                          void* stream);
+
+/* Decode attention over the three-segment cache ([W1] OSCAR 的设计: INT2 unpack and
+ * scale / zero-point dequantisation with float accumulation, a BF16 sink / recent pass, an
+ * online-softmax merge; [P] Abstract: an INT2 attention kernel over a paged KV cache).
+ *
+ * For each sequence b and query head i (KV head i / (Hq / Hkv)), with L = seq_lens[b]:
+ *   out[b][i] = sum_t softmax_t(sm_scale * q[b][i] . k_t) v_t   over the L cached tokens, where
+ * history keys / values are k_t = (scale * code + zero) R^T (dequantised in rotated space and
+ * mapped back).  The kernels work in the rotated frame: q' = q R_k scores the history directly,
+ * the history's value accumulator is mapped back by R_v^T once per head after the split-KV merge.
+ * q: bf16 [batch][Hq][d].  out: fp32 [batch][Hq][d].  lse: optional fp32 [batch][Hq] natural-log
+ * sum of exp(sm_scale * scores) (NULL to skip).  sm_scale <= 0 selects 1/sqrt(d).
+ * seq_lens[b] must be in [1, max_seq_len]; max_seq_len is a host-side bound used for work
+ * planning.  workspace: at least oscar_decode_workspace_bytes(layout, batch, max_seq_len) bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
+oscar_status oscar_decode_attn(const oscar_layout* layout, const void* pool,
+                               const int32_t* page_table, const void* sink_k, const void* sink_v,
+                               const void* recent_k, const void* recent_v,
+                               const int32_t* seq_slot, const int32_t* seq_lens, const void* q,
+                               const float* u_k, const float* u_v, float sm_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               int32_t batch, int32_t max_seq_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

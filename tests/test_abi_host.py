@@ -1,0 +1,177 @@
+"""Host-side tests of the C ABI: the library loads, exports every function include/oscar.h
+declares, answers size queries, and rejects bad arguments before any HIP call (no GPU needed:
+every call here fails validation or is a pure host function)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import bit_rotated_kv_decode_amd as ok
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(oscar_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 14
+    lib = ok.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", ok.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\b(oscar_\w+)\b", dyn))
+    assert set(names) <= exported
+    # the binding declares a signature for each one
+    assert set(names) == set(ok._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = ok.lib()
+    assert lib.oscar_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert lib.oscar_status_string(s)
+
+
+def _lay(**kw):
+    base = dict(head_dim=128, group_size=128, num_q_heads=32, num_kv_heads=8, page_tokens=64,
+                sink_tokens=64, recent_tokens=256, num_pages=10, max_seqs=2, max_pages_per_seq=5)
+    base.update(kw)
+    return ok.Layout(*[base[n] for n, _ in ok.Layout._fields_])
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=64), dict(group_size=32), dict(num_q_heads=30),
+                                 dict(num_q_heads=128, num_kv_heads=8), dict(page_tokens=32),
+                                 dict(sink_tokens=0), dict(recent_tokens=128), dict(num_pages=-1)])
+def test_layout_rejects_unsupported(bad):
+    lay = _lay(**bad)
+    assert ok.lib().oscar_layout_check(ctypes.byref(lay)) == -2
+    assert ok.page_block_bytes(lay) == 0 and ok.pool_bytes(lay) == 0
+    assert ok.lib().oscar_last_error()
+
+
+def test_layout_null():
+    assert ok.lib().oscar_layout_check(None) == -1
+
+
+def test_size_queries():
+    lay = _lay()
+    assert ok.page_block_bytes(lay) == 4608
+    assert ok.page_bytes(lay) == 8 * 4608
+    assert ok.pool_bytes(lay) == 10 * 8 * 4608
+    assert ok.sink_bytes(lay) == 2 * 8 * 64 * 128 * 2
+    assert ok.recent_bytes(lay) == 2 * 8 * 256 * 128 * 2
+    lay64 = _lay(group_size=64)
+    assert ok.page_block_bytes(lay64) == 5120
+    w1 = ok.decode_workspace_bytes(lay, 1, 1024)
+    w2 = ok.decode_workspace_bytes(lay, 4, 100000)
+    assert 0 < w1 < w2 and w1 % 256 == 0
+    assert ok.decode_workspace_bytes(lay, -1, 10) == 0
+
+
+def _call_demote(lay, **over):
+    a = dict(pool=4096, page_table=4096, u_k=4096, u_v=4096, clip_k=4096, clip_v=4096,
+             k_src=4096, v_src=4096, sb=0, st=0, sh=0, hist=4096, batch=1, n=1)
+    a.update(over)
+    return ok.lib().oscar_demote(ctypes.byref(lay), a["pool"], a["page_table"], a["u_k"],
+                                 a["u_v"], a["clip_k"], a["clip_v"], a["k_src"], a["v_src"],
+                                 a["sb"], a["st"], a["sh"], a["hist"], a["batch"], a["n"], None)
+
+
+def test_demote_validation_happens_before_launch():
+    lay = _lay()
+    assert _call_demote(lay, pool=None) == -1
+    assert _call_demote(lay, hist=None) == -1
+    assert _call_demote(lay, pool=4097) == -3
+    assert _call_demote(lay, k_src=4097) == -3
+    assert _call_demote(lay, batch=-1) == -4
+    assert _call_demote(lay, st=-2) == -4
+    assert _call_demote(_lay(group_size=16)) == -2
+    # nothing to do: OK without touching any pointer
+    assert _call_demote(lay, pool=None, n=0) == 0
+    assert _call_demote(lay, pool=None, batch=0) == 0
+
+
+def _call_decode(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, slot=4096, lens=4096,
+             q=4096, uk=4096, uv=4096, out=4096, lse=None, ws=4096, wsb=1 << 30, batch=1,
+             maxlen=600)
+    a.update(over)
+    return ok.lib().oscar_decode_attn(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["slot"],
+        a["lens"], a["q"], a["uk"], a["uv"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"],
+        a["batch"], a["maxlen"], None)
+
+
+def test_decode_validation_happens_before_launch():
+    lay = _lay()
+    assert _call_decode(lay, q=None) == -1
+    assert _call_decode(lay, out=None) == -1
+    assert _call_decode(lay, ws=None) == -5
+    assert _call_decode(lay, wsb=16) == -5
+    assert _call_decode(lay, ws=4096 + 64) == -3
+    assert _call_decode(lay, sk=4096 + 8) == -3
+    assert _call_decode(lay, maxlen=0) == -4
+    # 100000 tokens need 1558 pages > max_pages_per_seq 5
+    assert _call_decode(lay, maxlen=100000) == -4
+    assert _call_decode(lay, batch=-3) == -4
+    assert _call_decode(lay, batch=0, q=None) == 0
+    assert _call_decode(lay, wsb=16) == -5
+    assert "workspace" in ok.lib().oscar_last_error().decode()
+
+
+def test_append_validation_happens_before_launch():
+    lay = _lay()
+    f = ok.lib().oscar_append
+    args = [4096] * 14
+    assert f(ctypes.byref(lay), *([None] + args[1:]), 1, None) == -1
+    assert f(ctypes.byref(lay), *([4096 + 4] + args[1:]), 1, None) == -3
+    assert f(ctypes.byref(_lay(max_seqs=0)), *args, 1, None) == -2
+    assert f(ctypes.byref(lay), *args, -1, None) == -4
+
+
+def test_check_page_table():
+    lay = _lay(num_pages=8, max_pages_per_seq=4)
+    # 320 + 3*64 tokens -> 3 pages each
+    lens = [320 + 3 * 64, 320 + 2 * 64 + 1]
+    good = np.array([[5, 1, 7, 0], [2, 3, 6, 0]], np.int32)
+    ok.check_page_table(lay, good, lens)
+    with pytest.raises(ok.OscarError):
+        ok.check_page_table(lay, np.array([[5, 1, 8, 0], [2, 3, 6, 0]], np.int32), lens)
+    with pytest.raises(ok.OscarError):          # page 1 used twice by sequence 0
+        ok.check_page_table(lay, np.array([[5, 1, 1, 0], [2, 3, 6, 0]], np.int32), lens)
+    with pytest.raises(ok.OscarError):          # shared page at different logical positions
+        ok.check_page_table(lay, np.array([[5, 1, 7, 0], [1, 3, 6, 0]], np.int32), lens)
+    # a shared prefix of two pages is fine, a shared page after a private one is not
+    ok.check_page_table(lay, np.array([[5, 1, 7, 0], [5, 1, 6, 0]], np.int32), lens)
+    with pytest.raises(ok.OscarError):
+        ok.check_page_table(lay, np.array([[5, 1, 7, 0], [2, 1, 6, 0]], np.int32), lens)
+    with pytest.raises(ok.OscarError):          # 5 pages needed > 4
+        ok.check_page_table(lay, good, [320 + 4 * 64 + 1, 10])
+    ok.check_page_table(lay, good, [320 + 3 * 64, 10], extra_tokens=64)   # 4 pages fit
+    with pytest.raises(ok.OscarError):
+        ok.check_page_table(lay, good, [320 + 3 * 64, 10], extra_tokens=65)
+    with pytest.raises(ok.OscarError):
+        ok.check_page_table(lay, good, [-1, 10])
+
+
+def test_workload_page_tables_pass_the_checker():
+    import workloads
+    wl = workloads.scaled(workloads.get("qwen3_8b_b64_prefix"), batch=8)
+    lens = workloads.context_lengths(wl)
+    table, num_pages = workloads.page_tables(wl, lens, spare_tokens=10)
+    lay = _lay(num_pages=num_pages, max_pages_per_seq=table.shape[1], max_seqs=8)
+    ok.check_page_table(lay, table, lens, extra_tokens=10)
+    # every sequence shares the first pages of the prefix
+    shared = (32768 - 64) // 64
+    n0 = min(shared, workloads.history_pages(min(lens)))
+    assert (table[:, :n0] == table[0, :n0]).all()

@@ -1,0 +1,172 @@
+"""GPU parity of liboscar against the CPU oracle, called through the C ABI.
+
+Demotion: pool bytes bit-exact under the acceptance rule of oscar_cases.  Attention: the GPU reads
+pool bytes written by the oracle (so the attention comparison does not depend on demotion) and
+must match the oracle's softmax attention within 2e-3 max row error; an end-to-end case uses the
+GPU's own demotion."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_decode_amd as ok
+import oracle
+import workloads
+from oscar_cases import ATTN_TOL, Case, attention_error, compare_pool_blocks
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny(**kw):
+    return workloads.scaled(workloads.get("tiny_gqa4_1k"), **kw)
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def test_demote_tiny_two_calls_bit_exact():
+    # 704 history tokens written by two calls: 448 tokens, then 256 tokens
+    case = Case(_tiny())
+    _note(f"demote tiny: lengths={case.lengths} pages={case.num_pages}")
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g, pool_from_oracle=oracle.new_pool(case.num_pages, 1, case.geom))
+    k = case.k[0].to("cuda")[64:768].unsqueeze(0)
+    v = case.v[0].to("cuda")[64:768].unsqueeze(0)
+    ok.demote(case.layout, cache.pool, g["table"], g["u_k"], g["u_v"], g["clip_k"], g["clip_v"],
+              k[:, :448], v[:, :448], torch.zeros(1, dtype=torch.int32, device="cuda"))
+    ok.demote(case.layout, cache.pool, g["table"], g["u_k"], g["u_v"], g["clip_k"], g["clip_v"],
+              k[:, 448:], v[:, 448:], torch.full((1,), 448, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = case.oracle_pool()
+    flips = compare_pool_blocks(cache.pool.cpu().numpy(), ref, case)
+    _note(f"code flips: {flips}")
+
+
+@pytest.mark.parametrize("group,hq,hkv", [(128, 8, 2), (64, 8, 1), (64, 16, 2)])
+def test_demote_ragged_unaligned(group, hq, hkv):
+    wl = _tiny(group_size=group, num_q_heads=hq, num_kv_heads=hkv)
+    lengths = [321, 400, 1000, 385 + 64 * 5 + 3]
+    case = Case(wl, lengths)
+    _note(f"demote ragged g={group} hq={hq} hkv={hkv} lengths={lengths}")
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g)                           # GPU demotion, one call per sequence
+    torch.cuda.synchronize()
+    compare_pool_blocks(cache.pool.cpu().numpy(), case.oracle_pool(), case)
+    # unaligned starts: rewrite each sequence's history in pieces of 7, 13 and the rest
+    cache2 = case.gpu_cache(g, pool_from_oracle=oracle.new_pool(case.num_pages, hkv, case.geom))
+    for b, L in enumerate(lengths):
+        n = L - 320
+        k = case.k[b].to("cuda")[64:64 + n].unsqueeze(0)
+        v = case.v[b].to("cuda")[64:64 + n].unsqueeze(0)
+        for lo, hi in ((0, 7), (7, 20), (20, n)):
+            ok.demote(case.layout, cache2.pool, g["table"][b:b + 1], g["u_k"], g["u_v"],
+                      g["clip_k"], g["clip_v"], k[:, lo:hi], v[:, lo:hi],
+                      torch.full((1,), lo, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(cache2.pool, cache.pool)
+
+
+ATTN_CASES = {
+    "tiny_1k": dict(wl=dict(), lengths=None),
+    "edges_g4": dict(wl=dict(num_q_heads=8, num_kv_heads=2),
+                     lengths=[1, 63, 64, 65, 300, 320, 321, 385, 1000, 1024 + 64 * 3 + 7]),
+    "gqa1": dict(wl=dict(num_q_heads=2, num_kv_heads=2), lengths=[700, 2000]),
+    "gqa2": dict(wl=dict(num_q_heads=4, num_kv_heads=2), lengths=[2500, 333]),
+    "gqa8_g64": dict(wl=dict(num_q_heads=16, num_kv_heads=2, group_size=64),
+                     lengths=[3000, 1500, 321]),
+    "g64_gqa4": dict(wl=dict(num_q_heads=8, num_kv_heads=2, group_size=64), lengths=[4100]),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_attention_on_oracle_pool(name):
+    spec = ATTN_CASES[name]
+    case = Case(_tiny(**spec["wl"]), spec["lengths"])
+    _note(f"attention {name}: lengths={case.lengths}")
+    pool = case.oracle_pool()
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g, pool_from_oracle=pool)
+    out, lse = case.gpu_attention(g, cache)
+    ref, ref_lse = case.oracle_attention(pool)
+    err = attention_error(out, ref)
+    _note(f"max row error {err:.3e}")
+    assert err <= ATTN_TOL
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-3
+
+
+def test_attention_end_to_end_tiny():
+    case = Case(_tiny())
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g)                           # GPU demotion
+    out, _ = case.gpu_attention(g, cache)
+    ref, _ = case.oracle_attention(case.oracle_pool())  # oracle demotion
+    err = attention_error(out, ref)
+    _note(f"end-to-end max row error {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def test_page_shuffle_and_split_invariance():
+    wl = _tiny(num_q_heads=8, num_kv_heads=2)
+    case = Case(wl, [5000, 2222], spare=150000)   # room for a larger planning bound
+    pool = case.oracle_pool()
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g, pool_from_oracle=pool)
+    out1, _ = case.gpu_attention(g, cache)
+    # a different physical placement of the same pages
+    perm = np.random.default_rng(0).permutation(case.num_pages)
+    pool2 = np.zeros_like(pool)
+    pool2[perm] = pool
+    table2 = case.table.copy()
+    for b, L in enumerate(case.lengths):
+        n = workloads.history_pages(L)
+        table2[b, :n] = perm[case.table[b, :n]]
+    g2 = dict(g)
+    g2["table"] = torch.from_numpy(table2).to("cuda")
+    cache2 = case.gpu_cache(g2, pool_from_oracle=pool2)
+    out2, _ = case.gpu_attention(g2, cache2)
+    assert np.array_equal(out1, out2)
+    # a larger max_seq_len changes the split plan; the result changes only by fp32 rounding
+    out3, _ = case.gpu_attention(g, cache, max_seq_len=150000)
+    assert attention_error(out3, out1) < 1e-5
+
+
+def test_append_steps_match_oracle():
+    # decode-step writes from an empty cache across the sink / recent / history boundaries
+    wl = _tiny(num_q_heads=4, num_kv_heads=2)
+    steps = 400
+    case = Case(wl, [steps + 5, steps + 40], spare=64)
+    g = case.gpu_inputs()
+    lay = case.layout
+    cache = ok.Cache.allocate(lay)
+    start = [5, 0]            # sequence 1 starts empty, sequence 0 five tokens behind
+    hk = np.zeros((2, 2, 64, 128), np.float32)
+    hv = np.zeros_like(hk)
+    rk = np.zeros((2, 2, 256, 128), np.float32)
+    rv = np.zeros_like(rk)
+    pool = oracle.new_pool(case.num_pages, 2, case.geom)
+    lens = [0, 0]
+    for s in range(steps + 40):
+        active = [b for b in range(2) if s >= start[b] and lens[b] < case.lengths[b]]
+        if not active:
+            continue
+        idx = torch.tensor(active)
+        k_new = torch.stack([case.k[b][lens[b]] for b in active])
+        v_new = torch.stack([case.v[b][lens[b]] for b in active])
+        tab = g["table"][idx.to("cuda")].contiguous()
+        ok.append(lay, cache.pool, tab, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v,
+                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new.to("cuda"),
+                  v_new.to("cuda"), torch.tensor(active, dtype=torch.int32, device="cuda"),
+                  torch.tensor([lens[b] for b in active], dtype=torch.int32, device="cuda"))
+        oracle.append(pool, case.table[active], hk, hv, rk, rv, case.u_k.numpy(),
+                      case.u_v.numpy(), case.clip_k, case.clip_v, k_new.float().numpy(),
+                      v_new.float().numpy(), active, [lens[b] for b in active], case.geom)
+        for b in active:
+            lens[b] += 1
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.sink_k.float().cpu().numpy(), hk)
+    assert np.array_equal(cache.recent_v.float().cpu().numpy(), rv)
+    assert np.array_equal(cache.recent_k.float().cpu().numpy(), rk)
+    case.lengths = lens
+    compare_pool_blocks(cache.pool.cpu().numpy(), pool, case)
