@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the OSCAR INT2-history path on one MI355X.
+
+Workload: Qwen3-8B-shaped batch-1 decode at 100,000 tokens of context -- 36 layers, 32 query
+heads and 8 KV heads of dimension 128, 64 BF16 sink + 99,680 INT2 history + 256 BF16 recent
+tokens per layer, history in 64-token pages placed through a seeded shuffled page table, keys
+and values N(0,1) bf16 with one outlier channel (x16) per layer, head and tensor, U from the QR
+of a seeded Gaussian, clip 4.0, group 128.  Inputs are synthetic (no model weights).
+
+One step = for each of the 36 layers: oscar_append (write the new token into the BF16 recent
+window and demote the displaced token into the INT2 history) and oscar_decode_attn (query
+rotation, INT2 split-KV pass, BF16 sink/recent pass, merge and un-rotation).  The 36-layer step
+is captured once in a HIP graph and replayed; 36 distinct layer pools (2.1 GB) are cycled, so
+the 256 MB Infinity Cache cannot hold the timed data.
+
+Prints one JSON line: value = effective HBM GB/s of the whole decode step (algorithmic bytes of
+all 36 layers / step time); decode_steps_per_s; roofline of the INT2 decode kernel timed with
+events on its stream inside the timed region; cpu_baseline = the CPU oracle timed on one KV head
+of one layer and scaled.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import bit_rotated_kv_decode_amd as ok  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s peak) + decode steps/s, 100k ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_100k")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def bytes_per_token_head(group: int) -> int:
+    return 2 * 128 // 4 + 2 * (128 // group) * 4
+
+
+class Layer:
+    """One layer's resident cache and per-step inputs."""
+
+    def __init__(self, wl, layer, length, spare):
+        dev = "cuda"
+        self.table_np, self.num_pages = workloads.page_tables(wl, [length], layer,
+                                                              spare_tokens=spare)
+        self.lay = ok.make_layout(wl.num_q_heads, wl.num_kv_heads, self.num_pages, 1,
+                                  self.table_np.shape[1], wl.group_size)
+        self.cache = ok.Cache.allocate(self.lay, zero=False)
+        self.table = torch.from_numpy(self.table_np).to(dev)
+        uk, uv = workloads.rotation_bases(wl, layer)
+        self.u_k, self.u_v = uk.to(dev), uv.to(dev)
+        self.clip_k = torch.full((wl.num_kv_heads,), wl.clip, dtype=torch.float32, device=dev)
+        self.clip_v = self.clip_k.clone()
+        # history: positions 64 .. length-257 demoted in chunks; sink and recent copied
+        n_hist = length - 320
+        chunk = 16384
+        zero = torch.zeros(1, dtype=torch.int32, device=dev)
+        for lo in range(0, n_hist, chunk):
+            n = min(chunk, n_hist - lo)
+            k, v = workloads.kv_tokens(wl, layer, 0, 64 + lo, n, dev)
+            ok.demote(self.lay, self.cache.pool, self.table, self.u_k, self.u_v, self.clip_k,
+                      self.clip_v, k.unsqueeze(0), v.unsqueeze(0), zero + lo)
+        k, v = workloads.kv_tokens(wl, layer, 0, 0, 64, dev)
+        self.cache.sink_k[0] = k.transpose(0, 1)
+        self.cache.sink_v[0] = v.transpose(0, 1)
+        pos = torch.arange(length - 256, length, device=dev)
+        k, v = workloads.kv_tokens(wl, layer, 0, length - 256, 256, dev)
+        self.cache.recent_k[0][:, pos % 256] = k.transpose(0, 1)
+        self.cache.recent_v[0][:, pos % 256] = v.transpose(0, 1)
+        # per-step inputs (the same new token and query every step)
+        k, v = workloads.kv_tokens(wl, layer, 0, length, 1, dev)
+        self.k_new, self.v_new = k.contiguous(), v.contiguous()
+        self.q = workloads.queries(wl, layer, 0, dev).contiguous()
+        self.out = torch.empty((1, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (each GPU box here "
+              "has one GPU, and this path needs no collectives).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ok.lib()
+    wl = workloads.get(args.workload)
+    n_layers = args.layers or wl.num_layers
+    L0 = wl.context
+    total_steps = args.warmup + args.steps + 2       # +2: graph capture warm-up and capture
+    dev = "cuda"
+
+    t0 = time.time()
+    layers = [Layer(wl, i, L0, total_steps + 8) for i in range(n_layers)]
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
+
+    pos = torch.full((1,), L0, dtype=torch.int32, device=dev)      # position of the new token
+    lens = torch.full((1,), L0 + 1, dtype=torch.int32, device=dev)  # length seen by attention
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    max_len = L0 + total_steps + 4
+    ws = torch.empty(ok.decode_workspace_bytes(layers[0].lay, 1, max_len), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        for Lr in layers:
+            c = Lr.cache
+            ok.append(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                      Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos)
+            ok.decode_attn(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                           slots, lens, Lr.q, Lr.u_k, Lr.u_v, Lr.out, ws, max_len)
+        pos.add_(1)
+        lens.add_(1)
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()                                    # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    else:
+        step()
+        step()
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
+    # ---- timed region 1: whole decode steps
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    steps_before = int(pos.item()) - L0
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    # ---- timed region 2: the INT2 decode kernel alone, every layer, args.steps rounds.  Each
+    # launch is bracketed by events on its own stream; a short GPU spin before the first event
+    # keeps the GPU behind the host, so the events time the kernel and not host launch latency.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in layers]
+    int2_ms = []
+    for _ in range(args.steps):
+        for i, Lr in enumerate(layers):
+            c = Lr.cache
+            common = (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                      slots, lens, Lr.q, Lr.u_k, Lr.u_v, Lr.out, ws, max_len)
+            torch.cuda._sleep(20000)
+            ok.decode_attn(*common, stages=ok.STAGE_QUERY)
+            ev[i][0].record()
+            ok.decode_attn(*common, stages=ok.STAGE_INT2)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        int2_ms += [a.elapsed_time(b) for a, b in ev]
+
+    # algorithmic bytes of the timed steps
+    hkv, hq = wl.num_kv_heads, wl.num_q_heads
+    bpt = bytes_per_token_head(wl.group_size)
+    bf16_seg = hkv * 320 * 128 * 2 * 2
+    att_bytes = 0
+    int2_bytes_last = 0
+    L_int2 = int(lens.item())                         # length seen by the INT2-only region
+    for s_ in range(args.steps):
+        L = L0 + steps_before + s_ + 1                  # length seen by attention
+        n_hist = L - 320
+        n_pages = math.ceil(n_hist / 64)
+        att = hkv * n_hist * bpt + n_pages * 4 + bf16_seg + hq * 128 * 2 + hq * 128 * 4
+        append = hkv * 128 * 2 * 2 * 3 + hkv * bpt
+        att_bytes += n_layers * (att + append)
+    n_hist = L_int2 - 320
+    int2_bytes_last = hkv * n_hist * bpt + math.ceil(n_hist / 64) * 4 + hq * 128 * 4
+    step_bytes = att_bytes / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    int2_ms_avg = float(np.mean(int2_ms))
+    achieved = int2_bytes_last / (int2_ms_avg * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: Qwen3-8B-shaped decode, batch 1, context {L0}, "
+                               f"{n_layers} layers, Hq {hq}, Hkv {hkv}, head_dim 128, "
+                               f"group {wl.group_size}, 64-token shuffled pages",
+                   "batch": 1, "context": L0, "layers": n_layers,
+                   "launch": "hip-graph" if graph is not None else "eager"},
+        "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_bytes": int(step_bytes),
+        "roofline": {"kernel": "int2_kernel (INT2 split-KV decode)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(int2_bytes_last),
+                     "avg_launch_us": round(int2_ms_avg * 1e3, 3),
+                     "timing": f"HIP events on the launch stream around each INT2 launch, "
+                               f"{args.steps} rounds x {n_layers} layer pools, GPU-paced"},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers[0], L0)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, layer0, length):
+    """Time the CPU oracle on one KV head (4 query heads) of one layer at full context, plus the
+    demotion of one token, and scale to the whole 36-layer step."""
+    import oracle
+
+    def bf16_np(t):
+        return t.float().cpu().numpy()
+
+    kv = 0
+    geom = oracle.Geometry(group=wl.group_size)
+    n_hist = length - 320
+    table = layer0.table_np
+    uk = layer0.u_k.cpu().numpy()
+    uv = layer0.u_v.cpu().numpy()
+    k, v = workloads.kv_tokens(wl, 0, 0, 0, length, "cuda")
+    k = bf16_np(k[:, kv:kv + 1])
+    v = bf16_np(v[:, kv:kv + 1])
+    pool = oracle.new_pool(layer0.num_pages, wl.num_kv_heads, geom)
+    kq = oracle.encode(k[64:64 + n_hist, 0], uk[kv], wl.clip, geom.group)[:3]
+    vq = oracle.encode(v[64:64 + n_hist, 0], uv[kv], wl.clip, geom.group)[:3]
+    oracle.store_history(pool, table[0], np.arange(n_hist), kv, kq, vq, geom)
+    sk = np.zeros((1, wl.num_kv_heads, 64, 128), np.float32)
+    sv = np.zeros_like(sk)
+    rk = np.zeros((1, wl.num_kv_heads, 256, 128), np.float32)
+    rv = np.zeros_like(rk)
+    sk[0, kv] = k[:64, 0]
+    sv[0, kv] = v[:64, 0]
+    p = np.arange(length - 256, length)
+    rk[0, kv][p % 256] = k[p, 0]
+    rv[0, kv][p % 256] = v[p, 0]
+    q = bf16_np(layer0.q)
+    gq = wl.gqa
+    heads = [(0, kv * gq + i) for i in range(gq)]
+    clip = np.full(wl.num_kv_heads, wl.clip, np.float32)
+    times = []
+    for _ in range(2):
+        t = time.perf_counter()
+        oracle.demote(pool, table, uk, uv, clip, clip, k[None, 64:65], v[None, 64:65], [0], geom)
+        oracle.decode_attention(pool, table, sk, sv, rk, rv, [0], [length], q, uk, uv, geom,
+                                heads=heads)
+        times.append(time.perf_counter() - t)
+    per_head = min(times)
+    step_s = per_head * wl.num_kv_heads * wl.num_layers
+    head_bytes = n_hist * bytes_per_token_head(wl.group_size) + 320 * 128 * 2 * 2
+    step_bytes = head_bytes * wl.num_kv_heads * wl.num_layers
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "decode_steps_per_s": round(1.0 / step_s, 6),
+            "sample": f"numpy fp64 oracle, 1 KV head ({gq} query heads) of 1 layer at context "
+                      f"{length}: demotion of 1 token + decode attention over the 3-segment "
+                      f"cache ({per_head:.2f}s, best of 2), scaled x{wl.num_kv_heads} heads "
+                      f"x{wl.num_layers} layers"}
+
+
+if __name__ == "__main__":
+    main()

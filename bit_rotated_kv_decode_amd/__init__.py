@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
     "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "check_page_table",
-    "demote", "append", "decode_attn", "Cache", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
+    "demote", "append", "decode_attn", "Cache", "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16",
+    "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
     "RECENT_TOKENS",
 ]
 
@@ -76,7 +77,12 @@ _SIGNATURES = {
     "oscar_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _i32, _i32,
                                  _vp]),
+    "oscar_decode_attn_stages": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
+                                        _i32, _i32, ctypes.c_uint32, _vp]),
 }
+
+STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -209,14 +215,14 @@ def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_
 def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
                 seq_lens, q: torch.Tensor, u_k, u_v, out: torch.Tensor, workspace: torch.Tensor,
                 max_seq_len: int, lse: Optional[torch.Tensor] = None,
-                sm_scale: float = 0.0) -> None:
+                sm_scale: float = 0.0, stages: int = STAGE_ALL) -> None:
     """Decode attention of q (bf16 [B, Hq, 128]) into out (fp32 [B, Hq, 128]) and optionally
-    lse (fp32 [B, Hq]) (oscar_decode_attn).  workspace: uint8 tensor of at least
-    decode_workspace_bytes(lay, B, max_seq_len) bytes."""
+    lse (fp32 [B, Hq]) (oscar_decode_attn_stages; ``stages`` selects a subset of the stages).
+    workspace: uint8 tensor of at least decode_workspace_bytes(lay, B, max_seq_len) bytes."""
     bsz = seq_lens.numel()
     if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
         raise TypeError("q / out must be [batch, Hq, 128]")
-    _check(lib().oscar_decode_attn(
+    _check(lib().oscar_decode_attn_stages(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
         _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
@@ -226,7 +232,7 @@ def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         _contig(out, "out", torch.float32),
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
-        _stream()), "decode_attn")
+        int(stages), _stream()), "decode_attn")
 
 
 @dataclasses.dataclass

@@ -392,35 +392,40 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
 }
 
 template <int G>
-hipError_t launch_g(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
+hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStream_t stream) {
   const float scale_log2 = a.sm_scale * kLog2e;
-  if (p.max_pages > 0) {
+  if ((stages & OSCAR_STAGE_INT2) && p.max_pages > 0) {
     dim3 grid(p.num_splits, p.hkv, p.batch);
     if (p.n_groups == 1)
       hipLaunchKernelGGL((int2_kernel<G, 1>), grid, dim3(256), 0, stream, a, p, scale_log2);
     else
       hipLaunchKernelGGL((int2_kernel<G, 2>), grid, dim3(256), 0, stream, a, p, scale_log2);
   }
-  hipLaunchKernelGGL((bf16_kernel<G>), dim3(kBf16Chunks, p.hkv, p.batch), dim3(64), 0, stream, a,
-                     p, scale_log2);
-  hipLaunchKernelGGL((merge_kernel<G>), dim3(p.hkv, p.batch), dim3(256), 0, stream, a, p);
+  if (stages & OSCAR_STAGE_BF16)
+    hipLaunchKernelGGL((bf16_kernel<G>), dim3(kBf16Chunks, p.hkv, p.batch), dim3(64), 0, stream,
+                       a, p, scale_log2);
+  if (stages & OSCAR_STAGE_MERGE)
+    hipLaunchKernelGGL((merge_kernel<G>), dim3(p.hkv, p.batch), dim3(256), 0, stream, a, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, const Plan& p, uint32_t stages,
+                         hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
-  float* qrot = reinterpret_cast<float*>(a.workspace + p.off_qrot);
-  float* sigma = reinterpret_cast<float*>(a.workspace + p.off_sigma);
-  const int rows = p.batch * p.hq;
-  hipLaunchKernelGGL(qrot_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a.q, a.u_k,
-                     p.batch, p.hq, p.gqa, p.n_groups, qrot, sigma);
+  if (stages & OSCAR_STAGE_QUERY) {
+    float* qrot = reinterpret_cast<float*>(a.workspace + p.off_qrot);
+    float* sigma = reinterpret_cast<float*>(a.workspace + p.off_sigma);
+    const int rows = p.batch * p.hq;
+    hipLaunchKernelGGL(qrot_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a.q, a.u_k,
+                       p.batch, p.hq, p.gqa, p.n_groups, qrot, sigma);
+  }
   switch (p.gqa) {
-    case 1: return launch_g<1>(a, p, stream);
-    case 2: return launch_g<2>(a, p, stream);
-    case 4: return launch_g<4>(a, p, stream);
-    case 8: return launch_g<8>(a, p, stream);
+    case 1: return launch_g<1>(a, p, stages, stream);
+    case 2: return launch_g<2>(a, p, stages, stream);
+    case 4: return launch_g<4>(a, p, stages, stream);
+    case 8: return launch_g<8>(a, p, stages, stream);
     default: return hipErrorInvalidValue;
   }
 }

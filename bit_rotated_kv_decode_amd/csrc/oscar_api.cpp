@@ -285,7 +285,22 @@ oscar_status oscar_decode_attn(const oscar_layout* l, const void* pool, const in
                                const float* u_v, float sm_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, int32_t batch,
                                int32_t max_seq_len, void* stream) {
+  return oscar_decode_attn_stages(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                                  seq_slot, seq_lens, q, u_k, u_v, sm_scale, out, lse, workspace,
+                                  workspace_bytes, batch, max_seq_len, OSCAR_STAGE_ALL, stream);
+}
+
+oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
+                                      const int32_t* page_table, const void* sink_k,
+                                      const void* sink_v, const void* recent_k,
+                                      const void* recent_v, const int32_t* seq_slot,
+                                      const int32_t* seq_lens, const void* q, const float* u_k,
+                                      const float* u_v, float sm_scale, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, int32_t batch,
+                                      int32_t max_seq_len, uint32_t stages, void* stream) {
   oscar_status st = check_layout(l);
+  if (stages == 0 || (stages & ~OSCAR_STAGE_ALL) != 0)
+    return fail(OSCAR_ERR_RANGE, "stage mask 0x%x invalid", stages);
   if (st != OSCAR_OK) return st;
   if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
   if (batch == 0) return ok();
@@ -325,7 +340,7 @@ oscar_status oscar_decode_attn(const oscar_layout* l, const void* pool, const in
   a.out = out;
   a.lse = lse;
   a.workspace = static_cast<uint8_t*>(workspace);
-  return hip_status(oscar::launch_decode(a, plan, static_cast<hipStream_t>(stream)),
+  return hip_status(oscar::launch_decode(a, plan, stages, static_cast<hipStream_t>(stream)),
                     "oscar_decode_attn");
 }
 

@@ -100,6 +100,7 @@ struct DecodeArgs {
 
 hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, uint32_t stages,
+                         hipStream_t stream);
 
 }  // namespace oscar

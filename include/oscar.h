@@ -197,6 +197,28 @@ oscar_status oscar_decode_attn(const oscar_layout* layout, const void* pool,
                                float* lse, void* workspace, size_t workspace_bytes,
                                int32_t batch, int32_t max_seq_len, void* stream);
 
+/* Stages of oscar_decode_attn, selectable with a bit mask, for callers that schedule them
+ * separately -- for example the BF16 pass on a second stream next to the INT2 pass, or a
+ * profiler bracketing one stage with events.  The stages communicate through the workspace:
+ * OSCAR_STAGE_QUERY (rotate the queries) must complete before OSCAR_STAGE_INT2; OSCAR_STAGE_INT2
+ * and OSCAR_STAGE_BF16 may run in either order or concurrently; OSCAR_STAGE_MERGE needs both.
+ * Every call of a sequence of stages must pass the same arguments, workspace and max_seq_len.
+ * oscar_decode_attn(...) is oscar_decode_attn_stages(..., OSCAR_STAGE_ALL, ...). */
+#define OSCAR_STAGE_QUERY 1u
+#define OSCAR_STAGE_INT2  2u
+#define OSCAR_STAGE_BF16  4u
+#define OSCAR_STAGE_MERGE 8u
+#define OSCAR_STAGE_ALL   15u
+
+oscar_status oscar_decode_attn_stages(const oscar_layout* layout, const void* pool,
+                                      const int32_t* page_table, const void* sink_k,
+                                      const void* sink_v, const void* recent_k,
+                                      const void* recent_v, const int32_t* seq_slot,
+                                      const int32_t* seq_lens, const void* q, const float* u_k,
+                                      const float* u_v, float sm_scale, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, int32_t batch,
+                                      int32_t max_seq_len, uint32_t stages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
