@@ -188,59 +188,59 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode-step append: block = 2 waves for one (sequence, KV head); wave 0 keys, wave 1 values.
-__global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
-  __shared__ float xs[2][kHeadDim];
-  const int tensor = threadIdx.x >> 6;
-  const int lane = dev::lane_id();
-  const int h = blockIdx.x % a.hkv;
-  const int b = blockIdx.x / a.hkv;
+// Decode-step append: one 256-thread block per (sequence, KV head, K|V).  The displaced ring
+// row is staged in LDS, rotated by the whole block (rotate1_block), quantised and stored by wave
+// 0; the ring row is then overwritten with the new token.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ float x[kHeadDim];
+  __shared__ double red[4][kHeadDim];
+  const int tid = threadIdx.x;
+  const int tensor = blockIdx.x & 1;
+  const int h = (blockIdx.x >> 1) % a.hkv;
+  const int b = (blockIdx.x >> 1) / a.hkv;
   const int pos = a.seq_lens[b];
   const int64_t slot = a.seq_slot[b];
   const uint16_t* nw = (tensor == 0 ? a.k_new : a.v_new) +
                        (static_cast<int64_t>(b) * a.hkv + h) * kHeadDim;
-  const uint16_t n0 = nw[lane];
-  const uint16_t n1 = nw[lane + 64];
   if (pos < kSink) {
-    uint16_t* row = (tensor == 0 ? a.sink_k : a.sink_v) +
-                    ((slot * a.hkv + h) * kSink + pos) * kHeadDim;
-    row[lane] = n0;
-    row[lane + 64] = n1;
+    if (tid < kHeadDim) {
+      uint16_t* row = (tensor == 0 ? a.sink_k : a.sink_v) +
+                      ((slot * a.hkv + h) * kSink + pos) * kHeadDim;
+      row[tid] = nw[tid];
+    }
     return;
   }
   uint16_t* ring = (tensor == 0 ? a.recent_k : a.recent_v) +
                    ((slot * a.hkv + h) * kRecent + pos % kRecent) * kHeadDim;
   if (pos >= kSink + kRecent) {
-    float* x = xs[tensor];
-    x[lane] = dev::bf16_to_f32(ring[lane]);
-    x[lane + 64] = dev::bf16_to_f32(ring[lane + 64]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (tid < kHeadDim) x[tid] = dev::bf16_to_f32(ring[tid]);
+    __syncthreads();
     const float* u = (tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim;
-    const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
-    double r[1][2];
-    dev::rotate_fp64<1>(x, u, r);
-    const LaneCodes q = quantize_lane(r[0][0], r[0][1], clip, a.n_groups);
-    const int idx = pos - kSink - kRecent;
-    const int blk_bytes = block_bytes(a.n_groups);
-    uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
-                              blk_bytes);
-    const int slot_in_page = idx % kPage;
-    if (tensor == 0) {
-      store_key_row(blk, slot_in_page, q.c0, q.c1);
-      store_meta(blk, kKMetaOff, slot_in_page, a.n_groups, q);
-    } else {
-      uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-      const int dw = slot_in_page / 16;
-      const int sh = 2 * (slot_in_page % 16);
-      merge_bits(&vc[lane * 4 + dw], 3u << sh, q.c0 << sh);
-      merge_bits(&vc[(lane + 64) * 4 + dw], 3u << sh, q.c1 << sh);
-      store_meta(blk, v_meta_off(a.n_groups), slot_in_page, a.n_groups, q);
+    double r0, r1;
+    // the block barrier inside orders every read of the old row before the overwrite below
+    if (dev::rotate1_block(x, u, red, r0, r1)) {
+      const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+      const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups);
+      const int idx = pos - kSink - kRecent;
+      const int blk_bytes = block_bytes(a.n_groups);
+      uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
+                                blk_bytes);
+      const int slot_in_page = idx % kPage;
+      const int lane = dev::lane_id();
+      if (tensor == 0) {
+        store_key_row(blk, slot_in_page, q.c0, q.c1);
+        store_meta(blk, kKMetaOff, slot_in_page, a.n_groups, q);
+      } else {
+        uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
+        const int dw = slot_in_page / 16;
+        const int sh = 2 * (slot_in_page % 16);
+        merge_bits(&vc[lane * 4 + dw], 3u << sh, q.c0 << sh);
+        merge_bits(&vc[(lane + 64) * 4 + dw], 3u << sh, q.c1 << sh);
+        store_meta(blk, v_meta_off(a.n_groups), slot_in_page, a.n_groups, q);
+      }
     }
   }
-  // the old row has been read (its values were consumed above); overwrite it with the new token
-  ring[lane] = n0;
-  ring[lane + 64] = n1;
+  if (tid < kHeadDim) ring[tid] = nw[tid];
 }
 
 }  // namespace
@@ -257,7 +257,7 @@ hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(a.batch * a.hkv)), dim3(128), 0,
+  hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(a.batch * a.hkv * 2)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }

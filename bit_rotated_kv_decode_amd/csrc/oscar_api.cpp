@@ -73,17 +73,20 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for about 1024 work items (four per compute unit) with at least one page per wave.
+  // Aim for about 512 work items (two resident per compute unit) with at least one page per
+  // wave, within the per-item page and per-head item limits of the kernels.
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
-  p.pages_per_split = static_cast<int>(std::max<long long>(4, (items + 1023) / 1024));
+  long long pps = std::max<long long>(4, (items + 511) / 512);
+  pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
+  p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(batch) * p.hq;
   size_t off = 0;
   p.off_qrot = off;
-  off = al(off + rows * kHeadDim * 4);
+  off = al(off + rows * 2 * kHeadDim);
   p.off_sigma = off;
-  off = al(off + rows * 2 * 4);
+  off = al(off + rows * 4 * 4);
   p.off_int2_ml = off;
   off = al(off + rows * std::max(p.num_splits, 1) * 2 * 4);
   p.off_int2_acc = off;

@@ -14,7 +14,9 @@ constexpr int kPage = 64;
 constexpr int kSink = 64;
 constexpr int kRecent = 256;
 constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the BF16 segments
-constexpr int kMaxGqa = 16;
+constexpr int kMaxGqa = 8;
+constexpr int kMaxPagesPerSplit = 1024;   // history pages one INT2 work item may cover
+constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
 
 // Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
 constexpr int kKCodesOff = 0;
@@ -29,8 +31,8 @@ struct Plan {
   int max_pages = 0;         // history pages of the longest sequence
   int pages_per_split = 1;   // history pages per INT2 work item
   int num_splits = 0;        // work items per (sequence, KV head)
-  size_t off_qrot = 0;       // fp32 [B][Hq][128] rotated queries
-  size_t off_sigma = 0;      // fp32 [B][Hq][G] per-group sums of the rotated query
+  size_t off_qrot = 0;       // int8 [B][Hq][2][128] rotated queries, hi / lo parts, MFMA order
+  size_t off_sigma = 0;      // fp32 [B][Hq][4] score scale and per-group sums of the query
   size_t off_int2_ml = 0;    // fp32 [B][Hq][S][2] (m, l) of INT2 partials (log2 domain)
   size_t off_int2_acc = 0;   // fp32 [B][Hq][S][128] rotated-space accumulators
   size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]

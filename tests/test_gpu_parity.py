@@ -127,9 +127,9 @@ def test_page_shuffle_and_split_invariance():
     cache2 = case.gpu_cache(g2, pool_from_oracle=pool2)
     out2, _ = case.gpu_attention(g2, cache2)
     assert np.array_equal(out1, out2)
-    # a larger max_seq_len changes the split plan; the result changes only by fp32 rounding
+    # a larger max_seq_len changes the split plan; the result changes only by rounding
     out3, _ = case.gpu_attention(g, cache, max_seq_len=150000)
-    assert attention_error(out3, out1) < 1e-5
+    assert attention_error(out3, out1) < 1e-4
 
 
 def test_append_steps_match_oracle():
