@@ -115,9 +115,8 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
   constexpr int GP = G <= 4 ? 4 : 8;      // padded query heads per KV head
   constexpr int NACC = GP / 4;            // score accumulators (tokens per lane and page)
   constexpr int NPL = 16 / GP;            // operand placements
-  constexpr int PP = (GP == 8 && NG == 2) ? 1 : 2;  // pages per step (register budget)
-  constexpr int BLK = kKMetaOff + 2 * kPage * NG * 4;
-  constexpr int VMETA = kKMetaOff + kPage * NG * 4;
+  constexpr int PP = 1;                    // pages per step
+  constexpr int BLK = kMetaOff + kPage * 8 * NG;
   constexpr int QA_BYTES = NPL * 2 * 2 * 64 * 16;             // [pl][hf][hl][lane] int8 x16
   constexpr int PB_BYTES = 4 * PP * NG * 16 * kPage * 2;      // [wave][page][g][row][token] bf16
   constexpr int RED_BYTES = 4 * 2 * GP * kHeadDim * 4;        // [wave][row][ch] fp32, after loop
@@ -201,30 +200,48 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // One page's operands, fetched with 16-byte loads from the tiled block (one chunk row = 64 lanes
+  // x 16 bytes): key chunk row j holds this lane's words of sub-tiles 2j and 2j + 1, value chunk
+  // row j those of channel tiles 4j .. 4j + 3; the meta of a token is (key pairs, value pairs).
   struct PageRegs {
-    uint32_t k[4][2];        // key code dwords [sub-tile][half]
-    uint32_t v[8];           // value code dword of channel 16 nt + n, tokens 16 gq .. 16 gq + 15
+    uint4 k[2];              // k[st / 2] entry 2 (st % 2) + hf: key codes, sub-tile st, half hf
+    uint4 v[2];              // v[nt / 4] entry nt % 4: value codes, channel 16 nt + n
     uint32_t km[NACC][NG];   // key meta (scale | zero << 16) of the lane's token(s)
     uint32_t vm[NACC][NG];
   };
+  auto kword = [](const PageRegs& r, int st, int hf) {
+    const uint4& c = r.k[st >> 1];
+    const int e = ((st & 1) << 1) + hf;
+    return e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
+  };
+  auto vword = [](const PageRegs& r, int nt) {
+    const uint4& c = r.v[nt >> 2];
+    const int e = nt & 3;
+    return e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
+  };
   auto load_page = [&](int pg, PageRegs& r) {
     const uint8_t* blk = a.pool + (static_cast<int64_t>(page_ids[pg - p0]) * p.hkv + kv) * BLK;
+    const uint4* kc = reinterpret_cast<const uint4*>(blk + kKCodesOff);
+    const uint4* vc = reinterpret_cast<const uint4*>(blk + kVCodesOff);
+    r.k[0] = kc[lane];
+    r.k[1] = kc[64 + lane];
+    r.v[0] = vc[lane];
+    r.v[1] = vc[64 + lane];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        r.k[st][hf] = *reinterpret_cast<const uint32_t*>(blk + kKCodesOff + (16 * st + n) * 32 +
-                                                         4 * (4 * hf + gq));
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      r.v[nt] = *reinterpret_cast<const uint32_t*>(blk + kVCodesOff + (16 * nt + n) * 16 + 4 * gq);
-#pragma unroll
-    for (int pa = 0; pa < NACC; ++pa)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        r.km[pa][g] = reinterpret_cast<const uint32_t*>(blk + kKMetaOff)[tok_of(pa) * NG + g];
-        r.vm[pa][g] = reinterpret_cast<const uint32_t*>(blk + VMETA)[tok_of(pa) * NG + g];
+    for (int pa = 0; pa < NACC; ++pa) {
+      const uint8_t* m = blk + kMetaOff + tok_of(pa) * 8 * NG;
+      if (NG == 1) {
+        const uint2 w = *reinterpret_cast<const uint2*>(m);
+        r.km[pa][0] = w.x;
+        r.vm[pa][0] = w.y;
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(m);
+        r.km[pa][0] = w.x;
+        r.km[pa][NG - 1] = w.y;
+        r.vm[pa][0] = w.z;
+        r.vm[pa][NG - 1] = w.w;
       }
+    }
   };
 
   // Pages pg .. pg + PP - 1 on register sets r[0 .. PP - 1]; pages past p1 contribute nothing.
@@ -247,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
         const int g = NG == 2 ? hf : 0;
 #pragma unroll
         for (int pp = 0; pp < PP; ++pp) {
-          const uint32_t w = r[pp].k[st][hf];
+          const uint32_t w = kword(r[pp], st, hf);
           const v4i bk = {static_cast<int>(w & 0x03030303u),
                           static_cast<int>((w >> 2) & 0x03030303u),
                           static_cast<int>((w >> 4) & 0x03030303u),
@@ -358,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
       const int g = NG == 2 ? nt / 4 : 0;
 #pragma unroll
       for (int pp = 0; pp < PP; ++pp) {
-        const uint32_t w = r[pp].v[nt];
+        const uint32_t w = vword(r[pp], nt);
         const uint32_t xs = w & 0x33333333u;          // nibbles: tokens 0, 2, 4, ..., 14
         const uint32_t ys = (w >> 2) & 0x33333333u;   // nibbles: tokens 1, 3, 5, ..., 15
         {

@@ -69,7 +69,8 @@ __device__ __forceinline__ uint8_t* page_block(uint8_t* pool, const int32_t* pag
   return pool + (static_cast<int64_t>(page) * hkv + h) * blk_bytes;
 }
 
-// Key codes are packed along channels: dword w of a token row holds channels 16w..16w+15.
+// Key codes are packed along channels: word w of a token holds channels 16w..16w+15, and the
+// words sit in the tiled order of k_word_index.
 __device__ __forceinline__ void store_key_row(uint8_t* blk, int slot, uint32_t c0, uint32_t c1) {
   const int lane = dev::lane_id();
   uint32_t v0 = c0 << (2 * (lane & 15));
@@ -80,16 +81,18 @@ __device__ __forceinline__ void store_key_row(uint8_t* blk, int slot, uint32_t c
     v1 |= __shfl_xor(v1, m);
   }
   if ((lane & 15) == 0) {
-    uint32_t* row = reinterpret_cast<uint32_t*>(blk + kKCodesOff + slot * (kHeadDim / 4));
-    row[lane >> 4] = v0;
-    row[4 + (lane >> 4)] = v1;
+    uint32_t* words = reinterpret_cast<uint32_t*>(blk + kKCodesOff);
+    words[k_word_index(slot, lane >> 4)] = v0;
+    words[k_word_index(slot, 4 + (lane >> 4))] = v1;
   }
 }
 
-__device__ __forceinline__ void store_meta(uint8_t* blk, int meta_off, int slot, int n_groups,
+// Per-token meta: key groups first, then value groups (tensor 0 = K, 1 = V).
+__device__ __forceinline__ void store_meta(uint8_t* blk, int tensor, int slot, int n_groups,
                                            const LaneCodes& q) {
   if (dev::lane_id() == 0) {
-    uint32_t* m = reinterpret_cast<uint32_t*>(blk + meta_off) + slot * n_groups;
+    uint32_t* m = reinterpret_cast<uint32_t*>(blk + kMetaOff + slot * meta_bytes_per_token(n_groups)) +
+                  tensor * n_groups;
     for (int g = 0; g < n_groups; ++g) m[g] = q.meta[g];
   }
 }
@@ -157,7 +160,6 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
   uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, first, a.hkv, h,
                             blk_bytes);
   const int slot0 = first % kPage;
-  const int meta_off = tensor == 0 ? kKMetaOff : v_meta_off(a.n_groups);
   uint32_t vword0 = 0, vword1 = 0, vmask = 0;
 #pragma unroll
   for (int t = 0; t < kRun; ++t) {
@@ -171,18 +173,20 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
       vword1 |= q.c1 << (2 * t);
       vmask |= 3u << (2 * t);
     }
-    store_meta(blk, meta_off, slot0 + t, a.n_groups, q);
+    store_meta(blk, tensor, slot0 + t, a.n_groups, q);
   }
   if (tensor == 1) {
-    // value codes of channel j for this run: dword (j * 4 + slot0 / 16) of the value region
+    // value codes of channel j for this run: word (j, slot0 / 16) of the value region
     uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-    const int dw = slot0 / kRun;
+    const int uw = slot0 / kRun;
+    uint32_t* w0 = &vc[v_word_index(lane, uw)];
+    uint32_t* w1 = &vc[v_word_index(lane + 64, uw)];
     if (vmask == 0xFFFFFFFFu) {
-      vc[lane * 4 + dw] = vword0;
-      vc[(lane + 64) * 4 + dw] = vword1;
+      *w0 = vword0;
+      *w1 = vword1;
     } else {
-      merge_bits(&vc[lane * 4 + dw], vmask, vword0);
-      merge_bits(&vc[(lane + 64) * 4 + dw], vmask, vword1);
+      merge_bits(w0, vmask, vword0);
+      merge_bits(w1, vmask, vword1);
     }
   }
 }
@@ -229,15 +233,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       const int lane = dev::lane_id();
       if (tensor == 0) {
         store_key_row(blk, slot_in_page, q.c0, q.c1);
-        store_meta(blk, kKMetaOff, slot_in_page, a.n_groups, q);
       } else {
         uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-        const int dw = slot_in_page / 16;
+        const int u = slot_in_page / 16;
         const int sh = 2 * (slot_in_page % 16);
-        merge_bits(&vc[lane * 4 + dw], 3u << sh, q.c0 << sh);
-        merge_bits(&vc[(lane + 64) * 4 + dw], 3u << sh, q.c1 << sh);
-        store_meta(blk, v_meta_off(a.n_groups), slot_in_page, a.n_groups, q);
+        merge_bits(&vc[v_word_index(lane, u)], 3u << sh, q.c0 << sh);
+        merge_bits(&vc[v_word_index(lane + 64, u)], 3u << sh, q.c1 << sh);
       }
+      store_meta(blk, tensor, slot_in_page, a.n_groups, q);
     }
   }
   if (tid < kHeadDim) ring[tid] = nw[tid];

@@ -73,10 +73,10 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for about 512 work items (two resident per compute unit) with at least one page per
-  // wave, within the per-item page and per-head item limits of the kernels.
+  // Aim for one round of work items over the compute units (kInt2Items resident at once) with
+  // at least one page per wave, within the per-item page and per-head item limits of the kernels.
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
-  long long pps = std::max<long long>(4, (items + 511) / 512);
+  long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;

@@ -17,13 +17,28 @@ constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the B
 constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 1024;   // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
+constexpr int kInt2Items = 768;           // INT2 work items resident at once (3 per compute unit)
 
 // Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
 constexpr int kKCodesOff = 0;
 constexpr int kVCodesOff = kPage * kHeadDim / 4;              // 2048
-constexpr int kKMetaOff = kVCodesOff + kHeadDim * kPage / 4;  // 4096
-__host__ __device__ inline int v_meta_off(int n_groups) { return kKMetaOff + kPage * n_groups * 4; }
-__host__ __device__ inline int block_bytes(int n_groups) { return v_meta_off(n_groups) + kPage * n_groups * 4; }
+constexpr int kMetaOff = kVCodesOff + kHeadDim * kPage / 4;   // 4096
+// per token: fp16 (scale, zero) of each key group, then of each value group
+__host__ __device__ inline int meta_bytes_per_token(int n_groups) { return 8 * n_groups; }
+__host__ __device__ inline int block_bytes(int n_groups) {
+  return kMetaOff + kPage * meta_bytes_per_token(n_groups);
+}
+// Tiled word order of the code regions: a word holds 16 two-bit codes, and each 1 KiB row of a
+// region is 64 lanes x 16 bytes, so that one 16-byte load per lane fetches the words of that lane's
+// MFMA operands.  Key word (token t = 16 st + n, channels 16 w .. 16 w + 15 with w = 4 hf + q):
+// lane 16 q + n of chunk row st / 2, entry 2 (st % 2) + hf.  Value word (channel c = 16 nt + n,
+// tokens 16 u .. 16 u + 15): lane 16 u + n of chunk row nt / 4, entry nt % 4.
+__host__ __device__ inline int k_word_index(int t, int w) {
+  return (((t >> 5) * 64 + (w & 3) * 16 + (t & 15)) << 2) + (((t >> 4) & 1) << 1) + (w >> 2);
+}
+__host__ __device__ inline int v_word_index(int c, int u) {
+  return (((c >> 6) * 64 + u * 16 + (c & 15)) << 2) + ((c >> 4) & 3);
+}
 
 // Work plan of one decode-attention call, and the carve-up of its workspace.
 struct Plan {

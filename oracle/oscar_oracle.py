@@ -39,7 +39,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
       rounding, (x - z)/s) run in IEEE fp32, the kernels' precision; the rotation itself is fp64.
   R7  pack order: code of element 4b+i sits in bits [2i, 2i+1] of byte b (LSB first).
   R8  page layout (one block per page and KV head, 64 tokens): key codes packed along channels,
-      value codes packed along tokens, then key meta and value meta as fp16 (scale, zero) pairs.
+      value codes packed along tokens, then per token the fp16 (scale, zero) pairs of its key
+      groups followed by those of its value groups.  At the kernels' geometry (128 channels,
+      64-token pages) the 4-byte words of 16 codes are stored in a tiled order, one 16-byte chunk
+      per lane of a 64-lane wave (see ``k_word_index`` / ``v_word_index``); smaller test
+      geometries keep plain row order.
   R9  order within a decode step: append the new token, demote the token that leaves the recent
       window, then attend; the recent window holds the last min(256, L-64) tokens.
   R10 attention: scores scaled by 1/sqrt(d), no mask, query head i uses KV head i // G.
@@ -84,16 +88,20 @@ class Geometry:
         return self.page * self.head_dim // 4
 
     @property
-    def k_meta_off(self) -> int:
+    def meta_off(self) -> int:
         return self.v_codes_off + self.head_dim * self.page // 4
 
     @property
-    def v_meta_off(self) -> int:
-        return self.k_meta_off + self.page * self.n_groups * 4
+    def meta_bytes_per_token(self) -> int:
+        return 2 * self.n_groups * 4
 
     @property
     def block_bytes(self) -> int:
-        return self.v_meta_off + self.page * self.n_groups * 4
+        return self.meta_off + self.page * self.meta_bytes_per_token
+
+    @property
+    def tiled(self) -> bool:
+        return self.head_dim == 128 and self.page == 64
 
 
 # ----------------------------------------------------------------------------------------------
@@ -221,6 +229,46 @@ def new_pool(num_pages: int, num_kv_heads: int, geom: Geometry) -> np.ndarray:
     return np.zeros((num_pages, num_kv_heads, geom.block_bytes), dtype=np.uint8)
 
 
+def k_word_index(t, w):
+    """Word position of key codes (token t, channels 16w .. 16w+15) in the tiled order of a
+    64-token, 128-channel block (reading R8).  With t = 16 st + n and w = 4 hf + q, the word is
+    entry 2 (st mod 2) + hf of the 16-byte chunk of lane 16 q + n in 1 KiB chunk row st // 2."""
+    t = np.asarray(t)
+    w = np.asarray(w)
+    st, n = t // 16, t % 16
+    hf, q = w // 4, w % 4
+    return ((st // 2) * 64 + 16 * q + n) * 4 + (st % 2) * 2 + hf
+
+
+def v_word_index(c, u):
+    """Word position of value codes (channel c, tokens 16u .. 16u+15) in the tiled order (reading
+    R8).  With c = 16 nt + n, the word is entry nt mod 4 of the 16-byte chunk of lane 16 u + n in
+    1 KiB chunk row nt // 4."""
+    c = np.asarray(c)
+    u = np.asarray(u)
+    nt, n = c // 16, c % 16
+    return ((nt // 4) * 64 + 16 * u + n) * 4 + nt % 4
+
+
+def k_code_bytes(slot: int, geom: Geometry) -> np.ndarray:
+    """Byte offsets (within the block) of the d/4 packed key-code bytes of one token, in channel
+    order: byte j holds channels 4j .. 4j+3."""
+    j = np.arange(geom.head_dim // 4)
+    if geom.tiled:
+        return geom.k_codes_off + 4 * k_word_index(slot, j // 4) + j % 4
+    return geom.k_codes_off + slot * geom.head_dim // 4 + j
+
+
+def v_code_bytes(slot: int, geom: Geometry) -> np.ndarray:
+    """Byte offset, per channel, of the packed value-code byte that holds token `slot` (at bits
+    2 (slot mod 4)); a byte holds tokens 4b .. 4b+3 of its channel."""
+    c = np.arange(geom.head_dim)
+    tb = slot // 4
+    if geom.tiled:
+        return geom.v_codes_off + 4 * v_word_index(c, tb // 4) + tb % 4
+    return geom.v_codes_off + c * (geom.page // 4) + tb
+
+
 def _meta_bytes(scale16, zero16) -> np.ndarray:
     """(n, G) fp16 scale and zero -> (n, G*4) bytes: per group the scale's two bytes, then the
     zero's, little endian."""
@@ -239,7 +287,7 @@ def store_history(pool, table_row, hist_idx, head, kq, vq, geom: Geometry):
     hist_idx = np.asarray(hist_idx)
     kc, ks, kz = kq
     vc, vs, vz = vq
-    d, pg = geom.head_dim, geom.page
+    pg = geom.page
     kmeta = _meta_bytes(ks, kz)
     vmeta = _meta_bytes(vs, vz)
     kpacked = pack_codes(kc)
@@ -247,13 +295,14 @@ def store_history(pool, table_row, hist_idx, head, kq, vq, geom: Geometry):
     for n, t in enumerate(hist_idx):
         blk = pool[table_row[t // pg], head]
         slot = int(t % pg)
-        blk[geom.k_codes_off + slot * d // 4: geom.k_codes_off + (slot + 1) * d // 4] = kpacked[n]
+        blk[k_code_bytes(slot, geom)] = kpacked[n]
         # value codes: channel j's codes for the page's tokens are packed along tokens
-        byte = geom.v_codes_off + np.arange(d) * (pg // 4) + slot // 4
+        byte = v_code_bytes(slot, geom)
         shift = 2 * (slot % 4)
         blk[byte] = (blk[byte] & np.uint8(~(3 << shift) & 0xFF)) | (vc[n].astype(np.uint8) << shift)
-        blk[geom.k_meta_off + slot * msz: geom.k_meta_off + (slot + 1) * msz] = kmeta[n]
-        blk[geom.v_meta_off + slot * msz: geom.v_meta_off + (slot + 1) * msz] = vmeta[n]
+        m0 = geom.meta_off + slot * geom.meta_bytes_per_token
+        blk[m0: m0 + msz] = kmeta[n]
+        blk[m0 + msz: m0 + 2 * msz] = vmeta[n]
 
 
 def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
@@ -272,14 +321,11 @@ def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
     for t in range(n_hist):
         blk = pool[table_row[t // pg], head]
         slot = t % pg
-        kc[t] = unpack_codes(blk[geom.k_codes_off + slot * d // 4:
-                                 geom.k_codes_off + (slot + 1) * d // 4])
-        byte = geom.v_codes_off + np.arange(d) * (pg // 4) + slot // 4
-        vc[t] = (blk[byte] >> (2 * (slot % 4))) & 3
-        km = blk[geom.k_meta_off + slot * msz: geom.k_meta_off + (slot + 1) * msz]
-        vm = blk[geom.v_meta_off + slot * msz: geom.v_meta_off + (slot + 1) * msz]
-        km = km.view("<f2").reshape(ng, 2)
-        vm = vm.view("<f2").reshape(ng, 2)
+        kc[t] = unpack_codes(blk[k_code_bytes(slot, geom)])
+        vc[t] = (blk[v_code_bytes(slot, geom)] >> (2 * (slot % 4))) & 3
+        m0 = geom.meta_off + slot * geom.meta_bytes_per_token
+        km = blk[m0: m0 + msz].view("<f2").reshape(ng, 2)
+        vm = blk[m0 + msz: m0 + 2 * msz].view("<f2").reshape(ng, 2)
         ks[t], kz[t] = km[:, 0], km[:, 1]
         vs[t], vz[t] = vm[:, 0], vm[:, 1]
     return (kc, ks, kz), (vc, vs, vz)

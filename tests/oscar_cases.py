@@ -199,18 +199,11 @@ def compare_pool_blocks(gpu: np.ndarray, ref: np.ndarray, case: Case, heads=None
     head_ids = list(range(hkv)) if heads is None else list(heads)
     bad_tokens = set()
     pages, hh, offs = np.nonzero(gpu != ref)
+    byte_owner = _byte_owners(g)
     for pg, hi, off in zip(pages, hh, offs):
         b, p = owner[int(pg)]
         h = head_ids[hi]
-        if off < g.v_codes_off:
-            slots, tensor = [off // (g.head_dim // 4)], "k"
-        elif off < g.k_meta_off:
-            o = off - g.v_codes_off
-            slots, tensor = [4 * (o % (g.page // 4)) + i for i in range(4)], "v"
-        elif off < g.v_meta_off:
-            slots, tensor = [(off - g.k_meta_off) // (4 * g.n_groups)], "k"
-        else:
-            slots, tensor = [(off - g.v_meta_off) // (4 * g.n_groups)], "v"
+        slots, tensor = byte_owner[int(off)]
         for s in slots:
             bad_tokens.add((b, p * g.page + s, h, tensor))
     flips = 0
@@ -254,15 +247,33 @@ def compare_pool_blocks(gpu: np.ndarray, ref: np.ndarray, case: Case, heads=None
     return flips
 
 
+def _byte_owners(g):
+    """Block byte offset -> (history slots whose data it holds, tensor), from the oracle's
+    layout functions."""
+    own = {}
+    ng4 = 4 * g.n_groups
+    for s in range(g.page):
+        for off in oracle.k_code_bytes(s, g):
+            own[int(off)] = ([s], "k")
+        for off in oracle.v_code_bytes(s, g):
+            own.setdefault(int(off), ([], "v"))[0].append(s)
+        m0 = g.meta_off + s * g.meta_bytes_per_token
+        for off in range(m0, m0 + ng4):
+            own[off] = ([s], "k")
+        for off in range(m0 + ng4, m0 + 2 * ng4):
+            own[off] = ([s], "v")
+    return own
+
+
 def _token(blk, slot, tensor, g):
-    d, ng = g.head_dim, g.n_groups
+    ng = g.n_groups
+    m0 = g.meta_off + slot * g.meta_bytes_per_token + (0 if tensor == "k" else 4 * ng)
     if tensor == "k":
-        row = blk[g.k_codes_off + slot * d // 4: g.k_codes_off + (slot + 1) * d // 4]
+        row = blk[oracle.k_code_bytes(slot, g)]
         codes = np.stack([(row >> (2 * i)) & 3 for i in range(4)], -1).reshape(-1)
-        meta = blk[g.k_meta_off + slot * 4 * ng: g.k_meta_off + (slot + 1) * 4 * ng]
     else:
-        byte = blk[g.v_codes_off + np.arange(d) * (g.page // 4) + slot // 4]
+        byte = blk[oracle.v_code_bytes(slot, g)]
         codes = (byte >> (2 * (slot % 4))) & 3
-        meta = blk[g.v_meta_off + slot * 4 * ng: g.v_meta_off + (slot + 1) * 4 * ng]
+    meta = blk[m0: m0 + 4 * ng]
     m = np.frombuffer(meta.tobytes(), dtype="<f2").reshape(ng, 2)
     return codes.astype(np.uint8), m[:, 0].copy(), m[:, 1].copy()

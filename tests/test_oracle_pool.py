@@ -12,8 +12,8 @@ import oracle
 
 def test_hand_worked_block_layout():
     g = oracle.Geometry(head_dim=8, group=4, page=4, sink=2, recent=3)
-    assert (g.k_codes_off, g.v_codes_off, g.k_meta_off, g.v_meta_off, g.block_bytes) == \
-        (0, 8, 16, 48, 80)
+    assert (g.k_codes_off, g.v_codes_off, g.meta_off, g.block_bytes) == (0, 8, 16, 80)
+    assert not g.tiled
     pool = oracle.new_pool(2, 1, g)
     table = np.array([1, 0], np.int32)             # logical page 1 -> physical page 0
     kc = np.array([[1, 2, 3, 0, 0, 0, 0, 1]], np.uint8)
@@ -28,13 +28,48 @@ def test_hand_worked_block_layout():
     # history index 6 -> logical page 1 (physical 0), slot 2
     assert blk[4:6].tolist() == [0x39, 0x40]                      # key codes, 2 bytes per token
     assert blk[8:16].tolist() == [0x30, 0, 0x10, 0x20, 0, 0, 0, 0]  # value codes, shift 4 = slot 2
-    assert blk[32:40].tolist() == [0x00, 0x3C, 0x00, 0xBC, 0x00, 0x38, 0x00, 0x40]
-    assert blk[64:72].tolist() == [0x00, 0x34, 0x00, 0x00, 0x00, 0x00, 0x00, 0xC0]
+    # meta of slot 2 at 16 + 2 * 16: key (scale, zero) per group, then value
+    assert blk[48:56].tolist() == [0x00, 0x3C, 0x00, 0xBC, 0x00, 0x38, 0x00, 0x40]
+    assert blk[56:64].tolist() == [0x00, 0x34, 0x00, 0x00, 0x00, 0x00, 0x00, 0xC0]
     touched = np.zeros(80, bool)
     touched[[4, 5, 8, 10, 11]] = True
-    touched[32:40] = True
-    touched[64:72] = True
+    touched[48:64] = True
     assert not blk[~touched].any()
+
+
+def test_hand_worked_tiled_order():
+    # Full geometry: words of 16 codes in the tiled order.  Key code 2 at token 37, channel 103:
+    # 37 = 16*2 + 5 (st 2, n 5); 103 = 16*6 + 4*1 + 3 (word 6 = 4*1 + 2, byte 1, bits 6..7)
+    # -> chunk row 1, lane 16*2 + 5 = 37, entry 2*0 + 1 = 1: word 4*(64 + 37) + 1 = 405,
+    # byte 4*405 + 1 = 1621, value 2 << 6.
+    # Value code 3 at token 50, channel 77: 50 = 16*3 + 4*0 + 2 (word u 3, byte 0, bits 4..5);
+    # 77 = 16*4 + 13 (nt 4, n 13) -> chunk row 1, lane 16*3 + 13 = 61, entry 0: word
+    # 4*(64 + 61) = 500, byte 2048 + 2000 = 4048, value 3 << 4.
+    g = oracle.Geometry()
+    assert g.tiled and (g.v_codes_off, g.meta_off, g.block_bytes) == (2048, 4096, 4608)
+    assert oracle.k_word_index(37, 6) == 405 and oracle.v_word_index(77, 3) == 500
+    pool = oracle.new_pool(1, 1, g)
+    kc = np.zeros((2, 128), np.uint8)
+    vc = np.zeros((2, 128), np.uint8)
+    kc[0, 103] = 2
+    vc[1, 77] = 3
+    one = np.ones((2, 1), np.float16)
+    zero = np.zeros((2, 1), np.float16)
+    oracle.store_history(pool, np.array([0], np.int32), [37, 50], 0, (kc, zero, zero),
+                         (vc, zero, zero), g)
+    blk = pool[0, 0]
+    nz = np.nonzero(blk)[0].tolist()
+    assert nz == [1621, 4048]
+    assert blk[1621] == 2 << 6 and blk[4048] == 3 << 4
+    # the word orders are permutations of all 512 words of each region
+    t, w = np.meshgrid(np.arange(64), np.arange(8), indexing="ij")
+    assert sorted(oracle.k_word_index(t, w).ravel().tolist()) == list(range(512))
+    c, u = np.meshgrid(np.arange(128), np.arange(4), indexing="ij")
+    assert sorted(oracle.v_word_index(c, u).ravel().tolist()) == list(range(512))
+    # meta of token 50: key pair at 4096 + 50 * 8, value pair right after
+    oracle.store_history(pool, np.array([0], np.int32), [50], 0, (kc[:1], one[:1], zero[:1]),
+                         (vc[:1], zero[:1], one[:1]), g)
+    assert blk[4096 + 400: 4096 + 408].tolist() == [0x00, 0x3C, 0, 0, 0, 0, 0x00, 0x3C]
 
 
 def test_store_load_roundtrip_random():
