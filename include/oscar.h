@@ -37,12 +37,18 @@
  *  INT2 pool: num_pages pages; a page holds 64 consecutive history tokens of one sequence for
  *  every KV head: pool bytes [page][kv_head][block], block = oscar_page_block_bytes().  A block
  *  (d = 128 channels, g = group_size, G = d / g groups) is:
- *      offset 0                 key codes    [64 tokens][d/4 bytes]   packed along channels:
- *                               code of channel 4b+i in bits [2i, 2i+1] of byte b of the row
- *      offset 64*d/4 (2048)     value codes  [d channels][64/4 bytes] packed along tokens:
- *                               code of token-slot 4b+i in bits [2i, 2i+1] of byte b of the row
- *      offset 4096              key meta     [64 tokens][G][fp16 scale, fp16 zero]
- *      offset 4096 + 64*G*4     value meta   [64 tokens][G][fp16 scale, fp16 zero]
+ *      offset 0      key codes    2048 bytes = 512 words of 16 codes (4 bytes each)
+ *      offset 2048   value codes  2048 bytes = 512 words of 16 codes
+ *      offset 4096   meta         [64 tokens][key: G x (fp16 scale, fp16 zero),
+ *                                             value: G x (fp16 scale, fp16 zero)]
+ *  Key word (t, w) holds channels 16w .. 16w+15 of token t (w < 8), value word (c, u) holds
+ *  tokens 16u .. 16u+15 of channel c (u < 4); inside a word, element 4b+i of the 16 sits in bits
+ *  [2i, 2i+1] of byte b.  Words are tiled for 16-byte loads by a 64-lane wave: each region is
+ *  two rows of 64 chunks of 16 bytes (4 words), and
+ *      key word (t = 16 st + n, w = 4 hf + q)  ->  word index 4 (64 (st / 2) + 16 q + n) + 2 (st % 2) + hf
+ *      value word (c = 16 nt + n, u)           ->  word index 4 (64 (nt / 4) + 16 u + n) + nt % 4
+ *  so chunk (row j, lane l) is exactly the code words lane l of a wave needs as matrix-core
+ *  operands for key sub-tiles 2j, 2j+1 and value channel tiles 4j .. 4j+3.
  *  (4,608 bytes per block at g = 128, i.e. 72 bytes per token and KV head; 5,120 at g = 64.)
  *  Codes are of the rotated, clipped vector in rotated-channel order; the value of element j of
  *  token t in group m = j / g is  scale[t][m] * code[t][j] + zero[t][m]  (rotated space).
