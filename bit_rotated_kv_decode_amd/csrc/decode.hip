@@ -6,12 +6,13 @@
 //   1. query_kernel  q' = q R_k per query head (fp64 rotation), quantised for the INT2 pass into
 //                    int8 hi / lo parts (q' ~ a (hi + lo / 256)) laid out as MFMA operands, plus
 //                    the per-group sums of the quantised q' that the zero points multiply;
-//   2. int2_kernel   split-KV over history pages on the matrix cores: scores s (q' . codes) +
-//                    z sum(q') with the dot products as exact int32 i8 MFMAs, online softmax with
-//                    lazy rescaling, value accumulation in the rotated frame as bf16 MFMAs ->
-//                    (m, l, acc') partials;
-//   3. bf16_kernel   64-token chunks of the BF16 sink and recent ring -> (m, l, acc) partials;
-//   4. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
+//   2. attn_kernel   both segment passes in one grid:
+//                    INT2 blocks: split-KV over history pages on the matrix cores: scores
+//                    s (q' . codes) + z sum(q') with the dot products as exact int32 i8 MFMAs,
+//                    online softmax with lazy rescaling, value accumulation in the rotated frame
+//                    as bf16 MFMAs -> (m, l, acc') partials;
+//                    BF16 blocks: 64-token chunks of the BF16 sink and recent ring -> (m, l, acc);
+//   3. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
 //                    the BF16 partials, normalisation.
 // Softmax statistics are kept in the log2 domain: scores are scaled by sm_scale * log2(e).
 #include "device_common.h"
@@ -110,25 +111,40 @@ __device__ __forceinline__ v2bf codes_to_bf16(uint32_t x) {
 // Values: acc[row, ch] += sum_t P[row, t] V[t, ch] with v_mfma_f32_16x16x32_bf16; P rows are the
 // bf16 hi and lo parts of p * s_v for each head, transposed through LDS; V = value codes turned
 // into exact bf16 integers by the FP4 conversion path.
+// LDS carve-up of an INT2 block.  The query operands and P tiles are dead after the page loop,
+// where the same bytes take the per-wave accumulator rows.
 template <int G, int NG>
-__global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
-  constexpr int GP = G <= 4 ? 4 : 8;      // padded query heads per KV head
-  constexpr int NACC = GP / 4;            // score accumulators (tokens per lane and page)
-  constexpr int NPL = 16 / GP;            // operand placements
-  constexpr int PP = 1;                    // pages per step
-  constexpr int BLK = kMetaOff + kPage * 8 * NG;
-  constexpr int QA_BYTES = NPL * 2 * 2 * 64 * 16;             // [pl][hf][hl][lane] int8 x16
-  constexpr int PB_BYTES = 4 * PP * NG * 16 * kPage * 2;      // [wave][page][g][row][token] bf16
-  constexpr int RED_BYTES = 4 * 2 * GP * kHeadDim * 4;        // [wave][row][ch] fp32, after loop
-  constexpr int SMEM = (QA_BYTES + PB_BYTES) > RED_BYTES ? (QA_BYTES + PB_BYTES) : RED_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  __shared__ int page_ids[kMaxPagesPerSplit];
-  __shared__ float red_m[4][GP], red_l[4][GP], red_z[4][GP][NG];
-  v4i* qa_lds = reinterpret_cast<v4i*>(smem);
-  __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem + QA_BYTES);
-  float* red_acc = reinterpret_cast<float*>(smem);
+struct Int2Lds {
+  static constexpr int GP = G <= 4 ? 4 : 8;
+  static constexpr int NPL = 16 / GP;
+  static constexpr int QA = NPL * 2 * 2 * 64 * 16;           // [pl][hf][hl][lane] int8 x16
+  static constexpr int PB = 4 * NG * 16 * kPage * 2;         // [wave][g][row][token] bf16
+  static constexpr int RED = 4 * 2 * GP * kHeadDim * 4;      // [wave][row][ch] fp32
+  static constexpr int MAIN = (QA + PB) > RED ? (QA + PB) : RED;
+  static constexpr int PAGE_IDS = MAIN;                      // int [kMaxPagesPerSplit]
+  static constexpr int RED_M = PAGE_IDS + 4 * kMaxPagesPerSplit;
+  static constexpr int RED_L = RED_M + 4 * 4 * GP;
+  static constexpr int RED_Z = RED_L + 4 * 4 * GP;
+  static constexpr int TOTAL = RED_Z + 4 * 4 * GP * NG;
+};
 
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+template <int G, int NG>
+__device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
+                                           int b, unsigned char* smem) {
+  using S = Int2Lds<G, NG>;
+  constexpr int GP = S::GP;               // padded query heads per KV head
+  constexpr int NACC = GP / 4;            // score accumulators (tokens per lane and page)
+  constexpr int NPL = S::NPL;             // operand placements
+  constexpr int PP = 1;                   // pages per step
+  constexpr int BLK = kMetaOff + kPage * 8 * NG;
+  v4i* qa_lds = reinterpret_cast<v4i*>(smem);
+  __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem + S::QA);
+  float* red_acc = reinterpret_cast<float*>(smem);
+  int* page_ids = reinterpret_cast<int*>(smem + S::PAGE_IDS);
+  float (*red_m)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_M);
+  float (*red_l)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_L);
+  float (*red_z)[GP][NG] = reinterpret_cast<float (*)[GP][NG]>(smem + S::RED_Z);
+
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
@@ -181,10 +197,12 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
     return pbuf_all + ((((wave * PP + pp) * NG + g) * 16 + row) * kPage);
   };
   // rows 2 GP .. 15 of every P tile stay zero (value operands of unused rows)
-  for (int i = lane; i < PP * NG * (16 - 2 * GP) * kPage; i += 64) {
-    const int per = (16 - 2 * GP) * kPage;
-    const int pg2 = i / per, rem = i % per;
-    pbuf(pg2 / NG, pg2 % NG, 2 * GP + rem / kPage)[rem % kPage] = static_cast<__bf16>(0.f);
+  if constexpr (2 * GP < 16) {
+    constexpr int per = (16 - 2 * GP) * kPage;
+    for (int i = lane; i < PP * NG * per; i += 64) {
+      const int pg2 = i / per, rem = i % per;
+      pbuf(pg2 / NG, pg2 % NG, 2 * GP + rem / kPage)[rem % kPage] = static_cast<__bf16>(0.f);
+    }
   }
   __syncthreads();
 
@@ -476,22 +494,31 @@ __global__ __launch_bounds__(256, 2) void int2_kernel(DecodeArgs a, Plan p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. BF16 segments: one 256-thread block per (chunk, kv head, sequence).  Chunk 0 = sink rows
-// 0..63, chunk c >= 1 = recent ring rows 64(c-1) .. 64c-1.  The chunk's key and value rows are
-// staged in LDS with one round of 16-byte loads (rows that hold no cached token are zeroed: their
-// bytes are arbitrary); then thread (token t, head group w) scores heads w, w + 4, ... and thread
-// (channel pair c, head group w) accumulates their values.
-constexpr int kRowPad = kHeadDim + 8;   // bf16 elements per staged row (breaks bank conflicts)
+// 3. BF16 segments: one 256-thread block per (64-token chunk, kv head, sequence), launched in the
+// same grid as the INT2 blocks so the two segment passes run side by side.  Chunk 0 = sink rows
+// 0..63, chunk c >= 1 = recent ring rows 64(c-1) .. 64c-1.  Every global load is issued up front:
+// thread (token t, quarter) holds key row t, channels 32 quarter .. +31, for the scores (summed
+// over the four lanes of a quad); thread (channel pair, wave) holds the value pairs of rows
+// 16 wave .. 16 wave + 15 for the weighted sum.  Rows that hold no cached token count as -inf.
+template <int G>
+struct Bf16Lds {
+  static constexpr int Q = 0;                                // fp32 [G][128]
+  static constexpr int P = Q + G * kHeadDim * 4;             // fp32 [G][64]
+  static constexpr int RM = P + G * kPage * 4;               // fp32 [4][G] wave maxima
+  static constexpr int RL = RM + 4 * G * 4;                  // fp32 [4][G] wave sums
+  static constexpr int RACC = RL + 4 * G * 4;                // fp32 [4][G][128]
+  static constexpr int TOTAL = RACC + 4 * G * kHeadDim * 4;
+};
 
 template <int G>
-__global__ __launch_bounds__(256) void bf16_kernel(DecodeArgs a, Plan p, float scale_log2) {
-  constexpr int HPW = (G + 3) / 4;   // heads per wave
-  __shared__ __attribute__((aligned(16))) uint16_t ks[64][kRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t vsm[64][kRowPad];
-  __shared__ float q_s[G][kHeadDim];
-  __shared__ float p_s[G][64];
-  __shared__ float m_s[G], l_s[G];
-  const int chunk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, float scale_log2,
+                                           int chunk, int kv, int b, unsigned char* smem) {
+  using S = Bf16Lds<G>;
+  float (*q_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(smem + S::Q);
+  float (*p_s)[kPage] = reinterpret_cast<float (*)[kPage]>(smem + S::P);
+  float (*red_m)[G] = reinterpret_cast<float (*)[G]>(smem + S::RM);
+  float (*red_l)[G] = reinterpret_cast<float (*)[G]>(smem + S::RL);
+  float* red_acc = reinterpret_cast<float*>(smem + S::RACC);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
   const int L = a.seq_lens[b];
@@ -499,120 +526,134 @@ __global__ __launch_bounds__(256) void bf16_kernel(DecodeArgs a, Plan p, float s
   const int head0 = b * p.hq + kv * G;
   const int64_t row0 = chunk == 0 ? (slot * p.hkv + kv) * kSink
                                    : (slot * p.hkv + kv) * kRecent + (chunk - 1) * 64;
-  const uint16_t* kb = (chunk == 0 ? a.sink_k : a.recent_k) + row0 * kHeadDim;
-  const uint16_t* vb = (chunk == 0 ? a.sink_v : a.recent_v) + row0 * kHeadDim;
+  const uint16_t* krows = (chunk == 0 ? a.sink_k : a.recent_k) + row0 * kHeadDim;
+  const uint16_t* vrows = (chunk == 0 ? a.sink_v : a.recent_v) + row0 * kHeadDim;
+  const int n_recent = min(kRecent, max(0, L - kSink));
   auto row_valid = [&](int t) {
     if (chunk == 0) return t < min(L, kSink);
     const int r = (chunk - 1) * 64 + t;   // ring row
-    const int n_recent = min(kRecent, max(0, L - kSink));
     const int start = L - n_recent;
     const int posr = start + (((r - start) % kRecent) + kRecent) % kRecent;
     return n_recent > 0 && posr < L;
   };
-  // stage: 64 rows x 16 uint4 per tensor; thread tid takes uint4 c = tid & 15 of rows tid / 16 + 16 i
-  {
-    uint4 kr[4], vr[4];
-    const int c = tid & 15;
+  // ---- loads: key quarter rows, value pairs, query
+  const int t = tid >> 2, qq = tid & 3;
+  const bool kvalid = row_valid(t);
+  uint4 kr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = (tid >> 4) + 16 * i;
-      const bool ok = row_valid(t);
-      kr[i] = ok ? reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(t) * kHeadDim)[c]
-                 : make_uint4(0, 0, 0, 0);
-      vr[i] = ok ? reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(t) * kHeadDim)[c]
-                 : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i)
+    kr[i] = kvalid ? reinterpret_cast<const uint4*>(krows + static_cast<int64_t>(t) * kHeadDim +
+                                                    32 * qq)[i]
+                   : make_uint4(0, 0, 0, 0);
+  uint32_t vr[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = (tid >> 4) + 16 * i;
-      *reinterpret_cast<uint4*>(&ks[t][8 * c]) = kr[i];
-      *reinterpret_cast<uint4*>(&vsm[t][8 * c]) = vr[i];
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int tv = 16 * wave + i;
+    vr[i] = row_valid(tv) ? reinterpret_cast<const uint32_t*>(vrows + static_cast<int64_t>(tv) *
+                                                                         kHeadDim)[lane]
+                          : 0u;
   }
   for (int i = tid; i < G * kHeadDim; i += 256)
     q_s[i / kHeadDim][i % kHeadDim] =
         dev::bf16_to_f32(a.q[static_cast<int64_t>(head0) * kHeadDim + i]);
   __syncthreads();
-  // scores: thread (token lane, wave) for heads wave + 4 j
-  const bool valid = row_valid(lane);
-  float logit[HPW];
+  // ---- scores of token t (the four lanes of a quad share it), softmax statistics per head
+  float logit[G];
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) logit[j] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < kHeadDim / 8; ++c) {
-    const uint4 w = *reinterpret_cast<const uint4*>(&ks[lane][8 * c]);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+    const float* qh = q_s[h] + 32 * qq;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = __uint_as_float(ws[e] << 16);
-      const float hi = __uint_as_float(ws[e] & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        const int h = wave + 4 * j;
-        if (h < G) {
-          logit[j] = fmaf(q_s[h][8 * c + 2 * e], lo, logit[j]);
-          logit[j] = fmaf(q_s[h][8 * c + 2 * e + 1], hi, logit[j]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(qh[8 * i + 2 * e], __uint_as_float(w[e] << 16), acc);
+        acc = fmaf(qh[8 * i + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), acc);
       }
     }
-  }
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int h = wave + 4 * j;
-    if (h < G) {
-      const float lg = valid ? logit[j] * scale_log2 : -INFINITY;
-      const float mh = dev::wave_max(lg);
-      const float pr = (mh == -INFINITY) ? 0.f : exp2f(lg - mh);
-      const float lh = dev::wave_sum(pr);
-      p_s[h][lane] = pr;
-      if (lane == 0) {
-        m_s[h] = mh;
-        l_s[h] = lh;
-      }
-    }
+    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xF, 0xF, 0));
+    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xF, 0xF, 0));
+    logit[h] = kvalid ? acc * scale_log2 : -INFINITY;
+    const float mw = dev::wave_max(logit[h]);
+    if (lane == 0) red_m[wave][h] = mw;
   }
   __syncthreads();
-  // values: thread (channel pair lane, wave) for heads wave + 4 j
-  float acc[HPW][2];
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) acc[j][0] = acc[j][1] = 0.f;
-#pragma unroll 8
-  for (int t = 0; t < 64; ++t) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(&vsm[t][2 * lane]);
-    const float lo = __uint_as_float(w << 16);
-    const float hi = __uint_as_float(w & 0xFFFF0000u);
+  for (int h = 0; h < G; ++h) {
+    const float m = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    const float pr = kvalid ? exp2f(logit[h] - m) : 0.f;
+    if (qq == 0) p_s[h][t] = pr;
+    const float lw = dev::wave_sum(qq == 0 ? pr : 0.f);
+    if (lane == 0) red_l[wave][h] = lw;
+  }
+  __syncthreads();
+  // ---- weighted values: thread (channel pair lane, wave) over rows 16 wave .. 16 wave + 15
+  float acc[G][2];
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int h = wave + 4 * j;
-      if (h < G) {
-        acc[j][0] = fmaf(p_s[h][t], lo, acc[j][0]);
-        acc[j][1] = fmaf(p_s[h][t], hi, acc[j][1]);
-      }
+  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float lo = __uint_as_float(vr[i] << 16);
+    const float hi = __uint_as_float(vr[i] & 0xFFFF0000u);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = p_s[h][16 * wave + i];
+      acc[h][0] = fmaf(pr, lo, acc[h][0]);
+      acc[h][1] = fmaf(pr, hi, acc[h][1]);
     }
   }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    red_acc[(wave * G + h) * kHeadDim + 2 * lane] = acc[h][0];
+    red_acc[(wave * G + h) * kHeadDim + 2 * lane + 1] = acc[h][1];
+  }
+  __syncthreads();
   float* ml = reinterpret_cast<float*>(a.workspace + p.off_bf16_ml);
   float* pacc = reinterpret_cast<float*>(a.workspace + p.off_bf16_acc);
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int h = wave + 4 * j;
-    if (h < G) {
-      const int64_t prow = static_cast<int64_t>(head0 + h) * kBf16Chunks + chunk;
-      pacc[prow * kHeadDim + 2 * lane] = acc[j][0];
-      pacc[prow * kHeadDim + 2 * lane + 1] = acc[j][1];
-      if (lane == 0) {
-        ml[prow * 2] = m_s[h];
-        ml[prow * 2 + 1] = l_s[h];
-      }
+  for (int i = tid; i < G * kHeadDim; i += 256) {
+    const int h = i / kHeadDim, j = i % kHeadDim;
+    const float v = (red_acc[(0 * G + h) * kHeadDim + j] + red_acc[(1 * G + h) * kHeadDim + j]) +
+                    (red_acc[(2 * G + h) * kHeadDim + j] + red_acc[(3 * G + h) * kHeadDim + j]);
+    const int64_t prow = static_cast<int64_t>(head0 + h) * kBf16Chunks + chunk;
+    pacc[prow * kHeadDim + j] = v;
+    if (j == 0) {
+      ml[prow * 2] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+      ml[prow * 2 + 1] = (red_l[0][h] + red_l[1][h]) + (red_l[2][h] + red_l[3][h]);
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. merge: one 256-thread block per (sequence, query head).
-//   (1) weights f_s = 2^(m_s - m) of the INT2 splits (thread s), m and l by block reductions;
+// The segment passes share one launch: blocks x0 + blockIdx.x < kBf16Chunks are BF16 chunks,
+// the rest INT2 splits.
+template <int G, int NG>
+constexpr int attn_lds_bytes() {
+  return Int2Lds<G, NG>::TOTAL > Bf16Lds<G>::TOTAL ? Int2Lds<G, NG>::TOTAL : Bf16Lds<G>::TOTAL;
+}
+
+template <int G, int NG>
+__global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
+                                                      int x0) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
+  const int x = x0 + blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  if (x < kBf16Chunks)
+    bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
+  else
+    int2_block<G, NG>(a, p, x - kBf16Chunks, kv, b, smem);
+}
+
+// ------------------------------------------------------------------------------------------
+// 4. merge: one 256-thread block per (sequence, query head).  Every global load the block needs
+// (split statistics, the first 64 split accumulators, its rows of U_v, the BF16 partials) is
+// issued before the first reduction, so the block pays about one memory latency.
+//   (1) weights f_s = 2^(m_s - m) of the INT2 splits, m and l by block reductions;
 //   (2) acc' = sum_s f_s acc'_s with thread (channel quad, split residue mod 8) partial sums;
-//   (3) acc'P, then the Hadamard butterflies, then times U_v^T / sqrt(d) (two threads per output);
-//   (4) merge with the five BF16 chunk partials and normalise.
+//   (3) (acc' P) H / sqrt(d) by butterflies across one wave, then times U_v^T (two threads per
+//       output channel);
+//   (4) merge with the BF16 chunk partials and normalise.
+constexpr int kMergePrefetch = 8;   // split accumulators per thread loaded up front (64 splits)
+
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ float f_s[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float part[8][kHeadDim];
@@ -623,106 +664,155 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int b = row / p.hq;
   const int kv = (row % p.hq) / p.gqa;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = dev::lane_id();
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
   const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
   const float* iml = reinterpret_cast<const float*>(a.workspace + p.off_int2_ml) +
                      static_cast<int64_t>(row) * p.num_splits * 2;
-  const float* iacc = reinterpret_cast<const float*>(a.workspace + p.off_int2_acc) +
-                      static_cast<int64_t>(row) * p.num_splits * kHeadDim;
+  const float4* iacc = reinterpret_cast<const float4*>(a.workspace + p.off_int2_acc) +
+                       static_cast<int64_t>(row) * p.num_splits * (kHeadDim / 4);
+  const float* bml = reinterpret_cast<const float*>(a.workspace + p.off_bf16_ml) +
+                     static_cast<int64_t>(row) * kBf16Chunks * 2;
+  const float* bacc = reinterpret_cast<const float*>(a.workspace + p.off_bf16_acc) +
+                      static_cast<int64_t>(row) * kBf16Chunks * kHeadDim;
+  const int cq = tid & 31, sr = tid >> 5;     // (2): channel quad, split residue
+  const int oj = tid & 127, oh = tid >> 7;    // (3): output channel, half of the inputs
 
-  // (1) max and weights
-  float mloc = -INFINITY;
-  for (int s = tid; s < n_valid; s += 256) mloc = fmaxf(mloc, iml[2 * s]);
+  // ---- loads
+  float2 st[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = tid + 256 * i;
+    st[i] = s < n_valid ? reinterpret_cast<const float2*>(iml)[s] : make_float2(-INFINITY, 0.f);
+  }
+  float4 pa[kMergePrefetch];
+#pragma unroll
+  for (int i = 0; i < kMergePrefetch; ++i) {
+    const int s = sr + 8 * i;
+    pa[i] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 uv[16];
+  {
+    const float4* u = reinterpret_cast<const float4*>(
+        a.u_v + (static_cast<int64_t>(kv) * kHeadDim + oj) * kHeadDim + oh * 64);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) uv[c] = u[c];
+  }
+  float bm[kBf16Chunks], bl[kBf16Chunks], ba[kBf16Chunks];
+#pragma unroll
+  for (int c = 0; c < kBf16Chunks; ++c) {
+    bm[c] = bml[2 * c];
+    bl[c] = bml[2 * c + 1];
+    ba[c] = bacc[c * kHeadDim + oj];
+  }
+
+  // ---- (1) max and weights of the INT2 splits
+  float mloc = fmaxf(fmaxf(st[0].x, st[1].x), fmaxf(st[2].x, st[3].x));
+  for (int s = tid + 1024; s < n_valid; s += 256) mloc = fmaxf(mloc, iml[2 * s]);
   mloc = dev::wave_max(mloc);
-  if ((tid & 63) == 0) red[tid >> 6] = mloc;
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
   const float mi = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float lloc = 0.f;
-  for (int s = tid; s < n_valid; s += 256) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = tid + 256 * i;
+    if (s < n_valid) {
+      const float f = exp2f(st[i].x - mi);
+      f_s[s] = f;
+      lloc = fmaf(st[i].y, f, lloc);
+    }
+  }
+  for (int s = tid + 1024; s < n_valid; s += 256) {
     const float f = exp2f(iml[2 * s] - mi);
     f_s[s] = f;
     lloc = fmaf(iml[2 * s + 1], f, lloc);
   }
   lloc = dev::wave_sum(lloc);
-  if ((tid & 63) == 0) red[4 + (tid >> 6)] = lloc;
+  if (lane == 0) red[4 + wave] = lloc;
   __syncthreads();
-  const float li = red[4] + red[5] + red[6] + red[7];
-  // (2) weighted sum of the split accumulators
+  const float li = (red[4] + red[5]) + (red[6] + red[7]);
+  // ---- (2) weighted sum of the split accumulators
   {
-    const int cq = tid & 31, sr = tid >> 5;
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = sr; s < n_valid; s += 8) {
-      const float4 v =
-          reinterpret_cast<const float4*>(iacc + static_cast<int64_t>(s) * kHeadDim)[cq];
-      const float f = f_s[s];
+    auto add = [&](const float4& v, float f) {
       s4.x = fmaf(v.x, f, s4.x);
       s4.y = fmaf(v.y, f, s4.y);
       s4.z = fmaf(v.z, f, s4.z);
       s4.w = fmaf(v.w, f, s4.w);
+    };
+#pragma unroll
+    for (int i = 0; i < kMergePrefetch; ++i) {
+      const int s = sr + 8 * i;
+      if (s < n_valid) add(pa[i], f_s[s]);
     }
+    for (int s = sr + 8 * kMergePrefetch; s < n_valid; s += 8)
+      add(iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq], f_s[s]);
     reinterpret_cast<float4*>(part[sr])[cq] = s4;
   }
   __syncthreads();
-  if (tid < kHeadDim) {
-    // (acc' P)_j = acc'_rev(j)
-    const int src = dev::bitrev7(tid);
-    float v = 0.f;
+  // ---- (3) (acc' P) H / sqrt(d) in wave 0: lane holds entries lane and lane + 64
+  if (wave == 0) {
+    auto gather = [&](int j) {
+      const int src = dev::bitrev7(j);   // (acc' P)_j = acc'_rev(j)
+      float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v += part[r][src];
-    vec[tid] = v;
+      for (int r = 0; r < 8; ++r) v += part[r][src];
+      return v;
+    };
+    float y0 = gather(lane), y1 = gather(lane + 64);
+    {
+      const float t0 = y0 + y1, t1 = y0 - y1;
+      y0 = t0;
+      y1 = t1;
+    }
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+      const bool upper = (lane & h) != 0;
+      const float p0 = __shfl_xor(y0, h);
+      const float p1 = __shfl_xor(y1, h);
+      y0 = upper ? (p0 - y0) : (y0 + p0);
+      y1 = upper ? (p1 - y1) : (y1 + p1);
+    }
+    vec[lane] = y0;
+    vec[lane + 64] = y1;
   }
   __syncthreads();
-  // (3) Hadamard butterflies, then U_v^T / sqrt(d)
-  for (int hs = 1; hs < kHeadDim; hs <<= 1) {
-    if (tid < 64) {
-      const int i = (tid / hs) * 2 * hs + (tid % hs);
-      const float x = vec[i], y = vec[i + hs];
-      vec[i] = x + y;
-      vec[i + hs] = x - y;
-    }
-    __syncthreads();
-  }
   {
-    const int j = tid & 127, half = tid >> 7;
-    const float4* u = reinterpret_cast<const float4*>(
-        a.u_v + (static_cast<int64_t>(kv) * kHeadDim + j) * kHeadDim + half * 64);
     float o = 0.f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const float4 w = u[c];
-      const int i = half * 64 + 4 * c;
-      o = fmaf(vec[i], w.x, o);
-      o = fmaf(vec[i + 1], w.y, o);
-      o = fmaf(vec[i + 2], w.z, o);
-      o = fmaf(vec[i + 3], w.w, o);
+      const int i = oh * 64 + 4 * c;
+      o = fmaf(vec[i], uv[c].x, o);
+      o = fmaf(vec[i + 1], uv[c].y, o);
+      o = fmaf(vec[i + 2], uv[c].z, o);
+      o = fmaf(vec[i + 3], uv[c].w, o);
     }
-    outp[half][j] = o;
+    outp[oh][oj] = o;
   }
   __syncthreads();
-  // (4) merge with the BF16 partials
+  // ---- (4) merge with the BF16 partials
   if (tid < kHeadDim) {
     const int j = tid;
-    const float* bml = reinterpret_cast<const float*>(a.workspace + p.off_bf16_ml) +
-                       static_cast<int64_t>(row) * kBf16Chunks * 2;
-    const float* bacc = reinterpret_cast<const float*>(a.workspace + p.off_bf16_acc) +
-                        static_cast<int64_t>(row) * kBf16Chunks * kHeadDim;
     const float m_int2 = n_valid > 0 ? mi : -INFINITY;
     float mt = m_int2;
-    for (int c = 0; c < kBf16Chunks; ++c) mt = fmaxf(mt, bml[2 * c]);
+#pragma unroll
+    for (int c = 0; c < kBf16Chunks; ++c) mt = fmaxf(mt, bm[c]);
     float acc = 0.f, l = 0.f;
     if (m_int2 != -INFINITY) {
       const float f = exp2f(m_int2 - mt);
       acc = (outp[0][j] + outp[1][j]) * 0.08838834764831845f * f;
       l = li * f;
     }
+#pragma unroll
     for (int c = 0; c < kBf16Chunks; ++c) {
-      const float mc = bml[2 * c];
-      if (mc == -INFINITY) continue;
-      const float f = exp2f(mc - mt);
-      acc = fmaf(bacc[c * kHeadDim + j], f, acc);
-      l = fmaf(bml[2 * c + 1], f, l);
+      if (bm[c] == -INFINITY) continue;
+      const float f = exp2f(bm[c] - mt);
+      acc = fmaf(ba[c], f, acc);
+      l = fmaf(bl[c], f, l);
     }
     a.out[static_cast<int64_t>(row) * kHeadDim + j] = acc / l;
     if (a.lse != nullptr && j == 0) a.lse[row] = (mt + log2f(l)) * 0.6931471805599453f;
@@ -732,16 +822,15 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStream_t stream) {
   const float scale_log2 = a.sm_scale * kLog2e;
-  if ((stages & OSCAR_STAGE_INT2) && p.max_pages > 0) {
-    dim3 grid(p.num_splits, p.hkv, p.batch);
+  const int x0 = (stages & OSCAR_STAGE_BF16) ? 0 : kBf16Chunks;
+  const int x1 = kBf16Chunks + ((stages & OSCAR_STAGE_INT2) ? p.num_splits : 0);
+  if (x1 > x0) {
+    dim3 grid(x1 - x0, p.hkv, p.batch);
     if (p.n_groups == 1)
-      hipLaunchKernelGGL((int2_kernel<G, 1>), grid, dim3(256), 0, stream, a, p);
+      hipLaunchKernelGGL((attn_kernel<G, 1>), grid, dim3(256), 0, stream, a, p, scale_log2, x0);
     else
-      hipLaunchKernelGGL((int2_kernel<G, 2>), grid, dim3(256), 0, stream, a, p);
+      hipLaunchKernelGGL((attn_kernel<G, 2>), grid, dim3(256), 0, stream, a, p, scale_log2, x0);
   }
-  if (stages & OSCAR_STAGE_BF16)
-    hipLaunchKernelGGL((bf16_kernel<G>), dim3(kBf16Chunks, p.hkv, p.batch), dim3(256), 0, stream,
-                       a, p, scale_log2);
   if (stages & OSCAR_STAGE_MERGE)
     hipLaunchKernelGGL(merge_kernel, dim3(p.batch * p.hq), dim3(256), 0, stream, a, p);
   return hipGetLastError();

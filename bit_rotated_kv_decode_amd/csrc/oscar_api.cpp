@@ -73,10 +73,14 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for one round of work items over the compute units (kInt2Items resident at once) with
-  // at least one page per wave, within the per-item page and per-head item limits of the kernels.
+  // Aim for one round of blocks over the compute units: the INT2 work items share the launch
+  // with the BF16 chunk blocks, and kernels with more registers per lane hold fewer blocks per
+  // compute unit.  At least one page per wave, within the per-item page and per-head item limits.
+  const long long slots = p.gqa == 8 ? kInt2Items * 2 / 3 : kInt2Items;
+  const long long bf16_blocks = static_cast<long long>(kBf16Chunks) * batch * p.hkv;
+  const long long target = bf16_blocks * 2 <= slots ? slots - bf16_blocks : slots;
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
-  long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
+  long long pps = std::max<long long>(4, (items + target - 1) / target);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
