@@ -7,16 +7,16 @@ tokens per layer, history in 64-token pages placed through a seeded shuffled pag
 and values N(0,1) bf16 with one outlier channel (x16) per layer, head and tensor, U from the QR
 of a seeded Gaussian, clip 4.0, group 128.  Inputs are synthetic (no model weights).
 
-One step = for each of the 36 layers: oscar_append (write the new token into the BF16 recent
-window and demote the displaced token into the INT2 history) and oscar_decode_attn (query
-rotation, INT2 split-KV pass, BF16 sink/recent pass, merge and un-rotation).  The 36-layer step
-is captured once in a HIP graph and replayed; 36 distinct layer pools (2.1 GB) are cycled, so
-the 256 MB Infinity Cache cannot hold the timed data.
+One step = oscar_decode_step for each of the 36 layers: write the new token into the BF16 recent
+window, demote the displaced token into the INT2 history and rotate the query (one launch), the
+INT2 split-KV pass with the BF16 sink/recent pass (one launch), merge and un-rotation (one
+launch).  The 36-layer step is captured once in a HIP graph and replayed; 36 distinct layer
+pools (2.1 GB) are cycled, so the 256 MB Infinity Cache cannot hold the timed data.
 
 Prints one JSON line: value = effective HBM GB/s of the whole decode step (algorithmic bytes of
-all 36 layers / step time); decode_steps_per_s; roofline of the INT2 decode kernel timed with
-events on its stream inside the timed region; cpu_baseline = the CPU oracle timed on one KV head
-of one layer and scaled.
+all 36 layers / step time); decode_steps_per_s; roofline of the segment-pass kernel (the
+dominant one) timed with events on its stream; cpu_baseline = the CPU oracle timed on one KV
+head of one layer and scaled.
 """
 from __future__ import annotations
 
@@ -117,7 +117,6 @@ def main():
     print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
 
     pos = torch.full((1,), L0, dtype=torch.int32, device=dev)      # position of the new token
-    lens = torch.full((1,), L0 + 1, dtype=torch.int32, device=dev)  # length seen by attention
     slots = torch.zeros(1, dtype=torch.int32, device=dev)
     max_len = L0 + total_steps + 4
     ws = torch.empty(ok.decode_workspace_bytes(layers[0].lay, 1, max_len), dtype=torch.uint8,
@@ -126,26 +125,26 @@ def main():
     def step():
         for Lr in layers:
             c = Lr.cache
-            ok.append(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
-                      Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos)
-            ok.decode_attn(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
-                           slots, lens, Lr.q, Lr.u_k, Lr.u_v, Lr.out, ws, max_len)
+            ok.decode_step(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                           Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos,
+                           Lr.q, Lr.out, ws, max_len)
         pos.add_(1)
-        lens.add_(1)
 
-    graph = None
-    if not args.no_graph:
+    def capture(fn):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            step()                                    # warm-up outside capture
+            fn()                                      # warm-up outside capture
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
         torch.cuda.synchronize()
-    else:
+        return g
+
+    graph = None if args.no_graph else capture(step)
+    if graph is None:
         step()
         step()
 
@@ -167,32 +166,42 @@ def main():
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
 
-    # ---- timed region 2: the INT2 decode kernel alone, every layer, args.steps rounds.  Each
-    # launch is bracketed by events on its own stream; a short GPU spin before the first event
-    # keeps the GPU behind the host, so the events time the kernel and not host launch latency.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in layers]
-    int2_ms = []
+    # ---- timed region 2: the segment-pass kernel (INT2 history + BF16 sink / recent blocks in
+    # one launch) exactly as a step launches it, once per layer pool: a graph of n_layers launches
+    # replayed args.steps times, HIP events around each replay on the launch stream.  Each layer
+    # gets its own workspace holding its rotated query.
+    lens = pos + 1
+    seg = ok.STAGE_INT2 | ok.STAGE_BF16
+    wss = [torch.empty_like(ws) for _ in layers]
+
+    def seg_args(i):
+        Lr = layers[i]
+        c = Lr.cache
+        return (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v, slots, lens,
+                Lr.q, Lr.u_k, Lr.u_v, Lr.out, wss[i], max_len)
+
+    for i in range(len(layers)):
+        ok.decode_attn(*seg_args(i), stages=ok.STAGE_QUERY)
+
+    def seg_launches():
+        for i in range(len(layers)):
+            ok.decode_attn(*seg_args(i), stages=seg)
+
+    seg_graph = capture(seg_launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    seg_us = []
     for _ in range(args.steps):
-        for i, Lr in enumerate(layers):
-            c = Lr.cache
-            common = (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
-                      slots, lens, Lr.q, Lr.u_k, Lr.u_v, Lr.out, ws, max_len)
-            torch.cuda._sleep(20000)
-            ok.decode_attn(*common, stages=ok.STAGE_QUERY)
-            ev[i][0].record()
-            ok.decode_attn(*common, stages=ok.STAGE_INT2)
-            ev[i][1].record()
+        e0.record()
+        seg_graph.replay()
+        e1.record()
         torch.cuda.synchronize()
-        int2_ms += [a.elapsed_time(b) for a, b in ev]
+        seg_us.append(e0.elapsed_time(e1) * 1e3 / len(layers))
 
     # algorithmic bytes of the timed steps
     hkv, hq = wl.num_kv_heads, wl.num_q_heads
     bpt = bytes_per_token_head(wl.group_size)
     bf16_seg = hkv * 320 * 128 * 2 * 2
     att_bytes = 0
-    int2_bytes_last = 0
-    L_int2 = int(lens.item())                         # length seen by the INT2-only region
     for s_ in range(args.steps):
         L = L0 + steps_before + s_ + 1                  # length seen by attention
         n_hist = L - 320
@@ -200,12 +209,14 @@ def main():
         att = hkv * n_hist * bpt + n_pages * 4 + bf16_seg + hq * 128 * 2 + hq * 128 * 4
         append = hkv * 128 * 2 * 2 * 3 + hkv * bpt
         att_bytes += n_layers * (att + append)
-    n_hist = L_int2 - 320
-    int2_bytes_last = hkv * n_hist * bpt + math.ceil(n_hist / 64) * 4 + hq * 128 * 4
+    L_seg = int(lens.item())
+    n_hist = L_seg - 320
+    seg_bytes = (hkv * n_hist * bpt + math.ceil(n_hist / 64) * 4 + hq * 256 + bf16_seg +
+                 hq * 128 * 2)
     step_bytes = att_bytes / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    int2_ms_avg = float(np.mean(int2_ms))
-    achieved = int2_bytes_last / (int2_ms_avg * 1e-3) / 1e9
+    seg_us_avg = float(np.mean(seg_us))
+    achieved = seg_bytes / (seg_us_avg * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -228,13 +239,13 @@ def main():
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_bytes": int(step_bytes),
-        "roofline": {"kernel": "int2_kernel (INT2 split-KV decode)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(int2_bytes_last),
-                     "avg_launch_us": round(int2_ms_avg * 1e3, 3),
-                     "timing": f"HIP events on the launch stream around each INT2 launch, "
-                               f"{args.steps} rounds x {n_layers} layer pools, GPU-paced"},
+        "roofline": {"kernel": "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(seg_bytes),
+                     "avg_launch_us": round(seg_us_avg, 3),
+                     "timing": f"HIP events around {args.steps} replays of a graph of "
+                               f"{n_layers} launches (one per layer pool), per-launch mean"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], L0)

@@ -80,6 +80,9 @@ _SIGNATURES = {
     "oscar_decode_attn_stages": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
                                         _i32, _i32, ctypes.c_uint32, _vp]),
+    "oscar_decode_step": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
+                                 _i32, _i32, _vp]),
 }
 
 STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
@@ -233,6 +236,32 @@ def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
         int(stages), _stream()), "decode_attn")
+
+
+def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
+                clip_k, clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot, seq_pos,
+                q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
+                lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0) -> None:
+    """append(k_new, v_new at seq_pos) then decode_attn(q) over seq_pos + 1 tokens, in three
+    launches (oscar_decode_step); the caller advances seq_pos afterwards."""
+    bsz = seq_pos.numel()
+    if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
+        raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _check(lib().oscar_decode_step(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
+        _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
+        _contig(clip_v, "clip_v", torch.float32), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_pos, "seq_pos", torch.int32), _contig(q, "q", torch.bfloat16),
+        float(sm_scale), _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        _stream()), "decode_step")
 
 
 @dataclasses.dataclass

@@ -2,17 +2,16 @@
 //
 // Structure after the OSCAR write-up "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化",
 // section OSCAR 的设计: the INT2 history and the BF16 segments are processed separately and then
-// combined with an online-softmax merge.  Launch order on one stream:
-//   1. query_kernel  q' = q R_k per query head (fp64 rotation), quantised for the INT2 pass into
-//                    int8 hi / lo parts (q' ~ a (hi + lo / 256)) laid out as MFMA operands, plus
-//                    the per-group sums of the quantised q' that the zero points multiply;
-//   2. attn_kernel   both segment passes in one grid:
+// combined with an online-softmax merge.  Launch order on one stream (after the preparation
+// launch of encode.hip, which rotates the query and splits it into the int8 hi / lo MFMA
+// operands q' ~ a (hi + lo / 256) plus the per-group sums of the quantised q'):
+//   1. attn_kernel   both segment passes in one grid:
 //                    INT2 blocks: split-KV over history pages on the matrix cores: scores
 //                    s (q' . codes) + z sum(q') with the dot products as exact int32 i8 MFMAs,
 //                    online softmax with lazy rescaling, value accumulation in the rotated frame
 //                    as bf16 MFMAs -> (m, l, acc') partials;
 //                    BF16 blocks: 64-token chunks of the BF16 sink and recent ring -> (m, l, acc);
-//   3. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
+//   2. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
 //                    the BF16 partials, normalisation.
 // Softmax statistics are kept in the log2 domain: scores are scaled by sm_scale * log2(e).
 #include "device_common.h"
@@ -28,63 +27,6 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 8.0f;   // lazy rescaling: exponents up to 2^8 before the max is moved
-
-// ------------------------------------------------------------------------------------------
-// 1. query preparation: one 256-thread block per (sequence, query head)
-__global__ __launch_bounds__(256) void query_kernel(const uint16_t* __restrict__ q,
-                                                    const float* __restrict__ u_k, int hq,
-                                                    int gqa, int n_groups, float scale_log2,
-                                                    int8_t* __restrict__ qpack,
-                                                    float* __restrict__ qmeta) {
-  __shared__ float x[kHeadDim];
-  __shared__ double red[4][kHeadDim];
-  const int row = blockIdx.x;   // b * hq + head
-  const int kv = (row % hq) / gqa;
-  if (threadIdx.x < kHeadDim)
-    x[threadIdx.x] = dev::bf16_to_f32(q[static_cast<int64_t>(row) * kHeadDim + threadIdx.x]);
-  __syncthreads();
-  double r0, r1;
-  const bool lead = dev::rotate1_block(x, u_k + static_cast<int64_t>(kv) * kHeadDim * kHeadDim,
-                                       red, r0, r1);
-  if (!lead) return;
-  const int lane = dev::lane_id();
-  const float f0 = static_cast<float>(r0);   // rotated channel lane
-  const float f1 = static_cast<float>(r1);   // rotated channel lane + 64
-  const float amax = dev::wave_max(fmaxf(fabsf(f0), fabsf(f1)));
-  const float a = amax > 0.f ? amax / 127.f : 1.f;
-  auto split = [a](float v, int& hi, int& lo) {
-    hi = static_cast<int>(rintf(v / a));
-    const float r = fmaf(-static_cast<float>(hi), a, v);
-    lo = static_cast<int>(fminf(fmaxf(rintf(r * 256.f / a), -127.f), 127.f));
-  };
-  int h0, l0, h1, l1;
-  split(f0, h0, l0);
-  split(f1, h1, l1);
-  // MFMA operand order: channel j = 16 qd + 4 b + k sits at byte 16 qd + 4 k + b
-  auto pos = [](int j) { return (j >> 4) * 16 + (j & 3) * 4 + ((j >> 2) & 3); };
-  int8_t* dst = qpack + static_cast<int64_t>(row) * 256;
-  dst[pos(lane)] = static_cast<int8_t>(h0);
-  dst[pos(lane + 64)] = static_cast<int8_t>(h1);
-  dst[128 + pos(lane)] = static_cast<int8_t>(l0);
-  dst[128 + pos(lane + 64)] = static_cast<int8_t>(l1);
-  // sums of the quantised q' per group, in units of a / 256 (exact in int32)
-  const int e0 = 256 * h0 + l0, e1 = 256 * h1 + l1;
-  int s0, s1;
-  if (n_groups == 1) {
-    s0 = dev::wave_sum_i(e0 + e1);
-    s1 = 0;
-  } else {
-    s0 = dev::wave_sum_i(e0);
-    s1 = dev::wave_sum_i(e1);
-  }
-  if (lane == 0) {
-    float* m = qmeta + static_cast<int64_t>(row) * 4;
-    m[0] = a / 256.f * scale_log2;
-    m[1] = static_cast<float>(s0);
-    m[2] = static_cast<float>(s1);
-    m[3] = 0.f;
-  }
-}
 
 // FP4 (E2M1) pair in byte B of x -> two bf16; a 2-bit code zero-extended to a nibble encodes
 // code / 2, so the scale 2 gives the code itself.
@@ -145,7 +87,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   float (*red_l)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_L);
   float (*red_z)[GP][NG] = reinterpret_cast<float (*)[GP][NG]>(smem + S::RED_Z);
 
-  const int L = a.seq_lens[b];
+  const int L = a.seq_lens[b] + a.len_add;
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
   const int p0 = split * p.pages_per_split;
@@ -521,7 +463,7 @@ __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, f
   float* red_acc = reinterpret_cast<float*>(smem + S::RACC);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
-  const int L = a.seq_lens[b];
+  const int L = a.seq_lens[b] + a.len_add;
   const int64_t slot = a.seq_slot[b];
   const int head0 = b * p.hq + kv * G;
   const int64_t row0 = chunk == 0 ? (slot * p.hkv + kv) * kSink
@@ -665,7 +607,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int kv = (row % p.hq) / p.gqa;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
-  const int L = a.seq_lens[b];
+  const int L = a.seq_lens[b] + a.len_add;
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
   const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
@@ -841,12 +783,6 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
 hipError_t launch_decode(const DecodeArgs& a, const Plan& p, uint32_t stages,
                          hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
-  if (stages & OSCAR_STAGE_QUERY) {
-    int8_t* qpack = reinterpret_cast<int8_t*>(a.workspace + p.off_qrot);
-    float* qmeta = reinterpret_cast<float*>(a.workspace + p.off_sigma);
-    hipLaunchKernelGGL(query_kernel, dim3(p.batch * p.hq), dim3(256), 0, stream, a.q, a.u_k, p.hq,
-                       p.gqa, p.n_groups, a.sm_scale * kLog2e, qpack, qmeta);
-  }
   switch (p.gqa) {
     case 1: return launch_g<1>(a, p, stages, stream);
     case 2: return launch_g<2>(a, p, stages, stream);

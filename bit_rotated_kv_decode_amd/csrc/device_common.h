@@ -101,21 +101,37 @@ __device__ __forceinline__ void hadamard_bitrev(double y0, double y1, double& o0
 }
 
 // Rotation of one row vector x (fp32 in LDS, 128 entries) by R = U H P / sqrt(128) in fp64 by a
-// whole 256-thread block: wave w accumulates rows [32w, 32w + 32) of x U with all its U loads in
-// flight at once, wave 0 adds the four partial vectors (staged in `red`) and finishes with the
-// Hadamard and the bit reversal.  Every thread of the block must call this (it contains a block
-// barrier); it returns true in wave 0, whose lane l then holds rotated channels l and l + 64.
-__device__ __forceinline__ bool rotate1_block(const float* x, const float* __restrict__ u,
+// whole 256-thread block: wave w accumulates rows [32w, 32w + 32) of x U, wave 0 adds the four
+// partial vectors (staged in `red`) and finishes with the Hadamard and the bit reversal.  The U
+// entries a thread needs are loaded into registers first (load_u_rows), so the loads can be in
+// flight while x is still being staged.  Every thread of the block must call rotate1_block (it
+// contains a block barrier); it returns true in wave 0, whose lane l then holds rotated channels
+// l and l + 64.
+struct URows {
+  float v[32][2];   // U[32 w + k][lane], U[32 w + k][lane + 64]
+};
+
+__device__ __forceinline__ void load_u_rows(const float* __restrict__ u, URows& r) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int i = wave * 32 + k;
+    r.v[k][0] = u[i * 128 + lane];
+    r.v[k][1] = u[i * 128 + lane + 64];
+  }
+}
+
+__device__ __forceinline__ bool rotate1_block(const float* x, const URows& ur,
                                               double (*red)[128], double& o0, double& o1) {
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   double y0 = 0.0, y1 = 0.0;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const int i = wave * 32 + k;
-    const double xi = static_cast<double>(x[i]);
-    y0 = fma(xi, static_cast<double>(u[i * 128 + lane]), y0);
-    y1 = fma(xi, static_cast<double>(u[i * 128 + lane + 64]), y1);
+    const double xi = static_cast<double>(x[wave * 32 + k]);
+    y0 = fma(xi, static_cast<double>(ur.v[k][0]), y0);
+    y1 = fma(xi, static_cast<double>(ur.v[k][1]), y1);
   }
   red[wave][lane] = y0;
   red[wave][lane + 64] = y1;

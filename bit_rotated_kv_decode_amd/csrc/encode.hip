@@ -1,13 +1,16 @@
-// Demotion of keys / values into the rotated INT2 history, and the decode-step append.
+// Everything that rotates and encodes: bulk demotion of keys / values into the rotated INT2
+// history, and the per-step preparation launch (the decode-step append with the demotion of the
+// token that leaves the recent window, and the query rotation for the INT2 pass).
 //
 // The steps follow the OSCAR write-up "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化",
 // section OSCAR 的设计: the token leaving the BF16 recent window is rotated by R = U * Hadamard *
 // bit-reversal, clipped, quantised with a per-group scale and zero point and packed four 2-bit
-// codes to a byte.  One 64-lane wave encodes one (token, KV head, K|V) vector: lane l owns rotated
-// channels l and l + 64.  The rotation runs in fp64 (x U as a matrix-vector product, the Hadamard
-// as cross-lane butterflies), the rotated vector is rounded once to fp32 and every step that
-// decides a code (clip, group min / max, (max - min) / 3, fp16 rounding, (x - z) / s, rint) runs
-// in IEEE fp32.
+// codes to a byte; the query is rotated by the same R_k so that scores can be taken against the
+// stored rotated keys.  One 64-lane wave encodes one (token, KV head, K|V) vector: lane l owns
+// rotated channels l and l + 64.  The rotation runs in fp64 (x U as a matrix-vector product, the
+// Hadamard as cross-lane butterflies), the rotated vector is rounded once to fp32 and every step
+// that decides a code (clip, group min / max, (max - min) / 3, fp16 rounding, (x - z) / s, rint)
+// runs in IEEE fp32.
 #include "device_common.h"
 #include "oscar_internal.h"
 
@@ -192,16 +195,29 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode-step append: one 256-thread block per (sequence, KV head, K|V).  The displaced ring
-// row is staged in LDS, rotated by the whole block (rotate1_block), quantised and stored by wave
-// 0; the ring row is then overwritten with the new token.
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  __shared__ float x[kHeadDim];
-  __shared__ double red[4][kHeadDim];
+// Step preparation: one 256-thread block per work item.  Items [0, n_query) rotate one query
+// row each (sequence b, query head); the following batch * hkv * 2 items append one new token
+// per (sequence, KV head, K|V).  Both kinds start their U loads before anything else.
+//
+// Append: the token at position pos goes to the sink (pos < 64) or to ring row pos % 256; once
+// the ring is full the row's previous token (position pos - 256, history index pos - 320) is
+// first rotated, quantised and stored in its page slot.  Waves 2 and 3 overwrite the ring row
+// after the old row is staged; wave 0 quantises and stores.  The value-code bits of the slot are
+// replaced with a pair of no-return atomics (and, then or), which needs no read: no other writer
+// touches the word during the launch, since a sequence appends one token per call and a page is
+// written by its own sequence only.
+//
+// Query: q' = q R_k for the row's KV head, split for the INT2 pass into int8 hi / lo parts
+// (q' ~ a (hi + lo / 256), a = max |q'| / 127) stored in MFMA operand order, and per row the
+// score scale a / 256 * sm_scale * log2(e) and the per-group sums of the quantised q' (exact, in
+// units of a / 256) that the zero points multiply.
+__device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsigned char* smem) {
+  float* x = reinterpret_cast<float*>(smem);
+  double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(smem + 4 * kHeadDim);
   const int tid = threadIdx.x;
-  const int tensor = blockIdx.x & 1;
-  const int h = (blockIdx.x >> 1) % a.hkv;
-  const int b = (blockIdx.x >> 1) / a.hkv;
+  const int tensor = item & 1;
+  const int h = (item >> 1) % a.hkv;
+  const int b = (item >> 1) / a.hkv;
   const int pos = a.seq_lens[b];
   const int64_t slot = a.seq_slot[b];
   const uint16_t* nw = (tensor == 0 ? a.k_new : a.v_new) +
@@ -216,34 +232,102 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   uint16_t* ring = (tensor == 0 ? a.recent_k : a.recent_v) +
                    ((slot * a.hkv + h) * kRecent + pos % kRecent) * kHeadDim;
-  if (pos >= kSink + kRecent) {
-    if (tid < kHeadDim) x[tid] = dev::bf16_to_f32(ring[tid]);
-    __syncthreads();
-    const float* u = (tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim;
-    double r0, r1;
-    // the block barrier inside orders every read of the old row before the overwrite below
-    if (dev::rotate1_block(x, u, red, r0, r1)) {
-      const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
-      const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups);
-      const int idx = pos - kSink - kRecent;
-      const int blk_bytes = block_bytes(a.n_groups);
-      uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
-                                blk_bytes);
-      const int slot_in_page = idx % kPage;
-      const int lane = dev::lane_id();
-      if (tensor == 0) {
-        store_key_row(blk, slot_in_page, q.c0, q.c1);
-      } else {
-        uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-        const int u = slot_in_page / 16;
-        const int sh = 2 * (slot_in_page % 16);
-        merge_bits(&vc[v_word_index(lane, u)], 3u << sh, q.c0 << sh);
-        merge_bits(&vc[v_word_index(lane + 64, u)], 3u << sh, q.c1 << sh);
-      }
-      store_meta(blk, tensor, slot_in_page, a.n_groups, q);
-    }
+  const uint16_t nv = tid >= 128 ? nw[tid - 128] : 0;
+  if (pos < kSink + kRecent) {
+    if (tid >= 128) ring[tid - 128] = nv;
+    return;
   }
-  if (tid < kHeadDim) ring[tid] = nw[tid];
+  dev::URows ur;
+  dev::load_u_rows((tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim,
+                   ur);
+  if (tid < kHeadDim) x[tid] = dev::bf16_to_f32(ring[tid]);
+  __syncthreads();   // the old row is staged: waves 2 and 3 may overwrite it
+  if (tid >= 128) ring[tid - 128] = nv;
+  double r0, r1;
+  if (dev::rotate1_block(x, ur, red, r0, r1)) {
+    const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+    const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups);
+    const int idx = pos - kSink - kRecent;
+    uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
+                              block_bytes(a.n_groups));
+    const int slot_in_page = idx % kPage;
+    const int lane = dev::lane_id();
+    if (tensor == 0) {
+      store_key_row(blk, slot_in_page, q.c0, q.c1);
+    } else {
+      uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
+      const int u = slot_in_page / 16;
+      const int sh = 2 * (slot_in_page % 16);
+      uint32_t* w0 = &vc[v_word_index(lane, u)];
+      uint32_t* w1 = &vc[v_word_index(lane + 64, u)];
+      __hip_atomic_fetch_and(w0, ~(3u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_and(w1, ~(3u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(w0, q.c0 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(w1, q.c1 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_meta(blk, tensor, slot_in_page, a.n_groups, q);
+  }
+}
+
+__device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned char* smem) {
+  float* x = reinterpret_cast<float*>(smem);
+  double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(smem + 4 * kHeadDim);
+  const int kv = (row % a.hq) / a.gqa;
+  dev::URows ur;
+  dev::load_u_rows(a.u_k + static_cast<int64_t>(kv) * kHeadDim * kHeadDim, ur);
+  if (threadIdx.x < kHeadDim)
+    x[threadIdx.x] = dev::bf16_to_f32(a.q[static_cast<int64_t>(row) * kHeadDim + threadIdx.x]);
+  __syncthreads();
+  double r0, r1;
+  if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
+  const int lane = dev::lane_id();
+  const float f0 = static_cast<float>(r0);   // rotated channel lane
+  const float f1 = static_cast<float>(r1);   // rotated channel lane + 64
+  const float amax = dev::wave_max(fmaxf(fabsf(f0), fabsf(f1)));
+  const float sa = amax > 0.f ? amax / 127.f : 1.f;
+  auto split = [sa](float v, int& hi, int& lo) {
+    hi = static_cast<int>(rintf(v / sa));
+    const float r = fmaf(-static_cast<float>(hi), sa, v);
+    lo = static_cast<int>(fminf(fmaxf(rintf(r * 256.f / sa), -127.f), 127.f));
+  };
+  int h0, l0, h1, l1;
+  split(f0, h0, l0);
+  split(f1, h1, l1);
+  // MFMA operand order: channel j = 16 qd + 4 b + k sits at byte 16 qd + 4 k + b
+  auto opos = [](int j) { return (j >> 4) * 16 + (j & 3) * 4 + ((j >> 2) & 3); };
+  int8_t* dst = a.qpack + static_cast<int64_t>(row) * 256;
+  dst[opos(lane)] = static_cast<int8_t>(h0);
+  dst[opos(lane + 64)] = static_cast<int8_t>(h1);
+  dst[128 + opos(lane)] = static_cast<int8_t>(l0);
+  dst[128 + opos(lane + 64)] = static_cast<int8_t>(l1);
+  // sums of the quantised q' per group, in units of a / 256 (exact in int32)
+  const int e0 = 256 * h0 + l0, e1 = 256 * h1 + l1;
+  int s0, s1;
+  if (a.n_groups == 1) {
+    s0 = dev::wave_sum_i(e0 + e1);
+    s1 = 0;
+  } else {
+    s0 = dev::wave_sum_i(e0);
+    s1 = dev::wave_sum_i(e1);
+  }
+  if (lane == 0) {
+    float* m = a.qmeta + static_cast<int64_t>(row) * 4;
+    m[0] = sa / 256.f * a.scale_log2;
+    m[1] = static_cast<float>(s0);
+    m[2] = static_cast<float>(s1);
+    m[3] = 0.f;
+  }
+}
+
+// x0 + blockIdx.x < n_query: query row; else append item x0 + blockIdx.x - n_query.
+__global__ __launch_bounds__(256) void prep_kernel(AppendArgs ap, QueryArgs qa, int n_query,
+                                                   int x0) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kHeadDim + 4 * 8 * kHeadDim];
+  const int item = x0 + blockIdx.x;
+  if (item < n_query)
+    query_item(qa, item, smem);
+  else
+    append_item(ap, item - n_query, smem);
 }
 
 }  // namespace
@@ -258,10 +342,16 @@ hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(a.batch * a.hkv * 2)), dim3(256), 0,
-                     stream, a);
+hipError_t launch_prep(const AppendArgs* ap, const QueryArgs* qa, hipStream_t stream) {
+  const int n_query = qa ? qa->batch * qa->hq : 0;
+  const int n_append = ap ? ap->batch * ap->hkv * 2 : 0;
+  const int x0 = qa ? 0 : n_query;
+  const int n = n_query + n_append - x0;
+  if (n == 0) return hipSuccess;
+  const AppendArgs a0 = ap ? *ap : AppendArgs{};
+  const QueryArgs q0 = qa ? *qa : QueryArgs{};
+  hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(n)), dim3(256), 0, stream, a0, q0,
+                     n_query, x0);
   return hipGetLastError();
 }
 

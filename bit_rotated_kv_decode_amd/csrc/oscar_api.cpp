@@ -105,6 +105,112 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
 
 }  // namespace oscar
 
+namespace {
+
+oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* page_table,
+                              void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                              const float* u_k, const float* u_v, const float* clip_k,
+                              const float* clip_v, const void* k_new, const void* v_new,
+                              const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
+                              oscar::AppendArgs& a) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (batch == 0) return ok();
+  if (l->max_seqs == 0) return fail(OSCAR_ERR_SHAPE, "layout has no sequence slots");
+  if (!pool || !page_table || !sink_k || !sink_v || !recent_k || !recent_v || !u_k || !u_v ||
+      !clip_k || !clip_v || !k_new || !v_new || !seq_slot || !seq_lens)
+    return fail(OSCAR_ERR_NULL, "append: a required pointer is NULL");
+  if (!aligned(pool, 16) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
+      !aligned(recent_k, 16) || !aligned(recent_v, 16))
+    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
+      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(seq_slot, 4) ||
+      !aligned(seq_lens, 4) || !aligned(page_table, 4))
+    return fail(OSCAR_ERR_ALIGN, "append: misaligned pointer");
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.hkv = l->num_kv_heads;
+  a.n_groups = n_groups(l);
+  a.sink_k = static_cast<uint16_t*>(sink_k);
+  a.sink_v = static_cast<uint16_t*>(sink_v);
+  a.recent_k = static_cast<uint16_t*>(recent_k);
+  a.recent_v = static_cast<uint16_t*>(recent_v);
+  a.u_k = u_k;
+  a.u_v = u_v;
+  a.clip_k = clip_k;
+  a.clip_v = clip_v;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seq_slot = seq_slot;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  return ok();
+}
+
+oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int32_t* page_table,
+                              const void* sink_k, const void* sink_v, const void* recent_k,
+                              const void* recent_v, const int32_t* seq_slot,
+                              const int32_t* seq_lens, const void* q, const float* u_k,
+                              const float* u_v, float sm_scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, int32_t batch,
+                              int32_t max_seq_len, oscar::DecodeArgs& a, oscar::QueryArgs& qa,
+                              oscar::Plan& plan) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (batch == 0) return ok();
+  if (max_seq_len < 1) return fail(OSCAR_ERR_RANGE, "max_seq_len %d < 1", max_seq_len);
+  plan = oscar::make_plan(*l, batch, max_seq_len);
+  if (plan.max_pages > l->max_pages_per_seq)
+    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
+                max_seq_len, plan.max_pages, l->max_pages_per_seq);
+  if ((plan.max_pages > 0 && (!pool || !page_table)) || !sink_k || !sink_v || !recent_k ||
+      !recent_v || !seq_slot || !seq_lens || !q || !u_k || !u_v || !out)
+    return fail(OSCAR_ERR_NULL, "decode: a required pointer is NULL");
+  if (workspace == nullptr || workspace_bytes < plan.total)
+    return fail(OSCAR_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes,
+                plan.total);
+  if (!aligned(workspace, 256)) return fail(OSCAR_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((pool && !aligned(pool, 16)) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
+      !aligned(recent_k, 16) || !aligned(recent_v, 16))
+    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
+  if (!aligned(q, 4) || !aligned(u_k, 4) || !aligned(u_v, 4) || !aligned(out, 4) ||
+      (lse && !aligned(lse, 4)) || !aligned(seq_slot, 4) || !aligned(seq_lens, 4) ||
+      (page_table && !aligned(page_table, 4)))
+    return fail(OSCAR_ERR_ALIGN, "decode: misaligned pointer");
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.sink_k = static_cast<const uint16_t*>(sink_k);
+  a.sink_v = static_cast<const uint16_t*>(sink_v);
+  a.recent_k = static_cast<const uint16_t*>(recent_k);
+  a.recent_v = static_cast<const uint16_t*>(recent_v);
+  a.seq_slot = seq_slot;
+  a.seq_lens = seq_lens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.u_k = u_k;
+  a.u_v = u_v;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : 0.08838834764831845f;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = static_cast<uint8_t*>(workspace);
+  a.len_add = 0;
+  qa.q = a.q;
+  qa.u_k = u_k;
+  qa.batch = batch;
+  qa.hq = plan.hq;
+  qa.gqa = plan.gqa;
+  qa.n_groups = plan.n_groups;
+  qa.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
+  qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 uint32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
@@ -248,41 +354,13 @@ oscar_status oscar_append(const oscar_layout* l, void* pool, const int32_t* page
                           const float* clip_v, const void* k_new, const void* v_new,
                           const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
                           void* stream) {
-  oscar_status st = check_layout(l);
-  if (st != OSCAR_OK) return st;
-  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
-  if (batch == 0) return ok();
-  if (l->max_seqs == 0) return fail(OSCAR_ERR_SHAPE, "layout has no sequence slots");
-  if (!pool || !page_table || !sink_k || !sink_v || !recent_k || !recent_v || !u_k || !u_v ||
-      !clip_k || !clip_v || !k_new || !v_new || !seq_slot || !seq_lens)
-    return fail(OSCAR_ERR_NULL, "oscar_append: a required pointer is NULL");
-  if (!aligned(pool, 16) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
-      !aligned(recent_k, 16) || !aligned(recent_v, 16))
-    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
-  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
-      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(seq_slot, 4) ||
-      !aligned(seq_lens, 4) || !aligned(page_table, 4))
-    return fail(OSCAR_ERR_ALIGN, "oscar_append: misaligned pointer");
   oscar::AppendArgs a;
-  a.pool = static_cast<uint8_t*>(pool);
-  a.page_table = page_table;
-  a.max_pages_per_seq = l->max_pages_per_seq;
-  a.hkv = l->num_kv_heads;
-  a.n_groups = n_groups(l);
-  a.sink_k = static_cast<uint16_t*>(sink_k);
-  a.sink_v = static_cast<uint16_t*>(sink_v);
-  a.recent_k = static_cast<uint16_t*>(recent_k);
-  a.recent_v = static_cast<uint16_t*>(recent_v);
-  a.u_k = u_k;
-  a.u_v = u_v;
-  a.clip_k = clip_k;
-  a.clip_v = clip_v;
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.seq_slot = seq_slot;
-  a.seq_lens = seq_lens;
-  a.batch = batch;
-  return hip_status(oscar::launch_append(a, static_cast<hipStream_t>(stream)), "oscar_append");
+  const oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                                           u_k, u_v, clip_k, clip_v, k_new, v_new, seq_slot,
+                                           seq_lens, batch, a);
+  if (st != OSCAR_OK || batch == 0) return st;
+  return hip_status(oscar::launch_prep(&a, nullptr, static_cast<hipStream_t>(stream)),
+                    "oscar_append");
 }
 
 oscar_status oscar_decode_attn(const oscar_layout* l, const void* pool, const int32_t* page_table,
@@ -305,50 +383,49 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
                                       const float* u_v, float sm_scale, float* out, float* lse,
                                       void* workspace, size_t workspace_bytes, int32_t batch,
                                       int32_t max_seq_len, uint32_t stages, void* stream) {
-  oscar_status st = check_layout(l);
   if (stages == 0 || (stages & ~OSCAR_STAGE_ALL) != 0)
     return fail(OSCAR_ERR_RANGE, "stage mask 0x%x invalid", stages);
-  if (st != OSCAR_OK) return st;
-  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
-  if (batch == 0) return ok();
-  if (max_seq_len < 1) return fail(OSCAR_ERR_RANGE, "max_seq_len %d < 1", max_seq_len);
-  const oscar::Plan plan = oscar::make_plan(*l, batch, max_seq_len);
-  if (plan.max_pages > l->max_pages_per_seq)
-    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
-                max_seq_len, plan.max_pages, l->max_pages_per_seq);
-  if ((plan.max_pages > 0 && (!pool || !page_table)) || !sink_k || !sink_v || !recent_k ||
-      !recent_v || !seq_slot || !seq_lens || !q || !u_k || !u_v || !out)
-    return fail(OSCAR_ERR_NULL, "oscar_decode_attn: a required pointer is NULL");
-  if (workspace == nullptr || workspace_bytes < plan.total)
-    return fail(OSCAR_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes,
-                plan.total);
-  if (!aligned(workspace, 256)) return fail(OSCAR_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if ((pool && !aligned(pool, 16)) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
-      !aligned(recent_k, 16) || !aligned(recent_v, 16))
-    return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
-  if (!aligned(q, 4) || !aligned(u_k, 4) || !aligned(u_v, 4) || !aligned(out, 4) ||
-      (lse && !aligned(lse, 4)) || !aligned(seq_slot, 4) || !aligned(seq_lens, 4) ||
-      (page_table && !aligned(page_table, 4)))
-    return fail(OSCAR_ERR_ALIGN, "oscar_decode_attn: misaligned pointer");
   oscar::DecodeArgs a;
-  a.pool = static_cast<const uint8_t*>(pool);
-  a.page_table = page_table;
-  a.max_pages_per_seq = l->max_pages_per_seq;
-  a.sink_k = static_cast<const uint16_t*>(sink_k);
-  a.sink_v = static_cast<const uint16_t*>(sink_v);
-  a.recent_k = static_cast<const uint16_t*>(recent_k);
-  a.recent_v = static_cast<const uint16_t*>(recent_v);
-  a.seq_slot = seq_slot;
-  a.seq_lens = seq_lens;
-  a.q = static_cast<const uint16_t*>(q);
-  a.u_k = u_k;
-  a.u_v = u_v;
-  a.sm_scale = sm_scale > 0.f ? sm_scale : 0.08838834764831845f;
-  a.out = out;
-  a.lse = lse;
-  a.workspace = static_cast<uint8_t*>(workspace);
-  return hip_status(oscar::launch_decode(a, plan, stages, static_cast<hipStream_t>(stream)),
-                    "oscar_decode_attn");
+  oscar::QueryArgs qa;
+  oscar::Plan plan;
+  const oscar_status st = make_decode_args(l, pool, page_table, sink_k, sink_v, recent_k,
+                                           recent_v, seq_slot, seq_lens, q, u_k, u_v, sm_scale,
+                                           out, lse, workspace, workspace_bytes, batch,
+                                           max_seq_len, a, qa, plan);
+  if (st != OSCAR_OK || batch == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (stages & OSCAR_STAGE_QUERY) {
+    const hipError_t e = oscar::launch_prep(nullptr, &qa, s);
+    if (e != hipSuccess) return hip_status(e, "oscar_decode_attn");
+  }
+  return hip_status(oscar::launch_decode(a, plan, stages, s), "oscar_decode_attn");
+}
+
+oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t* page_table,
+                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                               const float* u_k, const float* u_v, const float* clip_k,
+                               const float* clip_v, const void* k_new, const void* v_new,
+                               const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
+                               float sm_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                               void* stream) {
+  oscar::AppendArgs ap;
+  oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                                     u_k, u_v, clip_k, clip_v, k_new, v_new, seq_slot, seq_pos,
+                                     batch, ap);
+  if (st != OSCAR_OK) return st;
+  oscar::DecodeArgs a;
+  oscar::QueryArgs qa;
+  oscar::Plan plan;
+  st = make_decode_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot, seq_pos,
+                        q, u_k, u_v, sm_scale, out, lse, workspace, workspace_bytes, batch,
+                        max_seq_len, a, qa, plan);
+  if (st != OSCAR_OK || batch == 0) return st;
+  a.len_add = 1;   // attention sees the appended token
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = oscar::launch_prep(&ap, &qa, s);
+  if (e != hipSuccess) return hip_status(e, "oscar_decode_step");
+  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_ALL, s), "oscar_decode_step");
 }
 
 }  // extern "C"

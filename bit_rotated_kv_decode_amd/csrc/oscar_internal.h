@@ -113,10 +113,21 @@ struct DecodeArgs {
   float* out;
   float* lse;
   uint8_t* workspace;
+  int len_add;            // added to seq_lens[b] (1 when seq_lens holds the new token's position)
+};
+
+struct QueryArgs {
+  const uint16_t* q;      // bf16 [batch][hq][128]
+  const float* u_k;
+  int batch, hq, gqa, n_groups;
+  float scale_log2;       // sm_scale * log2(e)
+  int8_t* qpack;          // workspace: int8 [batch][hq][2][128]
+  float* qmeta;           // workspace: fp32 [batch][hq][4]
 };
 
 hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
-hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// One launch for the append items (ap) and the query rows (qa); either may be null.
+hipError_t launch_prep(const AppendArgs* ap, const QueryArgs* qa, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, uint32_t stages,
                          hipStream_t stream);
 

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 1u
+#define OSCAR_ABI_VERSION 2u
 
 typedef int32_t oscar_status;
 
@@ -224,6 +224,25 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* layout, const void* po
                                       const float* u_v, float sm_scale, float* out, float* lse,
                                       void* workspace, size_t workspace_bytes, int32_t batch,
                                       int32_t max_seq_len, uint32_t stages, void* stream);
+
+/* One whole decode step of a layer ([W1] OSCAR 的设计: a new token enters the recent window, the
+ * token it displaces is demoted into the INT2 history, then attention runs over the three
+ * segments): the same result as
+ *   oscar_append(..., seq_slot, seq_pos, ...)  followed by
+ *   oscar_decode_attn(..., seq_lens = seq_pos + 1, ...),
+ * with the append and the query rotation sharing one launch (three launches in all).
+ * seq_pos[b] = position of the new token = tokens cached before the step; seq_pos[b] + 1 must be
+ * in [1, max_seq_len].  Arguments are those of the two calls, with the same requirements.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP; nothing is launched
+ * unless every argument check passes. */
+oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int32_t* page_table,
+                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                               const float* u_k, const float* u_v, const float* clip_k,
+                               const float* clip_v, const void* k_new, const void* v_new,
+                               const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
+                               float sm_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 1
+    assert lib.oscar_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -137,6 +137,30 @@ def test_append_validation_happens_before_launch():
     assert f(ctypes.byref(lay), *([4096 + 4] + args[1:]), 1, None) == -3
     assert f(ctypes.byref(_lay(max_seqs=0)), *args, 1, None) == -2
     assert f(ctypes.byref(lay), *args, -1, None) == -4
+
+
+def _call_step(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, uk=4096, uv=4096, ck=4096,
+             cv=4096, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, out=4096, lse=None, ws=4096,
+             wsb=1 << 30, batch=1, maxlen=600)
+    a.update(over)
+    return ok.lib().oscar_decode_step(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
+        a["uv"], a["ck"], a["cv"], a["kn"], a["vn"], a["slot"], a["pos"], a["q"], 0.0, a["out"],
+        a["lse"], a["ws"], a["wsb"], a["batch"], a["maxlen"], None)
+
+
+def test_step_validation_happens_before_launch():
+    lay = _lay()
+    # an append argument or a decode argument may fail; either way nothing is launched
+    assert _call_step(lay, kn=None) == -1
+    assert _call_step(lay, ck=4096 + 2) == -3
+    assert _call_step(_lay(max_seqs=0)) == -2
+    assert _call_step(lay, q=None) == -1
+    assert _call_step(lay, ws=None) == -5
+    assert _call_step(lay, maxlen=100000) == -4
+    assert _call_step(lay, batch=-1) == -4
+    assert _call_step(lay, batch=0, q=None, kn=None) == 0
 
 
 def test_check_page_table():

@@ -170,3 +170,44 @@ def test_append_steps_match_oracle():
     assert np.array_equal(cache.recent_k.float().cpu().numpy(), rk)
     case.lengths = lens
     compare_pool_blocks(cache.pool.cpu().numpy(), pool, case)
+
+
+def test_decode_step_matches_append_then_attend():
+    # oscar_decode_step (append + query rotation in one launch, then attention) against
+    # oscar_append followed by oscar_decode_attn: identical outputs and cache bytes every step;
+    # the sequences cross the full-ring threshold (320), value-word (16) and page (64) boundaries.
+    wl = _tiny(num_q_heads=8, num_kv_heads=2)
+    start, steps = [318, 1011], 30
+    case = Case(wl, [s + steps for s in start])
+    final = list(case.lengths)
+    case.lengths = list(start)
+    g = case.gpu_inputs()
+    lay = case.layout
+    ca, cb = case.gpu_cache(g), case.gpu_cache(g)
+    mx = max(final)
+    ws_a = torch.empty(ok.decode_workspace_bytes(lay, 2, mx), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty_like(ws_a)
+    out_a = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+    out_b = torch.empty_like(out_a)
+    for s in range(steps):
+        pos = [p + s for p in start]
+        _note(f"decode step {s}: positions {pos}")
+        k_new = torch.stack([case.k[b][pos[b]] for b in range(2)]).to("cuda")
+        v_new = torch.stack([case.v[b][pos[b]] for b in range(2)]).to("cuda")
+        pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        ok.decode_step(lay, ca.pool, g["table"], ca.sink_k, ca.sink_v, ca.recent_k, ca.recent_v,
+                       g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"],
+                       pos_t, g["q"], out_a, ws_a, mx)
+        ok.append(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t)
+        ok.decode_attn(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                       g["slots"], pos_t + 1, g["q"], g["u_k"], g["u_v"], out_b, ws_b, mx)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), s
+    assert torch.equal(ca.pool, cb.pool)
+    assert torch.equal(ca.recent_k, cb.recent_k) and torch.equal(ca.recent_v, cb.recent_v)
+    case.lengths = final
+    ref, _ = case.oracle_attention(case.oracle_pool())
+    err = attention_error(out_a.cpu().numpy(), ref)
+    _note(f"decode_step final max row error {err:.3e}")
+    assert err <= ATTN_TOL
