@@ -21,6 +21,7 @@ head of one layer and scaled.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -50,7 +51,42 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times "
+                         "(calibration of the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_qwen3_8b_100k_hbm_traffic.md")
+
+
+def recorded_traffic():
+    """HBM bytes per segment-kernel launch recorded from the FETCH_SIZE / WRITE_SIZE counters, or
+    None when the kernel sources changed since (their sha256 is stored with the figure)."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            key, _, val = line.strip().partition(": ")
+            fields[key] = val
+        h = hashlib.sha256()
+        for f in fields["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bytes_per_token_head(group: int) -> int:
@@ -103,6 +139,9 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
+        return
     ok.lib()
     wl = workloads.get(args.workload)
     n_layers = args.layers or wl.num_layers
@@ -241,7 +280,8 @@ def main():
         "step_bytes": int(step_bytes),
         "roofline": {"kernel": "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(),
                      "bytes_per_launch": int(seg_bytes),
                      "avg_launch_us": round(seg_us_avg, 3),
                      "timing": f"HIP events around {args.steps} replays of a graph of "
@@ -255,6 +295,8 @@ def main():
 def cpu_baseline(wl, layer0, length):
     """Time the CPU oracle on one KV head (4 query heads) of one layer at full context, plus the
     demotion of one token, and scale to the whole 36-layer step."""
+    import threadpoolctl
+
     import oracle
 
     def bf16_np(t):
@@ -287,21 +329,19 @@ def cpu_baseline(wl, layer0, length):
     heads = [(0, kv * gq + i) for i in range(gq)]
     clip = np.full(wl.num_kv_heads, wl.clip, np.float32)
     times = []
-    for _ in range(2):
-        t = time.perf_counter()
-        oracle.demote(pool, table, uk, uv, clip, clip, k[None, 64:65], v[None, 64:65], [0], geom)
-        oracle.decode_attention(pool, table, sk, sv, rk, rv, [0], [length], q, uk, uv, geom,
-                                heads=heads)
-        times.append(time.perf_counter() - t)
+    with threadpoolctl.threadpool_limits(1):      # one core: numpy's BLAS pool held to 1 thread
+        for _ in range(2):
+            t = time.perf_counter()
+            oracle.demote(pool, table, uk, uv, clip, clip, k[None, 64:65], v[None, 64:65], [0],
+                          geom)
+            oracle.decode_attention(pool, table, sk, sv, rk, rv, [0], [length], q, uk, uv, geom,
+                                    heads=heads)
+            times.append(time.perf_counter() - t)
     per_head = min(times)
     step_s = per_head * wl.num_kv_heads * wl.num_layers
     head_bytes = n_hist * bytes_per_token_head(wl.group_size) + 320 * 128 * 2 * 2
     step_bytes = head_bytes * wl.num_kv_heads * wl.num_layers
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": cores,
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "decode_steps_per_s": round(1.0 / step_s, 6),
             "sample": f"numpy fp64 oracle, 1 KV head ({gq} query heads) of 1 layer at context "
                       f"{length}: demotion of 1 token + decode attention over the 3-segment "
