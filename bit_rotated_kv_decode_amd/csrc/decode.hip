@@ -53,16 +53,14 @@ __device__ __forceinline__ v2bf codes_to_bf16(uint32_t x) {
 // Values: acc[row, ch] += sum_t P[row, t] V[t, ch] with v_mfma_f32_16x16x32_bf16; P rows are the
 // bf16 hi and lo parts of p * s_v for each head, transposed through LDS; V = value codes turned
 // into exact bf16 integers by the FP4 conversion path.
-// LDS carve-up of an INT2 block.  The query operands and P tiles are dead after the page loop,
-// where the same bytes take the per-wave accumulator rows.
+// LDS carve-up of an INT2 block.  The P tiles are dead after the page loop, where the same bytes
+// take the per-wave accumulator rows.
 template <int G, int NG>
 struct Int2Lds {
   static constexpr int GP = G <= 4 ? 4 : 8;
-  static constexpr int NPL = 16 / GP;
-  static constexpr int QA = NPL * 2 * 2 * 64 * 16;           // [pl][hf][hl][lane] int8 x16
   static constexpr int PB = 4 * NG * 16 * kPage * 2;         // [wave][g][row][token] bf16
   static constexpr int RED = 4 * 2 * GP * kHeadDim * 4;      // [wave][row][ch] fp32
-  static constexpr int MAIN = (QA + PB) > RED ? (QA + PB) : RED;
+  static constexpr int MAIN = PB > RED ? PB : RED;
   static constexpr int PAGE_IDS = MAIN;                      // int [kMaxPagesPerSplit]
   static constexpr int RED_M = PAGE_IDS + 4 * kMaxPagesPerSplit;
   static constexpr int RED_L = RED_M + 4 * 4 * GP;
@@ -76,11 +74,9 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   using S = Int2Lds<G, NG>;
   constexpr int GP = S::GP;               // padded query heads per KV head
   constexpr int NACC = GP / 4;            // score accumulators (tokens per lane and page)
-  constexpr int NPL = S::NPL;             // operand placements
   constexpr int PP = 1;                   // pages per step
   constexpr int BLK = kMetaOff + kPage * 8 * NG;
-  v4i* qa_lds = reinterpret_cast<v4i*>(smem);
-  __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem + S::QA);
+  __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem);
   float* red_acc = reinterpret_cast<float*>(smem);
   int* page_ids = reinterpret_cast<int*>(smem + S::PAGE_IDS);
   float (*red_m)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_M);
@@ -101,24 +97,27 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   for (int i = threadIdx.x; i < p1 - p0; i += 256)
     page_ids[i] = a.page_table[static_cast<int64_t>(b) * a.max_pages_per_seq + p0 + i];
 
-  // ---- query operands into LDS: operand (pl, hf, hl) is nonzero only in the lanes of placement
-  // pl; each wave writes the copy it will read (all four waves hold the same values)
+  // ---- query operands (registers, the same for every page).  Score tile rows hold the int8 hi
+  // part of a head's q' and, four rows further, its lo part; GP = 4: operand ts (sub-tiles of
+  // parity ts) fills rows 8 ts .. 8 ts + 7; GP = 8: rows 0..7 hi and 8..15 lo of heads 0..7.  Lane
+  // (k block gq, row n) holds channels [16 gq, 16 gq + 16) of half hf (MFMA operand order).
   const int8_t* qpack = reinterpret_cast<const int8_t*>(a.workspace + p.off_qrot);
   const float* qmeta = reinterpret_cast<const float*>(a.workspace + p.off_sigma);
-  if (wave == 0) {
-    const int pl = n / GP, hd = n % GP;
+  v4i qa[GP == 4 ? 2 : 1][2];
+  {
+    const int ts = GP == 4 ? n / 8 : 0;
+    const int hl = GP == 4 ? (n / 4) % 2 : n / 8;
+    const int hd = GP == 4 ? n % 4 : n % 8;
 #pragma unroll
-    for (int q = 0; q < NPL; ++q)
+    for (int t = 0; t < (GP == 4 ? 2 : 1); ++t)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          v4i v = {0, 0, 0, 0};
-          if (q == pl && hd < G)
-            v = *reinterpret_cast<const v4i*>(qpack + static_cast<int64_t>(head0 + hd) * 256 +
-                                              hl * 128 + (hf * 4 + gq) * 16);
-          qa_lds[((q * 2 + hf) * 2 + hl) * 64 + lane] = v;
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        v4i v = {0, 0, 0, 0};
+        if (t == ts && hd < G)
+          v = *reinterpret_cast<const v4i*>(qpack + static_cast<int64_t>(head0 + hd) * 256 +
+                                            hl * 128 + (hf * 4 + gq) * 16);
+        qa[t][hf] = v;
+      }
   }
   // per head-slot constants of this lane: head = hs (GP = 4) or 4 (gq & 1) + hs (GP = 8)
   float kh[4], sq[4][NG];
@@ -130,8 +129,11 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
     for (int g = 0; g < NG; ++g) sq[hs][g] = m[1 + g];
   }
-  // token (within a page) of this lane's score accumulator pa
-  auto tok_of = [&](int pa) { return GP == 4 ? lane : 16 * (2 * pa + (gq >> 1)) + n; };
+  // token (within a page) of this lane's score vector pa: after the hi / lo lane swap, lane group
+  // gq holds sub-tile (0, 2, 1, 3)[gq] (GP = 4) or sub-tile 2 pa + gq / 2 (GP = 8)
+  auto tok_of = [&](int pa) {
+    return GP == 4 ? 16 * (((gq & 1) << 1) | (gq >> 1)) + n : 16 * (2 * pa + (gq >> 1)) + n;
+  };
   // position of a token in a P row; value operands read 8 consecutive entries per lane, which
   // hold tokens 8 k + {0, 2, 4, 6, 1, 3, 5, 7}
   auto ppos = [](int t) { return (t & ~7) | ((t & 7) >> 1) | ((t & 1) << 2); };
@@ -206,33 +208,47 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 
   // Pages pg .. pg + PP - 1 on register sets r[0 .. PP - 1]; pages past p1 contribute nothing.
   auto process_step = [&](int pg, const PageRegs* r) {
-    // ---- scores
-    v4i dh[PP][NACC][NG], dl[PP][NACC][NG];
+    // ---- scores: exact int32 tiles of hi and lo dot products, then one lane swap per register
+    // puts hi and lo of the same token in one lane: S = 256 hi + lo
+    constexpr int NT = GP == 4 ? 2 : 4;
+    int sc[PP][NACC][NG][4];
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
+    for (int pp = 0; pp < PP; ++pp) {
+      v4i dt[NG][NT];
 #pragma unroll
-      for (int pa = 0; pa < NACC; ++pa)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) dh[pp][pa][g] = dl[pp][pa][g] = v4i{0, 0, 0, 0};
+        for (int t = 0; t < NT; ++t) dt[g][t] = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int pa = st / NPL, pl = st % NPL;
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const v4i ah = qa_lds[((pl * 2 + hf) * 2 + 0) * 64 + lane];
-        const v4i al = qa_lds[((pl * 2 + hf) * 2 + 1) * 64 + lane];
-        const int g = NG == 2 ? hf : 0;
-#pragma unroll
-        for (int pp = 0; pp < PP; ++pp) {
+        for (int hf = 0; hf < 2; ++hf) {
+          const int g = NG == 2 ? hf : 0;
           const uint32_t w = kword(r[pp], st, hf);
           const v4i bk = {static_cast<int>(w & 0x03030303u),
                           static_cast<int>((w >> 2) & 0x03030303u),
                           static_cast<int>((w >> 4) & 0x03030303u),
                           static_cast<int>((w >> 6) & 0x03030303u)};
-          dh[pp][pa][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bk, dh[pp][pa][g], 0, 0, 0);
-          dl[pp][pa][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bk, dl[pp][pa][g], 0, 0, 0);
+          if constexpr (GP == 4)
+            dt[g][st >> 1] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[st & 1][hf], bk, dt[g][st >> 1], 0, 0, 0);
+          else
+            dt[g][st] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][hf], bk, dt[g][st], 0, 0, 0);
         }
-      }
+#pragma unroll
+      for (int pa = 0; pa < NACC; ++pa)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int hs = 0; hs < 4; ++hs) {
+            // GP = 4: tiles (sub-tiles 0,1) and (2,3) hold rows [hi, lo, hi, lo] per lane group;
+            // GP = 8: tiles of sub-tiles 2 pa and 2 pa + 1 hold [hi, hi, lo, lo]
+            const uint32_t x = static_cast<uint32_t>(dt[g][GP == 4 ? 0 : 2 * pa][hs]);
+            const uint32_t y = static_cast<uint32_t>(dt[g][GP == 4 ? 1 : 2 * pa + 1][hs]);
+            const auto sw = GP == 4 ? __builtin_amdgcn_permlane16_swap(x, y, false, false)
+                                    : __builtin_amdgcn_permlane32_swap(x, y, false, false);
+            sc[pp][pa][g][hs] = (static_cast<int>(sw[0]) << 8) + static_cast<int>(sw[1]);
+          }
     }
     float logit[PP][NACC][4];
     bool valid[PP][NACC];
@@ -256,8 +272,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           float t = 0.f;
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            const int s = (dh[pp][pa][g][hs] << 8) + dl[pp][pa][g][hs];
-            t = fmaf(ks[g], static_cast<float>(s), fmaf(kz[g], sq[hs][g], t));
+            t = fmaf(ks[g], static_cast<float>(sc[pp][pa][g][hs]), fmaf(kz[g], sq[hs][g], t));
           }
           logit[pp][pa][hs] = valid[pp][pa] ? t * kh[hs] : -INFINITY;
         }
@@ -575,7 +590,7 @@ constexpr int attn_lds_bytes() {
 }
 
 template <int G, int NG>
-__global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
+__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
                                                       int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
   const int x = x0 + blockIdx.x, kv = blockIdx.y, b = blockIdx.z;

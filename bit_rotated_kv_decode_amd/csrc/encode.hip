@@ -12,104 +12,15 @@
 // that decides a code (clip, group min / max, (max - min) / 3, fp16 rounding, (x - z) / s, rint)
 // runs in IEEE fp32.
 #include "device_common.h"
+#include "encode_common.h"
 #include "oscar_internal.h"
 
 namespace oscar {
 namespace {
 
+using namespace enc;
+
 constexpr int kWaves = 4;
-
-struct LaneCodes {
-  uint32_t c0, c1;     // codes of channels lane and lane + 64
-  uint32_t meta[2];    // per group: fp16 scale in bits 0..15, fp16 zero in bits 16..31
-};
-
-// Clip and quantise the rotated channels (lane, lane + 64) of one vector; all lanes of the wave
-// must call this together (the group min / max are wave reductions).
-__device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float clip,
-                                                   int n_groups) {
-  float x0 = static_cast<float>(r0);
-  float x1 = static_cast<float>(r1);
-  x0 = fminf(fmaxf(x0, -clip), clip);
-  x1 = fminf(fmaxf(x1, -clip), clip);
-  float mn[2], mx[2];
-  if (n_groups == 1) {
-    mn[0] = mn[1] = dev::wave_min(fminf(x0, x1));
-    mx[0] = mx[1] = dev::wave_max(fmaxf(x0, x1));
-  } else {
-    // group 0 = channels 0..63 (slot 0 of every lane), group 1 = channels 64..127 (slot 1)
-    mn[0] = dev::wave_min(x0);
-    mx[0] = dev::wave_max(x0);
-    mn[1] = dev::wave_min(x1);
-    mx[1] = dev::wave_max(x1);
-  }
-  LaneCodes out;
-  float sf[2], zf[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const float s32 = (mx[m] - mn[m]) / 3.0f;
-    const __half s16 = __float2half_rn(s32);
-    const __half z16 = __float2half_rn(mn[m]);
-    sf[m] = __half2float(s16);
-    zf[m] = __half2float(z16);
-    out.meta[m] = static_cast<uint32_t>(__half_as_ushort(s16)) |
-                  (static_cast<uint32_t>(__half_as_ushort(z16)) << 16);
-  }
-  auto code = [](float x, float s, float z) -> uint32_t {
-    if (s == 0.0f) return 0u;
-    const float t = rintf((x - z) / s);
-    return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
-  };
-  out.c0 = code(x0, sf[0], zf[0]);
-  out.c1 = code(x1, sf[1], zf[1]);
-  return out;
-}
-
-__device__ __forceinline__ uint8_t* page_block(uint8_t* pool, const int32_t* page_table,
-                                               int max_pages_per_seq, int b, int hist_idx, int hkv,
-                                               int h, int blk_bytes) {
-  const int page = page_table[static_cast<int64_t>(b) * max_pages_per_seq + hist_idx / kPage];
-  return pool + (static_cast<int64_t>(page) * hkv + h) * blk_bytes;
-}
-
-// Key codes are packed along channels: word w of a token holds channels 16w..16w+15, and the
-// words sit in the tiled order of k_word_index.
-__device__ __forceinline__ void store_key_row(uint8_t* blk, int slot, uint32_t c0, uint32_t c1) {
-  const int lane = dev::lane_id();
-  uint32_t v0 = c0 << (2 * (lane & 15));
-  uint32_t v1 = c1 << (2 * (lane & 15));
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    v0 |= __shfl_xor(v0, m);
-    v1 |= __shfl_xor(v1, m);
-  }
-  if ((lane & 15) == 0) {
-    uint32_t* words = reinterpret_cast<uint32_t*>(blk + kKCodesOff);
-    words[k_word_index(slot, lane >> 4)] = v0;
-    words[k_word_index(slot, 4 + (lane >> 4))] = v1;
-  }
-}
-
-// Per-token meta: key groups first, then value groups (tensor 0 = K, 1 = V).
-__device__ __forceinline__ void store_meta(uint8_t* blk, int tensor, int slot, int n_groups,
-                                           const LaneCodes& q) {
-  if (dev::lane_id() == 0) {
-    uint32_t* m = reinterpret_cast<uint32_t*>(blk + kMetaOff + slot * meta_bytes_per_token(n_groups)) +
-                  tensor * n_groups;
-    for (int g = 0; g < n_groups; ++g) m[g] = q.meta[g];
-  }
-}
-
-// Replace the bits under `mask` of a pool dword that other waves may update concurrently.
-__device__ __forceinline__ void merge_bits(uint32_t* p, uint32_t mask, uint32_t bits) {
-  uint32_t old = *p;
-  while (true) {
-    const uint32_t want = (old & ~mask) | bits;
-    const uint32_t prev = atomicCAS(p, old, want);
-    if (prev == old) break;
-    old = prev;
-  }
-}
 
 // ------------------------------------------------------------------------------------------
 // Bulk demotion.  A wave encodes the tokens of one 16-slot run of a page (history indices
@@ -250,22 +161,7 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
     const int idx = pos - kSink - kRecent;
     uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
                               block_bytes(a.n_groups));
-    const int slot_in_page = idx % kPage;
-    const int lane = dev::lane_id();
-    if (tensor == 0) {
-      store_key_row(blk, slot_in_page, q.c0, q.c1);
-    } else {
-      uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-      const int u = slot_in_page / 16;
-      const int sh = 2 * (slot_in_page % 16);
-      uint32_t* w0 = &vc[v_word_index(lane, u)];
-      uint32_t* w1 = &vc[v_word_index(lane + 64, u)];
-      __hip_atomic_fetch_and(w0, ~(3u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_and(w1, ~(3u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_or(w0, q.c0 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_or(w1, q.c1 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    store_meta(blk, tensor, slot_in_page, a.n_groups, q);
+    store_token(blk, tensor, idx % kPage, a.n_groups, q);
   }
 }
 
@@ -280,43 +176,8 @@ __device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned
   __syncthreads();
   double r0, r1;
   if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
-  const int lane = dev::lane_id();
-  const float f0 = static_cast<float>(r0);   // rotated channel lane
-  const float f1 = static_cast<float>(r1);   // rotated channel lane + 64
-  const float amax = dev::wave_max(fmaxf(fabsf(f0), fabsf(f1)));
-  const float sa = amax > 0.f ? amax / 127.f : 1.f;
-  auto split = [sa](float v, int& hi, int& lo) {
-    hi = static_cast<int>(rintf(v / sa));
-    const float r = fmaf(-static_cast<float>(hi), sa, v);
-    lo = static_cast<int>(fminf(fmaxf(rintf(r * 256.f / sa), -127.f), 127.f));
-  };
-  int h0, l0, h1, l1;
-  split(f0, h0, l0);
-  split(f1, h1, l1);
-  // MFMA operand order: channel j = 16 qd + 4 b + k sits at byte 16 qd + 4 k + b
-  auto opos = [](int j) { return (j >> 4) * 16 + (j & 3) * 4 + ((j >> 2) & 3); };
-  int8_t* dst = a.qpack + static_cast<int64_t>(row) * 256;
-  dst[opos(lane)] = static_cast<int8_t>(h0);
-  dst[opos(lane + 64)] = static_cast<int8_t>(h1);
-  dst[128 + opos(lane)] = static_cast<int8_t>(l0);
-  dst[128 + opos(lane + 64)] = static_cast<int8_t>(l1);
-  // sums of the quantised q' per group, in units of a / 256 (exact in int32)
-  const int e0 = 256 * h0 + l0, e1 = 256 * h1 + l1;
-  int s0, s1;
-  if (a.n_groups == 1) {
-    s0 = dev::wave_sum_i(e0 + e1);
-    s1 = 0;
-  } else {
-    s0 = dev::wave_sum_i(e0);
-    s1 = dev::wave_sum_i(e1);
-  }
-  if (lane == 0) {
-    float* m = a.qmeta + static_cast<int64_t>(row) * 4;
-    m[0] = sa / 256.f * a.scale_log2;
-    m[1] = static_cast<float>(s0);
-    m[2] = static_cast<float>(s1);
-    m[3] = 0.f;
-  }
+  split_query(r0, r1, a.n_groups, a.scale_log2, a.qpack + static_cast<int64_t>(row) * 256,
+              a.qmeta + static_cast<int64_t>(row) * 4);
 }
 
 // x0 + blockIdx.x < n_query: query row; else append item x0 + blockIdx.x - n_query.

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <unordered_map>
 
@@ -425,7 +426,9 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = oscar::launch_prep(&ap, &qa, s);
   if (e != hipSuccess) return hip_status(e, "oscar_decode_step");
-  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_ALL, s), "oscar_decode_step");
+  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
+                                                      OSCAR_STAGE_MERGE, s),
+                    "oscar_decode_step");
 }
 
 }  // extern "C"

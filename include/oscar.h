@@ -230,7 +230,7 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* layout, const void* po
  * segments): the same result as
  *   oscar_append(..., seq_slot, seq_pos, ...)  followed by
  *   oscar_decode_attn(..., seq_lens = seq_pos + 1, ...),
- * with the append and the query rotation sharing one launch (three launches in all).
+ * in three launches: the append and the query rotation share the first.
  * seq_pos[b] = position of the new token = tokens cached before the step; seq_pos[b] + 1 must be
  * in [1, max_seq_len].  Arguments are those of the two calls, with the same requirements.
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP; nothing is launched

@@ -185,8 +185,9 @@ def test_decode_step_matches_append_then_attend():
     lay = case.layout
     ca, cb = case.gpu_cache(g), case.gpu_cache(g)
     mx = max(final)
-    ws_a = torch.empty(ok.decode_workspace_bytes(lay, 2, mx), dtype=torch.uint8, device="cuda")
+    ws_a = torch.zeros(ok.decode_workspace_bytes(lay, 2, mx), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty_like(ws_a)
+    gen = torch.Generator().manual_seed(11)   # a different query every step
     out_a = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
     out_b = torch.empty_like(out_a)
     for s in range(steps):
@@ -195,18 +196,20 @@ def test_decode_step_matches_append_then_attend():
         k_new = torch.stack([case.k[b][pos[b]] for b in range(2)]).to("cuda")
         v_new = torch.stack([case.v[b][pos[b]] for b in range(2)]).to("cuda")
         pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        q_s = torch.randn(g["q"].shape, generator=gen).to(torch.bfloat16).to("cuda")
         ok.decode_step(lay, ca.pool, g["table"], ca.sink_k, ca.sink_v, ca.recent_k, ca.recent_v,
                        g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"],
-                       pos_t, g["q"], out_a, ws_a, mx)
+                       pos_t, q_s, out_a, ws_a, mx)
         ok.append(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
                   g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t)
         ok.decode_attn(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
-                       g["slots"], pos_t + 1, g["q"], g["u_k"], g["u_v"], out_b, ws_b, mx)
+                       g["slots"], pos_t + 1, q_s, g["u_k"], g["u_v"], out_b, ws_b, mx)
         torch.cuda.synchronize()
         assert torch.equal(out_a, out_b), s
-    assert torch.equal(ca.pool, cb.pool)
+    assert torch.equal(ca.pool, cb.pool) and torch.equal(ca.sink_v, cb.sink_v)
     assert torch.equal(ca.recent_k, cb.recent_k) and torch.equal(ca.recent_v, cb.recent_v)
     case.lengths = final
+    case.q = q_s.cpu()
     ref, _ = case.oracle_attention(case.oracle_pool())
     err = attention_error(out_a.cpu().numpy(), ref)
     _note(f"decode_step final max row error {err:.3e}")
