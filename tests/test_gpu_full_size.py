@@ -1,0 +1,210 @@
+"""Full-size GPU parity on sampled outputs, through the C ABI.
+
+Each workload's layer is built at its full size by the library's own bulk demotion, then one
+oscar_decode_step (append, demotion of the displaced token, attention) runs in the launch
+configuration the benchmark uses.  The oracle then checks, on samples it can compute one by one:
+  * demotion: sampled history tokens (and the token demoted by the step) re-encoded by the oracle
+    against the GPU's page bytes, under the acceptance rule of oscar_cases;
+  * attention: sampled (sequence, KV head) pairs, the oracle's softmax attention over the same
+    cache bytes (the GPU-written pool and BF16 segments after the step) against the GPU rows,
+    within 2e-3 max row error.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_decode_amd as ok
+import oracle
+import workloads
+from oscar_cases import ATTN_TOL, MAX_FLIP_FRACTION, attention_error, bf16_np, check_token
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+class FullLayer:
+    """One layer of a workload at full size on the GPU after one decode step."""
+
+    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None):
+        self.wl, self.layer = wl, layer
+        self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
+        self.B = len(self.lengths)
+        hkv = wl.num_kv_heads
+        self.table, self.num_pages = workloads.page_tables(wl, self.lengths, layer, spare_tokens=1)
+        self.u_k, self.u_v = workloads.rotation_bases(wl, layer) if u is None else u
+        if clip is None:
+            clip = (np.full(hkv, wl.clip, np.float32), np.full(hkv, wl.clip, np.float32))
+        self.clip_k, self.clip_v = (np.asarray(c, np.float32) for c in clip)
+        self.geom = oracle.Geometry(group=wl.group_size)
+        self.lay = ok.make_layout(wl.num_q_heads, hkv, self.num_pages, self.B,
+                                  self.table.shape[1], wl.group_size)
+        dev = "cuda"
+        cache = ok.Cache.allocate(self.lay, zero=False)
+        table = torch.from_numpy(self.table).to(dev)
+        uk, uv = self.u_k.to(dev).contiguous(), self.u_v.to(dev).contiguous()
+        ck, cv = torch.from_numpy(self.clip_k).to(dev), torch.from_numpy(self.clip_v).to(dev)
+        # history: shared-prefix pages once (from the longest sequence), private pages per sequence
+        n_hist = [max(0, L - 320) for L in self.lengths]
+        shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
+        longest = int(np.argmax(self.lengths))
+        for b in range(self.B):
+            lo0 = 0 if (b == longest or not shared_hist) else min(shared_hist, n_hist[b])
+            for lo in range(lo0, n_hist[b], 16384):
+                n = min(16384, n_hist[b] - lo)
+                k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)
+                ok.demote(self.lay, cache.pool, table[b:b + 1], uk, uv, ck, cv, k.unsqueeze(0),
+                          v.unsqueeze(0), torch.full((1,), lo, dtype=torch.int32, device=dev))
+            L = self.lengths[b]
+            k, v = workloads.kv_tokens(wl, layer, b, 0, min(L, 64), dev)
+            cache.sink_k[b, :, :k.shape[0]] = k.transpose(0, 1)
+            cache.sink_v[b, :, :k.shape[0]] = v.transpose(0, 1)
+            if L > 64:
+                pos = torch.arange(max(64, L - 256), L, device=dev)
+                k, v = workloads.kv_tokens(wl, layer, b, int(pos[0]), len(pos), dev)
+                cache.recent_k[b][:, pos % 256] = k.transpose(0, 1)
+                cache.recent_v[b][:, pos % 256] = v.transpose(0, 1)
+        # one decode step: the new token at position L, attention over L + 1 tokens
+        kn, vn = zip(*[workloads.kv_tokens(wl, layer, b, L, 1, dev)
+                       for b, L in enumerate(self.lengths)])
+        self.k_new = torch.cat(kn).contiguous()
+        self.v_new = torch.cat(vn).contiguous()
+        self.q = workloads.queries(wl, layer, 0, dev, batch=self.B).contiguous()
+        pos = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
+        slots = torch.arange(self.B, dtype=torch.int32, device=dev)
+        mx = max(self.lengths) + 1
+        ws = torch.empty(ok.decode_workspace_bytes(self.lay, self.B, mx), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty((self.B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+        ok.decode_step(self.lay, cache.pool, table, cache.sink_k, cache.sink_v, cache.recent_k,
+                       cache.recent_v, uk, uv, ck, cv, self.k_new, self.v_new, slots, pos,
+                       self.q, out, ws, mx)
+        torch.cuda.synchronize()
+        self.cache = cache
+        self.out = out.cpu().numpy()
+        self.blocks = cache.pool.view(self.num_pages, hkv, self.geom.block_bytes)
+
+    def token(self, b, position):
+        """(k, v) fp32 [Hkv, d] of one position, drawn on the device the layer was built from."""
+        k, v = workloads.kv_tokens(self.wl, self.layer, b, position, 1, "cuda")
+        return bf16_np(k[0]), bf16_np(v[0])
+
+    def check_demotion(self, samples):
+        """samples: (b, history index, kv head) triples; both K and V of each are checked."""
+        flips = 0
+        for b, t, h in samples:
+            k, v = self.token(b, 64 + t)
+            blk = self.blocks[int(self.table[b, t // 64]), h].cpu().numpy()
+            for tensor, x, u, c in (("k", k, self.u_k, self.clip_k), ("v", v, self.u_v,
+                                                                     self.clip_v)):
+                flips += check_token(blk, t % 64, tensor, x[h][None], u[h].numpy(), c[h],
+                                     self.geom, (b, t, h, tensor))
+        assert flips <= MAX_FLIP_FRACTION * len(samples) * 2 * 128 + 1, flips
+        return flips
+
+    def check_attention(self, b, kv):
+        """Oracle attention of sequence b, KV head kv's query heads on the GPU's cache bytes."""
+        wl, g = self.wl, self.geom
+        L = self.lengths[b] + 1
+        n_pages = workloads.history_pages(L)
+        ids = torch.from_numpy(self.table[b, :n_pages].astype(np.int64)).cuda()
+        pool = self.blocks.index_select(0, ids).cpu().numpy() if n_pages else \
+            np.zeros((1, wl.num_kv_heads, g.block_bytes), np.uint8)
+        table = np.arange(max(n_pages, 1), dtype=np.int32)[None]
+        seg = [bf16_np(t[b:b + 1]) for t in (self.cache.sink_k, self.cache.sink_v,
+                                             self.cache.recent_k, self.cache.recent_v)]
+        heads = [(0, kv * wl.gqa + i) for i in range(wl.gqa)]
+        ref, _ = oracle.decode_attention(pool, table, *seg, [0], [L],
+                                         bf16_np(self.q[b:b + 1]), self.u_k.numpy(),
+                                         self.u_v.numpy(), g, heads=heads)
+        rows = [(0, h) for _, h in heads]
+        err = attention_error(self.out[b:b + 1], ref, rows)
+        _note(f"  attention b={b} kv={kv} L={L}: max row error {err:.2e}")
+        assert err <= ATTN_TOL
+        return err
+
+
+def _samples(rng, layer, count, heads=None):
+    """Random (b, history index, kv) triples over the layer's history before the step, plus the
+    token each sampled sequence demoted during the step."""
+    out = []
+    hkv = layer.wl.num_kv_heads
+    seqs = [b for b, L in enumerate(layer.lengths) if L > 320]
+    for _ in range(count):
+        b = int(rng.choice(seqs))
+        out.append((b, int(rng.integers(0, layer.lengths[b] - 320)),
+                    int(rng.integers(0, hkv)) if heads is None else int(rng.choice(heads))))
+    for b in sorted({s[0] for s in out})[:4]:
+        out.append((b, layer.lengths[b] - 320, int(rng.integers(0, hkv))))
+    return out
+
+
+def test_full_size_qwen3_8b_100k():
+    wl = workloads.get("qwen3_8b_100k")
+    _note("qwen3_8b_100k layer 0: building 99,681 history tokens x 8 KV heads")
+    layer = FullLayer(wl, layer=0)
+    rng = np.random.default_rng(31)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    for kv in (0, 5):
+        layer.check_attention(0, kv)
+
+
+def test_full_size_qwen3_8b_b64_shared_prefix():
+    wl = workloads.get("qwen3_8b_b64_prefix")
+    layer = FullLayer(wl, layer=0)
+    lens = layer.lengths
+    _note(f"qwen3_8b_b64_prefix: 64 sequences, lengths {min(lens)}..{max(lens)}")
+    rng = np.random.default_rng(32)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    order = np.argsort(lens)
+    for b, kv in ((int(order[-1]), 3), (int(order[0]), 6), (int(order[32]), 0)):
+        layer.check_attention(b, kv)
+
+
+def test_full_size_qwen3_32b_131k_gqa8_group64():
+    wl = workloads.get("qwen3_32b_131k")
+    u = workloads.rotation_bases(wl, 0)
+    # calibrated clip: 99.9th percentile of |x R| over the first clip_calib_tokens positions
+    k, v = workloads.kv_tokens(wl, 0, 0, 0, wl.clip_calib_tokens, "cuda")
+    k, v = bf16_np(k), bf16_np(v)
+    clip_k = np.array([oracle.clip_threshold(k[:, h], u[0][h].numpy())
+                       for h in range(wl.num_kv_heads)], np.float32)
+    clip_v = np.array([oracle.clip_threshold(v[:, h], u[1][h].numpy())
+                       for h in range(wl.num_kv_heads)], np.float32)
+    _note(f"qwen3_32b_131k: 16 x 130,752 history tokens, clip_k {clip_k.round(2).tolist()}")
+    layer = FullLayer(wl, layer=0, u=u, clip=(clip_k, clip_v))
+    rng = np.random.default_rng(33)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    for b, kv in ((0, 2), (15, 7)):
+        layer.check_attention(b, kv)
+
+
+def test_full_size_qwen3_4b_32k_calibrated():
+    # KV head 0 is calibrated by the oracle (U_k, U_v from the calibration queries of its query
+    # heads over the layer's own context, clip = 99.9th percentile); the other heads keep seeded
+    # orthogonal bases and clip 4.0 (they only fill the launch).
+    wl = workloads.get("qwen3_4b_32k")
+    hkv, gq = wl.num_kv_heads, wl.gqa
+    qr = workloads.rotation_bases(workloads.scaled(wl, rotation="qr"), 0)
+    u_k, u_v = qr[0].clone(), qr[1].clone()
+    clip_k = np.full(hkv, 4.0, np.float32)
+    clip_v = np.full(hkv, 4.0, np.float32)
+    q_cal = workloads.calibration_queries(wl, 0).double().numpy()[:, :gq].reshape(-1, 128)
+    k, v = workloads.kv_tokens(wl, 0, 0, 0, wl.context, "cuda")
+    k0, v0 = bf16_np(k[:, 0]), bf16_np(v[:, 0])
+    uk0 = oracle.key_rotation(q_cal)
+    uv0 = oracle.value_rotation(q_cal, k0, v0, 1.0 / math.sqrt(128))
+    u_k[0] = torch.from_numpy(uk0.astype(np.float32))
+    u_v[0] = torch.from_numpy(uv0.astype(np.float32))
+    clip_k[0] = oracle.clip_threshold(k0, u_k[0].numpy())
+    clip_v[0] = oracle.clip_threshold(v0, u_v[0].numpy())
+    _note(f"qwen3_4b_32k: calibrated KV head 0, clip ({clip_k[0]:.3f}, {clip_v[0]:.3f})")
+    layer = FullLayer(wl, layer=0, u=(u_k, u_v), clip=(clip_k, clip_v))
+    rng = np.random.default_rng(34)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96, heads=[0]))}")
+    for kv in (0, 5):
+        layer.check_attention(0, kv)
