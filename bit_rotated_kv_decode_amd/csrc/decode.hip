@@ -59,13 +59,14 @@ template <int G, int NG>
 struct Int2Lds {
   static constexpr int GP = G <= 4 ? 4 : 8;
   static constexpr int PB = 4 * NG * 16 * kPage * 2;         // [wave][g][row][token] bf16
-  static constexpr int RED = 4 * 2 * GP * kHeadDim * 4;      // [wave][row][ch] fp32
+  static constexpr int RED = 4 * 2 * GP * kHeadDim * 4;      // [wave][ch][row] fp32
   static constexpr int MAIN = PB > RED ? PB : RED;
   static constexpr int PAGE_IDS = MAIN;                      // int [kMaxPagesPerSplit]
   static constexpr int RED_M = PAGE_IDS + 4 * kMaxPagesPerSplit;
   static constexpr int RED_L = RED_M + 4 * 4 * GP;
   static constexpr int RED_Z = RED_L + 4 * 4 * GP;
-  static constexpr int TOTAL = RED_Z + 4 * 4 * GP * NG;
+  static constexpr int CF = RED_Z + 4 * 4 * GP * NG;          // [G][4] wave weights
+  static constexpr int TOTAL = CF + 4 * 4 * G;
 };
 
 template <int G, int NG>
@@ -89,7 +90,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   const int p0 = split * p.pages_per_split;
   if (p0 >= n_pages) return;
   const int p1 = min(p0 + p.pages_per_split, n_pages);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = dev::lane_id();
   const int gq = lane >> 4, n = lane & 15;
   const int head0 = b * p.hq + kv * G;
@@ -140,20 +141,22 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   auto pbuf = [&](int pp, int g, int row) -> __bf16* {
     return pbuf_all + ((((wave * PP + pp) * NG + g) * 16 + row) * kPage);
   };
-  // rows 2 GP .. 15 of every P tile stay zero (value operands of unused rows)
-  if constexpr (2 * GP < 16) {
-    constexpr int per = (16 - 2 * GP) * kPage;
-    for (int i = lane; i < PP * NG * per; i += 64) {
-      const int pg2 = i / per, rem = i % per;
-      pbuf(pg2 / NG, pg2 % NG, 2 * GP + rem / kPage)[rem % kPage] = static_cast<__bf16>(0.f);
-    }
+  // rows 2 GP .. 15 of every P tile stay zero (value operands of unused rows): 8 rows x 64
+  // tokens x 2 bytes = 64 lanes x 16 bytes per tile
+  if constexpr (2 * GP == 8) {
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        reinterpret_cast<uint4*>(pbuf(pp, g, 2 * GP))[lane] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
-  float m_run[4], l_run[4], z_run[4][NG];
+  float m_run[4], m_thr[4], l_run[4], z_run[4][NG];   // m_thr = m_run + tau
 #pragma unroll
   for (int hs = 0; hs < 4; ++hs) {
     m_run[hs] = -INFINITY;
+    m_thr[hs] = -INFINITY;
     l_run[hs] = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) z_run[hs][g] = 0.f;
@@ -182,7 +185,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     return e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
   };
   auto load_page = [&](int pg, PageRegs& r) {
-    const uint8_t* blk = a.pool + (static_cast<int64_t>(page_ids[pg - p0]) * p.hkv + kv) * BLK;
+    const int pid = __builtin_amdgcn_readfirstlane(page_ids[pg - p0]);   // wave-uniform
+    const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
     const uint4* kc = reinterpret_cast<const uint4*>(blk + kKCodesOff);
     const uint4* vc = reinterpret_cast<const uint4*>(blk + kVCodesOff);
     r.k[0] = kc[lane];
@@ -257,16 +261,20 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
       for (int pa = 0; pa < NACC; ++pa) {
+        // a slot past the history holds arbitrary bytes: its meta is replaced by zeros (finite
+        // scores, no value contribution) and its logit by -inf
         valid[pp][pa] = (pg + pp) * kPage + tok_of(pa) < n_hist && pg + pp < p1;
         float ks[NG], kz[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          const uint32_t km = r[pp].km[pa][g], vm = r[pp].vm[pa][g];
+          const uint32_t km = valid[pp][pa] ? r[pp].km[pa][g] : 0u;
+          const uint32_t vm = valid[pp][pa] ? r[pp].vm[pa][g] : 0u;
           ks[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km & 0xFFFF)));
           kz[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km >> 16)));
           vs[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm & 0xFFFF)));
           vz[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm >> 16)));
         }
+        const float bias = valid[pp][pa] ? 0.f : -INFINITY;
 #pragma unroll
         for (int hs = 0; hs < 4; ++hs) {
           float t = 0.f;
@@ -274,7 +282,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           for (int g = 0; g < NG; ++g) {
             t = fmaf(ks[g], static_cast<float>(sc[pp][pa][g][hs]), fmaf(kz[g], sq[hs][g], t));
           }
-          logit[pp][pa][hs] = valid[pp][pa] ? t * kh[hs] : -INFINITY;
+          logit[pp][pa][hs] = fmaf(t, kh[hs], bias);
         }
       }
     // ---- online softmax with lazy rescaling (wave-uniform branch)
@@ -284,7 +292,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
       for (int pa = 0; pa < NACC; ++pa)
 #pragma unroll
-        for (int hs = 0; hs < 4; ++hs) grow |= logit[pp][pa][hs] > m_run[hs] + kTau;
+        for (int hs = 0; hs < 4; ++hs) grow |= logit[pp][pa][hs] > m_thr[hs];
     if (__any(grow)) {
 #pragma unroll
       for (int hs = 0; hs < 4; ++hs) {
@@ -304,6 +312,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
         const float mn = fmaxf(m_run[hs], v);
         const float alpha = __builtin_amdgcn_exp2f(m_run[hs] - mn);
         m_run[hs] = mn;
+        m_thr[hs] = mn + kTau;
         l_run[hs] *= alpha;
 #pragma unroll
         for (int g = 0; g < NG; ++g) z_run[hs][g] *= alpha;
@@ -319,13 +328,13 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
         const int t = ppos(tok_of(pa));
 #pragma unroll
         for (int hs = 0; hs < 4; ++hs) {
-          const float pr = __builtin_amdgcn_exp2f(logit[pp][pa][hs] - m_run[hs]);  // 0: invalid
+          const float pr = __builtin_amdgcn_exp2f(logit[pp][pa][hs] - m_run[hs]);  // 0: invalid slot
           l_run[hs] += pr;
           const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            z_run[hs][g] = valid[pp][pa] ? fmaf(pr, vz[pp][pa][g], z_run[hs][g]) : z_run[hs][g];
-            const float pt = valid[pp][pa] ? pr * vs[pp][pa][g] : 0.f;
+            z_run[hs][g] = fmaf(pr, vz[pp][pa][g], z_run[hs][g]);
+            const float pt = pr * vs[pp][pa][g];
             const __bf16 hi = static_cast<__bf16>(pt);
             const __bf16 lo = static_cast<__bf16>(pt - static_cast<float>(hi));
             pbuf(pp, g, hd)[t] = hi;
@@ -414,39 +423,47 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     }
   }
   __syncthreads();
+  // accumulator rows to LDS as [wave][channel][row]: lane (gq, n) holds rows 4 gq .. 4 gq + 3 of
+  // channel 16 nt + n, one 16-byte store each
+  if (gq < 2 * GP / 4) {
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * gq + i;
-      if (row < 2 * GP) red_acc[(wave * 2 * GP + row) * kHeadDim + 16 * nt + n] = acc[nt][i];
-    }
-  __syncthreads();
-
+    for (int nt = 0; nt < 8; ++nt)
+      *reinterpret_cast<v4f*>(red_acc + ((wave * kHeadDim + 16 * nt + n) * 2 * GP + 4 * gq)) =
+          acc[nt];
+  }
   // ---- combine the 4 waves and write this split's partial:
   // acc'[h][ch] = sum_w f_w (P_hi row + P_lo row + z_w)  with f_w = 2^(m_w - m)
   float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
   float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
+  float (*cf)[4] = reinterpret_cast<float (*)[4]>(smem + S::CF);
   const int nw = min(4, (p1 - p0 + PP - 1) / PP);
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float mm = -INFINITY;
+    for (int w = 0; w < nw; ++w) mm = fmaxf(mm, red_m[w][h]);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = w < nw ? __builtin_amdgcn_exp2f(red_m[w][h] - mm) : 0.f;
+      cf[h][w] = f;
+      l = fmaf(w < nw ? red_l[w][h] : 0.f, f, l);
+    }
+    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
+    ml[prow * 2] = mm;
+    ml[prow * 2 + 1] = l;
+  }
+  __syncthreads();
   for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
     const int h = i / kHeadDim, j = i % kHeadDim;
     const int g = NG == 2 ? j / 64 : 0;
-    float mm = -INFINITY;
-    for (int w = 0; w < nw; ++w) mm = fmaxf(mm, red_m[w][h]);
-    float s = 0.f, l = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float f = exp2f(red_m[w][h] - mm);
-      s = fmaf(red_acc[(w * 2 * GP + h) * kHeadDim + j] + red_acc[(w * 2 * GP + GP + h) * kHeadDim + j] +
-                   red_z[w][h][g],
-               f, s);
-      l = fmaf(red_l[w][h], f, l);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* rw = red_acc + (w * kHeadDim + j) * 2 * GP;
+      s = fmaf((rw[h] + rw[GP + h]) + red_z[w][h][g], cf[h][w], s);
     }
     const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
     pacc[prow * kHeadDim + j] = s;
-    if (j == 0) {
-      ml[prow * 2] = mm;
-      ml[prow * 2 + 1] = l;
-    }
   }
 }
 
