@@ -38,11 +38,9 @@ __device__ __forceinline__ v2bf codes_to_bf16(uint32_t x) {
 // ------------------------------------------------------------------------------------------
 // 2. INT2 split-KV decode on the matrix cores.
 //
-// Block = 4 waves on pages [p0, p1) of one (sequence, KV head).  A wave takes PP consecutive
-// pages per step (PP = 2 unless registers do not allow it): wave w's steps start at pages
-// p0 + PP (4 i + w), i = 0, 1, ...  The pages of a step are independent chains that the wave
-// interleaves, and the next step's loads are in flight while a step is processed (two register
-// sets used in turn).
+// Block = 4 waves on pages [p0, p1) of one (sequence, KV head).  Wave w takes pages p0 + w + 4 i,
+// i = 0, 1, ..., one per step; the next page's loads are in flight while a page is processed
+// (two register sets used in turn).
 //
 // Scores: D[row, token] = sum_k A[row, k] B[k, token] with v_mfma_i32_16x16x64_i8.  B = key codes
 // of 16 tokens (lane n + 16 qd holds token n's packed dwords qd and 4 + qd, spread into bytes);
@@ -53,20 +51,16 @@ __device__ __forceinline__ v2bf codes_to_bf16(uint32_t x) {
 // Values: acc[row, ch] += sum_t P[row, t] V[t, ch] with v_mfma_f32_16x16x32_bf16; P rows are the
 // bf16 hi and lo parts of p * s_v for each head, transposed through LDS; V = value codes turned
 // into exact bf16 integers by the FP4 conversion path.
-// LDS carve-up of an INT2 block.  The P tiles are dead after the page loop, where the same bytes
-// take the per-wave accumulator rows.
+// LDS carve-up of an INT2 block: per-wave P tiles, and apart from them the per-wave accumulator
+// rows and softmax statistics that the block combines at the end.
 template <int G, int NG>
 struct Int2Lds {
   static constexpr int GP = G <= 4 ? 4 : 8;
   static constexpr int PB = 4 * NG * 16 * kPage * 2;         // [wave][g][row][token] bf16
-  static constexpr int RED = 4 * 2 * GP * kHeadDim * 4;      // [wave][ch][row] fp32
-  static constexpr int MAIN = PB > RED ? PB : RED;
-  static constexpr int PAGE_IDS = MAIN;                      // int [kMaxPagesPerSplit]
-  static constexpr int RED_M = PAGE_IDS + 4 * kMaxPagesPerSplit;
+  static constexpr int RED = PB;                             // [wave][head][ch] fp32
+  static constexpr int RED_M = RED + 4 * G * kHeadDim * 4;   // [wave][GP] fp32
   static constexpr int RED_L = RED_M + 4 * 4 * GP;
-  static constexpr int RED_Z = RED_L + 4 * 4 * GP;
-  static constexpr int CF = RED_Z + 4 * 4 * GP * NG;          // [G][4] wave weights
-  static constexpr int TOTAL = CF + 4 * 4 * G;
+  static constexpr int TOTAL = RED_L + 4 * 4 * GP;
 };
 
 template <int G, int NG>
@@ -78,25 +72,27 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   constexpr int PP = 1;                   // pages per step
   constexpr int BLK = kMetaOff + kPage * 8 * NG;
   __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem);
-  float* red_acc = reinterpret_cast<float*>(smem);
-  int* page_ids = reinterpret_cast<int*>(smem + S::PAGE_IDS);
+  float* red_acc = reinterpret_cast<float*>(smem + S::RED);
   float (*red_m)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_M);
   float (*red_l)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_L);
-  float (*red_z)[GP][NG] = reinterpret_cast<float (*)[GP][NG]>(smem + S::RED_Z);
 
-  const int L = a.seq_lens[b] + a.len_add;
-  const int n_hist = max(0, L - kSink - kRecent);
-  const int n_pages = (n_hist + kPage - 1) / kPage;
   const int p0 = split * p.pages_per_split;
-  if (p0 >= n_pages) return;
-  const int p1 = min(p0 + p.pages_per_split, n_pages);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = dev::lane_id();
   const int gq = lane >> 4, n = lane & 15;
   const int head0 = b * p.hq + kv * G;
-
-  for (int i = threadIdx.x; i < p1 - p0; i += 256)
-    page_ids[i] = a.page_table[static_cast<int64_t>(b) * a.max_pages_per_seq + p0 + i];
+  // Table entries of this wave's pages p0 + wave + 4 j, one per lane j (at most 64: a split
+  // covers at most 256 pages), read before the sequence length is known so that the first page
+  // loads wait on one memory round trip only.  The index stays inside the table row; entries of
+  // pages past the sequence's end are read but never used.
+  static_assert(PP == 1 && kMaxPagesPerSplit <= 4 * 64, "one page id per lane and wave");
+  const int wave_ids = a.page_table[static_cast<int64_t>(b) * a.max_pages_per_seq +
+                                    min(p0 + wave + 4 * lane, a.max_pages_per_seq - 1)];
+  const int L = a.seq_lens[b] + a.len_add;
+  const int n_hist = max(0, L - kSink - kRecent);
+  const int n_pages = (n_hist + kPage - 1) / kPage;
+  if (p0 >= n_pages) return;
+  const int p1 = min(p0 + p.pages_per_split, n_pages);
 
   // ---- query operands (registers, the same for every page).  Score tile rows hold the int8 hi
   // part of a head's q' and, four rows further, its lo part; GP = 4: operand ts (sub-tiles of
@@ -142,7 +138,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     return pbuf_all + ((((wave * PP + pp) * NG + g) * 16 + row) * kPage);
   };
   // rows 2 GP .. 15 of every P tile stay zero (value operands of unused rows): 8 rows x 64
-  // tokens x 2 bytes = 64 lanes x 16 bytes per tile
+  // tokens x 2 bytes = 64 lanes x 16 bytes per tile.  The tiles are the wave's own and LDS
+  // operations of one wave execute in order, so no barrier is needed before the page loop.
   if constexpr (2 * GP == 8) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
@@ -150,7 +147,6 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       for (int g = 0; g < NG; ++g)
         reinterpret_cast<uint4*>(pbuf(pp, g, 2 * GP))[lane] = make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
 
   float m_run[4], m_thr[4], l_run[4], z_run[4][NG];   // m_thr = m_run + tau
 #pragma unroll
@@ -185,7 +181,9 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     return e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
   };
   auto load_page = [&](int pg, PageRegs& r) {
-    const int pid = __builtin_amdgcn_readfirstlane(page_ids[pg - p0]);   // wave-uniform
+    // lane (pg - p0 - wave) / 4 holds page pg's id; a clamped prefetch index p1 - 1 maps to the
+    // wave's last page below p1 (floor division), whose id is valid
+    const int pid = __builtin_amdgcn_readlane(wave_ids, (pg - p0 - wave) >> 2);
     const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
     const uint4* kc = reinterpret_cast<const uint4*>(blk + kKCodesOff);
     const uint4* vc = reinterpret_cast<const uint4*>(blk + kVCodesOff);
@@ -380,8 +378,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   };
 
   // Ping-pong over steps: while one step is processed from one register set, the next step's
-  // loads are in flight into the other.  Prefetch indices are clamped to the last
-  // page, so every iteration issues the same loads.
+  // loads are in flight into the other.  Prefetch indices are clamped to the last page, so every
+  // iteration issues the same loads (the wait before a step then never covers the next one's).
   PageRegs x[PP], y[PP];
   int pg = p0 + PP * wave;
   auto load_step = [&](int q, PageRegs* r) {
@@ -399,71 +397,86 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     pg += 4 * PP;
   }
 
-  // ---- finish the wave: sums over lanes of the same head; accumulator rows to LDS (the LDS of
-  // the query operands and P tiles is reused, so every wave must be done with it first)
+  // ---- finish the wave: l and z summed over the lanes holding each head; each accumulator row
+  // as hi + lo + z.  acc[nt][hs] of lane (gq, n) is tile row 4 gq + hs of channel 16 nt + n, the
+  // rows being [hi | lo] of heads 0-3 (GP = 4) or [hi 0-7 | lo 0-7] (GP = 8), so one swap of lane
+  // groups 0 <-> 1 (GP = 4) or of wave halves (GP = 8) meets each hi row with its lo row.  The
+  // rows go to the wave's own LDS rows [wave][head][ch], apart from every P tile, so a single
+  // barrier orders them before the combine.
+  auto head_sum = [&](float v) {   // over the lanes of one head, as for the max in the page loop
+    v = dev::row16_sum(v);
+    const float r0 = dev::lane_value(v, 0), r1 = dev::lane_value(v, 16);
+    const float r2 = dev::lane_value(v, 32), r3 = dev::lane_value(v, 48);
+    return GP == 4 ? (r0 + r1) + (r2 + r3) : ((gq & 1) ? r1 + r3 : r0 + r2);
+  };
+  float zs[4][NG];
 #pragma unroll
   for (int hs = 0; hs < 4; ++hs) {
-    // sums over the lanes holding the same head (see the max in the page loop)
-    auto head_sum = [&](float v) {
-      v = dev::row16_sum(v);
-      const float r0 = dev::lane_value(v, 0), r1 = dev::lane_value(v, 16);
-      const float r2 = dev::lane_value(v, 32), r3 = dev::lane_value(v, 48);
-      return GP == 4 ? (r0 + r1) + (r2 + r3) : ((gq & 1) ? r1 + r3 : r0 + r2);
-    };
     const float l = head_sum(l_run[hs]);
-    float z[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) z[g] = head_sum(z_run[hs][g]);
+    for (int g = 0; g < NG; ++g) zs[hs][g] = head_sum(z_run[hs][g]);
     const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
     if (n == 0 && gq < GP / 4) {
       red_m[wave][hd] = m_run[hs];
       red_l[wave][hd] = l;
+    }
+  }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) red_z[wave][hd][g] = z[g];
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int hs = 0; hs < 4; ++hs) {
+      const uint32_t x = __float_as_uint(acc[nt][hs]);
+      const auto sw = GP == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      acc[nt][hs] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) +   // hi + lo
+                    zs[hs][NG == 2 ? nt / 4 : 0];
+    }
+  if (gq < GP / 4) {
+    float* red_w = red_acc + wave * G * kHeadDim;
+#pragma unroll
+    for (int hs = 0; hs < 4; ++hs) {
+      const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
+      if (G % 4 == 0 || hd < G) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) red_w[hd * kHeadDim + 16 * nt + n] = acc[nt][hs];
+      }
     }
   }
   __syncthreads();
-  // accumulator rows to LDS as [wave][channel][row]: lane (gq, n) holds rows 4 gq .. 4 gq + 3 of
-  // channel 16 nt + n, one 16-byte store each
-  if (gq < 2 * GP / 4) {
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      *reinterpret_cast<v4f*>(red_acc + ((wave * kHeadDim + 16 * nt + n) * 2 * GP + 4 * gq)) =
-          acc[nt];
-  }
   // ---- combine the 4 waves and write this split's partial:
-  // acc'[h][ch] = sum_w f_w (P_hi row + P_lo row + z_w)  with f_w = 2^(m_w - m)
+  // acc'[h][ch] = sum_w f_w (P_hi row + P_lo row + z_w)  with f_w = 2^(m_w - m).  Every wave has
+  // written its rows (a wave without pages: m = -inf, l = 0, zero rows, so f_w = 0), and every
+  // LDS read below is issued before the first one is used.
   float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
   float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
-  float (*cf)[4] = reinterpret_cast<float (*)[4]>(smem + S::CF);
-  const int nw = min(4, (p1 - p0 + PP - 1) / PP);
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float mm = -INFINITY;
-    for (int w = 0; w < nw; ++w) mm = fmaxf(mm, red_m[w][h]);
-    float l = 0.f;
+  static_assert(G * kHeadDim % 256 == 0 || G * kHeadDim < 256, "whole rounds of outputs");
+  if (threadIdx.x < G * kHeadDim) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = w < nw ? __builtin_amdgcn_exp2f(red_m[w][h] - mm) : 0.f;
-      cf[h][w] = f;
-      l = fmaf(w < nw ? red_l[w][h] : 0.f, f, l);
-    }
-    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
-    ml[prow * 2] = mm;
-    ml[prow * 2 + 1] = l;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
-    const int h = i / kHeadDim, j = i % kHeadDim;
-    const int g = NG == 2 ? j / 64 : 0;
-    float s = 0.f;
+    for (int r = 0; r < (G * kHeadDim + 255) / 256; ++r) {
+      const int i = threadIdx.x + 256 * r;
+      const int h = i / kHeadDim, j = i % kHeadDim;
+      float mw[4], lw[4], aw[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float* rw = red_acc + (w * kHeadDim + j) * 2 * GP;
-      s = fmaf((rw[h] + rw[GP + h]) + red_z[w][h][g], cf[h][w], s);
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = red_m[w][h];
+        lw[w] = red_l[w][h];
+        aw[w] = red_acc[(w * G + h) * kHeadDim + j];
+      }
+      const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));   // finite: wave 0 has a page
+      float s = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mw[w] - mm);
+        s = fmaf(aw[w], f, s);
+        l = fmaf(lw[w], f, l);
+      }
+      const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
+      pacc[prow * kHeadDim + j] = s;
+      if (j == 0) {
+        ml[prow * 2] = mm;
+        ml[prow * 2 + 1] = l;
+      }
     }
-    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
-    pacc[prow * kHeadDim + j] = s;
   }
 }
 
@@ -606,9 +619,16 @@ constexpr int attn_lds_bytes() {
   return Int2Lds<G, NG>::TOTAL > Bf16Lds<G>::TOTAL ? Int2Lds<G, NG>::TOTAL : Bf16Lds<G>::TOTAL;
 }
 
+// Blocks per compute unit the register budget allows: 3 for one group per vector and up to 4
+// query heads per KV head, else 2 (the work planner sizes the grid with the same rule).
 template <int G, int NG>
-__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
-                                                      int x0) {
+constexpr int attn_blocks_per_cu() {
+  return G <= 4 && NG == 1 ? 3 : 2;
+}
+
+template <int G, int NG>
+__global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kernel(DecodeArgs a, Plan p,
+                                                                    float scale_log2, int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
   const int x = x0 + blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   if (x < kBf16Chunks)
@@ -619,14 +639,15 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void attn_kernel(DecodeArgs a,
 
 // ------------------------------------------------------------------------------------------
 // 4. merge: one 256-thread block per (sequence, query head).  Every global load the block needs
-// (split statistics, the first 64 split accumulators, its rows of U_v, the BF16 partials) is
-// issued before the first reduction, so the block pays about one memory latency.
+// (split statistics, the first 96 split accumulators, its rows of U_v, the BF16 partials) is
+// issued before the first reduction and none waits on the sequence length (entries of splits the
+// sequence does not reach are read but masked), so the block pays about one memory latency.
 //   (1) weights f_s = 2^(m_s - m) of the INT2 splits, m and l by block reductions;
 //   (2) acc' = sum_s f_s acc'_s with thread (channel quad, split residue mod 8) partial sums;
 //   (3) (acc' P) H / sqrt(d) by butterflies across one wave, then times U_v^T (two threads per
 //       output channel);
 //   (4) merge with the BF16 chunk partials and normalise.
-constexpr int kMergePrefetch = 8;   // split accumulators per thread loaded up front (64 splits)
+constexpr int kMergePrefetch = 12;   // split accumulators per thread loaded up front (96 splits)
 
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ float f_s[kMaxSplits];
@@ -655,18 +676,20 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int oj = tid & 127, oh = tid >> 7;    // (3): output channel, half of the inputs
 
   // ---- loads
+  static_assert(kMaxSplits <= 4 * 256, "split statistics: four per thread");
   float2 st[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = tid + 256 * i;
-    st[i] = s < n_valid ? reinterpret_cast<const float2*>(iml)[s] : make_float2(-INFINITY, 0.f);
+    st[i] = s < p.num_splits ? reinterpret_cast<const float2*>(iml)[s]
+                             : make_float2(-INFINITY, 0.f);
   }
   float4 pa[kMergePrefetch];
 #pragma unroll
   for (int i = 0; i < kMergePrefetch; ++i) {
     const int s = sr + 8 * i;
-    pa[i] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    pa[i] = s < p.num_splits ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 uv[16];
   {
@@ -683,9 +706,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     ba[c] = bacc[c * kHeadDim + oj];
   }
 
-  // ---- (1) max and weights of the INT2 splits
+  // ---- (1) max and weights of the INT2 splits the sequence reaches
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (tid + 256 * i >= n_valid) st[i] = make_float2(-INFINITY, 0.f);
   float mloc = fmaxf(fmaxf(st[0].x, st[1].x), fmaxf(st[2].x, st[3].x));
-  for (int s = tid + 1024; s < n_valid; s += 256) mloc = fmaxf(mloc, iml[2 * s]);
   mloc = dev::wave_max(mloc);
   if (lane == 0) red[wave] = mloc;
   __syncthreads();
@@ -699,11 +724,6 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
       f_s[s] = f;
       lloc = fmaf(st[i].y, f, lloc);
     }
-  }
-  for (int s = tid + 1024; s < n_valid; s += 256) {
-    const float f = exp2f(iml[2 * s] - mi);
-    f_s[s] = f;
-    lloc = fmaf(iml[2 * s + 1], f, lloc);
   }
   lloc = dev::wave_sum(lloc);
   if (lane == 0) red[4 + wave] = lloc;
@@ -723,8 +743,19 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
       const int s = sr + 8 * i;
       if (s < n_valid) add(pa[i], f_s[s]);
     }
-    for (int s = sr + 8 * kMergePrefetch; s < n_valid; s += 8)
-      add(iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq], f_s[s]);
+    // splits past the prefetch: four loads in flight per round
+    for (int s0 = sr + 8 * kMergePrefetch; s0 < n_valid; s0 += 32) {
+      float4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int s = s0 + 8 * k;
+        v[k] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (s0 + 8 * k < n_valid) add(v[k], f_s[s0 + 8 * k]);
+    }
     reinterpret_cast<float4*>(part[sr])[cq] = s4;
   }
   __syncthreads();

@@ -77,7 +77,7 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   // Aim for one round of blocks over the compute units: the INT2 work items share the launch
   // with the BF16 chunk blocks, and kernels with more registers per lane hold fewer blocks per
   // compute unit.  At least one page per wave, within the per-item page and per-head item limits.
-  const long long slots = p.gqa == 8 ? kInt2Items * 2 / 3 : kInt2Items;
+  const long long slots = p.gqa <= 4 && p.n_groups == 1 ? kInt2Items : kInt2Items * 2 / 3;
   const long long bf16_blocks = static_cast<long long>(kBf16Chunks) * batch * p.hkv;
   const long long target = bf16_blocks * 2 <= slots ? slots - bf16_blocks : slots;
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
@@ -167,6 +167,9 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   if (plan.max_pages > l->max_pages_per_seq)
     return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
                 max_seq_len, plan.max_pages, l->max_pages_per_seq);
+  if (plan.num_splits > oscar::kMaxSplits)
+    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d INT2 work items per head > %d",
+                max_seq_len, plan.num_splits, oscar::kMaxSplits);
   if ((plan.max_pages > 0 && (!pool || !page_table)) || !sink_k || !sink_v || !recent_k ||
       !recent_v || !seq_slot || !seq_lens || !q || !u_k || !u_v || !out)
     return fail(OSCAR_ERR_NULL, "decode: a required pointer is NULL");

@@ -15,7 +15,7 @@ constexpr int kSink = 64;
 constexpr int kRecent = 256;
 constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the BF16 segments
 constexpr int kMaxGqa = 8;
-constexpr int kMaxPagesPerSplit = 1024;   // history pages one INT2 work item may cover
+constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
 constexpr int kInt2Items = 768;           // 256-thread blocks resident at once (3 per compute unit)
 

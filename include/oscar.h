@@ -192,7 +192,7 @@ oscar_status oscar_append(const oscar_layout* layout, void* pool, const int32_t*
  * q: bf16 [batch][Hq][d].  out: fp32 [batch][Hq][d].  lse: optional fp32 [batch][Hq] natural-log
  * sum of exp(sm_scale * scores) (NULL to skip).  sm_scale <= 0 selects 1/sqrt(d).
  * seq_lens[b] must be in [1, max_seq_len]; max_seq_len is a host-side bound used for work
- * planning.  workspace: at least oscar_decode_workspace_bytes(layout, batch, max_seq_len) bytes,
+ * planning, at most 64 * 256 * 1024 + 320 tokens (RANGE beyond).  workspace: at least oscar_decode_workspace_bytes(layout, batch, max_seq_len) bytes,
  * 256-byte aligned; its contents on entry do not matter.
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
 oscar_status oscar_decode_attn(const oscar_layout* layout, const void* pool,
