@@ -126,6 +126,16 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
     for (int g = 0; g < NG; ++g) sq[hs][g] = m[1 + g];
   }
+  // Combines the per-row results of a 16-lane reduction over the rows holding the same head: all
+  // four rows (GP = 4) or rows r and r ^ 2 (GP = 8), with lane swaps; every lane gets the result.
+  auto head_reduce = [](float v, auto op) {
+    if constexpr (GP == 4) {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));   // rows (0 + 1), (2 + 3)
+    }
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  };
   // token (within a page) of this lane's score vector pa: after the hi / lo lane swap, lane group
   // gq holds sub-tile (0, 2, 1, 3)[gq] (GP = 4) or sub-tile 2 pa + gq / 2 (GP = 8)
   auto tok_of = [&](int pa) {
@@ -300,13 +310,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
           for (int pa = 0; pa < NACC; ++pa) v = fmaxf(v, logit[pp][pa][hs]);
         // lanes holding the same head: all 64 (GP = 4) or lane groups of the same parity (GP = 8)
-        v = dev::row16_max(v);
-        const float r0 = dev::lane_value(v, 0), r1 = dev::lane_value(v, 16);
-        const float r2 = dev::lane_value(v, 32), r3 = dev::lane_value(v, 48);
-        if (GP == 4)
-          v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-        else
-          v = (gq & 1) ? fmaxf(r1, r3) : fmaxf(r0, r2);
+        v = head_reduce(dev::row16_max(v), [](float a, float b) { return fmaxf(a, b); });
         const float mn = fmaxf(m_run[hs], v);
         const float alpha = __builtin_amdgcn_exp2f(m_run[hs] - mn);
         m_run[hs] = mn;
@@ -404,10 +408,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // rows go to the wave's own LDS rows [wave][head][ch], apart from every P tile, so a single
   // barrier orders them before the combine.
   auto head_sum = [&](float v) {   // over the lanes of one head, as for the max in the page loop
-    v = dev::row16_sum(v);
-    const float r0 = dev::lane_value(v, 0), r1 = dev::lane_value(v, 16);
-    const float r2 = dev::lane_value(v, 32), r3 = dev::lane_value(v, 48);
-    return GP == 4 ? (r0 + r1) + (r2 + r3) : ((gq & 1) ? r1 + r3 : r0 + r2);
+    return head_reduce(dev::row16_sum(v), [](float a, float b) { return a + b; });
   };
   float zs[4][NG];
 #pragma unroll
