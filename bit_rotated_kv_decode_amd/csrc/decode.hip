@@ -639,32 +639,32 @@ __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kerne
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. merge: one 256-thread block per (sequence, query head).  Every global load the block needs
-// (split statistics, the first 96 split accumulators, its rows of U_v, the BF16 partials) is
-// issued before the first reduction and none waits on the sequence length (entries of splits the
-// sequence does not reach are read but masked), so the block pays about one memory latency.
+// 4. merge: kMergeParts 256-thread blocks per (sequence, query head); block part q produces output
+// channels [32 q, 32 q + 32).  Each block combines all INT2 splits of its row (the rotated-frame
+// vector is needed whole for the Hadamard transform) but reads only its 32 rows of U_v, so the
+// per-block load volume is about half of one block doing the whole row, spread over four times
+// as many compute units.  Every global load is issued before the first reduction and none waits
+// on the sequence length (entries of splits the sequence does not reach are read but masked).
 //   (1) weights f_s = 2^(m_s - m) of the INT2 splits, m and l by block reductions;
 //   (2) acc' = sum_s f_s acc'_s with thread (channel quad, split residue mod 8) partial sums;
-//   (3) (acc' P) H / sqrt(d) by butterflies across one wave, then times U_v^T (two threads per
-//       output channel);
+//   (3) (acc' P) H / sqrt(d) by butterflies across one wave; then times U_v^T: eight threads per
+//       output channel, 16 inputs each, summed across the eight lanes;
 //   (4) merge with the BF16 chunk partials and normalise.
 constexpr int kMergePrefetch = 12;   // split accumulators per thread loaded up front (96 splits)
+constexpr int kMergeParts = 4;       // blocks per (sequence, query head)
+constexpr int kMergeCols = kHeadDim / kMergeParts;
 
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ float f_s[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float part[8][kHeadDim];
-  __shared__ float vec[kHeadDim];
-  __shared__ float outp[2][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float vec[kHeadDim];
   __shared__ float red[8];
-  const int row = blockIdx.x;   // b * hq + head
+  const int row = blockIdx.x / kMergeParts;   // b * hq + head
+  const int q = blockIdx.x % kMergeParts;
   const int b = row / p.hq;
   const int kv = (row % p.hq) / p.gqa;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
-  const int L = a.seq_lens[b] + a.len_add;
-  const int n_hist = max(0, L - kSink - kRecent);
-  const int n_pages = (n_hist + kPage - 1) / kPage;
-  const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
   const float* iml = reinterpret_cast<const float*>(a.workspace + p.off_int2_ml) +
                      static_cast<int64_t>(row) * p.num_splits * 2;
   const float4* iacc = reinterpret_cast<const float4*>(a.workspace + p.off_int2_acc) +
@@ -674,7 +674,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const float* bacc = reinterpret_cast<const float*>(a.workspace + p.off_bf16_acc) +
                       static_cast<int64_t>(row) * kBf16Chunks * kHeadDim;
   const int cq = tid & 31, sr = tid >> 5;     // (2): channel quad, split residue
-  const int oj = tid & 127, oh = tid >> 7;    // (3): output channel, half of the inputs
+  const int jl = tid >> 3, ip = tid & 7;      // (3): output channel 32 q + jl, input part
+  const int j = kMergeCols * q + jl;
 
   // ---- loads
   static_assert(kMaxSplits <= 4 * 256, "split statistics: four per thread");
@@ -692,20 +693,24 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     pa[i] = s < p.num_splits ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float4 uv[16];
+  float4 uv[4];   // U_v[kv][j][16 ip .. 16 ip + 15]
   {
     const float4* u = reinterpret_cast<const float4*>(
-        a.u_v + (static_cast<int64_t>(kv) * kHeadDim + oj) * kHeadDim + oh * 64);
+        a.u_v + (static_cast<int64_t>(kv) * kHeadDim + j) * kHeadDim + 16 * ip);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) uv[c] = u[c];
+    for (int c = 0; c < 4; ++c) uv[c] = u[c];
   }
   float bm[kBf16Chunks], bl[kBf16Chunks], ba[kBf16Chunks];
 #pragma unroll
   for (int c = 0; c < kBf16Chunks; ++c) {
     bm[c] = bml[2 * c];
     bl[c] = bml[2 * c + 1];
-    ba[c] = bacc[c * kHeadDim + oj];
+    ba[c] = ip == 0 ? bacc[c * kHeadDim + j] : 0.f;
   }
+  const int L = a.seq_lens[b] + a.len_add;
+  const int n_hist = max(0, L - kSink - kRecent);
+  const int n_pages = (n_hist + kPage - 1) / kPage;
+  const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
 
   // ---- (1) max and weights of the INT2 splits the sequence reaches
 #pragma unroll
@@ -762,8 +767,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __syncthreads();
   // ---- (3) (acc' P) H / sqrt(d) in wave 0: lane holds entries lane and lane + 64
   if (wave == 0) {
-    auto gather = [&](int j) {
-      const int src = dev::bitrev7(j);   // (acc' P)_j = acc'_rev(j)
+    auto gather = [&](int jj) {
+      const int src = dev::bitrev7(jj);   // (acc' P)_j = acc'_rev(j)
       float v = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) v += part[r][src];
@@ -787,22 +792,26 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     vec[lane + 64] = y1;
   }
   __syncthreads();
+  float o = 0.f;
   {
-    float o = 0.f;
+    const float4 v4[4] = {reinterpret_cast<const float4*>(vec)[4 * ip],
+                          reinterpret_cast<const float4*>(vec)[4 * ip + 1],
+                          reinterpret_cast<const float4*>(vec)[4 * ip + 2],
+                          reinterpret_cast<const float4*>(vec)[4 * ip + 3]};
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int i = oh * 64 + 4 * c;
-      o = fmaf(vec[i], uv[c].x, o);
-      o = fmaf(vec[i + 1], uv[c].y, o);
-      o = fmaf(vec[i + 2], uv[c].z, o);
-      o = fmaf(vec[i + 3], uv[c].w, o);
+    for (int c = 0; c < 4; ++c) {
+      o = fmaf(v4[c].x, uv[c].x, o);
+      o = fmaf(v4[c].y, uv[c].y, o);
+      o = fmaf(v4[c].z, uv[c].z, o);
+      o = fmaf(v4[c].w, uv[c].w, o);
     }
-    outp[oh][oj] = o;
+    // sum over the eight input parts (lanes 8 jl .. 8 jl + 7 of the wave)
+    o += __shfl_xor(o, 1);
+    o += __shfl_xor(o, 2);
+    o += __shfl_xor(o, 4);
   }
-  __syncthreads();
   // ---- (4) merge with the BF16 partials
-  if (tid < kHeadDim) {
-    const int j = tid;
+  if (ip == 0) {
     const float m_int2 = n_valid > 0 ? mi : -INFINITY;
     float mt = m_int2;
 #pragma unroll
@@ -810,7 +819,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     float acc = 0.f, l = 0.f;
     if (m_int2 != -INFINITY) {
       const float f = exp2f(m_int2 - mt);
-      acc = (outp[0][j] + outp[1][j]) * 0.08838834764831845f * f;
+      acc = o * 0.08838834764831845f * f;
       l = li * f;
     }
 #pragma unroll
@@ -838,7 +847,8 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
       hipLaunchKernelGGL((attn_kernel<G, 2>), grid, dim3(256), 0, stream, a, p, scale_log2, x0);
   }
   if (stages & OSCAR_STAGE_MERGE)
-    hipLaunchKernelGGL(merge_kernel, dim3(p.batch * p.hq), dim3(256), 0, stream, a, p);
+    hipLaunchKernelGGL(merge_kernel, dim3(p.batch * p.hq * kMergeParts), dim3(256), 0, stream, a,
+                       p);
   return hipGetLastError();
 }
 
