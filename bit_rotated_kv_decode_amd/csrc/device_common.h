@@ -19,22 +19,48 @@ __device__ __forceinline__ int bitrev7(int j) {
   return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(j)) >> 25);
 }
 
+// DPP move of a 32-bit value: lane l receives the source lane that `ctrl` selects within its row
+// of 16 (row_mask / bank_mask all on; lanes without a source keep `old`).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old),
+                                                           static_cast<int>(v), CTRL, 0xF, 0xF,
+                                                           false));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1, 0, 3, 2]: lane l ^ 1
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2, 3, 0, 1]: lane l ^ 2
+constexpr int kRowShl4 = 0x104;    // lane l + 4 (within the row)
+constexpr int kRowShr4 = 0x114;    // lane l - 4
+constexpr int kRowRor4 = 0x124;    // lane (l + 4) mod 16
+constexpr int kRowRor8 = 0x128;    // lane (l + 8) mod 16 = l ^ 8
+
+// Reduction of a 32-bit value over the whole wave without LDS traffic: DPP steps within each
+// row of 16, then the swaps of rows 0 <-> 1, 2 <-> 3 and of the wave halves.  Every lane gets
+// the result.  Requires all 64 lanes active.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  auto bits = [](T x) { return __builtin_bit_cast(uint32_t, x); };
+  auto val = [](uint32_t x) { return __builtin_bit_cast(T, x); };
+  v = op(v, val(dpp<kQuadSwap1>(0u, bits(v))));
+  v = op(v, val(dpp<kQuadSwap2>(0u, bits(v))));
+  v = op(v, val(dpp<kRowRor4>(0u, bits(v))));
+  v = op(v, val(dpp<kRowRor8>(0u, bits(v))));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(bits(v), bits(v), false, false);
+  v = op(val(s16[0]), val(s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(bits(v), bits(v), false, false);
+  return op(val(s32[0]), val(s32[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fminf(a, b); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 // Max / sum over each row of 16 lanes with DPP moves (no LDS traffic): after the call every lane
@@ -62,9 +88,55 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  return wave_reduce(v, [](int a, int b) { return a + b; });
+}
+
+// Value of lane l ^ M for a 64-bit value (M in 1, 2, 4, 8: within the row of 16, by DPP).
+template <int M>
+__device__ __forceinline__ double lane_xor_dpp(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  if constexpr (M == 1) {
+    lo = dpp<kQuadSwap1>(0u, lo);
+    hi = dpp<kQuadSwap1>(0u, hi);
+  } else if constexpr (M == 2) {
+    lo = dpp<kQuadSwap2>(0u, lo);
+    hi = dpp<kQuadSwap2>(0u, hi);
+  } else if constexpr (M == 8) {
+    lo = dpp<kRowRor8>(0u, lo);
+    hi = dpp<kRowRor8>(0u, hi);
+  } else {
+    static_assert(M == 4, "lane distance");
+    const bool up = (lane_id() & 4) != 0;
+    const uint32_t lo_d = dpp<kRowShr4>(0u, lo), hi_d = dpp<kRowShr4>(0u, hi);
+    const uint32_t lo_u = dpp<kRowShl4>(0u, lo), hi_u = dpp<kRowShl4>(0u, hi);
+    lo = up ? lo_d : lo_u;
+    hi = up ? hi_d : hi_u;
+  }
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// One butterfly stage of distance H (a power of two below 64) on a 64-bit value: a lane with bit
+// H clear returns y + partner, a lane with it set partner - y.  H = 16 and 32 use the row and
+// half-wave swaps (which hand every lane both values of its pair), the others DPP.
+template <int H>
+__device__ __forceinline__ double butterfly(double y) {
+  const bool upper = (lane_id() & H) != 0;
+  if constexpr (H >= 16) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, y);
+    const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+    const auto sl = H == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                            : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto sh = H == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                            : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    // element [0]: the value of the pair's lower lane, [1]: of its upper lane
+    const double a = __builtin_bit_cast(double, (static_cast<uint64_t>(sh[0]) << 32) | sl[0]);
+    const double b = __builtin_bit_cast(double, (static_cast<uint64_t>(sh[1]) << 32) | sl[1]);
+    return upper ? (a - b) : (a + b);
+  } else {
+    const double p = lane_xor_dpp<H>(y);
+    return upper ? (p - y) : (y + p);
+  }
 }
 
 // Hadamard butterflies across a wave on the vector held as (y0 = element l, y1 = element l + 64)
@@ -80,14 +152,18 @@ __device__ __forceinline__ void hadamard_bitrev(double y0, double y1, double& o0
     y0 = a;
     y1 = b;
   }
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const bool upper = (lane & h) != 0;
-    const double p0 = __shfl_xor(y0, h);
-    const double p1 = __shfl_xor(y1, h);
-    y0 = upper ? (p0 - y0) : (y0 + p0);
-    y1 = upper ? (p1 - y1) : (y1 + p1);
-  }
+  y0 = butterfly<32>(y0);
+  y1 = butterfly<32>(y1);
+  y0 = butterfly<16>(y0);
+  y1 = butterfly<16>(y1);
+  y0 = butterfly<8>(y0);
+  y1 = butterfly<8>(y1);
+  y0 = butterfly<4>(y0);
+  y1 = butterfly<4>(y1);
+  y0 = butterfly<2>(y0);
+  y1 = butterfly<2>(y1);
+  y0 = butterfly<1>(y0);
+  y1 = butterfly<1>(y1);
   const double inv_sqrt_d = 0.08838834764831845;  // 1 / sqrt(128)
   const int r = bitrev7(lane);
   const int src = r & 63;
@@ -101,44 +177,48 @@ __device__ __forceinline__ void hadamard_bitrev(double y0, double y1, double& o0
 }
 
 // Rotation of one row vector x (fp32 in LDS, 128 entries) by R = U H P / sqrt(128) in fp64 by a
-// whole 256-thread block: wave w accumulates rows [32w, 32w + 32) of x U, wave 0 adds the four
-// partial vectors (staged in `red`) and finishes with the Hadamard and the bit reversal.  The U
-// entries a thread needs are loaded into registers first (load_u_rows), so the loads can be in
-// flight while x is still being staged.  Every thread of the block must call rotate1_block (it
-// contains a block barrier); it returns true in wave 0, whose lane l then holds rotated channels
-// l and l + 64.
+// whole 256-thread block: thread t accumulates rows [16 g, 16 g + 16) (g = t / 32) of x U for
+// columns 4 c .. 4 c + 3 (c = t % 32), wave 0 adds the eight partial vectors (staged in `red`) and
+// finishes with the Hadamard and the bit reversal.  The U entries a thread needs (16 float4 rows
+// slices) are loaded into registers first (load_u_rows), so the loads can be in flight while x
+// is still being staged.  Every thread of the block must call rotate1_block (it contains a block
+// barrier); it returns true in wave 0, whose lane l then holds rotated channels l and l + 64.
+constexpr int kRotGroups = 8;   // row groups of the block rotation (red holds one vector each)
+
 struct URows {
-  float v[32][2];   // U[32 w + k][lane], U[32 w + k][lane + 64]
+  float4 v[16];   // U[16 g + k][4 c .. 4 c + 3]
 };
 
 __device__ __forceinline__ void load_u_rows(const float* __restrict__ u, URows& r) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
+  const int g = threadIdx.x >> 5, c = threadIdx.x & 31;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int i = wave * 32 + k;
-    r.v[k][0] = u[i * 128 + lane];
-    r.v[k][1] = u[i * 128 + lane + 64];
-  }
+  for (int k = 0; k < 16; ++k)
+    r.v[k] = reinterpret_cast<const float4*>(u + (16 * g + k) * 128)[c];
 }
 
 __device__ __forceinline__ bool rotate1_block(const float* x, const URows& ur,
                                               double (*red)[128], double& o0, double& o1) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  double y0 = 0.0, y1 = 0.0;
+  const int g = threadIdx.x >> 5, c = threadIdx.x & 31;
+  double y[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const double xi = static_cast<double>(x[wave * 32 + k]);
-    y0 = fma(xi, static_cast<double>(ur.v[k][0]), y0);
-    y1 = fma(xi, static_cast<double>(ur.v[k][1]), y1);
+  for (int k = 0; k < 16; ++k) {
+    const double xi = static_cast<double>(x[16 * g + k]);
+    y[0] = fma(xi, static_cast<double>(ur.v[k].x), y[0]);
+    y[1] = fma(xi, static_cast<double>(ur.v[k].y), y[1]);
+    y[2] = fma(xi, static_cast<double>(ur.v[k].z), y[2]);
+    y[3] = fma(xi, static_cast<double>(ur.v[k].w), y[3]);
   }
-  red[wave][lane] = y0;
-  red[wave][lane + 64] = y1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[g][4 * c + e] = y[e];
   __syncthreads();
-  if (wave != 0) return false;
-  y0 = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-  y1 = ((red[0][lane + 64] + red[1][lane + 64]) + red[2][lane + 64]) + red[3][lane + 64];
+  if ((threadIdx.x >> 6) != 0) return false;
+  const int lane = lane_id();
+  double y0 = red[0][lane], y1 = red[0][lane + 64];
+#pragma unroll
+  for (int r = 1; r < kRotGroups; ++r) {
+    y0 += red[r][lane];
+    y1 += red[r][lane + 64];
+  }
   hadamard_bitrev(y0, y1, o0, o1);
   return true;
 }

@@ -183,7 +183,8 @@ __device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned
 // x0 + blockIdx.x < n_query: query row; else append item x0 + blockIdx.x - n_query.
 __global__ __launch_bounds__(256) void prep_kernel(AppendArgs ap, QueryArgs qa, int n_query,
                                                    int x0) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kHeadDim + 4 * 8 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kHeadDim +
+                                                           dev::kRotGroups * 8 * kHeadDim];
   const int item = x0 + blockIdx.x;
   if (item < n_query)
     query_item(qa, item, smem);

@@ -71,11 +71,14 @@ __device__ __forceinline__ void store_key_row(uint8_t* blk, int slot, uint32_t c
   const int lane = dev::lane_id();
   uint32_t v0 = c0 << (2 * (lane & 15));
   uint32_t v1 = c1 << (2 * (lane & 15));
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    v0 |= __shfl_xor(v0, m);
-    v1 |= __shfl_xor(v1, m);
-  }
+  auto row_or = [](uint32_t v) {   // OR over the 16 lanes of the row (DPP steps)
+    v |= dev::dpp<dev::kQuadSwap1>(0u, v);
+    v |= dev::dpp<dev::kQuadSwap2>(0u, v);
+    v |= dev::dpp<dev::kRowRor4>(0u, v);
+    return v | dev::dpp<dev::kRowRor8>(0u, v);
+  };
+  v0 = row_or(v0);
+  v1 = row_or(v1);
   if ((lane & 15) == 0) {
     uint32_t* words = reinterpret_cast<uint32_t*>(blk + kKCodesOff);
     words[k_word_index(slot, lane >> 4)] = v0;
