@@ -127,6 +127,11 @@ def test_decode_validation_happens_before_launch():
     assert _call_decode(lay, batch=0, q=None) == 0
     assert _call_decode(lay, wsb=16) == -5
     assert "workspace" in ok.lib().oscar_last_error().decode()
+    # a split covers at most 256 pages and a head at most 1024 splits: 64 * 256 * 1024 history
+    # tokens plus the 320 BF16 ones is the longest context the plan accepts
+    big = _lay(max_pages_per_seq=300000)
+    assert _call_decode(big, maxlen=64 * 256 * 1024 + 320 + 1) == -4
+    assert "work items" in ok.lib().oscar_last_error().decode()
 
 
 def test_append_validation_happens_before_launch():
