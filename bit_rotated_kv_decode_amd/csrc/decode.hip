@@ -645,53 +645,48 @@ __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kerne
 // per-block load volume is about half of one block doing the whole row, spread over four times
 // as many compute units.  Every global load is issued before the first reduction and none waits
 // on the sequence length (entries of splits the sequence does not reach are read but masked).
-//   (1) weights f_s = 2^(m_s - m) of the INT2 splits, m and l by block reductions;
-//   (2) acc' = sum_s f_s acc'_s with thread (channel quad, split residue mod 8) partial sums;
-//   (3) (acc' P) H / sqrt(d) by butterflies across one wave; then times U_v^T: eight threads per
-//       output channel, 16 inputs each, summed across the eight lanes;
+//   (1) thread (channel quad, split residue r mod 8) merges its own splits r, r + 8, ... into a
+//       local (m, l, acc') with a local maximum;
+//   (2) wave 0 merges the eight residue partials (one barrier before), gathers the channels in
+//       bit-reversed order and applies H / sqrt(d) as butterflies across the wave;
+//   (3) times U_v^T: eight threads per output channel, 16 inputs each, summed across the lanes;
 //   (4) merge with the BF16 chunk partials and normalise.
-constexpr int kMergePrefetch = 12;   // split accumulators per thread loaded up front (96 splits)
+constexpr int kMergePrefetch = 12;   // splits per thread loaded up front (96 splits per row)
 constexpr int kMergeParts = 4;       // blocks per (sequence, query head)
 constexpr int kMergeCols = kHeadDim / kMergeParts;
 
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
-  __shared__ float f_s[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float part[8][kHeadDim];
+  __shared__ float part_m[8], part_l[8];
   __shared__ __attribute__((aligned(16))) float vec[kHeadDim];
-  __shared__ float red[8];
   const int row = blockIdx.x / kMergeParts;   // b * hq + head
   const int q = blockIdx.x % kMergeParts;
   const int b = row / p.hq;
   const int kv = (row % p.hq) / p.gqa;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
-  const float* iml = reinterpret_cast<const float*>(a.workspace + p.off_int2_ml) +
-                     static_cast<int64_t>(row) * p.num_splits * 2;
+  const float2* iml = reinterpret_cast<const float2*>(a.workspace + p.off_int2_ml) +
+                      static_cast<int64_t>(row) * p.num_splits;
   const float4* iacc = reinterpret_cast<const float4*>(a.workspace + p.off_int2_acc) +
                        static_cast<int64_t>(row) * p.num_splits * (kHeadDim / 4);
   const float* bml = reinterpret_cast<const float*>(a.workspace + p.off_bf16_ml) +
                      static_cast<int64_t>(row) * kBf16Chunks * 2;
   const float* bacc = reinterpret_cast<const float*>(a.workspace + p.off_bf16_acc) +
                       static_cast<int64_t>(row) * kBf16Chunks * kHeadDim;
-  const int cq = tid & 31, sr = tid >> 5;     // (2): channel quad, split residue
+  const int cq = tid & 31, sr = tid >> 5;     // (1): channel quad, split residue
   const int jl = tid >> 3, ip = tid & 7;      // (3): output channel 32 q + jl, input part
   const int j = kMergeCols * q + jl;
 
   // ---- loads
-  static_assert(kMaxSplits <= 4 * 256, "split statistics: four per thread");
-  float2 st[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = tid + 256 * i;
-    st[i] = s < p.num_splits ? reinterpret_cast<const float2*>(iml)[s]
-                             : make_float2(-INFINITY, 0.f);
-  }
+  float2 st[kMergePrefetch];
   float4 pa[kMergePrefetch];
 #pragma unroll
   for (int i = 0; i < kMergePrefetch; ++i) {
     const int s = sr + 8 * i;
-    pa[i] = s < p.num_splits ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool in = s < p.num_splits;
+    st[i] = in ? iml[s] : make_float2(-INFINITY, 0.f);
+    pa[i] = in ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+               : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 uv[4];   // U_v[kv][j][16 ip .. 16 ip + 15]
   {
@@ -712,66 +707,69 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int n_pages = (n_hist + kPage - 1) / kPage;
   const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
 
-  // ---- (1) max and weights of the INT2 splits the sequence reaches
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (tid + 256 * i >= n_valid) st[i] = make_float2(-INFINITY, 0.f);
-  float mloc = fmaxf(fmaxf(st[0].x, st[1].x), fmaxf(st[2].x, st[3].x));
-  mloc = dev::wave_max(mloc);
-  if (lane == 0) red[wave] = mloc;
-  __syncthreads();
-  const float mi = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float lloc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = tid + 256 * i;
-    if (s < n_valid) {
-      const float f = exp2f(st[i].x - mi);
-      f_s[s] = f;
-      lloc = fmaf(st[i].y, f, lloc);
+  // ---- (1) this thread's splits (those the sequence reaches), with its own maximum
+  float m_loc = -INFINITY, l_loc = 0.f;
+  float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto absorb = [&](const float2* ml, const float4* v, int s0, int n) {
+    float mb = -INFINITY;
+    for (int i = 0; i < n; ++i)
+      if (s0 + 8 * i < n_valid) mb = fmaxf(mb, ml[i].x);
+    if (mb == -INFINITY) return;
+    const float mn = fmaxf(m_loc, mb);
+    const float al = exp2f(m_loc - mn);   // 0 while nothing is held yet
+    l_loc *= al;
+    s4.x *= al;
+    s4.y *= al;
+    s4.z *= al;
+    s4.w *= al;
+    m_loc = mn;
+    for (int i = 0; i < n; ++i) {
+      if (s0 + 8 * i >= n_valid) continue;
+      const float f = exp2f(ml[i].x - mn);
+      l_loc = fmaf(ml[i].y, f, l_loc);
+      s4.x = fmaf(v[i].x, f, s4.x);
+      s4.y = fmaf(v[i].y, f, s4.y);
+      s4.z = fmaf(v[i].z, f, s4.z);
+      s4.w = fmaf(v[i].w, f, s4.w);
     }
+  };
+  absorb(st, pa, sr, kMergePrefetch);
+  // splits past the prefetch (more than 96 per row): rounds of four
+  for (int s0 = sr + 8 * kMergePrefetch; s0 < n_valid; s0 += 32) {
+    float2 ml4[4];
+    float4 v4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + 8 * k;
+      ml4[k] = s < n_valid ? iml[s] : make_float2(-INFINITY, 0.f);
+      v4[k] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    absorb(ml4, v4, s0, 4);
   }
-  lloc = dev::wave_sum(lloc);
-  if (lane == 0) red[4 + wave] = lloc;
-  __syncthreads();
-  const float li = (red[4] + red[5]) + (red[6] + red[7]);
-  // ---- (2) weighted sum of the split accumulators
-  {
-    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto add = [&](const float4& v, float f) {
-      s4.x = fmaf(v.x, f, s4.x);
-      s4.y = fmaf(v.y, f, s4.y);
-      s4.z = fmaf(v.z, f, s4.z);
-      s4.w = fmaf(v.w, f, s4.w);
-    };
-#pragma unroll
-    for (int i = 0; i < kMergePrefetch; ++i) {
-      const int s = sr + 8 * i;
-      if (s < n_valid) add(pa[i], f_s[s]);
-    }
-    // splits past the prefetch: four loads in flight per round
-    for (int s0 = sr + 8 * kMergePrefetch; s0 < n_valid; s0 += 32) {
-      float4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int s = s0 + 8 * k;
-        v[k] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (s0 + 8 * k < n_valid) add(v[k], f_s[s0 + 8 * k]);
-    }
-    reinterpret_cast<float4*>(part[sr])[cq] = s4;
+  reinterpret_cast<float4*>(part[sr])[cq] = s4;
+  if (cq == 0) {
+    part_m[sr] = m_loc;
+    part_l[sr] = l_loc;
   }
   __syncthreads();
-  // ---- (3) (acc' P) H / sqrt(d) in wave 0: lane holds entries lane and lane + 64
+  // ---- (2) merge of the residues, (acc' P) H / sqrt(d) in wave 0: lane holds entries lane and
+  // lane + 64
   if (wave == 0) {
+    float mi = part_m[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mi = fmaxf(mi, part_m[r]);
+    float w[8], li = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      w[r] = mi == -INFINITY ? 0.f : exp2f(part_m[r] - mi);
+      li = fmaf(part_l[r], w[r], li);
+    }
     auto gather = [&](int jj) {
       const int src = dev::bitrev7(jj);   // (acc' P)_j = acc'_rev(j)
       float v = 0.f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v += part[r][src];
+      for (int r = 0; r < 8; ++r) v = fmaf(part[r][src], w[r], v);
       return v;
     };
     float y0 = gather(lane), y1 = gather(lane + 64);
@@ -790,8 +788,13 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     }
     vec[lane] = y0;
     vec[lane + 64] = y1;
+    if (lane == 0) {
+      part_m[0] = mi;   // every reader of part_m / part_l has passed: only wave 0 read them
+      part_l[0] = li;
+    }
   }
   __syncthreads();
+  const float mi = part_m[0], li = part_l[0];
   float o = 0.f;
   {
     const float4 v4[4] = {reinterpret_cast<const float4*>(vec)[4 * ip],
