@@ -94,41 +94,77 @@ def bytes_per_token_head(group: int) -> int:
 
 
 class Layer:
-    """One layer's resident cache and per-step inputs."""
+    """One layer's resident cache and per-step inputs for the workload's sequences.  History
+    pages inside a shared prefix are built once (from the longest sequence) and aliased by the
+    page table; every other page is private."""
 
-    def __init__(self, wl, layer, length, spare):
+    def __init__(self, wl, layer, lengths, spare):
         dev = "cuda"
-        self.table_np, self.num_pages = workloads.page_tables(wl, [length], layer,
+        self.lengths = list(lengths)
+        B = len(self.lengths)
+        hkv = wl.num_kv_heads
+        self.table_np, self.num_pages = workloads.page_tables(wl, self.lengths, layer,
                                                               spare_tokens=spare)
-        self.lay = ok.make_layout(wl.num_q_heads, wl.num_kv_heads, self.num_pages, 1,
+        self.lay = ok.make_layout(wl.num_q_heads, hkv, self.num_pages, B,
                                   self.table_np.shape[1], wl.group_size)
         self.cache = ok.Cache.allocate(self.lay, zero=False)
         self.table = torch.from_numpy(self.table_np).to(dev)
         uk, uv = workloads.rotation_bases(wl, layer)
-        self.u_k, self.u_v = uk.to(dev), uv.to(dev)
-        self.clip_k = torch.full((wl.num_kv_heads,), wl.clip, dtype=torch.float32, device=dev)
+        self.u_k, self.u_v = uk.to(dev).contiguous(), uv.to(dev).contiguous()
+        # the clip threshold changes code values, not the work; a workload without a fixed one
+        # (calibrated offline) is timed with 4.0
+        clip = wl.clip if wl.clip is not None else 4.0
+        self.clip_k = torch.full((hkv,), clip, dtype=torch.float32, device=dev)
         self.clip_v = self.clip_k.clone()
-        # history: positions 64 .. length-257 demoted in chunks; sink and recent copied
-        n_hist = length - 320
+        n_hist = [max(0, L - 320) for L in self.lengths]
+        shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
+        longest = int(np.argmax(self.lengths))
         chunk = 16384
-        zero = torch.zeros(1, dtype=torch.int32, device=dev)
-        for lo in range(0, n_hist, chunk):
-            n = min(chunk, n_hist - lo)
-            k, v = workloads.kv_tokens(wl, layer, 0, 64 + lo, n, dev)
-            ok.demote(self.lay, self.cache.pool, self.table, self.u_k, self.u_v, self.clip_k,
-                      self.clip_v, k.unsqueeze(0), v.unsqueeze(0), zero + lo)
-        k, v = workloads.kv_tokens(wl, layer, 0, 0, 64, dev)
-        self.cache.sink_k[0] = k.transpose(0, 1)
-        self.cache.sink_v[0] = v.transpose(0, 1)
-        pos = torch.arange(length - 256, length, device=dev)
-        k, v = workloads.kv_tokens(wl, layer, 0, length - 256, 256, dev)
-        self.cache.recent_k[0][:, pos % 256] = k.transpose(0, 1)
-        self.cache.recent_v[0][:, pos % 256] = v.transpose(0, 1)
+        for b in range(B):
+            lo0 = 0 if (b == longest or not shared_hist) else min(shared_hist, n_hist[b])
+            for lo in range(lo0, n_hist[b], chunk):
+                n = min(chunk, n_hist[b] - lo)
+                k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)
+                ok.demote(self.lay, self.cache.pool, self.table[b:b + 1], self.u_k, self.u_v,
+                          self.clip_k, self.clip_v, k.unsqueeze(0), v.unsqueeze(0),
+                          torch.full((1,), lo, dtype=torch.int32, device=dev))
+            L = self.lengths[b]
+            k, v = workloads.kv_tokens(wl, layer, b, 0, min(L, 64), dev)
+            self.cache.sink_k[b, :, :k.shape[0]] = k.transpose(0, 1)
+            self.cache.sink_v[b, :, :k.shape[0]] = v.transpose(0, 1)
+            if L > 64:
+                pos = torch.arange(max(64, L - 256), L, device=dev)
+                k, v = workloads.kv_tokens(wl, layer, b, int(pos[0]), len(pos), dev)
+                self.cache.recent_k[b][:, pos % 256] = k.transpose(0, 1)
+                self.cache.recent_v[b][:, pos % 256] = v.transpose(0, 1)
         # per-step inputs (the same new token and query every step)
-        k, v = workloads.kv_tokens(wl, layer, 0, length, 1, dev)
-        self.k_new, self.v_new = k.contiguous(), v.contiguous()
-        self.q = workloads.queries(wl, layer, 0, dev).contiguous()
-        self.out = torch.empty((1, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+        kn, vn = zip(*[workloads.kv_tokens(wl, layer, b, L, 1, dev)
+                       for b, L in enumerate(self.lengths)])
+        self.k_new = torch.cat(kn).contiguous()
+        self.v_new = torch.cat(vn).contiguous()
+        self.q = workloads.queries(wl, layer, 0, dev, batch=B).contiguous()
+        self.out = torch.empty((B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+
+def history_bytes(wl, lengths, table=None):
+    """Cache bytes one attention pass reads for sequences of the given lengths: INT2 history
+    (codes + meta), its page-table entries, and the BF16 sink + recent rows.  With the page
+    table, a history page shared by several sequences counts once (unique bytes)."""
+    hkv = wl.num_kv_heads
+    bpt = bytes_per_token_head(wl.group_size)
+    total = 0
+    page_tokens = {}
+    for b, L in enumerate(lengths):
+        n_hist = max(0, L - 320)
+        n_bf16 = min(L, 64) + min(256, max(0, L - 64))
+        total += math.ceil(n_hist / 64) * 4 + hkv * n_bf16 * 128 * 2 * 2
+        if table is None:
+            total += hkv * n_hist * bpt
+        else:
+            for p_ in range(math.ceil(n_hist / 64)):
+                pid = int(table[b, p_])
+                page_tokens[pid] = max(page_tokens.get(pid, 0), min(64, n_hist - 64 * p_))
+    return total + hkv * bpt * sum(page_tokens.values())
 
 
 def main():
@@ -145,20 +181,22 @@ def main():
     ok.lib()
     wl = workloads.get(args.workload)
     n_layers = args.layers or wl.num_layers
-    L0 = wl.context
+    lengths = workloads.context_lengths(wl)
+    B = len(lengths)
     total_steps = args.warmup + args.steps + 2       # +2: graph capture warm-up and capture
     dev = "cuda"
 
     t0 = time.time()
-    layers = [Layer(wl, i, L0, total_steps + 8) for i in range(n_layers)]
+    layers = [Layer(wl, i, lengths, total_steps + 8) for i in range(n_layers)]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
 
-    pos = torch.full((1,), L0, dtype=torch.int32, device=dev)      # position of the new token
-    slots = torch.zeros(1, dtype=torch.int32, device=dev)
-    max_len = L0 + total_steps + 4
-    ws = torch.empty(ok.decode_workspace_bytes(layers[0].lay, 1, max_len), dtype=torch.uint8,
+    # position of each sequence's new token
+    pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    max_len = max(lengths) + total_steps + 4
+    ws = torch.empty(ok.decode_workspace_bytes(layers[0].lay, B, max_len), dtype=torch.uint8,
                      device=dev)
 
     def step():
@@ -197,7 +235,7 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    steps_before = int(pos.item()) - L0
+    steps_before = int(pos[0].item()) - lengths[0]
     t_start = time.perf_counter()
     for _ in range(args.steps):
         run_step()
@@ -236,29 +274,36 @@ def main():
         torch.cuda.synchronize()
         seg_us.append(e0.elapsed_time(e1) * 1e3 / len(layers))
 
-    # algorithmic bytes of the timed steps
+    # algorithmic bytes of the timed steps: attention (as the segment launch counts them, plus
+    # the bf16 query in and the fp32 output) and the append (new K/V rows in, the displaced row
+    # read and its codes written)
     hkv, hq = wl.num_kv_heads, wl.num_q_heads
     bpt = bytes_per_token_head(wl.group_size)
-    bf16_seg = hkv * 320 * 128 * 2 * 2
     att_bytes = 0
     for s_ in range(args.steps):
-        L = L0 + steps_before + s_ + 1                  # length seen by attention
-        n_hist = L - 320
-        n_pages = math.ceil(n_hist / 64)
-        att = hkv * n_hist * bpt + n_pages * 4 + bf16_seg + hq * 128 * 2 + hq * 128 * 4
-        append = hkv * 128 * 2 * 2 * 3 + hkv * bpt
+        seen = [L + steps_before + s_ + 1 for L in lengths]   # lengths seen by attention
+        att = history_bytes(wl, seen, layers[0].table_np) + B * hq * 128 * (2 + 4)
+        append = B * (hkv * 128 * 2 * 2 * 3 + hkv * bpt)
         att_bytes += n_layers * (att + append)
-    L_seg = int(lens.item())
-    n_hist = L_seg - 320
-    seg_bytes = (hkv * n_hist * bpt + math.ceil(n_hist / 64) * 4 + hq * 256 + bf16_seg +
-                 hq * 128 * 2)
+    seg_lengths = [int(x) for x in lens.tolist()]
+    # the segment launch also reads the rotated int8 query (INT2 blocks) and the bf16 query;
+    # pages shared by several sequences count once (logical bytes reported alongside)
+    seg_bytes = history_bytes(wl, seg_lengths, layers[0].table_np) + B * hq * (256 + 128 * 2)
+    seg_logical = history_bytes(wl, seg_lengths) + B * hq * (256 + 128 * 2)
     step_bytes = att_bytes / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     seg_us_avg = float(np.mean(seg_us))
     achieved = seg_bytes / (seg_us_avg * 1e-6) / 1e9
 
+    ctx = (f"context {lengths[0]}" if len(set(lengths)) == 1 else
+           f"contexts {min(lengths)}..{max(lengths)}")
+    shape = {"qwen3_8b_100k": "Qwen3-8B-shaped decode, batch 1",
+             "qwen3_32b_131k": "Qwen3-32B-shaped decode, batch 16",
+             "qwen3_8b_b64_prefix": "Qwen3-8B-shaped decode, batch 64 with a 32768-token shared "
+                                    "prefix"}.get(wl.name, f"decode, batch {B}")
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "qwen3_8b_100k" else
+        f"decode-attn effective HBM GB/s (% of 8 TB/s peak) + decode steps/s, {wl.name}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -270,10 +315,11 @@ def main():
         "vs_baseline": None,
         "dtype": "int2+bf16 (fp32 accumulate)",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: Qwen3-8B-shaped decode, batch 1, context {L0}, "
+        "config": {"workload": f"{wl.name}: {shape}, {ctx}, "
                                f"{n_layers} layers, Hq {hq}, Hkv {hkv}, head_dim 128, "
                                f"group {wl.group_size}, 64-token shuffled pages",
-                   "batch": 1, "context": L0, "layers": n_layers,
+                   "batch": B, "context": lengths[0] if len(set(lengths)) == 1 else
+                   [min(lengths), max(lengths)], "layers": n_layers,
                    "launch": "hip-graph" if graph is not None else "eager"},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -283,18 +329,20 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(),
                      "bytes_per_launch": int(seg_bytes),
+                     **({"logical_bytes_per_launch": int(seg_logical)}
+                        if seg_logical != seg_bytes else {}),
                      "avg_launch_us": round(seg_us_avg, 3),
                      "timing": f"HIP events around {args.steps} replays of a graph of "
                                f"{n_layers} launches (one per layer pool), per-launch mean"},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, layers[0], L0)
+        result["cpu_baseline"] = cpu_baseline(wl, layers[0], lengths[0], B)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, layer0, length):
-    """Time the CPU oracle on one KV head (4 query heads) of one layer at full context, plus the
-    demotion of one token, and scale to the whole 36-layer step."""
+def cpu_baseline(wl, layer0, length, batch):
+    """Time the CPU oracle on one KV head of sequence 0 of one layer at full context, plus the
+    demotion of one token, and scale to the whole step (every KV head, sequence and layer)."""
     import threadpoolctl
 
     import oracle
@@ -312,8 +360,9 @@ def cpu_baseline(wl, layer0, length):
     k = bf16_np(k[:, kv:kv + 1])
     v = bf16_np(v[:, kv:kv + 1])
     pool = oracle.new_pool(layer0.num_pages, wl.num_kv_heads, geom)
-    kq = oracle.encode(k[64:64 + n_hist, 0], uk[kv], wl.clip, geom.group)[:3]
-    vq = oracle.encode(v[64:64 + n_hist, 0], uv[kv], wl.clip, geom.group)[:3]
+    c0 = float(layer0.clip_k[kv])
+    kq = oracle.encode(k[64:64 + n_hist, 0], uk[kv], c0, geom.group)[:3]
+    vq = oracle.encode(v[64:64 + n_hist, 0], uv[kv], c0, geom.group)[:3]
     oracle.store_history(pool, table[0], np.arange(n_hist), kv, kq, vq, geom)
     sk = np.zeros((1, wl.num_kv_heads, 64, 128), np.float32)
     sv = np.zeros_like(sk)
@@ -324,10 +373,10 @@ def cpu_baseline(wl, layer0, length):
     p = np.arange(length - 256, length)
     rk[0, kv][p % 256] = k[p, 0]
     rv[0, kv][p % 256] = v[p, 0]
-    q = bf16_np(layer0.q)
+    q = bf16_np(layer0.q[:1])
     gq = wl.gqa
     heads = [(0, kv * gq + i) for i in range(gq)]
-    clip = np.full(wl.num_kv_heads, wl.clip, np.float32)
+    clip = layer0.clip_k.cpu().numpy()
     times = []
     with threadpoolctl.threadpool_limits(1):      # one core: numpy's BLAS pool held to 1 thread
         for _ in range(2):
@@ -338,15 +387,15 @@ def cpu_baseline(wl, layer0, length):
                                     heads=heads)
             times.append(time.perf_counter() - t)
     per_head = min(times)
-    step_s = per_head * wl.num_kv_heads * wl.num_layers
+    step_s = per_head * wl.num_kv_heads * wl.num_layers * batch
     head_bytes = n_hist * bytes_per_token_head(wl.group_size) + 320 * 128 * 2 * 2
-    step_bytes = head_bytes * wl.num_kv_heads * wl.num_layers
+    step_bytes = head_bytes * wl.num_kv_heads * wl.num_layers * batch
     return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "decode_steps_per_s": round(1.0 / step_s, 6),
             "sample": f"numpy fp64 oracle, 1 KV head ({gq} query heads) of 1 layer at context "
                       f"{length}: demotion of 1 token + decode attention over the 3-segment "
                       f"cache ({per_head:.2f}s, best of 2), scaled x{wl.num_kv_heads} heads "
-                      f"x{wl.num_layers} layers"}
+                      f"x{wl.num_layers} layers" + (f" x{batch} sequences" if batch > 1 else "")}
 
 
 if __name__ == "__main__":
