@@ -26,7 +26,9 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTau = 8.0f;   // lazy rescaling: exponents up to 2^8 before the max is moved
+// The softmax reference of a wave is the maximum logit of its first page; later logits may exceed
+// it by up to 2^kRefSpan (p <= 2^64 keeps p * s_v, the value sums and l finite in fp32 / bf16).
+constexpr float kRefSpan = 64.0f;
 
 // FP4 (E2M1) pair in byte B of x -> two bf16; a 2-bit code zero-extended to a nibble encodes
 // code / 2, so the scale 2 gives the code itself.
@@ -158,18 +160,24 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
         reinterpret_cast<uint4*>(pbuf(pp, g, 2 * GP))[lane] = make_uint4(0, 0, 0, 0);
   }
 
-  float m_run[4], m_thr[4], l_run[4], z_run[4][NG];   // m_thr = m_run + tau
+  float m_ref[4], m_lim[4], l_run[4], z_run[4][NG];   // m_lim = m_ref + kRefSpan
+  v4f acc[8];
+  auto reset_sums = [&]() {
+#pragma unroll
+    for (int hs = 0; hs < 4; ++hs) {
+      l_run[hs] = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) z_run[hs][g] = 0.f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  };
 #pragma unroll
   for (int hs = 0; hs < 4; ++hs) {
-    m_run[hs] = -INFINITY;
-    m_thr[hs] = -INFINITY;
-    l_run[hs] = 0.f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) z_run[hs][g] = 0.f;
+    m_ref[hs] = -INFINITY;   // a wave without pages leaves -inf (its partial weighs nothing)
+    m_lim[hs] = -INFINITY;
   }
-  v4f acc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  reset_sums();
 
   // One page's operands, fetched with 16-byte loads from the tiled block (one chunk row = 64 lanes
   // x 16 bytes): key chunk row j holds this lane's words of sub-tiles 2j and 2j + 1, value chunk
@@ -218,8 +226,14 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     }
   };
 
-  // Pages pg .. pg + PP - 1 on register sets r[0 .. PP - 1]; pages past p1 contribute nothing.
-  auto process_step = [&](int pg, const PageRegs* r) {
+  // Per-page work in two parts: the logits (with the value scales and zero points they come
+  // with), then probabilities and values.  Pages pg .. pg + PP - 1 are on register sets
+  // r[0 .. PP - 1]; pages past p1 contribute nothing.
+  struct Scores {
+    float logit[PP][NACC][4];
+    float vs[PP][NACC][NG], vz[PP][NACC][NG];
+  };
+  auto page_scores = [&](int pg, const PageRegs* r, Scores& so) {
     // ---- scores: exact int32 tiles of hi and lo dot products, then one lane swap per register
     // puts hi and lo of the same token in one lane: S = 256 hi + lo
     constexpr int NT = GP == 4 ? 2 : 4;
@@ -262,9 +276,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
             sc[pp][pa][g][hs] = (static_cast<int>(sw[0]) << 8) + static_cast<int>(sw[1]);
           }
     }
-    float logit[PP][NACC][4];
     bool valid[PP][NACC];
-    float vs[PP][NACC][NG], vz[PP][NACC][NG];
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
@@ -279,8 +291,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           const uint32_t vm = valid[pp][pa] ? r[pp].vm[pa][g] : 0u;
           ks[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km & 0xFFFF)));
           kz[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km >> 16)));
-          vs[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm & 0xFFFF)));
-          vz[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm >> 16)));
+          so.vs[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm & 0xFFFF)));
+          so.vz[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm >> 16)));
         }
         const float bias = valid[pp][pa] ? 0.f : -INFINITY;
 #pragma unroll
@@ -290,38 +302,36 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           for (int g = 0; g < NG; ++g) {
             t = fmaf(ks[g], static_cast<float>(sc[pp][pa][g][hs]), fmaf(kz[g], sq[hs][g], t));
           }
-          logit[pp][pa][hs] = fmaf(t, kh[hs], bias);
+          so.logit[pp][pa][hs] = fmaf(t, kh[hs], bias);
         }
       }
-    // ---- online softmax with lazy rescaling (wave-uniform branch)
-    bool grow = false;
+  };
+  // maximum of head slot hs over the page, the same in every lane holding the head
+  auto page_max = [&](const Scores& so, int hs) {
+    float v = so.logit[0][0][hs];
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int pa = 0; pa < NACC; ++pa) v = fmaxf(v, so.logit[pp][pa][hs]);
+    return head_reduce(dev::row16_max(v), [](float a, float b) { return fmaxf(a, b); });
+  };
+  auto set_ref = [&](int hs, float m) {
+    m_ref[hs] = m;
+    m_lim[hs] = m + kRefSpan;
+  };
+  // lanes holding a logit past the limit, one ballot per compare
+  auto over_limit = [&](const Scores& so) {
+    uint64_t over = 0;
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
       for (int pa = 0; pa < NACC; ++pa)
 #pragma unroll
-        for (int hs = 0; hs < 4; ++hs) grow |= logit[pp][pa][hs] > m_thr[hs];
-    if (__any(grow)) {
-#pragma unroll
-      for (int hs = 0; hs < 4; ++hs) {
-        float v = logit[0][0][hs];
-#pragma unroll
-        for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-          for (int pa = 0; pa < NACC; ++pa) v = fmaxf(v, logit[pp][pa][hs]);
-        // lanes holding the same head: all 64 (GP = 4) or lane groups of the same parity (GP = 8)
-        v = head_reduce(dev::row16_max(v), [](float a, float b) { return fmaxf(a, b); });
-        const float mn = fmaxf(m_run[hs], v);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[hs] - mn);
-        m_run[hs] = mn;
-        m_thr[hs] = mn + kTau;
-        l_run[hs] *= alpha;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) z_run[hs][g] *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[nt][hs] *= alpha;
-      }
-    }
+        for (int hs = 0; hs < 4; ++hs)
+          over |= __builtin_amdgcn_ballot_w64(so.logit[pp][pa][hs] > m_lim[hs]);
+    return over;
+  };
+  auto page_values = [&](const PageRegs* r, const Scores& so) {
     // ---- probabilities, bf16 hi / lo split of p * s_v, transpose through LDS
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
@@ -330,13 +340,13 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
         const int t = ppos(tok_of(pa));
 #pragma unroll
         for (int hs = 0; hs < 4; ++hs) {
-          const float pr = __builtin_amdgcn_exp2f(logit[pp][pa][hs] - m_run[hs]);  // 0: invalid slot
+          const float pr = __builtin_amdgcn_exp2f(so.logit[pp][pa][hs] - m_ref[hs]);  // 0: invalid slot
           l_run[hs] += pr;
           const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            z_run[hs][g] = fmaf(pr, vz[pp][pa][g], z_run[hs][g]);
-            const float pt = pr * vs[pp][pa][g];
+            z_run[hs][g] = fmaf(pr, so.vz[pp][pa][g], z_run[hs][g]);
+            const float pt = pr * so.vs[pp][pa][g];
             const __bf16 hi = static_cast<__bf16>(pt);
             const __bf16 lo = static_cast<__bf16>(pt - static_cast<float>(hi));
             pbuf(pp, g, hd)[t] = hi;
@@ -381,24 +391,57 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Ping-pong over steps: while one step is processed from one register set, the next step's
+
+  // Ping-pong over pages: while one page is processed from one register set, the next page's
   // loads are in flight into the other.  Prefetch indices are clamped to the last page, so every
-  // iteration issues the same loads (the wait before a step then never covers the next one's).
+  // iteration issues the same loads (the wait before a page then never covers the next one's).
+  // The first page of the wave sets the softmax reference; nothing rescales the accumulators
+  // afterwards.  Should a later logit pass the reference by more than 2^kRefSpan, the wave finds
+  // its exact maxima in a scores-only pass and takes its pages again from zero (second attempt,
+  // which cannot pass them).
   PageRegs x[PP], y[PP];
-  int pg = p0 + PP * wave;
+  Scores so;
   auto load_step = [&](int q, PageRegs* r) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) load_page(min(q + pp, p1 - 1), r[pp]);
   };
-  if (pg < p1) load_step(pg, x);
-  while (pg < p1) {
+  for (int attempt = 0; p0 + PP * wave < p1; ++attempt) {
+    int pg = p0 + PP * wave;
+    uint64_t over = 0;
+    load_step(pg, x);
     load_step(pg + 4 * PP, y);
-    process_step(pg, x);
+    page_scores(pg, x, so);
+    if (attempt == 0) {
+#pragma unroll
+      for (int hs = 0; hs < 4; ++hs) set_ref(hs, page_max(so, hs));
+    }
+    page_values(x, so);
     pg += 4 * PP;
-    if (pg >= p1) break;
-    load_step(pg + 4 * PP, x);
-    process_step(pg, y);
-    pg += 4 * PP;
+    while (pg < p1) {
+      load_step(pg + 4 * PP, x);
+      page_scores(pg, y, so);
+      over |= over_limit(so);
+      page_values(y, so);
+      pg += 4 * PP;
+      if (pg >= p1) break;
+      load_step(pg + 4 * PP, y);
+      page_scores(pg, x, so);
+      over |= over_limit(so);
+      page_values(x, so);
+      pg += 4 * PP;
+    }
+    if (over == 0) break;
+    // exact maxima over the wave's pages, then a second attempt from zero
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int q = p0 + PP * wave; q < p1; q += 4 * PP) {
+      load_step(q, x);
+      page_scores(q, x, so);
+#pragma unroll
+      for (int hs = 0; hs < 4; ++hs) mx[hs] = fmaxf(mx[hs], page_max(so, hs));
+    }
+#pragma unroll
+    for (int hs = 0; hs < 4; ++hs) set_ref(hs, mx[hs]);
+    reset_sums();
   }
 
   // ---- finish the wave: l and z summed over the lanes holding each head; each accumulator row
@@ -418,7 +461,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     for (int g = 0; g < NG; ++g) zs[hs][g] = head_sum(z_run[hs][g]);
     const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
     if (n == 0 && gq < GP / 4) {
-      red_m[wave][hd] = m_run[hs];
+      red_m[wave][hd] = m_ref[hs];
       red_l[wave][hd] = l;
     }
   }

@@ -132,6 +132,34 @@ def test_page_shuffle_and_split_invariance():
     assert attention_error(out3, out1) < 1e-4
 
 
+def test_softmax_reference_fallback():
+    # A wave takes its softmax reference from its first page.  Here wave 0 of split 0 (pages 0
+    # and 4 at 7 pages per split) sees small keys on page 0 and, on page 4, one key aligned with
+    # query head 0 whose logit passes the reference by far more than 2^64: the wave must redo its
+    # pages against its exact maxima (without that the output would overflow).
+    wl = _tiny(num_q_heads=8, num_kv_heads=2)
+    hkv = wl.num_kv_heads
+    big = np.full(hkv, 1e4, np.float32)
+    case = Case(wl, [5000, 700], spare=150000, clip=(big, big))
+    for b in range(case.batch):
+        k = case.k[b].float()
+        k[64:64 + 7 * 64] *= 0.01                      # pages 0..6: small keys
+        if b == 0:
+            k[64 + 4 * 64 + 5, 0] = 10.0 * case.q[0, 0].float()   # page 4, KV head 0
+        case.k[b] = k.to(torch.bfloat16)
+    pool = case.oracle_pool()
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g, pool_from_oracle=pool)
+    out, lse = case.gpu_attention(g, cache, max_seq_len=150000)
+    ref, ref_lse = case.oracle_attention(pool)
+    err = attention_error(out, ref)
+    _note(f"reference fallback: max row error {err:.3e}, lse head 0 {lse[0, 0]:.2f} "
+          f"(oracle {ref_lse[0, 0]:.2f})")
+    assert np.isfinite(out).all()
+    assert err <= ATTN_TOL
+    assert np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))) <= 1e-3
+
+
 def test_append_steps_match_oracle():
     # decode-step writes from an empty cache across the sink / recent / history boundaries
     wl = _tiny(num_q_heads=4, num_kv_heads=2)
