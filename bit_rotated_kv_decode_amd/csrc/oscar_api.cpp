@@ -74,10 +74,11 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for one round of blocks over the compute units: the INT2 work items share the launch
-  // with the BF16 chunk blocks, and kernels with more registers per lane hold fewer blocks per
-  // compute unit.  At least one page per wave, within the per-item page and per-head item limits.
-  const long long slots = p.gqa <= 4 && p.n_groups == 1 ? kInt2Items : kInt2Items * 2 / 3;
+  // Aim for one round of two blocks per compute unit: the INT2 pass is bound by memory once two
+  // blocks (eight waves) share a unit, and a grid that leaves some units a third block finishes
+  // when those do.  The INT2 work items share the launch with the BF16 chunk blocks.  At least
+  // one page per wave, within the per-item page and per-head item limits.
+  const long long slots = kInt2Items;
   const long long bf16_blocks = static_cast<long long>(kBf16Chunks) * batch * p.hkv;
   const long long target = bf16_blocks * 2 <= slots ? slots - bf16_blocks : slots;
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;

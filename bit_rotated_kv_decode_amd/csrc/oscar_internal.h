@@ -17,7 +17,7 @@ constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the B
 constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
-constexpr int kInt2Items = 768;           // 256-thread blocks resident at once (3 per compute unit)
+constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
 
 // Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
 constexpr int kKCodesOff = 0;
