@@ -129,6 +129,11 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
   const int tensor = item & 1;
   const int h = (item >> 1) % a.hkv;
   const int b = (item >> 1) / a.hkv;
+  // the U slice is read before anything else (it does not depend on the position), so its loads
+  // overlap the round trips for the position and the ring row
+  dev::URows ur;
+  dev::load_u_rows((tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim,
+                   ur);
   const int pos = a.seq_lens[b];
   const int64_t slot = a.seq_slot[b];
   const uint16_t* nw = (tensor == 0 ? a.k_new : a.v_new) +
@@ -148,19 +153,17 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
     if (tid >= 128) ring[tid - 128] = nv;
     return;
   }
-  dev::URows ur;
-  dev::load_u_rows((tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim,
-                   ur);
+  // the slot's page and the clip threshold are fetched alongside the old row
+  const int idx = pos - kSink - kRecent;
+  uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
+                            block_bytes(a.n_groups));
+  const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
   if (tid < kHeadDim) x[tid] = dev::bf16_to_f32(ring[tid]);
   __syncthreads();   // the old row is staged: waves 2 and 3 may overwrite it
   if (tid >= 128) ring[tid - 128] = nv;
   double r0, r1;
   if (dev::rotate1_block(x, ur, red, r0, r1)) {
-    const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
     const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups);
-    const int idx = pos - kSink - kRecent;
-    uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
-                              block_bytes(a.n_groups));
     store_token(blk, tensor, idx % kPage, a.n_groups, q);
   }
 }
