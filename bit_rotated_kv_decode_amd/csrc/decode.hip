@@ -493,34 +493,33 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // LDS read below is issued before the first one is used.
   float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
   float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
-  static_assert(G * kHeadDim % 256 == 0 || G * kHeadDim < 256, "whole rounds of outputs");
-  if (threadIdx.x < G * kHeadDim) {
+  // thread i: head i / 32, channels 4 (i % 32) .. 4 (i % 32) + 3 (one 16-byte store)
+  static_assert(G * kHeadDim / 4 <= 256, "one round of outputs");
+  if (threadIdx.x < G * kHeadDim / 4) {
+    const int h = threadIdx.x / (kHeadDim / 4), jq = threadIdx.x % (kHeadDim / 4);
+    float mw[4], lw[4];
+    float4 aw[4];
 #pragma unroll
-    for (int r = 0; r < (G * kHeadDim + 255) / 256; ++r) {
-      const int i = threadIdx.x + 256 * r;
-      const int h = i / kHeadDim, j = i % kHeadDim;
-      float mw[4], lw[4], aw[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mw[w] = red_m[w][h];
-        lw[w] = red_l[w][h];
-        aw[w] = red_acc[(w * G + h) * kHeadDim + j];
-      }
-      const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));   // finite: wave 0 has a page
-      float s = 0.f, l = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = __builtin_amdgcn_exp2f(mw[w] - mm);
-        s = fmaf(aw[w], f, s);
-        l = fmaf(lw[w], f, l);
-      }
-      const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
-      pacc[prow * kHeadDim + j] = s;
-      if (j == 0) {
-        ml[prow * 2] = mm;
-        ml[prow * 2 + 1] = l;
-      }
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = red_m[w][h];
+      lw[w] = red_l[w][h];
+      aw[w] = reinterpret_cast<const float4*>(red_acc + (w * G + h) * kHeadDim)[jq];
     }
+    const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));   // finite: wave 0 has a page
+    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w] - mm);
+      s4.x = fmaf(aw[w].x, f, s4.x);
+      s4.y = fmaf(aw[w].y, f, s4.y);
+      s4.z = fmaf(aw[w].z, f, s4.z);
+      s4.w = fmaf(aw[w].w, f, s4.w);
+      l = fmaf(lw[w], f, l);
+    }
+    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
+    reinterpret_cast<float4*>(pacc + prow * kHeadDim)[jq] = s4;
+    if (jq == 0) reinterpret_cast<float2*>(ml)[prow] = make_float2(mm, l);
   }
 }
 
