@@ -65,7 +65,10 @@ struct Int2Lds {
   static constexpr int TOTAL = RED_L + 4 * 4 * GP;
 };
 
-template <int G, int NG>
+// STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
+// sequence, so no page is read twice in it; with several sequences pages may be shared (a prefix
+// cache), and cached loads let the second reader hit.
+template <int G, int NG, bool STREAM>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
                                            int b, unsigned char* smem) {
   using S = Int2Lds<G, NG>;
@@ -205,19 +208,20 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
     const uint4* kc = reinterpret_cast<const uint4*>(blk + kKCodesOff);
     const uint4* vc = reinterpret_cast<const uint4*>(blk + kVCodesOff);
-    r.k[0] = kc[lane];
-    r.k[1] = kc[64 + lane];
-    r.v[0] = vc[lane];
-    r.v[1] = vc[64 + lane];
+    auto ld = [](const auto* q) { return STREAM ? dev::load_stream(q) : *q; };
+    r.k[0] = ld(&kc[lane]);
+    r.k[1] = ld(&kc[64 + lane]);
+    r.v[0] = ld(&vc[lane]);
+    r.v[1] = ld(&vc[64 + lane]);
 #pragma unroll
     for (int pa = 0; pa < NACC; ++pa) {
       const uint8_t* m = blk + kMetaOff + tok_of(pa) * 8 * NG;
       if (NG == 1) {
-        const uint2 w = *reinterpret_cast<const uint2*>(m);
+        const uint2 w = ld(reinterpret_cast<const uint2*>(m));
         r.km[pa][0] = w.x;
         r.vm[pa][0] = w.y;
       } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(m);
+        const uint4 w = ld(reinterpret_cast<const uint4*>(m));
         r.km[pa][0] = w.x;
         r.km[pa][NG - 1] = w.y;
         r.vm[pa][0] = w.z;
@@ -669,7 +673,7 @@ constexpr int attn_blocks_per_cu() {
   return G <= 4 && NG == 1 ? 3 : 2;
 }
 
-template <int G, int NG>
+template <int G, int NG, bool STREAM>
 __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kernel(DecodeArgs a, Plan p,
                                                                     float scale_log2, int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
@@ -677,7 +681,7 @@ __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kerne
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
   else
-    int2_block<G, NG>(a, p, x - kBf16Chunks, kv, b, smem);
+    int2_block<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -886,10 +890,19 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
   const int x1 = kBf16Chunks + ((stages & OSCAR_STAGE_INT2) ? p.num_splits : 0);
   if (x1 > x0) {
     dim3 grid(x1 - x0, p.hkv, p.batch);
-    if (p.n_groups == 1)
-      hipLaunchKernelGGL((attn_kernel<G, 1>), grid, dim3(256), 0, stream, a, p, scale_log2, x0);
+    const bool one = p.batch == 1;
+    if (p.n_groups == 1 && one)
+      hipLaunchKernelGGL((attn_kernel<G, 1, true>), grid, dim3(256), 0, stream, a, p, scale_log2,
+                         x0);
+    else if (p.n_groups == 1)
+      hipLaunchKernelGGL((attn_kernel<G, 1, false>), grid, dim3(256), 0, stream, a, p, scale_log2,
+                         x0);
+    else if (one)
+      hipLaunchKernelGGL((attn_kernel<G, 2, true>), grid, dim3(256), 0, stream, a, p, scale_log2,
+                         x0);
     else
-      hipLaunchKernelGGL((attn_kernel<G, 2>), grid, dim3(256), 0, stream, a, p, scale_log2, x0);
+      hipLaunchKernelGGL((attn_kernel<G, 2, false>), grid, dim3(256), 0, stream, a, p, scale_log2,
+                         x0);
   }
   if (stages & OSCAR_STAGE_MERGE)
     hipLaunchKernelGGL(merge_kernel, dim3(p.batch * p.hq * kMergeParts), dim3(256), 0, stream, a,

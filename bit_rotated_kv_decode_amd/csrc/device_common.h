@@ -14,6 +14,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Loads of data a launch reads once (history pages): non-temporal, so the stream does not
+// displace what later launches read again (rotation matrices, partials).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 t = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  const u2 t = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+  return make_uint2(t[0], t[1]);
+}
+
 // 7-bit bit reversal of a channel index in [0, 128).
 __device__ __forceinline__ int bitrev7(int j) {
   return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(j)) >> 25);
