@@ -824,14 +824,18 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
       y0 = t0;
       y1 = t1;
     }
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) {
-      const bool upper = (lane & h) != 0;
-      const float p0 = __shfl_xor(y0, h);
-      const float p1 = __shfl_xor(y1, h);
-      y0 = upper ? (p0 - y0) : (y0 + p0);
-      y1 = upper ? (p1 - y1) : (y1 + p1);
-    }
+    y0 = dev::butterfly<32>(y0);
+    y1 = dev::butterfly<32>(y1);
+    y0 = dev::butterfly<16>(y0);
+    y1 = dev::butterfly<16>(y1);
+    y0 = dev::butterfly<8>(y0);
+    y1 = dev::butterfly<8>(y1);
+    y0 = dev::butterfly<4>(y0);
+    y1 = dev::butterfly<4>(y1);
+    y0 = dev::butterfly<2>(y0);
+    y1 = dev::butterfly<2>(y1);
+    y0 = dev::butterfly<1>(y0);
+    y1 = dev::butterfly<1>(y1);
     vec[lane] = y0;
     vec[lane + 64] = y1;
     if (lane == 0) {
@@ -855,9 +859,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
       o = fmaf(v4[c].w, uv[c].w, o);
     }
     // sum over the eight input parts (lanes 8 jl .. 8 jl + 7 of the wave)
-    o += __shfl_xor(o, 1);
-    o += __shfl_xor(o, 2);
-    o += __shfl_xor(o, 4);
+    o += dev::lane_xor_dpp<1>(o);
+    o += dev::lane_xor_dpp<2>(o);
+    o += dev::lane_xor_dpp<4>(o);
   }
   // ---- (4) merge with the BF16 partials
   if (ip == 0) {

@@ -129,6 +129,35 @@ __device__ __forceinline__ double lane_xor_dpp(double v) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Value of lane l ^ M for a 32-bit value (M in 1, 2, 4, 8: within the row of 16, by DPP).
+template <int M>
+__device__ __forceinline__ float lane_xor_dpp(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (M == 1) return __uint_as_float(dpp<kQuadSwap1>(0u, u));
+  if constexpr (M == 2) return __uint_as_float(dpp<kQuadSwap2>(0u, u));
+  if constexpr (M == 8) return __uint_as_float(dpp<kRowRor8>(0u, u));
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "lane distance");
+  const bool up = (lane_id() & 4) != 0;
+  const uint32_t d = dpp<kRowShr4>(0u, u), w = dpp<kRowShl4>(0u, u);
+  return __uint_as_float(up ? d : w);
+}
+
+// The butterfly stage below on a 32-bit value.
+template <int H>
+__device__ __forceinline__ float butterfly(float y) {
+  const bool upper = (lane_id() & H) != 0;
+  if constexpr (H >= 16) {
+    const uint32_t u = __float_as_uint(y);
+    const auto sw = H == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+    return upper ? (a - b) : (a + b);
+  } else {
+    const float p = lane_xor_dpp<H>(y);
+    return upper ? (p - y) : (y + p);
+  }
+}
+
 // One butterfly stage of distance H (a power of two below 64) on a 64-bit value: a lane with bit
 // H clear returns y + partner, a lane with it set partner - y.  H = 16 and 32 use the row and
 // half-wave swaps (which hand every lane both values of its pair), the others DPP.
