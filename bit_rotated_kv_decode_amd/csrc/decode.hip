@@ -29,6 +29,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // The softmax reference of a wave is the maximum logit of its first page; later logits may exceed
 // it by up to 2^kRefSpan (p <= 2^64 keeps p * s_v, the value sums and l finite in fp32 / bf16).
 constexpr float kRefSpan = 64.0f;
+// Buffer resources: the last descriptor word for raw 32-bit-element access on gfx9-family parts,
+// and the cache-policy bit of a non-temporal access.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+// Pages a wave has in flight or in process: register sets of the page loop.
+constexpr int kDepth = 2;
 
 // FP4 (E2M1) pair in byte B of x -> two bf16; a 2-bit code zero-extended to a nibble encodes
 // code / 2, so the scale 2 gives the code itself.
@@ -215,13 +221,19 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     r.v[1] = ld(&vc[64 + lane]);
 #pragma unroll
     for (int pa = 0; pa < NACC; ++pa) {
-      const uint8_t* m = blk + kMetaOff + tok_of(pa) * 8 * NG;
+      // The meta region lies past the immediate-offset range of a global load, and a global
+      // load there takes a per-page 64-bit vector address whose register makes the next page's
+      // loads wait for every load in flight; a buffer load over the block takes the block
+      // address in scalar registers and the lane's offset in one loop-invariant register.
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, BLK, kBufferWord3);
+      const int moff = kMetaOff + tok_of(pa) * 8 * NG;
       if (NG == 1) {
-        const uint2 w = ld(reinterpret_cast<const uint2*>(m));
+        const uint2 w = dev::to_uint2(__builtin_amdgcn_raw_buffer_load_b64(rs, moff, 0, STREAM ? kNonTemporal : 0));
         r.km[pa][0] = w.x;
         r.vm[pa][0] = w.y;
       } else {
-        const uint4 w = ld(reinterpret_cast<const uint4*>(m));
+        const uint4 w = dev::to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, moff, 0, STREAM ? kNonTemporal : 0));
         r.km[pa][0] = w.x;
         r.km[pa][NG - 1] = w.y;
         r.vm[pa][0] = w.z;
@@ -396,50 +408,62 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   };
 
 
-  // Ping-pong over pages: while one page is processed from one register set, the next page's
-  // loads are in flight into the other.  Prefetch indices are clamped to the last page, so every
-  // iteration issues the same loads (the wait before a page then never covers the next one's).
+  // kDepth register sets used in turn: while one page is processed, the loads of the wave's next
+  // kDepth - 1 pages are in flight.  Prefetch indices are clamped to the last page, so every round
+  // issues the same loads (the wait before a page then never covers a later one's), and the loop
+  // over full rounds has a single exit, so the compiler's wait counts stay exact across it.
   // The first page of the wave sets the softmax reference; nothing rescales the accumulators
   // afterwards.  Should a later logit pass the reference by more than 2^kRefSpan, the wave finds
   // its exact maxima in a scores-only pass and takes its pages again from zero (second attempt,
   // which cannot pass them).
-  PageRegs x[PP], y[PP];
+  PageRegs r[kDepth][PP];
   Scores so;
-  auto load_step = [&](int q, PageRegs* r) {
+  auto load_step = [&](int q, PageRegs* rr) {
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp) load_page(min(q + pp, p1 - 1), r[pp]);
+    for (int pp = 0; pp < PP; ++pp) load_page(min(q + pp, p1 - 1), rr[pp]);
   };
+  constexpr int WS = 4 * PP;   // page stride of a wave (four waves per block)
   for (int attempt = 0; p0 + PP * wave < p1; ++attempt) {
     int pg = p0 + PP * wave;
     uint64_t over = 0;
-    load_step(pg, x);
-    load_step(pg + 4 * PP, y);
-    page_scores(pg, x, so);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) load_step(pg + k * WS, r[k]);
+    page_scores(pg, r[0], so);
     if (attempt == 0) {
 #pragma unroll
       for (int hs = 0; hs < 4; ++hs) set_ref(hs, page_max(so, hs));
     }
-    page_values(x, so);
-    pg += 4 * PP;
-    while (pg < p1) {
-      load_step(pg + 4 * PP, x);
-      page_scores(pg, y, so);
-      over |= over_limit(so);
-      page_values(y, so);
-      pg += 4 * PP;
-      if (pg >= p1) break;
-      load_step(pg + 4 * PP, y);
-      page_scores(pg, x, so);
-      over |= over_limit(so);
-      page_values(x, so);
-      pg += 4 * PP;
+    page_values(r[0], so);
+    pg += WS;
+    int rest = (p1 - pg + WS - 1) / WS;   // pages of the wave after the first
+    for (; rest >= kDepth; rest -= kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        load_step(pg + (kDepth - 1) * WS, r[k]);
+        page_scores(pg, r[(k + 1) % kDepth], so);
+        over |= over_limit(so);
+        page_values(r[(k + 1) % kDepth], so);
+        pg += WS;
+        // keep the scheduler from pulling a later page's work (and the wait for its loads)
+        // into this one
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kDepth - 1; ++k) {
+      if (k < rest) {
+        page_scores(pg, r[(k + 1) % kDepth], so);
+        over |= over_limit(so);
+        page_values(r[(k + 1) % kDepth], so);
+        pg += WS;
+      }
     }
     if (over == 0) break;
     // exact maxima over the wave's pages, then a second attempt from zero
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    for (int q = p0 + PP * wave; q < p1; q += 4 * PP) {
-      load_step(q, x);
-      page_scores(q, x, so);
+    for (int q = p0 + PP * wave; q < p1; q += WS) {
+      load_step(q, r[0]);
+      page_scores(q, r[0], so);
 #pragma unroll
       for (int hs = 0; hs < 4; ++hs) mx[hs] = fmaxf(mx[hs], page_max(so, hs));
     }
@@ -670,14 +694,14 @@ constexpr int attn_lds_bytes() {
 // query heads per KV head, else 2 (the work planner sizes the grid with the same rule).
 template <int G, int NG>
 constexpr int attn_blocks_per_cu() {
-  return G <= 4 && NG == 1 ? 3 : 2;
+  return 2;
 }
 
 template <int G, int NG, bool STREAM>
 __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kernel(DecodeArgs a, Plan p,
                                                                     float scale_log2, int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
-  const int x = x0 + blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int x = x0 + static_cast<int>(blockIdx.x) / p.hkv, kv = blockIdx.x % p.hkv, b = blockIdx.z;
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
   else
@@ -893,7 +917,7 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
   const int x0 = (stages & OSCAR_STAGE_BF16) ? 0 : kBf16Chunks;
   const int x1 = kBf16Chunks + ((stages & OSCAR_STAGE_INT2) ? p.num_splits : 0);
   if (x1 > x0) {
-    dim3 grid(x1 - x0, p.hkv, p.batch);
+    dim3 grid((x1 - x0) * p.hkv, 1, p.batch);
     const bool one = p.batch == 1;
     if (p.n_groups == 1 && one)
       hipLaunchKernelGGL((attn_kernel<G, 1, true>), grid, dim3(256), 0, stream, a, p, scale_log2,

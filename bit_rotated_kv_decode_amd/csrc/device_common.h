@@ -27,6 +27,14 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return make_uint2(t[0], t[1]);
 }
 
+// Vector results of the buffer-load builtins as HIP vector structs.
+__device__ __forceinline__ uint2 to_uint2(unsigned int __attribute__((ext_vector_type(2))) t) {
+  return make_uint2(t[0], t[1]);
+}
+__device__ __forceinline__ uint4 to_uint4(unsigned int __attribute__((ext_vector_type(4))) t) {
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 // 7-bit bit reversal of a channel index in [0, 128).
 __device__ __forceinline__ int bitrev7(int j) {
   return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(j)) >> 25);
