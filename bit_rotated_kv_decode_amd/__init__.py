@@ -25,7 +25,8 @@ __all__ = [
     "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "check_page_table",
     "demote", "append", "decode_attn", "Cache", "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16",
     "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
-    "RECENT_TOKENS",
+    "RECENT_TOKENS", "bf16_page_block_bytes", "bf16_page_bytes", "bf16_pool_bytes",
+    "bf16_decode_workspace_bytes", "bf16_store", "bf16_decode_attn",
 ]
 
 HEAD_DIM = 128
@@ -83,6 +84,13 @@ _SIGNATURES = {
     "oscar_decode_step": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
                                  _i32, _i32, _vp]),
+    "oscar_bf16_page_block_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_bf16_page_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_bf16_pool_bytes": (ctypes.c_size_t, [_LP]),
+    "oscar_bf16_decode_workspace_bytes": (ctypes.c_size_t, [_LP, _i32, _i32]),
+    "oscar_bf16_store": (_i32, [_LP, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp]),
+    "oscar_bf16_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _i32, _i32, _vp]),
 }
 
 STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
@@ -262,6 +270,59 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
         _stream()), "decode_step")
+
+
+# ----------------------------------------------------------------------------------------------
+# paged BF16 baseline (every cached token in BF16 pages of 64 tokens; include/oscar.h)
+
+def bf16_page_block_bytes(lay: Layout) -> int:
+    return lib().oscar_bf16_page_block_bytes(ctypes.byref(lay))
+
+
+def bf16_page_bytes(lay: Layout) -> int:
+    return lib().oscar_bf16_page_bytes(ctypes.byref(lay))
+
+
+def bf16_pool_bytes(lay: Layout) -> int:
+    return lib().oscar_bf16_pool_bytes(ctypes.byref(lay))
+
+
+def bf16_decode_workspace_bytes(lay: Layout, batch: int, max_seq_len: int) -> int:
+    return lib().oscar_bf16_decode_workspace_bytes(ctypes.byref(lay), batch, max_seq_len)
+
+
+def bf16_store(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, k_src: torch.Tensor,
+               v_src: torch.Tensor, start_pos: torch.Tensor) -> None:
+    """Write k_src / v_src (bf16 [B, n, Hkv, 128], unit stride on the last axis, the same strides
+    for both) to positions start_pos[b] + i of the BF16 pool (oscar_bf16_store)."""
+    if k_src.dim() != 4 or k_src.shape != v_src.shape or k_src.stride() != v_src.stride():
+        raise TypeError("k_src / v_src must be [B, n, Hkv, 128] with identical strides")
+    if k_src.stride(3) != 1 or k_src.shape[3] != HEAD_DIM or k_src.shape[2] != lay.num_kv_heads:
+        raise TypeError("k_src last axis must be contiguous head_dim; axis 2 the KV heads")
+    bsz, n = k_src.shape[0], k_src.shape[1]
+    _check(lib().oscar_bf16_store(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _dev(k_src, "k_src", torch.bfloat16),
+        _dev(v_src, "v_src", torch.bfloat16), k_src.stride(0), k_src.stride(1), k_src.stride(2),
+        _contig(start_pos, "start_pos", torch.int32), bsz, n, _stream()), "bf16_store")
+
+
+def bf16_decode_attn(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor,
+                     seq_lens: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                     workspace: torch.Tensor, max_seq_len: int,
+                     lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0) -> None:
+    """Decode attention of q (bf16 [B, Hq, 128]) over the BF16 pool into out (fp32
+    [B, Hq, 128]) and optionally lse (fp32 [B, Hq]) (oscar_bf16_decode_attn)."""
+    bsz = seq_lens.numel()
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _check(lib().oscar_bf16_decode_attn(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(seq_lens, "seq_lens", torch.int32),
+        _contig(q, "q", torch.bfloat16), float(sm_scale), _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        _stream()), "bf16_decode_attn")
 
 
 @dataclasses.dataclass

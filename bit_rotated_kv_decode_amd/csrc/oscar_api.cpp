@@ -105,6 +105,27 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   return p;
 }
 
+Bf16Plan make_bf16_plan(const oscar_layout& lay, int batch, int max_seq_len) {
+  Bf16Plan p;
+  p.batch = batch;
+  p.hq = lay.num_q_heads;
+  p.hkv = lay.num_kv_heads;
+  p.gqa = p.hq / p.hkv;
+  p.max_pages = (std::max(0, max_seq_len) + kPage - 1) / kPage;
+  // one round of two blocks per compute unit, as for the INT2 pass; at least one page per wave
+  const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
+  long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
+  pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
+  p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
+  p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t rows = static_cast<size_t>(batch) * p.hq;
+  p.off_ml = 0;
+  p.off_acc = al(rows * std::max(p.num_splits, 1) * 2 * 4);
+  p.total = al(p.off_acc + rows * std::max(p.num_splits, 1) * kHeadDim * 4);
+  return p;
+}
+
 }  // namespace oscar
 
 namespace {
@@ -433,6 +454,103 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
   return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
                                                       OSCAR_STAGE_MERGE, s),
                     "oscar_decode_step");
+}
+
+size_t oscar_bf16_page_block_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(oscar::kBf16Block);
+}
+
+size_t oscar_bf16_page_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return static_cast<size_t>(oscar::kBf16Block) * l->num_kv_heads;
+}
+
+size_t oscar_bf16_pool_bytes(const oscar_layout* l) {
+  if (check_layout(l) != OSCAR_OK) return 0;
+  return oscar_bf16_page_bytes(l) * static_cast<size_t>(l->num_pages);
+}
+
+size_t oscar_bf16_decode_workspace_bytes(const oscar_layout* l, int32_t batch,
+                                         int32_t max_seq_len) {
+  if (check_layout(l) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
+  return oscar::make_bf16_plan(*l, batch, max_seq_len).total;
+}
+
+oscar_status oscar_bf16_store(const oscar_layout* l, void* pool, const int32_t* page_table,
+                              const void* k_src, const void* v_src, int64_t stride_b,
+                              int64_t stride_t, int64_t stride_h, const int32_t* start_pos,
+                              int32_t batch, int32_t n_tokens, void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || n_tokens < 0) return fail(OSCAR_ERR_RANGE, "negative batch or n_tokens");
+  if (batch == 0 || n_tokens == 0) return ok();
+  if (!pool || !page_table || !k_src || !v_src || !start_pos)
+    return fail(OSCAR_ERR_NULL, "oscar_bf16_store: a required pointer is NULL");
+  if (stride_b < 0 || stride_t < 0 || stride_h < 0)
+    return fail(OSCAR_ERR_RANGE, "negative source stride");
+  if (!aligned(pool, 16)) return fail(OSCAR_ERR_ALIGN, "pool must be 16-byte aligned");
+  if (!aligned(k_src, 2) || !aligned(v_src, 2) || !aligned(page_table, 4) ||
+      !aligned(start_pos, 4))
+    return fail(OSCAR_ERR_ALIGN, "oscar_bf16_store: misaligned pointer");
+  oscar::Bf16StoreArgs a;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.hkv = l->num_kv_heads;
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.stride_b = stride_b;
+  a.stride_t = stride_t;
+  a.stride_h = stride_h;
+  a.start_pos = start_pos;
+  a.batch = batch;
+  a.n_tokens = n_tokens;
+  return hip_status(oscar::launch_bf16_store(a, static_cast<hipStream_t>(stream)),
+                    "oscar_bf16_store");
+}
+
+oscar_status oscar_bf16_decode_attn(const oscar_layout* l, const void* pool,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    const void* q, float sm_scale, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, int32_t batch,
+                                    int32_t max_seq_len, void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (batch == 0) return ok();
+  if (max_seq_len < 1) return fail(OSCAR_ERR_RANGE, "max_seq_len %d < 1", max_seq_len);
+  const oscar::Bf16Plan plan = oscar::make_bf16_plan(*l, batch, max_seq_len);
+  if (plan.max_pages > l->max_pages_per_seq)
+    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
+                max_seq_len, plan.max_pages, l->max_pages_per_seq);
+  if (plan.num_splits > oscar::kMaxSplits)
+    return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d work items per head > %d",
+                max_seq_len, plan.num_splits, oscar::kMaxSplits);
+  if (!pool || !page_table || !seq_lens || !q || !out)
+    return fail(OSCAR_ERR_NULL, "oscar_bf16_decode_attn: a required pointer is NULL");
+  if (workspace == nullptr || workspace_bytes < plan.total)
+    return fail(OSCAR_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes,
+                plan.total);
+  if (!aligned(workspace, 256)) return fail(OSCAR_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(pool, 16) || !aligned(q, 16))
+    return fail(OSCAR_ERR_ALIGN, "pool and q must be 16-byte aligned");
+  if (!aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(seq_lens, 4) ||
+      !aligned(page_table, 4))
+    return fail(OSCAR_ERR_ALIGN, "oscar_bf16_decode_attn: misaligned pointer");
+  oscar::Bf16DecodeArgs a;
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.page_table = page_table;
+  a.max_pages_per_seq = l->max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.sm_scale = sm_scale > 0.f ? sm_scale : 0.08838834764831845f;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = static_cast<uint8_t*>(workspace);
+  a.stream_loads = batch == 1 ? 1 : 0;
+  return hip_status(oscar::launch_bf16_decode(a, plan, static_cast<hipStream_t>(stream)),
+                    "oscar_bf16_decode_attn");
 }
 
 }  // extern "C"

@@ -125,6 +125,52 @@ struct QueryArgs {
   float* qmeta;           // workspace: fp32 [batch][hq][4]
 };
 
+// ---- paged BF16 baseline: every cached token in a BF16 page block of 64 tokens and one KV head,
+// keys [64][128] row-major then values [128][64] channel-major (32 KiB).
+constexpr int kBf16ValOff = kPage * kHeadDim * 2;   // 16384
+constexpr int kBf16Block = 2 * kBf16ValOff;         // 32768
+
+struct Bf16Plan {
+  int batch = 0, hq = 0, hkv = 0, gqa = 0;
+  int max_pages = 0;         // pages of the longest sequence
+  int pages_per_split = 1;   // pages per work item
+  int num_splits = 0;        // work items per (sequence, KV head)
+  size_t off_ml = 0;         // fp32 [B][Hq][S][2] (m, l), log2 domain
+  size_t off_acc = 0;        // fp32 [B][Hq][S][128]
+  size_t total = 0;
+};
+
+Bf16Plan make_bf16_plan(const oscar_layout& lay, int batch, int max_seq_len);
+
+struct Bf16DecodeArgs {
+  const uint8_t* pool;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+  const int32_t* seq_lens;
+  const uint16_t* q;
+  float sm_scale;
+  float* out;
+  float* lse;
+  uint8_t* workspace;
+  int stream_loads;       // non-temporal page loads (one sequence: no page is read twice)
+};
+
+struct Bf16StoreArgs {
+  uint8_t* pool;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+  int hkv;
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t stride_b, stride_t, stride_h;
+  const int32_t* start_pos;
+  int batch;
+  int n_tokens;
+};
+
+hipError_t launch_bf16_decode(const Bf16DecodeArgs& a, const Bf16Plan& plan, hipStream_t stream);
+hipError_t launch_bf16_store(const Bf16StoreArgs& a, hipStream_t stream);
+
 hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
 // One launch for the append items (ap) and the query rows (qa); either may be null.
 hipError_t launch_prep(const AppendArgs* ap, const QueryArgs* qa, hipStream_t stream);

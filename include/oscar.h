@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 2u
+#define OSCAR_ABI_VERSION 3u
 
 typedef int32_t oscar_status;
 
@@ -243,6 +243,62 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
                                float sm_scale, float* out, float* lse, void* workspace,
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                                void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Paged BF16 baseline.  The pages report the INT2 history's system gains against a history kept
+ * in BF16 ([W1] and its repost, evaluation part: about 8x less KV memory, up to 3x faster
+ * batch-1 decoding at 100k context with a full prefix-cache hit, up to 7x throughput at large
+ * batch under one memory budget; [P] Abstract: "up to 3x over BF16" at batch size 1).  These
+ * entry points keep every cached token of a sequence, from position 0, in BF16 pages on the same
+ * kind of page table, and compute the same attention without rotation or quantisation.
+ *
+ * BF16 pool: num_pages pages; pool bytes [page][kv_head][block], block =
+ * oscar_bf16_page_block_bytes() = 32,768 bytes for 64 tokens of one KV head:
+ *     offset 0       keys   [64 tokens][128 channels] bf16, row-major
+ *     offset 16384   values [128 channels][64 tokens] bf16, channel-major
+ * Token at position t of sequence b lives in page page_table[b][t / 64], slot t % 64.  Slots past
+ * a sequence's length may hold any bits; the kernels never let them reach a result.
+ * Of the layout, these calls use head_dim (128), num_q_heads, num_kv_heads, page_tokens (64),
+ * num_pages and max_pages_per_seq; the other fields must still pass oscar_layout_check().
+ * --------------------------------------------------------------------------------------------- */
+
+/* Size queries (0 for an unsupported layout). */
+size_t oscar_bf16_page_block_bytes(const oscar_layout* layout);   /* one (page, KV head) block */
+size_t oscar_bf16_page_bytes(const oscar_layout* layout);         /* one page, all KV heads */
+size_t oscar_bf16_pool_bytes(const oscar_layout* layout);         /* num_pages pages */
+/* Device workspace oscar_bf16_decode_attn needs (0 for invalid arguments). */
+size_t oscar_bf16_decode_workspace_bytes(const oscar_layout* layout, int32_t batch,
+                                         int32_t max_seq_len);
+
+/* Writes keys and values into the BF16 pool: for every sequence b < batch, token i < n_tokens
+ * and KV head h, k_src[b * stride_b + i * stride_t + h * stride_h + (0..127)] (bf16 elements;
+ * likewise v_src) goes to position start_pos[b] + i of sequence b (key row and value column of
+ * its slot).  A decode step appends its token with n_tokens = 1 and start_pos = the token's
+ * position.  pool: oscar_bf16_pool_bytes(layout) bytes, 16-byte aligned; page_table int32
+ * [batch][max_pages_per_seq]; start_pos int32 [batch] (device).  Strides >= 0, in elements.
+ * Returns OSCAR_OK, or NULL / ALIGN / RANGE (negative batch, n_tokens or stride) / SHAPE / HIP. */
+oscar_status oscar_bf16_store(const oscar_layout* layout, void* pool, const int32_t* page_table,
+                              const void* k_src, const void* v_src, int64_t stride_b,
+                              int64_t stride_t, int64_t stride_h, const int32_t* start_pos,
+                              int32_t batch, int32_t n_tokens, void* stream);
+
+/* Decode attention over the BF16 pool: for each sequence b and query head i (KV head
+ * i / (Hq / Hkv)), with L = seq_lens[b] in [1, max_seq_len],
+ *   out[b][i] = sum_{t < L} softmax_t(sm_scale * q[b][i] . k_t) v_t.
+ * Split-KV over pages (scores and value sums on the bf16 matrix cores with fp32 accumulation;
+ * the softmax weights enter the value products as a bf16 hi + lo pair), then a log-sum-exp merge
+ * of the splits.  q: bf16 [batch][Hq][128], 16-byte aligned.  out: fp32 [batch][Hq][128].  lse:
+ * optional fp32 [batch][Hq] (natural log of sum exp(sm_scale * scores)).  sm_scale <= 0 selects
+ * 1/sqrt(128).  max_seq_len: host bound for work planning, at most 64 * 256 * 1024 tokens and
+ * 64 * max_pages_per_seq (RANGE beyond).  workspace: at least
+ * oscar_bf16_decode_workspace_bytes(layout, batch, max_seq_len) bytes, 256-byte aligned.
+ * Two launches on `stream`.  Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE /
+ * HIP. */
+oscar_status oscar_bf16_decode_attn(const oscar_layout* layout, const void* pool,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    const void* q, float sm_scale, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, int32_t batch,
+                                    int32_t max_seq_len, void* stream);
 
 #ifdef __cplusplus
 }

@@ -468,6 +468,45 @@ def merge_partials(parts):
 
 
 # ----------------------------------------------------------------------------------------------
+# paged BF16 baseline ([W1] and [W3], evaluation part, and [P] Abstract state the INT2 history's
+# memory and decode-speed gains against a history kept in BF16).  The layout is this project's
+# own (include/oscar.h): one block per (page, KV head) of ``page`` tokens holds the keys
+# [page][d] row-major, then the values [d][page] channel-major; the token at position t of a
+# sequence lives in page table_row[t // page], slot t % page.  Values are bf16 bit patterns.
+
+def bf16_new_pool(num_pages: int, num_kv_heads: int, d: int = 128, page: int = 64,
+                  fill: int = 0) -> np.ndarray:
+    """uint16 [num_pages, num_kv_heads, 2 * page * d], every element set to ``fill``."""
+    return np.full((num_pages, num_kv_heads, 2 * page * d), fill, dtype=np.uint16)
+
+
+def bf16_store(pool, table_row, pos: int, head: int, k_bits, v_bits, page: int = 64) -> None:
+    """Write one token's key and value (uint16 bit patterns, length d) at position ``pos``."""
+    d = len(k_bits)
+    blk = pool[int(table_row[pos // page]), head]
+    slot = pos % page
+    blk[slot * d:(slot + 1) * d] = k_bits
+    blk[page * d + np.arange(d) * page + slot] = v_bits
+
+
+def bf16_gather(pool, table_row, length: int, head: int, d: int = 128, page: int = 64):
+    """Keys and values (length, d) of positions 0 .. length-1, as uint16 bit patterns."""
+    keys = np.empty((length, d), dtype=np.uint16)
+    values = np.empty((length, d), dtype=np.uint16)
+    for t in range(length):
+        blk = pool[int(table_row[t // page]), head]
+        slot = t % page
+        keys[t] = blk[slot * d:(slot + 1) * d]
+        values[t] = blk[page * d + np.arange(d) * page + slot]
+    return keys, values
+
+
+def bf16_bits_to_float(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp64 values (a bf16 is the upper half of an IEEE binary32)."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
 # offline calibration ([W1] §OSCAR 的设计 and figure 2, left side; [P] 摘要; reading R11)
 
 def _sorted_eigenvectors(c: np.ndarray) -> np.ndarray:

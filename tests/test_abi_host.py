@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 2
+    assert lib.oscar_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -76,6 +76,57 @@ def test_size_queries():
     w2 = ok.decode_workspace_bytes(lay, 4, 100000)
     assert 0 < w1 < w2 and w1 % 256 == 0
     assert ok.decode_workspace_bytes(lay, -1, 10) == 0
+
+
+def test_bf16_size_queries():
+    lay = _lay()
+    assert ok.bf16_page_block_bytes(lay) == 32768      # 64 tokens x 128 channels x (K, V) x 2 B
+    assert ok.bf16_page_bytes(lay) == 8 * 32768
+    assert ok.bf16_pool_bytes(lay) == 10 * 8 * 32768
+    big = _lay(max_pages_per_seq=2000)
+    # 100,000 tokens, batch 1, 8 KV heads: 1,563 pages in splits of 25 -> 63 splits; 32 rows of
+    # (m, l) pairs (16,128 B) then 32 x 63 accumulators of 512 B
+    assert ok.bf16_decode_workspace_bytes(big, 1, 100000) == 16128 + 32 * 63 * 512
+    assert ok.bf16_decode_workspace_bytes(big, -1, 10) == 0
+    assert ok.bf16_page_block_bytes(_lay(head_dim=64)) == 0
+
+
+def _call_bf16_decode(lay, **over):
+    a = dict(pool=4096, pt=4096, lens=4096, q=4096, out=4096, lse=None, ws=4096, wsb=1 << 30,
+             batch=1, maxlen=300)
+    a.update(over)
+    return ok.lib().oscar_bf16_decode_attn(ctypes.byref(lay), a["pool"], a["pt"], a["lens"],
+                                           a["q"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"],
+                                           a["batch"], a["maxlen"], None)
+
+
+def _call_bf16_store(lay, **over):
+    a = dict(pool=4096, pt=4096, k=4096, v=4096, sb=0, st=0, sh=0, start=4096, batch=1, n=1)
+    a.update(over)
+    return ok.lib().oscar_bf16_store(ctypes.byref(lay), a["pool"], a["pt"], a["k"], a["v"],
+                                     a["sb"], a["st"], a["sh"], a["start"], a["batch"], a["n"],
+                                     None)
+
+
+def test_bf16_validation_happens_before_launch():
+    lay = _lay()
+    assert _call_bf16_decode(lay, q=None) == -1
+    assert _call_bf16_decode(lay, pool=None) == -1
+    assert _call_bf16_decode(lay, ws=None) == -5
+    assert _call_bf16_decode(lay, wsb=16) == -5
+    assert _call_bf16_decode(lay, q=4096 + 8) == -3      # operands are read 16 bytes at a time
+    assert _call_bf16_decode(lay, ws=4096 + 64) == -3
+    assert _call_bf16_decode(lay, maxlen=0) == -4
+    assert _call_bf16_decode(lay, maxlen=5 * 64 + 1) == -4   # 6 pages > max_pages_per_seq 5
+    assert _call_bf16_decode(lay, batch=-1) == -4
+    assert _call_bf16_decode(lay, batch=0, q=None) == 0
+    assert _call_bf16_decode(_lay(num_q_heads=24)) == -2
+    assert _call_bf16_store(lay, pool=None) == -1
+    assert _call_bf16_store(lay, start=4098) == -3
+    assert _call_bf16_store(lay, pool=4100) == -3
+    assert _call_bf16_store(lay, n=-1) == -4
+    assert _call_bf16_store(lay, sh=-1) == -4
+    assert _call_bf16_store(lay, n=0, pool=None) == 0
 
 
 def _call_demote(lay, **over):
