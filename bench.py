@@ -16,7 +16,9 @@ pools (2.1 GB) are cycled, so the 256 MB Infinity Cache cannot hold the timed da
 Prints one JSON line: value = effective HBM GB/s of the whole decode step (algorithmic bytes of
 all 36 layers / step time); decode_steps_per_s; roofline of the segment-pass kernel (the
 dominant one) timed with events on its stream; cpu_baseline = the CPU oracle timed on one KV
-head of one layer and scaled.
+head of one layer and scaled; bf16_baseline = the same decode step over a cache that keeps every
+token in BF16 pages (the comparison the pages' speedup figures are stated against), with the
+INT2 / BF16 step-time ratio.
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true",
+                    help="skip the all-BF16 paged cache leg (the comparison the pages quote)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibration of the HBM byte counters) and exit")
@@ -335,9 +339,124 @@ def main():
                      "timing": f"HIP events around {args.steps} replays of a graph of "
                                f"{n_layers} launches (one per layer pool), per-launch mean"},
     }
+    if not args.no_bf16_baseline:
+        int2_layer_bytes = ok.pool_bytes(layers[0].lay) + 2 * (ok.sink_bytes(layers[0].lay) +
+                                                               ok.recent_bytes(layers[0].lay))
+        result["bf16_baseline"] = bf16_baseline(wl, lengths, n_layers, args, capture, ms_per_step,
+                                                int2_layer_bytes)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], lengths[0], B)
     print(json.dumps(result), flush=True)
+
+
+BF16_POOL_BUDGET = 64e9   # bytes of BF16 layer pools a run may hold
+
+
+def bf16_baseline(wl, lengths, n_layers, args, capture, int2_ms_per_step, int2_layer_bytes):
+    """The same decode step over an all-BF16 paged cache: per layer, store the new token
+    (oscar_bf16_store) and attend over every cached token (oscar_bf16_decode_attn: split-KV
+    kernel + merge), all layers in one HIP graph.  Layers cycle over distinct pools that together
+    exceed the Infinity Cache (every layer has its own pool when they fit BF16_POOL_BUDGET)."""
+    dev = "cuda"
+    B = len(lengths)
+    total_steps = args.warmup + args.steps + 2
+    spare = total_steps + 8
+    hkv, hq = wl.num_kv_heads, wl.num_q_heads
+    table_np, num_pages = workloads.page_tables(wl, lengths, 0, spare_tokens=spare, sink=0,
+                                                recent=0)
+    lay = ok.make_layout(hq, hkv, num_pages, B, table_np.shape[1], wl.group_size)
+    layer_bytes = ok.bf16_pool_bytes(lay)
+    n_pools = max(1, min(n_layers, int(BF16_POOL_BUDGET // layer_bytes)))
+    pools = []
+    t0 = time.time()
+    shared = (wl.shared_prefix // 64) * 64 if wl.shared_prefix else 0
+    longest = int(np.argmax(lengths))
+    for i in range(n_pools):
+        t_np, _ = workloads.page_tables(wl, lengths, i, spare_tokens=spare, sink=0, recent=0)
+        table = torch.from_numpy(t_np).to(dev)
+        pool = torch.empty(layer_bytes, dtype=torch.uint8, device=dev)
+        for b, L in enumerate(lengths):
+            lo0 = 0 if (b == longest or not shared) else min(shared, L)
+            for lo in range(lo0, L, 16384):
+                n = min(16384, L - lo)
+                k, v = workloads.kv_tokens(wl, i, b, lo, n, dev)
+                ok.bf16_store(lay, pool, table[b:b + 1], k.unsqueeze(0), v.unsqueeze(0),
+                              torch.full((1,), lo, dtype=torch.int32, device=dev))
+        kn, vn = zip(*[workloads.kv_tokens(wl, i, b, L, 1, dev) for b, L in enumerate(lengths)])
+        pools.append(dict(table=table, pool=pool,
+                          k_new=torch.cat(kn).unsqueeze(1).contiguous(),
+                          v_new=torch.cat(vn).unsqueeze(1).contiguous(),
+                          q=workloads.queries(wl, i, 0, dev, batch=B).contiguous(),
+                          out=torch.empty((B, hq, 128), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    print(f"[bench] built {n_pools} BF16 layer pools ({layer_bytes / 1e9:.2f} GB each) in "
+          f"{time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    lens = pos + 1
+    max_len = max(lengths) + total_steps + 4
+    ws = torch.empty(ok.bf16_decode_workspace_bytes(lay, B, max_len), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        for i in range(n_layers):
+            P = pools[i % n_pools]
+            ok.bf16_store(lay, P["pool"], P["table"], P["k_new"], P["v_new"], pos)
+            ok.bf16_decode_attn(lay, P["pool"], P["table"], lens, P["q"], P["out"], ws, max_len)
+        pos.add_(1)
+        lens.add_(1)
+
+    graph = capture(step)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+
+    # attention alone (split-KV kernel + merge), one launch pair per layer, as in a step
+    wss = [torch.empty_like(ws) for _ in range(n_layers)]
+
+    def attn_launches():
+        for i in range(n_layers):
+            P = pools[i % n_pools]
+            ok.bf16_decode_attn(lay, P["pool"], P["table"], lens, P["q"], P["out"], wss[i],
+                                max_len)
+
+    g2 = capture(attn_launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(args.steps):
+        e0.record()
+        g2.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / n_layers)
+    seen = [int(x) for x in lens.tolist()]
+    # algorithmic bytes per attention launch: K and V rows (512 B per token and KV head, pages
+    # shared by several sequences once), page-table entries, the bf16 query and fp32 output
+    page_tokens = {}
+    for b, L in enumerate(seen):
+        for p_ in range(math.ceil(L / 64)):
+            pid = int(table_np[b, p_])
+            page_tokens[pid] = max(page_tokens.get(pid, 0), min(64, L - 64 * p_))
+    att_bytes = (hkv * 512 * sum(page_tokens.values()) +
+                 4 * sum(math.ceil(L / 64) for L in seen) + B * hq * 128 * (2 + 4))
+    us_avg = float(np.mean(us))
+    achieved = att_bytes / (us_avg * 1e-6) / 1e9
+    return {"decode_steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+            "int2_speedup": round(ms / int2_ms_per_step, 3),
+            "kernel": "bf16_attn_kernel + bf16_merge_kernel (split-KV over BF16 pages)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": int(att_bytes),
+            "avg_launch_us": round(us_avg, 3),
+            "kv_bytes_per_layer": {"int2_pool_plus_bf16_segments": int(int2_layer_bytes),
+                                   "bf16_pool": int(layer_bytes)},
+            "pools": n_pools,
+            "timing": f"step: graph of {n_layers} x (bf16_store + bf16_decode_attn) replayed "
+                      f"{args.steps} times; attention: HIP events around {args.steps} replays "
+                      f"of a graph of {n_layers} bf16_decode_attn calls, per-call mean"}
 
 
 def cpu_baseline(wl, layer0, length, batch):

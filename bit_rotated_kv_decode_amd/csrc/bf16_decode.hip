@@ -8,11 +8,11 @@
 // This file is that baseline on the same page table: every cached token of a sequence, from
 // position 0, sits in a BF16 page.
 //
-// Page block (one page of 64 tokens, one KV head), 32 KiB:
-//   [0, 16384)      keys   [64 tokens][128 channels] bf16, row-major
-//   [16384, 32768)  values [128 channels][64 tokens] bf16 (channel-major)
-// so that one 16-byte load per lane yields 8 channels of one key (a key operand of the matrix
-// cores) or 8 tokens of one value channel (a value operand).
+// Page block (one page of 64 tokens, one KV head), 32 KiB in matrix-core operand order: 32 rows
+// of 64 lanes x 16 bytes; row 16 h + 4 tt + s holds, for lane 16 j + n, key channels
+// 32 s + 8 j .. + 7 of token 32 h + 16 tt + n, and row 16 h + 8 + nt holds, for lane 16 j + n,
+// value channel 16 nt + n of tokens 32 h + 8 j .. + 7.  Every load instruction of a wave then
+// reads 1 KiB of contiguous memory, and each 8-byte group of bf16 elements is one lane's operand.
 //
 // Launch order on one stream:
 //   1. bf16_attn_kernel   split-KV: block = 4 waves on pages [p0, p1) of one (sequence, KV head);
@@ -96,8 +96,7 @@ __global__ __launch_bounds__(256, 2) void bf16_attn_kernel(Bf16DecodeArgs a, Bf1
 
   const int n_wave_pages = max(0, (p1 - p0 - wave + 3) / 4);
   const int n_chunks = 2 * n_wave_pages;
-  const int koff = n * 256 + j * 16;                        // key row n, 8 j-th channel octet
-  const int voff = kBf16ValOff + n * 128 + j * 16;          // value channel n, 8 j-th token octet
+  const int loff = lane * 16;   // the lane's 16 bytes in each 1 KiB row of the block
   auto load_chunk = [&](int ci, Chunk& c) {
     ci = min(ci, n_chunks - 1);   // clamped prefetch: the same loads every round
     const int half = ci & 1;
@@ -110,11 +109,11 @@ __global__ __launch_bounds__(256, 2) void bf16_attn_kernel(Bf16DecodeArgs a, Bf1
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        c.k[tt][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff,
-                                                           (32 * half + 16 * tt) * 256 + 64 * s, aux);
+        c.k[tt][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, loff,
+                                                           (16 * half + 4 * tt + s) * 1024, aux);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
-      c.v[nt] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, nt * 2048 + 64 * half, aux);
+      c.v[nt] = __builtin_amdgcn_raw_buffer_load_b128(rs, loff, (16 * half + 8 + nt) * 1024, aux);
   };
   auto process_chunk = [&](int ci, Chunk& c) {
     const int tok0 = (p0 + wave + 4 * (ci >> 1)) * kPage + 32 * (ci & 1);
@@ -269,9 +268,9 @@ __global__ __launch_bounds__(128) void bf16_merge_kernel(Bf16DecodeArgs a, Bf16P
   if (a.lse != nullptr && c == 0) a.lse[row] = (m + log2f(l)) * 0.6931471805599453f;
 }
 
-// Token i of sequence b goes to position start_pos[b] + i: key row and value column of slot
-// pos % 64 in page page_table[b][pos / 64].  One wave per (token, KV head, sequence); lane l
-// moves channels 2 l and 2 l + 1.
+// Token i of sequence b goes to position start_pos[b] + i, slot pos % 64 of page
+// page_table[b][pos / 64], in the operand order of the block (see the top of this file).  One
+// wave per (token, KV head, sequence); lane l moves channels 2 l and 2 l + 1.
 __global__ __launch_bounds__(64) void bf16_store_kernel(Bf16StoreArgs a) {
   const int i = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int l = threadIdx.x;
@@ -281,10 +280,18 @@ __global__ __launch_bounds__(64) void bf16_store_kernel(Bf16StoreArgs a) {
   uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * a.hkv + kv) * kBf16Block;
   const int64_t src = b * a.stride_b + i * a.stride_t + kv * a.stride_h + 2 * l;
   const uint32_t k0 = a.k_src[src], k1 = a.k_src[src + 1];
-  reinterpret_cast<uint32_t*>(blk + slot * kHeadDim * 2)[l] = k0 | (k1 << 16);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(blk + kBf16ValOff);
-  vt[(2 * l) * kPage + slot] = a.v_src[src];
-  vt[(2 * l + 1) * kPage + slot] = a.v_src[src + 1];
+  const int h = slot >> 5, tt = (slot >> 4) & 1, tn = slot & 15;
+  const int c = 2 * l;   // key: channels c, c + 1 = elements (c % 8), (c % 8) + 1 of one lane
+  const int krow = 16 * h + 4 * tt + (c >> 5), klane = 16 * ((c & 31) >> 3) + tn;
+  reinterpret_cast<uint32_t*>(blk + krow * 1024 + klane * 16)[(c & 7) >> 1] = k0 | (k1 << 16);
+  uint16_t* v = reinterpret_cast<uint16_t*>(blk);
+  const int vj = (slot & 31) >> 3, ve = slot & 7;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int ch = c + e;
+    const int vrow = 16 * h + 8 + (ch >> 4), vlane = 16 * vj + (ch & 15);
+    v[(vrow * 1024 + vlane * 16) / 2 + ve] = a.v_src[src + e];
+  }
 }
 
 }  // namespace

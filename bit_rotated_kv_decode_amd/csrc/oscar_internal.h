@@ -125,10 +125,9 @@ struct QueryArgs {
   float* qmeta;           // workspace: fp32 [batch][hq][4]
 };
 
-// ---- paged BF16 baseline: every cached token in a BF16 page block of 64 tokens and one KV head,
-// keys [64][128] row-major then values [128][64] channel-major (32 KiB).
-constexpr int kBf16ValOff = kPage * kHeadDim * 2;   // 16384
-constexpr int kBf16Block = 2 * kBf16ValOff;         // 32768
+// ---- paged BF16 baseline: every cached token in a BF16 page block of 64 tokens and one KV head
+// (keys and values, 32 KiB, in matrix-core operand order: see bf16_decode.hip).
+constexpr int kBf16Block = 2 * kPage * kHeadDim * 2;   // 32768
 
 struct Bf16Plan {
   int batch = 0, hq = 0, hkv = 0, gqa = 0;

@@ -253,9 +253,14 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
  * kind of page table, and compute the same attention without rotation or quantisation.
  *
  * BF16 pool: num_pages pages; pool bytes [page][kv_head][block], block =
- * oscar_bf16_page_block_bytes() = 32,768 bytes for 64 tokens of one KV head:
- *     offset 0       keys   [64 tokens][128 channels] bf16, row-major
- *     offset 16384   values [128 channels][64 tokens] bf16, channel-major
+ * oscar_bf16_page_block_bytes() = 32,768 bytes for 64 tokens of one KV head, stored as 32 rows
+ * of 64 chunks of 16 bytes (8 bf16 elements) in matrix-core operand order:
+ *     key   (slot t, channel c): row 16 (t / 32) + 4 ((t / 16) % 2) + c / 32,
+ *                                chunk 16 ((c % 32) / 8) + t % 16, element c % 8
+ *     value (slot t, channel c): row 16 (t / 32) + 8 + c / 16,
+ *                                chunk 16 ((t % 32) / 8) + c % 16, element t % 8
+ * (byte offset = 1024 row + 16 chunk + 2 element), so that each row is exactly what one load
+ * instruction of a 64-lane wave fetches for its key or value operands.
  * Token at position t of sequence b lives in page page_table[b][t / 64], slot t % 64.  Slots past
  * a sequence's length may hold any bits; the kernels never let them reach a result.
  * Of the layout, these calls use head_dim (128), num_q_heads, num_kv_heads, page_tokens (64),

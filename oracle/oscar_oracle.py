@@ -470,9 +470,23 @@ def merge_partials(parts):
 # ----------------------------------------------------------------------------------------------
 # paged BF16 baseline ([W1] and [W3], evaluation part, and [P] Abstract state the INT2 history's
 # memory and decode-speed gains against a history kept in BF16).  The layout is this project's
-# own (include/oscar.h): one block per (page, KV head) of ``page`` tokens holds the keys
-# [page][d] row-major, then the values [d][page] channel-major; the token at position t of a
-# sequence lives in page table_row[t // page], slot t % page.  Values are bf16 bit patterns.
+# own (include/oscar.h): one block per (page, KV head) of 64 tokens holds every key and value
+# element of those tokens, 32 rows of 64 chunks of 8 bf16 elements; the token at position t of a
+# sequence lives in page table_row[t // 64], slot t % 64.  Values are bf16 bit patterns.
+
+def bf16_key_index(slot, c):
+    """Element index (in bf16 units) of key channel c of page slot ``slot`` inside a block."""
+    row = 16 * (slot // 32) + 4 * ((slot // 16) % 2) + c // 32
+    chunk = 16 * ((c % 32) // 8) + slot % 16
+    return row * 512 + chunk * 8 + c % 8
+
+
+def bf16_value_index(slot, c):
+    """Element index (in bf16 units) of value channel c of page slot ``slot`` inside a block."""
+    row = 16 * (slot // 32) + 8 + c // 16
+    chunk = 16 * ((slot % 32) // 8) + c % 16
+    return row * 512 + chunk * 8 + slot % 8
+
 
 def bf16_new_pool(num_pages: int, num_kv_heads: int, d: int = 128, page: int = 64,
                   fill: int = 0) -> np.ndarray:
@@ -481,23 +495,23 @@ def bf16_new_pool(num_pages: int, num_kv_heads: int, d: int = 128, page: int = 6
 
 
 def bf16_store(pool, table_row, pos: int, head: int, k_bits, v_bits, page: int = 64) -> None:
-    """Write one token's key and value (uint16 bit patterns, length d) at position ``pos``."""
-    d = len(k_bits)
+    """Write one token's key and value (uint16 bit patterns, length 128) at position ``pos``."""
+    c = np.arange(len(k_bits))
     blk = pool[int(table_row[pos // page]), head]
     slot = pos % page
-    blk[slot * d:(slot + 1) * d] = k_bits
-    blk[page * d + np.arange(d) * page + slot] = v_bits
+    blk[bf16_key_index(slot, c)] = k_bits
+    blk[bf16_value_index(slot, c)] = v_bits
 
 
 def bf16_gather(pool, table_row, length: int, head: int, d: int = 128, page: int = 64):
     """Keys and values (length, d) of positions 0 .. length-1, as uint16 bit patterns."""
     keys = np.empty((length, d), dtype=np.uint16)
     values = np.empty((length, d), dtype=np.uint16)
+    c = np.arange(d)
     for t in range(length):
         blk = pool[int(table_row[t // page]), head]
-        slot = t % page
-        keys[t] = blk[slot * d:(slot + 1) * d]
-        values[t] = blk[page * d + np.arange(d) * page + slot]
+        keys[t] = blk[bf16_key_index(t % page, c)]
+        values[t] = blk[bf16_value_index(t % page, c)]
     return keys, values
 
 

@@ -14,23 +14,35 @@ import oracle
 
 
 def test_hand_worked_positions():
-    # token 70 of a sequence whose page table row is [5, 2]: page 2, slot 6.  Key channel 3 sits
-    # at element 6 * 128 + 3 = 771 of the block; value channel 3 at 64 * 128 + 3 * 64 + 6 = 8390.
+    # token 70 of a sequence whose page table row is [5, 2]: page 2, slot 6.  Key channel 3:
+    # row 0, chunk 6 (key octet 0, token 6 of its 16), element 3 -> 0 * 512 + 6 * 8 + 3 = 51.
+    # Value channel 3: row 8 (value tile 0), chunk 3 (token octet 0, channel 3), element 6
+    # -> 8 * 512 + 3 * 8 + 6 = 4126.
     pool = oracle.bf16_new_pool(6, 2)
     k = np.zeros(128, np.uint16)
     v = np.zeros(128, np.uint16)
     k[3] = 0x1234
     v[3] = 0xABCD
     oracle.bf16_store(pool, [5, 2], 70, 1, k, v)
-    assert pool[2, 1, 771] == 0x1234
-    assert pool[2, 1, 8390] == 0xABCD
+    assert pool[2, 1, 51] == 0x1234
+    assert pool[2, 1, 4126] == 0xABCD
     assert np.count_nonzero(pool) == 2
-    # token 0 of the same row: page 5, slot 0 -> key element c, value element 8192 + 64 c
-    k[:] = np.arange(128)
-    v[:] = np.arange(128) + 1000
-    oracle.bf16_store(pool, [5, 2], 0, 0, k, v)
-    assert np.array_equal(pool[5, 0, :128], np.arange(128))
-    assert np.array_equal(pool[5, 0, 8192 + 64 * np.arange(128)], np.arange(128) + 1000)
+    # slot 53 (second half of the page, second 16-token tile, token 5 of it), channel 77:
+    # key row 16 + 4 + 2 = 22, chunk 16 * 1 + 5 = 21, element 5 -> 11437;
+    # value row 16 + 8 + 4 = 28, chunk 16 * 2 + 13 = 45, element 5 -> 14701
+    assert oracle.bf16_key_index(53, 77) == 11437
+    assert oracle.bf16_value_index(53, 77) == 14701
+    # one lane's 16-byte chunk holds 8 consecutive key channels of one token, or one value
+    # channel of 8 consecutive tokens
+    assert [oracle.bf16_key_index(0, c) for c in range(10)] == [0, 1, 2, 3, 4, 5, 6, 7, 128, 129]
+    assert [oracle.bf16_value_index(t, 0) for t in range(10)] == \
+        [4096, 4097, 4098, 4099, 4100, 4101, 4102, 4103, 4096 + 128, 4096 + 129]
+
+
+def test_block_indices_are_a_bijection():
+    idx = [oracle.bf16_key_index(t, c) for t in range(64) for c in range(128)]
+    idx += [oracle.bf16_value_index(t, c) for t in range(64) for c in range(128)]
+    assert sorted(idx) == list(range(2 * 64 * 128))
 
 
 def test_store_gather_round_trip_on_shuffled_pages():
@@ -48,8 +60,10 @@ def test_store_gather_round_trip_on_shuffled_pages():
         assert np.array_equal(k, keys[:, h]) and np.array_equal(v, values[:, h])
     # slots past the length and pages not in the row keep the fill
     blk = pool[row[3], 0]
-    slot = length % 64
-    assert np.all(blk[slot * 128:64 * 128] == 0x7FC0)
+    c = np.arange(128)
+    for slot in range(length % 64, 64):
+        assert np.all(blk[oracle.bf16_key_index(slot, c)] == 0x7FC0)
+        assert np.all(blk[oracle.bf16_value_index(slot, c)] == 0x7FC0)
     for pg in set(range(8)) - set(row.tolist()):
         assert np.all(pool[pg] == 0x7FC0)
     # every element of a stored token is written exactly once: the pages used hold
