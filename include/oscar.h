@@ -248,7 +248,7 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
  * Paged BF16 baseline.  The pages report the INT2 history's system gains against a history kept
  * in BF16 ([W1] and its repost, evaluation part: about 8x less KV memory, up to 3x faster
  * batch-1 decoding at 100k context with a full prefix-cache hit, up to 7x throughput at large
- * batch under one memory budget; [P] Abstract: "up to 3x over BF16" at batch size 1).  These
+ * batch under one memory budget; [P] Abstract: batch-1 decoding up to 3x faster than BF16).  These
  * entry points keep every cached token of a sequence, from position 0, in BF16 pages on the same
  * kind of page table, and compute the same attention without rotation or quantisation.
  *
