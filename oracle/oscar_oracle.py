@@ -567,6 +567,47 @@ def clip_threshold(x, u, percentile: float = 99.9) -> float:
 
 
 # ----------------------------------------------------------------------------------------------
+# the error chain of the rotation choices ([W1] figure 1, section OSCAR 的动机: naive INT2,
+# Hadamard-only, clip-only and OSCAR compared by the attention-score KL and the attention-output
+# MSE their quantisation noise causes, not only by K/V reconstruction error).  The frame of each
+# variant is an orthogonal R: identity (naive, clip-only), H P / sqrt(d) (Hadamard-only, U = I)
+# or U H P / sqrt(d) (OSCAR); no clip is an infinite threshold.
+
+def frame_matrix(u=None, d: int = 128) -> np.ndarray:
+    """Orthogonal frame of a variant: U H P / sqrt(d) for a basis U, the identity for None."""
+    return np.eye(d) if u is None else rotation_matrix(u)
+
+
+def quantize_roundtrip(x, r, clip, group: int) -> np.ndarray:
+    """Vectors x (n, d) quantised in the frame R (x' = x R, rounded to fp32, clipped to |x'| <=
+    clip, group INT2 codes with fp16 scale and zero point) and mapped back: (s c + z) R^T, fp64."""
+    xr = (np.asarray(x, dtype=np.float64) @ r).astype(np.float32)
+    codes, scale, zero, _ = quantize(xr, clip, group)
+    return dequantize(codes, scale, zero, group) @ np.asarray(r, dtype=np.float64).T
+
+
+def attention_error_metrics(q, keys, values, keys_hat, values_hat, sm_scale: float):
+    """Errors that replacing (keys, values) (n, d) by (keys_hat, values_hat) causes for queries
+    q (m, d): mean over queries of KL(p || p_hat) of the softmax score distributions, mean squared
+    error of the attention outputs per element, and mean squared K and V reconstruction errors."""
+    q = np.asarray(q, dtype=np.float64)
+    s = (q @ np.asarray(keys, np.float64).T) * sm_scale
+    sh = (q @ np.asarray(keys_hat, np.float64).T) * sm_scale
+    ls = s - s.max(axis=1, keepdims=True)
+    ls -= np.log(np.exp(ls).sum(axis=1, keepdims=True))
+    lsh = sh - sh.max(axis=1, keepdims=True)
+    lsh -= np.log(np.exp(lsh).sum(axis=1, keepdims=True))
+    p = np.exp(ls)
+    kl = float(np.mean(np.sum(p * (ls - lsh), axis=1)))
+    o = p @ np.asarray(values, np.float64)
+    oh = np.exp(lsh) @ np.asarray(values_hat, np.float64)
+    mse = float(np.mean((o - oh) ** 2))
+    k_err = float(np.mean((np.asarray(keys, np.float64) - keys_hat) ** 2))
+    v_err = float(np.mean((np.asarray(values, np.float64) - values_hat) ** 2))
+    return kl, mse, k_err, v_err
+
+
+# ----------------------------------------------------------------------------------------------
 # byte accounting ([W3] evaluation: effective bits per KV element and the ~8x memory claim)
 
 def history_bytes_per_token_head(head_dim: int, group: int) -> int:

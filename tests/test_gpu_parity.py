@@ -107,6 +107,22 @@ def test_attention_end_to_end_tiny():
     assert err <= ATTN_TOL
 
 
+def test_hadamard_only_variant_end_to_end():
+    # the Hadamard-only variant of the error chain (U = I, no clip: the largest finite clip):
+    # GPU demotion and attention against the oracle's, through the same kernels
+    wl = _tiny(num_q_heads=8, num_kv_heads=2)
+    eye = torch.eye(128, dtype=torch.float32).expand(2, 128, 128).contiguous()
+    no_clip = np.full(2, 65504.0, np.float32)
+    case = Case(wl, [1500, 777], u=(eye, eye.clone()), clip=(no_clip, no_clip))
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g)
+    out, _ = case.gpu_attention(g, cache)
+    ref, _ = case.oracle_attention(case.oracle_pool())
+    err = attention_error(out, ref)
+    _note(f"hadamard-only end-to-end max row error {err:.3e}")
+    assert err <= ATTN_TOL
+
+
 def test_page_shuffle_and_split_invariance():
     wl = _tiny(num_q_heads=8, num_kv_heads=2)
     case = Case(wl, [5000, 2222], spare=150000)   # room for a larger planning bound
