@@ -242,9 +242,13 @@ __global__ __launch_bounds__(256, 2) void bf16_attn_kernel(Bf16DecodeArgs a, Bf1
   }
 }
 
-// One 128-thread block per (sequence, query head); thread c owns output channel c.  Splits the
-// sequence does not reach were never written and are skipped.
+// One 128-thread block per (sequence, query head); thread c owns output channel c.  The split
+// statistics go through LDS (one load per thread and round), the accumulators are loaded eight
+// splits at a time so that their round trips overlap.  Splits the sequence does not reach were
+// never written and are skipped.
 __global__ __launch_bounds__(128) void bf16_merge_kernel(Bf16DecodeArgs a, Bf16Plan p) {
+  __shared__ float2 st[kMaxSplits];
+  __shared__ float red[2];
   const int row = blockIdx.x;   // b * hq + head
   const int b = row / p.hq;
   const int c = threadIdx.x;
@@ -256,12 +260,31 @@ __global__ __launch_bounds__(128) void bf16_merge_kernel(Bf16DecodeArgs a, Bf16P
   const float* pacc = reinterpret_cast<const float*>(a.workspace + p.off_acc) +
                       static_cast<int64_t>(row) * p.num_splits * kHeadDim;
   float m = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) m = fmaxf(m, ml[s].x);
+  for (int s = c; s < n_valid; s += 128) {
+    const float2 v = ml[s];
+    st[s] = v;
+    m = fmaxf(m, v.x);
+  }
+  m = dev::wave_max(m);
+  if ((c & 63) == 0) red[c >> 6] = m;
+  __syncthreads();
+  m = fmaxf(red[0], red[1]);
   float l = 0.f, o = 0.f;
-  for (int s = 0; s < n_valid; ++s) {
-    const float2 st = ml[s];
-    const float f = __builtin_amdgcn_exp2f(st.x - m);
-    l = fmaf(st.y, f, l);
+  int s = 0;
+  for (; s + 8 <= n_valid; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = pacc[static_cast<int64_t>(s + i) * kHeadDim + c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = __builtin_amdgcn_exp2f(st[s + i].x - m);
+      l = fmaf(st[s + i].y, f, l);
+      o = fmaf(v[i], f, o);
+    }
+  }
+  for (; s < n_valid; ++s) {
+    const float f = __builtin_amdgcn_exp2f(st[s].x - m);
+    l = fmaf(st[s].y, f, l);
     o = fmaf(pacc[static_cast<int64_t>(s) * kHeadDim + c], f, o);
   }
   a.out[static_cast<int64_t>(row) * kHeadDim + c] = o / l;
