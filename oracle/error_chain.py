@@ -20,6 +20,7 @@ U_v from the score-weighted values (S V)^T (S V)); evaluation queries are drawn 
 stream of their own.
 
 Usage:  python -m oracle.error_chain [--context N] [--calib N] [--eval N] [--kv-heads 0,1]
+                                    [--group 64]
 """
 from __future__ import annotations
 
@@ -94,10 +95,13 @@ def main(argv=None):
     ap.add_argument("--calib", type=int, default=None, help="calibration query positions")
     ap.add_argument("--eval", type=int, default=64, help="held-out decode query positions")
     ap.add_argument("--kv-heads", default="0")
+    ap.add_argument("--group", type=int, default=None, help="channels per scale / zero group")
     args = ap.parse_args(argv)
     wl = workloads.get(args.workload)
     if args.context:
         wl = workloads.scaled(wl, context=args.context)
+    if args.group:
+        wl = workloads.scaled(wl, group_size=args.group)
     n_calib = args.calib or wl.calib_queries or 4096
     for kv in (int(x) for x in args.kv_heads.split(",")):
         res = layer_errors(wl, kv, n_calib, args.eval)
