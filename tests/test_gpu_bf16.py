@@ -190,3 +190,26 @@ def test_bf16_shared_prefix_batch():
     case.store_all()
     q = workloads.queries(wl, 0, device="cuda")
     _check(case, q, rows=[(b, h) for b in range(3) for h in (0, 13, 31)])
+
+
+def test_bf16_full_size_qwen3_32b_131k_gqa8():
+    # batch 16 at 131,072 tokens, 64 query / 8 KV heads (G = 8): the shape bench.py times for
+    # this workload's BF16 baseline; sampled rows of the first and last sequence
+    wl = workloads.get("qwen3_32b_131k")
+    case = Bf16Case(wl, workloads.context_lengths(wl))
+    _note(f"bf16 full size 32b: pages={case.num_pages}")
+    case.store_all()
+    q = workloads.queries(wl, 0, device="cuda")
+    _check(case, q, rows=[(b, h) for b in (0, 15) for h in (0, 33, 63)])
+
+
+def test_bf16_full_size_qwen3_8b_b64_shared_prefix():
+    # batch 64, ragged 8k..128k, 32k shared prefix: the batched workload's BF16 baseline shape
+    wl = workloads.get("qwen3_8b_b64_prefix")
+    lengths = workloads.context_lengths(wl)
+    case = Bf16Case(wl, lengths)
+    _note(f"bf16 full size b64: pages={case.num_pages}, lengths {min(lengths)}..{max(lengths)}")
+    case.store_all()
+    q = workloads.queries(wl, 0, device="cuda")
+    longest, shortest = int(np.argmax(lengths)), int(np.argmin(lengths))
+    _check(case, q, rows=[(b, h) for b in (longest, shortest, 7) for h in (2, 29)])
