@@ -127,6 +127,16 @@ def test_bf16_store_and_attention_ragged(hq, hkv):
     _check(case, q)
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 2)])
+def test_bf16_single_sequence_every_gqa(hq, hkv):
+    # one sequence per launch selects the non-temporal page loads
+    wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
+    case = Bf16Case(wl, [2345])
+    case.store_all()
+    q = workloads.queries(wl, 0, device="cuda", batch=1)
+    _check(case, q)
+
+
 def test_bf16_page_table_shuffle_gives_identical_output():
     wl = workloads.get("tiny_gqa4_1k")
     lengths = [2000, 777]

@@ -77,6 +77,11 @@ ATTN_CASES = {
     "gqa8_g64": dict(wl=dict(num_q_heads=16, num_kv_heads=2, group_size=64),
                      lengths=[3000, 1500, 321]),
     "g64_gqa4": dict(wl=dict(num_q_heads=8, num_kv_heads=2, group_size=64), lengths=[4100]),
+    # one sequence per launch selects the kernels' non-temporal page loads: every GQA width
+    "gqa1_b1": dict(wl=dict(num_q_heads=2, num_kv_heads=2), lengths=[1700]),
+    "gqa2_b1_g64": dict(wl=dict(num_q_heads=4, num_kv_heads=2, group_size=64), lengths=[2222]),
+    "gqa8_b1": dict(wl=dict(num_q_heads=16, num_kv_heads=2), lengths=[2600]),
+    "gqa8_b1_g64": dict(wl=dict(num_q_heads=16, num_kv_heads=2, group_size=64), lengths=[1901]),
 }
 
 
