@@ -26,7 +26,7 @@ What the path computes, in the pages' terms:
     with an online-softmax merge; the result is ordinary softmax attention over the whole cache
     ([W1] §OSCAR 的设计).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1  x' = x R for a row vector x (U first, then the Hadamard, then the permutation).
   R2  Hadamard in Sylvester order, scaled by 1/sqrt(d); bit-reversal reverses the log2(d)-bit
       channel index, P[i, j] = 1 iff i = rev(j).
@@ -66,7 +66,7 @@ import numpy as np
 @dataclasses.dataclass(frozen=True)
 class Geometry:
     """Cache geometry.  The pages fix sink = 64 and recent = 256 ([W1] §OSCAR 的设计); page = 64
-    tokens is this build's paged-KV block.  Smaller values serve brute-force tests."""
+    tokens is the library's paged-KV block.  Smaller values serve brute-force tests."""
 
     head_dim: int = 128
     group: int = 128

@@ -3,7 +3,7 @@
 The pages require a paged KV pool ("超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化",
 section OSCAR 的设计: compatible with paged KV and a radix prefix cache) and say that a new token
 first enters the recent window and that the oldest recent token is then demoted; the byte layout
-inside a page is this build's own (documented in include/oscar.h) and is pinned here by a
+inside a page is this library's own (documented in include/oscar.h) and is pinned here by a
 hand-worked example."""
 import numpy as np
 
