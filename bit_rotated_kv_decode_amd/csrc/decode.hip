@@ -423,9 +423,25 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     for (int pp = 0; pp < PP; ++pp) load_page(min(q + pp, p1 - 1), rr[pp]);
   };
   constexpr int WS = 4 * PP;   // page stride of a wave (four waves per block)
+  // Issue priority by the pages a wave has left (including the current one): the arbiter
+  // otherwise favours the older of the two blocks sharing a compute unit throughout, which then
+  // finishes well before the younger one, and the younger one ends its pages alone at one wave
+  // per SIMD.  Waves far from their end run first, so the two blocks finish together.
+  auto set_prio = [&](int pg_now) {
+    const int rem = (p1 - pg_now + WS - 1) / WS;
+    if (rem >= 6)
+      __builtin_amdgcn_s_setprio(3);
+    else if (rem >= 4)
+      __builtin_amdgcn_s_setprio(2);
+    else if (rem >= 2)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
   for (int attempt = 0; p0 + PP * wave < p1; ++attempt) {
     int pg = p0 + PP * wave;
     uint64_t over = 0;
+    set_prio(pg);
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) load_step(pg + k * WS, r[k]);
     page_scores(pg, r[0], so);
@@ -439,6 +455,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     for (; rest >= kDepth; rest -= kDepth) {
 #pragma unroll
       for (int k = 0; k < kDepth; ++k) {
+        set_prio(pg);
         load_step(pg + (kDepth - 1) * WS, r[k]);
         page_scores(pg, r[(k + 1) % kDepth], so);
         over |= over_limit(so);
@@ -452,6 +469,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
     for (int k = 0; k < kDepth - 1; ++k) {
       if (k < rest) {
+        set_prio(pg);
         page_scores(pg, r[(k + 1) % kDepth], so);
         over |= over_limit(so);
         page_values(r[(k + 1) % kDepth], so);
