@@ -75,14 +75,17 @@ def copy_calibration(mib: int) -> None:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_qwen3_8b_100k_hbm_traffic.md")
 
 
-def recorded_traffic():
-    """HBM bytes per segment-kernel launch recorded from the FETCH_SIZE / WRITE_SIZE counters, or
-    None when the kernel sources changed since (their sha256 is stored with the figure)."""
+def recorded_traffic(workload: str):
+    """HBM bytes per segment-kernel launch recorded from the FETCH_SIZE / WRITE_SIZE counters for
+    ``workload``, or None when they were taken on another workload or the kernel sources changed
+    since (their sha256 is stored with the figure)."""
     try:
         fields = {}
         for line in open(TRAFFIC_FILE):
             key, _, val = line.strip().partition(": ")
             fields[key] = val
+        if fields["workload"] != workload:
+            return None
         h = hashlib.sha256()
         for f in fields["sources"].split():
             h.update(open(os.path.join(ROOT, f), "rb").read())
@@ -249,8 +252,9 @@ def main():
 
     # ---- timed region 2: the segment-pass kernel (INT2 history + BF16 sink / recent blocks in
     # one launch) exactly as a step launches it, once per layer pool: a graph of n_layers launches
-    # replayed args.steps times, HIP events around each replay on the launch stream.  Each layer
-    # gets its own workspace holding its rotated query.
+    # (the pools repeated in turn up to at least 8 launches, so that one graph launch's overhead
+    # is spread) replayed args.steps times, HIP events around each replay on the launch stream.
+    # Each layer gets its own workspace holding its rotated query.
     lens = pos + 1
     seg = ok.STAGE_INT2 | ok.STAGE_BF16
     wss = [torch.empty_like(ws) for _ in layers]
@@ -264,9 +268,12 @@ def main():
     for i in range(len(layers)):
         ok.decode_attn(*seg_args(i), stages=ok.STAGE_QUERY)
 
+    seg_reps = -(-8 // len(layers))
+
     def seg_launches():
-        for i in range(len(layers)):
-            ok.decode_attn(*seg_args(i), stages=seg)
+        for _ in range(seg_reps):
+            for i in range(len(layers)):
+                ok.decode_attn(*seg_args(i), stages=seg)
 
     seg_graph = capture(seg_launches)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -276,7 +283,7 @@ def main():
         seg_graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        seg_us.append(e0.elapsed_time(e1) * 1e3 / len(layers))
+        seg_us.append(e0.elapsed_time(e1) * 1e3 / (seg_reps * len(layers)))
 
     # algorithmic bytes of the timed steps: attention (as the segment launch counts them, plus
     # the bf16 query in and the fp32 output) and the append (new K/V rows in, the displaced row
@@ -331,13 +338,14 @@ def main():
         "roofline": {"kernel": "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(),
+                     "traffic": recorded_traffic(wl.name),
                      "bytes_per_launch": int(seg_bytes),
                      **({"logical_bytes_per_launch": int(seg_logical)}
                         if seg_logical != seg_bytes else {}),
                      "avg_launch_us": round(seg_us_avg, 3),
                      "timing": f"HIP events around {args.steps} replays of a graph of "
-                               f"{n_layers} launches (one per layer pool), per-launch mean"},
+                               f"{seg_reps * n_layers} launches ({seg_reps} per layer pool), "
+                               f"per-launch mean"},
     }
     if not args.no_bf16_baseline:
         int2_layer_bytes = ok.pool_bytes(layers[0].lay) + 2 * (ok.sink_bytes(layers[0].lay) +

@@ -14,6 +14,9 @@ cache.
   clip_only      R = I,              clip = 99.9th percentile of |x|
   oscar          R = U H P / sqrt(d) with the calibrated U_k / U_v, clip = 99.9th percentile
                  of |x R|
+  oscar_lloyd_max  the OSCAR frame and clip with a Lloyd-Max codebook in place of the uniform
+                 grid (the oracle's reading R19), its levels fitted on the keys / values of
+                 another sequence of the same layer (calibration data, not the evaluated history)
 
 Calibration follows the oracle's calibration functions (U_k from the calibration queries' Q^T Q,
 U_v from the score-weighted values (S V)^T (S V)); evaluation queries are drawn from a seed
@@ -37,14 +40,15 @@ if __package__ in (None, ""):
 import workloads  # noqa: E402
 from oracle import oscar_oracle as O  # noqa: E402
 
-VARIANTS = ("naive", "hadamard_only", "clip_only", "oscar")
+VARIANTS = ("naive", "hadamard_only", "clip_only", "oscar", "oscar_lloyd_max")
 
 
 def _f64(t) -> np.ndarray:
     return t.double().cpu().numpy()
 
 
-def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percentile=99.9):
+def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percentile=99.9,
+                 variants=VARIANTS):
     """{variant: (score KL, output MSE, key MSE, value MSE)} for KV head ``kv`` of sequence 0."""
     d = wl.head_dim
     gq = wl.gqa
@@ -69,20 +73,38 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
         "oscar": (O.frame_matrix(u_k, d), O.clip_threshold(k, u_k, percentile),
                   O.frame_matrix(u_v, d), O.clip_threshold(v, u_v, percentile)),
     }
+    frames["oscar_lloyd_max"] = frames["oscar"]
+    levels = codebooks(wl, kv, frames["oscar"], layer) if "oscar_lloyd_max" in variants else None
     out = {}
-    for name in VARIANTS:
+    for name in variants:
         rk, ck, rv, cv = frames[name]
         k_hat, v_hat = k.copy(), v.copy()
-        k_hat[hist] = O.quantize_roundtrip(k[hist], rk, ck, wl.group_size)
-        v_hat[hist] = O.quantize_roundtrip(v[hist], rv, cv, wl.group_size)
+        if name == "oscar_lloyd_max":
+            k_hat[hist] = O.quantize_roundtrip_codebook(k[hist], rk, ck, wl.group_size, levels[0])
+            v_hat[hist] = O.quantize_roundtrip_codebook(v[hist], rv, cv, wl.group_size, levels[1])
+        else:
+            k_hat[hist] = O.quantize_roundtrip(k[hist], rk, ck, wl.group_size)
+            v_hat[hist] = O.quantize_roundtrip(v[hist], rv, cv, wl.group_size)
         out[name] = O.attention_error_metrics(q_eval, k, v, k_hat, v_hat, sm)
+    return out
+
+
+def codebooks(wl, kv: int, frame, layer: int = 0, n_tokens: int = 4096, iters: int = 100):
+    """Lloyd-Max levels (keys, values) for KV head ``kv``, fitted on the coordinates t of the
+    first ``n_tokens`` keys / values of sequence 1 in the given (R_k, clip_k, R_v, clip_v) frame."""
+    rk, ck, rv, cv = frame
+    k_cal, v_cal = workloads.kv_tokens(wl, layer, 1, 0, n_tokens)
+    out = []
+    for x, r, c in ((_f64(k_cal[:, kv]), rk, ck), (_f64(v_cal[:, kv]), rv, cv)):
+        t = O.codebook_coordinates((x @ r).astype(np.float32), c, wl.group_size)
+        out.append(O.lloyd_max(t, iters=iters)[0])
     return out
 
 
 def table(results) -> str:
     lines = ["| variant | attention-score KL | attention-output MSE | key MSE | value MSE |",
              "|---|---|---|---|---|"]
-    for name in VARIANTS:
+    for name in (v for v in VARIANTS if v in results):
         kl, mse, ke, ve = results[name]
         lines.append(f"| {name} | {kl:.4e} | {mse:.4e} | {ke:.4e} | {ve:.4e} |")
     return "\n".join(lines)

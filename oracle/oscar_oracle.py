@@ -51,6 +51,8 @@ Readings taken where the pages are silent:
       eigenvectors of (S V)^T (S V) with S = softmax(Q K^T / sqrt(d)) ([W1] §OSCAR 的设计 names the
       two covariances); eigenvectors in descending eigenvalue order, each column's largest-magnitude
       entry made positive; clip = a percentile of |x R|.
+  R19 (analysis only, not on the GPU path) a Lloyd-Max codebook keeps R5's scale and zero and
+      replaces the grid {0, 1, 2, 3} by four levels fitted by Lloyd's algorithm (``lloyd_max``).
 """
 from __future__ import annotations
 
@@ -584,6 +586,73 @@ def quantize_roundtrip(x, r, clip, group: int) -> np.ndarray:
     xr = (np.asarray(x, dtype=np.float64) @ r).astype(np.float32)
     codes, scale, zero, _ = quantize(xr, clip, group)
     return dequantize(codes, scale, zero, group) @ np.asarray(r, dtype=np.float64).T
+
+
+# ----------------------------------------------------------------------------------------------
+# a Lloyd-Max codebook in place of the uniform INT2 grid ([W3], the closing comparison with
+# TurboQuant: OSCAR's newer code pairs the attention-aware rotation with a Lloyd-Max codebook;
+# the page gives no further detail).  Reading R19: the group's fp16 scale and zero point stay as
+# in R5 and map the clipped group onto t = (x'' - z) / s in [0, 3]; a code names one of four
+# levels l_0 < l_1 < l_2 < l_3 in that coordinate (the nearest; a value halfway between two
+# levels takes the lower code), and the stored value is s * l_code + z.  The levels are fitted
+# per (layer, KV head, K|V) on calibration data by Lloyd's algorithm.  {0, 1, 2, 3} is the
+# uniform grid of R5.
+
+def lloyd_max(values, weights=None, levels=(0.0, 1.0, 2.0, 3.0), iters: int = 100):
+    """Lloyd's algorithm for a scalar quantiser with len(levels) reconstruction levels.
+
+    Alternates the two conditions a Lloyd-Max quantiser satisfies: each decision threshold lies
+    halfway between the two levels around it (nearest-neighbour condition), and each level is the
+    (weighted) mean of the values in its cell (centroid condition).  A cell with no weight keeps
+    its level.  ``values`` are samples (or grid points of a density, with ``weights``).
+    Returns (levels, thresholds, distortion before each update and after the last one), the
+    distortion being the weighted mean squared error.
+    """
+    x = np.asarray(values, dtype=np.float64).ravel()
+    w = np.ones_like(x) if weights is None else np.asarray(weights, dtype=np.float64).ravel()
+    lv = np.sort(np.asarray(levels, dtype=np.float64))
+    history = []
+    for _ in range(iters + 1):
+        thr = (lv[:-1] + lv[1:]) / 2
+        cell = np.searchsorted(thr, x, side="left")
+        history.append(float(np.sum(w * (x - lv[cell]) ** 2) / np.sum(w)))
+        if len(history) == iters + 1:
+            break
+        new = lv.copy()
+        for i in range(len(lv)):
+            wi = w[cell == i]
+            if wi.sum() > 0:
+                new[i] = float(np.sum(wi * x[cell == i]) / wi.sum())
+        lv = new
+    return lv, (lv[:-1] + lv[1:]) / 2, history
+
+
+def codebook_coordinates(xr, clip, group: int) -> np.ndarray:
+    """t = (x'' - z) / s of every element of rotated fp32 vectors xr (..., d), with the group's
+    fp16 scale and zero (R5): the coordinate a codebook is fitted in and applied to."""
+    return quantize(xr, clip, group)[3]["t"].astype(np.float64)
+
+
+def quantize_codebook(xr, clip, group: int, levels):
+    """Codes (..., d) of rotated vectors under a codebook (R19), with the fp16 scale and zero of
+    R5 (returned as in ``quantize``)."""
+    _, s16, z16, pre = quantize(xr, clip, group)
+    lv = np.sort(np.asarray(levels, dtype=np.float64))
+    codes = np.searchsorted((lv[:-1] + lv[1:]) / 2, pre["t"].astype(np.float64), side="left")
+    return codes.astype(np.uint8), s16, z16
+
+
+def dequantize_codebook(codes, scale, zero, group: int, levels) -> np.ndarray:
+    """Rotated-space values s * l_code + z in fp64, (..., d)."""
+    lv = np.sort(np.asarray(levels, dtype=np.float64))
+    return dequantize(lv[np.asarray(codes, dtype=np.int64)], scale, zero, group)
+
+
+def quantize_roundtrip_codebook(x, r, clip, group: int, levels) -> np.ndarray:
+    """``quantize_roundtrip`` with the codebook levels in place of the uniform grid."""
+    xr = (np.asarray(x, dtype=np.float64) @ r).astype(np.float32)
+    codes, scale, zero = quantize_codebook(xr, clip, group, levels)
+    return dequantize_codebook(codes, scale, zero, group, levels) @ np.asarray(r, np.float64).T
 
 
 def attention_error_metrics(q, keys, values, keys_hat, values_hat, sm_scale: float):

@@ -1,0 +1,111 @@
+"""Pins of the oracle's Lloyd-Max codebook (reading R19: four levels in the group's normalised
+coordinate, fitted by Lloyd's algorithm, with the uniform INT2 scale and zero point kept).
+
+Lloyd's algorithm is pinned by textbook results it must reproduce: the 4-level Lloyd-Max quantiser
+of a unit Gaussian (J. Max, "Quantizing for minimum distortion", IRE Trans. Inf. Theory, 1960:
+levels +-0.4528 and +-1.510, thresholds 0 and +-0.9816, mean squared error 0.1175) and of a
+uniform density (the uniform mid-rise quantiser, error step^2 / 12); by the two optimality
+conditions at its fixed point; by its non-increasing distortion; and by brute force on four and
+on seven points.  The codebook quantiser is pinned by the special case that reduces it to the uniform INT2
+quantiser (levels 0, 1, 2, 3) and by the nearest-level property."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import error_chain
+
+
+def test_unit_gaussian_matches_max_1960():
+    x = np.linspace(-8.0, 8.0, 400001)
+    lv, thr, hist = oracle.lloyd_max(x, np.exp(-x * x / 2), levels=(-1.5, -0.5, 0.5, 1.5),
+                                     iters=300)
+    assert np.allclose(lv, [-1.510, -0.4528, 0.4528, 1.510], atol=6e-4)
+    assert np.allclose(thr, [-0.9816, 0.0, 0.9816], atol=2e-4)
+    assert hist[-1] == pytest.approx(0.1175, abs=1e-4)
+
+
+def test_uniform_density_gives_the_uniform_mid_rise_quantiser():
+    x = np.linspace(0.0, 3.0, 300001)
+    lv, thr, hist = oracle.lloyd_max(x, levels=(0, 1, 2, 3), iters=300)
+    assert np.allclose(lv, [0.375, 1.125, 1.875, 2.625], atol=1e-4)
+    assert np.allclose(thr, [0.75, 1.5, 2.25], atol=1e-4)
+    assert hist[-1] == pytest.approx(0.75 ** 2 / 12, rel=1e-4)
+
+
+def test_four_points_four_levels_brute_force():
+    pts = np.array([0.1, 0.9, 2.2, 2.95])
+    lv, _, hist = oracle.lloyd_max(pts, levels=(0, 1, 2, 3), iters=3)
+    assert np.allclose(lv, pts) and hist[-1] == 0.0
+    # brute force over every split of 7 sorted points into 4 contiguous cells: the optimal
+    # split's centroids satisfy both conditions, so Lloyd's algorithm started there stays there
+    for seed in range(5):
+        r = np.sort(np.random.default_rng(seed).uniform(0, 3, 7))
+        splits = [(a, b, e) for a in range(1, 5) for b in range(a + 1, 6) for e in range(b + 1, 7)]
+        cost = [sum(((c - c.mean()) ** 2).sum() for c in np.split(r, s)) / 7 for s in splits]
+        best = splits[int(np.argmin(cost))]
+        cent = [c.mean() for c in np.split(r, best)]
+        lv, _, h = oracle.lloyd_max(r, levels=cent, iters=5)
+        assert np.allclose(lv, cent, rtol=0, atol=1e-15)
+        assert h[-1] == pytest.approx(min(cost), rel=1e-12)
+
+
+def test_fixed_point_conditions_and_monotone_distortion():
+    r = np.random.default_rng(1)
+    t = np.clip(r.normal(1.5, 0.6, 20000), 0, 3)
+    lv, thr, hist = oracle.lloyd_max(t, iters=200)
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+    assert np.allclose(thr, (lv[:-1] + lv[1:]) / 2)
+    cell = np.searchsorted(thr, t, side="left")
+    for i in range(4):
+        assert lv[i] == pytest.approx(t[cell == i].mean(), abs=1e-9)
+    # a bell-shaped density pulls the outer levels inwards from the grid's end points
+    assert 0 < lv[0] and lv[3] < 3
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_uniform_levels_reduce_to_the_int2_quantiser(group):
+    r = np.random.default_rng(2)
+    xr = (r.standard_normal((64, 128)) * 3).astype(np.float32)
+    codes, s, z, pre = oracle.quantize(xr, 4.0, group)
+    cb, cs, cz = oracle.quantize_codebook(xr, 4.0, group, (0, 1, 2, 3))
+    assert np.array_equal(s.view(np.uint16), cs.view(np.uint16))
+    assert np.array_equal(z.view(np.uint16), cz.view(np.uint16))
+    frac = pre["t"] - np.floor(pre["t"])
+    tie = frac == 0.5
+    assert not tie.any()   # halfway values would round to even in one and down in the other
+    assert np.array_equal(codes, cb)
+    assert np.array_equal(oracle.dequantize(codes, s, z, group),
+                          oracle.dequantize_codebook(cb, cs, cz, group, (0, 1, 2, 3)))
+
+
+def test_codebook_codes_name_the_nearest_level():
+    r = np.random.default_rng(3)
+    xr = r.standard_normal((32, 128)).astype(np.float32)
+    levels = (0.2, 0.9, 2.05, 2.8)
+    codes, s, z = oracle.quantize_codebook(xr, np.inf, 64, levels)
+    t = oracle.codebook_coordinates(xr, np.inf, 64)
+    dist = np.abs(t[..., None] - np.asarray(levels))
+    assert np.all(dist[np.arange(32)[:, None], np.arange(128), codes] <= dist.min(-1) + 1e-12)
+    # reconstruction is s * level + z group by group
+    sf = np.repeat(s.astype(np.float64), 64, -1)
+    zf = np.repeat(z.astype(np.float64), 64, -1)
+    assert np.allclose(oracle.dequantize_codebook(codes, s, z, 64, levels),
+                       sf * np.asarray(levels)[codes] + zf, rtol=0, atol=1e-12)
+
+
+def test_fitted_codebooks_do_not_lose_on_their_calibration_data():
+    # Lloyd's iterations start from the uniform grid and never increase the distortion, so on the
+    # calibration coordinates the fitted levels do at least as well as the INT2 grid
+    wl = workloads.scaled(workloads.get("qwen3_4b_32k"), context=2048)
+    d = wl.head_dim
+    r = oracle.frame_matrix(np.eye(d), d)
+    k_cal, _ = workloads.kv_tokens(wl, 0, 1, 0, 1024)
+    t = oracle.codebook_coordinates((k_cal[:, 0].double().numpy() @ r).astype(np.float32),
+                                    np.inf, wl.group_size)
+    lv, _, hist = oracle.lloyd_max(t, iters=50)
+    assert hist[-1] <= hist[0]
+    grid = np.clip(np.rint(t), 0, 3)
+    assert hist[0] == pytest.approx(np.mean((t - grid) ** 2), rel=1e-12)
+    levels = error_chain.codebooks(wl, 0, (r, np.inf, r, np.inf), n_tokens=1024, iters=50)
+    assert np.allclose(levels[0], lv)
