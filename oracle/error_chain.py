@@ -17,6 +17,8 @@ cache.
   oscar_lloyd_max  the OSCAR frame and clip with a Lloyd-Max codebook in place of the uniform
                  grid (the oracle's reading R19), its levels fitted on the keys / values of
                  another sequence of the same layer (calibration data, not the evaluated history)
+  oscar_lm_uniform  the same with the codebook held to equally spaced levels (reading R20: the
+                 form the GPU encoder takes; fitted on the same calibration data)
 
 Calibration follows the oracle's calibration functions (U_k from the calibration queries' Q^T Q,
 U_v from the score-weighted values (S V)^T (S V)); evaluation queries are drawn from a seed
@@ -40,7 +42,7 @@ if __package__ in (None, ""):
 import workloads  # noqa: E402
 from oracle import oscar_oracle as O  # noqa: E402
 
-VARIANTS = ("naive", "hadamard_only", "clip_only", "oscar", "oscar_lloyd_max")
+VARIANTS = ("naive", "hadamard_only", "clip_only", "oscar", "oscar_lloyd_max", "oscar_lm_uniform")
 
 
 def _f64(t) -> np.ndarray:
@@ -73,8 +75,10 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
         "oscar": (O.frame_matrix(u_k, d), O.clip_threshold(k, u_k, percentile),
                   O.frame_matrix(u_v, d), O.clip_threshold(v, u_v, percentile)),
     }
-    frames["oscar_lloyd_max"] = frames["oscar"]
+    frames["oscar_lloyd_max"] = frames["oscar_lm_uniform"] = frames["oscar"]
     levels = codebooks(wl, kv, frames["oscar"], layer) if "oscar_lloyd_max" in variants else None
+    spaced = (codebooks(wl, kv, frames["oscar"], layer, uniform=True)
+              if "oscar_lm_uniform" in variants else None)
     out = {}
     for name in variants:
         rk, ck, rv, cv = frames[name]
@@ -82,6 +86,9 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
         if name == "oscar_lloyd_max":
             k_hat[hist] = O.quantize_roundtrip_codebook(k[hist], rk, ck, wl.group_size, levels[0])
             v_hat[hist] = O.quantize_roundtrip_codebook(v[hist], rv, cv, wl.group_size, levels[1])
+        elif name == "oscar_lm_uniform":
+            k_hat[hist] = O.quantize_roundtrip(k[hist], rk, ck, wl.group_size, spaced[0])
+            v_hat[hist] = O.quantize_roundtrip(v[hist], rv, cv, wl.group_size, spaced[1])
         else:
             k_hat[hist] = O.quantize_roundtrip(k[hist], rk, ck, wl.group_size)
             v_hat[hist] = O.quantize_roundtrip(v[hist], rv, cv, wl.group_size)
@@ -89,15 +96,21 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
     return out
 
 
-def codebooks(wl, kv: int, frame, layer: int = 0, n_tokens: int = 4096, iters: int = 100):
+def codebooks(wl, kv: int, frame, layer: int = 0, n_tokens: int = 4096, iters: int = 100,
+              uniform: bool = False):
     """Lloyd-Max levels (keys, values) for KV head ``kv``, fitted on the coordinates t of the
-    first ``n_tokens`` keys / values of sequence 1 in the given (R_k, clip_k, R_v, clip_v) frame."""
+    first ``n_tokens`` keys / values of sequence 1 in the given (R_k, clip_k, R_v, clip_v) frame;
+    with ``uniform`` the equally spaced optimum instead, as (lo, step) in fp32."""
     rk, ck, rv, cv = frame
     k_cal, v_cal = workloads.kv_tokens(wl, layer, 1, 0, n_tokens)
     out = []
     for x, r, c in ((_f64(k_cal[:, kv]), rk, ck), (_f64(v_cal[:, kv]), rv, cv)):
         t = O.codebook_coordinates((x @ r).astype(np.float32), c, wl.group_size)
-        out.append(O.lloyd_max(t, iters=iters)[0])
+        if uniform:
+            lo, step, _ = O.lloyd_max_uniform(t, iters=iters)
+            out.append((np.float32(lo), np.float32(step)))
+        else:
+            out.append(O.lloyd_max(t, iters=iters)[0])
     return out
 
 

@@ -53,6 +53,10 @@ Readings taken where the pages are silent:
       entry made positive; clip = a percentile of |x R|.
   R19 (analysis only, not on the GPU path) a Lloyd-Max codebook keeps R5's scale and zero and
       replaces the grid {0, 1, 2, 3} by four levels fitted by Lloyd's algorithm (``lloyd_max``).
+  R20 the Lloyd-Max codebook restricted to equally spaced levels lo + step * c in the same
+      coordinate (``lloyd_max_uniform``): the same as storing scale' = s * step and zero' =
+      z + s * lo with R5's codes, so it runs on the GPU path unchanged past the encoder
+      (``quantize(..., levels=(lo, step))``).
 """
 from __future__ import annotations
 
@@ -165,13 +169,17 @@ def rotate_to_fp32(x, u) -> np.ndarray:
     return rotate(x, u).astype(np.float32)
 
 
-def quantize(xr, clip, group: int):
+def quantize(xr, clip, group: int, levels=None):
     """Clip and quantise rotated vectors xr (..., d) (fp32) group by group (readings R3-R6).
 
+    ``levels`` = (lo, step) selects an equally spaced codebook (reading R20): the stored scale
+    and zero point become fp16((max-min)/3 * step) and fp16(min + (max-min)/3 * lo), each product
+    and sum rounded to fp32 on its own; None, or (0, 1), is the uniform grid of R5.
     Returns (codes uint8 (..., d), scale fp16 (..., d/g), zero fp16 (..., d/g), pre) where
     ``pre`` holds the values just before each rounding step, for acceptance windows:
-    pre["t"] fp32 (..., d) is (x'' - z) / s before rint, pre["s"] fp32 is (max-min)/3 before the
-    fp16 rounding and pre["z"] fp32 is the group minimum.
+    pre["t"] fp32 (..., d) is (x'' - z) / s before rint, pre["s"] fp32 is the scale before the
+    fp16 rounding ((max-min)/3 on the uniform grid) and pre["z"] fp32 the zero point before it
+    (the group minimum on the uniform grid).
     """
     x = np.asarray(xr, dtype=np.float32)
     c = np.float32(clip)
@@ -181,15 +189,19 @@ def quantize(xr, clip, group: int):
     mn = xg.min(axis=-1)
     mx = xg.max(axis=-1)
     s32 = (mx - mn) / np.float32(3.0)
+    lo, step = (0.0, 1.0) if levels is None else (float(levels[0]), float(levels[1]))
+    z32 = mn if lo == 0.0 else mn + s32 * np.float32(lo)
+    if step != 1.0:
+        s32 = s32 * np.float32(step)
     s16 = s32.astype(np.float16)
-    z16 = mn.astype(np.float16)
+    z16 = z32.astype(np.float16)
     sf = s16.astype(np.float32)[..., None]
     zf = z16.astype(np.float32)[..., None]
     safe = np.where(sf == 0, np.float32(1.0), sf)
     t = (xg - zf) / safe
     codes = np.clip(np.rint(t), 0, 3)
     codes = np.where(sf == 0, 0, codes).astype(np.uint8).reshape(x.shape)
-    pre = {"t": np.where(sf == 0, np.float32(0), t).reshape(x.shape), "s": s32, "z": mn}
+    pre = {"t": np.where(sf == 0, np.float32(0), t).reshape(x.shape), "s": s32, "z": z32}
     return codes, s16, z16, pre
 
 
@@ -203,9 +215,9 @@ def dequantize(codes, scale, zero, group: int) -> np.ndarray:
     return (s * cg + z).reshape(c.shape)
 
 
-def encode(x, u, clip, group: int):
+def encode(x, u, clip, group: int, levels=None):
     """Rotate, clip and quantise vectors x (..., d): the demotion step on values."""
-    return quantize(rotate_to_fp32(x, u), clip, group)
+    return quantize(rotate_to_fp32(x, u), clip, group, levels)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -337,22 +349,25 @@ def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
 # the demotion step and the decode-step write ([W1] §OSCAR 的设计; reading R9)
 
 def demote(pool, page_table, u_k, u_v, clip_k, clip_v, k_src, v_src, hist_start,
-           geom: Geometry):
+           geom: Geometry, levels_k=None, levels_v=None):
     """Encode tokens k_src / v_src (B, n, Hkv, d) and store them at history indices
-    hist_start[b] + i.  Modifies ``pool`` in place."""
+    hist_start[b] + i.  levels_k / levels_v: None (uniform grid) or (lo, step) per KV head
+    (reading R20).  Modifies ``pool`` in place."""
     k_src = np.asarray(k_src, dtype=np.float64)
     v_src = np.asarray(v_src, dtype=np.float64)
     bsz, n, hkv, _ = k_src.shape
     for b in range(bsz):
         idx = int(hist_start[b]) + np.arange(n)
         for h in range(hkv):
-            kq = encode(k_src[b, :, h], u_k[h], clip_k[h], geom.group)[:3]
-            vq = encode(v_src[b, :, h], u_v[h], clip_v[h], geom.group)[:3]
+            kq = encode(k_src[b, :, h], u_k[h], clip_k[h], geom.group,
+                        None if levels_k is None else levels_k[h])[:3]
+            vq = encode(v_src[b, :, h], u_v[h], clip_v[h], geom.group,
+                        None if levels_v is None else levels_v[h])[:3]
             store_history(pool, page_table[b], idx, h, kq, vq, geom)
 
 
 def append(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_k, clip_v,
-           k_new, v_new, seq_slot, seq_lens, geom: Geometry):
+           k_new, v_new, seq_slot, seq_lens, geom: Geometry, levels_k=None, levels_v=None):
     """One decode-step write (reading R9).  seq_lens[b] is the length before the append, i.e. the
     position P of the new token.  P < sink: the token goes to the sink.  Otherwise it goes to
     recent-window ring slot P % recent, and when P >= sink + recent the token it replaces
@@ -370,7 +385,7 @@ def append(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_
             old_k = np.asarray(recent_k[slot, :, r], dtype=np.float64)[None, None]
             old_v = np.asarray(recent_v[slot, :, r], dtype=np.float64)[None, None]
             demote(pool, page_table[b:b + 1], u_k, u_v, clip_k, clip_v, old_k, old_v,
-                   [pos - geom.sink - geom.recent], geom)
+                   [pos - geom.sink - geom.recent], geom, levels_k, levels_v)
         recent_k[slot, :, r] = k_new[b]
         recent_v[slot, :, r] = v_new[b]
 
@@ -580,11 +595,12 @@ def frame_matrix(u=None, d: int = 128) -> np.ndarray:
     return np.eye(d) if u is None else rotation_matrix(u)
 
 
-def quantize_roundtrip(x, r, clip, group: int) -> np.ndarray:
+def quantize_roundtrip(x, r, clip, group: int, levels=None) -> np.ndarray:
     """Vectors x (n, d) quantised in the frame R (x' = x R, rounded to fp32, clipped to |x'| <=
-    clip, group INT2 codes with fp16 scale and zero point) and mapped back: (s c + z) R^T, fp64."""
+    clip, group INT2 codes with fp16 scale and zero point, optionally on the equally spaced
+    codebook ``levels`` = (lo, step)) and mapped back: (s c + z) R^T, fp64."""
     xr = (np.asarray(x, dtype=np.float64) @ r).astype(np.float32)
-    codes, scale, zero, _ = quantize(xr, clip, group)
+    codes, scale, zero, _ = quantize(xr, clip, group, levels)
     return dequantize(codes, scale, zero, group) @ np.asarray(r, dtype=np.float64).T
 
 
@@ -625,6 +641,30 @@ def lloyd_max(values, weights=None, levels=(0.0, 1.0, 2.0, 3.0), iters: int = 10
                 new[i] = float(np.sum(wi * x[cell == i]) / wi.sum())
         lv = new
     return lv, (lv[:-1] + lv[1:]) / 2, history
+
+
+def lloyd_max_uniform(values, weights=None, lo: float = 0.0, step: float = 1.0,
+                      iters: int = 100):
+    """The optimum equally spaced 4-level quantiser (levels lo + step * c, c = 0..3; reading R20)
+    by alternating its two conditions: each value takes the nearest level, code
+    clamp(rint((t - lo) / step), 0, 3); (lo, step) is the (weighted) least-squares line of the
+    values on their codes.  Neither step increases the distortion.  Returns (lo, step,
+    distortion before each update and after the last one)."""
+    x = np.asarray(values, dtype=np.float64).ravel()
+    w = np.ones_like(x) if weights is None else np.asarray(weights, dtype=np.float64).ravel()
+    wt = w.sum()
+    history = []
+    for it in range(iters + 1):
+        c = np.clip(np.rint((x - lo) / step), 0, 3)
+        history.append(float(np.sum(w * (x - lo - step * c) ** 2) / wt))
+        if it == iters:
+            break
+        mc, mx = np.sum(w * c) / wt, np.sum(w * x) / wt
+        var = np.sum(w * (c - mc) ** 2) / wt
+        if var > 0:
+            step = float(np.sum(w * (c - mc) * (x - mx)) / wt / var)
+            lo = float(mx - step * mc)
+    return lo, step, history
 
 
 def codebook_coordinates(xr, clip, group: int) -> np.ndarray:

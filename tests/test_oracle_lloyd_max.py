@@ -109,3 +109,60 @@ def test_fitted_codebooks_do_not_lose_on_their_calibration_data():
     assert hist[0] == pytest.approx(np.mean((t - grid) ** 2), rel=1e-12)
     levels = error_chain.codebooks(wl, 0, (r, np.inf, r, np.inf), n_tokens=1024, iters=50)
     assert np.allclose(levels[0], lv)
+
+
+# ---- the equally spaced codebook that the GPU encoder runs (reading R20)
+
+def test_optimum_uniform_quantiser_of_a_unit_gaussian_matches_max_1960():
+    # Max's table of optimum uniform quantisers: 4 levels, step 0.9957, mean squared error 0.1188
+    x = np.linspace(-8.0, 8.0, 400001)
+    lo, step, hist = oracle.lloyd_max_uniform(x, np.exp(-x * x / 2), lo=-1.5, step=1.0, iters=300)
+    assert step == pytest.approx(0.9957, abs=2e-4)
+    assert lo == pytest.approx(-1.5 * step, abs=1e-4)
+    assert hist[-1] == pytest.approx(0.1188, abs=1e-4)
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+    # and it cannot beat the unconstrained Lloyd-Max quantiser (0.1175)
+    assert hist[-1] > 0.1175
+
+
+def test_optimum_uniform_quantiser_of_a_uniform_density():
+    x = np.linspace(0.0, 3.0, 300001)
+    lo, step, hist = oracle.lloyd_max_uniform(x, iters=300)
+    assert lo == pytest.approx(0.375, abs=1e-4) and step == pytest.approx(0.75, abs=1e-4)
+    assert hist[-1] == pytest.approx(0.75 ** 2 / 12, rel=1e-4)
+
+
+def test_equally_spaced_levels_hand_worked():
+    # groups of 4: [0, 1, 2, 3] and [-2, -1, 0.5, 4] with (lo, step) = (0.5, 2/3):
+    #   group 0: r = 1, scale = fp16(2/3) = 0x3955, zero = fp16(0 + 0.5) = 0x3800;
+    #            t = (x - 0.5) / 0.66650390625 = -0.75, 0.75, 2.25, 3.75 -> codes 0, 1, 2, 3
+    #   group 1: r = 2, scale = fp16(4/3) = 0x3D55, zero = fp16(-2 + 1) = 0xBC00;
+    #            t = -0.75, 0, 1.125, 3.75 -> codes 0, 0, 1, 3
+    x = np.array([[0, 1, 2, 3, -2, -1, 0.5, 4]], np.float32)
+    codes, s, z, _ = oracle.quantize(x, np.inf, 4, (0.5, np.float32(2 / 3)))
+    assert codes.tolist() == [[0, 1, 2, 3, 0, 0, 1, 3]]
+    assert s.view(np.uint16).tolist() == [[0x3955, 0x3D55]]
+    assert z.view(np.uint16).tolist() == [[0x3800, 0xBC00]]
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_plain_levels_are_the_int2_grid(group):
+    r = np.random.default_rng(7)
+    xr = (r.standard_normal((40, 128)) * 2).astype(np.float32)
+    a = oracle.quantize(xr, 3.0, group)
+    b = oracle.quantize(xr, 3.0, group, (0.0, 1.0))
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_equally_spaced_levels_are_a_codebook_on_the_same_coordinate():
+    # with (lo, step) the stored values are zero' + scale' * c; away from rounding boundaries the
+    # codes are those of the R19 codebook quantiser with levels lo + step * c
+    r = np.random.default_rng(8)
+    xr = r.standard_normal((64, 128)).astype(np.float32)
+    lo, step = 0.55, 0.63
+    codes, s, z, pre = oracle.quantize(xr, np.inf, 64, (lo, np.float32(step)))
+    cb, _, _ = oracle.quantize_codebook(xr, np.inf, 64, lo + step * np.arange(4))
+    far = np.abs(pre["t"] - np.floor(pre["t"]) - 0.5) > 1e-2
+    assert np.array_equal(codes[far], cb[far])
+    assert (codes != cb).mean() < 1e-2
