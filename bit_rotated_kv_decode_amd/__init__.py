@@ -71,19 +71,16 @@ _SIGNATURES = {
     "oscar_recent_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_decode_workspace_bytes": (ctypes.c_size_t, [_LP, _i32, _i32]),
     "oscar_check_page_table": (_i32, [_LP, _vp, _vp, _i32, _i32]),
-    "oscar_demote": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
-                            _i32, _i32, _vp]),
-    "oscar_append": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                            _vp, _i32, _vp]),
+    "oscar_demote": (_i32, [_LP] + [_vp] * 10 + [_i64, _i64, _i64, _vp, _i32, _i32, _vp]),
+    "oscar_append": (_i32, [_LP] + [_vp] * 16 + [_i32, _vp]),
     "oscar_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _i32, _i32,
                                  _vp]),
     "oscar_decode_attn_stages": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
                                         _i32, _i32, ctypes.c_uint32, _vp]),
-    "oscar_decode_step": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                 _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
-                                 _i32, _i32, _vp]),
+    "oscar_decode_step": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _vp,
+                                                       ctypes.c_size_t, _i32, _i32, _vp]),
     "oscar_bf16_page_block_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_page_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_pool_bytes": (ctypes.c_size_t, [_LP]),
@@ -185,11 +182,22 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _levels(t: Optional[torch.Tensor], name: str, lay: Layout):
+    if t is None:
+        return None
+    if tuple(t.shape) != (lay.num_kv_heads, 2):
+        raise TypeError(f"{name} must be [Hkv, 2] (lo, step) per KV head")
+    return _contig(t, name, torch.float32)
+
+
 def demote(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, u_k: torch.Tensor,
            u_v: torch.Tensor, clip_k: torch.Tensor, clip_v: torch.Tensor, k_src: torch.Tensor,
-           v_src: torch.Tensor, hist_start: torch.Tensor) -> None:
+           v_src: torch.Tensor, hist_start: torch.Tensor,
+           levels_k: Optional[torch.Tensor] = None,
+           levels_v: Optional[torch.Tensor] = None) -> None:
     """Encode k_src / v_src (bf16 [B, n, Hkv, 128], unit stride on the last axis, the same
-    strides for both) into history indices hist_start[b] + i (oscar_demote)."""
+    strides for both) into history indices hist_start[b] + i (oscar_demote).  levels_k /
+    levels_v: optional fp32 [Hkv, 2] (lo, step) of an equally spaced codebook per KV head."""
     if k_src.dim() != 4 or k_src.shape != v_src.shape or k_src.stride() != v_src.stride():
         raise TypeError("k_src / v_src must be [B, n, Hkv, 128] with identical strides")
     if k_src.stride(3) != 1 or k_src.shape[3] != HEAD_DIM or k_src.shape[2] != lay.num_kv_heads:
@@ -199,14 +207,16 @@ def demote(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, u_k: torch
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(u_k, "u_k", torch.float32),
         _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
-        _contig(clip_v, "clip_v", torch.float32), _dev(k_src, "k_src", torch.bfloat16),
+        _contig(clip_v, "clip_v", torch.float32), _levels(levels_k, "levels_k", lay),
+        _levels(levels_v, "levels_v", lay), _dev(k_src, "k_src", torch.bfloat16),
         _dev(v_src, "v_src", torch.bfloat16), k_src.stride(0), k_src.stride(1), k_src.stride(2),
         _contig(hist_start, "hist_start", torch.int32), bsz, n, _stream()), "demote")
 
 
 def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_k,
            clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot: torch.Tensor,
-           seq_lens: torch.Tensor) -> None:
+           seq_lens: torch.Tensor, levels_k: Optional[torch.Tensor] = None,
+           levels_v: Optional[torch.Tensor] = None) -> None:
     """Decode-step write of k_new / v_new (bf16 [B, Hkv, 128]) at positions seq_lens[b]
     (oscar_append); the caller advances seq_lens afterwards."""
     bsz = seq_lens.numel()
@@ -218,7 +228,8 @@ def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_
         _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
         _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
         _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
-        _contig(clip_v, "clip_v", torch.float32), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(clip_v, "clip_v", torch.float32), _levels(levels_k, "levels_k", lay),
+        _levels(levels_v, "levels_v", lay), _contig(k_new, "k_new", torch.bfloat16),
         _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
         _contig(seq_lens, "seq_lens", torch.int32), bsz, _stream()), "append")
 
@@ -249,7 +260,9 @@ def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
 def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
                 clip_k, clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot, seq_pos,
                 q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
-                lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0) -> None:
+                lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0,
+                levels_k: Optional[torch.Tensor] = None,
+                levels_v: Optional[torch.Tensor] = None) -> None:
     """append(k_new, v_new at seq_pos) then decode_attn(q) over seq_pos + 1 tokens, in three
     launches (oscar_decode_step); the caller advances seq_pos afterwards."""
     bsz = seq_pos.numel()
@@ -263,7 +276,8 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
         _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
         _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
-        _contig(clip_v, "clip_v", torch.float32), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(clip_v, "clip_v", torch.float32), _levels(levels_k, "levels_k", lay),
+        _levels(levels_v, "levels_v", lay), _contig(k_new, "k_new", torch.bfloat16),
         _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
         _contig(seq_pos, "seq_pos", torch.int32), _contig(q, "q", torch.bfloat16),
         float(sm_scale), _contig(out, "out", torch.float32),

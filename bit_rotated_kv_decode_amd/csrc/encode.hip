@@ -67,6 +67,9 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 
   const float* u = (tensor == 0 ? a.u_k : a.u_v) + static_cast<int64_t>(h) * kHeadDim * kHeadDim;
   const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+  const float* lvp = tensor == 0 ? a.levels_k : a.levels_v;
+  const float lv_lo = lvp ? lvp[2 * h] : 0.0f;
+  const float lv_step = lvp ? lvp[2 * h + 1] : 1.0f;
   double r[kRun][2];
   dev::rotate_fp64<kRun>(x, u, r);
 
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
   uint32_t vword0 = 0, vword1 = 0, vmask = 0;
 #pragma unroll
   for (int t = 0; t < kRun; ++t) {
-    const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups);
+    const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups, lv_lo, lv_step);
     const int idx = first + t;
     if (idx < lo || idx >= hi) continue;
     if (tensor == 0) {
@@ -158,12 +161,15 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
   uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, idx, a.hkv, h,
                             block_bytes(a.n_groups));
   const float clip = (tensor == 0 ? a.clip_k : a.clip_v)[h];
+  const float* lvp = tensor == 0 ? a.levels_k : a.levels_v;
+  const float lv_lo = lvp ? lvp[2 * h] : 0.0f;
+  const float lv_step = lvp ? lvp[2 * h + 1] : 1.0f;
   if (tid < kHeadDim) x[tid] = dev::bf16_to_f32(ring[tid]);
   __syncthreads();   // the old row is staged: waves 2 and 3 may overwrite it
   if (tid >= 128) ring[tid - 128] = nv;
   double r0, r1;
   if (dev::rotate1_block(x, ur, red, r0, r1)) {
-    const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups);
+    const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups, lv_lo, lv_step);
     store_token(blk, tensor, idx % kPage, a.n_groups, q);
   }
 }

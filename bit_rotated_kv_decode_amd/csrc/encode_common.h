@@ -18,9 +18,14 @@ struct LaneCodes {
 };
 
 // Clip and quantise the rotated channels (lane, lane + 64) of one vector; all lanes of the wave
-// must call this together (the group min / max are wave reductions).
+// must call this together (the group min / max are wave reductions).  (lv_lo, lv_step) places the
+// four levels of an equally spaced codebook at lv_lo + lv_step * c in units of (max - min) / 3
+// above the group minimum: the stored scale is (max - min) / 3 * lv_step and the zero point
+// min + (max - min) / 3 * lv_lo, every product and sum rounded to fp32 on its own; (0, 1) is the
+// plain grid (scale (max - min) / 3, zero point min).
 __device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float clip,
-                                                   int n_groups) {
+                                                   int n_groups, float lv_lo, float lv_step) {
+#pragma clang fp contract(off)
   float x0 = static_cast<float>(r0);
   float x1 = static_cast<float>(r1);
   x0 = fminf(fmaxf(x0, -clip), clip);
@@ -40,9 +45,11 @@ __device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float c
   float sf[2], zf[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float s32 = (mx[m] - mn[m]) / 3.0f;
+    const float r3 = (mx[m] - mn[m]) / 3.0f;
+    const float s32 = lv_step == 1.0f ? r3 : r3 * lv_step;
+    const float z32 = lv_lo == 0.0f ? mn[m] : mn[m] + r3 * lv_lo;
     const __half s16 = __float2half_rn(s32);
-    const __half z16 = __float2half_rn(mn[m]);
+    const __half z16 = __float2half_rn(z32);
     sf[m] = __half2float(s16);
     zf[m] = __half2float(z16);
     out.meta[m] = static_cast<uint32_t>(__half_as_ushort(s16)) |

@@ -133,9 +133,9 @@ namespace {
 oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* page_table,
                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                               const float* u_k, const float* u_v, const float* clip_k,
-                              const float* clip_v, const void* k_new, const void* v_new,
-                              const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
-                              oscar::AppendArgs& a) {
+                              const float* clip_v, const float* levels_k, const float* levels_v,
+                              const void* k_new, const void* v_new, const int32_t* seq_slot,
+                              const int32_t* seq_lens, int32_t batch, oscar::AppendArgs& a) {
   oscar_status st = check_layout(l);
   if (st != OSCAR_OK) return st;
   if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
@@ -148,8 +148,9 @@ oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* 
       !aligned(recent_k, 16) || !aligned(recent_v, 16))
     return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
   if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
-      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(seq_slot, 4) ||
-      !aligned(seq_lens, 4) || !aligned(page_table, 4))
+      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(levels_k, 4) ||
+      !aligned(levels_v, 4) || !aligned(seq_slot, 4) || !aligned(seq_lens, 4) ||
+      !aligned(page_table, 4))
     return fail(OSCAR_ERR_ALIGN, "append: misaligned pointer");
   a.pool = static_cast<uint8_t*>(pool);
   a.page_table = page_table;
@@ -164,6 +165,8 @@ oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* 
   a.u_v = u_v;
   a.clip_k = clip_k;
   a.clip_v = clip_v;
+  a.levels_k = levels_k;
+  a.levels_v = levels_v;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.seq_slot = seq_slot;
@@ -335,7 +338,8 @@ oscar_status oscar_check_page_table(const oscar_layout* l, const int32_t* table,
 
 oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page_table,
                           const float* u_k, const float* u_v, const float* clip_k,
-                          const float* clip_v, const void* k_src, const void* v_src,
+                          const float* clip_v, const float* levels_k, const float* levels_v,
+                          const void* k_src, const void* v_src,
                           int64_t stride_b, int64_t stride_t, int64_t stride_h,
                           const int32_t* hist_start, int32_t batch, int32_t n_tokens,
                           void* stream) {
@@ -350,8 +354,8 @@ oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page
     return fail(OSCAR_ERR_RANGE, "negative source stride");
   if (!aligned(pool, 16)) return fail(OSCAR_ERR_ALIGN, "pool must be 16-byte aligned");
   if (!aligned(k_src, 2) || !aligned(v_src, 2) || !aligned(u_k, 4) || !aligned(u_v, 4) ||
-      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(page_table, 4) ||
-      !aligned(hist_start, 4))
+      !aligned(clip_k, 4) || !aligned(clip_v, 4) || !aligned(levels_k, 4) ||
+      !aligned(levels_v, 4) || !aligned(page_table, 4) || !aligned(hist_start, 4))
     return fail(OSCAR_ERR_ALIGN, "oscar_demote: misaligned pointer");
   oscar::DemoteArgs a;
   a.pool = static_cast<uint8_t*>(pool);
@@ -363,6 +367,8 @@ oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page
   a.u_v = u_v;
   a.clip_k = clip_k;
   a.clip_v = clip_v;
+  a.levels_k = levels_k;
+  a.levels_v = levels_v;
   a.k_src = static_cast<const uint16_t*>(k_src);
   a.v_src = static_cast<const uint16_t*>(v_src);
   a.stride_b = stride_b;
@@ -377,13 +383,13 @@ oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page
 oscar_status oscar_append(const oscar_layout* l, void* pool, const int32_t* page_table,
                           void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                           const float* u_k, const float* u_v, const float* clip_k,
-                          const float* clip_v, const void* k_new, const void* v_new,
-                          const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
-                          void* stream) {
+                          const float* clip_v, const float* levels_k, const float* levels_v,
+                          const void* k_new, const void* v_new, const int32_t* seq_slot,
+                          const int32_t* seq_lens, int32_t batch, void* stream) {
   oscar::AppendArgs a;
   const oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
-                                           u_k, u_v, clip_k, clip_v, k_new, v_new, seq_slot,
-                                           seq_lens, batch, a);
+                                           u_k, u_v, clip_k, clip_v, levels_k, levels_v,
+                                           k_new, v_new, seq_slot, seq_lens, batch, a);
   if (st != OSCAR_OK || batch == 0) return st;
   return hip_status(oscar::launch_prep(&a, nullptr, static_cast<hipStream_t>(stream)),
                     "oscar_append");
@@ -430,15 +436,16 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
 oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t* page_table,
                                void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                                const float* u_k, const float* u_v, const float* clip_k,
-                               const float* clip_v, const void* k_new, const void* v_new,
+                               const float* clip_v, const float* levels_k,
+                               const float* levels_v, const void* k_new, const void* v_new,
                                const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
                                float sm_scale, float* out, float* lse, void* workspace,
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                                void* stream) {
   oscar::AppendArgs ap;
   oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
-                                     u_k, u_v, clip_k, clip_v, k_new, v_new, seq_slot, seq_pos,
-                                     batch, ap);
+                                     u_k, u_v, clip_k, clip_v, levels_k, levels_v, k_new, v_new,
+                                     seq_slot, seq_pos, batch, ap);
   if (st != OSCAR_OK) return st;
   oscar::DecodeArgs a;
   oscar::QueryArgs qa;

@@ -67,6 +67,8 @@ struct DemoteArgs {
   const float* u_v;
   const float* clip_k;
   const float* clip_v;
+  const float* levels_k;   // [hkv][2] (lo, step) of an equally spaced codebook, or NULL
+  const float* levels_v;
   const uint16_t* k_src;
   const uint16_t* v_src;
   int64_t stride_b, stride_t, stride_h;
@@ -89,6 +91,8 @@ struct AppendArgs {
   const float* u_v;
   const float* clip_k;
   const float* clip_v;
+  const float* levels_k;   // [hkv][2] (lo, step) of an equally spaced codebook, or NULL
+  const float* levels_v;
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int32_t* seq_slot;

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 3u
+#define OSCAR_ABI_VERSION 4u
 
 typedef int32_t oscar_status;
 
@@ -146,11 +146,20 @@ oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* h
  * hist_start[b] + i of sequence b:
  *   1. x' = x U H P / sqrt(d) computed in fp64, then rounded to fp32;
  *   2. x'' = min(max(x', -clip), clip)  (fp32);
- *   3. per group m of g rotated channels: mn = min, mx = max; scale = fp16((mx - mn) / 3),
- *      zero = fp16(mn) (fp32 arithmetic, round-to-nearest-even);
+ *   3. per group m of g rotated channels: mn = min, mx = max, r = (mx - mn) / 3;
+ *      scale = fp16(r * step), zero = fp16(mn + r * lo) (fp32 arithmetic, each product and sum
+ *      rounded on its own, round-to-nearest-even); (lo, step) = (0, 1), i.e. scale = fp16(r) and
+ *      zero = fp16(mn), unless levels_k / levels_v give them;
  *   4. code_j = min(max(rint((x''_j - zero) / scale), 0), 3) in fp32 with ties to even, or 0 for
  *      every j of a group whose fp16 scale is 0;
  *   5. codes and meta are stored in the block layout described above.
+ * levels_k / levels_v: NULL for the plain grid (lo, step) = (0, 1), or device fp32 [num_kv_heads][2] =
+ * (lo, step) per KV head, 4-byte aligned: an equally spaced codebook whose four levels sit at
+ * lo + step * c in units of (mx - mn) / 3 above the group minimum -- the Lloyd-Max codebook that
+ * OSCAR's newer code pairs with its rotation ([W3], closing comparison with TurboQuant), held to
+ * equal spacing so that decoding stays scale * code + zero and the attention kernels are
+ * unchanged.  lo and step must be finite, step > 0 (the library does not read device memory to
+ * check); fitted values lie near lo = 0.5, step = 2/3.
  * pool: oscar_pool_bytes(layout) bytes, 16-byte aligned.  page_table: int32
  * [batch][max_pages_per_seq].  U_k / U_v / clip_k / clip_v as described above.  hist_start:
  * int32 [batch].  Strides are in bf16 elements, >= 0; k_src / v_src 2-byte aligned.  The call
@@ -158,7 +167,8 @@ oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* h
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE (negative batch or n_tokens) / HIP. */
 oscar_status oscar_demote(const oscar_layout* layout, void* pool, const int32_t* page_table,
                           const float* u_k, const float* u_v, const float* clip_k,
-                          const float* clip_v, const void* k_src, const void* v_src,
+                          const float* clip_v, const float* levels_k, const float* levels_v,
+                          const void* k_src, const void* v_src,
                           int64_t stride_b, int64_t stride_t, int64_t stride_h,
                           const int32_t* hist_start, int32_t batch, int32_t n_tokens,
                           void* stream);
@@ -171,14 +181,15 @@ oscar_status oscar_demote(const oscar_layout* layout, void* pool, const int32_t*
  * sink row P of slot s.  Otherwise they go to recent ring row P % 256 of slot s, and when
  * P >= 320 the token held in that row (position P - 256) is first demoted (as oscar_demote) to
  * history index P - 320.  The caller advances seq_lens afterwards.  sink / recent arrays as in
- * the layout above; seq_slot, seq_lens int32 [batch] device arrays.
+ * the layout above; seq_slot, seq_lens int32 [batch] device arrays; levels_k / levels_v as for
+ * oscar_demote.
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / HIP. */
 oscar_status oscar_append(const oscar_layout* layout, void* pool, const int32_t* page_table,
                           void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                           const float* u_k, const float* u_v, const float* clip_k,
-                          const float* clip_v, const void* k_new, const void* v_new,
-                          const int32_t* seq_slot, const int32_t* seq_lens, int32_t batch,
-                          void* stream);
+                          const float* clip_v, const float* levels_k, const float* levels_v,
+                          const void* k_new, const void* v_new, const int32_t* seq_slot,
+                          const int32_t* seq_lens, int32_t batch, void* stream);
 
 /* Decode attention over the three-segment cache ([W1] OSCAR 的设计: INT2 unpack and
  * scale / zero-point dequantisation with float accumulation, a BF16 sink / recent pass, an
@@ -238,7 +249,8 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* layout, const void* po
 oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int32_t* page_table,
                                void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                                const float* u_k, const float* u_v, const float* clip_k,
-                               const float* clip_v, const void* k_new, const void* v_new,
+                               const float* clip_v, const float* levels_k,
+                               const float* levels_v, const void* k_new, const void* v_new,
                                const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
                                float sm_scale, float* out, float* lse, void* workspace,
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,

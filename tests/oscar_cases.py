@@ -32,7 +32,8 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
 class Case:
     """Inputs of one layer: token K/V per sequence (bf16, host), queries, U, clip, page table."""
 
-    def __init__(self, wl, lengths=None, layer=0, spare=0, u=None, clip=None, device_tokens=None):
+    def __init__(self, wl, lengths=None, layer=0, spare=0, u=None, clip=None, device_tokens=None,
+                 levels=None):
         self.wl = wl
         self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
         self.batch = len(self.lengths)
@@ -46,6 +47,9 @@ class Case:
         if clip is None:
             clip = (np.full(hkv, wl.clip, np.float32), np.full(hkv, wl.clip, np.float32))
         self.clip_k, self.clip_v = (np.asarray(c, np.float32) for c in clip)
+        # optional equally spaced codebooks: (lo, step) per KV head for keys and for values
+        self.levels_k, self.levels_v = ((None, None) if levels is None else
+                                        (np.asarray(lv, np.float32) for lv in levels))
         dev = device_tokens or "cpu"
         self.k, self.v = [], []
         for b, L in enumerate(self.lengths):
@@ -85,14 +89,19 @@ class Case:
             if heads is not None:
                 for h in heads:
                     kq = oracle.encode(k[0, :, h], self.u_k[h].numpy(), self.clip_k[h],
-                                       self.geom.group)[:3]
+                                       self.geom.group, self.head_levels("k", h))[:3]
                     vq = oracle.encode(v[0, :, h], self.u_v[h].numpy(), self.clip_v[h],
-                                       self.geom.group)[:3]
+                                       self.geom.group, self.head_levels("v", h))[:3]
                     oracle.store_history(pool, self.table[b], np.arange(n), h, kq, vq, self.geom)
             else:
                 oracle.demote(pool, self.table[b:b + 1], self.u_k.numpy(), self.u_v.numpy(),
-                              self.clip_k, self.clip_v, k, v, [0], self.geom)
+                              self.clip_k, self.clip_v, k, v, [0], self.geom, self.levels_k,
+                              self.levels_v)
         return pool
+
+    def head_levels(self, tensor, h):
+        lv = self.levels_k if tensor == "k" else self.levels_v
+        return None if lv is None else lv[h]
 
     def oracle_attention(self, pool, heads=None):
         sk, sv, rk, rv = self.oracle_segments()
@@ -109,7 +118,9 @@ class Case:
                  clip_v=torch.from_numpy(self.clip_v).to(dev),
                  q=self.q.to(dev).contiguous(),
                  lens=torch.tensor(self.lengths, dtype=torch.int32, device=dev),
-                 slots=torch.arange(self.batch, dtype=torch.int32, device=dev))
+                 slots=torch.arange(self.batch, dtype=torch.int32, device=dev),
+                 levels_k=None if self.levels_k is None else torch.from_numpy(self.levels_k).to(dev),
+                 levels_v=None if self.levels_v is None else torch.from_numpy(self.levels_v).to(dev))
         return g
 
     def gpu_cache(self, g, pool_from_oracle=None):
@@ -135,7 +146,8 @@ class Case:
                 k = self.k[b].to("cuda")[64:64 + n].unsqueeze(0)
                 v = self.v[b].to("cuda")[64:64 + n].unsqueeze(0)
                 ok.demote(self.layout, cache.pool, g["table"][b:b + 1], g["u_k"], g["u_v"],
-                          g["clip_k"], g["clip_v"], k, v, zero)
+                          g["clip_k"], g["clip_v"], k, v, zero, levels_k=g["levels_k"],
+                          levels_v=g["levels_v"])
         return cache
 
     def gpu_attention(self, g, cache, max_seq_len=None, with_lse=True):
@@ -216,19 +228,20 @@ def compare_pool_blocks(gpu: np.ndarray, ref: np.ndarray, case: Case, heads=None
         page = int(case.table[b, t // g.page])
         blk_g = gpu[page][head_ids.index(h)]
         blk_r = ref[page][head_ids.index(h)]
+        lv = case.head_levels(tensor, h)
         rc, _, _ = _token(blk_r, t % g.page, tensor, g)
-        assert np.array_equal(rc, oracle.encode(x, u, c, g.group)[0][0]), \
+        assert np.array_equal(rc, oracle.encode(x, u, c, g.group, lv)[0][0]), \
             "oracle pool and oracle encode disagree"
-        flips += check_token(blk_g, t % g.page, tensor, x, u, c, g, (b, t, h, tensor))
+        flips += check_token(blk_g, t % g.page, tensor, x, u, c, g, (b, t, h, tensor), lv)
     assert flips <= MAX_FLIP_FRACTION * total_codes, (flips, total_codes)
     return flips
 
 
-def check_token(blk, slot, tensor, x, u, c, g, where=None):
+def check_token(blk, slot, tensor, x, u, c, g, where=None, levels=None):
     """Check one token's bytes in a GPU-written block against the oracle's encoding of x (fp32
-    [1, d] of the bf16 token) under the acceptance rule; returns the number of codes that differ
-    (all of them inside the rounding window)."""
-    codes, s16, z16, pre = oracle.encode(x, u, c, g.group)
+    [1, d] of the bf16 token; ``levels`` the head's (lo, step) or None) under the acceptance rule;
+    returns the number of codes that differ (all of them inside the rounding window)."""
+    codes, s16, z16, pre = oracle.encode(x, u, c, g.group, levels)
     gc, gs, gz = _token(blk, slot, tensor, g)
     flips = 0
     for m in range(g.n_groups):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 3
+    assert lib.oscar_abi_version() == 4
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -131,11 +131,13 @@ def test_bf16_validation_happens_before_launch():
 
 def _call_demote(lay, **over):
     a = dict(pool=4096, page_table=4096, u_k=4096, u_v=4096, clip_k=4096, clip_v=4096,
-             k_src=4096, v_src=4096, sb=0, st=0, sh=0, hist=4096, batch=1, n=1)
+             lv_k=None, lv_v=None, k_src=4096, v_src=4096, sb=0, st=0, sh=0, hist=4096, batch=1,
+             n=1)
     a.update(over)
     return ok.lib().oscar_demote(ctypes.byref(lay), a["pool"], a["page_table"], a["u_k"],
-                                 a["u_v"], a["clip_k"], a["clip_v"], a["k_src"], a["v_src"],
-                                 a["sb"], a["st"], a["sh"], a["hist"], a["batch"], a["n"], None)
+                                 a["u_v"], a["clip_k"], a["clip_v"], a["lv_k"], a["lv_v"],
+                                 a["k_src"], a["v_src"], a["sb"], a["st"], a["sh"], a["hist"],
+                                 a["batch"], a["n"], None)
 
 
 def test_demote_validation_happens_before_launch():
@@ -147,6 +149,10 @@ def test_demote_validation_happens_before_launch():
     assert _call_demote(lay, batch=-1) == -4
     assert _call_demote(lay, st=-2) == -4
     assert _call_demote(_lay(group_size=16)) == -2
+    # the codebook levels are optional; given, they must be 4-byte aligned
+    assert _call_demote(lay, lv_k=4098, pool=None) == -1
+    assert _call_demote(lay, lv_k=4098) == -3
+    assert _call_demote(lay, lv_v=4097) == -3
     # nothing to do: OK without touching any pointer
     assert _call_demote(lay, pool=None, n=0) == 0
     assert _call_demote(lay, pool=None, batch=0) == 0
@@ -188,22 +194,26 @@ def test_decode_validation_happens_before_launch():
 def test_append_validation_happens_before_launch():
     lay = _lay()
     f = ok.lib().oscar_append
-    args = [4096] * 14
+    args = [4096] * 16
+    args[10] = args[11] = None   # levels_k, levels_v: optional
     assert f(ctypes.byref(lay), *([None] + args[1:]), 1, None) == -1
     assert f(ctypes.byref(lay), *([4096 + 4] + args[1:]), 1, None) == -3
     assert f(ctypes.byref(_lay(max_seqs=0)), *args, 1, None) == -2
     assert f(ctypes.byref(lay), *args, -1, None) == -4
+    bad = list(args)
+    bad[11] = 4096 + 2
+    assert f(ctypes.byref(lay), *bad, 1, None) == -3
 
 
 def _call_step(lay, **over):
     a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, uk=4096, uv=4096, ck=4096,
-             cv=4096, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, out=4096, lse=None, ws=4096,
-             wsb=1 << 30, batch=1, maxlen=600)
+             cv=4096, lk=None, lv=None, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, out=4096,
+             lse=None, ws=4096, wsb=1 << 30, batch=1, maxlen=600)
     a.update(over)
     return ok.lib().oscar_decode_step(
         ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
-        a["uv"], a["ck"], a["cv"], a["kn"], a["vn"], a["slot"], a["pos"], a["q"], 0.0, a["out"],
-        a["lse"], a["ws"], a["wsb"], a["batch"], a["maxlen"], None)
+        a["uv"], a["ck"], a["cv"], a["lk"], a["lv"], a["kn"], a["vn"], a["slot"], a["pos"],
+        a["q"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"], a["batch"], a["maxlen"], None)
 
 
 def test_step_validation_happens_before_launch():
@@ -211,6 +221,7 @@ def test_step_validation_happens_before_launch():
     # an append argument or a decode argument may fail; either way nothing is launched
     assert _call_step(lay, kn=None) == -1
     assert _call_step(lay, ck=4096 + 2) == -3
+    assert _call_step(lay, lk=4096 + 2) == -3
     assert _call_step(_lay(max_seqs=0)) == -2
     assert _call_step(lay, q=None) == -1
     assert _call_step(lay, ws=None) == -5
