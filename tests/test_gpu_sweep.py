@@ -4,12 +4,15 @@ Each draw picks a batch (1-4), a GQA width (1, 2, 4, 8), a group size (64, 128),
 KV heads (1-2) and per-sequence lengths clustered around the places where the work changes shape
 (the sink and recent boundaries at 64 and 320, page boundaries, 16-slot word boundaries); the
 INT2 path (the GPU reads the oracle's pool bytes; attention within 2e-3 max row error, LSE within
-1e-3) and the BF16 baseline (GPU store and attention) are both checked on the same draws."""
+1e-3) and the BF16 baseline (GPU store and attention) are both checked on the same draws.  Odd
+draws also give every KV head an equally spaced codebook (lo, step) and check the GPU's own
+demotion against the oracle's pool bytes."""
 import numpy as np
 import pytest
+import torch
 
 import workloads
-from oscar_cases import ATTN_TOL, Case, attention_error
+from oscar_cases import ATTN_TOL, Case, attention_error, compare_pool_blocks
 from bf16_cases import Bf16Case, check_bf16
 
 pytestmark = pytest.mark.gpu
@@ -29,17 +32,25 @@ def _draw(seed):
         lengths.append(max(1, base + int(rng.integers(-2, 3)) + 64 * int(rng.integers(0, 20))))
     wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=gqa * hkv,
                           num_kv_heads=hkv, group_size=group, seed=100 + seed)
-    return wl, lengths
+    levels = None
+    if seed % 2:
+        levels = tuple(np.stack([rng.uniform(0.2, 0.8, hkv), rng.uniform(0.5, 1.0, hkv)],
+                                -1).astype(np.float32) for _ in range(2))
+    return wl, lengths, levels
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_sweep_int2_and_bf16(seed):
-    wl, lengths = _draw(seed)
-    print(f"sweep {seed}: G={wl.gqa} Hkv={wl.num_kv_heads} g={wl.group_size} lengths={lengths}",
-          flush=True)
-    case = Case(wl, lengths)
+    wl, lengths, levels = _draw(seed)
+    print(f"sweep {seed}: G={wl.gqa} Hkv={wl.num_kv_heads} g={wl.group_size} lengths={lengths} "
+          f"levels={None if levels is None else [lv.tolist() for lv in levels]}", flush=True)
+    case = Case(wl, lengths, levels=levels)
     pool = case.oracle_pool()
     g = case.gpu_inputs()
+    if levels is not None:
+        own = case.gpu_cache(g)
+        torch.cuda.synchronize()
+        compare_pool_blocks(own.pool.cpu().numpy(), pool, case)
     cache = case.gpu_cache(g, pool_from_oracle=pool)
     out, lse = case.gpu_attention(g, cache)
     ref, ref_lse = case.oracle_attention(pool)
