@@ -727,11 +727,12 @@ __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kerne
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. merge: kMergeParts 256-thread blocks per (sequence, query head); block part q produces output
-// channels [32 q, 32 q + 32).  Each block combines all INT2 splits of its row (the rotated-frame
-// vector is needed whole for the Hadamard transform) but reads only its 32 rows of U_v, so the
-// per-block load volume is about half of one block doing the whole row, spread over four times
-// as many compute units.  Every global load is issued before the first reduction and none waits
+// 4. merge: four 256-thread blocks per (sequence, query head) row, block q producing output
+// channels [32 q, 32 q + 32) -- or, in launches of at least kMergeRowsOneBlock rows, one block per
+// row that produces the four quarters in turn.  Each block combines all INT2 splits of its row
+// (the rotated-frame vector is needed whole for the Hadamard transform); a quarter block reads
+// only its 32 rows of U_v, so its load volume is about half of one block doing the whole row,
+// spread over four times as many compute units.  Every global load is issued before the first reduction and none waits
 // on the sequence length (entries of splits the sequence does not reach are read but masked).
 //   (1) thread (channel quad, split residue r mod 8) merges its own splits r, r + 8, ... into a
 //       local (m, l, acc') with a local maximum;
@@ -740,15 +741,21 @@ __global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kerne
 //   (3) times U_v^T: eight threads per output channel, 16 inputs each, summed across the lanes;
 //   (4) merge with the BF16 chunk partials and normalise.
 constexpr int kMergePrefetch = 12;   // splits per thread loaded up front (96 splits per row)
-constexpr int kMergeParts = 4;       // blocks per (sequence, query head)
-constexpr int kMergeCols = kHeadDim / kMergeParts;
+constexpr int kMergeQuarters = 4;    // output-channel quarters of a row (32 channels each)
+constexpr int kMergeCols = kHeadDim / kMergeQuarters;
+// Rows (sequence, query head) from which a launch gives each row one block that takes all four
+// quarters instead of one block per quarter: with enough rows to fill the chip, fewer blocks
+// repeat less of the per-row work (the split loads and merges of steps 1 and 2).
+constexpr int kMergeRowsOneBlock = 512;
 
+template <int PARTS>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ __attribute__((aligned(16))) float part[8][kHeadDim];
   __shared__ float part_m[8], part_l[8];
   __shared__ __attribute__((aligned(16))) float vec[kHeadDim];
-  const int row = blockIdx.x / kMergeParts;   // b * hq + head
-  const int q = blockIdx.x % kMergeParts;
+  static_assert(PARTS == 1 || PARTS == kMergeQuarters, "one block per row or per quarter");
+  const int row = blockIdx.x / PARTS;   // b * hq + head
+  const int q0 = blockIdx.x % PARTS;    // first quarter of this block
   const int b = row / p.hq;
   const int kv = (row % p.hq) / p.gqa;
   const int tid = threadIdx.x;
@@ -763,7 +770,6 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
                       static_cast<int64_t>(row) * kBf16Chunks * kHeadDim;
   const int cq = tid & 31, sr = tid >> 5;     // (1): channel quad, split residue
   const int jl = tid >> 3, ip = tid & 7;      // (3): output channel 32 q + jl, input part
-  const int j = kMergeCols * q + jl;
 
   // ---- loads
   float2 st[kMergePrefetch];
@@ -776,19 +782,22 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     pa[i] = in ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float4 uv[4];   // U_v[kv][j][16 ip .. 16 ip + 15]
-  {
+  float4 uv[4];   // U_v[kv][j][16 ip .. 16 ip + 15] of the current quarter's channel j
+  float ba[kBf16Chunks];
+  auto load_quarter = [&](int j) {
     const float4* u = reinterpret_cast<const float4*>(
         a.u_v + (static_cast<int64_t>(kv) * kHeadDim + j) * kHeadDim + 16 * ip);
 #pragma unroll
     for (int c = 0; c < 4; ++c) uv[c] = u[c];
-  }
-  float bm[kBf16Chunks], bl[kBf16Chunks], ba[kBf16Chunks];
+#pragma unroll
+    for (int c = 0; c < kBf16Chunks; ++c) ba[c] = ip == 0 ? bacc[c * kHeadDim + j] : 0.f;
+  };
+  load_quarter(kMergeCols * q0 + jl);
+  float bm[kBf16Chunks], bl[kBf16Chunks];
 #pragma unroll
   for (int c = 0; c < kBf16Chunks; ++c) {
     bm[c] = bml[2 * c];
     bl[c] = bml[2 * c + 1];
-    ba[c] = ip == 0 ? bacc[c * kHeadDim + j] : 0.f;
   }
   const int L = a.seq_lens[b] + a.len_add;
   const int n_hist = max(0, L - kSink - kRecent);
@@ -887,45 +896,49 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   }
   __syncthreads();
   const float mi = part_m[0], li = part_l[0];
-  float o = 0.f;
-  {
-    const float4 v4[4] = {reinterpret_cast<const float4*>(vec)[4 * ip],
-                          reinterpret_cast<const float4*>(vec)[4 * ip + 1],
-                          reinterpret_cast<const float4*>(vec)[4 * ip + 2],
-                          reinterpret_cast<const float4*>(vec)[4 * ip + 3]};
+  for (int qq = 0; qq < kMergeQuarters / PARTS; ++qq) {
+    const int j = kMergeCols * (q0 + qq) + jl;
+    if (qq > 0) load_quarter(j);
+    float o = 0.f;
+    {
+      const float4 v4[4] = {reinterpret_cast<const float4*>(vec)[4 * ip],
+                            reinterpret_cast<const float4*>(vec)[4 * ip + 1],
+                            reinterpret_cast<const float4*>(vec)[4 * ip + 2],
+                            reinterpret_cast<const float4*>(vec)[4 * ip + 3]};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      o = fmaf(v4[c].x, uv[c].x, o);
-      o = fmaf(v4[c].y, uv[c].y, o);
-      o = fmaf(v4[c].z, uv[c].z, o);
-      o = fmaf(v4[c].w, uv[c].w, o);
+      for (int c = 0; c < 4; ++c) {
+        o = fmaf(v4[c].x, uv[c].x, o);
+        o = fmaf(v4[c].y, uv[c].y, o);
+        o = fmaf(v4[c].z, uv[c].z, o);
+        o = fmaf(v4[c].w, uv[c].w, o);
+      }
+      // sum over the eight input parts (lanes 8 jl .. 8 jl + 7 of the wave)
+      o += dev::lane_xor_dpp<1>(o);
+      o += dev::lane_xor_dpp<2>(o);
+      o += dev::lane_xor_dpp<4>(o);
     }
-    // sum over the eight input parts (lanes 8 jl .. 8 jl + 7 of the wave)
-    o += dev::lane_xor_dpp<1>(o);
-    o += dev::lane_xor_dpp<2>(o);
-    o += dev::lane_xor_dpp<4>(o);
-  }
-  // ---- (4) merge with the BF16 partials
-  if (ip == 0) {
-    const float m_int2 = n_valid > 0 ? mi : -INFINITY;
-    float mt = m_int2;
+    // ---- (4) merge with the BF16 partials
+    if (ip == 0) {
+      const float m_int2 = n_valid > 0 ? mi : -INFINITY;
+      float mt = m_int2;
 #pragma unroll
-    for (int c = 0; c < kBf16Chunks; ++c) mt = fmaxf(mt, bm[c]);
-    float acc = 0.f, l = 0.f;
-    if (m_int2 != -INFINITY) {
-      const float f = exp2f(m_int2 - mt);
-      acc = o * 0.08838834764831845f * f;
-      l = li * f;
-    }
+      for (int c = 0; c < kBf16Chunks; ++c) mt = fmaxf(mt, bm[c]);
+      float acc = 0.f, l = 0.f;
+      if (m_int2 != -INFINITY) {
+        const float f = exp2f(m_int2 - mt);
+        acc = o * 0.08838834764831845f * f;
+        l = li * f;
+      }
 #pragma unroll
-    for (int c = 0; c < kBf16Chunks; ++c) {
-      if (bm[c] == -INFINITY) continue;
-      const float f = exp2f(bm[c] - mt);
-      acc = fmaf(ba[c], f, acc);
-      l = fmaf(bl[c], f, l);
+      for (int c = 0; c < kBf16Chunks; ++c) {
+        if (bm[c] == -INFINITY) continue;
+        const float f = exp2f(bm[c] - mt);
+        acc = fmaf(ba[c], f, acc);
+        l = fmaf(bl[c], f, l);
+      }
+      a.out[static_cast<int64_t>(row) * kHeadDim + j] = acc / l;
+      if (a.lse != nullptr && j == 0) a.lse[row] = (mt + log2f(l)) * 0.6931471805599453f;
     }
-    a.out[static_cast<int64_t>(row) * kHeadDim + j] = acc / l;
-    if (a.lse != nullptr && j == 0) a.lse[row] = (mt + log2f(l)) * 0.6931471805599453f;
   }
 }
 
@@ -950,9 +963,14 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
       hipLaunchKernelGGL((attn_kernel<G, 2, false>), grid, dim3(256), 0, stream, a, p, scale_log2,
                          x0);
   }
-  if (stages & OSCAR_STAGE_MERGE)
-    hipLaunchKernelGGL(merge_kernel, dim3(p.batch * p.hq * kMergeParts), dim3(256), 0, stream, a,
-                       p);
+  if (stages & OSCAR_STAGE_MERGE) {
+    const int rows = p.batch * p.hq;
+    if (rows >= kMergeRowsOneBlock)
+      hipLaunchKernelGGL(merge_kernel<1>, dim3(rows), dim3(256), 0, stream, a, p);
+    else
+      hipLaunchKernelGGL(merge_kernel<kMergeQuarters>, dim3(rows * kMergeQuarters), dim3(256), 0,
+                         stream, a, p);
+  }
   return hipGetLastError();
 }
 

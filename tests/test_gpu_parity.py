@@ -101,6 +101,25 @@ def test_attention_on_oracle_pool(name):
     assert np.max(np.abs(lse - ref_lse)) <= 1e-3
 
 
+def test_attention_many_rows_one_merge_block_per_row():
+    # 64 sequences x 8 query heads = 512 rows: the merge takes one block per row (all four
+    # output quarters) instead of one block per quarter; ragged lengths, some with no history
+    wl = _tiny(num_q_heads=8, num_kv_heads=2)
+    lengths = [int(x) for x in np.random.default_rng(3).integers(1, 1400, 64)]
+    lengths[:4] = [1, 320, 321, 1399]
+    case = Case(wl, lengths)
+    _note(f"attention 512 rows: lengths {min(lengths)}..{max(lengths)}")
+    pool = case.oracle_pool()
+    g = case.gpu_inputs()
+    cache = case.gpu_cache(g, pool_from_oracle=pool)
+    out, lse = case.gpu_attention(g, cache)
+    ref, ref_lse = case.oracle_attention(pool)
+    err = attention_error(out, ref)
+    _note(f"max row error {err:.3e}")
+    assert err <= ATTN_TOL
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-3
+
+
 def test_attention_end_to_end_tiny():
     case = Case(_tiny())
     g = case.gpu_inputs()
