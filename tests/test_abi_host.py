@@ -266,3 +266,15 @@ def test_workload_page_tables_pass_the_checker():
     shared = (32768 - 64) // 64
     n0 = min(shared, workloads.history_pages(min(lens)))
     assert (table[:, :n0] == table[0, :n0]).all()
+
+
+def test_levels_marshalling_checks_shape_and_device():
+    # the binding accepts None (plain grid) or an fp32 [Hkv, 2] device tensor for levels_k /
+    # levels_v; anything else raises before the library is called
+    import torch
+    lay = _lay()
+    assert ok._levels(None, "levels_k", lay) is None
+    with pytest.raises(TypeError, match="Hkv, 2"):
+        ok._levels(torch.zeros(lay.num_kv_heads + 1, 2), "levels_k", lay)
+    with pytest.raises(TypeError, match="GPU"):
+        ok._levels(torch.zeros(lay.num_kv_heads, 2), "levels_k", lay)
