@@ -116,7 +116,10 @@ class Layer:
                                   self.table_np.shape[1], wl.group_size)
         self.cache = ok.Cache.allocate(self.lay, zero=False)
         self.table = torch.from_numpy(self.table_np).to(dev)
-        uk, uv = workloads.rotation_bases(wl, layer)
+        # a calibrated U (computed offline from query statistics on the CPU) changes code
+        # values, not the work: such a workload is timed with seeded orthogonal bases
+        uk, uv = workloads.rotation_bases(
+            workloads.scaled(wl, rotation="qr") if wl.rotation == "calibrated" else wl, layer)
         self.u_k, self.u_v = uk.to(dev).contiguous(), uv.to(dev).contiguous()
         # the clip threshold changes code values, not the work; a workload without a fixed one
         # (calibrated offline) is timed with 4.0
@@ -309,6 +312,9 @@ def main():
     ctx = (f"context {lengths[0]}" if len(set(lengths)) == 1 else
            f"contexts {min(lengths)}..{max(lengths)}")
     shape = {"qwen3_8b_100k": "Qwen3-8B-shaped decode, batch 1",
+             "qwen3_4b_32k": "Qwen3-4B-shaped decode, batch 1 (seeded orthogonal U in place of "
+                             "the calibrated one)",
+             "tiny_gqa4_1k": "tiny single-layer decode, batch 1",
              "qwen3_32b_131k": "Qwen3-32B-shaped decode, batch 16",
              "qwen3_8b_b64_prefix": "Qwen3-8B-shaped decode, batch 64 with a 32768-token shared "
                                     "prefix"}.get(wl.name, f"decode, batch {B}")
