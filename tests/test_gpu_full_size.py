@@ -30,7 +30,7 @@ def _note(msg):
 class FullLayer:
     """One layer of a workload at full size on the GPU after one decode step."""
 
-    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None):
+    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None, levels=None):
         self.wl, self.layer = wl, layer
         self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
         self.B = len(self.lengths)
@@ -40,6 +40,8 @@ class FullLayer:
         if clip is None:
             clip = (np.full(hkv, wl.clip, np.float32), np.full(hkv, wl.clip, np.float32))
         self.clip_k, self.clip_v = (np.asarray(c, np.float32) for c in clip)
+        # optional equally spaced codebooks, (lo, step) per KV head for keys and for values
+        self.levels = None if levels is None else tuple(np.asarray(x, np.float32) for x in levels)
         self.geom = oracle.Geometry(group=wl.group_size)
         self.lay = ok.make_layout(wl.num_q_heads, hkv, self.num_pages, self.B,
                                   self.table.shape[1], wl.group_size)
@@ -48,6 +50,8 @@ class FullLayer:
         table = torch.from_numpy(self.table).to(dev)
         uk, uv = self.u_k.to(dev).contiguous(), self.u_v.to(dev).contiguous()
         ck, cv = torch.from_numpy(self.clip_k).to(dev), torch.from_numpy(self.clip_v).to(dev)
+        lk, lv = ((None, None) if self.levels is None else
+                  (torch.from_numpy(self.levels[0]).to(dev), torch.from_numpy(self.levels[1]).to(dev)))
         # history: shared-prefix pages once (from the longest sequence), private pages per sequence
         n_hist = [max(0, L - 320) for L in self.lengths]
         shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
@@ -58,7 +62,8 @@ class FullLayer:
                 n = min(16384, n_hist[b] - lo)
                 k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)
                 ok.demote(self.lay, cache.pool, table[b:b + 1], uk, uv, ck, cv, k.unsqueeze(0),
-                          v.unsqueeze(0), torch.full((1,), lo, dtype=torch.int32, device=dev))
+                          v.unsqueeze(0), torch.full((1,), lo, dtype=torch.int32, device=dev),
+                          levels_k=lk, levels_v=lv)
             L = self.lengths[b]
             k, v = workloads.kv_tokens(wl, layer, b, 0, min(L, 64), dev)
             cache.sink_k[b, :, :k.shape[0]] = k.transpose(0, 1)
@@ -82,7 +87,7 @@ class FullLayer:
         out = torch.empty((self.B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
         ok.decode_step(self.lay, cache.pool, table, cache.sink_k, cache.sink_v, cache.recent_k,
                        cache.recent_v, uk, uv, ck, cv, self.k_new, self.v_new, slots, pos,
-                       self.q, out, ws, mx)
+                       self.q, out, ws, mx, levels_k=lk, levels_v=lv)
         torch.cuda.synchronize()
         self.cache = cache
         self.out = out.cpu().numpy()
@@ -99,10 +104,11 @@ class FullLayer:
         for b, t, h in samples:
             k, v = self.token(b, 64 + t)
             blk = self.blocks[int(self.table[b, t // 64]), h].cpu().numpy()
-            for tensor, x, u, c in (("k", k, self.u_k, self.clip_k), ("v", v, self.u_v,
-                                                                     self.clip_v)):
+            for i, (tensor, x, u, c) in enumerate((("k", k, self.u_k, self.clip_k),
+                                                   ("v", v, self.u_v, self.clip_v))):
+                lv = None if self.levels is None else self.levels[i][h]
                 flips += check_token(blk, t % 64, tensor, x[h][None], u[h].numpy(), c[h],
-                                     self.geom, (b, t, h, tensor))
+                                     self.geom, (b, t, h, tensor), lv)
         assert flips <= MAX_FLIP_FRACTION * len(samples) * 2 * 128 + 1, flips
         return flips
 
@@ -150,6 +156,31 @@ def test_full_size_qwen3_8b_100k():
     rng = np.random.default_rng(31)
     _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
     for kv in (0, 5):
+        layer.check_attention(0, kv)
+
+
+def test_full_size_qwen3_8b_100k_equally_spaced_codebook():
+    # layer 1 of the benchmark workload with an equally spaced Lloyd-Max codebook per KV head,
+    # fitted by the oracle on the coordinates of the layer's first 2,048 history tokens
+    wl = workloads.get("qwen3_8b_100k")
+    u_k, u_v = workloads.rotation_bases(wl, 1)
+    k, v = workloads.kv_tokens(wl, 1, 0, 64, 2048, "cuda")
+    k, v = bf16_np(k), bf16_np(v)
+    levels = []
+    for x, u in ((k, u_k), (v, u_v)):
+        lv = []
+        for h in range(wl.num_kv_heads):
+            xr = oracle.rotate_to_fp32(x[:, h], u[h].numpy())
+            lo, step, _ = oracle.lloyd_max_uniform(
+                oracle.codebook_coordinates(xr, wl.clip, wl.group_size), iters=30)
+            lv.append((lo, step))
+        levels.append(np.array(lv, np.float32))
+    _note(f"qwen3_8b_100k layer 1 with codebooks: keys {levels[0][:2].round(3).tolist()}, "
+          f"values {levels[1][:2].round(3).tolist()}")
+    layer = FullLayer(wl, layer=1, levels=levels)
+    rng = np.random.default_rng(35)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    for kv in (1, 6):
         layer.check_attention(0, kv)
 
 
