@@ -21,13 +21,16 @@ def _note(msg):
 
 def _levels(hkv, seed):
     """(lo, step) per KV head for keys and values: symmetric codebooks around the group's middle
-    (lo in [0.3, 0.7], step = (3 - 2 lo) / 3) and, on the last head, an asymmetric one."""
+    (lo in [0.3, 0.7], step = (3 - 2 lo) / 3), on the last head an asymmetric one, and with two
+    or more heads one that changes only the step (keys) or only the offset (values)."""
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(2):
+    for t in range(2):
         lo = rng.uniform(0.3, 0.7, hkv)
         lv = np.stack([lo, (3 - 2 * lo) / 3], -1).astype(np.float32)
         lv[-1] = (0.25, 0.8)
+        if hkv > 1:
+            lv[0] = (0.0, 0.7) if t == 0 else (0.3, 1.0)
         out.append(lv)
     return out
 
