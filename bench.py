@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true",
                     help="skip the all-BF16 paged cache leg (the comparison the pages quote)")
+    ap.add_argument("--levels", default=None, metavar="LO,STEP",
+                    help="demote with an equally spaced codebook (lo, step) on every KV head, "
+                         "keys and values (default: the plain grid)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibration of the HBM byte counters) and exit")
@@ -105,7 +108,7 @@ class Layer:
     pages inside a shared prefix are built once (from the longest sequence) and aliased by the
     page table; every other page is private."""
 
-    def __init__(self, wl, layer, lengths, spare):
+    def __init__(self, wl, layer, lengths, spare, levels=None):
         dev = "cuda"
         self.lengths = list(lengths)
         B = len(self.lengths)
@@ -126,6 +129,8 @@ class Layer:
         clip = wl.clip if wl.clip is not None else 4.0
         self.clip_k = torch.full((hkv,), clip, dtype=torch.float32, device=dev)
         self.clip_v = self.clip_k.clone()
+        self.levels = None if levels is None else torch.tensor(
+            [levels] * hkv, dtype=torch.float32, device=dev)
         n_hist = [max(0, L - 320) for L in self.lengths]
         shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
         longest = int(np.argmax(self.lengths))
@@ -137,7 +142,8 @@ class Layer:
                 k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)
                 ok.demote(self.lay, self.cache.pool, self.table[b:b + 1], self.u_k, self.u_v,
                           self.clip_k, self.clip_v, k.unsqueeze(0), v.unsqueeze(0),
-                          torch.full((1,), lo, dtype=torch.int32, device=dev))
+                          torch.full((1,), lo, dtype=torch.int32, device=dev),
+                          levels_k=self.levels, levels_v=self.levels)
             L = self.lengths[b]
             k, v = workloads.kv_tokens(wl, layer, b, 0, min(L, 64), dev)
             self.cache.sink_k[b, :, :k.shape[0]] = k.transpose(0, 1)
@@ -197,7 +203,8 @@ def main():
     dev = "cuda"
 
     t0 = time.time()
-    layers = [Layer(wl, i, lengths, total_steps + 8) for i in range(n_layers)]
+    levels = None if args.levels is None else tuple(float(x) for x in args.levels.split(","))
+    layers = [Layer(wl, i, lengths, total_steps + 8, levels) for i in range(n_layers)]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
@@ -214,7 +221,7 @@ def main():
             c = Lr.cache
             ok.decode_step(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
                            Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos,
-                           Lr.q, Lr.out, ws, max_len)
+                           Lr.q, Lr.out, ws, max_len, levels_k=Lr.levels, levels_v=Lr.levels)
         pos.add_(1)
 
     def capture(fn):
@@ -337,7 +344,8 @@ def main():
                                f"group {wl.group_size}, 64-token shuffled pages",
                    "batch": B, "context": lengths[0] if len(set(lengths)) == 1 else
                    [min(lengths), max(lengths)], "layers": n_layers,
-                   "launch": "hip-graph" if graph is not None else "eager"},
+                   "launch": "hip-graph" if graph is not None else "eager",
+                   **({"codebook": {"lo": levels[0], "step": levels[1]}} if levels else {})},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_bytes": int(step_bytes),
