@@ -109,6 +109,15 @@ def test_fitted_codebooks_do_not_lose_on_their_calibration_data():
     assert hist[0] == pytest.approx(np.mean((t - grid) ** 2), rel=1e-12)
     levels = error_chain.codebooks(wl, 0, (r, np.inf, r, np.inf), n_tokens=1024, iters=50)
     assert np.allclose(levels[0], lv)
+    # the equally spaced fit likewise starts from the plain grid (lo 0, step 1) and cannot lose
+    lo, step, hist_u = oracle.lloyd_max_uniform(t, iters=50)
+    assert hist_u[-1] <= hist_u[0] and hist_u[0] == pytest.approx(hist[0], rel=1e-12)
+    # equally spaced levels are a special case of free ones, so on these data the free fit (a
+    # local optimum from the same start) is not beaten beyond a small margin
+    assert hist_u[-1] >= hist[-1] - 1e-3
+    spaced = error_chain.codebooks(wl, 0, (r, np.inf, r, np.inf), n_tokens=1024, iters=50,
+                                   uniform=True)
+    assert spaced[0] == (np.float32(lo), np.float32(step))
 
 
 # ---- the equally spaced codebook that the GPU encoder runs (reading R20)
