@@ -47,12 +47,16 @@ METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s peak) + decode steps/s, 10
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_100k")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the memory probes (plain stream read, INT2-page gather)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only build the layer pools and run the memory probes, then exit")
     ap.add_argument("--no-bf16-baseline", action="store_true",
                     help="skip the all-BF16 paged cache leg (the comparison the pages quote)")
     ap.add_argument("--levels", default=None, metavar="LO,STEP",
@@ -132,11 +136,12 @@ class Layer:
         self.levels = None if levels is None else torch.tensor(
             [levels] * hkv, dtype=torch.float32, device=dev)
         n_hist = [max(0, L - 320) for L in self.lengths]
-        shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
         longest = int(np.argmax(self.lengths))
         chunk = 16384
         for b in range(B):
-            lo0 = 0 if (b == longest or not shared_hist) else min(shared_hist, n_hist[b])
+            # pages of the shared prefix are built once, from the longest sequence; a sequence
+            # still inside the prefix has private copies from the page its next write falls in
+            lo0 = 0 if b == longest else 64 * workloads.shared_pages(wl, self.lengths[b], spare)
             for lo in range(lo0, n_hist[b], chunk):
                 n = min(chunk, n_hist[b] - lo)
                 k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)
@@ -160,6 +165,85 @@ class Layer:
         self.v_new = torch.cat(vn).contiguous()
         self.q = workloads.queries(wl, layer, 0, dev, batch=B).contiguous()
         self.out = torch.empty((B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+
+def distribution(xs, digits):
+    """Median, 10th and 90th percentile of a list of timings."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), digits),
+            "p10": round(float(np.percentile(a, 10)), digits),
+            "p90": round(float(np.percentile(a, 90)), digits), "n": int(a.size)}
+
+
+def timed_graph(fn, reps, per):
+    """Capture fn() (``per`` launches) in a HIP graph, replay it ``reps`` times with HIP events
+    around each replay on the launch stream; per-launch microseconds of every replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / per)
+    return us
+
+
+def probes(wl, layers, steps):
+    """Practical HBM ceilings measured in the same run: a plain streaming read of 2 GiB, a plain
+    streaming read of one attention launch's INT2 history bytes per launch (36 launches over
+    distinct slices, as the attention kernel cycles its layer pools), and the INT2 pages read
+    through the page table in the attention kernel's grid order with 2 and 4 pages in flight per
+    wave (no arithmetic)."""
+    dev = "cuda"
+    reps = max(5, min(steps, 20))
+    big = 2 << 30
+    buf = torch.ones(big, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    us = timed_graph(lambda: ok.probe_read(buf, sink, 2048), reps, 1)
+    out = {"stream_read_2GiB": {"GB/s": round(big / (float(np.median(us)) * 1e-6) / 1e9, 1),
+                                "us": distribution(us, 2),
+                                "kernel": "probe_read_kernel (16-byte non-temporal loads, 2048 "
+                                          "workgroups)"}}
+    lr0 = layers[0]
+    n_pages = [workloads.history_pages(L + 1) for L in lr0.lengths]
+    hist = ok.pool_bytes(lr0.lay) // max(1, lr0.num_pages) * sum(n_pages)
+    hist = hist // 256 * 256
+    n_slices = len(layers)
+    if hist * n_slices <= big:
+        slices = [buf[i * hist:(i + 1) * hist] for i in range(n_slices)]
+        us = timed_graph(lambda: [ok.probe_read(x, sink, 2048) for x in slices], reps, n_slices)
+        out["stream_read_int2_launch_bytes"] = {
+            "bytes": int(hist), "GB/s": round(hist / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+            "us": distribution(us, 2),
+            "note": f"{n_slices} launches over distinct slices, per-launch mean"}
+    del buf
+    if len(lr0.lengths) == 1:
+        splits, pps = ok.decode_splits(lr0.lay, 1, lr0.lengths[0] + 1)
+        blocks = 4 * splits * wl.num_kv_heads
+        for depth in (2, 4):
+            us = timed_graph(lambda: [ok.probe_gather(Lr.lay, Lr.cache.pool, Lr.table[0],
+                                                      n_pages[0], pps, depth, sink)
+                                      for Lr in layers], reps, len(layers))
+            out[f"int2_page_gather_depth{depth}"] = {
+                "bytes": int(hist), "GB/s": round(hist / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+                "us": distribution(us, 2),
+                "note": f"{splits} splits x {wl.num_kv_heads} KV heads of {pps} pages, "
+                        f"{blocks} waves, {depth} pages in flight per wave, "
+                        f"{len(layers)} layer pools"}
+    return out
 
 
 def history_bytes(wl, lengths, table=None):
@@ -208,6 +292,10 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
+    if args.probe:
+        print(json.dumps({"workload": wl.name, "probes": probes(wl, layers, args.steps)}),
+              flush=True)
+        return
 
     # position of each sequence's new token
     pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
@@ -248,17 +336,23 @@ def main():
         else:
             step()
 
-    # ---- timed region 1: whole decode steps
+    # ---- timed region 1: whole decode steps (HIP events around each step on the launch stream
+    # for the distribution; the wall clock between two synchronisations for the mean)
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
     steps_before = int(pos[0].item()) - lengths[0]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for e_a, e_b in evs:
+        e_a.record()
         run_step()
+        e_b.record()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    step_ms = [e_a.elapsed_time(e_b) for e_a, e_b in evs]
 
     # ---- timed region 2: the segment-pass kernel (INT2 history + BF16 sink / recent blocks in
     # one launch) exactly as a step launches it, once per layer pool: a graph of n_layers launches
@@ -319,6 +413,8 @@ def main():
     ctx = (f"context {lengths[0]}" if len(set(lengths)) == 1 else
            f"contexts {min(lengths)}..{max(lengths)}")
     shape = {"qwen3_8b_100k": "Qwen3-8B-shaped decode, batch 1",
+             "qwen3_8b_100k_kv1": "one GPU's share (1 of 8 KV heads, tensor-parallel) of "
+                                  "Qwen3-8B-shaped decode, batch 1",
              "qwen3_4b_32k": "Qwen3-4B-shaped decode, batch 1 (seeded orthogonal U in place of "
                              "the calibrated one)",
              "tiny_gqa4_1k": "tiny single-layer decode, batch 1",
@@ -347,6 +443,7 @@ def main():
                    "launch": "hip-graph" if graph is not None else "eager",
                    **({"codebook": {"lo": levels[0], "step": levels[1]}} if levels else {})},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "step_ms": distribution(step_ms, 4),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_bytes": int(step_bytes),
         "roofline": {"kernel": "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)",
@@ -357,10 +454,13 @@ def main():
                      **({"logical_bytes_per_launch": int(seg_logical)}
                         if seg_logical != seg_bytes else {}),
                      "avg_launch_us": round(seg_us_avg, 3),
+                     "launch_us": distribution(seg_us, 3),
                      "timing": f"HIP events around {args.steps} replays of a graph of "
                                f"{seg_reps * n_layers} launches ({seg_reps} per layer pool), "
                                f"per-launch mean"},
     }
+    if not args.no_probes:
+        result["probes"] = probes(wl, layers, args.steps)
     if not args.no_bf16_baseline:
         int2_layer_bytes = ok.pool_bytes(layers[0].lay) + 2 * (ok.sink_bytes(layers[0].lay) +
                                                                ok.recent_bytes(layers[0].lay))
@@ -391,14 +491,14 @@ def bf16_baseline(wl, lengths, n_layers, args, capture, int2_ms_per_step, int2_l
     n_pools = max(1, min(n_layers, int(BF16_POOL_BUDGET // layer_bytes)))
     pools = []
     t0 = time.time()
-    shared = (wl.shared_prefix // 64) * 64 if wl.shared_prefix else 0
     longest = int(np.argmax(lengths))
     for i in range(n_pools):
         t_np, _ = workloads.page_tables(wl, lengths, i, spare_tokens=spare, sink=0, recent=0)
         table = torch.from_numpy(t_np).to(dev)
         pool = torch.empty(layer_bytes, dtype=torch.uint8, device=dev)
         for b, L in enumerate(lengths):
-            lo0 = 0 if (b == longest or not shared) else min(shared, L)
+            lo0 = 0 if b == longest else 64 * workloads.shared_pages(wl, L, spare, sink=0,
+                                                                     recent=0)
             for lo in range(lo0, L, 16384):
                 n = min(16384, L - lo)
                 k, v = workloads.kv_tokens(wl, i, b, lo, n, dev)
@@ -481,9 +581,30 @@ def bf16_baseline(wl, lengths, n_layers, args, capture, int2_ms_per_step, int2_l
                       f"of a graph of {n_layers} bf16_decode_attn calls, per-call mean"}
 
 
+def host_facts():
+    """The host the CPU baseline runs on: model name, logical CPUs, CPUs this process may run
+    on, and the BLAS thread pool numpy uses."""
+    import threadpoolctl
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)),
+            "blas_threads": blas[0]["num_threads"] if blas else None,
+            "blas": blas[0].get("internal_api") if blas else None}
+
+
 def cpu_baseline(wl, layer0, length, batch):
-    """Time the CPU oracle on one KV head of sequence 0 of one layer at full context, plus the
-    demotion of one token, and scale to the whole step (every KV head, sequence and layer)."""
+    """Time the CPU oracle (numpy, fp64) on one KV head of sequence 0 of one layer at full
+    context -- demotion of one token and decode attention over the three-segment cache for the
+    head's query heads -- with numpy's BLAS pool on every core this process may use; median of
+    three runs, scaled to the whole step (every KV head, sequence and layer)."""
     import threadpoolctl
 
     import oracle
@@ -518,24 +639,28 @@ def cpu_baseline(wl, layer0, length, batch):
     gq = wl.gqa
     heads = [(0, kv * gq + i) for i in range(gq)]
     clip = layer0.clip_k.cpu().numpy()
+    threads = len(os.sched_getaffinity(0))
     times = []
-    with threadpoolctl.threadpool_limits(1):      # one core: numpy's BLAS pool held to 1 thread
-        for _ in range(2):
+    with threadpoolctl.threadpool_limits(threads, user_api="blas"):
+        for _ in range(3):
             t = time.perf_counter()
             oracle.demote(pool, table, uk, uv, clip, clip, k[None, 64:65], v[None, 64:65], [0],
                           geom)
             oracle.decode_attention(pool, table, sk, sv, rk, rv, [0], [length], q, uk, uv, geom,
                                     heads=heads)
             times.append(time.perf_counter() - t)
-    per_head = min(times)
+    per_head = float(np.median(times))
     step_s = per_head * wl.num_kv_heads * wl.num_layers * batch
     head_bytes = n_hist * bytes_per_token_head(wl.group_size) + 320 * 128 * 2 * 2
     step_bytes = head_bytes * wl.num_kv_heads * wl.num_layers * batch
-    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "decode_steps_per_s": round(1.0 / step_s, 6),
+    facts = host_facts()
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "decode_steps_per_s": round(1.0 / step_s, 6), "host": facts,
             "sample": f"numpy fp64 oracle, 1 KV head ({gq} query heads) of 1 layer at context "
                       f"{length}: demotion of 1 token + decode attention over the 3-segment "
-                      f"cache ({per_head:.2f}s, best of 2), scaled x{wl.num_kv_heads} heads "
+                      f"cache ({per_head:.2f}s, median of 3: "
+                      f"{', '.join(f'{x:.2f}' for x in times)}), BLAS pool of {threads} threads "
+                      f"(the elementwise numpy work runs on one), scaled x{wl.num_kv_heads} heads "
                       f"x{wl.num_layers} layers" + (f" x{batch} sequences" if batch > 1 else "")}
 
 

@@ -22,11 +22,13 @@ import torch
 
 __all__ = [
     "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
-    "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "check_page_table",
+    "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "decode_splits",
+    "check_page_table",
     "demote", "append", "decode_attn", "Cache", "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16",
     "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
     "RECENT_TOKENS", "bf16_page_block_bytes", "bf16_page_bytes", "bf16_pool_bytes",
-    "bf16_decode_workspace_bytes", "bf16_store", "bf16_decode_attn",
+    "bf16_decode_workspace_bytes", "bf16_store", "bf16_decode_attn", "probe_read",
+    "probe_gather",
 ]
 
 HEAD_DIM = 128
@@ -70,6 +72,7 @@ _SIGNATURES = {
     "oscar_sink_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_recent_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_decode_workspace_bytes": (ctypes.c_size_t, [_LP, _i32, _i32]),
+    "oscar_decode_splits": (_i32, [_LP, _i32, _i32, _vp]),
     "oscar_check_page_table": (_i32, [_LP, _vp, _vp, _i32, _i32]),
     "oscar_demote": (_i32, [_LP] + [_vp] * 10 + [_i64, _i64, _i64, _vp, _i32, _i32, _vp]),
     "oscar_append": (_i32, [_LP] + [_vp] * 16 + [_i32, _vp]),
@@ -88,6 +91,8 @@ _SIGNATURES = {
     "oscar_bf16_store": (_i32, [_LP, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp]),
     "oscar_bf16_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                       ctypes.c_size_t, _i32, _i32, _vp]),
+    "oscar_probe_read": (_i32, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _i32, _vp]),
+    "oscar_probe_gather": (_i32, [_LP, _vp, _vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp]),
 }
 
 STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
@@ -149,6 +154,15 @@ def decode_workspace_bytes(lay: Layout, batch: int, max_seq_len: int) -> int:
     return lib().oscar_decode_workspace_bytes(ctypes.byref(lay), batch, max_seq_len)
 
 
+def decode_splits(lay: Layout, batch: int, max_seq_len: int):
+    """(splits per (sequence, KV head), history pages per split) of the decode work plan."""
+    pps = ctypes.c_int32(0)
+    n = lib().oscar_decode_splits(ctypes.byref(lay), batch, max_seq_len, ctypes.byref(pps))
+    if n < 0:
+        raise OscarError("decode_splits: invalid arguments")
+    return n, pps.value
+
+
 def check_page_table(lay: Layout, page_table, seq_lens, extra_tokens: int = 0) -> None:
     """Validate a host copy of a page table (int32 [B, max_pages_per_seq]) and lengths."""
     pt = torch.as_tensor(page_table, dtype=torch.int32).cpu().contiguous()
@@ -182,6 +196,46 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+# Size checks of device buffers.  The C ABI takes bare pointers and cannot see allocation sizes,
+# and the kernels index these buffers from the layout without bounds checks, so a buffer that is
+# too small must be caught here, before the library is called.
+
+def _min_bytes(t: torch.Tensor, name: str, nbytes: int) -> None:
+    if t.numel() * t.element_size() < nbytes:
+        raise TypeError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise TypeError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t: torch.Tensor, name: str, n: int) -> None:
+    if t.numel() != n:
+        raise TypeError(f"{name} must hold {n} entries (one per sequence), got {t.numel()}")
+
+
+def _table(t: torch.Tensor, lay: Layout, batch: int) -> None:
+    if t.dim() != 2 or t.shape[1] != lay.max_pages_per_seq or t.shape[0] < batch:
+        raise TypeError(f"page_table must be [>= {batch}, {lay.max_pages_per_seq}] "
+                        f"(max_pages_per_seq), got {tuple(t.shape)}")
+
+
+def _rotation(lay: Layout, u_k, u_v, clip_k=None, clip_v=None) -> None:
+    for name, u in (("u_k", u_k), ("u_v", u_v)):
+        _shape(u, name, (lay.num_kv_heads, HEAD_DIM, HEAD_DIM))
+    for name, c in (("clip_k", clip_k), ("clip_v", clip_v)):
+        if c is not None:
+            _shape(c, name, (lay.num_kv_heads,))
+
+
+def _segments(lay: Layout, sink_k, sink_v, recent_k, recent_v) -> None:
+    for name, t, n in (("sink_k", sink_k, SINK_TOKENS), ("sink_v", sink_v, SINK_TOKENS),
+                       ("recent_k", recent_k, RECENT_TOKENS),
+                       ("recent_v", recent_v, RECENT_TOKENS)):
+        _min_bytes(t, name, lay.max_seqs * lay.num_kv_heads * n * HEAD_DIM * 2)
+
+
 def _levels(t: Optional[torch.Tensor], name: str, lay: Layout):
     if t is None:
         return None
@@ -203,6 +257,10 @@ def demote(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, u_k: torch
     if k_src.stride(3) != 1 or k_src.shape[3] != HEAD_DIM or k_src.shape[2] != lay.num_kv_heads:
         raise TypeError("k_src last axis must be contiguous head_dim; axis 2 the KV heads")
     bsz, n = k_src.shape[0], k_src.shape[1]
+    _min_bytes(pool, "pool", pool_bytes(lay))
+    _table(page_table, lay, bsz)
+    _rotation(lay, u_k, u_v, clip_k, clip_v)
+    _rows(hist_start, "hist_start", bsz)
     _check(lib().oscar_demote(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(u_k, "u_k", torch.float32),
@@ -222,6 +280,11 @@ def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_
     bsz = seq_lens.numel()
     if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
         raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
+    _min_bytes(pool, "pool", pool_bytes(lay))
+    _table(page_table, lay, bsz)
+    _segments(lay, sink_k, sink_v, recent_k, recent_v)
+    _rotation(lay, u_k, u_v, clip_k, clip_v)
+    _rows(seq_slot, "seq_slot", bsz)
     _check(lib().oscar_append(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
@@ -234,6 +297,17 @@ def append(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_
         _contig(seq_lens, "seq_lens", torch.int32), bsz, _stream()), "append")
 
 
+def _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse):
+    _min_bytes(pool, "pool", pool_bytes(lay))
+    _table(page_table, lay, bsz)
+    _segments(lay, sink_k, sink_v, recent_k, recent_v)
+    _rotation(lay, u_k, u_v)
+    _rows(seq_slot, "seq_slot", bsz)
+    if lse is not None:
+        _shape(lse, "lse", (bsz, lay.num_q_heads))
+
+
 def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
                 seq_lens, q: torch.Tensor, u_k, u_v, out: torch.Tensor, workspace: torch.Tensor,
                 max_seq_len: int, lse: Optional[torch.Tensor] = None,
@@ -244,6 +318,8 @@ def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
     bsz = seq_lens.numel()
     if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
         raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
     _check(lib().oscar_decode_attn_stages(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
@@ -270,6 +346,10 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
     if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
         raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
+    _shape(clip_k, "clip_k", (lay.num_kv_heads,))
+    _shape(clip_v, "clip_v", (lay.num_kv_heads,))
     _check(lib().oscar_decode_step(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
@@ -314,6 +394,9 @@ def bf16_store(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor, k_src:
     if k_src.stride(3) != 1 or k_src.shape[3] != HEAD_DIM or k_src.shape[2] != lay.num_kv_heads:
         raise TypeError("k_src last axis must be contiguous head_dim; axis 2 the KV heads")
     bsz, n = k_src.shape[0], k_src.shape[1]
+    _min_bytes(pool, "pool", bf16_pool_bytes(lay))
+    _table(page_table, lay, bsz)
+    _rows(start_pos, "start_pos", bsz)
     _check(lib().oscar_bf16_store(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _dev(k_src, "k_src", torch.bfloat16),
@@ -330,6 +413,10 @@ def bf16_decode_attn(lay: Layout, pool: torch.Tensor, page_table: torch.Tensor,
     bsz = seq_lens.numel()
     if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
         raise TypeError("q / out must be [batch, Hq, 128]")
+    _min_bytes(pool, "pool", bf16_pool_bytes(lay))
+    _table(page_table, lay, bsz)
+    if lse is not None:
+        _shape(lse, "lse", (bsz, lay.num_q_heads))
     _check(lib().oscar_bf16_decode_attn(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(seq_lens, "seq_lens", torch.int32),
@@ -358,3 +445,28 @@ class Cache:
                            dtype=torch.bfloat16, device=device)
         return cls(lay, pool, seg(SINK_TOKENS), seg(SINK_TOKENS), seg(RECENT_TOKENS),
                    seg(RECENT_TOKENS))
+
+
+# ----------------------------------------------------------------------------------------------
+# memory probes (measurement only: plain reads for the practical HBM ceilings; include/oscar.h)
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 2048) -> None:
+    """Stream every byte of ``buf`` once (oscar_probe_read); ``sink``: int32 device tensor of at
+    least ``blocks`` entries."""
+    _check(lib().oscar_probe_read(_contig(buf, "buf", buf.dtype),
+                                  buf.numel() * buf.element_size(),
+                                  _contig(sink, "sink", torch.int32), sink.numel(), blocks,
+                                  _stream()), "probe_read")
+
+
+def probe_gather(lay: Layout, pool: torch.Tensor, table_row: torch.Tensor, n_pages: int,
+                 pages_per_split: int, depth: int, sink: torch.Tensor) -> None:
+    """Read the INT2 pool blocks of ``n_pages`` pages of one page-table row in the decode kernel's
+    order (oscar_probe_gather)."""
+    _min_bytes(pool, "pool", pool_bytes(lay))
+    if table_row.numel() < n_pages:
+        raise TypeError(f"table_row holds {table_row.numel()} entries, needs {n_pages}")
+    _check(lib().oscar_probe_gather(ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+                                    _contig(table_row, "table_row", torch.int32), n_pages,
+                                    pages_per_split, depth, _contig(sink, "sink", torch.int32),
+                                    sink.numel(), _stream()), "probe_gather")

@@ -8,8 +8,9 @@
 //   1. attn_kernel   both segment passes in one grid:
 //                    INT2 blocks: split-KV over history pages on the matrix cores: scores
 //                    s (q' . codes) + z sum(q') with the dot products as exact int32 i8 MFMAs,
-//                    online softmax with lazy rescaling, value accumulation in the rotated frame
-//                    as bf16 MFMAs -> (m, l, acc') partials;
+//                    softmax against a fixed per-wave reference (the first page's maxima, with a
+//                    scores-only fallback pass when a later logit passes it by 2^64), value
+//                    accumulation in the rotated frame as bf16 MFMAs -> (m, l, acc') partials;
 //                    BF16 blocks: 64-token chunks of the BF16 sink and recent ring -> (m, l, acc);
 //   2. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
 //                    the BF16 partials, normalisation.
@@ -708,8 +709,8 @@ constexpr int attn_lds_bytes() {
   return Int2Lds<G, NG>::TOTAL > Bf16Lds<G>::TOTAL ? Int2Lds<G, NG>::TOTAL : Bf16Lds<G>::TOTAL;
 }
 
-// Blocks per compute unit the register budget allows: 3 for one group per vector and up to 4
-// query heads per KV head, else 2 (the work planner sizes the grid with the same rule).
+// Blocks per compute unit the kernel is compiled for (its register budget); the work planner
+// sizes the grid for two blocks per compute unit as well.
 template <int G, int NG>
 constexpr int attn_blocks_per_cu() {
   return 2;

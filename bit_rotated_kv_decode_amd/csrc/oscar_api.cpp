@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <string>
 #include <unordered_map>
+#include <unordered_set>
 
 #include "oscar.h"
 #include "oscar_internal.h"
@@ -295,6 +296,14 @@ size_t oscar_decode_workspace_bytes(const oscar_layout* l, int32_t batch, int32_
   return oscar::make_plan(*l, batch, max_seq_len).total;
 }
 
+int32_t oscar_decode_splits(const oscar_layout* l, int32_t batch, int32_t max_seq_len,
+                            int32_t* pages_per_split) {
+  if (check_layout(l) != OSCAR_OK || batch < 0 || max_seq_len < 0) return -1;
+  const oscar::Plan p = oscar::make_plan(*l, batch, max_seq_len);
+  if (pages_per_split != nullptr) *pages_per_split = p.pages_per_split;
+  return p.num_splits;
+}
+
 oscar_status oscar_check_page_table(const oscar_layout* l, const int32_t* table,
                                     const int32_t* seq_lens, int32_t batch, int32_t extra) {
   oscar_status st = check_layout(l);
@@ -304,6 +313,7 @@ oscar_status oscar_check_page_table(const oscar_layout* l, const int32_t* table,
     return fail(OSCAR_ERR_NULL, "page table or seq_lens is NULL");
   // page id -> (sequence, logical page) of its first user
   std::unordered_map<int32_t, std::pair<int32_t, int32_t>> owner;
+  std::unordered_set<int32_t> shared;   // page ids used by more than one sequence
   for (int32_t b = 0; b < batch; ++b) {
     const long long len = static_cast<long long>(seq_lens[b]) + extra;
     if (seq_lens[b] < 0) return fail(OSCAR_ERR_RANGE, "seq_lens[%d] = %d < 0", b, seq_lens[b]);
@@ -331,6 +341,25 @@ oscar_status oscar_check_page_table(const oscar_layout* l, const int32_t* table,
         if (orow[q] != row[q])
           return fail(OSCAR_ERR_RANGE, "shared page %d of sequences %d and %d is not part of a "
                       "common prefix", id, ob, b);
+      shared.insert(id);
+    }
+  }
+  // pages the next extra_tokens decode steps write (history indices [L - 320, L + extra - 320)
+  // of each sequence) must belong to that sequence alone: a shared page holds another sequence's
+  // tokens, and its copy must be made private (copy-on-write) before the first write
+  if (extra > 0) {
+    const long long bf16 = oscar::kSink + oscar::kRecent;
+    for (int32_t b = 0; b < batch; ++b) {
+      const long long first = std::max(0LL, static_cast<long long>(seq_lens[b]) - bf16);
+      const long long end = static_cast<long long>(seq_lens[b]) + extra - bf16;   // exclusive
+      const int32_t* row = table + static_cast<size_t>(b) * l->max_pages_per_seq;
+      if (end <= first) continue;
+      for (long long p = first / oscar::kPage; p <= (end - 1) / oscar::kPage; ++p) {
+        if (shared.count(row[p]))
+          return fail(OSCAR_ERR_RANGE, "sequence %d writes history page %lld (page id %d), "
+                      "which other sequences share (give the sequence a private copy first)",
+                      b, p, row[p]);
+      }
     }
   }
   return ok();
@@ -558,6 +587,48 @@ oscar_status oscar_bf16_decode_attn(const oscar_layout* l, const void* pool,
   a.stream_loads = batch == 1 ? 1 : 0;
   return hip_status(oscar::launch_bf16_decode(a, plan, static_cast<hipStream_t>(stream)),
                     "oscar_bf16_decode_attn");
+}
+
+oscar_status oscar_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                              int32_t blocks, void* stream) {
+  if (buf == nullptr || sink == nullptr) return fail(OSCAR_ERR_NULL, "probe_read: NULL pointer");
+  if (!aligned(buf, 16) || bytes % 16 != 0 || !aligned(sink, 4))
+    return fail(OSCAR_ERR_ALIGN, "probe_read: buffer and size must be 16-byte aligned");
+  if (blocks < 1 || blocks > 65536)
+    return fail(OSCAR_ERR_RANGE, "probe_read: blocks %d outside [1, 65536]", blocks);
+  if (sink_words < static_cast<size_t>(blocks))
+    return fail(OSCAR_ERR_SHAPE, "probe_read: sink of %zu words < %d blocks", sink_words, blocks);
+  if (bytes == 0) return ok();
+  return hip_status(oscar::launch_probe_read(buf, bytes, sink, blocks,
+                                             static_cast<hipStream_t>(stream)),
+                    "oscar_probe_read");
+}
+
+oscar_status oscar_probe_gather(const oscar_layout* l, const void* pool,
+                                const int32_t* page_table_row, int32_t n_pages,
+                                int32_t pages_per_split, int32_t depth, uint32_t* sink,
+                                size_t sink_words, void* stream) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (!pool || !page_table_row || !sink) return fail(OSCAR_ERR_NULL, "probe_gather: NULL pointer");
+  if (!aligned(pool, 16) || !aligned(page_table_row, 4) || !aligned(sink, 4))
+    return fail(OSCAR_ERR_ALIGN, "probe_gather: misaligned pointer");
+  if (n_pages < 0 || n_pages > l->num_pages || n_pages > l->max_pages_per_seq)
+    return fail(OSCAR_ERR_RANGE, "probe_gather: n_pages %d outside [0, min(num_pages, "
+                "max_pages_per_seq)]", n_pages);
+  if (pages_per_split < 1 || depth < 1 || depth > 4)
+    return fail(OSCAR_ERR_RANGE, "probe_gather: pages_per_split %d < 1 or depth %d outside [1, 4]",
+                pages_per_split, depth);
+  const long long blocks =
+      static_cast<long long>((n_pages + pages_per_split - 1) / pages_per_split) * l->num_kv_heads;
+  if (blocks > (1LL << 30)) return fail(OSCAR_ERR_RANGE, "probe_gather: grid too large");
+  if (sink_words < static_cast<size_t>(4 * blocks))
+    return fail(OSCAR_ERR_SHAPE, "probe_gather: sink of %zu words < %lld", sink_words, 4 * blocks);
+  if (n_pages == 0) return ok();
+  return hip_status(oscar::launch_probe_gather(pool, page_table_row, n_pages, l->num_kv_heads,
+                                               oscar::block_bytes(n_groups(l)), pages_per_split,
+                                               depth, sink, static_cast<hipStream_t>(stream)),
+                    "oscar_probe_gather");
 }
 
 }  // extern "C"

@@ -175,6 +175,11 @@ hipError_t launch_bf16_decode(const Bf16DecodeArgs& a, const Bf16Plan& plan, hip
 hipError_t launch_bf16_store(const Bf16StoreArgs& a, hipStream_t stream);
 
 hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t stream);
+hipError_t launch_probe_gather(const void* pool, const int32_t* table, int n_pages, int hkv,
+                               int block_bytes, int pages_per_split, int depth, uint32_t* sink,
+                               hipStream_t stream);
 // One launch for the append items (ap) and the query rows (qa); either may be null.
 hipError_t launch_prep(const AppendArgs* ap, const QueryArgs* qa, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, uint32_t stages,

@@ -54,7 +54,9 @@
  *  token t in group m = j / g is  scale[t][m] * code[t][j] + zero[t][m]  (rotated space).
  *  History index h of a sequence (h = position - 64) lives in page page_table[b][h / 64],
  *  slot h % 64.  Prefix sharing is expressed by page-table aliasing only; the caller must not
- *  demote into a page that other sequences alias (copy-on-write is the caller's job).
+ *  demote into a page that other sequences alias (copy-on-write is the caller's job; a sequence
+ *  whose next history index lies in a shared page needs a private copy of that page first, and
+ *  oscar_check_page_table() rejects a table that breaks this rule).
  *
  *  BF16 sink:   [max_seqs][num_kv_heads][64][d]  bf16, token at position p < 64 in row p.
  *  BF16 recent: [max_seqs][num_kv_heads][256][d] bf16 ring, token at position p >= 64 in row
@@ -129,10 +131,20 @@ size_t oscar_recent_bytes(const oscar_layout* layout);       /* keys or values: 
 size_t oscar_decode_workspace_bytes(const oscar_layout* layout, int32_t batch,
                                     int32_t max_seq_len);
 
+/* Work plan of oscar_decode_attn for `batch` sequences of at most `max_seq_len` tokens: returns
+ * the number of INT2 work items (splits) per (sequence, KV head) and stores the history pages
+ * each covers in *pages_per_split (when not NULL); -1 for invalid arguments.  Host only. */
+int32_t oscar_decode_splits(const oscar_layout* layout, int32_t batch, int32_t max_seq_len,
+                            int32_t* pages_per_split);
+
 /* Host-side check of a host copy of a page table and sequence lengths: every page that a
  * sequence of length seq_lens[b] + extra_tokens uses must be in [0, num_pages), fit in
  * max_pages_per_seq, and no two sequences may share a page beyond the pages they share from
- * position 0 (shared pages must be a common prefix of both rows).  Touches no device memory. */
+ * position 0 (shared pages must be a common prefix of both rows).  With extra_tokens > 0 (that
+ * many decode steps will follow), every page those steps demote into -- history indices
+ * [seq_lens[b] - 320, seq_lens[b] + extra_tokens - 320) -- must be used by that sequence alone:
+ * a page shared with another sequence must be replaced by a private copy (copy-on-write) before
+ * the first write.  Touches no device memory. */
 oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* host_page_table,
                                     const int32_t* host_seq_lens, int32_t batch,
                                     int32_t extra_tokens);
@@ -316,6 +328,31 @@ oscar_status oscar_bf16_decode_attn(const oscar_layout* layout, const void* pool
                                     const void* q, float sm_scale, float* out, float* lse,
                                     void* workspace, size_t workspace_bytes, int32_t batch,
                                     int32_t max_seq_len, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Memory probes.  Not part of the method: plain reads with no arithmetic, for the practical HBM
+ * ceilings that the attention kernel's bandwidth is read against (each is timed by the caller,
+ * e.g. with events on `stream`).  The sink receives a word only in the case no data produces
+ * (it keeps the loads from being optimised away); its contents are unspecified.
+ * --------------------------------------------------------------------------------------------- */
+
+/* Streaming read of `bytes` (a multiple of 16) from `buf` (16-byte aligned) with 16-byte
+ * non-temporal loads, `blocks` workgroups of 256 threads in a grid-stride loop.  sink: device
+ * uint32 array of at least `blocks` words.  Returns OSCAR_OK, or NULL / ALIGN / RANGE / SHAPE /
+ * HIP. */
+oscar_status oscar_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                              int32_t blocks, void* stream);
+
+/* Reads the INT2 pool's (page, KV head) blocks of the pages page_table_row[0 .. n_pages) (device
+ * int32, entries in [0, num_pages)), every KV head, in the decode kernel's order: workgroups of
+ * four waves on `pages_per_split` consecutive logical pages of one KV head, wave w taking pages
+ * w, w + 4, ..., with `depth` (1..4) pages in flight per wave.  sink: device uint32 array of at
+ * least 4 * ceil(n_pages / pages_per_split) * num_kv_heads words.  Returns OSCAR_OK, or NULL /
+ * SHAPE / ALIGN / RANGE / HIP. */
+oscar_status oscar_probe_gather(const oscar_layout* layout, const void* pool,
+                                const int32_t* page_table_row, int32_t n_pages,
+                                int32_t pages_per_split, int32_t depth, uint32_t* sink,
+                                size_t sink_words, void* stream);
 
 #ifdef __cplusplus
 }

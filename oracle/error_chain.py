@@ -63,19 +63,8 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
     q_eval = np.concatenate([
         _f64(workloads.queries(wl, layer, step=1000 + i, batch=1)[0, kv * gq:(kv + 1) * gq])
         for i in range(n_eval)])
-    u_k = O.key_rotation(q_cal).astype(np.float32)
-    u_v = O.value_rotation(q_cal, k, v, sm).astype(np.float32)
+    frames = variant_frames(q_cal, k, v, sm, percentile)
     hist = slice(64, max(64, length - 256))
-    frames = {
-        "naive": (O.frame_matrix(None, d), np.inf, O.frame_matrix(None, d), np.inf),
-        "hadamard_only": (O.frame_matrix(np.eye(d), d), np.inf, O.frame_matrix(np.eye(d), d),
-                          np.inf),
-        "clip_only": (O.frame_matrix(None, d), float(np.percentile(np.abs(k), percentile)),
-                      O.frame_matrix(None, d), float(np.percentile(np.abs(v), percentile))),
-        "oscar": (O.frame_matrix(u_k, d), O.clip_threshold(k, u_k, percentile),
-                  O.frame_matrix(u_v, d), O.clip_threshold(v, u_v, percentile)),
-    }
-    frames["oscar_lloyd_max"] = frames["oscar_lm_uniform"] = frames["oscar"]
     levels = codebooks(wl, kv, frames["oscar"], layer) if "oscar_lloyd_max" in variants else None
     spaced = (codebooks(wl, kv, frames["oscar"], layer, uniform=True)
               if "oscar_lm_uniform" in variants else None)
@@ -94,6 +83,26 @@ def layer_errors(wl, kv: int, n_calib: int, n_eval: int, layer: int = 0, percent
             v_hat[hist] = O.quantize_roundtrip(v[hist], rv, cv, wl.group_size)
         out[name] = O.attention_error_metrics(q_eval, k, v, k_hat, v_hat, sm)
     return out
+
+
+def variant_frames(q_cal, k, v, sm_scale: float, percentile=99.9):
+    """{variant: (R_k, clip_k, R_v, clip_v)}: each variant's orthogonal frame (fp64) and clip
+    threshold (inf = no clip) for one KV head, from its calibration queries q_cal (n, d) and the
+    keys / values k, v (L, d) of the evaluated context."""
+    d = k.shape[1]
+    u_k = O.key_rotation(q_cal).astype(np.float32)
+    u_v = O.value_rotation(q_cal, k, v, sm_scale).astype(np.float32)
+    frames = {
+        "naive": (O.frame_matrix(None, d), np.inf, O.frame_matrix(None, d), np.inf),
+        "hadamard_only": (O.frame_matrix(np.eye(d), d), np.inf, O.frame_matrix(np.eye(d), d),
+                          np.inf),
+        "clip_only": (O.frame_matrix(None, d), float(np.percentile(np.abs(k), percentile)),
+                      O.frame_matrix(None, d), float(np.percentile(np.abs(v), percentile))),
+        "oscar": (O.frame_matrix(u_k, d), O.clip_threshold(k, u_k, percentile),
+                  O.frame_matrix(u_v, d), O.clip_threshold(v, u_v, percentile)),
+    }
+    frames["oscar_lloyd_max"] = frames["oscar_lm_uniform"] = frames["oscar"]
+    return frames
 
 
 def codebooks(wl, kv: int, frame, layer: int = 0, n_tokens: int = 4096, iters: int = 100,

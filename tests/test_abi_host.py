@@ -262,10 +262,52 @@ def test_workload_page_tables_pass_the_checker():
     table, num_pages = workloads.page_tables(wl, lens, spare_tokens=10)
     lay = _lay(num_pages=num_pages, max_pages_per_seq=table.shape[1], max_seqs=8)
     ok.check_page_table(lay, table, lens, extra_tokens=10)
-    # every sequence shares the first pages of the prefix
+    # every sequence shares the prefix pages below the page its next write falls in
     shared = (32768 - 64) // 64
-    n0 = min(shared, workloads.history_pages(min(lens)))
-    assert (table[:, :n0] == table[0, :n0]).all()
+    for b, L in enumerate(lens):
+        n0 = min(shared, (L - 320) // 64)
+        assert workloads.shared_pages(wl, L, 10) == n0
+        assert (table[b, :n0] == table[0, :n0]).all()
+        # from there on the sequence's pages are its own
+        own = table[b, n0:workloads.history_pages(L + 10)]
+        others = np.concatenate([table[c, :workloads.history_pages(lens[c] + 10)]
+                                 for c in range(len(lens)) if c != b])
+        assert not np.isin(own, others).any()
+    # without private copies, a sequence inside the prefix would demote into a shared page
+    short = int(np.argmin(lens))
+    assert lens[short] - 320 < shared * 64
+    aliased = table.copy()
+    n_short = workloads.history_pages(lens[short] + 10)
+    longest = int(np.argmax(lens))
+    aliased[short, :n_short] = table[longest, :n_short]
+    ok.check_page_table(lay, aliased, lens)                    # reading shared pages is fine
+    with pytest.raises(ok.OscarError, match="share"):
+        ok.check_page_table(lay, aliased, lens, extra_tokens=10)
+
+
+def test_check_page_table_rejects_writes_into_shared_pages():
+    lay = _lay(num_pages=8, max_pages_per_seq=4)
+    # sequence 1 holds 1.5 pages of history, both its pages are aliased from sequence 0
+    lens = [320 + 3 * 64, 320 + 64 + 32]
+    table = np.array([[5, 1, 7, 0], [5, 1, 0, 0]], np.int32)
+    ok.check_page_table(lay, table, lens)
+    with pytest.raises(ok.OscarError, match="share"):    # next write: slot 32 of page 1
+        ok.check_page_table(lay, table, lens, extra_tokens=1)
+    # a private copy of the written page makes the table valid
+    ok.check_page_table(lay, np.array([[5, 1, 7, 0], [5, 2, 0, 0]], np.int32), lens,
+                        extra_tokens=1)
+    # a write range that reaches into the next page needs that page private too
+    ok.check_page_table(lay, np.array([[5, 1, 7, 0], [5, 2, 3, 0]], np.int32), lens,
+                        extra_tokens=33)
+    with pytest.raises(ok.OscarError, match="share"):
+        ok.check_page_table(lay, np.array([[5, 1, 7, 0], [5, 2, 7, 0]], np.int32),
+                            [320 + 3 * 64, 320 + 64 + 32], extra_tokens=33)
+    # contexts without history yet: the first demotion writes history index 0
+    with pytest.raises(ok.OscarError, match="share"):
+        ok.check_page_table(lay, np.array([[5, 1, 7, 0], [5, 0, 0, 0]], np.int32),
+                            [320 + 3 * 64, 320], extra_tokens=1)
+    ok.check_page_table(lay, np.array([[5, 1, 7, 0], [4, 0, 0, 0]], np.int32),
+                        [320 + 3 * 64, 320], extra_tokens=1)
 
 
 def test_levels_marshalling_checks_shape_and_device():
@@ -278,3 +320,118 @@ def test_levels_marshalling_checks_shape_and_device():
         ok._levels(torch.zeros(lay.num_kv_heads + 1, 2), "levels_k", lay)
     with pytest.raises(TypeError, match="GPU"):
         ok._levels(torch.zeros(lay.num_kv_heads, 2), "levels_k", lay)
+
+
+def _int2_buffers(lay, bsz, **wrong):
+    """Host tensors of the sizes the INT2 entry points need; ``wrong`` replaces some of them."""
+    import torch
+    hkv, hq = lay.num_kv_heads, lay.num_q_heads
+    t = dict(pool=torch.zeros(ok.pool_bytes(lay), dtype=torch.uint8),
+             table=torch.zeros(bsz, lay.max_pages_per_seq, dtype=torch.int32),
+             sink_k=torch.zeros(lay.max_seqs, hkv, 64, 128, dtype=torch.bfloat16),
+             recent_k=torch.zeros(lay.max_seqs, hkv, 256, 128, dtype=torch.bfloat16),
+             u=torch.zeros(hkv, 128, 128), clip=torch.ones(hkv),
+             rows=torch.zeros(bsz, dtype=torch.int32),
+             q=torch.zeros(bsz, hq, 128, dtype=torch.bfloat16),
+             out=torch.zeros(bsz, hq, 128), lse=torch.zeros(bsz, hq),
+             kn=torch.zeros(bsz, hkv, 128, dtype=torch.bfloat16),
+             ws=torch.zeros(1 << 20, dtype=torch.uint8))
+    t.update(wrong)
+    return t
+
+
+@pytest.mark.parametrize("wrong, name", [
+    (dict(pool="short"), "pool"), (dict(table="cols"), "page_table"),
+    (dict(table="rows"), "page_table"), (dict(u="heads"), "u_k"), (dict(clip="heads"), "clip_k"),
+    (dict(sink_k="slots"), "sink_k"), (dict(recent_k="slots"), "recent_k"),
+    (dict(rows="short"), "seq_slot"), (dict(lse="shape"), "lse")])
+def test_binding_rejects_undersized_buffers(wrong, name):
+    # the C ABI cannot see allocation sizes, so the binding checks every buffer against the
+    # layout before the call; a wrong size raises TypeError naming the buffer
+    import torch
+    lay = _lay(num_pages=6, max_seqs=3, max_pages_per_seq=4)
+    bsz = 2
+    good = _int2_buffers(lay, bsz)
+    bad = {"short": lambda t: t[:-1] if t.dim() == 1 else t[:, :-1],
+           "cols": lambda t: t[:, :-1], "rows": lambda t: t[:1],
+           "heads": lambda t: t[:-1], "slots": lambda t: t[:-1],
+           "shape": lambda t: t[:, :-1]}
+    key = next(iter(wrong))
+    t = dict(good)
+    t[key] = bad[wrong[key]](good[key]).contiguous()
+    calls = {
+        "append": lambda: ok.append(lay, t["pool"], t["table"], t["sink_k"], t["sink_k"],
+                                    t["recent_k"], t["recent_k"], t["u"], t["u"], t["clip"],
+                                    t["clip"], t["kn"], t["kn"], t["rows"], good["rows"]),
+        "decode_attn": lambda: ok.decode_attn(lay, t["pool"], t["table"], t["sink_k"],
+                                              t["sink_k"], t["recent_k"], t["recent_k"],
+                                              t["rows"], good["rows"], t["q"], t["u"], t["u"],
+                                              t["out"], t["ws"], 1000, lse=t["lse"]),
+        "decode_step": lambda: ok.decode_step(lay, t["pool"], t["table"], t["sink_k"],
+                                              t["sink_k"], t["recent_k"], t["recent_k"], t["u"],
+                                              t["u"], t["clip"], t["clip"], t["kn"], t["kn"],
+                                              t["rows"], good["rows"], t["q"], t["out"],
+                                              t["ws"], 1000, lse=t["lse"]),
+    }
+    uses = {"append": {"pool", "table", "sink_k", "recent_k", "u", "clip", "rows"},
+            "decode_attn": {"pool", "table", "sink_k", "recent_k", "u", "rows", "lse"},
+            "decode_step": {"pool", "table", "sink_k", "recent_k", "u", "clip", "rows", "lse"}}
+    for fn, call in calls.items():
+        if key not in uses[fn]:
+            continue
+        with pytest.raises(TypeError, match=name):
+            call()
+    # with every size right, the call gets as far as the device check (host tensors here)
+    t = dict(good)
+    for call in calls.values():
+        with pytest.raises(TypeError, match="GPU"):
+            call()
+    # demote: pool, table, rotation, clip and hist_start against the layout
+    src = torch.zeros(bsz, 3, lay.num_kv_heads, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="hist_start"):
+        ok.demote(lay, good["pool"], good["table"], good["u"], good["u"], good["clip"],
+                  good["clip"], src, src, good["rows"][:1])
+    with pytest.raises(TypeError, match="pool"):
+        ok.demote(lay, good["pool"][:-1], good["table"], good["u"], good["u"], good["clip"],
+                  good["clip"], src, src, good["rows"])
+    # BF16 baseline entry points
+    bpool = torch.zeros(ok.bf16_pool_bytes(lay), dtype=torch.uint8)
+    with pytest.raises(TypeError, match="pool"):
+        ok.bf16_store(lay, bpool[:-1], good["table"], src, src, good["rows"])
+    with pytest.raises(TypeError, match="start_pos"):
+        ok.bf16_store(lay, bpool, good["table"], src, src, good["rows"][:1])
+    with pytest.raises(TypeError, match="page_table"):
+        ok.bf16_decode_attn(lay, bpool, good["table"][:, :-1].contiguous(), good["rows"],
+                            good["q"], good["out"], good["ws"], 1000)
+
+
+def test_decode_splits_query():
+    # the plan aims at one round of two blocks per compute unit (512 blocks with the BF16 chunk
+    # blocks), at least 4 pages per split
+    lay = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2000)
+    assert ok.decode_splits(lay, 1, 100000) == (58, 27)      # 1558 pages x 8 heads / 472 blocks
+    assert ok.decode_splits(lay, 1, 320) == (0, 4)
+    one = _lay(num_kv_heads=1, num_q_heads=4, max_pages_per_seq=2000)
+    assert ok.decode_splits(one, 1, 100000) == (390, 4)
+    with pytest.raises(ok.OscarError):
+        ok.decode_splits(lay, -1, 10)
+
+
+def test_probe_validation_happens_before_launch():
+    lib = ok.lib()
+    lay = _lay()
+    buf, sink = 4096, 8192            # fake, aligned addresses: every call below is rejected
+    assert lib.oscar_probe_read(None, 64, sink, 16, 16, None) == -1
+    assert lib.oscar_probe_read(buf + 8, 64, sink, 16, 16, None) == -3
+    assert lib.oscar_probe_read(buf, 72, sink, 16, 16, None) == -3
+    assert lib.oscar_probe_read(buf, 64, sink, 16, 0, None) == -4
+    assert lib.oscar_probe_read(buf, 64, sink, 15, 16, None) == -2
+    assert lib.oscar_probe_read(buf, 0, sink, 16, 16, None) == 0      # nothing to read
+    L = ctypes.byref(lay)
+    assert lib.oscar_probe_gather(L, None, buf, 4, 2, 2, sink, 64, None) == -1
+    assert lib.oscar_probe_gather(L, buf, buf, 11, 2, 2, sink, 64, None) == -4   # > num_pages
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 0, 2, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 5, sink, 64, None) == -4
+    # 2 splits x 8 heads x 4 waves = 64 sink words needed
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 2, sink, 63, None) == -2
+    assert lib.oscar_probe_gather(L, buf, buf, 0, 2, 2, sink, 0, None) == 0

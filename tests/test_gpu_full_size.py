@@ -52,12 +52,12 @@ class FullLayer:
         ck, cv = torch.from_numpy(self.clip_k).to(dev), torch.from_numpy(self.clip_v).to(dev)
         lk, lv = ((None, None) if self.levels is None else
                   (torch.from_numpy(self.levels[0]).to(dev), torch.from_numpy(self.levels[1]).to(dev)))
-        # history: shared-prefix pages once (from the longest sequence), private pages per sequence
+        # history: shared-prefix pages once (from the longest sequence), private pages per
+        # sequence (including the copies of prefix pages a short sequence will write into)
         n_hist = [max(0, L - 320) for L in self.lengths]
-        shared_hist = ((wl.shared_prefix - 64) // 64) * 64 if wl.shared_prefix else 0
         longest = int(np.argmax(self.lengths))
         for b in range(self.B):
-            lo0 = 0 if (b == longest or not shared_hist) else min(shared_hist, n_hist[b])
+            lo0 = 0 if b == longest else 64 * workloads.shared_pages(wl, self.lengths[b], 1)
             for lo in range(lo0, n_hist[b], 16384):
                 n = min(16384, n_hist[b] - lo)
                 k, v = workloads.kv_tokens(wl, layer, b, 64 + lo, n, dev)

@@ -76,6 +76,11 @@ WORKLOADS = {
         name="qwen3_8b_100k", seed=3, num_layers=36, batch=1, num_q_heads=32, num_kv_heads=8,
         head_dim=128, group_size=128, context=100000, outliers="one_per_head", rotation="qr",
         clip=4.0),
+    # one GPU's share of the same layers under 8-way tensor parallelism (one KV head per GPU)
+    "qwen3_8b_100k_kv1": Workload(
+        name="qwen3_8b_100k_kv1", seed=3, num_layers=36, batch=1, num_q_heads=4, num_kv_heads=1,
+        head_dim=128, group_size=128, context=100000, outliers="one_per_head", rotation="qr",
+        clip=4.0),
     # Qwen3-8B-shaped batch 64, ragged 8k..128k contexts, 32768-token shared prefix
     "qwen3_8b_b64_prefix": Workload(
         name="qwen3_8b_b64_prefix", seed=4, num_layers=36, batch=64, num_q_heads=32,
@@ -132,29 +137,42 @@ def history_pages(length: int, sink: int = 64, recent: int = 256, page: int = 64
     return max(0, -(-(length - sink - recent) // page))
 
 
+def shared_pages(wl: Workload, length: int, spare_tokens: int = 0, sink: int = 64,
+                 recent: int = 256, page: int = 64) -> int:
+    """Logical pages of a sequence of ``length`` tokens that alias the shared prefix's physical
+    pages.  Pages inside ``wl.shared_prefix`` are shared, except from the page that the
+    sequence's next write (history index length - sink - recent, when ``spare_tokens`` > 0) falls
+    in: a sequence still inside the prefix gets private copies of the pages it will write
+    (copy-on-write), so that its own new tokens never land in a page other sequences read."""
+    if not wl.shared_prefix:
+        return 0
+    n = min((wl.shared_prefix - sink) // page, history_pages(length + spare_tokens, sink, recent,
+                                                             page))
+    if spare_tokens > 0:
+        n = min(n, max(0, length - sink - recent) // page)
+    return n
+
+
 def page_tables(wl: Workload, lengths: Sequence[int], layer: int = 0, spare_tokens: int = 0,
                 sink: int = 64, recent: int = 256, page: int = 64):
     """Shuffled page tables.
 
     Every sequence gets room for ``spare_tokens`` more history tokens than its context holds.
     Logical pages that fall inside ``wl.shared_prefix`` map to the same physical pages in every
-    sequence (a full prefix-cache hit); all other pages are private.  Physical page ids are a
-    seeded permutation of ``range(num_pages)``.  Returns (table int32 [B, max_pages], num_pages);
-    entries past a sequence's last page are 0 and are never read.
+    sequence (a full prefix-cache hit), up to the page a sequence will write next (see
+    ``shared_pages``); all other pages are private.  Physical page ids are a seeded permutation
+    of ``range(num_pages)``.  Returns (table int32 [B, max_pages], num_pages); entries past a
+    sequence's last page are 0 and are never read.
     """
-    n_shared = 0
-    if wl.shared_prefix:
-        n_shared = (wl.shared_prefix - sink) // page
     need = [history_pages(L + spare_tokens, sink, recent, page) for L in lengths]
-    private = [max(0, n - n_shared) for n in need]
-    shared_used = min(n_shared, max(need) if need else 0)
-    num_pages = shared_used + sum(private)
+    share = [shared_pages(wl, L, spare_tokens, sink, recent, page) for L in lengths]
+    shared_used = max(share) if share else 0
+    num_pages = shared_used + sum(n - s for n, s in zip(need, share))
     max_pages = max(1, max(need) if need else 1)
     perm = _np_rng(wl.seed, _PAGES, layer).permutation(max(num_pages, 1)).astype(np.int32)
     table = np.zeros((len(lengths), max_pages), dtype=np.int32)
     nxt = shared_used
-    for b, n in enumerate(need):
-        s = min(n, shared_used)
+    for b, (n, s) in enumerate(zip(need, share)):
         table[b, :s] = perm[:s]
         table[b, s:n] = perm[nxt:nxt + (n - s)]
         nxt += n - s
