@@ -24,8 +24,8 @@ __all__ = [
     "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
     "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "decode_splits",
     "check_page_table",
-    "demote", "append", "decode_attn", "Cache", "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16",
-    "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
+    "demote", "append", "decode_attn", "decode_step", "decode_step_noalloc", "Cache",
+    "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16", "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
     "RECENT_TOKENS", "bf16_page_block_bytes", "bf16_page_bytes", "bf16_pool_bytes",
     "bf16_decode_workspace_bytes", "bf16_store", "bf16_decode_attn", "probe_read",
     "probe_gather",
@@ -84,6 +84,8 @@ _SIGNATURES = {
                                         _i32, _i32, ctypes.c_uint32, _vp]),
     "oscar_decode_step": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _vp,
                                                        ctypes.c_size_t, _i32, _i32, _vp]),
+    "oscar_decode_step_noalloc": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _i32,
+                                                               _i32, _vp]),
     "oscar_bf16_page_block_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_page_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_pool_bytes": (ctypes.c_size_t, [_LP]),
@@ -364,6 +366,38 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
         _stream()), "decode_step")
+
+
+def decode_step_noalloc(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k,
+                        u_v, clip_k, clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot,
+                        seq_pos, q: torch.Tensor, out: torch.Tensor, max_seq_len: int,
+                        lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0,
+                        levels_k: Optional[torch.Tensor] = None,
+                        levels_v: Optional[torch.Tensor] = None) -> None:
+    """decode_step with the library's own per-GPU scratch array as workspace
+    (oscar_decode_step_noalloc): nothing is allocated; calls that overlap on one GPU race."""
+    bsz = seq_pos.numel()
+    if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
+        raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
+    _shape(clip_k, "clip_k", (lay.num_kv_heads,))
+    _shape(clip_v, "clip_v", (lay.num_kv_heads,))
+    _check(lib().oscar_decode_step_noalloc(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
+        _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
+        _contig(clip_v, "clip_v", torch.float32), _levels(levels_k, "levels_k", lay),
+        _levels(levels_v, "levels_v", lay), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_pos, "seq_pos", torch.int32), _contig(q, "q", torch.bfloat16),
+        float(sm_scale), _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32), bsz, int(max_seq_len),
+        _stream()), "decode_step_noalloc")
 
 
 # ----------------------------------------------------------------------------------------------

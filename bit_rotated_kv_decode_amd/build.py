@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "liboscar.so")
 
-DEVICE_SOURCES = ["encode.hip", "decode.hip", "bf16_decode.hip", "probe.hip"]
+DEVICE_SOURCES = ["encode.hip", "decode.hip", "bf16_decode.hip", "probe.hip", "noalloc.hip"]
 HOST_SOURCES = ["oscar_api.cpp"]
 ARCH = "gfx950"
 

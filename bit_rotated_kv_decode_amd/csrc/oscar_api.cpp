@@ -492,6 +492,52 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
                     "oscar_decode_step");
 }
 
+oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
+                                       const int32_t* page_table, void* sink_k, void* sink_v,
+                                       void* recent_k, void* recent_v, const float* u_k,
+                                       const float* u_v, const float* clip_k, const float* clip_v,
+                                       const float* levels_k, const float* levels_v,
+                                       const void* k_new, const void* v_new,
+                                       const int32_t* seq_slot, const int32_t* seq_pos,
+                                       const void* q, float sm_scale, float* out, float* lse,
+                                       int32_t batch, int32_t max_seq_len, void* stream) {
+  oscar::AppendArgs ap;
+  oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                                     u_k, u_v, clip_k, clip_v, levels_k, levels_v, k_new, v_new,
+                                     seq_slot, seq_pos, batch, ap);
+  if (st != OSCAR_OK) return st;
+  if (batch > 0 && max_seq_len >= 1 && check_layout(l) == OSCAR_OK) {
+    const size_t need = oscar::make_plan(*l, batch, max_seq_len).total;
+    if (need > oscar::kScratchBytes)
+      return fail(OSCAR_ERR_WORKSPACE, "oscar_decode_step_noalloc: %d sequences of up to %d "
+                  "tokens need %zu bytes of workspace, more than its %zu-byte scratch array "
+                  "(use oscar_decode_step with a caller workspace)", batch, max_seq_len, need,
+                  oscar::kScratchBytes);
+  }
+  // every host check first, against an aligned stand-in of the scratch array's size; the
+  // device address is looked up only once they all pass
+  oscar::DecodeArgs a;
+  oscar::QueryArgs qa;
+  oscar::Plan plan;
+  st = make_decode_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot, seq_pos,
+                        q, u_k, u_v, sm_scale, out, lse, reinterpret_cast<void*>(uintptr_t{256}),
+                        oscar::kScratchBytes, batch, max_seq_len, a, qa, plan);
+  if (st != OSCAR_OK || batch == 0) return st;
+  void* ws = nullptr;
+  hipError_t e = oscar::scratch_on_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e, "oscar_decode_step_noalloc: scratch address");
+  a.workspace = static_cast<uint8_t*>(ws);
+  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
+  qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
+  a.len_add = 1;   // attention sees the appended token
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  e = oscar::launch_prep(&ap, &qa, s);
+  if (e != hipSuccess) return hip_status(e, "oscar_decode_step_noalloc");
+  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
+                                                      OSCAR_STAGE_MERGE, s),
+                    "oscar_decode_step_noalloc");
+}
+
 size_t oscar_bf16_page_block_bytes(const oscar_layout* l) {
   if (check_layout(l) != OSCAR_OK) return 0;
   return static_cast<size_t>(oscar::kBf16Block);

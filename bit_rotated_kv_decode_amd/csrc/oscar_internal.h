@@ -180,6 +180,10 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int 
 hipError_t launch_probe_gather(const void* pool, const int32_t* table, int n_pages, int hkv,
                                int block_bytes, int pages_per_split, int depth, uint32_t* sink,
                                hipStream_t stream);
+// Library-owned decode workspace of oscar_decode_step_noalloc (noalloc.hip): one array of this
+// many bytes per GPU, its device address looked up once per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_on_current_device(void** ptr);
 // One launch for the append items (ap) and the query rows (qa); either may be null.
 hipError_t launch_prep(const AppendArgs* ap, const QueryArgs* qa, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, uint32_t stages,

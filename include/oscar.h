@@ -22,7 +22,9 @@
  * ---------------------------------------
  *  - All buffers are caller-owned device memory (allocated by the caller, e.g. through PyTorch).
  *    The library never allocates, frees or synchronises; it keeps no state between calls and is
- *    safe to call from several host threads on different streams.
+ *    safe to call from several host threads on different streams.  (One exception, for callers
+ *    that cannot allocate: oscar_decode_step_noalloc takes its workspace from a device array the
+ *    library owns, one per GPU, and concurrent calls on one GPU race on it.)
  *  - Every compute call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *  - All argument checks that can be made on the host run before any HIP call; on failure the
  *    call returns a negative status and touches no device memory.  A kernel launch failure
@@ -267,6 +269,27 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
                                float sm_scale, float* out, float* lse, void* workspace,
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                                void* stream);
+
+/* oscar_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  The same step, with the
+ * same arguments minus the workspace: the library takes its workspace from a device array it owns,
+ * 16 MiB on each GPU it runs on (held until the process ends, its address looked up on the first
+ * call on each device).  Calls whose plan needs more than 16 MiB of workspace (as reported by
+ * oscar_decode_workspace_bytes) are rejected with OSCAR_ERR_WORKSPACE before anything is
+ * launched.  The call allocates and frees nothing.  Every call on one GPU uses that GPU's one
+ * array, whose contents on entry do not matter (each call writes every byte it reads before
+ * reading it): calls that overlap on one GPU -- on different streams without ordering between
+ * them, or from several host threads -- race on it and give wrong results.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
+oscar_status oscar_decode_step_noalloc(const oscar_layout* layout, void* pool,
+                                       const int32_t* page_table, void* sink_k, void* sink_v,
+                                       void* recent_k, void* recent_v, const float* u_k,
+                                       const float* u_v, const float* clip_k, const float* clip_v,
+                                       const float* levels_k, const float* levels_v,
+                                       const void* k_new, const void* v_new,
+                                       const int32_t* seq_slot, const int32_t* seq_pos,
+                                       const void* q, float sm_scale, float* out, float* lse,
+                                       int32_t batch, int32_t max_seq_len, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Paged BF16 baseline.  The pages report the INT2 history's system gains against a history kept

@@ -435,3 +435,34 @@ def test_probe_validation_happens_before_launch():
     # 2 splits x 8 heads x 4 waves = 64 sink words needed
     assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 2, sink, 63, None) == -2
     assert lib.oscar_probe_gather(L, buf, buf, 0, 2, 2, sink, 0, None) == 0
+
+
+def _call_step_noalloc(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, uk=4096, uv=4096, ck=4096,
+             cv=4096, lk=None, lv=None, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, out=4096,
+             lse=None, batch=1, maxlen=600)
+    a.update(over)
+    return ok.lib().oscar_decode_step_noalloc(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
+        a["uv"], a["ck"], a["cv"], a["lk"], a["lv"], a["kn"], a["vn"], a["slot"], a["pos"],
+        a["q"], 0.0, a["out"], a["lse"], a["batch"], a["maxlen"], None)
+
+
+def test_step_noalloc_validation_happens_before_launch():
+    # the no-allocation step checks what oscar_decode_step checks, plus its scratch limit, all
+    # before it looks up the scratch array or launches anything
+    lay = _lay()
+    assert _call_step_noalloc(lay, kn=None) == -1
+    assert _call_step_noalloc(lay, q=None) == -1
+    assert _call_step_noalloc(lay, ck=4096 + 2) == -3
+    assert _call_step_noalloc(lay, maxlen=100000) == -4
+    assert _call_step_noalloc(lay, batch=-1) == -4
+    assert _call_step_noalloc(lay, batch=0, q=None, kn=None) == 0
+    # a plan larger than the 16 MiB scratch array is refused with a message that says so
+    big = _lay(num_q_heads=64, num_kv_heads=8, max_seqs=512, max_pages_per_seq=2100)
+    need = ok.decode_workspace_bytes(big, 512, 131072)
+    assert need > (16 << 20)
+    assert _call_step_noalloc(big, batch=512, maxlen=131072) == -5
+    assert "scratch" in ok.lib().oscar_last_error().decode()
+    # the same plan with a caller workspace gets past that check (and fails on the fake pool)
+    assert ok.decode_workspace_bytes(_lay(), 1, 600) <= (16 << 20)
