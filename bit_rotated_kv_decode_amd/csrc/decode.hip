@@ -3,14 +3,13 @@
 // Structure after the OSCAR write-up "超越TurboQuant！OSCAR：面向真实服务的2-bit KV Cache量化",
 // section OSCAR 的设计: the INT2 history and the BF16 segments are processed separately and then
 // combined with an online-softmax merge.  Launch order on one stream (after the preparation
-// launch of encode.hip, which rotates the query and splits it into the int8 hi / lo MFMA
-// operands q' ~ a (hi + lo / 256) plus the per-group sums of the quantised q'):
+// launch of encode.hip, which rotates the query and writes it as the fp8 operand of the key
+// contraction, q'' = q' * sm_scale * log2(e) in four parts, plus its per-group sums):
 //   1. attn_kernel   both segment passes in one grid:
-//                    INT2 blocks: split-KV over history pages on the matrix cores: scores
-//                    s (q' . codes) + z sum(q') with the dot products as exact int32 i8 MFMAs,
-//                    softmax against a fixed per-wave reference (the first page's maxima, with a
-//                    scores-only fallback pass when a later logit passes it by 2^64), value
-//                    accumulation in the rotated frame as bf16 MFMAs -> (m, l, acc') partials;
+//                    INT2 blocks: split-KV over history pages on the matrix cores, the codes as
+//                    FP4 operands: scores s (q'' . codes) + z sum(q''), a softmax reference per
+//                    page pair, values p * s_v (fp8 parts) against the value codes, accumulated
+//                    in the rotated frame -> (m, l, acc') partials;
 //                    BF16 blocks: 64-token chunks of the BF16 sink and recent ring -> (m, l, acc);
 //   2. merge_kernel  log-sum-exp merge of the INT2 partials, un-rotation acc' R_v^T, merge with
 //                    the BF16 partials, normalisation.
@@ -21,55 +20,79 @@
 namespace oscar {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-// The softmax reference of a wave is the maximum logit of its first page; later logits may exceed
-// it by up to 2^kRefSpan (p <= 2^64 keeps p * s_v, the value sums and l finite in fp32 / bf16).
-constexpr float kRefSpan = 64.0f;
 // Buffer resources: the last descriptor word for raw 32-bit-element access on gfx9-family parts,
 // and the cache-policy bit of a non-temporal access.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
-// Pages a wave has in flight or in process: register sets of the page loop.
-constexpr int kDepth = 2;
-
-// FP4 (E2M1) pair in byte B of x -> two bf16; a 2-bit code zero-extended to a nibble encodes
-// code / 2, so the scale 2 gives the code itself.
-template <int B>
-__device__ __forceinline__ v2bf codes_to_bf16(uint32_t x) {
-  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, B);
-}
 
 // ------------------------------------------------------------------------------------------
 // 2. INT2 split-KV decode on the matrix cores.
 //
-// Block = 4 waves on pages [p0, p1) of one (sequence, KV head).  Wave w takes pages p0 + w + 4 i,
-// i = 0, 1, ..., one per step; the next page's loads are in flight while a page is processed
-// (two register sets used in turn).
+// Block = 4 waves on pages [p0, p1) of one (sequence, KV head).  Wave w takes pages
+// p0 + w + 4 i in pairs (i = 2 j, 2 j + 1); the next pair's loads are in flight while a pair is
+// processed (two register sets used in turn).
 //
-// Scores: D[row, token] = sum_k A[row, k] B[k, token] with v_mfma_i32_16x16x64_i8.  B = key codes
-// of 16 tokens (lane n + 16 qd holds token n's packed dwords qd and 4 + qd, spread into bytes);
-// A = the int8 hi (or lo) part of q' placed in rows 4 st + h (GP = 4) or 8 (st % 2) + h (GP = 8)
-// for sub-tile st (zero elsewhere), kept in LDS.  The output rows of one sub-tile land in one
-// lane group, so after the page's sub-tiles every lane holds the scores of its own token(s) for
-// 4 heads, one per register.
-// Values: acc[row, ch] += sum_t P[row, t] V[t, ch] with v_mfma_f32_16x16x32_bf16; P rows are the
-// bf16 hi and lo parts of p * s_v for each head, transposed through LDS; V = value codes turned
-// into exact bf16 integers by the FP4 conversion path.
-// LDS carve-up of an INT2 block: per-wave P tiles, and apart from them the per-wave accumulator
-// rows and softmax statistics that the block combines at the end.
+// Both contractions are v_mfma_scale_f32_16x16x128_f8f6f4 with the stored 2-bit codes as the FP4
+// operand B -- a code c zero-extended to a nibble is the E2M1 value c / 2, so a 32-bit word of 16
+// codes becomes two operand dwords with one mask and one shift-and-mask -- and an fp8 (e4m3)
+// operand A in several parts whose E8M0 row scales restore the magnitudes:
+//   keys:   D[(head, part)][token] = sum over 128 channels of the parts of q'' = q' * sm_scale *
+//           log2(e) (written by the preparation launch, four parts, about 16 bits) times the key
+//           codes of 16 tokens; a lane (g, n) then holds head 4 ht + g of token 16 st + n in its
+//           four accumulators (one per part), so the logit is s (d0 + d1 + d2 + d3) + z sum(q'');
+//   values: D[(head, part)][channel] = sum over the 128 tokens of a page pair of the parts of
+//           x = p * s_v (four parts, about 16 bits, bytes transposed through the wave's own LDS
+//           tile) times the value codes; the accumulators sum the parts once, at the end.
+// The matrix cores add the products of each 8-element K-slice with about 16 bits relative to the
+// slice's largest product, truncating toward zero.  Products of x and the non-negative codes all
+// share one sign, so that truncation would bias every value sum low; at 100k tokens, where the
+// output is a small average of large terms, it shows as ~5e-4 of error.  The leading part of each
+// operand is therefore an integer on a fixed grid (products that are multiples of one step sum
+// exactly), and only the small remainders, of either sign, go through the floating parts.
+// Softmax: each pair takes its own reference, the integer ceil(m_pair) of the head's largest
+// logit in the pair, so every p = 2^(logit - m_pair + 8 - e_v) lies in (0, 2^(8 - e_v)] and
+// x = p * s_v < 256 (e_v: the pair's largest value scale is below 2^e_v) -- the range of e4m3
+// with room for the parts' remainders.  The pair's weight relative to the wave's reference m_ref,
+// 2^(m_pair - 8 + e_v - m_ref), is a power of two: it is the value operand's E8M0 row scale and
+// one multiply for the sums of p and p * z_v.  m_ref is the first pair's m_pair and moves (with an
+// exact power-of-two rescale of the accumulators) only when a later pair's exceeds it by 32.
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kNibbles = 0x33333333u;
+constexpr int kScaleTwo = 128;          // E8M0 2^1: FP4 holds a 2-bit code c as c / 2
+constexpr float kRescaleSpan = 32.0f;   // m_ref moves once a pair's reference passes it by this
+
+__device__ __forceinline__ v4f mfma_f8_f4(const v8i& a, const v8i& b, v4f c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, kScaleTwo);
+}
+// 32 codes (two words) as an FP4 operand: even codes of w0, odd codes of w0, then of w1
+__device__ __forceinline__ v8i fp4_operand(uint32_t w0, uint32_t w1) {
+  return v8i{static_cast<int>(w0 & kNibbles), static_cast<int>((w0 >> 2) & kNibbles),
+             static_cast<int>(w1 & kNibbles), static_cast<int>((w1 >> 2) & kNibbles), 0, 0, 0, 0};
+}
+__device__ __forceinline__ float lo_half(uint32_t w) {
+  return __half2float(__ushort_as_half(static_cast<uint16_t>(w & 0xFFFF)));
+}
+__device__ __forceinline__ float hi_half(uint32_t w) {
+  return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)));
+}
+
+// LDS carve-up of an INT2 block: per wave and value operand (tile ht, group g) one fp8 operand
+// tile of 64 lanes x 32 bytes, and apart from them the per-wave rows the block combines at the end.
 template <int G, int NG>
 struct Int2Lds {
-  static constexpr int GP = G <= 4 ? 4 : 8;
-  static constexpr int PB = 4 * NG * 16 * kPage * 2;         // [wave][g][row][token] bf16
-  static constexpr int RED = PB;                             // [wave][head][ch] fp32
-  static constexpr int RED_M = RED + 4 * G * kHeadDim * 4;   // [wave][GP] fp32
-  static constexpr int RED_L = RED_M + 4 * 4 * GP;
-  static constexpr int TOTAL = RED_L + 4 * 4 * GP;
+  static constexpr int NT = G > 4 ? 2 : 1;                    // head tiles of four heads
+  static constexpr int NA = NT * NG;                          // fp8 operands per contraction
+  static constexpr int PT = 0;                                // [wave][NA][64][32] bytes
+  static constexpr int RED = PT + 4 * NA * 2048;              // [wave][head][ch] fp32
+  static constexpr int RED_M = RED + 4 * G * kHeadDim * 4;    // [wave][8] fp32
+  static constexpr int RED_L = RED_M + 4 * 8 * 4;
+  static constexpr int TOTAL = RED_L + 4 * 8 * 4;
 };
 
 // STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
@@ -79,124 +102,108 @@ template <int G, int NG, bool STREAM>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
                                            int b, unsigned char* smem) {
   using S = Int2Lds<G, NG>;
-  constexpr int GP = S::GP;               // padded query heads per KV head
-  constexpr int NACC = GP / 4;            // score accumulators (tokens per lane and page)
-  constexpr int PP = 1;                   // pages per step
+  constexpr int NT = S::NT, NA = S::NA;
   constexpr int BLK = kMetaOff + kPage * 8 * NG;
-  __bf16* pbuf_all = reinterpret_cast<__bf16*>(smem);
   float* red_acc = reinterpret_cast<float*>(smem + S::RED);
-  float (*red_m)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_M);
-  float (*red_l)[GP] = reinterpret_cast<float (*)[GP]>(smem + S::RED_L);
+  float (*red_m)[8] = reinterpret_cast<float (*)[8]>(smem + S::RED_M);
+  float (*red_l)[8] = reinterpret_cast<float (*)[8]>(smem + S::RED_L);
 
   const int p0 = split * p.pages_per_split;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = dev::lane_id();
   const int gq = lane >> 4, n = lane & 15;
   const int head0 = b * p.hq + kv * G;
-  // Table entries of this wave's pages p0 + wave + 4 j, one per lane j (at most 64: a split
-  // covers at most 256 pages), read before the sequence length is known so that the first page
-  // loads wait on one memory round trip only.  The index stays inside the table row; entries of
-  // pages past the sequence's end are read but never used.
-  static_assert(PP == 1 && kMaxPagesPerSplit <= 4 * 64, "one page id per lane and wave");
-  const int wave_ids = a.page_table[static_cast<int64_t>(b) * a.max_pages_per_seq +
-                                    min(p0 + wave + 4 * lane, a.max_pages_per_seq - 1)];
+  // Wave w takes the contiguous pages [w0, w0 + qw) of the item.  Its first eight page ids are
+  // read with scalar loads, before anything else: they return through the scalar cache, not behind
+  // the page streams of the unit's other waves, which a vector load's return would queue after.
+  // Indices stay inside the table row; ids of pages past the sequence's end are read, never used.
+  static_assert((kMaxPagesPerSplit + 3) / 4 <= 8 + 64, "eight scalar ids and one per lane");
+  const int qw = (p.pages_per_split + 3) >> 2;
+  const int w0 = p0 + wave * qw;
+  const int* trow = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
+  const int tmax = a.max_pages_per_seq - 1;
+  int ids[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ids[j] = trow[min(w0 + j, tmax)];
   const int L = a.seq_lens[b] + a.len_add;
+  // ids of the wave's pages from the ninth on, one per lane, issued ahead of every page load so
+  // that waiting for it later never waits for those
+  const int more_ids = trow[min(w0 + 8 + lane, tmax)];
+  __builtin_amdgcn_sched_barrier(0);
+  // all of the above are issued before the first wait
+  asm volatile("" ::"s"(ids[0]), "s"(ids[1]), "s"(ids[2]), "s"(ids[3]), "s"(ids[4]),
+               "s"(ids[5]), "s"(ids[6]), "s"(ids[7]), "s"(L));
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
   if (p0 >= n_pages) return;
   const int p1 = min(p0 + p.pages_per_split, n_pages);
+  const int w1 = min(w0 + qw, p1);   // w1 <= w0: a wave without pages (it still combines)
 
-  // ---- query operands (registers, the same for every page).  Score tile rows hold the int8 hi
-  // part of a head's q' and, four rows further, its lo part; GP = 4: operand ts (sub-tiles of
-  // parity ts) fills rows 8 ts .. 8 ts + 7; GP = 8: rows 0..7 hi and 8..15 lo of heads 0..7.  Lane
-  // (k block gq, row n) holds channels [16 gq, 16 gq + 16) of half hf (MFMA operand order).
-  const int8_t* qpack = reinterpret_cast<const int8_t*>(a.workspace + p.off_qrot);
-  const float* qmeta = reinterpret_cast<const float*>(a.workspace + p.off_sigma);
-  v4i qa[GP == 4 ? 2 : 1][2];
-  {
-    const int ts = GP == 4 ? n / 8 : 0;
-    const int hl = GP == 4 ? (n / 4) % 2 : n / 8;
-    const int hd = GP == 4 ? n % 4 : n % 8;
+  // ---- key operands of the query (registers, the same for every page) and, per lane, the sums
+  // of q'' of its head in each tile (head 4 ht + gq; a head the group does not have gets -inf
+  // logits); loaded after the first pages' loads are issued (see the pair loop)
+  const int64_t op0 = (static_cast<int64_t>(b) * p.hkv + kv) * NA;
+  v8i aq[NA];
+  int sq[NA];
+  float sig[NT][NG], hbias[NT];
+  auto load_query = [&]() {
 #pragma unroll
-    for (int t = 0; t < (GP == 4 ? 2 : 1); ++t)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        v4i v = {0, 0, 0, 0};
-        if (t == ts && hd < G)
-          v = *reinterpret_cast<const v4i*>(qpack + static_cast<int64_t>(head0 + hd) * 256 +
-                                            hl * 128 + (hf * 4 + gq) * 16);
-        qa[t][hf] = v;
-      }
-  }
-  // per head-slot constants of this lane: head = hs (GP = 4) or 4 (gq & 1) + hs (GP = 8)
-  float kh[4], sq[4][NG];
-#pragma unroll
-  for (int hs = 0; hs < 4; ++hs) {
-    const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
-    const float* m = qmeta + static_cast<int64_t>(head0 + min(hd, G - 1)) * 4;
-    kh[hs] = hd < G ? m[0] : 0.f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) sq[hs][g] = m[1 + g];
-  }
-  // Combines the per-row results of a 16-lane reduction over the rows holding the same head: all
-  // four rows (GP = 4) or rows r and r ^ 2 (GP = 8), with lane swaps; every lane gets the result.
-  auto head_reduce = [](float v, auto op) {
-    if constexpr (GP == 4) {
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      v = op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));   // rows (0 + 1), (2 + 3)
+    for (int i = 0; i < NA; ++i) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.workspace + p.off_qops +
+                                                        (op0 + i) * 2048 + lane * 32);
+      const uint4 x = src[0], y = src[1];
+      aq[i] = v8i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z),
+                  static_cast<int>(x.w), static_cast<int>(y.x), static_cast<int>(y.y),
+                  static_cast<int>(y.z), static_cast<int>(y.w)};
+      sq[i] = reinterpret_cast<const int32_t*>(a.workspace + p.off_qscale)[(op0 + i) * 64 + lane];
     }
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-  };
-  // token (within a page) of this lane's score vector pa: after the hi / lo lane swap, lane group
-  // gq holds sub-tile (0, 2, 1, 3)[gq] (GP = 4) or sub-tile 2 pa + gq / 2 (GP = 8)
-  auto tok_of = [&](int pa) {
-    return GP == 4 ? 16 * (((gq & 1) << 1) | (gq >> 1)) + n : 16 * (2 * pa + (gq >> 1)) + n;
-  };
-  // position of a token in a P row; value operands read 8 consecutive entries per lane, which
-  // hold tokens 8 k + {0, 2, 4, 6, 1, 3, 5, 7}
-  auto ppos = [](int t) { return (t & ~7) | ((t & 7) >> 1) | ((t & 1) << 2); };
-  auto pbuf = [&](int pp, int g, int row) -> __bf16* {
-    return pbuf_all + ((((wave * PP + pp) * NG + g) * 16 + row) * kPage);
-  };
-  // rows 2 GP .. 15 of every P tile stay zero (value operands of unused rows): 8 rows x 64
-  // tokens x 2 bytes = 64 lanes x 16 bytes per tile.  The tiles are the wave's own and LDS
-  // operations of one wave execute in order, so no barrier is needed before the page loop.
-  if constexpr (2 * GP == 8) {
+    const float* qmeta = reinterpret_cast<const float*>(a.workspace + p.off_sigma);
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
+    for (int ht = 0; ht < NT; ++ht) {
+      const int hd = 4 * ht + gq;
+      const float* m = qmeta + static_cast<int64_t>(head0 + min(hd, G - 1)) * 4;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        reinterpret_cast<uint4*>(pbuf(pp, g, 2 * GP))[lane] = make_uint4(0, 0, 0, 0);
-  }
+      for (int g = 0; g < NG; ++g) sig[ht][g] = hd < G ? m[g] : 0.f;
+      hbias[ht] = hd < G ? 0.f : -INFINITY;
+    }
+  };
 
-  float m_ref[4], m_lim[4], l_run[4], z_run[4][NG];   // m_lim = m_ref + kRefSpan
-  v4f acc[8];
-  auto reset_sums = [&]() {
+  // ---- this wave's fp8 operand tiles for the values.  The value codes' K order: in the FP4
+  // operand of lane group u, element 8 r + i is the code at position 2 i + (r & 1) of the word of
+  // page r >> 1, i.e. token 16 s + 4 u + j with s = i & 3, j = 2 (i >> 2) + (r & 1).  So the fp8
+  // operand's four consecutive bytes 16 (u >> 1) + 8 (j & 1) + 4 (j >> 1) + s, s = 0..3, of lane
+  // 16 (2 (u & 1) + P) + 4 g + pt (row: head g, part pt) hold part pt of the four sub-tiles of
+  // token 4 u + j of page P -- the four logits lane (g, n = 4 u + j) holds: one dword store per
+  // (page, part).
+  uint8_t* ptile = smem + S::PT + wave * NA * 2048;
+  uint8_t* pbase = ptile + (32 * ((n >> 2) & 1) + 4 * gq) * 32 + 16 * (n >> 3) + 8 * (n & 1) +
+                   4 * ((n >> 1) & 1);
+  // E8M0 row scales of the value operand come from the row's head, whose reference lives in
+  // lane group (lane & 15) >> 2
+  const int src_lane4 = 4 * 16 * ((lane & 15) >> 2);
+  const int row_part = lane & 3;
+
+  float m_ref[NT], l_run[NT], z_run[NT][NG];
+  v4f acc[NT][8];
 #pragma unroll
-    for (int hs = 0; hs < 4; ++hs) {
-      l_run[hs] = 0.f;
+  for (int ht = 0; ht < NT; ++ht) {
+    m_ref[ht] = -INFINITY;   // a wave without pages leaves -inf (its partial weighs nothing)
+    l_run[ht] = 0.f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) z_run[hs][g] = 0.f;
-    }
+    for (int g = 0; g < NG; ++g) z_run[ht][g] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
-  };
-#pragma unroll
-  for (int hs = 0; hs < 4; ++hs) {
-    m_ref[hs] = -INFINITY;   // a wave without pages leaves -inf (its partial weighs nothing)
-    m_lim[hs] = -INFINITY;
+    for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  reset_sums();
 
   // One page's operands, fetched with 16-byte loads from the tiled block (one chunk row = 64 lanes
   // x 16 bytes): key chunk row j holds this lane's words of sub-tiles 2j and 2j + 1, value chunk
-  // row j those of channel tiles 4j .. 4j + 3; the meta of a token is (key pairs, value pairs).
+  // row j those of channel tiles 4j .. 4j + 3; m[st]: the meta of token 16 st + n, the token whose
+  // logits the lane holds in sub-tile st (key groups, then value groups; the four lanes of one n
+  // read the same bytes).
   struct PageRegs {
-    uint4 k[2];              // k[st / 2] entry 2 (st % 2) + hf: key codes, sub-tile st, half hf
-    uint4 v[2];              // v[nt / 4] entry nt % 4: value codes, channel 16 nt + n
-    uint32_t km[NACC][NG];   // key meta (scale | zero << 16) of the lane's token(s)
-    uint32_t vm[NACC][NG];
+    uint4 k[2];
+    uint4 v[2];
+    uint32_t m[4][2 * NG];
   };
   auto kword = [](const PageRegs& r, int st, int hf) {
     const uint4& c = r.k[st >> 1];
@@ -208,336 +215,337 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     const int e = nt & 3;
     return e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
   };
-  auto load_page = [&](int pg, PageRegs& r) {
-    // lane (pg - p0 - wave) / 4 holds page pg's id; a clamped prefetch index p1 - 1 maps to the
-    // wave's last page below p1 (floor division), whose id is valid
-    const int pid = __builtin_amdgcn_readlane(wave_ids, (pg - p0 - wave) >> 2);
-    const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
-    const uint4* kc = reinterpret_cast<const uint4*>(blk + kKCodesOff);
-    const uint4* vc = reinterpret_cast<const uint4*>(blk + kVCodesOff);
-    auto ld = [](const auto* q) { return STREAM ? dev::load_stream(q) : *q; };
-    r.k[0] = ld(&kc[lane]);
-    r.k[1] = ld(&kc[64 + lane]);
-    r.v[0] = ld(&vc[lane]);
-    r.v[1] = ld(&vc[64 + lane]);
+  // the first eight ids in lanes 0..7 of one register (no memory wait: written from the scalars)
+  int first_ids = ids[0];
 #pragma unroll
-    for (int pa = 0; pa < NACC; ++pa) {
-      // The meta region lies past the immediate-offset range of a global load, and a global
-      // load there takes a per-page 64-bit vector address whose register makes the next page's
-      // loads wait for every load in flight; a buffer load over the block takes the block
-      // address in scalar registers and the lane's offset in one loop-invariant register.
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, BLK, kBufferWord3);
-      const int moff = kMetaOff + tok_of(pa) * 8 * NG;
-      if (NG == 1) {
-        const uint2 w = dev::to_uint2(__builtin_amdgcn_raw_buffer_load_b64(rs, moff, 0, STREAM ? kNonTemporal : 0));
-        r.km[pa][0] = w.x;
-        r.vm[pa][0] = w.y;
+  for (int j = 1; j < 8; ++j) first_ids = lane == j ? ids[j] : first_ids;
+  auto page_id = [&](int pg) {
+    const int j = pg - w0;
+    if (j < 8) return __builtin_amdgcn_readlane(first_ids, j);
+    return __builtin_amdgcn_readlane(more_ids, j - 8);
+  };
+  // Buffer loads over the page's block: the block address in scalar registers, the lane's
+  // offsets in loop-invariant registers.  A slot past the wave's pages (a clamped prefetch index)
+  // gets a zero-length range, so its loads return zeros without touching memory and every round
+  // still issues the same loads.
+  auto load_page = [&](int pg, PageRegs& r) {
+    const int pid = page_id(min(pg, w1 - 1));
+    const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(blk), 0, pg < w1 ? BLK : 0, kBufferWord3);
+    const int cp = STREAM ? kNonTemporal : 0;
+    r.k[0] = dev::to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, kKCodesOff + lane * 16, 0, cp));
+    r.k[1] = dev::to_uint4(
+        __builtin_amdgcn_raw_buffer_load_b128(rs, kKCodesOff + 1024 + lane * 16, 0, cp));
+    r.v[0] = dev::to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, kVCodesOff + lane * 16, 0, cp));
+    r.v[1] = dev::to_uint4(
+        __builtin_amdgcn_raw_buffer_load_b128(rs, kVCodesOff + 1024 + lane * 16, 0, cp));
+    const int moff = kMetaOff + n * 8 * NG;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if constexpr (NG == 1) {
+        const uint2 w = dev::to_uint2(
+            __builtin_amdgcn_raw_buffer_load_b64(rs, moff + st * 16 * 8 * NG, 0, cp));
+        r.m[st][0] = w.x;
+        r.m[st][1] = w.y;
       } else {
-        const uint4 w = dev::to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, moff, 0, STREAM ? kNonTemporal : 0));
-        r.km[pa][0] = w.x;
-        r.km[pa][NG - 1] = w.y;
-        r.vm[pa][0] = w.z;
-        r.vm[pa][NG - 1] = w.w;
+        const uint4 w = dev::to_uint4(
+            __builtin_amdgcn_raw_buffer_load_b128(rs, moff + st * 16 * 8 * NG, 0, cp));
+        r.m[st][0] = w.x;
+        r.m[st][1] = w.y;
+        r.m[st][2] = w.z;
+        r.m[st][3] = w.w;
       }
     }
+  };
+  // pair q: pages w0 + 2 q and w0 + 2 q + 1
+  auto load_pair = [&](int q, PageRegs* rr) {
+    load_page(w0 + 2 * q, rr[0]);
+    load_page(w0 + 2 * q + 1, rr[1]);
   };
 
-  // Per-page work in two parts: the logits (with the value scales and zero points they come
-  // with), then probabilities and values.  Pages pg .. pg + PP - 1 are on register sets
-  // r[0 .. PP - 1]; pages past p1 contribute nothing.
-  struct Scores {
-    float logit[PP][NACC][4];
-    float vs[PP][NACC][NG], vz[PP][NACC][NG];
-  };
-  auto page_scores = [&](int pg, const PageRegs* r, Scores& so) {
-    // ---- scores: exact int32 tiles of hi and lo dot products, then one lane swap per register
-    // puts hi and lo of the same token in one lane: S = 256 hi + lo
-    constexpr int NT = GP == 4 ? 2 : 4;
-    int sc[PP][NACC][NG][4];
+  // ---- one pair of pages
+  auto process_pair = [&](int q, PageRegs* rr, bool first) {
+    const int pgs[2] = {w0 + 2 * q, w0 + 2 * q + 1};
+    // a slot past the history (or a page past the wave's range) holds arbitrary bytes: its meta
+    // becomes zero (no value contribution, finite products) and its logit -inf
+    const bool tail = pgs[1] >= w1 || (pgs[1] + 1) * kPage > n_hist;
+    if (tail) {
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp) {
-      v4i dt[NG][NT];
+      for (int P = 0; P < 2; ++P)
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+        for (int st = 0; st < 4; ++st) {
+          const bool ok = pgs[P] < w1 && pgs[P] * kPage + 16 * st + n < n_hist;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) dt[g][t] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int g = NG == 2 ? hf : 0;
-          const uint32_t w = kword(r[pp], st, hf);
-          const v4i bk = {static_cast<int>(w & 0x03030303u),
-                          static_cast<int>((w >> 2) & 0x03030303u),
-                          static_cast<int>((w >> 4) & 0x03030303u),
-                          static_cast<int>((w >> 6) & 0x03030303u)};
-          if constexpr (GP == 4)
-            dt[g][st >> 1] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[st & 1][hf], bk, dt[g][st >> 1], 0, 0, 0);
-          else
-            dt[g][st] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][hf], bk, dt[g][st], 0, 0, 0);
+          for (int w = 0; w < 2 * NG; ++w) rr[P].m[st][w] = ok ? rr[P].m[st][w] : 0u;
         }
-#pragma unroll
-      for (int pa = 0; pa < NACC; ++pa)
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int hs = 0; hs < 4; ++hs) {
-            // GP = 4: tiles (sub-tiles 0,1) and (2,3) hold rows [hi, lo, hi, lo] per lane group;
-            // GP = 8: tiles of sub-tiles 2 pa and 2 pa + 1 hold [hi, hi, lo, lo]
-            const uint32_t x = static_cast<uint32_t>(dt[g][GP == 4 ? 0 : 2 * pa][hs]);
-            const uint32_t y = static_cast<uint32_t>(dt[g][GP == 4 ? 1 : 2 * pa + 1][hs]);
-            const auto sw = GP == 4 ? __builtin_amdgcn_permlane16_swap(x, y, false, false)
-                                    : __builtin_amdgcn_permlane32_swap(x, y, false, false);
-            sc[pp][pa][g][hs] = (static_cast<int>(sw[0]) << 8) + static_cast<int>(sw[1]);
-          }
     }
-    bool valid[PP][NACC];
+    // meta of token 16 st + n of page P
+    uint32_t km[2][NG][4], vm[2][NG][4];
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-      for (int pa = 0; pa < NACC; ++pa) {
-        // a slot past the history holds arbitrary bytes: its meta is replaced by zeros (finite
-        // scores, no value contribution) and its logit by -inf
-        valid[pp][pa] = (pg + pp) * kPage + tok_of(pa) < n_hist && pg + pp < p1;
-        float ks[NG], kz[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const uint32_t km = valid[pp][pa] ? r[pp].km[pa][g] : 0u;
-          const uint32_t vm = valid[pp][pa] ? r[pp].vm[pa][g] : 0u;
-          ks[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km & 0xFFFF)));
-          kz[g] = __half2float(__ushort_as_half(static_cast<uint16_t>(km >> 16)));
-          so.vs[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm & 0xFFFF)));
-          so.vz[pp][pa][g] = __half2float(__ushort_as_half(static_cast<uint16_t>(vm >> 16)));
-        }
-        const float bias = valid[pp][pa] ? 0.f : -INFINITY;
-#pragma unroll
-        for (int hs = 0; hs < 4; ++hs) {
-          float t = 0.f;
-#pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            t = fmaf(ks[g], static_cast<float>(sc[pp][pa][g][hs]), fmaf(kz[g], sq[hs][g], t));
-          }
-          so.logit[pp][pa][hs] = fmaf(t, kh[hs], bias);
-        }
-      }
-  };
-  // maximum of head slot hs over the page, the same in every lane holding the head
-  auto page_max = [&](const Scores& so, int hs) {
-    float v = so.logit[0][0][hs];
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-      for (int pa = 0; pa < NACC; ++pa) v = fmaxf(v, so.logit[pp][pa][hs]);
-    return head_reduce(dev::row16_max(v), [](float a, float b) { return fmaxf(a, b); });
-  };
-  auto set_ref = [&](int hs, float m) {
-    m_ref[hs] = m;
-    m_lim[hs] = m + kRefSpan;
-  };
-  // lanes holding a logit past the limit, one ballot per compare
-  auto over_limit = [&](const Scores& so) {
-    uint64_t over = 0;
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-      for (int pa = 0; pa < NACC; ++pa)
-#pragma unroll
-        for (int hs = 0; hs < 4; ++hs)
-          over |= __builtin_amdgcn_ballot_w64(so.logit[pp][pa][hs] > m_lim[hs]);
-    return over;
-  };
-  auto page_values = [&](const PageRegs* r, const Scores& so) {
-    // ---- probabilities, bf16 hi / lo split of p * s_v, transpose through LDS
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-      for (int pa = 0; pa < NACC; ++pa) {
-        const int t = ppos(tok_of(pa));
-#pragma unroll
-        for (int hs = 0; hs < 4; ++hs) {
-          const float pr = __builtin_amdgcn_exp2f(so.logit[pp][pa][hs] - m_ref[hs]);  // 0: invalid slot
-          l_run[hs] += pr;
-          const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
-#pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            z_run[hs][g] = fmaf(pr, so.vz[pp][pa][g], z_run[hs][g]);
-            const float pt = pr * so.vs[pp][pa][g];
-            const __bf16 hi = static_cast<__bf16>(pt);
-            const __bf16 lo = static_cast<__bf16>(pt - static_cast<float>(hi));
-            pbuf(pp, g, hd)[t] = hi;
-            pbuf(pp, g, GP + hd)[t] = lo;
-          }
-        }
-      }
-    // LDS operations of one wave execute in order, so the reads below see the writes above; a
-    // memory fence here would also wait for the next pages' global loads.
-    __builtin_amdgcn_wave_barrier();
-    v8bf pa_op[PP][NG][2];
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
+    for (int P = 0; P < 2; ++P)
 #pragma unroll
       for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pa_op[pp][g][ks] = *reinterpret_cast<const v8bf*>(pbuf(pp, g, n) + 16 * gq + 8 * ks);
-    // ---- values
+        for (int st = 0; st < 4; ++st) {
+          km[P][g][st] = rr[P].m[st][g];
+          vm[P][g][st] = rr[P].m[st][NG + g];
+        }
+    // the pair's largest value scale (positive fp16 bits order like their values): over the
+    // lane's 8 tokens, then over the 16 lanes of its row (each row holds all 128 tokens)
+    uint32_t smax = 0;
+#pragma unroll
+    for (int P = 0; P < 2; ++P)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) smax = max(smax, vm[P][g][st] & 0xFFFFu);
+    smax = max(smax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(smax), 0xB1, 0xF, 0xF, 0)));
+    smax = max(smax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(smax), 0x4E, 0xF, 0xF, 0)));
+    smax = max(smax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(smax), 0x124, 0xF, 0xF, 0)));
+    smax = max(smax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(smax), 0x128, 0xF, 0xF, 0)));
+    int ev = 0;
+    if (smax != 0) frexpf(__half2float(__ushort_as_half(static_cast<uint16_t>(smax))), &ev);
+
+    // ---- logits of head 4 ht + gq for token 16 st + n of page P
+    float lg[NT][2][4];
+#pragma unroll
+    for (int P = 0; P < 2; ++P)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const v8i bk = fp4_operand(kword(rr[P], st, 0), kword(rr[P], st, 1));
+        float sc[NT][NG];
+#pragma unroll
+        for (int ht = 0; ht < NT; ++ht)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const v4f d = mfma_f8_f4(aq[ht * NG + g], bk, v4f{0.f, 0.f, 0.f, 0.f}, sq[ht * NG + g]);
+            sc[ht][g] = (d[0] + d[1]) + (d[2] + d[3]);
+          }
+#pragma unroll
+        for (int ht = 0; ht < NT; ++ht) {
+          float t = hbias[ht];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            t = fmaf(hi_half(km[P][g][st]), sig[ht][g], t);
+            t = fmaf(lo_half(km[P][g][st]), sc[ht][g], t);
+          }
+          lg[ht][P][st] = t;
+        }
+      }
+    if (tail) {
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const bool ok = pgs[P] < w1 && pgs[P] * kPage + 16 * st + n < n_hist;
+#pragma unroll
+          for (int ht = 0; ht < NT; ++ht) lg[ht][P][st] = ok ? lg[ht][P][st] : -INFINITY;
+        }
+    }
+    // ---- the pair's reference per head, and the wave's
+    float mp[NT];
+#pragma unroll
+    for (int ht = 0; ht < NT; ++ht) {
+      float v = lg[ht][0][0];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) v = fmaxf(v, lg[ht][P][st]);
+      v = dev::row16_max(v);
+      mp[ht] = v == -INFINITY ? 0.f : ceilf(v);   // -inf: a head the group does not have
+      if (first) m_ref[ht] = mp[ht];
+    }
+    if (!first) {
+      bool up = false;
+#pragma unroll
+      for (int ht = 0; ht < NT; ++ht) up |= mp[ht] > m_ref[ht] + kRescaleSpan;
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+        for (int ht = 0; ht < NT; ++ht) {
+          const float d = mp[ht] > m_ref[ht] + kRescaleSpan ? m_ref[ht] - mp[ht] : 0.f;
+          const int di = static_cast<int>(d);
+          l_run[ht] = ldexpf(l_run[ht], di);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) z_run[ht][g] = ldexpf(z_run[ht][g], di);
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[ht][nt][i] = ldexpf(acc[ht][nt][i], di);
+          if (mp[ht] > m_ref[ht] + kRescaleSpan) m_ref[ht] = mp[ht];
+        }
+      }
+    }
+    // ---- probabilities against the pair's reference, sums, the value operand parts
+    int sv[NT];
+#pragma unroll
+    for (int ht = 0; ht < NT; ++ht) {
+      const float nb = 8.f - static_cast<float>(ev) - mp[ht];
+      const int dexp = static_cast<int>(mp[ht] - m_ref[ht]) - 8 + ev;   // pair weight 2^dexp
+      const float wgt = ldexpf(1.f, dexp);
+      float lp = 0.f, zp[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) zp[g] = 0.f;
+      float x[NG][2][4];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float pr = __builtin_amdgcn_exp2f(lg[ht][P][st] + nb);   // 0 for -inf
+          lp += pr;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            zp[g] = fmaf(pr, hi_half(vm[P][g][st]), zp[g]);
+            x[g][P][st] = pr * lo_half(vm[P][g][st]);
+          }
+        }
+      l_run[ht] = fmaf(lp, wgt, l_run[ht]);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) z_run[ht][g] = fmaf(zp[g], wgt, z_run[ht][g]);
+      // parts of x, bytes to the tile: part 0 the integer i = rint(x / 16) in [0, 16] (a row of
+      // multiples of one step, which the matrix cores sum exactly), parts 1-3 e4m3 values of the
+      // remainder scaled by 16, 256 and 4096 in the conversion
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        uint8_t* tb = pbase + (ht * NG + g) * 2048;
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+          float r[4];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) r[st] = x[g][P][st];
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            float in[4];
+            if (pt == 0) {
+#pragma unroll
+              for (int st = 0; st < 4; ++st) {
+                in[st] = rintf(r[st] * 0.0625f);
+                r[st] = fmaf(in[st], -16.f, r[st]);
+              }
+            } else {
+#pragma unroll
+              for (int st = 0; st < 4; ++st) in[st] = r[st];
+            }
+            const float div = pt <= 1 ? (pt == 0 ? 1.f : 0.0625f)
+                                      : pt == 2 ? 0.00390625f : 0.000244140625f;
+            v2s w01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, in[0], in[1], div, false);
+            const v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w01, in[2], in[3], div, true);
+            uint32_t pk;
+            __builtin_memcpy(&pk, &w, 4);
+            *reinterpret_cast<uint32_t*>(tb + P * 512 + pt * 32) = pk;   // bytes: st 0..3
+            if (pt == 1 || pt == 2) {
+              const v2f b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<int>(pk), div, false);
+              const v2f b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<int>(pk), div, true);
+              r[0] -= b01[0];
+              r[1] -= b01[1];
+              r[2] -= b23[0];
+              r[3] -= b23[1];
+            }
+          }
+        }
+      }
+      // row scale of this lane's value-operand row (head (lane & 15) >> 2, part lane & 3)
+      const int rd = __builtin_amdgcn_ds_bpermute(src_lane4, dexp);
+      sv[ht] = min(max(127 + rd + (row_part == 0 ? 4 : -4 * row_part), 0), 254);
+    }
+    // LDS operations of one wave execute in order, so the reads below see the writes above
+    __builtin_amdgcn_wave_barrier();
+    v8i pa[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const uint4* src = reinterpret_cast<const uint4*>(ptile + i * 2048 + lane * 32);
+      const uint4 x0 = src[0], x1 = src[1];
+      pa[i] = v8i{static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z),
+                  static_cast<int>(x0.w), static_cast<int>(x1.x), static_cast<int>(x1.y),
+                  static_cast<int>(x1.z), static_cast<int>(x1.w)};
+    }
+    // ---- values: channel tile nt of both pages against the pair's probability parts
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
+      const v8i bv = fp4_operand(vword(rr[0], nt), vword(rr[1], nt));
       const int g = NG == 2 ? nt / 4 : 0;
 #pragma unroll
-      for (int pp = 0; pp < PP; ++pp) {
-        const uint32_t w = vword(r[pp], nt);
-        const uint32_t xs = w & 0x33333333u;          // nibbles: tokens 0, 2, 4, ..., 14
-        const uint32_t ys = (w >> 2) & 0x33333333u;   // nibbles: tokens 1, 3, 5, ..., 15
-        {
-          const v2bf r0 = codes_to_bf16<0>(xs), r1 = codes_to_bf16<1>(xs);
-          const v2bf r2 = codes_to_bf16<0>(ys), r3 = codes_to_bf16<1>(ys);
-          const v8bf bv = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_op[pp][g][0], bv, acc[nt], 0, 0, 0);
-        }
-        {
-          const v2bf r0 = codes_to_bf16<2>(xs), r1 = codes_to_bf16<3>(xs);
-          const v2bf r2 = codes_to_bf16<2>(ys), r3 = codes_to_bf16<3>(ys);
-          const v8bf bv = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_op[pp][g][1], bv, acc[nt], 0, 0, 0);
-        }
-      }
+      for (int ht = 0; ht < NT; ++ht)
+        acc[ht][nt] = mfma_f8_f4(pa[ht * NG + g], bv, acc[ht][nt], sv[ht]);
     }
     __builtin_amdgcn_wave_barrier();
   };
 
-
-  // kDepth register sets used in turn: while one page is processed, the loads of the wave's next
-  // kDepth - 1 pages are in flight.  Prefetch indices are clamped to the last page, so every round
-  // issues the same loads (the wait before a page then never covers a later one's), and the loop
-  // over full rounds has a single exit, so the compiler's wait counts stay exact across it.
-  // The first page of the wave sets the softmax reference; nothing rescales the accumulators
-  // afterwards.  Should a later logit pass the reference by more than 2^kRefSpan, the wave finds
-  // its exact maxima in a scores-only pass and takes its pages again from zero (second attempt,
-  // which cannot pass them).
-  PageRegs r[kDepth][PP];
-  Scores so;
-  auto load_step = [&](int q, PageRegs* rr) {
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp) load_page(min(q + pp, p1 - 1), rr[pp]);
-  };
-  constexpr int WS = 4 * PP;   // page stride of a wave (four waves per block)
-  // Issue priority by the pages a wave has left (including the current one): the arbiter
-  // otherwise favours the older of the two blocks sharing a compute unit throughout, which then
-  // finishes well before the younger one, and the younger one ends its pages alone at one wave
-  // per SIMD.  Waves far from their end run first, so the two blocks finish together.
-  auto set_prio = [&](int pg_now) {
-    const int rem = (p1 - pg_now + WS - 1) / WS;
-    if (rem >= 6)
+  // Pairs of this wave: pages w0 + 2 q and + 1.  Two register sets used in turn: while one pair
+  // is processed, the next pair's loads are in flight.  Every round issues the same loads (slots
+  // past the wave's pages read nothing), so the wait before a pair never covers a later one's,
+  // and the loop over full rounds has a single exit, so the wait counts stay exact.  The query
+  // operands are loaded between the first two pairs' loads: the first pair waits on them and on
+  // its own pages only.
+  const int npairs = w1 > w0 ? (w1 - w0 + 1) / 2 : 0;
+  // Issue priority by the pairs a wave has left: two blocks share a compute unit, and the arbiter
+  // otherwise favours the older one throughout, so the younger one would end its pages alone.
+  auto set_prio = [&](int q) {
+    const int rem = npairs - q;
+    if (rem >= 3)
       __builtin_amdgcn_s_setprio(3);
-    else if (rem >= 4)
-      __builtin_amdgcn_s_setprio(2);
     else if (rem >= 2)
-      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(2);
     else
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(1);
   };
-  for (int attempt = 0; p0 + PP * wave < p1; ++attempt) {
-    int pg = p0 + PP * wave;
-    uint64_t over = 0;
-    set_prio(pg);
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) load_step(pg + k * WS, r[k]);
-    page_scores(pg, r[0], so);
-    if (attempt == 0) {
-#pragma unroll
-      for (int hs = 0; hs < 4; ++hs) set_ref(hs, page_max(so, hs));
+  if (npairs > 0) {
+    PageRegs r0[2], r1[2];
+    set_prio(0);
+    load_pair(0, r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_query();
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair(1, r1);
+    __builtin_amdgcn_sched_barrier(0);
+    process_pair(0, r0, true);
+    int q = 1, rest = npairs - 1;
+    for (; rest >= 2; rest -= 2) {
+      set_prio(q);
+      load_pair(q + 1, r0);
+      process_pair(q, r1, false);
+      ++q;
+      __builtin_amdgcn_sched_barrier(0);
+      set_prio(q);
+      load_pair(q + 1, r1);
+      process_pair(q, r0, false);
+      ++q;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    page_values(r[0], so);
-    pg += WS;
-    int rest = (p1 - pg + WS - 1) / WS;   // pages of the wave after the first
-    for (; rest >= kDepth; rest -= kDepth) {
-#pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
-        set_prio(pg);
-        load_step(pg + (kDepth - 1) * WS, r[k]);
-        page_scores(pg, r[(k + 1) % kDepth], so);
-        over |= over_limit(so);
-        page_values(r[(k + 1) % kDepth], so);
-        pg += WS;
-        // keep the scheduler from pulling a later page's work (and the wait for its loads)
-        // into this one
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    if (rest == 1) {
+      set_prio(q);
+      process_pair(q, r1, false);
     }
-#pragma unroll
-    for (int k = 0; k < kDepth - 1; ++k) {
-      if (k < rest) {
-        set_prio(pg);
-        page_scores(pg, r[(k + 1) % kDepth], so);
-        over |= over_limit(so);
-        page_values(r[(k + 1) % kDepth], so);
-        pg += WS;
-      }
-    }
-    if (over == 0) break;
-    // exact maxima over the wave's pages, then a second attempt from zero
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    for (int q = p0 + PP * wave; q < p1; q += WS) {
-      load_step(q, r[0]);
-      page_scores(q, r[0], so);
-#pragma unroll
-      for (int hs = 0; hs < 4; ++hs) mx[hs] = fmaxf(mx[hs], page_max(so, hs));
-    }
-#pragma unroll
-    for (int hs = 0; hs < 4; ++hs) set_ref(hs, mx[hs]);
-    reset_sums();
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  // ---- finish the wave: l and z summed over the lanes holding each head; each accumulator row
-  // as hi + lo + z.  acc[nt][hs] of lane (gq, n) is tile row 4 gq + hs of channel 16 nt + n, the
-  // rows being [hi | lo] of heads 0-3 (GP = 4) or [hi 0-7 | lo 0-7] (GP = 8), so one swap of lane
-  // groups 0 <-> 1 (GP = 4) or of wave halves (GP = 8) meets each hi row with its lo row.  The
-  // rows go to the wave's own LDS rows [wave][head][ch], apart from every P tile, so a single
-  // barrier orders them before the combine.
-  auto head_sum = [&](float v) {   // over the lanes of one head, as for the max in the page loop
-    return head_reduce(dev::row16_sum(v), [](float a, float b) { return a + b; });
-  };
-  float zs[4][NG];
+  // ---- finish the wave: l and z summed over the 16 lanes of each head; each accumulator row as
+  // the sum of its parts plus z; rows to the wave's own LDS rows [wave][head][ch], apart from
+  // every operand tile, so a single barrier orders them before the combine.
 #pragma unroll
-  for (int hs = 0; hs < 4; ++hs) {
-    const float l = head_sum(l_run[hs]);
+  for (int ht = 0; ht < NT; ++ht) {
+    const int hd = 4 * ht + gq;
+    const float l = dev::row16_sum(l_run[ht]);
+    float zs[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) zs[hs][g] = head_sum(z_run[hs][g]);
-    const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
-    if (n == 0 && gq < GP / 4) {
-      red_m[wave][hd] = m_ref[hs];
-      red_l[wave][hd] = l;
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int hs = 0; hs < 4; ++hs) {
-      const uint32_t x = __float_as_uint(acc[nt][hs]);
-      const auto sw = GP == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
-                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-      acc[nt][hs] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) +   // hi + lo
-                    zs[hs][NG == 2 ? nt / 4 : 0];
-    }
-  if (gq < GP / 4) {
-    float* red_w = red_acc + wave * G * kHeadDim;
-#pragma unroll
-    for (int hs = 0; hs < 4; ++hs) {
-      const int hd = GP == 4 ? hs : 4 * (gq & 1) + hs;
-      if (G % 4 == 0 || hd < G) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) red_w[hd * kHeadDim + 16 * nt + n] = acc[nt][hs];
+    for (int g = 0; g < NG; ++g) zs[g] = dev::row16_sum(z_run[ht][g]);
+    if (hd < G) {
+      if (n == 0) {
+        red_m[wave][hd] = m_ref[ht];
+        red_l[wave][hd] = l;
       }
+      float* red_w = red_acc + (wave * G + hd) * kHeadDim;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        red_w[16 * nt + n] = ((acc[ht][nt][0] + acc[ht][nt][1]) + (acc[ht][nt][2] + acc[ht][nt][3])) +
+                             zs[NG == 2 ? nt / 4 : 0];
     }
   }
   __syncthreads();
   // ---- combine the 4 waves and write this split's partial:
-  // acc'[h][ch] = sum_w f_w (P_hi row + P_lo row + z_w)  with f_w = 2^(m_w - m).  Every wave has
-  // written its rows (a wave without pages: m = -inf, l = 0, zero rows, so f_w = 0), and every
-  // LDS read below is issued before the first one is used.
+  // acc'[h][ch] = sum_w f_w acc_w[h][ch] with f_w = 2^(m_w - m).  Every wave has written its rows
+  // (a wave without pages: m = -inf, l = 0, zero rows, so f_w = 0), and every LDS read below is
+  // issued before the first one is used.
   float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
   float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
   // thread i: head i / 32, channels 4 (i % 32) .. 4 (i % 32) + 3 (one 16-byte store)

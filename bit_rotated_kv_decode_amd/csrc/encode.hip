@@ -23,11 +23,14 @@ using namespace enc;
 constexpr int kWaves = 4;
 
 // ------------------------------------------------------------------------------------------
-// Bulk demotion.  A wave encodes the tokens of one 16-slot run of a page (history indices
-// [16k, 16k + 16) that the call covers) for one (sequence, KV head, K|V).  The 16 slots share the
-// value-code dwords, which a full run writes with plain stores; a partly covered run merges its
-// bits with compare-and-swap.
+// Bulk demotion.  A wave encodes the 16 slots of one value-word group of a page, the slots
+// 16 s + 4 u + j (s, j = 0..3) whose value codes share one word per channel, for one (sequence,
+// KV head, K|V), taking the ones the call covers.  A fully covered group writes its value-code
+// words with plain stores; a partly covered one merges its bits with compare-and-swap.
 constexpr int kRun = 16;
+constexpr int kGroupsPerPage = kPage / kRun;
+
+__device__ __forceinline__ int group_slot(int u, int t) { return 16 * (t >> 2) + 4 * u + (t & 3); }
 
 __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_seq) {
   __shared__ float xs[kWaves][kRun * kHeadDim];
@@ -43,15 +46,21 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
   if (b >= a.batch) return;
 
   const int hs = a.hist_start[b];
-  const int first = (hs / kRun + run) * kRun;   // first history index of this run
-  const int lo = max(first, hs);
-  const int hi = min(first + kRun, hs + a.n_tokens);
-  if (lo >= hi) return;
+  const int first = (hs / kPage + run / kGroupsPerPage) * kPage;   // history index of slot 0
+  const int ug = run % kGroupsPerPage;
+  const int lo = hs, hi = hs + a.n_tokens;
+  bool any = false;
+#pragma unroll
+  for (int t = 0; t < kRun; ++t) {
+    const int idx = first + group_slot(ug, t);
+    any |= idx >= lo && idx < hi;
+  }
+  if (!any) return;
 
   const uint16_t* src = tensor == 0 ? a.k_src : a.v_src;
   float* x = xs[wave];
   for (int t = 0; t < kRun; ++t) {
-    const int idx = first + t;
+    const int idx = first + group_slot(ug, t);
     float v0 = 0.0f, v1 = 0.0f;
     if (idx >= lo && idx < hi) {
       const uint16_t* row = src + b * a.stride_b + static_cast<int64_t>(idx - hs) * a.stride_t +
@@ -76,28 +85,28 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
   const int blk_bytes = block_bytes(a.n_groups);
   uint8_t* blk = page_block(a.pool, a.page_table, a.max_pages_per_seq, b, first, a.hkv, h,
                             blk_bytes);
-  const int slot0 = first % kPage;
   uint32_t vword0 = 0, vword1 = 0, vmask = 0;
 #pragma unroll
   for (int t = 0; t < kRun; ++t) {
     const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups, lv_lo, lv_step);
-    const int idx = first + t;
+    const int slot = group_slot(ug, t);
+    const int idx = first + slot;
     if (idx < lo || idx >= hi) continue;
     if (tensor == 0) {
-      store_key_row(blk, slot0 + t, q.c0, q.c1);
+      store_key_row(blk, slot, q.c0, q.c1);
     } else {
-      vword0 |= q.c0 << (2 * t);
-      vword1 |= q.c1 << (2 * t);
-      vmask |= 3u << (2 * t);
+      const int sh = 2 * v_code_pos(slot);
+      vword0 |= q.c0 << sh;
+      vword1 |= q.c1 << sh;
+      vmask |= 3u << sh;
     }
-    store_meta(blk, tensor, slot0 + t, a.n_groups, q);
+    store_meta(blk, tensor, slot, a.n_groups, q);
   }
   if (tensor == 1) {
-    // value codes of channel j for this run: word (j, slot0 / 16) of the value region
+    // value codes of channel j for this group: word (j, ug) of the value region
     uint32_t* vc = reinterpret_cast<uint32_t*>(blk + kVCodesOff);
-    const int uw = slot0 / kRun;
-    uint32_t* w0 = &vc[v_word_index(lane, uw)];
-    uint32_t* w1 = &vc[v_word_index(lane + 64, uw)];
+    uint32_t* w0 = &vc[v_word_index(lane, ug)];
+    uint32_t* w1 = &vc[v_word_index(lane + 64, ug)];
     if (vmask == 0xFFFFFFFFu) {
       *w0 = vword0;
       *w1 = vword1;
@@ -121,10 +130,9 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 // touches the word during the launch, since a sequence appends one token per call and a page is
 // written by its own sequence only.
 //
-// Query: q' = q R_k for the row's KV head, split for the INT2 pass into int8 hi / lo parts
-// (q' ~ a (hi + lo / 256), a = max |q'| / 127) stored in MFMA operand order, and per row the
-// score scale a / 256 * sm_scale * log2(e) and the per-group sums of the quantised q' (exact, in
-// units of a / 256) that the zero points multiply.
+// Query: q' = q R_k for the row's KV head, scaled by sm_scale * log2(e) and written as the fp8
+// operand of the INT2 pass's key contraction (four parts per channel, E8M0 row scales), with the
+// per-group sums of the represented values that the zero points multiply.
 __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsigned char* smem) {
   float* x = reinterpret_cast<float*>(smem);
   double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(smem + 4 * kHeadDim);
@@ -185,8 +193,10 @@ __device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned
   __syncthreads();
   double r0, r1;
   if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
-  split_query(r0, r1, a.n_groups, a.scale_log2, a.qpack + static_cast<int64_t>(row) * 256,
-              a.qmeta + static_cast<int64_t>(row) * 4);
+  const int b = row / a.hq, hd = (row % a.hq) % a.gqa;
+  const int64_t op = (static_cast<int64_t>(b) * a.hkv + kv) * key_tiles(a.gqa) * a.n_groups;
+  query_operands(r0, r1, a.n_groups, a.gqa, hd, a.scale_log2, a.qops + op * 2048,
+                 a.qscales + op * 64, a.qmeta + static_cast<int64_t>(row) * 4);
 }
 
 // x0 + blockIdx.x < n_query: query row; else append item x0 + blockIdx.x - n_query.
@@ -205,7 +215,8 @@ __global__ __launch_bounds__(256) void prep_kernel(AppendArgs ap, QueryArgs qa, 
 
 hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.n_tokens == 0) return hipSuccess;
-  const int runs_per_seq = (a.n_tokens + kRun - 1) / kRun + 1;
+  // value-word groups of the pages a call can touch: at most ceil(n / 64) + 1 pages
+  const int runs_per_seq = ((a.n_tokens + kPage - 1) / kPage + 1) * kGroupsPerPage;
   const int64_t waves = static_cast<int64_t>(a.batch) * runs_per_seq * a.hkv * 2;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(demote_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a,

@@ -90,8 +90,11 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(batch) * p.hq;
   size_t off = 0;
-  p.off_qrot = off;
-  off = al(off + rows * 2 * kHeadDim);
+  const size_t ops = static_cast<size_t>(batch) * p.hkv * key_tiles(p.gqa) * p.n_groups;
+  p.off_qops = off;
+  off = al(off + ops * 64 * 32);
+  p.off_qscale = off;
+  off = al(off + ops * 64 * 4);
   p.off_sigma = off;
   off = al(off + rows * 4 * 4);
   p.off_int2_ml = off;
@@ -231,10 +234,12 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   qa.u_k = u_k;
   qa.batch = batch;
   qa.hq = plan.hq;
+  qa.hkv = plan.hkv;
   qa.gqa = plan.gqa;
   qa.n_groups = plan.n_groups;
   qa.scale_log2 = a.sm_scale * 1.4426950408889634f;
-  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
+  qa.qops = a.workspace + plan.off_qops;
+  qa.qscales = reinterpret_cast<int32_t*>(a.workspace + plan.off_qscale);
   qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
   return ok();
 }
@@ -527,7 +532,8 @@ oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
   hipError_t e = oscar::scratch_on_current_device(&ws);
   if (e != hipSuccess) return hip_status(e, "oscar_decode_step_noalloc: scratch address");
   a.workspace = static_cast<uint8_t*>(ws);
-  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
+  qa.qops = a.workspace + plan.off_qops;
+  qa.qscales = reinterpret_cast<int32_t*>(a.workspace + plan.off_qscale);
   qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
   a.len_add = 1;   // attention sees the appended token
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -32,12 +32,18 @@ __host__ __device__ inline int block_bytes(int n_groups) {
 // region is 64 lanes x 16 bytes, so that one 16-byte load per lane fetches the words of that lane's
 // MFMA operands.  Key word (token t = 16 st + n, channels 16 w .. 16 w + 15 with w = 4 hf + q):
 // lane 16 q + n of chunk row st / 2, entry 2 (st % 2) + hf.  Value word (channel c = 16 nt + n,
-// tokens 16 u .. 16 u + 15): lane 16 u + n of chunk row nt / 4, entry nt % 4.
+// token group u): lane 16 u + n of chunk row nt / 4, entry nt % 4; it holds the codes of the 16
+// tokens 16 s + 4 u + j (s, j = 0..3), token (s, j) at code position v_code_pos.
 __host__ __device__ inline int k_word_index(int t, int w) {
   return (((t >> 5) * 64 + (w & 3) * 16 + (t & 15)) << 2) + (((t >> 4) & 1) << 1) + (w >> 2);
 }
 __host__ __device__ inline int v_word_index(int c, int u) {
   return (((c >> 6) * 64 + u * 16 + (c & 15)) << 2) + ((c >> 4) & 3);
+}
+// value-code word group and code position of page slot t = 16 s + 4 u + j
+__host__ __device__ inline int v_code_group(int t) { return (t >> 2) & 3; }
+__host__ __device__ inline int v_code_pos(int t) {
+  return 8 * ((t >> 1) & 1) + 2 * (t >> 4) + (t & 1);
 }
 
 // Work plan of one decode-attention call, and the carve-up of its workspace.
@@ -46,8 +52,9 @@ struct Plan {
   int max_pages = 0;         // history pages of the longest sequence
   int pages_per_split = 1;   // history pages per INT2 work item
   int num_splits = 0;        // work items per (sequence, KV head)
-  size_t off_qrot = 0;       // int8 [B][Hq][2][128] rotated queries, hi / lo parts, MFMA order
-  size_t off_sigma = 0;      // fp32 [B][Hq][4] score scale and per-group sums of the query
+  size_t off_qops = 0;       // fp8 key operands [B][Hkv][tiles][groups][64 lanes][32 B]
+  size_t off_qscale = 0;     // int32 E8M0 row scales [B][Hkv][tiles][groups][64 lanes]
+  size_t off_sigma = 0;      // fp32 [B][Hq][4] per-group sums of the rotated, scaled query
   size_t off_int2_ml = 0;    // fp32 [B][Hq][S][2] (m, l) of INT2 partials (log2 domain)
   size_t off_int2_acc = 0;   // fp32 [B][Hq][S][128] rotated-space accumulators
   size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]
@@ -123,11 +130,15 @@ struct DecodeArgs {
 struct QueryArgs {
   const uint16_t* q;      // bf16 [batch][hq][128]
   const float* u_k;
-  int batch, hq, gqa, n_groups;
+  int batch, hq, hkv, gqa, n_groups;
   float scale_log2;       // sm_scale * log2(e)
-  int8_t* qpack;          // workspace: int8 [batch][hq][2][128]
-  float* qmeta;           // workspace: fp32 [batch][hq][4]
+  uint8_t* qops;          // workspace: key operands [batch][hkv][tiles][groups][64][32] (fp8)
+  int32_t* qscales;       // workspace: their E8M0 row scales [batch][hkv][tiles][groups][64]
+  float* qmeta;           // workspace: fp32 [batch][hq][4] per-group sums of the operand's q''
 };
+
+// Key-operand tiles per (sequence, KV head): four query heads per matrix-core tile.
+__host__ __device__ inline int key_tiles(int gqa) { return gqa > 4 ? 2 : 1; }
 
 // ---- paged BF16 baseline: every cached token in a BF16 page block of 64 tokens and one KV head
 // (keys and values, 32 KiB, in matrix-core operand order: see bf16_decode.hip).

@@ -255,13 +255,23 @@ def k_word_index(t, w):
 
 
 def v_word_index(c, u):
-    """Word position of value codes (channel c, tokens 16u .. 16u+15) in the tiled order (reading
+    """Word position of the value-code word (channel c, token group u) in the tiled order (reading
     R8).  With c = 16 nt + n, the word is entry nt mod 4 of the 16-byte chunk of lane 16 u + n in
     1 KiB chunk row nt // 4."""
     c = np.asarray(c)
     u = np.asarray(u)
     nt, n = c // 16, c % 16
     return ((nt // 4) * 64 + 16 * u + n) * 4 + nt % 4
+
+
+def v_code_pos(slot: int):
+    """(token group u, code position 0..15 in the word) of token `slot`'s value codes in the tiled
+    order (reading R8).  With slot = 16 s + 4 u + j, the word of group u holds the 16 tokens
+    16 s' + 4 u + j' (every 16-token tile s', four consecutive tokens of each), the code of
+    (s, j) at position 8 (j // 2) + 2 s + (j mod 2)."""
+    s, n = slot // 16, slot % 16
+    u, j = n // 4, n % 4
+    return u, 8 * (j // 2) + 2 * s + (j % 2)
 
 
 def k_code_bytes(slot: int, geom: Geometry) -> np.ndarray:
@@ -274,13 +284,20 @@ def k_code_bytes(slot: int, geom: Geometry) -> np.ndarray:
 
 
 def v_code_bytes(slot: int, geom: Geometry) -> np.ndarray:
-    """Byte offset, per channel, of the packed value-code byte that holds token `slot` (at bits
-    2 (slot mod 4)); a byte holds tokens 4b .. 4b+3 of its channel."""
+    """Byte offset, per channel, of the packed value-code byte that holds token `slot`'s code (at
+    bits v_code_shift(slot))."""
     c = np.arange(geom.head_dim)
-    tb = slot // 4
     if geom.tiled:
-        return geom.v_codes_off + 4 * v_word_index(c, tb // 4) + tb % 4
-    return geom.v_codes_off + c * (geom.page // 4) + tb
+        u, pos = v_code_pos(slot)
+        return geom.v_codes_off + 4 * v_word_index(c, u) + pos // 4
+    return geom.v_codes_off + c * (geom.page // 4) + slot // 4
+
+
+def v_code_shift(slot: int, geom: Geometry) -> int:
+    """Bit offset of token `slot`'s value code inside its byte (see v_code_bytes)."""
+    if geom.tiled:
+        return 2 * (v_code_pos(slot)[1] % 4)
+    return 2 * (slot % 4)
 
 
 def _meta_bytes(scale16, zero16) -> np.ndarray:
@@ -312,7 +329,7 @@ def store_history(pool, table_row, hist_idx, head, kq, vq, geom: Geometry):
         blk[k_code_bytes(slot, geom)] = kpacked[n]
         # value codes: channel j's codes for the page's tokens are packed along tokens
         byte = v_code_bytes(slot, geom)
-        shift = 2 * (slot % 4)
+        shift = v_code_shift(slot, geom)
         blk[byte] = (blk[byte] & np.uint8(~(3 << shift) & 0xFF)) | (vc[n].astype(np.uint8) << shift)
         m0 = geom.meta_off + slot * geom.meta_bytes_per_token
         blk[m0: m0 + msz] = kmeta[n]
@@ -336,7 +353,7 @@ def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
         blk = pool[table_row[t // pg], head]
         slot = t % pg
         kc[t] = unpack_codes(blk[k_code_bytes(slot, geom)])
-        vc[t] = (blk[v_code_bytes(slot, geom)] >> (2 * (slot % 4))) & 3
+        vc[t] = (blk[v_code_bytes(slot, geom)] >> v_code_shift(slot, geom)) & 3
         m0 = geom.meta_off + slot * geom.meta_bytes_per_token
         km = blk[m0: m0 + msz].view("<f2").reshape(ng, 2)
         vm = blk[m0 + msz: m0 + 2 * msz].view("<f2").reshape(ng, 2)

@@ -294,7 +294,7 @@ def _token(blk, slot, tensor, g):
         codes = np.stack([(row >> (2 * i)) & 3 for i in range(4)], -1).reshape(-1)
     else:
         byte = blk[oracle.v_code_bytes(slot, g)]
-        codes = (byte >> (2 * (slot % 4))) & 3
+        codes = (byte >> oracle.v_code_shift(slot, g)) & 3
     meta = blk[m0: m0 + 4 * ng]
     m = np.frombuffer(meta.tobytes(), dtype="<f2").reshape(ng, 2)
     return codes.astype(np.uint8), m[:, 0].copy(), m[:, 1].copy()

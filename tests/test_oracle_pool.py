@@ -42,9 +42,10 @@ def test_hand_worked_tiled_order():
     # 37 = 16*2 + 5 (st 2, n 5); 103 = 16*6 + 4*1 + 3 (word 6 = 4*1 + 2, byte 1, bits 6..7)
     # -> chunk row 1, lane 16*2 + 5 = 37, entry 2*0 + 1 = 1: word 4*(64 + 37) + 1 = 405,
     # byte 4*405 + 1 = 1621, value 2 << 6.
-    # Value code 3 at token 50, channel 77: 50 = 16*3 + 4*0 + 2 (word u 3, byte 0, bits 4..5);
-    # 77 = 16*4 + 13 (nt 4, n 13) -> chunk row 1, lane 16*3 + 13 = 61, entry 0: word
-    # 4*(64 + 61) = 500, byte 2048 + 2000 = 4048, value 3 << 4.
+    # Value code 3 at token 50, channel 77: 50 = 16*3 + 4*0 + 2 (tile s 3, group u 0, j 2) sits
+    # at code position 8*1 + 2*3 + 0 = 14 of word (77, u 0), i.e. byte 3, bits 4..5;
+    # 77 = 16*4 + 13 (nt 4, n 13) -> chunk row 1, lane 16*0 + 13 = 13, entry 0: word
+    # 4*(64 + 13) = 308, byte 2048 + 4*308 + 3 = 3283, value 3 << 4.
     g = oracle.Geometry()
     assert g.tiled and (g.v_codes_off, g.meta_off, g.block_bytes) == (2048, 4096, 4608)
     assert oracle.k_word_index(37, 6) == 405 and oracle.v_word_index(77, 3) == 500
@@ -59,13 +60,17 @@ def test_hand_worked_tiled_order():
                          (vc, zero, zero), g)
     blk = pool[0, 0]
     nz = np.nonzero(blk)[0].tolist()
-    assert nz == [1621, 4048]
-    assert blk[1621] == 2 << 6 and blk[4048] == 3 << 4
+    assert oracle.v_word_index(77, 0) == 308 and oracle.v_code_pos(50) == (0, 14)
+    assert nz == [1621, 3283]
+    assert blk[1621] == 2 << 6 and blk[3283] == 3 << 4
     # the word orders are permutations of all 512 words of each region
     t, w = np.meshgrid(np.arange(64), np.arange(8), indexing="ij")
     assert sorted(oracle.k_word_index(t, w).ravel().tolist()) == list(range(512))
     c, u = np.meshgrid(np.arange(128), np.arange(4), indexing="ij")
     assert sorted(oracle.v_word_index(c, u).ravel().tolist()) == list(range(512))
+    # the value-code positions of a page's 64 tokens fill the 16 positions of each of 4 words
+    assert sorted(oracle.v_code_pos(t) for t in range(64)) == [(u, p) for u in range(4)
+                                                                for p in range(16)]
     # meta of token 50: key pair at 4096 + 50 * 8, value pair right after
     oracle.store_history(pool, np.array([0], np.int32), [50], 0, (kc[:1], one[:1], zero[:1]),
                          (vc[:1], zero[:1], one[:1]), g)
