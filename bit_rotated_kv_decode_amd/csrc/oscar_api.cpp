@@ -75,11 +75,11 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for one round of two blocks per compute unit: the INT2 pass is bound by memory once two
-  // blocks (eight waves) share a unit, and a grid that leaves some units a third block finishes
-  // when those do.  The INT2 work items share the launch with the BF16 chunk blocks.  At least
-  // one page per wave, within the per-item page and per-head item limits.
-  const long long slots = kInt2Items;
+  // Aim for one round of the blocks a compute unit holds (int2_blocks_per_cu): a grid that leaves
+  // some units one more block finishes when those do.  The INT2 work items share the launch with
+  // the BF16 chunk blocks.  At least one page per wave, within the per-item page and per-head
+  // item limits.
+  const long long slots = static_cast<long long>(kComputeUnits) * int2_blocks_per_cu(p.gqa, p.n_groups);
   const long long bf16_blocks = static_cast<long long>(kBf16Chunks) * batch * p.hkv;
   const long long target = bf16_blocks * 2 <= slots ? slots - bf16_blocks : slots;
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
@@ -118,7 +118,8 @@ Bf16Plan make_bf16_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.max_pages = (std::max(0, max_seq_len) + kPage - 1) / kPage;
   // one round of two blocks per compute unit, as for the INT2 pass; at least one page per wave
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
-  long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
+  const long long slots = 2LL * kComputeUnits;
+  long long pps = std::max<long long>(4, (items + slots - 1) / slots);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;

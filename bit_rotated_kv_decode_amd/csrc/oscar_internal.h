@@ -17,7 +17,13 @@ constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the B
 constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
-constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
+constexpr int kComputeUnits = 256;        // MI355X
+// INT2 attention blocks one compute unit holds: two (eight waves, at most 256 registers each)
+// for up to four query heads per KV head and one group per head; one block (four waves with up
+// to 512 registers) when the wave keeps eight heads' or two groups' operands and accumulators.
+__host__ __device__ constexpr int int2_blocks_per_cu(int gqa, int n_groups) {
+  return gqa > 4 || n_groups > 1 ? 1 : 2;
+}
 
 // Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
 constexpr int kKCodesOff = 0;
