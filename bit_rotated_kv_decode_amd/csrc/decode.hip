@@ -471,14 +471,12 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Pairs of this wave: pages w0 + 2 q and + 1.  SETS register sets used in turn: while one pair
-  // is processed, the next SETS - 1 pairs' loads are in flight (three sets when one block holds
-  // the compute unit and its waves have twice the registers).  Every round issues the same loads
+  // Pairs of this wave: pages w0 + 2 q and + 1.  Two register sets used in turn: while one pair
+  // is processed, the next pair's loads are in flight.  Every round issues the same loads
   // (slots past the wave's pages read nothing), so the wait before a pair never covers a later
   // one's, and the loop over full rounds has a single exit, so the wait counts stay exact.  The
   // query operands are loaded between the first two pairs' loads: the first pair waits on them
   // and on its own pages only.
-  constexpr int SETS = int2_blocks_per_cu(G, NG) == 1 ? 3 : 2;
   const int npairs = w1 > w0 ? (w1 - w0 + 1) / 2 : 0;
   // Issue priority by the pairs a wave has left: two blocks share a compute unit, and the arbiter
   // otherwise favours the older one throughout, so the younger one would end its pages alone.
@@ -492,61 +490,31 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       __builtin_amdgcn_s_setprio(1);
   };
   if (npairs > 0) {
-    PageRegs r0[2], r1[2], r2[2];
+    PageRegs r0[2], r1[2];
     set_prio(0);
     load_pair(0, r0);
     __builtin_amdgcn_sched_barrier(0);
     load_query();
     __builtin_amdgcn_sched_barrier(0);
     load_pair(1, r1);
-    if constexpr (SETS == 3) load_pair(2, r2);
     __builtin_amdgcn_sched_barrier(0);
     process_pair(0, r0, true);
     int q = 1, rest = npairs - 1;
-    if constexpr (SETS == 2) {
-      for (; rest >= 2; rest -= 2) {
-        set_prio(q);
-        load_pair(q + 1, r0);
-        process_pair(q, r1, false);
-        ++q;
-        __builtin_amdgcn_sched_barrier(0);
-        set_prio(q);
-        load_pair(q + 1, r1);
-        process_pair(q, r0, false);
-        ++q;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (rest == 1) {
-        set_prio(q);
-        process_pair(q, r1, false);
-      }
-    } else {
-      // at the top of a round pairs q (r1) and q + 1 (r2) are loaded or in flight
-      for (; rest >= 3; rest -= 3) {
-        set_prio(q);
-        load_pair(q + 2, r0);
-        process_pair(q, r1, false);
-        ++q;
-        __builtin_amdgcn_sched_barrier(0);
-        set_prio(q);
-        load_pair(q + 2, r1);
-        process_pair(q, r2, false);
-        ++q;
-        __builtin_amdgcn_sched_barrier(0);
-        set_prio(q);
-        load_pair(q + 2, r2);
-        process_pair(q, r0, false);
-        ++q;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (rest >= 1) {
-        set_prio(q);
-        process_pair(q, r1, false);
-      }
-      if (rest == 2) {
-        set_prio(q + 1);
-        process_pair(q + 1, r2, false);
-      }
+    for (; rest >= 2; rest -= 2) {
+      set_prio(q);
+      load_pair(q + 1, r0);
+      process_pair(q, r1, false);
+      ++q;
+      __builtin_amdgcn_sched_barrier(0);
+      set_prio(q);
+      load_pair(q + 1, r1);
+      process_pair(q, r0, false);
+      ++q;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (rest == 1) {
+      set_prio(q);
+      process_pair(q, r1, false);
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -609,6 +577,10 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     if (jq == 0) reinterpret_cast<float2*>(ml)[prow] = make_float2(mm, l);
   }
 }
+
+// ------------------------------------------------------------------------------------------
+// 2b. the int8 / bf16 INT2 pass (eight-head or two-group tiles)
+#include "int2_i8.h"
 
 // ------------------------------------------------------------------------------------------
 // 3. BF16 segments: one 256-thread block per (64-token chunk, kv head, sequence), launched in the
@@ -746,25 +718,21 @@ __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, f
 // the rest INT2 splits.
 template <int G, int NG>
 constexpr int attn_lds_bytes() {
-  return Int2Lds<G, NG>::TOTAL > Bf16Lds<G>::TOTAL ? Int2Lds<G, NG>::TOTAL : Bf16Lds<G>::TOTAL;
-}
-
-// Blocks per compute unit the kernel is compiled for (its register budget); the work planner
-// sizes the grid with the same count (int2_blocks_per_cu).
-template <int G, int NG>
-constexpr int attn_blocks_per_cu() {
-  return int2_blocks_per_cu(G, NG);
+  constexpr int i2 = int2_fp8_pass(G, NG) ? Int2Lds<G, NG>::TOTAL : Int2LdsI8<G, NG>::TOTAL;
+  return i2 > Bf16Lds<G>::TOTAL ? i2 : Bf16Lds<G>::TOTAL;
 }
 
 template <int G, int NG, bool STREAM>
-__global__ __launch_bounds__(256, (attn_blocks_per_cu<G, NG>())) void attn_kernel(DecodeArgs a, Plan p,
+__global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p,
                                                                     float scale_log2, int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
   const int x = x0 + static_cast<int>(blockIdx.x) / p.hkv, kv = blockIdx.x % p.hkv, b = blockIdx.z;
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
-  else
+  else if constexpr (int2_fp8_pass(G, NG))
     int2_block<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
+  else
+    int2_block_i8<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 // touches the word during the launch, since a sequence appends one token per call and a page is
 // written by its own sequence only.
 //
-// Query: q' = q R_k for the row's KV head, scaled by sm_scale * log2(e) and written as the fp8
-// operand of the INT2 pass's key contraction (four parts per channel, E8M0 row scales), with the
-// per-group sums of the represented values that the zero points multiply.
+// Query: q' = q R_k for the row's KV head, scaled by sm_scale * log2(e) and written as the key
+// operand of the INT2 pass the shape takes: fp8 parts with E8M0 row scales (up to four heads,
+// one group) or int8 hi / lo parts (otherwise), with the per-group sums the zero points multiply.
 __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsigned char* smem) {
   float* x = reinterpret_cast<float*>(smem);
   double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(smem + 4 * kHeadDim);
@@ -193,6 +193,11 @@ __device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned
   __syncthreads();
   double r0, r1;
   if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
+  if (!int2_fp8_pass(a.gqa, a.n_groups)) {
+    split_query(r0, r1, a.n_groups, a.scale_log2, a.qpack + static_cast<int64_t>(row) * 256,
+                a.qmeta + static_cast<int64_t>(row) * 4);
+    return;
+  }
   const int b = row / a.hq, hd = (row % a.hq) % a.gqa;
   const int64_t op = (static_cast<int64_t>(b) * a.hkv + kv) * key_tiles(a.gqa) * a.n_groups;
   query_operands(r0, r1, a.n_groups, a.gqa, hd, a.scale_log2, a.qops + op * 2048,

@@ -245,5 +245,47 @@ __device__ __forceinline__ void query_operands(double r0, double r1, int n_group
   }
 }
 
+// Split of one rotated query (lane l holds channels l and l + 64, fp64) into the INT2 pass's
+// operands: q' ~ a (hi + lo / 256), a = max |q'| / 127, written to dst[0..255] (hi bytes, then lo
+// bytes, each in MFMA operand order: channel j = 16 qd + 4 b + k at byte 16 qd + 4 k + b), and
+// the query meta (a / 256 * scale_log2, then the per-group sums of 256 hi + lo, exact in int32).
+// A whole wave calls this.
+__device__ __forceinline__ void split_query(double r0, double r1, int n_groups, float scale_log2,
+                                            int8_t* dst, float* meta) {
+  const int lane = dev::lane_id();
+  const float f0 = static_cast<float>(r0);   // rotated channel lane
+  const float f1 = static_cast<float>(r1);   // rotated channel lane + 64
+  const float amax = dev::wave_max(fmaxf(fabsf(f0), fabsf(f1)));
+  const float sa = amax > 0.f ? amax / 127.f : 1.f;
+  auto split = [sa](float v, int& hi, int& lo) {
+    hi = static_cast<int>(rintf(v / sa));
+    const float r = fmaf(-static_cast<float>(hi), sa, v);
+    lo = static_cast<int>(fminf(fmaxf(rintf(r * 256.f / sa), -127.f), 127.f));
+  };
+  int h0, l0, h1, l1;
+  split(f0, h0, l0);
+  split(f1, h1, l1);
+  auto opos = [](int j) { return (j >> 4) * 16 + (j & 3) * 4 + ((j >> 2) & 3); };
+  dst[opos(lane)] = static_cast<int8_t>(h0);
+  dst[opos(lane + 64)] = static_cast<int8_t>(h1);
+  dst[128 + opos(lane)] = static_cast<int8_t>(l0);
+  dst[128 + opos(lane + 64)] = static_cast<int8_t>(l1);
+  const int e0 = 256 * h0 + l0, e1 = 256 * h1 + l1;
+  int s0, s1;
+  if (n_groups == 1) {
+    s0 = dev::wave_sum_i(e0 + e1);
+    s1 = 0;
+  } else {
+    s0 = dev::wave_sum_i(e0);
+    s1 = dev::wave_sum_i(e1);
+  }
+  if (lane == 0) {
+    meta[0] = sa / 256.f * scale_log2;
+    meta[1] = static_cast<float>(s0);
+    meta[2] = static_cast<float>(s1);
+    meta[3] = 0.f;
+  }
+}
+
 }  // namespace enc
 }  // namespace oscar

@@ -75,11 +75,10 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.n_groups = kHeadDim / lay.group_size;
   const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
   p.max_pages = (n_hist + kPage - 1) / kPage;
-  // Aim for one round of the blocks a compute unit holds (int2_blocks_per_cu): a grid that leaves
-  // some units one more block finishes when those do.  The INT2 work items share the launch with
-  // the BF16 chunk blocks.  At least one page per wave, within the per-item page and per-head
-  // item limits.
-  const long long slots = static_cast<long long>(kComputeUnits) * int2_blocks_per_cu(p.gqa, p.n_groups);
+  // Aim for one round of two blocks per compute unit: a grid that leaves some units a third
+  // block finishes when those do.  The INT2 work items share the launch with the BF16 chunk
+  // blocks.  At least one page per wave, within the per-item page and per-head item limits.
+  const long long slots = kInt2Items;
   const long long bf16_blocks = static_cast<long long>(kBf16Chunks) * batch * p.hkv;
   const long long target = bf16_blocks * 2 <= slots ? slots - bf16_blocks : slots;
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
@@ -91,6 +90,8 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   const size_t rows = static_cast<size_t>(batch) * p.hq;
   size_t off = 0;
   const size_t ops = static_cast<size_t>(batch) * p.hkv * key_tiles(p.gqa) * p.n_groups;
+  p.off_qrot = off;
+  off = al(off + rows * 256);
   p.off_qops = off;
   off = al(off + ops * 64 * 32);
   p.off_qscale = off;
@@ -118,8 +119,7 @@ Bf16Plan make_bf16_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.max_pages = (std::max(0, max_seq_len) + kPage - 1) / kPage;
   // one round of two blocks per compute unit, as for the INT2 pass; at least one page per wave
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
-  const long long slots = 2LL * kComputeUnits;
-  long long pps = std::max<long long>(4, (items + slots - 1) / slots);
+  long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
@@ -239,6 +239,7 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   qa.gqa = plan.gqa;
   qa.n_groups = plan.n_groups;
   qa.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
   qa.qops = a.workspace + plan.off_qops;
   qa.qscales = reinterpret_cast<int32_t*>(a.workspace + plan.off_qscale);
   qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
@@ -533,6 +534,7 @@ oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
   hipError_t e = oscar::scratch_on_current_device(&ws);
   if (e != hipSuccess) return hip_status(e, "oscar_decode_step_noalloc: scratch address");
   a.workspace = static_cast<uint8_t*>(ws);
+  qa.qpack = reinterpret_cast<int8_t*>(a.workspace + plan.off_qrot);
   qa.qops = a.workspace + plan.off_qops;
   qa.qscales = reinterpret_cast<int32_t*>(a.workspace + plan.off_qscale);
   qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);

@@ -17,12 +17,12 @@ constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the B
 constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
-constexpr int kComputeUnits = 256;        // MI355X
-// INT2 attention blocks one compute unit holds: two (eight waves, at most 256 registers each)
-// for up to four query heads per KV head and one group per head; one block (four waves with up
-// to 512 registers) when the wave keeps eight heads' or two groups' operands and accumulators.
-__host__ __device__ constexpr int int2_blocks_per_cu(int gqa, int n_groups) {
-  return gqa > 4 || n_groups > 1 ? 1 : 2;
+constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
+// The INT2 pass a (query heads per KV head, groups per head) shape takes: the fp8 x FP4 pass for
+// tiles of up to four heads and one group, the int8 / bf16 pass otherwise.  The preparation
+// launch writes the query operand that pass reads.
+__host__ __device__ constexpr bool int2_fp8_pass(int gqa, int n_groups) {
+  return gqa <= 4 && n_groups == 1;
 }
 
 // Byte offsets inside one (page, KV head) block for head_dim 128 (see include/oscar.h).
@@ -58,6 +58,7 @@ struct Plan {
   int max_pages = 0;         // history pages of the longest sequence
   int pages_per_split = 1;   // history pages per INT2 work item
   int num_splits = 0;        // work items per (sequence, KV head)
+  size_t off_qrot = 0;       // int8 [B][Hq][2][128] rotated queries, hi / lo parts (int8 pass)
   size_t off_qops = 0;       // fp8 key operands [B][Hkv][tiles][groups][64 lanes][32 B]
   size_t off_qscale = 0;     // int32 E8M0 row scales [B][Hkv][tiles][groups][64 lanes]
   size_t off_sigma = 0;      // fp32 [B][Hq][4] per-group sums of the rotated, scaled query
@@ -138,9 +139,11 @@ struct QueryArgs {
   const float* u_k;
   int batch, hq, hkv, gqa, n_groups;
   float scale_log2;       // sm_scale * log2(e)
+  int8_t* qpack;          // workspace: int8 [batch][hq][2][128] (int8 pass)
   uint8_t* qops;          // workspace: key operands [batch][hkv][tiles][groups][64][32] (fp8)
   int32_t* qscales;       // workspace: their E8M0 row scales [batch][hkv][tiles][groups][64]
-  float* qmeta;           // workspace: fp32 [batch][hq][4] per-group sums of the operand's q''
+  float* qmeta;           // workspace: fp32 [batch][hq][4]: fp8 pass: per-group sums of the
+                          // operand's q''; int8 pass: score scale, per-group sums of hi / lo
 };
 
 // Key-operand tiles per (sequence, KV head): four query heads per matrix-core tile.
