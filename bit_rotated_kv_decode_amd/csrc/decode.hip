@@ -763,10 +763,13 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ float part_m[8], part_l[8];
   __shared__ __attribute__((aligned(16))) float vec[kHeadDim];
   static_assert(PARTS == 1 || PARTS == kMergeQuarters, "one block per row or per quarter");
-  const int row = blockIdx.x / PARTS;   // b * hq + head
-  const int q0 = blockIdx.x % PARTS;    // first quarter of this block
-  const int b = row / p.hq;
-  const int kv = (row % p.hq) / p.gqa;
+  // blocks numbered (sequence, head in group, quarter, KV head) with the KV head fastest: the
+  // blocks of one KV head (which share its U_v rows) run on one die, as its attention blocks did
+  const int kv = blockIdx.x % p.hkv;
+  const int q0 = (blockIdx.x / p.hkv) % PARTS;   // first quarter of this block
+  const int r = blockIdx.x / p.hkv / PARTS;      // b * gqa + head within the group
+  const int b = r / p.gqa;
+  const int row = b * p.hq + kv * p.gqa + r % p.gqa;   // b * hq + head
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
   const float2* iml = reinterpret_cast<const float2*>(a.workspace + p.off_int2_ml) +

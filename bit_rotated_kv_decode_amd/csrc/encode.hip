@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
 
 // ------------------------------------------------------------------------------------------
 // Step preparation: one 256-thread block per work item.  Items [0, n_query) rotate one query
-// row each (sequence b, query head); the following batch * hkv * 2 items append one new token
-// per (sequence, KV head, K|V).  Both kinds start their U loads before anything else.
+// row each (sequence b, query head); the following batch * 2 * hkv items append one new token
+// per (sequence, K|V, KV head).  Both kinds start their U loads before anything else.
 //
 // Append: the token at position pos goes to the sink (pos < 64) or to ring row pos % 256; once
 // the ring is full the row's previous token (position pos - 256, history index pos - 320) is
@@ -137,9 +137,9 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
   float* x = reinterpret_cast<float*>(smem);
   double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(smem + 4 * kHeadDim);
   const int tid = threadIdx.x;
-  const int tensor = item & 1;
-  const int h = (item >> 1) % a.hkv;
-  const int b = (item >> 1) / a.hkv;
+  const int h = item % a.hkv;
+  const int tensor = (item / a.hkv) & 1;
+  const int b = item / a.hkv / 2;
   // the U slice is read before anything else (it does not depend on the position), so its loads
   // overlap the round trips for the position and the ring row
   dev::URows ur;
@@ -209,11 +209,16 @@ __global__ __launch_bounds__(256) void prep_kernel(AppendArgs ap, QueryArgs qa, 
                                                    int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kHeadDim +
                                                            dev::kRotGroups * 8 * kHeadDim];
+  // Items are numbered with the KV head fastest: consecutive blocks go to the eight dies in turn,
+  // so the items of one KV head (which share its U) run on one die, as do that head's attention
+  // blocks (block x of the attention grid serves KV head x mod Hkv).
   const int item = x0 + blockIdx.x;
-  if (item < n_query)
-    query_item(qa, item, smem);
-  else
+  if (item < n_query) {
+    const int kv = item % qa.hkv, r = item / qa.hkv;
+    query_item(qa, (r / qa.gqa) * qa.hq + kv * qa.gqa + r % qa.gqa, smem);
+  } else {
     append_item(ap, item - n_query, smem);
+  }
 }
 
 }  // namespace
