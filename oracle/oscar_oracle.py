@@ -51,12 +51,18 @@ Readings taken where the pages are silent:
       eigenvectors of (S V)^T (S V) with S = softmax(Q K^T / sqrt(d)) ([W1] §OSCAR 的设计 names the
       two covariances); eigenvectors in descending eigenvalue order, each column's largest-magnitude
       entry made positive; clip = a percentile of |x R|.
-  R19 (analysis only, not on the GPU path) a Lloyd-Max codebook keeps R5's scale and zero and
-      replaces the grid {0, 1, 2, 3} by four levels fitted by Lloyd's algorithm (``lloyd_max``).
+  R19 a Lloyd-Max codebook keeps R5's scale and zero and replaces the grid {0, 1, 2, 3} by four
+      levels fitted by Lloyd's algorithm (``lloyd_max``); codes name the nearest level (a value
+      halfway takes the lower code) and decode to s * level + z (``quantize_codebook``,
+      ``dequantize_codebook``; ``demote`` / ``append`` / ``decode_attention`` take per-KV-head
+      levels as ``codebook_k`` / ``codebook_v``).
   R20 the Lloyd-Max codebook restricted to equally spaced levels lo + step * c in the same
       coordinate (``lloyd_max_uniform``): the same as storing scale' = s * step and zero' =
       z + s * lo with R5's codes, so it runs on the GPU path unchanged past the encoder
       (``quantize(..., levels=(lo, step))``).
+  R21 the Lloyd-Max codebook restricted to levels symmetric about 1.5, (l0, l1, 3 - l1, 3 - l0)
+      (``lloyd_max_symmetric``, ``symmetric_levels``): the codebooks the GPU path decodes, since
+      such levels are a + b c + d (c >> 1) in the code's bits.
 """
 from __future__ import annotations
 
@@ -366,25 +372,33 @@ def load_history(pool, table_row, n_hist: int, head, geom: Geometry):
 # the demotion step and the decode-step write ([W1] §OSCAR 的设计; reading R9)
 
 def demote(pool, page_table, u_k, u_v, clip_k, clip_v, k_src, v_src, hist_start,
-           geom: Geometry, levels_k=None, levels_v=None):
+           geom: Geometry, levels_k=None, levels_v=None, codebook_k=None, codebook_v=None):
     """Encode tokens k_src / v_src (B, n, Hkv, d) and store them at history indices
     hist_start[b] + i.  levels_k / levels_v: None (uniform grid) or (lo, step) per KV head
-    (reading R20).  Modifies ``pool`` in place."""
+    (reading R20); codebook_k / codebook_v: None or four sorted levels per KV head (reading R19),
+    exclusive with levels.  Modifies ``pool`` in place."""
     k_src = np.asarray(k_src, dtype=np.float64)
     v_src = np.asarray(v_src, dtype=np.float64)
     bsz, n, hkv, _ = k_src.shape
+
+    def enc(x, u, clip, lv, cb):
+        if cb is not None:
+            return quantize_codebook(rotate_to_fp32(x, u), clip, geom.group, cb)
+        return encode(x, u, clip, geom.group, lv)[:3]
+
     for b in range(bsz):
         idx = int(hist_start[b]) + np.arange(n)
         for h in range(hkv):
-            kq = encode(k_src[b, :, h], u_k[h], clip_k[h], geom.group,
-                        None if levels_k is None else levels_k[h])[:3]
-            vq = encode(v_src[b, :, h], u_v[h], clip_v[h], geom.group,
-                        None if levels_v is None else levels_v[h])[:3]
+            kq = enc(k_src[b, :, h], u_k[h], clip_k[h], None if levels_k is None else levels_k[h],
+                     None if codebook_k is None else codebook_k[h])
+            vq = enc(v_src[b, :, h], u_v[h], clip_v[h], None if levels_v is None else levels_v[h],
+                     None if codebook_v is None else codebook_v[h])
             store_history(pool, page_table[b], idx, h, kq, vq, geom)
 
 
 def append(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_k, clip_v,
-           k_new, v_new, seq_slot, seq_lens, geom: Geometry, levels_k=None, levels_v=None):
+           k_new, v_new, seq_slot, seq_lens, geom: Geometry, levels_k=None, levels_v=None,
+           codebook_k=None, codebook_v=None):
     """One decode-step write (reading R9).  seq_lens[b] is the length before the append, i.e. the
     position P of the new token.  P < sink: the token goes to the sink.  Otherwise it goes to
     recent-window ring slot P % recent, and when P >= sink + recent the token it replaces
@@ -402,7 +416,8 @@ def append(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, clip_
             old_k = np.asarray(recent_k[slot, :, r], dtype=np.float64)[None, None]
             old_v = np.asarray(recent_v[slot, :, r], dtype=np.float64)[None, None]
             demote(pool, page_table[b:b + 1], u_k, u_v, clip_k, clip_v, old_k, old_v,
-                   [pos - geom.sink - geom.recent], geom, levels_k, levels_v)
+                   [pos - geom.sink - geom.recent], geom, levels_k, levels_v, codebook_k,
+                   codebook_v)
         recent_k[slot, :, r] = k_new[b]
         recent_v[slot, :, r] = v_new[b]
 
@@ -425,16 +440,23 @@ def recent_slots(length: int, geom: Geometry) -> np.ndarray:
 
 
 def gather_cache(pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v, slot, b, kv,
-                 length: int, geom: Geometry):
+                 length: int, geom: Geometry, codebook_k=None, codebook_v=None):
     """All cached keys and values of one (sequence, KV head) in fp64, unrotated: sink tokens,
-    then history tokens dequantised in rotated space and mapped back by R^T, then recent tokens."""
+    then history tokens dequantised in rotated space and mapped back by R^T, then recent tokens.
+    codebook_k / codebook_v: None (codes are the uniform grid) or four levels per KV head (R19)."""
     n_sink, n_hist, _ = segment_lengths(length, geom)
     ks = [np.asarray(sink_k[slot, kv, :n_sink], dtype=np.float64)]
     vs = [np.asarray(sink_v[slot, kv, :n_sink], dtype=np.float64)]
     if n_hist:
         (kc, kS, kZ), (vc, vS, vZ) = load_history(pool, page_table[b], n_hist, kv, geom)
-        ks.append(unrotate(dequantize(kc, kS, kZ, geom.group), u_k[kv]))
-        vs.append(unrotate(dequantize(vc, vS, vZ, geom.group), u_v[kv]))
+
+        def deq(c, sc, z, cb):
+            if cb is None:
+                return dequantize(c, sc, z, geom.group)
+            return dequantize_codebook(c, sc, z, geom.group, cb[kv])
+
+        ks.append(unrotate(deq(kc, kS, kZ, codebook_k), u_k[kv]))
+        vs.append(unrotate(deq(vc, vS, vZ, codebook_v), u_v[kv]))
     rs = recent_slots(length, geom)
     ks.append(np.asarray(recent_k[slot, kv, rs], dtype=np.float64))
     vs.append(np.asarray(recent_v[slot, kv, rs], dtype=np.float64))
@@ -451,11 +473,13 @@ def attend(q, keys, values, sm_scale: float):
 
 
 def decode_attention(pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot, seq_lens,
-                     q, u_k, u_v, geom: Geometry, sm_scale=None, heads=None):
+                     q, u_k, u_v, geom: Geometry, sm_scale=None, heads=None, codebook_k=None,
+                     codebook_v=None):
     """Decode attention of q (B, Hq, d) over each sequence's three-segment cache.
 
     Returns (out fp64 (B, Hq, d), lse fp64 (B, Hq)); ``heads`` optionally restricts the work to a
-    list of (b, q_head) pairs (other rows stay NaN)."""
+    list of (b, q_head) pairs (other rows stay NaN); codebook_k / codebook_v as for
+    ``gather_cache``."""
     q = np.asarray(q, dtype=np.float64)
     bsz, hq, d = q.shape
     hkv = np.asarray(u_k).shape[0]
@@ -471,7 +495,7 @@ def decode_attention(pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_s
         if (b, kv) not in cache:
             cache = {(b, kv): gather_cache(pool, page_table, sink_k, sink_v, recent_k, recent_v,
                                            u_k, u_v, int(seq_slot[b]), b, kv, int(seq_lens[b]),
-                                           geom)}
+                                           geom, codebook_k, codebook_v)}
         keys, values = cache[(b, kv)]
         out[b, h], lse[b, h] = attend(q[b, h], keys, values, sm_scale)
     return out, lse
@@ -682,6 +706,42 @@ def lloyd_max_uniform(values, weights=None, lo: float = 0.0, step: float = 1.0,
             step = float(np.sum(w * (c - mc) * (x - mx)) / wt / var)
             lo = float(mx - step * mc)
     return lo, step, history
+
+
+def symmetric_levels(l0: float, l1: float) -> np.ndarray:
+    """The four levels (l0, l1, 3 - l1, 3 - l0) of a codebook symmetric about 1.5 (reading R21)."""
+    return np.array([l0, l1, 3.0 - l1, 3.0 - l0], dtype=np.float64)
+
+
+def lloyd_max_symmetric(values, weights=None, l0: float = 0.0, l1: float = 1.0,
+                        iters: int = 100):
+    """Lloyd's algorithm restricted to codebooks symmetric about 1.5 (reading R21): levels
+    (l0, l1, 3 - l1, 3 - l0).  Each step applies the two conditions within that family: every
+    value takes the nearest level (thresholds (l0 + l1) / 2, 1.5 and their mirror; a value halfway
+    takes the lower code), then l0 (l1) is the least-squares level of cell 0 (1) together with the
+    mirror images 3 - t of cell 3 (2) -- the centroid of the pair of cells that share it.  A pair
+    with no weight keeps its level.  Returns (levels (4,), thresholds (3,), distortion before each
+    update and after the last one)."""
+    x = np.asarray(values, dtype=np.float64).ravel()
+    w = np.ones_like(x) if weights is None else np.asarray(weights, dtype=np.float64).ravel()
+    history = []
+    for it in range(iters + 1):
+        lv = symmetric_levels(l0, l1)
+        thr = (lv[:-1] + lv[1:]) / 2
+        cell = np.searchsorted(thr, x, side="left")
+        history.append(float(np.sum(w * (x - lv[cell]) ** 2) / np.sum(w)))
+        if it == iters:
+            break
+        new = []
+        for lo_c, hi_c, cur in ((0, 3, l0), (1, 2, l1)):
+            wl, wh = w[cell == lo_c], w[cell == hi_c]
+            tot = wl.sum() + wh.sum()
+            new.append(cur if tot == 0 else
+                       float((np.sum(wl * x[cell == lo_c]) + np.sum(wh * (3.0 - x[cell == hi_c])))
+                             / tot))
+        l0, l1 = new
+    lv = symmetric_levels(l0, l1)
+    return lv, (lv[:-1] + lv[1:]) / 2, history
 
 
 def codebook_coordinates(xr, clip, group: int) -> np.ndarray:

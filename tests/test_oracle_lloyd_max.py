@@ -175,3 +175,93 @@ def test_equally_spaced_levels_are_a_codebook_on_the_same_coordinate():
     far = np.abs(pre["t"] - np.floor(pre["t"]) - 0.5) > 1e-2
     assert np.array_equal(codes[far], cb[far])
     assert (codes != cb).mean() < 1e-2
+
+
+# ---- the codebook symmetric about 1.5 that the GPU attention runs (reading R21)
+
+def test_symmetric_fit_of_a_centred_gaussian_matches_max_1960():
+    # t ~ N(1.5, 0.5^2): the 4-level Lloyd-Max quantiser of a Gaussian is symmetric, so the
+    # restricted fit reaches Max's levels 1.5 +- 0.5 {0.4528, 1.510} and error 0.25 * 0.1175
+    x = np.linspace(1.5 - 4.0, 1.5 + 4.0, 400001)
+    wgt = np.exp(-(x - 1.5) ** 2 / (2 * 0.25))
+    lv, thr, hist = oracle.lloyd_max_symmetric(x, wgt, l0=0.0, l1=1.0, iters=300)
+    assert np.allclose(lv, 1.5 + 0.5 * np.array([-1.510, -0.4528, 0.4528, 1.510]), atol=4e-4)
+    assert np.allclose(thr, 1.5 + 0.5 * np.array([-0.9816, 0.0, 0.9816]), atol=2e-4)
+    assert hist[-1] == pytest.approx(0.25 * 0.1175, abs=1e-4)
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+
+
+def test_symmetric_fit_of_a_uniform_density():
+    x = np.linspace(0.0, 3.0, 300001)
+    lv, thr, hist = oracle.lloyd_max_symmetric(x, iters=300)
+    assert np.allclose(lv, [0.375, 1.125, 1.875, 2.625], atol=1e-4)
+    assert hist[-1] == pytest.approx(0.75 ** 2 / 12, rel=1e-4)
+
+
+def test_symmetric_fit_agrees_with_the_free_fit_on_mirrored_data():
+    # on a sample closed under t -> 3 - t the free Lloyd iteration started from a symmetric
+    # codebook stays symmetric, so both algorithms walk the same levels
+    # (no sample sits on the middle threshold 1.5, where a tie takes the lower code and would
+    # break the mirror symmetry of the free iteration)
+    r = np.random.default_rng(11)
+    half = r.gamma(2.0, 0.4, 5000)
+    half = half[half < 1.45]
+    t = np.concatenate([half, 3.0 - half])
+    lv_f, _, hist_f = oracle.lloyd_max(t, levels=(0.1, 1.0, 2.0, 2.9), iters=60)
+    lv_s, _, hist_s = oracle.lloyd_max_symmetric(t, l0=0.1, l1=1.0, iters=60)
+    assert np.allclose(lv_f, lv_s, rtol=0, atol=1e-12)
+    assert np.allclose(hist_f, hist_s, rtol=1e-12, atol=0)
+
+
+def test_symmetric_fit_brute_force_on_a_small_mirrored_set():
+    # six points and their mirrors: every symmetric split into four contiguous cells, scored by
+    # the symmetric least-squares levels, has its optimum as a fixed point of the iteration
+    r = np.sort(np.random.default_rng(12).uniform(0, 1.5, 6))
+    t = np.sort(np.concatenate([r, 3.0 - r]))
+    best = None
+    for a in range(1, 6):   # cell 0 = first a points (mirror: cell 3), cell 1 = the rest below 1.5
+        c0, c1 = r[:a], r[a:]
+        l0, l1 = c0.mean(), c1.mean()
+        cost = 2 * (((c0 - l0) ** 2).sum() + ((c1 - l1) ** 2).sum()) / 12
+        if best is None or cost < best[0]:
+            best = (cost, l0, l1)
+    lv, _, hist = oracle.lloyd_max_symmetric(t, l0=best[1], l1=best[2], iters=5)
+    assert np.allclose(lv, oracle.symmetric_levels(best[1], best[2]), rtol=0, atol=1e-15)
+    assert hist[-1] == pytest.approx(best[0], rel=1e-12)
+
+
+def test_symmetric_levels_write_the_codebook_as_bit_planes():
+    # (l0, l1, 3 - l1, 3 - l0) = a + b c + d b1 with a = l0, b = l1 - l0, d = 3 + l0 - 3 l1 and
+    # b1 = c >> 1: the form in which the attention kernel applies the codebook
+    l0, l1 = 0.37, 1.21
+    lv = oracle.symmetric_levels(l0, l1)
+    c = np.arange(4)
+    a, b, d = l0, l1 - l0, 3 + l0 - 3 * l1
+    assert np.allclose(lv, a + b * c + d * (c >> 1), rtol=0, atol=1e-15)
+
+
+def test_grid_codebook_through_demote_and_attention_is_the_plain_path():
+    # the codebook (0, 1, 2, 3) is the uniform grid: demotion writes the same bytes and attention
+    # returns the same outputs as without a codebook (away from halfway points, where the grid
+    # rounds to even and the codebook takes the lower code)
+    g = oracle.Geometry(group=64)
+    rng = np.random.default_rng(5)
+    hkv, n = 2, 150
+    u = np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(hkv)])
+    k = rng.standard_normal((1, n, hkv, 128)).astype(np.float32)
+    v = rng.standard_normal((1, n, hkv, 128)).astype(np.float32)
+    table = np.array([[2, 0, 1]], np.int32)
+    clip = np.full(hkv, 3.5)
+    grid = np.tile(np.arange(4.0), (hkv, 1))
+    p0, p1 = oracle.new_pool(3, hkv, g), oracle.new_pool(3, hkv, g)
+    oracle.demote(p0, table, u, u, clip, clip, k, v, [0], g)
+    oracle.demote(p1, table, u, u, clip, clip, k, v, [0], g, codebook_k=grid, codebook_v=grid)
+    assert np.array_equal(p0, p1)
+    L = n + 320
+    sink = rng.standard_normal((1, hkv, 64, 128)).astype(np.float32)
+    rec = rng.standard_normal((1, hkv, 256, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 4, 128))
+    a = oracle.decode_attention(p0, table, sink, sink, rec, rec, [0], [L], q, u, u, g)
+    b = oracle.decode_attention(p0, table, sink, sink, rec, rec, [0], [L], q, u, u, g,
+                                codebook_k=grid, codebook_v=grid)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
