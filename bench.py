@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--levels", default=None, metavar="LO,STEP",
                     help="demote with an equally spaced codebook (lo, step) on every KV head, "
                          "keys and values (default: the plain grid)")
+    ap.add_argument("--codebook", default=None, metavar="L0,L1",
+                    help="demote with the symmetric codebook (l0, l1, 3 - l1, 3 - l0) on every "
+                         "KV head, keys and values, and attend with its levels")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibration of the HBM byte counters) and exit")
@@ -112,7 +115,7 @@ class Layer:
     pages inside a shared prefix are built once (from the longest sequence) and aliased by the
     page table; every other page is private."""
 
-    def __init__(self, wl, layer, lengths, spare, levels=None):
+    def __init__(self, wl, layer, lengths, spare, levels=None, levels_kind=0):
         dev = "cuda"
         self.lengths = list(lengths)
         B = len(self.lengths)
@@ -120,7 +123,8 @@ class Layer:
         self.table_np, self.num_pages = workloads.page_tables(wl, self.lengths, layer,
                                                               spare_tokens=spare)
         self.lay = ok.make_layout(wl.num_q_heads, hkv, self.num_pages, B,
-                                  self.table_np.shape[1], wl.group_size)
+                                  self.table_np.shape[1], wl.group_size,
+                                  levels_kind=levels_kind)
         self.cache = ok.Cache.allocate(self.lay, zero=False)
         self.table = torch.from_numpy(self.table_np).to(dev)
         # a calibrated U (computed offline from query statistics on the CPU) changes code
@@ -287,8 +291,12 @@ def main():
     dev = "cuda"
 
     t0 = time.time()
-    levels = None if args.levels is None else tuple(float(x) for x in args.levels.split(","))
-    layers = [Layer(wl, i, lengths, total_steps + 8, levels) for i in range(n_layers)]
+    if args.levels is not None and args.codebook is not None:
+        raise SystemExit("--levels and --codebook exclude each other")
+    spec = args.codebook if args.codebook is not None else args.levels
+    levels = None if spec is None else tuple(float(x) for x in spec.split(","))
+    kind = ok.LEVELS_SYMMETRIC if args.codebook is not None else ok.LEVELS_SPACED
+    layers = [Layer(wl, i, lengths, total_steps + 8, levels, kind) for i in range(n_layers)]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] built {n_layers} layer pools in {setup_s:.1f}s", file=sys.stderr, flush=True)
@@ -369,15 +377,23 @@ def main():
         return (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v, slots, lens,
                 Lr.q, Lr.u_k, Lr.u_v, Lr.out, wss[i], max_len)
 
+    def attn(i, stages):
+        a = seg_args(i)
+        if layers[i].lay.levels_kind == ok.LEVELS_SYMMETRIC:
+            ok.decode_attn_codebook(*a[:12], layers[i].levels, layers[i].levels, *a[12:],
+                                    stages=stages)
+        else:
+            ok.decode_attn(*a, stages=stages)
+
     for i in range(len(layers)):
-        ok.decode_attn(*seg_args(i), stages=ok.STAGE_QUERY)
+        attn(i, ok.STAGE_QUERY)
 
     seg_reps = -(-8 // len(layers))
 
     def seg_launches():
         for _ in range(seg_reps):
             for i in range(len(layers)):
-                ok.decode_attn(*seg_args(i), stages=seg)
+                attn(i, seg)
 
     seg_graph = capture(seg_launches)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -441,7 +457,9 @@ def main():
                    "batch": B, "context": lengths[0] if len(set(lengths)) == 1 else
                    [min(lengths), max(lengths)], "layers": n_layers,
                    "launch": "hip-graph" if graph is not None else "eager",
-                   **({"codebook": {"lo": levels[0], "step": levels[1]}} if levels else {})},
+                   **({} if not levels else
+                      {"codebook": {"symmetric_l0_l1": list(levels)}} if kind else
+                      {"codebook": {"lo": levels[0], "step": levels[1]}})},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "step_ms": distribution(step_ms, 4),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

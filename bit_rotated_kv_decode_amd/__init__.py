@@ -49,7 +49,7 @@ class Layout(ctypes.Structure):
 
     _fields_ = [(name, ctypes.c_int32) for name in (
         "head_dim", "group_size", "num_q_heads", "num_kv_heads", "page_tokens", "sink_tokens",
-        "recent_tokens", "num_pages", "max_seqs", "max_pages_per_seq")]
+        "recent_tokens", "num_pages", "max_seqs", "max_pages_per_seq", "levels_kind")]
 
     def __repr__(self):
         return "Layout(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -82,6 +82,9 @@ _SIGNATURES = {
     "oscar_decode_attn_stages": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t,
                                         _i32, _i32, ctypes.c_uint32, _vp]),
+    "oscar_decode_attn_codebook": (_i32, [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                          ctypes.c_size_t, _i32, _i32, ctypes.c_uint32, _vp]),
     "oscar_decode_step": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _vp,
                                                        ctypes.c_size_t, _i32, _i32, _vp]),
     "oscar_decode_step_noalloc": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _i32,
@@ -98,6 +101,7 @@ _SIGNATURES = {
 }
 
 STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
+LEVELS_SPACED, LEVELS_SYMMETRIC = 0, 1
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -125,9 +129,12 @@ def _check(status: int, what: str) -> None:
 
 
 def make_layout(num_q_heads: int, num_kv_heads: int, num_pages: int, max_seqs: int,
-                max_pages_per_seq: int, group_size: int = 128, head_dim: int = HEAD_DIM) -> Layout:
+                max_pages_per_seq: int, group_size: int = 128, head_dim: int = HEAD_DIM,
+                levels_kind: int = 0) -> Layout:
+    """levels_kind: what levels_k / levels_v hold -- 0: (lo, step) of equally spaced codebooks;
+    1: (l0, l1) of Lloyd-Max codebooks symmetric about 1.5 (LEVELS_SYMMETRIC)."""
     lay = Layout(head_dim, group_size, num_q_heads, num_kv_heads, PAGE_TOKENS, SINK_TOKENS,
-                 RECENT_TOKENS, num_pages, max_seqs, max_pages_per_seq)
+                 RECENT_TOKENS, num_pages, max_seqs, max_pages_per_seq, levels_kind)
     _check(lib().oscar_layout_check(ctypes.byref(lay)), "layout")
     return lay
 
@@ -333,6 +340,32 @@ def decode_attn(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
         int(stages), _stream()), "decode_attn")
+
+
+def decode_attn_codebook(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                         seq_slot, seq_lens, q: torch.Tensor, u_k, u_v, levels_k: torch.Tensor,
+                         levels_v: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                         max_seq_len: int, lse: Optional[torch.Tensor] = None,
+                         sm_scale: float = 0.0, stages: int = STAGE_ALL) -> None:
+    """decode_attn over a history encoded with symmetric codebooks (lay.levels_kind 1):
+    levels_k / levels_v fp32 [Hkv, 2] = (l0, l1) per KV head (oscar_decode_attn_codebook)."""
+    bsz = seq_lens.numel()
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
+    _check(lib().oscar_decode_attn_codebook(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_lens, "seq_lens", torch.int32), _contig(q, "q", torch.bfloat16),
+        _contig(u_k, "u_k", torch.float32), _contig(u_v, "u_v", torch.float32),
+        _levels(levels_k, "levels_k", lay), _levels(levels_v, "levels_v", lay), float(sm_scale),
+        _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        int(stages), _stream()), "decode_attn_codebook")
 
 
 def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,

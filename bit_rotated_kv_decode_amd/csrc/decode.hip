@@ -75,6 +75,13 @@ __device__ __forceinline__ v8i fp4_operand(uint32_t w0, uint32_t w1) {
   return v8i{static_cast<int>(w0 & kNibbles), static_cast<int>((w0 >> 2) & kNibbles),
              static_cast<int>(w1 & kNibbles), static_cast<int>((w1 >> 2) & kNibbles), 0, 0, 0, 0};
 }
+// The high bits (c >> 1) of the same 32 codes, in the same element order, as an FP4 operand
+// (a bit b zero-extended to a nibble is the E2M1 value b / 2)
+__device__ __forceinline__ v8i fp4_high_bits(uint32_t w0, uint32_t w1) {
+  constexpr uint32_t kOnes = 0x11111111u;
+  return v8i{static_cast<int>((w0 >> 1) & kOnes), static_cast<int>((w0 >> 3) & kOnes),
+             static_cast<int>((w1 >> 1) & kOnes), static_cast<int>((w1 >> 3) & kOnes), 0, 0, 0, 0};
+}
 __device__ __forceinline__ float lo_half(uint32_t w) {
   return __half2float(__ushort_as_half(static_cast<uint16_t>(w & 0xFFFF)));
 }
@@ -98,7 +105,7 @@ struct Int2Lds {
 // STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
 // sequence, so no page is read twice in it; with several sequences pages may be shared (a prefix
 // cache), and cached loads let the second reader hit.
-template <int G, int NG, bool STREAM>
+template <int G, int NG, bool STREAM, bool CB>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
                                            int b, unsigned char* smem) {
   using S = Int2Lds<G, NG>;
@@ -183,8 +190,25 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   const int src_lane4 = 4 * 16 * ((lane & 15) >> 2);
   const int row_part = lane & 3;
 
+  // CB: the history's codes name the levels (l0, l1, 3 - l1, 3 - l0) of symmetric codebooks,
+  // i.e. a + b c + d (c >> 1): a key's dot product is b q''.c + d q''.(c >> 1) + a sum(q''), a
+  // value's weighted sum b x.c + d x.(c >> 1) + a sum(x) -- one more matrix-core contraction of
+  // the codes' high bits for each, and a second set of value accumulators (accb).
+  float cbk_a = 0.f, cbk_b = 1.f, cbk_d = 0.f, cbv_a = 0.f, cbv_b = 1.f, cbv_d = 0.f;
+  if constexpr (CB) {
+    const float k0 = a.cb_k[2 * kv], k1 = a.cb_k[2 * kv + 1];
+    const float v0 = a.cb_v[2 * kv], v1 = a.cb_v[2 * kv + 1];
+    cbk_a = k0;
+    cbk_b = k1 - k0;
+    cbk_d = 3.f + k0 - 3.f * k1;
+    cbv_a = v0;
+    cbv_b = v1 - v0;
+    cbv_d = 3.f + v0 - 3.f * v1;
+  }
+  constexpr int NB = CB ? NT : 0;
   float m_ref[NT], l_run[NT], z_run[NT][NG];
   v4f acc[NT][8];
+  v4f accb[NB > 0 ? NB : 1][8];
 #pragma unroll
   for (int ht = 0; ht < NT; ++ht) {
     m_ref[ht] = -INFINITY;   // a wave without pages leaves -inf (its partial weighs nothing)
@@ -194,6 +218,10 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int ht = 0; ht < NB; ++ht)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) accb[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // One page's operands, fetched with 16-byte loads from the tiled block (one chunk row = 64 lanes
   // x 16 bytes): key chunk row j holds this lane's words of sub-tiles 2j and 2j + 1, value chunk
@@ -313,7 +341,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     for (int P = 0; P < 2; ++P)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const v8i bk = fp4_operand(kword(rr[P], st, 0), kword(rr[P], st, 1));
+        const uint32_t kw0 = kword(rr[P], st, 0), kw1 = kword(rr[P], st, 1);
+        const v8i bk = fp4_operand(kw0, kw1);
         float sc[NT][NG];
 #pragma unroll
         for (int ht = 0; ht < NT; ++ht)
@@ -322,13 +351,26 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
             const v4f d = mfma_f8_f4(aq[ht * NG + g], bk, v4f{0.f, 0.f, 0.f, 0.f}, sq[ht * NG + g]);
             sc[ht][g] = (d[0] + d[1]) + (d[2] + d[3]);
           }
+        if constexpr (CB) {
+          const v8i bh = fp4_high_bits(kw0, kw1);
+#pragma unroll
+          for (int ht = 0; ht < NT; ++ht)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+              const v4f d =
+                  mfma_f8_f4(aq[ht * NG + g], bh, v4f{0.f, 0.f, 0.f, 0.f}, sq[ht * NG + g]);
+              sc[ht][g] = fmaf(cbk_d, (d[0] + d[1]) + (d[2] + d[3]), cbk_b * sc[ht][g]);
+            }
+        }
 #pragma unroll
         for (int ht = 0; ht < NT; ++ht) {
           float t = hbias[ht];
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            t = fmaf(hi_half(km[P][g][st]), sig[ht][g], t);
-            t = fmaf(lo_half(km[P][g][st]), sc[ht][g], t);
+            const float ks = lo_half(km[P][g][st]);
+            const float kz = CB ? fmaf(cbk_a, ks, hi_half(km[P][g][st])) : hi_half(km[P][g][st]);
+            t = fmaf(kz, sig[ht][g], t);
+            t = fmaf(ks, sc[ht][g], t);
           }
           lg[ht][P][st] = t;
         }
@@ -372,6 +414,12 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[ht][nt][i] = ldexpf(acc[ht][nt][i], di);
+          if constexpr (CB) {
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) accb[ht][nt][i] = ldexpf(accb[ht][nt][i], di);
+          }
           if (mp[ht] > m_ref[ht] + kRescaleSpan) m_ref[ht] = mp[ht];
         }
       }
@@ -395,8 +443,10 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           lp += pr;
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            zp[g] = fmaf(pr, hi_half(vm[P][g][st]), zp[g]);
-            x[g][P][st] = pr * lo_half(vm[P][g][st]);
+            const float vs = lo_half(vm[P][g][st]);
+            const float vz = CB ? fmaf(cbv_a, vs, hi_half(vm[P][g][st])) : hi_half(vm[P][g][st]);
+            zp[g] = fmaf(pr, vz, zp[g]);
+            x[g][P][st] = pr * vs;
           }
         }
       l_run[ht] = fmaf(lp, wgt, l_run[ht]);
@@ -462,11 +512,18 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     // ---- values: channel tile nt of both pages against the pair's probability parts
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const v8i bv = fp4_operand(vword(rr[0], nt), vword(rr[1], nt));
+      const uint32_t vw0 = vword(rr[0], nt), vw1 = vword(rr[1], nt);
+      const v8i bv = fp4_operand(vw0, vw1);
       const int g = NG == 2 ? nt / 4 : 0;
 #pragma unroll
       for (int ht = 0; ht < NT; ++ht)
         acc[ht][nt] = mfma_f8_f4(pa[ht * NG + g], bv, acc[ht][nt], sv[ht]);
+      if constexpr (CB) {
+        const v8i bh = fp4_high_bits(vw0, vw1);
+#pragma unroll
+        for (int ht = 0; ht < NB; ++ht)
+          accb[ht][nt] = mfma_f8_f4(pa[ht * NG + g], bh, accb[ht][nt], sv[ht]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -536,9 +593,14 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       }
       float* red_w = red_acc + (wave * G + hd) * kHeadDim;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        red_w[16 * nt + n] = ((acc[ht][nt][0] + acc[ht][nt][1]) + (acc[ht][nt][2] + acc[ht][nt][3])) +
-                             zs[NG == 2 ? nt / 4 : 0];
+      for (int nt = 0; nt < 8; ++nt) {
+        float v = (acc[ht][nt][0] + acc[ht][nt][1]) + (acc[ht][nt][2] + acc[ht][nt][3]);
+        if constexpr (CB) {
+          const float h = (accb[ht][nt][0] + accb[ht][nt][1]) + (accb[ht][nt][2] + accb[ht][nt][3]);
+          v = fmaf(cbv_d, h, cbv_b * v);
+        }
+        red_w[16 * nt + n] = v + zs[NG == 2 ? nt / 4 : 0];
+      }
     }
   }
   __syncthreads();
@@ -722,7 +784,7 @@ constexpr int attn_lds_bytes() {
   return i2 > Bf16Lds<G>::TOTAL ? i2 : Bf16Lds<G>::TOTAL;
 }
 
-template <int G, int NG, bool STREAM>
+template <int G, int NG, bool STREAM, bool CB>
 __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p,
                                                                     float scale_log2, int x0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
@@ -730,7 +792,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p,
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
   else if constexpr (int2_fp8_pass(G, NG))
-    int2_block<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
+    int2_block<G, NG, STREAM, CB>(a, p, x - kBf16Chunks, kv, b, smem);
   else
     int2_block_i8<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
 }
@@ -959,21 +1021,39 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
   const float scale_log2 = a.sm_scale * kLog2e;
   const int x0 = (stages & OSCAR_STAGE_BF16) ? 0 : kBf16Chunks;
   const int x1 = kBf16Chunks + ((stages & OSCAR_STAGE_INT2) ? p.num_splits : 0);
+  bool cb_done = false;
   if (x1 > x0) {
     dim3 grid((x1 - x0) * p.hkv, 1, p.batch);
     const bool one = p.batch == 1;
-    if (p.n_groups == 1 && one)
-      hipLaunchKernelGGL((attn_kernel<G, 1, true>), grid, dim3(256), 0, stream, a, p, scale_log2,
-                         x0);
+    // a codebook history (cb_k / cb_v) runs on the fp8 pass; the host admits it only there
+    const bool cb = a.cb_k != nullptr;
+    if constexpr (int2_fp8_pass(G, 1)) {
+      if (cb && p.n_groups == 1) {
+        if (one)
+          hipLaunchKernelGGL((attn_kernel<G, 1, true, true>), grid, dim3(256), 0, stream, a, p,
+                             scale_log2, x0);
+        else
+          hipLaunchKernelGGL((attn_kernel<G, 1, false, true>), grid, dim3(256), 0, stream, a, p,
+                             scale_log2, x0);
+        cb_done = true;
+      }
+    }
+    if (cb_done)
+      ;
+    else if (cb)
+      return hipErrorInvalidValue;
+    else if (p.n_groups == 1 && one)
+      hipLaunchKernelGGL((attn_kernel<G, 1, true, false>), grid, dim3(256), 0, stream, a, p,
+                         scale_log2, x0);
     else if (p.n_groups == 1)
-      hipLaunchKernelGGL((attn_kernel<G, 1, false>), grid, dim3(256), 0, stream, a, p, scale_log2,
-                         x0);
+      hipLaunchKernelGGL((attn_kernel<G, 1, false, false>), grid, dim3(256), 0, stream, a, p,
+                         scale_log2, x0);
     else if (one)
-      hipLaunchKernelGGL((attn_kernel<G, 2, true>), grid, dim3(256), 0, stream, a, p, scale_log2,
-                         x0);
+      hipLaunchKernelGGL((attn_kernel<G, 2, true, false>), grid, dim3(256), 0, stream, a, p,
+                         scale_log2, x0);
     else
-      hipLaunchKernelGGL((attn_kernel<G, 2, false>), grid, dim3(256), 0, stream, a, p, scale_log2,
-                         x0);
+      hipLaunchKernelGGL((attn_kernel<G, 2, false, false>), grid, dim3(256), 0, stream, a, p,
+                         scale_log2, x0);
   }
   if (stages & OSCAR_STAGE_MERGE) {
     const int rows = p.batch * p.hq;

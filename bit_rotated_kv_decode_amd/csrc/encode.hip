@@ -88,7 +88,8 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a, int runs_per_
   uint32_t vword0 = 0, vword1 = 0, vmask = 0;
 #pragma unroll
   for (int t = 0; t < kRun; ++t) {
-    const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups, lv_lo, lv_step);
+    const LaneCodes q = quantize_lane(r[t][0], r[t][1], clip, a.n_groups, lv_lo, lv_step,
+                                     a.levels_kind);
     const int slot = group_slot(ug, t);
     const int idx = first + slot;
     if (idx < lo || idx >= hi) continue;
@@ -177,7 +178,7 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int item, unsig
   if (tid >= 128) ring[tid - 128] = nv;
   double r0, r1;
   if (dev::rotate1_block(x, ur, red, r0, r1)) {
-    const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups, lv_lo, lv_step);
+    const LaneCodes q = quantize_lane(r0, r1, clip, a.n_groups, lv_lo, lv_step, a.levels_kind);
     store_token(blk, tensor, idx % kPage, a.n_groups, q);
   }
 }

@@ -22,9 +22,12 @@ struct LaneCodes {
 // four levels of an equally spaced codebook at lv_lo + lv_step * c in units of (max - min) / 3
 // above the group minimum: the stored scale is (max - min) / 3 * lv_step and the zero point
 // min + (max - min) / 3 * lv_lo, every product and sum rounded to fp32 on its own; (0, 1) is the
-// plain grid (scale (max - min) / 3, zero point min).
+// plain grid (scale (max - min) / 3, zero point min).  levels_kind 1: (lv_lo, lv_step) = (l0, l1)
+// of a codebook symmetric about 1.5, levels (l0, l1, 3 - l1, 3 - l0) in t = (x - z) / s with the
+// plain grid's scale and zero point; the code names the nearest level.
 __device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float clip,
-                                                   int n_groups, float lv_lo, float lv_step) {
+                                                   int n_groups, float lv_lo, float lv_step,
+                                                   int levels_kind) {
 #pragma clang fp contract(off)
   float x0 = static_cast<float>(r0);
   float x1 = static_cast<float>(r1);
@@ -43,11 +46,12 @@ __device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float c
   }
   LaneCodes out;
   float sf[2], zf[2];
+  const bool spaced = levels_kind == 0;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const float r3 = (mx[m] - mn[m]) / 3.0f;
-    const float s32 = lv_step == 1.0f ? r3 : r3 * lv_step;
-    const float z32 = lv_lo == 0.0f ? mn[m] : mn[m] + r3 * lv_lo;
+    const float s32 = !spaced || lv_step == 1.0f ? r3 : r3 * lv_step;
+    const float z32 = !spaced || lv_lo == 0.0f ? mn[m] : mn[m] + r3 * lv_lo;
     const __half s16 = __float2half_rn(s32);
     const __half z16 = __float2half_rn(z32);
     sf[m] = __half2float(s16);
@@ -55,10 +59,25 @@ __device__ __forceinline__ LaneCodes quantize_lane(double r0, double r1, float c
     out.meta[m] = static_cast<uint32_t>(__half_as_ushort(s16)) |
                   (static_cast<uint32_t>(__half_as_ushort(z16)) << 16);
   }
-  auto code = [](float x, float s, float z) -> uint32_t {
-    if (s == 0.0f) return 0u;
-    const float t = rintf((x - z) / s);
-    return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
+  if (spaced) {
+    auto code = [](float x, float s, float z) -> uint32_t {
+      if (s == 0.0f) return 0u;
+      const float t = rintf((x - z) / s);
+      return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
+    };
+    out.c0 = code(x0, sf[0], zf[0]);
+    out.c1 = code(x1, sf[1], zf[1]);
+    return out;
+  }
+  // the number of midpoints strictly below t = (x - z) / s (0 when s is 0): (l0 + l1) / 2, 1.5
+  // and 3 - (l0 + l1) / 2 in fp64 (exact from the fp32 levels), so a value on a midpoint takes
+  // the lower code
+  const double th0 = (static_cast<double>(lv_lo) + static_cast<double>(lv_step)) * 0.5;
+  const double th2 = 3.0 - th0;
+  auto code = [th0, th2](float x, float s, float z) -> uint32_t {
+    const double t = s == 0.0f ? 0.0 : static_cast<double>((x - z) / s);
+    return static_cast<uint32_t>(t > th0) + static_cast<uint32_t>(t > 1.5) +
+           static_cast<uint32_t>(t > th2);
   };
   out.c0 = code(x0, sf[0], zf[0]);
   out.c1 = code(x1, sf[1], zf[1]);

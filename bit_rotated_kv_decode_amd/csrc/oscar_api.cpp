@@ -52,6 +52,17 @@ oscar_status check_layout(const oscar_layout* l) {
                 l->page_tokens, l->sink_tokens, l->recent_tokens);
   if (l->num_pages < 0 || l->max_seqs < 0 || l->max_pages_per_seq < 0)
     return fail(OSCAR_ERR_SHAPE, "negative num_pages / max_seqs / max_pages_per_seq");
+  if (l->levels_kind != 0 && l->levels_kind != 1)
+    return fail(OSCAR_ERR_SHAPE, "levels_kind %d unsupported (0 or 1)", l->levels_kind);
+  return OSCAR_OK;
+}
+
+// A history encoded with symmetric codebooks (levels_kind 1) needs their levels to encode and
+// to decode.
+oscar_status check_codebook(const oscar_layout* l, const float* levels_k, const float* levels_v,
+                            const char* what) {
+  if (l->levels_kind == 1 && (levels_k == nullptr || levels_v == nullptr))
+    return fail(OSCAR_ERR_NULL, "%s: levels_kind 1 needs levels_k and levels_v", what);
   return OSCAR_OK;
 }
 
@@ -149,6 +160,8 @@ oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* 
   if (!pool || !page_table || !sink_k || !sink_v || !recent_k || !recent_v || !u_k || !u_v ||
       !clip_k || !clip_v || !k_new || !v_new || !seq_slot || !seq_lens)
     return fail(OSCAR_ERR_NULL, "append: a required pointer is NULL");
+  st = check_codebook(l, levels_k, levels_v, "append");
+  if (st != OSCAR_OK) return st;
   if (!aligned(pool, 16) || !aligned(sink_k, 16) || !aligned(sink_v, 16) ||
       !aligned(recent_k, 16) || !aligned(recent_v, 16))
     return fail(OSCAR_ERR_ALIGN, "pool and BF16 segments must be 16-byte aligned");
@@ -172,6 +185,7 @@ oscar_status make_append_args(const oscar_layout* l, void* pool, const int32_t* 
   a.clip_v = clip_v;
   a.levels_k = levels_k;
   a.levels_v = levels_v;
+  a.levels_kind = l->levels_kind;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.seq_slot = seq_slot;
@@ -231,6 +245,8 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   a.lse = lse;
   a.workspace = static_cast<uint8_t*>(workspace);
   a.len_add = 0;
+  a.cb_k = nullptr;
+  a.cb_v = nullptr;
   qa.q = a.q;
   qa.u_k = u_k;
   qa.batch = batch;
@@ -386,6 +402,8 @@ oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page
   if (!pool || !page_table || !u_k || !u_v || !clip_k || !clip_v || !k_src || !v_src ||
       !hist_start)
     return fail(OSCAR_ERR_NULL, "oscar_demote: a required pointer is NULL");
+  st = check_codebook(l, levels_k, levels_v, "oscar_demote");
+  if (st != OSCAR_OK) return st;
   if (stride_b < 0 || stride_t < 0 || stride_h < 0)
     return fail(OSCAR_ERR_RANGE, "negative source stride");
   if (!aligned(pool, 16)) return fail(OSCAR_ERR_ALIGN, "pool must be 16-byte aligned");
@@ -405,6 +423,7 @@ oscar_status oscar_demote(const oscar_layout* l, void* pool, const int32_t* page
   a.clip_v = clip_v;
   a.levels_k = levels_k;
   a.levels_v = levels_v;
+  a.levels_kind = l->levels_kind;
   a.k_src = static_cast<const uint16_t*>(k_src);
   a.v_src = static_cast<const uint16_t*>(v_src);
   a.stride_b = stride_b;
@@ -443,14 +462,30 @@ oscar_status oscar_decode_attn(const oscar_layout* l, const void* pool, const in
                                   workspace_bytes, batch, max_seq_len, OSCAR_STAGE_ALL, stream);
 }
 
-oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
-                                      const int32_t* page_table, const void* sink_k,
-                                      const void* sink_v, const void* recent_k,
-                                      const void* recent_v, const int32_t* seq_slot,
-                                      const int32_t* seq_lens, const void* q, const float* u_k,
-                                      const float* u_v, float sm_scale, float* out, float* lse,
-                                      void* workspace, size_t workspace_bytes, int32_t batch,
-                                      int32_t max_seq_len, uint32_t stages, void* stream) {
+namespace {
+
+// The symmetric-codebook attention runs on the fp8 x FP4 pass only.
+oscar_status check_codebook_attention(const oscar_layout* l, const float* levels_k,
+                                      const float* levels_v, const char* what) {
+  if (l == nullptr || l->levels_kind != 1) return OSCAR_OK;
+  oscar_status st = check_codebook(l, levels_k, levels_v, what);
+  if (st != OSCAR_OK) return st;
+  if (!aligned(levels_k, 4) || !aligned(levels_v, 4))
+    return fail(OSCAR_ERR_ALIGN, "%s: misaligned levels", what);
+  if (!oscar::int2_fp8_pass(l->num_q_heads / l->num_kv_heads, n_groups(l)))
+    return fail(OSCAR_ERR_SHAPE, "%s: codebook attention supports up to 4 query heads per KV head "
+                "and group_size 128", what);
+  return OSCAR_OK;
+}
+
+oscar_status decode_attn_impl(const oscar_layout* l, const void* pool, const int32_t* page_table,
+                              const void* sink_k, const void* sink_v, const void* recent_k,
+                              const void* recent_v, const int32_t* seq_slot,
+                              const int32_t* seq_lens, const void* q, const float* u_k,
+                              const float* u_v, const float* cb_k, const float* cb_v,
+                              float sm_scale, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                              uint32_t stages, void* stream) {
   if (stages == 0 || (stages & ~OSCAR_STAGE_ALL) != 0)
     return fail(OSCAR_ERR_RANGE, "stage mask 0x%x invalid", stages);
   oscar::DecodeArgs a;
@@ -461,12 +496,52 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
                                            out, lse, workspace, workspace_bytes, batch,
                                            max_seq_len, a, qa, plan);
   if (st != OSCAR_OK || batch == 0) return st;
+  a.cb_k = cb_k;
+  a.cb_v = cb_v;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (stages & OSCAR_STAGE_QUERY) {
     const hipError_t e = oscar::launch_prep(nullptr, &qa, s);
     if (e != hipSuccess) return hip_status(e, "oscar_decode_attn");
   }
   return hip_status(oscar::launch_decode(a, plan, stages, s), "oscar_decode_attn");
+}
+
+}  // namespace
+
+oscar_status oscar_decode_attn_stages(const oscar_layout* l, const void* pool,
+                                      const int32_t* page_table, const void* sink_k,
+                                      const void* sink_v, const void* recent_k,
+                                      const void* recent_v, const int32_t* seq_slot,
+                                      const int32_t* seq_lens, const void* q, const float* u_k,
+                                      const float* u_v, float sm_scale, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, int32_t batch,
+                                      int32_t max_seq_len, uint32_t stages, void* stream) {
+  if (l != nullptr && l->levels_kind == 1)
+    return fail(OSCAR_ERR_SHAPE, "oscar_decode_attn: a layout with levels_kind 1 needs the "
+                "codebook levels (oscar_decode_attn_codebook)");
+  return decode_attn_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                          seq_lens, q, u_k, u_v, nullptr, nullptr, sm_scale, out, lse, workspace,
+                          workspace_bytes, batch, max_seq_len, stages, stream);
+}
+
+oscar_status oscar_decode_attn_codebook(const oscar_layout* l, const void* pool,
+                                        const int32_t* page_table, const void* sink_k,
+                                        const void* sink_v, const void* recent_k,
+                                        const void* recent_v, const int32_t* seq_slot,
+                                        const int32_t* seq_lens, const void* q, const float* u_k,
+                                        const float* u_v, const float* levels_k,
+                                        const float* levels_v, float sm_scale, float* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        int32_t batch, int32_t max_seq_len, uint32_t stages,
+                                        void* stream) {
+  const oscar_status st =
+      check_codebook_attention(l, levels_k, levels_v, "oscar_decode_attn_codebook");
+  if (st != OSCAR_OK) return st;
+  const bool cb = l != nullptr && l->levels_kind == 1;
+  return decode_attn_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                          seq_lens, q, u_k, u_v, cb ? levels_k : nullptr, cb ? levels_v : nullptr,
+                          sm_scale, out, lse, workspace, workspace_bytes, batch, max_seq_len,
+                          stages, stream);
 }
 
 oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t* page_table,
@@ -490,6 +565,12 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
                         q, u_k, u_v, sm_scale, out, lse, workspace, workspace_bytes, batch,
                         max_seq_len, a, qa, plan);
   if (st != OSCAR_OK || batch == 0) return st;
+  st = check_codebook_attention(l, levels_k, levels_v, "oscar_decode_step");
+  if (st != OSCAR_OK) return st;
+  if (l->levels_kind == 1) {
+    a.cb_k = levels_k;
+    a.cb_v = levels_v;
+  }
   a.len_add = 1;   // attention sees the appended token
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = oscar::launch_prep(&ap, &qa, s);
@@ -512,6 +593,8 @@ oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
   oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
                                      u_k, u_v, clip_k, clip_v, levels_k, levels_v, k_new, v_new,
                                      seq_slot, seq_pos, batch, ap);
+  if (st != OSCAR_OK) return st;
+  st = check_codebook_attention(l, levels_k, levels_v, "oscar_decode_step_noalloc");
   if (st != OSCAR_OK) return st;
   if (batch > 0 && max_seq_len >= 1 && check_layout(l) == OSCAR_OK) {
     const size_t need = oscar::make_plan(*l, batch, max_seq_len).total;
@@ -538,6 +621,10 @@ oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
   qa.qops = a.workspace + plan.off_qops;
   qa.qscales = reinterpret_cast<int32_t*>(a.workspace + plan.off_qscale);
   qa.qmeta = reinterpret_cast<float*>(a.workspace + plan.off_sigma);
+  if (l->levels_kind == 1) {
+    a.cb_k = levels_k;
+    a.cb_v = levels_v;
+  }
   a.len_add = 1;   // attention sees the appended token
   const hipStream_t s = static_cast<hipStream_t>(stream);
   e = oscar::launch_prep(&ap, &qa, s);

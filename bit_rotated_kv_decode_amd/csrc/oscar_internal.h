@@ -81,8 +81,9 @@ struct DemoteArgs {
   const float* u_v;
   const float* clip_k;
   const float* clip_v;
-  const float* levels_k;   // [hkv][2] (lo, step) of an equally spaced codebook, or NULL
-  const float* levels_v;
+  const float* levels_k;   // [hkv][2] (lo, step) of an equally spaced codebook, (l0, l1) of a
+  const float* levels_v;   // symmetric one (levels_kind 1), or NULL
+  int levels_kind;
   const uint16_t* k_src;
   const uint16_t* v_src;
   int64_t stride_b, stride_t, stride_h;
@@ -105,8 +106,9 @@ struct AppendArgs {
   const float* u_v;
   const float* clip_k;
   const float* clip_v;
-  const float* levels_k;   // [hkv][2] (lo, step) of an equally spaced codebook, or NULL
+  const float* levels_k;   // as in DemoteArgs
   const float* levels_v;
+  int levels_kind;
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int32_t* seq_slot;
@@ -132,6 +134,10 @@ struct DecodeArgs {
   float* lse;
   uint8_t* workspace;
   int len_add;            // added to seq_lens[b] (1 when seq_lens holds the new token's position)
+  // [hkv][2] (l0, l1) of the symmetric codebooks the history was encoded with (levels
+  // (l0, l1, 3 - l1, 3 - l0)), or NULL for the grid {0, 1, 2, 3}
+  const float* cb_k;
+  const float* cb_v;
 };
 
 struct QueryArgs {

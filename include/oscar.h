@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 4u
+#define OSCAR_ABI_VERSION 5u
 
 typedef int32_t oscar_status;
 
@@ -107,6 +107,9 @@ typedef struct oscar_layout {
   int32_t num_pages;          /* physical pages in the INT2 pool */
   int32_t max_seqs;           /* sequence slots in the BF16 sink / recent arrays */
   int32_t max_pages_per_seq;  /* row stride of the page table */
+  int32_t levels_kind;        /* what levels_k / levels_v hold: 0 = (lo, step) of an equally
+                                 spaced codebook; 1 = (l0, l1) of a codebook symmetric about 1.5
+                                 (see oscar_demote) */
 } oscar_layout;
 
 /* Library ABI version (OSCAR_ABI_VERSION of the build). */
@@ -174,6 +177,12 @@ oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* h
  * equal spacing so that decoding stays scale * code + zero and the attention kernels are
  * unchanged.  lo and step must be finite, step > 0 (the library does not read device memory to
  * check); fitted values lie near lo = 0.5, step = 2/3.
+ * With layout->levels_kind 1, levels_k / levels_v (then required) hold (l0, l1) per KV head of a
+ * Lloyd-Max codebook symmetric about 1.5: steps 3 and 4 become scale = fp16(r), zero = fp16(mn)
+ * and code_j = the number of the midpoints (l0 + l1) / 2, 1.5, 3 - (l0 + l1) / 2 (in fp64)
+ * strictly below t = (x''_j - zero) / scale (fp32; t = 0 for a zero scale), i.e. the nearest of
+ * the levels (l0, l1, 3 - l1, 3 - l0), a value on a midpoint taking the lower code; such a history
+ * decodes to scale * level + zero (oscar_decode_attn_codebook).  Requires l0 <= l1 <= 1.5.
  * pool: oscar_pool_bytes(layout) bytes, 16-byte aligned.  page_table: int32
  * [batch][max_pages_per_seq].  U_k / U_v / clip_k / clip_v as described above.  hist_start:
  * int32 [batch].  Strides are in bf16 elements, >= 0; k_src / v_src 2-byte aligned.  The call
@@ -217,8 +226,10 @@ oscar_status oscar_append(const oscar_layout* layout, void* pool, const int32_t*
  * q: bf16 [batch][Hq][d].  out: fp32 [batch][Hq][d].  lse: optional fp32 [batch][Hq] natural-log
  * sum of exp(sm_scale * scores) (NULL to skip).  sm_scale <= 0 selects 1/sqrt(d).
  * seq_lens[b] must be in [1, max_seq_len]; max_seq_len is a host-side bound used for work
- * planning, at most 64 * 256 * 1024 + 320 tokens (RANGE beyond).  workspace: at least oscar_decode_workspace_bytes(layout, batch, max_seq_len) bytes,
- * 256-byte aligned; its contents on entry do not matter.
+ * planning, at most 64 * 256 * 1024 + 320 tokens (RANGE beyond).  workspace: at least
+ * oscar_decode_workspace_bytes(layout, batch, max_seq_len) bytes, 256-byte aligned; its contents
+ * on entry do not matter.  A layout with levels_kind 1 needs the codebook levels: use
+ * oscar_decode_attn_codebook (SHAPE here).
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
 oscar_status oscar_decode_attn(const oscar_layout* layout, const void* pool,
                                const int32_t* page_table, const void* sink_k, const void* sink_v,
@@ -250,11 +261,32 @@ oscar_status oscar_decode_attn_stages(const oscar_layout* layout, const void* po
                                       void* workspace, size_t workspace_bytes, int32_t batch,
                                       int32_t max_seq_len, uint32_t stages, void* stream);
 
+/* oscar_decode_attn_stages over a history encoded with symmetric Lloyd-Max codebooks
+ * (layout->levels_kind 1; see oscar_demote): history keys / values are (scale * level_code +
+ * zero) R^T with levels (l0, l1, 3 - l1, 3 - l0) from levels_k / levels_v (device fp32
+ * [num_kv_heads][2], 4-byte aligned, required) -- the Lloyd-Max codebook of [W3]'s closing
+ * comparison with TurboQuant, restricted to levels symmetric about 1.5 so that a level is
+ * a + b code + d (code >> 1), two matrix-core contractions of the stored bits.  Supported for up
+ * to four query heads per KV head and group_size 128 (SHAPE otherwise).  With levels_kind 0 the
+ * levels are ignored and the call is oscar_decode_attn_stages.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
+oscar_status oscar_decode_attn_codebook(const oscar_layout* layout, const void* pool,
+                                        const int32_t* page_table, const void* sink_k,
+                                        const void* sink_v, const void* recent_k,
+                                        const void* recent_v, const int32_t* seq_slot,
+                                        const int32_t* seq_lens, const void* q, const float* u_k,
+                                        const float* u_v, const float* levels_k,
+                                        const float* levels_v, float sm_scale, float* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        int32_t batch, int32_t max_seq_len, uint32_t stages,
+                                        void* stream);
+
 /* One whole decode step of a layer ([W1] OSCAR 的设计: a new token enters the recent window, the
  * token it displaces is demoted into the INT2 history, then attention runs over the three
  * segments): the same result as
  *   oscar_append(..., seq_slot, seq_pos, ...)  followed by
- *   oscar_decode_attn(..., seq_lens = seq_pos + 1, ...),
+ *   oscar_decode_attn(..., seq_lens = seq_pos + 1, ...)
+ * (oscar_decode_attn_codebook with the same levels for a layout with levels_kind 1),
  * in three launches: the append and the query rotation share the first.
  * seq_pos[b] = position of the new token = tokens cached before the step; seq_pos[b] + 1 must be
  * in [1, max_seq_len].  Arguments are those of the two calls, with the same requirements.

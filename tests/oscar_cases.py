@@ -33,7 +33,7 @@ class Case:
     """Inputs of one layer: token K/V per sequence (bf16, host), queries, U, clip, page table."""
 
     def __init__(self, wl, lengths=None, layer=0, spare=0, u=None, clip=None, device_tokens=None,
-                 levels=None):
+                 levels=None, codebook=None):
         self.wl = wl
         self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
         self.batch = len(self.lengths)
@@ -50,6 +50,11 @@ class Case:
         # optional equally spaced codebooks: (lo, step) per KV head for keys and for values
         self.levels_k, self.levels_v = ((None, None) if levels is None else
                                         (np.asarray(lv, np.float32) for lv in levels))
+        # optional symmetric Lloyd-Max codebooks (reading R21): (l0, l1) per KV head for keys and
+        # values, levels (l0, l1, 3 - l1, 3 - l0)
+        assert levels is None or codebook is None
+        self.cb_k, self.cb_v = ((None, None) if codebook is None else
+                                (np.asarray(c, np.float32) for c in codebook))
         dev = device_tokens or "cpu"
         self.k, self.v = [], []
         for b, L in enumerate(self.lengths):
@@ -59,7 +64,8 @@ class Case:
         self.q = workloads.queries(wl, layer, 0, "cpu", batch=self.batch)
         self.geom = oracle.Geometry(group=wl.group_size)
         self.layout = ok.make_layout(wl.num_q_heads, wl.num_kv_heads, self.num_pages, self.batch,
-                                     self.table.shape[1], wl.group_size)
+                                     self.table.shape[1], wl.group_size,
+                                     levels_kind=0 if codebook is None else ok.LEVELS_SYMMETRIC)
 
     # -------------------------------------------------------------------------------- oracle
     def oracle_segments(self):
@@ -88,26 +94,45 @@ class Case:
             v = bf16_np(self.v[b][64:64 + n])[None]
             if heads is not None:
                 for h in heads:
-                    kq = oracle.encode(k[0, :, h], self.u_k[h].numpy(), self.clip_k[h],
-                                       self.geom.group, self.head_levels("k", h))[:3]
-                    vq = oracle.encode(v[0, :, h], self.u_v[h].numpy(), self.clip_v[h],
-                                       self.geom.group, self.head_levels("v", h))[:3]
+                    kq = self.encode(k[0, :, h], "k", h)
+                    vq = self.encode(v[0, :, h], "v", h)
                     oracle.store_history(pool, self.table[b], np.arange(n), h, kq, vq, self.geom)
             else:
                 oracle.demote(pool, self.table[b:b + 1], self.u_k.numpy(), self.u_v.numpy(),
                               self.clip_k, self.clip_v, k, v, [0], self.geom, self.levels_k,
-                              self.levels_v)
+                              self.levels_v, self.codebooks("k"), self.codebooks("v"))
         return pool
 
     def head_levels(self, tensor, h):
         lv = self.levels_k if tensor == "k" else self.levels_v
         return None if lv is None else lv[h]
 
+    def codebooks(self, tensor):
+        """Four levels per KV head of the symmetric codebooks, or None."""
+        cb = self.cb_k if tensor == "k" else self.cb_v
+        return None if cb is None else np.stack([oracle.symmetric_levels(float(a), float(b))
+                                                 for a, b in cb])
+
+    def head_codebook(self, tensor, h):
+        cb = self.codebooks(tensor)
+        return None if cb is None else cb[h]
+
+    def encode(self, x, tensor, h):
+        """The oracle's (codes, scale, zero) of tokens x (fp32 [n, d]) for KV head h."""
+        u = (self.u_k if tensor == "k" else self.u_v)[h].numpy()
+        c = (self.clip_k if tensor == "k" else self.clip_v)[h]
+        cb = self.head_codebook(tensor, h)
+        if cb is not None:
+            return oracle.quantize_codebook(oracle.rotate_to_fp32(x, u), c, self.geom.group, cb)
+        return oracle.encode(x, u, c, self.geom.group, self.head_levels(tensor, h))[:3]
+
     def oracle_attention(self, pool, heads=None):
         sk, sv, rk, rv = self.oracle_segments()
         return oracle.decode_attention(pool, self.table, sk, sv, rk, rv, np.arange(self.batch),
                                        self.lengths, bf16_np(self.q), self.u_k.numpy(),
-                                       self.u_v.numpy(), self.geom, heads=heads)
+                                       self.u_v.numpy(), self.geom, heads=heads,
+                                       codebook_k=self.codebooks("k"),
+                                       codebook_v=self.codebooks("v"))
 
     # -------------------------------------------------------------------------------- GPU
     def gpu_inputs(self):
@@ -121,6 +146,9 @@ class Case:
                  slots=torch.arange(self.batch, dtype=torch.int32, device=dev),
                  levels_k=None if self.levels_k is None else torch.from_numpy(self.levels_k).to(dev),
                  levels_v=None if self.levels_v is None else torch.from_numpy(self.levels_v).to(dev))
+        if self.cb_k is not None:
+            g["levels_k"] = torch.from_numpy(self.cb_k).to(dev)
+            g["levels_v"] = torch.from_numpy(self.cb_v).to(dev)
         return g
 
     def gpu_cache(self, g, pool_from_oracle=None):
@@ -158,9 +186,15 @@ class Case:
                           device="cuda") if with_lse else None
         ws = torch.empty(ok.decode_workspace_bytes(self.layout, self.batch, mx),
                          dtype=torch.uint8, device="cuda")
-        ok.decode_attn(self.layout, cache.pool, g["table"], cache.sink_k, cache.sink_v,
-                       cache.recent_k, cache.recent_v, g["slots"], g["lens"], g["q"], g["u_k"],
-                       g["u_v"], out, ws, mx, lse=lse)
+        if self.cb_k is not None:
+            ok.decode_attn_codebook(self.layout, cache.pool, g["table"], cache.sink_k,
+                                    cache.sink_v, cache.recent_k, cache.recent_v, g["slots"],
+                                    g["lens"], g["q"], g["u_k"], g["u_v"], g["levels_k"],
+                                    g["levels_v"], out, ws, mx, lse=lse)
+        else:
+            ok.decode_attn(self.layout, cache.pool, g["table"], cache.sink_k, cache.sink_v,
+                           cache.recent_k, cache.recent_v, g["slots"], g["lens"], g["q"],
+                           g["u_k"], g["u_v"], out, ws, mx, lse=lse)
         torch.cuda.synchronize()
         return out.cpu().numpy(), (lse.cpu().numpy() if lse is not None else None)
 
@@ -229,19 +263,29 @@ def compare_pool_blocks(gpu: np.ndarray, ref: np.ndarray, case: Case, heads=None
         blk_g = gpu[page][head_ids.index(h)]
         blk_r = ref[page][head_ids.index(h)]
         lv = case.head_levels(tensor, h)
+        cb = case.head_codebook(tensor, h)
         rc, _, _ = _token(blk_r, t % g.page, tensor, g)
-        assert np.array_equal(rc, oracle.encode(x, u, c, g.group, lv)[0][0]), \
+        assert np.array_equal(rc, case.encode(x, tensor, h)[0][0]), \
             "oracle pool and oracle encode disagree"
-        flips += check_token(blk_g, t % g.page, tensor, x, u, c, g, (b, t, h, tensor), lv)
+        flips += check_token(blk_g, t % g.page, tensor, x, u, c, g, (b, t, h, tensor), lv, cb)
     assert flips <= MAX_FLIP_FRACTION * total_codes, (flips, total_codes)
     return flips
 
 
-def check_token(blk, slot, tensor, x, u, c, g, where=None, levels=None):
+def check_token(blk, slot, tensor, x, u, c, g, where=None, levels=None, codebook=None):
     """Check one token's bytes in a GPU-written block against the oracle's encoding of x (fp32
-    [1, d] of the bf16 token; ``levels`` the head's (lo, step) or None) under the acceptance rule;
-    returns the number of codes that differ (all of them inside the rounding window)."""
+    [1, d] of the bf16 token; ``levels`` the head's (lo, step) or None; ``codebook`` its four
+    levels or None) under the acceptance rule; returns the number of codes that differ (all of
+    them inside the rounding window, which for a codebook is around the midpoints of its
+    levels)."""
     codes, s16, z16, pre = oracle.encode(x, u, c, g.group, levels)
+    if codebook is not None:
+        codes = oracle.quantize_codebook(oracle.rotate_to_fp32(x, u), c, g.group, codebook)[0]
+        mids = (np.asarray(codebook)[:-1] + np.asarray(codebook)[1:]) / 2
+        near = lambda t: np.any(np.abs(np.asarray(t, np.float64)[:, None] - mids) <=
+                                WINDOW * np.maximum(np.abs(np.asarray(t))[:, None], 1.0), axis=1)
+    else:
+        near = _near_half
     gc, gs, gz = _token(blk, slot, tensor, g)
     flips = 0
     for m in range(g.n_groups):
@@ -254,12 +298,13 @@ def check_token(blk, slot, tensor, x, u, c, g, where=None, levels=None):
             assert _near_fp16_midpoint(pre["z"][0, m]), (where, "zero")
         if same_s and same_z:
             diff = gc[sl] != codes[0, sl]
-            assert _near_half(pre["t"][0, sl][diff]).all(), (where, "code")
+            assert near(pre["t"][0, sl][diff]).all(), (where, "code")
             flips += int(diff.sum())
         else:
             # legitimate meta difference: the GPU codes must be nearest levels under its meta
             xr = np.clip(oracle.rotate(x, u)[0, sl], -c, c)
-            lv = float(gs[m]) * np.arange(4)[None, :] + float(gz[m])
+            grid = np.arange(4) if codebook is None else np.asarray(codebook)
+            lv = float(gs[m]) * grid[None, :] + float(gz[m])
             dist = np.abs(xr[:, None] - lv)
             best = np.sort(dist, axis=1)
             chosen = dist[np.arange(g.group), gc[sl]]

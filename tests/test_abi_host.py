@@ -37,21 +37,23 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 4
+    assert lib.oscar_abi_version() == 5
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
 
 def _lay(**kw):
     base = dict(head_dim=128, group_size=128, num_q_heads=32, num_kv_heads=8, page_tokens=64,
-                sink_tokens=64, recent_tokens=256, num_pages=10, max_seqs=2, max_pages_per_seq=5)
+                sink_tokens=64, recent_tokens=256, num_pages=10, max_seqs=2, max_pages_per_seq=5,
+                levels_kind=0)
     base.update(kw)
     return ok.Layout(*[base[n] for n, _ in ok.Layout._fields_])
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=64), dict(group_size=32), dict(num_q_heads=30),
                                  dict(num_q_heads=128, num_kv_heads=8), dict(page_tokens=32),
-                                 dict(sink_tokens=0), dict(recent_tokens=128), dict(num_pages=-1)])
+                                 dict(sink_tokens=0), dict(recent_tokens=128), dict(num_pages=-1),
+                                 dict(levels_kind=2)])
 def test_layout_rejects_unsupported(bad):
     lay = _lay(**bad)
     assert ok.lib().oscar_layout_check(ctypes.byref(lay)) == -2
@@ -189,6 +191,31 @@ def test_decode_validation_happens_before_launch():
     big = _lay(max_pages_per_seq=300000)
     assert _call_decode(big, maxlen=64 * 256 * 1024 + 320 + 1) == -4
     assert "work items" in ok.lib().oscar_last_error().decode()
+
+
+def _call_decode_cb(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, slot=4096, lens=4096,
+             q=4096, uk=4096, uv=4096, lk=4096, lv=4096, out=4096, lse=None, ws=4096,
+             wsb=1 << 30, batch=1, maxlen=600, stages=ok.STAGE_ALL)
+    a.update(over)
+    return ok.lib().oscar_decode_attn_codebook(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["slot"],
+        a["lens"], a["q"], a["uk"], a["uv"], a["lk"], a["lv"], 0.0, a["out"], a["lse"], a["ws"],
+        a["wsb"], a["batch"], a["maxlen"], a["stages"], None)
+
+
+def test_codebook_attention_validation_happens_before_launch():
+    # a history encoded with symmetric codebooks needs their levels, and runs on the fp8 pass only
+    sym = _lay(levels_kind=1)
+    assert _call_decode(sym) == -2                       # the plain entry point refuses it
+    assert "codebook" in ok.lib().oscar_last_error().decode()
+    assert _call_decode_cb(sym, lk=None) == -1
+    assert _call_decode_cb(sym, lv=4096 + 2) == -3
+    assert _call_decode_cb(_lay(levels_kind=1, num_q_heads=64), ) == -2   # 8 heads per KV head
+    assert _call_decode_cb(_lay(levels_kind=1, group_size=64)) == -2
+    assert _call_decode_cb(sym, q=None) == -1            # the usual checks still run
+    assert _call_decode_cb(sym, maxlen=100000) == -4
+    assert _call_decode_cb(sym, batch=0, q=None) == 0
 
 
 def test_append_validation_happens_before_launch():
