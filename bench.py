@@ -237,16 +237,18 @@ def probes(wl, layers, steps):
     if len(lr0.lengths) == 1:
         splits, pps = ok.decode_splits(lr0.lay, 1, lr0.lengths[0] + 1)
         blocks = 4 * splits * wl.num_kv_heads
-        for depth in (2, 4):
+        # the attention kernel's own access pattern (two register sets of page pairs per wave),
+        # bare and with per-pair arithmetic on the waves' paths, then with deeper prefetch
+        for sets, work in ((2, 0), (2, 200), (2, 400), (4, 0), (4, 400)):
             us = timed_graph(lambda: [ok.probe_gather(Lr.lay, Lr.cache.pool, Lr.table[0],
-                                                      n_pages[0], pps, depth, sink)
+                                                      n_pages[0], pps, sets, sink, work)
                                       for Lr in layers], reps, len(layers))
-            out[f"int2_page_gather_depth{depth}"] = {
+            out[f"int2_page_gather_sets{sets}_work{work}"] = {
                 "bytes": int(hist), "GB/s": round(hist / (float(np.mean(us)) * 1e-6) / 1e9, 1),
                 "us": distribution(us, 2),
                 "note": f"{splits} splits x {wl.num_kv_heads} KV heads of {pps} pages, "
-                        f"{blocks} waves, {depth} pages in flight per wave, "
-                        f"{len(layers)} layer pools"}
+                        f"{blocks} waves, {sets} register sets of page pairs per wave, {work} "
+                        f"fp32 FMAs per lane per pair, {len(layers)} layer pools"}
     return out
 
 

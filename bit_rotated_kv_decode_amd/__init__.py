@@ -97,7 +97,8 @@ _SIGNATURES = {
     "oscar_bf16_decode_attn": (_i32, [_LP, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                       ctypes.c_size_t, _i32, _i32, _vp]),
     "oscar_probe_read": (_i32, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _i32, _vp]),
-    "oscar_probe_gather": (_i32, [_LP, _vp, _vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "oscar_probe_gather": (_i32, [_LP, _vp, _vp, _i32, _i32, _i32, _i32, _vp, ctypes.c_size_t,
+                                   _vp]),
 }
 
 STAGE_QUERY, STAGE_INT2, STAGE_BF16, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 8, 15
@@ -527,13 +528,15 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 2048) -> Non
 
 
 def probe_gather(lay: Layout, pool: torch.Tensor, table_row: torch.Tensor, n_pages: int,
-                 pages_per_split: int, depth: int, sink: torch.Tensor) -> None:
+                 pages_per_split: int, sets: int, sink: torch.Tensor, work: int = 0) -> None:
     """Read the INT2 pool blocks of ``n_pages`` pages of one page-table row in the decode kernel's
-    order (oscar_probe_gather)."""
+    order, ``sets`` register sets of page pairs per wave and ``work`` fp32 multiply-adds per pair
+    (oscar_probe_gather)."""
     _min_bytes(pool, "pool", pool_bytes(lay))
     if table_row.numel() < n_pages:
         raise TypeError(f"table_row holds {table_row.numel()} entries, needs {n_pages}")
     _check(lib().oscar_probe_gather(ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
                                     _contig(table_row, "table_row", torch.int32), n_pages,
-                                    pages_per_split, depth, _contig(sink, "sink", torch.int32),
+                                    pages_per_split, sets, work,
+                                    _contig(sink, "sink", torch.int32),
                                     sink.numel(), _stream()), "probe_gather")

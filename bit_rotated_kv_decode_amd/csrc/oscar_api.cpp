@@ -748,8 +748,8 @@ oscar_status oscar_probe_read(const void* buf, size_t bytes, uint32_t* sink, siz
 
 oscar_status oscar_probe_gather(const oscar_layout* l, const void* pool,
                                 const int32_t* page_table_row, int32_t n_pages,
-                                int32_t pages_per_split, int32_t depth, uint32_t* sink,
-                                size_t sink_words, void* stream) {
+                                int32_t pages_per_split, int32_t sets, int32_t work,
+                                uint32_t* sink, size_t sink_words, void* stream) {
   oscar_status st = check_layout(l);
   if (st != OSCAR_OK) return st;
   if (!pool || !page_table_row || !sink) return fail(OSCAR_ERR_NULL, "probe_gather: NULL pointer");
@@ -758,9 +758,11 @@ oscar_status oscar_probe_gather(const oscar_layout* l, const void* pool,
   if (n_pages < 0 || n_pages > l->num_pages || n_pages > l->max_pages_per_seq)
     return fail(OSCAR_ERR_RANGE, "probe_gather: n_pages %d outside [0, min(num_pages, "
                 "max_pages_per_seq)]", n_pages);
-  if (pages_per_split < 1 || depth < 1 || depth > 4)
-    return fail(OSCAR_ERR_RANGE, "probe_gather: pages_per_split %d < 1 or depth %d outside [1, 4]",
-                pages_per_split, depth);
+  if (pages_per_split < 1 || pages_per_split > oscar::kMaxPagesPerSplit || sets < 1 || sets > 4 ||
+      work < 0 || work > (1 << 20))
+    return fail(OSCAR_ERR_RANGE, "probe_gather: pages_per_split %d outside [1, %d], sets %d "
+                "outside [1, 4] or work %d outside [0, 2^20]", pages_per_split,
+                oscar::kMaxPagesPerSplit, sets, work);
   const long long blocks =
       static_cast<long long>((n_pages + pages_per_split - 1) / pages_per_split) * l->num_kv_heads;
   if (blocks > (1LL << 30)) return fail(OSCAR_ERR_RANGE, "probe_gather: grid too large");
@@ -769,7 +771,8 @@ oscar_status oscar_probe_gather(const oscar_layout* l, const void* pool,
   if (n_pages == 0) return ok();
   return hip_status(oscar::launch_probe_gather(pool, page_table_row, n_pages, l->num_kv_heads,
                                                oscar::block_bytes(n_groups(l)), pages_per_split,
-                                               depth, sink, static_cast<hipStream_t>(stream)),
+                                               sets, work, sink,
+                                               static_cast<hipStream_t>(stream)),
                     "oscar_probe_gather");
 }
 

@@ -204,7 +204,7 @@ hipError_t launch_demote(const DemoteArgs& a, hipStream_t stream);
 hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream);
 hipError_t launch_probe_gather(const void* pool, const int32_t* table, int n_pages, int hkv,
-                               int block_bytes, int pages_per_split, int depth, uint32_t* sink,
+                               int block_bytes, int pages_per_split, int sets, int work, uint32_t* sink,
                                hipStream_t stream);
 // Library-owned decode workspace of oscar_decode_step_noalloc (noalloc.hip): one array of this
 // many bytes per GPU, its device address looked up once per device.

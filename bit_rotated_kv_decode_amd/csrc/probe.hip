@@ -4,8 +4,11 @@
 //                        eight loads in flight per thread): the plain streaming-read ceiling.
 //   probe_gather_kernel  the INT2 pool's (page, KV head) blocks through a page table in the
 //                        attention kernel's grid and wave order (blocks of four waves on a page
-//                        range of one KV head, wave w taking pages p0 + w + 4 i), with DEPTH
-//                        pages in flight per wave: what that access pattern alone can reach.
+//                        range of one KV head, wave w taking a contiguous quarter of it, its page
+//                        ids read once up front, pairs of pages in SETS register sets used in
+//                        turn with static waits), plus WORK dependency-free fp32 FMAs per pair:
+//                        what that access pattern reaches alone (WORK 0) and how per-pair
+//                        arithmetic on each wave's critical path stretches it.
 #include "device_common.h"
 #include "oscar_internal.h"
 
@@ -35,46 +38,78 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict
   if (acc == kNever) sink[blockIdx.x] = acc;
 }
 
-template <int DEPTH>
+template <int SETS>
 __global__ __launch_bounds__(256) void probe_gather_kernel(const uint8_t* __restrict__ pool,
                                                            const int32_t* __restrict__ table,
                                                            int n_pages, int hkv, int block_bytes,
-                                                           int pages_per_split,
+                                                           int pages_per_split, int work,
                                                            uint32_t* sink) {
   const int kv = blockIdx.x % hkv, split = blockIdx.x / hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int p0 = split * pages_per_split;
   const int p1 = min(p0 + pages_per_split, n_pages);
-  const int meta16 = (block_bytes - kMetaOff) / 16;   // 16-byte chunks of the meta region
+  const int qw = (pages_per_split + 3) >> 2;   // at most 64: one id per lane
+  const int w0 = p0 + wave * qw, w1 = min(w0 + qw, p1);
+  const int npairs = w1 > w0 ? (w1 - w0 + 1) >> 1 : 0;
+  const int ids = w1 > w0 ? table[min(w0 + lane, w1 - 1)] : 0;
   struct Regs {
     uint4 c[4];
-    uint4 m;
+    uint2 m[2];
   };
-  auto load = [&](int pg, Regs& r) {
-    const uint8_t* blk = pool + (static_cast<int64_t>(table[pg]) * hkv + kv) * block_bytes;
-    const uint4* q = reinterpret_cast<const uint4*>(blk);
+  // a slot past the wave's pages reads nothing (zero-length range), so every round issues the
+  // same loads and the waits stay static
+  auto load_pair = [&](int q, Regs* r) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r.c[k] = dev::load_stream(q + 64 * k + lane);
-    r.m = lane < meta16 ? dev::load_stream(q + 256 + lane) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int pg = w0 + 2 * q + i;
+      const int pid = __builtin_amdgcn_readlane(ids, min(pg, w1 - 1) - w0);
+      const uint8_t* blk = pool + (static_cast<int64_t>(pid) * hkv + kv) * block_bytes;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(blk), 0, pg < w1 ? block_bytes : 0, 0x00020000);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        r[i].c[k] = dev::to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, k * 1024 + lane * 16, 0, 2));
+      // the meta region: 512 bytes (group 128) or 1024 (group 64)
+      r[i].m[0] = dev::to_uint2(__builtin_amdgcn_raw_buffer_load_b64(rs, kMetaOff + lane * 8, 0, 2));
+      r[i].m[1] = dev::to_uint2(
+          __builtin_amdgcn_raw_buffer_load_b64(rs, kMetaOff + 512 + lane * 8, 0, 2));
+    }
   };
-  uint32_t acc = 0;
-  Regs r[DEPTH];
-  int pg = p0 + wave;
+  float f[8];
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k)
-    if (pg + 4 * k < p1) load(pg + 4 * k, r[k]);
-  for (int i = 0; pg < p1; ++i, pg += 4) {
-    // consume the oldest set, then refill it with the page DEPTH steps ahead
+  for (int i = 0; i < 8; ++i) f[i] = 1.0f + static_cast<float>(i);
+  auto use = [&](const Regs* r) {
+    uint32_t x = 0;
 #pragma unroll
-    for (int k = 0; k < DEPTH; ++k) {
-      if (k == i % DEPTH) {
-        acc ^= fold(r[k].c[0]) ^ fold(r[k].c[1]) ^ fold(r[k].c[2]) ^ fold(r[k].c[3]) ^
-               fold(r[k].m);
-        if (pg + 4 * DEPTH < p1) load(pg + 4 * DEPTH, r[k]);
+    for (int i = 0; i < 2; ++i)
+      x ^= fold(r[i].c[0]) ^ fold(r[i].c[1]) ^ fold(r[i].c[2]) ^ fold(r[i].c[3]) ^ r[i].m[0].x ^
+           r[i].m[0].y ^ r[i].m[1].x ^ r[i].m[1].y;
+    const float xf = __uint_as_float((x & 0x007FFFFFu) | 0x3F800000u);
+    for (int c = 0; c < work; c += 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = fmaf(f[i], xf, 0.5f);
+    }
+  };
+  if (npairs > 0) {
+    Regs r[SETS][2];
+#pragma unroll
+    for (int k = 0; k < SETS; ++k) load_pair(k, r[k]);
+    int q = 0;
+    for (; q + SETS < npairs; q += SETS) {
+#pragma unroll
+      for (int k = 0; k < SETS; ++k) {
+        use(r[k]);
+        load_pair(q + k + SETS, r[k]);
       }
     }
+#pragma unroll
+    for (int k = 0; k < SETS; ++k)
+      if (q + k < npairs) use(r[k]);
   }
-  if (acc == kNever) sink[blockIdx.x * 4 + wave] = acc;
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t += f[i];
+  if (__float_as_uint(t) == kNever) sink[blockIdx.x * 4 + wave] = kNever;
 }
 
 }  // namespace
@@ -87,20 +122,20 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int 
 }
 
 hipError_t launch_probe_gather(const void* pool, const int32_t* table, int n_pages, int hkv,
-                               int block_bytes, int pages_per_split, int depth, uint32_t* sink,
-                               hipStream_t stream) {
+                               int block_bytes, int pages_per_split, int sets, int work,
+                               uint32_t* sink, hipStream_t stream) {
   const int splits = (n_pages + pages_per_split - 1) / pages_per_split;
   const dim3 grid(splits * hkv);
   const uint8_t* p = static_cast<const uint8_t*>(pool);
-  switch (depth) {
+  switch (sets) {
     case 1: hipLaunchKernelGGL(probe_gather_kernel<1>, grid, dim3(256), 0, stream, p, table,
-                               n_pages, hkv, block_bytes, pages_per_split, sink); break;
+                               n_pages, hkv, block_bytes, pages_per_split, work, sink); break;
     case 2: hipLaunchKernelGGL(probe_gather_kernel<2>, grid, dim3(256), 0, stream, p, table,
-                               n_pages, hkv, block_bytes, pages_per_split, sink); break;
+                               n_pages, hkv, block_bytes, pages_per_split, work, sink); break;
     case 3: hipLaunchKernelGGL(probe_gather_kernel<3>, grid, dim3(256), 0, stream, p, table,
-                               n_pages, hkv, block_bytes, pages_per_split, sink); break;
+                               n_pages, hkv, block_bytes, pages_per_split, work, sink); break;
     default: hipLaunchKernelGGL(probe_gather_kernel<4>, grid, dim3(256), 0, stream, p, table,
-                                n_pages, hkv, block_bytes, pages_per_split, sink); break;
+                                n_pages, hkv, block_bytes, pages_per_split, work, sink); break;
   }
   return hipGetLastError();
 }

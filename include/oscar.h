@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 5u
+#define OSCAR_ABI_VERSION 6u
 
 typedef int32_t oscar_status;
 
@@ -400,14 +400,18 @@ oscar_status oscar_probe_read(const void* buf, size_t bytes, uint32_t* sink, siz
 
 /* Reads the INT2 pool's (page, KV head) blocks of the pages page_table_row[0 .. n_pages) (device
  * int32, entries in [0, num_pages)), every KV head, in the decode kernel's order: workgroups of
- * four waves on `pages_per_split` consecutive logical pages of one KV head, wave w taking pages
- * w, w + 4, ..., with `depth` (1..4) pages in flight per wave.  sink: device uint32 array of at
- * least 4 * ceil(n_pages / pages_per_split) * num_kv_heads words.  Returns OSCAR_OK, or NULL /
- * SHAPE / ALIGN / RANGE / HIP. */
+ * four waves on `pages_per_split` (1..256) consecutive logical pages of one KV head, wave w taking
+ * the w-th contiguous quarter of them, its page ids read once before any page, pairs of pages
+ * loaded into `sets` (1..4) register sets used in turn -- the next sets' loads in flight while one
+ * is consumed -- and `work` (0..2^20) dependency-free fp32 multiply-adds per lane on each pair as
+ * it is consumed (a stand-in for the attention arithmetic that sits on each wave's path between
+ * one pair's arrival and the next pair's issue).  sink: device uint32 array of at least
+ * 4 * ceil(n_pages / pages_per_split) * num_kv_heads words.  Returns OSCAR_OK, or NULL / SHAPE /
+ * ALIGN / RANGE / HIP. */
 oscar_status oscar_probe_gather(const oscar_layout* layout, const void* pool,
                                 const int32_t* page_table_row, int32_t n_pages,
-                                int32_t pages_per_split, int32_t depth, uint32_t* sink,
-                                size_t sink_words, void* stream);
+                                int32_t pages_per_split, int32_t sets, int32_t work,
+                                uint32_t* sink, size_t sink_words, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 5
+    assert lib.oscar_abi_version() == 6
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -455,13 +455,16 @@ def test_probe_validation_happens_before_launch():
     assert lib.oscar_probe_read(buf, 64, sink, 15, 16, None) == -2
     assert lib.oscar_probe_read(buf, 0, sink, 16, 16, None) == 0      # nothing to read
     L = ctypes.byref(lay)
-    assert lib.oscar_probe_gather(L, None, buf, 4, 2, 2, sink, 64, None) == -1
-    assert lib.oscar_probe_gather(L, buf, buf, 11, 2, 2, sink, 64, None) == -4   # > num_pages
-    assert lib.oscar_probe_gather(L, buf, buf, 4, 0, 2, sink, 64, None) == -4
-    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 5, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, None, buf, 4, 2, 2, 0, sink, 64, None) == -1
+    assert lib.oscar_probe_gather(L, buf, buf, 11, 2, 2, 0, sink, 64, None) == -4   # > num_pages
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 0, 2, 0, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 257, 2, 0, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 5, 0, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 0, 0, sink, 64, None) == -4
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 2, -1, sink, 64, None) == -4
     # 2 splits x 8 heads x 4 waves = 64 sink words needed
-    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 2, sink, 63, None) == -2
-    assert lib.oscar_probe_gather(L, buf, buf, 0, 2, 2, sink, 0, None) == 0
+    assert lib.oscar_probe_gather(L, buf, buf, 4, 2, 2, 0, sink, 63, None) == -2
+    assert lib.oscar_probe_gather(L, buf, buf, 0, 2, 2, 0, sink, 0, None) == 0
 
 
 def _call_step_noalloc(lay, **over):
