@@ -30,7 +30,7 @@ def _note(msg):
 class FullLayer:
     """One layer of a workload at full size on the GPU after one decode step."""
 
-    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None, levels=None):
+    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None, levels=None, codebook=None):
         self.wl, self.layer = wl, layer
         self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
         self.B = len(self.lengths)
@@ -42,16 +42,24 @@ class FullLayer:
         self.clip_k, self.clip_v = (np.asarray(c, np.float32) for c in clip)
         # optional equally spaced codebooks, (lo, step) per KV head for keys and for values
         self.levels = None if levels is None else tuple(np.asarray(x, np.float32) for x in levels)
+        # optional symmetric Lloyd-Max codebooks, (l0, l1) per KV head for keys and for values
+        # (reading R21); the oracle takes their four levels from the same fp32 values
+        assert levels is None or codebook is None
+        self.cb = None if codebook is None else tuple(np.asarray(x, np.float32) for x in codebook)
+        self.cb4 = None if codebook is None else tuple(
+            np.stack([oracle.symmetric_levels(float(a), float(c)) for a, c in x]) for x in self.cb)
         self.geom = oracle.Geometry(group=wl.group_size)
         self.lay = ok.make_layout(wl.num_q_heads, hkv, self.num_pages, self.B,
-                                  self.table.shape[1], wl.group_size)
+                                  self.table.shape[1], wl.group_size,
+                                  levels_kind=0 if codebook is None else ok.LEVELS_SYMMETRIC)
         dev = "cuda"
         cache = ok.Cache.allocate(self.lay, zero=False)
         table = torch.from_numpy(self.table).to(dev)
         uk, uv = self.u_k.to(dev).contiguous(), self.u_v.to(dev).contiguous()
         ck, cv = torch.from_numpy(self.clip_k).to(dev), torch.from_numpy(self.clip_v).to(dev)
-        lk, lv = ((None, None) if self.levels is None else
-                  (torch.from_numpy(self.levels[0]).to(dev), torch.from_numpy(self.levels[1]).to(dev)))
+        given = self.levels if self.levels is not None else self.cb
+        lk, lv = ((None, None) if given is None else
+                  (torch.from_numpy(given[0]).to(dev), torch.from_numpy(given[1]).to(dev)))
         # history: shared-prefix pages once (from the longest sequence), private pages per
         # sequence (including the copies of prefix pages a short sequence will write into)
         n_hist = [max(0, L - 320) for L in self.lengths]
@@ -107,8 +115,9 @@ class FullLayer:
             for i, (tensor, x, u, c) in enumerate((("k", k, self.u_k, self.clip_k),
                                                    ("v", v, self.u_v, self.clip_v))):
                 lv = None if self.levels is None else self.levels[i][h]
+                cb = None if self.cb4 is None else self.cb4[i][h]
                 flips += check_token(blk, t % 64, tensor, x[h][None], u[h].numpy(), c[h],
-                                     self.geom, (b, t, h, tensor), lv)
+                                     self.geom, (b, t, h, tensor), lv, cb)
         assert flips <= MAX_FLIP_FRACTION * len(samples) * 2 * 128 + 1, flips
         return flips
 
@@ -126,12 +135,63 @@ class FullLayer:
         heads = [(0, kv * wl.gqa + i) for i in range(wl.gqa)]
         ref, _ = oracle.decode_attention(pool, table, *seg, [0], [L],
                                          bf16_np(self.q[b:b + 1]), self.u_k.numpy(),
-                                         self.u_v.numpy(), g, heads=heads)
+                                         self.u_v.numpy(), g, heads=heads,
+                                         codebook_k=None if self.cb4 is None else self.cb4[0],
+                                         codebook_v=None if self.cb4 is None else self.cb4[1])
         rows = [(0, h) for _, h in heads]
         err = attention_error(self.out[b:b + 1], ref, rows)
         _note(f"  attention b={b} kv={kv} L={L}: max row error {err:.2e}")
         assert err <= ATTN_TOL
         return err
+
+
+    def check_head_bytes(self, b, h):
+        """Every history token of sequence b and KV head h after the step: the oracle encodes
+        them all and writes its own blocks; GPU blocks must match them byte for byte except in
+        tokens whose own fields differ, and those must pass the acceptance rule one by one.
+        Returns (tokens checked, tokens whose bytes differ)."""
+        g, wl = self.geom, self.wl
+        n = max(0, self.lengths[b] + 1 - 320)
+        n_pages = (n + 63) // 64
+        k, v = workloads.kv_tokens(wl, self.layer, b, 64, n, "cuda")
+        k, v = bf16_np(k[:, h]), bf16_np(v[:, h])
+        enc = []
+        for i, (x, u, c) in enumerate(((k, self.u_k, self.clip_k), (v, self.u_v, self.clip_v))):
+            cb = None if self.cb4 is None else self.cb4[i][h]
+            lv = None if self.levels is None else self.levels[i][h]
+            if cb is not None:
+                enc.append(oracle.quantize_codebook(oracle.rotate_to_fp32(x, u[h].numpy()), c[h],
+                                                    g.group, cb))
+            else:
+                enc.append(oracle.encode(x, u[h].numpy(), c[h], g.group, lv)[:3])
+        row = np.arange(n_pages, dtype=np.int64)
+        ref = oracle.new_pool(n_pages, 1, g)
+        oracle.store_history(ref, row, np.arange(n), 0, enc[0], enc[1], g)
+        ids = torch.from_numpy(self.table[b, :n_pages].astype(np.int64)).cuda()
+        got = self.blocks[:, h].index_select(0, ids).cpu().numpy()
+        ref = ref[:, 0]
+        differ = 0
+        for p in np.nonzero((got != ref).any(axis=1))[0]:
+            for slot in range(min(64, n - 64 * p)):
+                t = 64 * int(p) + slot
+                m0 = g.meta_off + slot * g.meta_bytes_per_token
+                kb = oracle.k_code_bytes(slot, g)
+                vb, vs = oracle.v_code_bytes(slot, g), oracle.v_code_shift(slot, g)
+                own = (np.array_equal(got[p, kb], ref[p, kb]) and
+                       np.array_equal(got[p, m0:m0 + g.meta_bytes_per_token],
+                                      ref[p, m0:m0 + g.meta_bytes_per_token]) and
+                       np.array_equal((got[p, vb] >> vs) & 3, (ref[p, vb] >> vs) & 3))
+                if own:
+                    continue
+                differ += 1
+                for i, (tensor, x, u, c) in enumerate((("k", k, self.u_k, self.clip_k),
+                                                       ("v", v, self.u_v, self.clip_v))):
+                    check_token(got[p], slot, tensor, x[t][None], u[h].numpy(), c[h], g,
+                                (b, t, h, tensor),
+                                None if self.levels is None else self.levels[i][h],
+                                None if self.cb4 is None else self.cb4[i][h])
+        assert differ <= MAX_FLIP_FRACTION * n * 2 * 128 + 1, differ
+        return n, differ
 
 
 def _samples(rng, layer, count, heads=None):
@@ -155,7 +215,9 @@ def test_full_size_qwen3_8b_100k():
     layer = FullLayer(wl, layer=0)
     rng = np.random.default_rng(31)
     _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
-    for kv in (0, 5):
+    n, differ = layer.check_head_bytes(0, 2)
+    _note(f"  KV head 2: all {n} history tokens' bytes, {differ} tokens inside rounding windows")
+    for kv in range(wl.num_kv_heads):     # all 32 query rows
         layer.check_attention(0, kv)
 
 
@@ -181,6 +243,34 @@ def test_full_size_qwen3_8b_100k_equally_spaced_codebook():
     rng = np.random.default_rng(35)
     _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
     for kv in (1, 6):
+        layer.check_attention(0, kv)
+
+
+def test_full_size_qwen3_8b_100k_symmetric_codebook():
+    # layer 2 of the benchmark workload with symmetric Lloyd-Max codebooks per KV head (reading
+    # R21), fitted by the oracle on the coordinates of the layer's first 2,048 history tokens;
+    # attention through the codebook decode (decode_step on a levels_kind 1 layout)
+    wl = workloads.get("qwen3_8b_100k")
+    u_k, u_v = workloads.rotation_bases(wl, 2)
+    k, v = workloads.kv_tokens(wl, 2, 0, 64, 2048, "cuda")
+    k, v = bf16_np(k), bf16_np(v)
+    cbs = []
+    for x, u in ((k, u_k), (v, u_v)):
+        cb = []
+        for h in range(wl.num_kv_heads):
+            xr = oracle.rotate_to_fp32(x[:, h], u[h].numpy())
+            lv = oracle.lloyd_max_symmetric(
+                oracle.codebook_coordinates(xr, wl.clip, wl.group_size), iters=30)[0]
+            cb.append((lv[0], lv[1]))
+        cbs.append(np.array(cb, np.float32))
+    _note(f"qwen3_8b_100k layer 2 with symmetric codebooks: keys {cbs[0][:2].round(3).tolist()}, "
+          f"values {cbs[1][:2].round(3).tolist()}")
+    layer = FullLayer(wl, layer=2, codebook=cbs)
+    rng = np.random.default_rng(36)
+    _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    n, differ = layer.check_head_bytes(0, 4)
+    _note(f"  KV head 4: all {n} history tokens' bytes, {differ} tokens inside rounding windows")
+    for kv in range(wl.num_kv_heads):
         layer.check_attention(0, kv)
 
 
