@@ -43,9 +43,12 @@
  *      offset 2048   value codes  2048 bytes = 512 words of 16 codes
  *      offset 4096   meta         [64 tokens][key: G x (fp16 scale, fp16 zero),
  *                                             value: G x (fp16 scale, fp16 zero)]
- *  Key word (t, w) holds channels 16w .. 16w+15 of token t (w < 8), value word (c, u) holds
- *  tokens 16u .. 16u+15 of channel c (u < 4); inside a word, element 4b+i of the 16 sits in bits
- *  [2i, 2i+1] of byte b.  Words are tiled for 16-byte loads by a 64-lane wave: each region is
+ *  Key word (t, w) holds channels 16w .. 16w+15 of token t (w < 8); inside it, element 4b+i of
+ *  the 16 sits in bits [2i, 2i+1] of byte b.  Value word (c, u) holds channel c of the 16 tokens
+ *  16 s + 4 u + j (s, j = 0..3: four consecutive tokens of every 16-token tile), the code of token
+ *  16 s + 4 u + j at position 8 (j / 2) + 2 s + (j % 2) (bits [2 pos, 2 pos + 1] of the word); this
+ *  order makes the word, spread to nibbles, the matrix cores' FP4 operand in the token order the
+ *  score tiles produce.  Words are tiled for 16-byte loads by a 64-lane wave: each region is
  *  two rows of 64 chunks of 16 bytes (4 words), and
  *      key word (t = 16 st + n, w = 4 hf + q)  ->  word index 4 (64 (st / 2) + 16 q + n) + 2 (st % 2) + hf
  *      value word (c = 16 nt + n, u)           ->  word index 4 (64 (nt / 4) + 16 u + n) + nt % 4
