@@ -65,6 +65,12 @@ def parse():
     ap.add_argument("--codebook", default=None, metavar="L0,L1",
                     help="demote with the symmetric codebook (l0, l1, 3 - l1, 3 - l0) on every "
                          "KV head, keys and values, and attend with its levels")
+    ap.add_argument("--cascade", action="store_true",
+                    help="with a shared prefix, time the shared-prefix cascade step "
+                         "(oscar_decode_step_prefix) as the step, the plain step beside it")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="with a shared prefix, time the plain step alone (by default the cascade "
+                         "step is timed beside it)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibration of the HBM byte counters) and exit")
@@ -169,6 +175,12 @@ class Layer:
         self.v_new = torch.cat(vn).contiguous()
         self.q = workloads.queries(wl, layer, 0, dev, batch=B).contiguous()
         self.out = torch.empty((B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+        # the shared prefix as the cascade takes it: the prefix's page ids and, per sequence, how
+        # many leading pages of its row are those
+        ids, shared = workloads.shared_prefix(wl, self.table_np, self.lengths, spare)
+        ok.check_shared_prefix(self.lay, self.table_np, ids, shared)
+        self.prefix_ids = torch.from_numpy(ids).to(dev)
+        self.shared_pages = torch.from_numpy(shared).to(dev)
 
 
 def distribution(xs, digits):
@@ -289,7 +301,13 @@ def main():
     n_layers = args.layers or wl.num_layers
     lengths = workloads.context_lengths(wl)
     B = len(lengths)
+    # with a shared prefix both steps are timed (unless --no-cascade): the plain one as the
+    # step, or the cascade one with --cascade, and the other beside it
+    both = bool(wl.shared_prefix) and not args.no_cascade
+    cascade = both and args.cascade
     total_steps = args.warmup + args.steps + 2       # +2: graph capture warm-up and capture
+    if both:
+        total_steps *= 2                             # the other step is timed after it
     dev = "cuda"
 
     t0 = time.time()
@@ -311,16 +329,28 @@ def main():
     pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     max_len = max(lengths) + total_steps + 4
-    ws = torch.empty(ok.decode_workspace_bytes(layers[0].lay, B, max_len), dtype=torch.uint8,
-                     device=dev)
+    n_prefix = layers[0].prefix_ids.numel() if both else 0
+    ws = torch.empty(ok.decode_workspace_bytes_prefix(layers[0].lay, B, max_len, n_prefix),
+                     dtype=torch.uint8, device=dev)
 
-    def step():
+    def plain_step():
         for Lr in layers:
             c = Lr.cache
             ok.decode_step(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
                            Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos,
                            Lr.q, Lr.out, ws, max_len, levels_k=Lr.levels, levels_v=Lr.levels)
         pos.add_(1)
+
+    def cascade_step():
+        for Lr in layers:
+            c = Lr.cache
+            ok.decode_step_prefix(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k,
+                                  c.recent_v, Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new,
+                                  Lr.v_new, slots, pos, Lr.q, Lr.prefix_ids, Lr.shared_pages,
+                                  Lr.out, ws, max_len)
+        pos.add_(1)
+
+    step, other_step = (cascade_step, plain_step) if cascade else (plain_step, cascade_step)
 
     def capture(fn):
         s = torch.cuda.Stream()
@@ -335,34 +365,43 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    graph = None if args.no_graph else capture(step)
-    if graph is None:
-        step()
-        step()
+    def time_steps(fn):
+        """Warm-up, then args.steps whole decode steps (HIP events around each step on the launch
+        stream for the distribution; the wall clock between two synchronisations for the mean).
+        Returns (ms per step, per-step ms, steps run before the timed ones, graph or None)."""
+        graph = None if args.no_graph else capture(fn)
+        if graph is None:
+            fn()
+            fn()
 
-    def run_step():
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
+        def run_step():
+            if graph is not None:
+                graph.replay()
+            else:
+                fn()
 
-    # ---- timed region 1: whole decode steps (HIP events around each step on the launch stream
-    # for the distribution; the wall clock between two synchronisations for the mean)
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-    steps_before = int(pos[0].item()) - lengths[0]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = time.perf_counter()
-    for e_a, e_b in evs:
-        e_a.record()
-        run_step()
-        e_b.record()
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    step_ms = [e_a.elapsed_time(e_b) for e_a, e_b in evs]
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+        before = int(pos[0].item()) - lengths[0]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t_start = time.perf_counter()
+        for e_a, e_b in evs:
+            e_a.record()
+            run_step()
+            e_b.record()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+        return ((t_end - t_start) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in evs],
+                before, graph)
+
+    # ---- timed region 1: whole decode steps
+    ms_per_step, step_ms, steps_before, graph = time_steps(step)
+    if both:
+        # the same steps the other way, timed right after on the same pools
+        other_ms, other_step_ms, _, other_graph = time_steps(other_step)
+        del other_graph
 
     # ---- timed region 2: the segment-pass kernel (INT2 history + BF16 sink / recent blocks in
     # one launch) exactly as a step launches it, once per layer pool: a graph of n_layers launches
@@ -381,7 +420,10 @@ def main():
 
     def attn(i, stages):
         a = seg_args(i)
-        if layers[i].lay.levels_kind == ok.LEVELS_SYMMETRIC:
+        if cascade:
+            ok.decode_attn_prefix(*a[:12], layers[i].prefix_ids, layers[i].shared_pages,
+                                  *a[12:], stages=stages)
+        elif layers[i].lay.levels_kind == ok.LEVELS_SYMMETRIC:
             ok.decode_attn_codebook(*a[:12], layers[i].levels, layers[i].levels, *a[12:],
                                     stages=stages)
         else:
@@ -466,7 +508,11 @@ def main():
         "step_ms": distribution(step_ms, 4),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_bytes": int(step_bytes),
-        "roofline": {"kernel": "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)",
+        "roofline": {"kernel": ("cascade_kernel + attn_kernel (shared-prefix chunks staged in LDS "
+                               "per group of 16 sequences, then the INT2 split-KV items of the "
+                               "other pages + BF16 sink/recent blocks; two launches timed as one)"
+                               if cascade else
+                               "attn_kernel (INT2 split-KV history + BF16 sink/recent blocks)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(wl.name),
@@ -479,6 +525,19 @@ def main():
                                f"{seg_reps * n_layers} launches ({seg_reps} per layer pool), "
                                f"per-launch mean"},
     }
+    if both:
+        casc_ms, plain_ms = (ms_per_step, other_ms) if cascade else (other_ms, ms_per_step)
+        result["cascade"] = {
+            "prefix_pages": n_prefix,
+            "chunks": n_prefix // 12,
+            "timed_as_step": "cascade" if cascade else "plain",
+            "cascade_ms_per_step": round(casc_ms, 4),
+            "plain_ms_per_step": round(plain_ms, 4),
+            "other_step_ms": distribution(other_step_ms, 4),
+            "cascade_speedup_vs_plain": round(plain_ms / casc_ms, 3),
+            "note": "the same decode steps on the same pools, the other way (oscar_decode_step: "
+                    "split-KV items read every page of every sequence; oscar_decode_step_prefix: "
+                    "cascade blocks take the shared chunks), timed right after the step"}
     if not args.no_probes:
         result["probes"] = probes(wl, layers, args.steps)
     if not args.no_bf16_baseline:

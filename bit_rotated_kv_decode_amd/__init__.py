@@ -23,8 +23,9 @@ import torch
 __all__ = [
     "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
     "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "decode_splits",
-    "check_page_table",
-    "demote", "append", "decode_attn", "decode_step", "decode_step_noalloc", "Cache",
+    "check_page_table", "decode_workspace_bytes_prefix", "check_shared_prefix",
+    "demote", "append", "decode_attn", "decode_attn_codebook", "decode_attn_prefix",
+    "decode_step", "decode_step_prefix", "decode_step_noalloc", "Cache",
     "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16", "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
     "RECENT_TOKENS", "bf16_page_block_bytes", "bf16_page_bytes", "bf16_pool_bytes",
     "bf16_decode_workspace_bytes", "bf16_store", "bf16_decode_attn", "probe_read",
@@ -89,6 +90,14 @@ _SIGNATURES = {
                                                        ctypes.c_size_t, _i32, _i32, _vp]),
     "oscar_decode_step_noalloc": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _i32,
                                                                _i32, _vp]),
+    "oscar_decode_workspace_bytes_prefix": (ctypes.c_size_t, [_LP, _i32, _i32, _i32]),
+    "oscar_check_shared_prefix": (_i32, [_LP, _vp, _i32, _vp, _vp, _i32]),
+    "oscar_decode_attn_prefix": (_i32, [_LP] + [_vp] * 13 + [_i32, ctypes.c_float, _vp, _vp,
+                                                              _vp, ctypes.c_size_t, _i32, _i32,
+                                                              ctypes.c_uint32, _vp]),
+    "oscar_decode_step_prefix": (_i32, [_LP] + [_vp] * 17 + [_i32, ctypes.c_float, _vp, _vp,
+                                                              _vp, ctypes.c_size_t, _i32, _i32,
+                                                              _vp]),
     "oscar_bf16_page_block_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_page_bytes": (ctypes.c_size_t, [_LP]),
     "oscar_bf16_pool_bytes": (ctypes.c_size_t, [_LP]),
@@ -164,6 +173,12 @@ def decode_workspace_bytes(lay: Layout, batch: int, max_seq_len: int) -> int:
     return lib().oscar_decode_workspace_bytes(ctypes.byref(lay), batch, max_seq_len)
 
 
+def decode_workspace_bytes_prefix(lay: Layout, batch: int, max_seq_len: int,
+                                  prefix_pages: int) -> int:
+    return lib().oscar_decode_workspace_bytes_prefix(ctypes.byref(lay), batch, max_seq_len,
+                                                     prefix_pages)
+
+
 def decode_splits(lay: Layout, batch: int, max_seq_len: int):
     """(splits per (sequence, KV head), history pages per split) of the decode work plan."""
     pps = ctypes.c_int32(0)
@@ -181,6 +196,21 @@ def check_page_table(lay: Layout, page_table, seq_lens, extra_tokens: int = 0) -
         raise OscarError("page table must be [batch, max_pages_per_seq] with one length per row")
     _check(lib().oscar_check_page_table(ctypes.byref(lay), pt.data_ptr(), sl.data_ptr(),
                                         sl.numel(), extra_tokens), "check_page_table")
+
+
+def check_shared_prefix(lay: Layout, page_table, prefix_ids, shared_pages) -> None:
+    """Validate host copies of a shared-prefix description (oscar_check_shared_prefix): page ids
+    in range and, per sequence b, its first shared_pages[b] page-table entries equal to
+    prefix_ids[0 ..)."""
+    pt = torch.as_tensor(page_table, dtype=torch.int32).cpu().contiguous()
+    ids = torch.as_tensor(prefix_ids, dtype=torch.int32).cpu().contiguous().reshape(-1)
+    sh = torch.as_tensor(shared_pages, dtype=torch.int32).cpu().contiguous().reshape(-1)
+    if pt.dim() != 2 or pt.shape[1] != lay.max_pages_per_seq or pt.shape[0] != sh.numel():
+        raise OscarError("page table must be [batch, max_pages_per_seq] with one shared_pages "
+                         "entry per row")
+    _check(lib().oscar_check_shared_prefix(ctypes.byref(lay), pt.data_ptr(), sh.numel(),
+                                           ids.data_ptr(), sh.data_ptr(), ids.numel()),
+           "check_shared_prefix")
 
 
 # ----------------------------------------------------------------------------------------------
@@ -369,6 +399,46 @@ def decode_attn_codebook(lay: Layout, pool, page_table, sink_k, sink_v, recent_k
         int(stages), _stream()), "decode_attn_codebook")
 
 
+def _prefix(prefix_ids: torch.Tensor, shared_pages: torch.Tensor, bsz: int):
+    if prefix_ids.dim() != 1:
+        raise TypeError("prefix_ids must be int32 [prefix_pages]")
+    _rows(shared_pages, "shared_pages", bsz)
+    n = prefix_ids.numel()
+    if n == 0:
+        return None, None, 0
+    return (_contig(prefix_ids, "prefix_ids", torch.int32),
+            _contig(shared_pages, "shared_pages", torch.int32), n)
+
+
+def decode_attn_prefix(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v,
+                       seq_slot, seq_lens, q: torch.Tensor, u_k, u_v, prefix_ids: torch.Tensor,
+                       shared_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                       max_seq_len: int, lse: Optional[torch.Tensor] = None,
+                       sm_scale: float = 0.0, stages: int = STAGE_ALL) -> None:
+    """decode_attn for sequences that share a prefix through the page table
+    (oscar_decode_attn_prefix): prefix_ids int32 [P] = the prefix's page ids, shared_pages int32
+    [B] = leading pages of each row that are those.  The same result as decode_attn; whole chunks
+    of shared pages are read once per group of sequences.  workspace: at least
+    decode_workspace_bytes_prefix(lay, B, max_seq_len, P) bytes."""
+    bsz = seq_lens.numel()
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
+    ids, shared, n = _prefix(prefix_ids, shared_pages, bsz)
+    _check(lib().oscar_decode_attn_prefix(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_lens, "seq_lens", torch.int32), _contig(q, "q", torch.bfloat16),
+        _contig(u_k, "u_k", torch.float32), _contig(u_v, "u_v", torch.float32), ids, shared, n,
+        float(sm_scale), _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        int(stages), _stream()), "decode_attn_prefix")
+
+
 def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
                 clip_k, clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot, seq_pos,
                 q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
@@ -400,6 +470,39 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
         _stream()), "decode_step")
+
+
+def decode_step_prefix(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k,
+                       u_v, clip_k, clip_v, k_new: torch.Tensor, v_new: torch.Tensor, seq_slot,
+                       seq_pos, q: torch.Tensor, prefix_ids: torch.Tensor,
+                       shared_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                       max_seq_len: int, lse: Optional[torch.Tensor] = None,
+                       sm_scale: float = 0.0) -> None:
+    """decode_step over a shared prefix (oscar_decode_step_prefix): append, then
+    decode_attn_prefix over seq_pos + 1 tokens."""
+    bsz = seq_pos.numel()
+    if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
+        raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
+    if tuple(q.shape) != (bsz, lay.num_q_heads, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise TypeError("q / out must be [batch, Hq, 128]")
+    _int2_attn_sizes(lay, bsz, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                     u_k, u_v, lse)
+    _shape(clip_k, "clip_k", (lay.num_kv_heads,))
+    _shape(clip_v, "clip_v", (lay.num_kv_heads,))
+    ids, shared, n = _prefix(prefix_ids, shared_pages, bsz)
+    _check(lib().oscar_decode_step_prefix(
+        ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
+        _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
+        _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
+        _contig(recent_v, "recent_v", torch.bfloat16), _contig(u_k, "u_k", torch.float32),
+        _contig(u_v, "u_v", torch.float32), _contig(clip_k, "clip_k", torch.float32),
+        _contig(clip_v, "clip_v", torch.float32), _contig(k_new, "k_new", torch.bfloat16),
+        _contig(v_new, "v_new", torch.bfloat16), _contig(seq_slot, "seq_slot", torch.int32),
+        _contig(seq_pos, "seq_pos", torch.int32), _contig(q, "q", torch.bfloat16), ids, shared,
+        n, float(sm_scale), _contig(out, "out", torch.float32),
+        None if lse is None else _contig(lse, "lse", torch.float32),
+        _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
+        _stream()), "decode_step_prefix")
 
 
 def decode_step_noalloc(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k,

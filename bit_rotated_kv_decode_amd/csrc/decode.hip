@@ -101,14 +101,22 @@ struct Int2Lds {
   static constexpr int RED_M = RED + 4 * G * kHeadDim * 4;    // [wave][8] fp32
   static constexpr int RED_L = RED_M + 4 * 8 * 4;
   static constexpr int TOTAL = RED_L + 4 * 8 * 4;
+  // cascade blocks: the chunk's kCascPages page blocks of one KV head, staged once for all waves
+  static constexpr int STAGE = (TOTAL + 15) & ~15;
+  static constexpr int CASC_TOTAL = STAGE + kCascPages * (kMetaOff + kPage * 8 * NG);
 };
 
 // STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
 // sequence, so no page is read twice in it; with several sequences pages may be shared (a prefix
 // cache), and cached loads let the second reader hit.
-template <int G, int NG, bool STREAM, bool CB>
+// CASC: a cascade block -- chunk `split` of a shared prefix (kCascPages pages of KV head kv, the
+// physical ids in a.prefix_ids) for the sequences of group `grp` (kCascGroup of them).  The
+// chunk's pages are staged in LDS once; each wave then takes its sequences in turn (those whose
+// history wholly holds the chunk), runs the same page-pair arithmetic as a split block against
+// the staged pages and writes the sequence's partial for the chunk itself.
+template <int G, int NG, bool STREAM, bool CB, bool CASC = false>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
-                                           int b, unsigned char* smem) {
+                                           int grp, unsigned char* smem) {
   using S = Int2Lds<G, NG>;
   constexpr int NT = S::NT, NA = S::NA;
   constexpr int BLK = kMetaOff + kPage * 8 * NG;
@@ -116,41 +124,52 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   float (*red_m)[8] = reinterpret_cast<float (*)[8]>(smem + S::RED_M);
   float (*red_l)[8] = reinterpret_cast<float (*)[8]>(smem + S::RED_L);
 
-  const int p0 = split * p.pages_per_split;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = dev::lane_id();
   const int gq = lane >> 4, n = lane & 15;
-  const int head0 = b * p.hq + kv * G;
-  // Wave w takes the contiguous pages [w0, w0 + qw) of the item.  Its first eight page ids are
-  // read with scalar loads, before anything else: they return through the scalar cache, not behind
-  // the page streams of the unit's other waves, which a vector load's return would queue after.
-  // Indices stay inside the table row; ids of pages past the sequence's end are read, never used.
+  int b = grp;                 // the sequence (a cascade block sets it per sequence)
+  int head0 = b * p.hq + kv * G;
+  // Wave w takes the contiguous pages [w0, w0 + qw) of the item, from wa = max(w0, the pages the
+  // cascade took) on.  Its first eight page ids are read with scalar loads, before anything else:
+  // they return through the scalar cache, not behind the page streams of the unit's other waves,
+  // which a vector load's return would queue after.  Indices stay inside the table row; ids of
+  // pages past the sequence's end are read, never used.  A cascade block's pages are the staged
+  // chunk: local indices 0 .. kCascPages - 1, all of them history.
   static_assert((kMaxPagesPerSplit + 3) / 4 <= 8 + 64, "eight scalar ids and one per lane");
-  const int qw = (p.pages_per_split + 3) >> 2;
-  const int w0 = p0 + wave * qw;
-  const int* trow = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
-  const int tmax = a.max_pages_per_seq - 1;
-  int ids[8];
+  int w0 = 0, w1 = kCascPages, wa = 0, n_hist = 1 << 30;
+  int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int more_ids = 0;
+  if constexpr (!CASC) {
+    const int p0 = split * p.pages_per_split;
+    const int qw = (p.pages_per_split + 3) >> 2;
+    w0 = p0 + wave * qw;
+    const int* trow = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
+    const int tmax = a.max_pages_per_seq - 1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ids[j] = trow[min(w0 + j, tmax)];
-  const int L = a.seq_lens[b] + a.len_add;
-  // ids of the wave's pages from the ninth on, one per lane, issued ahead of every page load so
-  // that waiting for it later never waits for those
-  const int more_ids = trow[min(w0 + 8 + lane, tmax)];
-  __builtin_amdgcn_sched_barrier(0);
-  // all of the above are issued before the first wait
-  asm volatile("" ::"s"(ids[0]), "s"(ids[1]), "s"(ids[2]), "s"(ids[3]), "s"(ids[4]),
-               "s"(ids[5]), "s"(ids[6]), "s"(ids[7]), "s"(L));
-  const int n_hist = max(0, L - kSink - kRecent);
-  const int n_pages = (n_hist + kPage - 1) / kPage;
-  if (p0 >= n_pages) return;
-  const int p1 = min(p0 + p.pages_per_split, n_pages);
-  const int w1 = min(w0 + qw, p1);   // w1 <= w0: a wave without pages (it still combines)
+    for (int j = 0; j < 8; ++j) ids[j] = trow[min(w0 + j, tmax)];
+    const int L = a.seq_lens[b] + a.len_add;
+    // ids of the wave's pages from the ninth on, one per lane, issued ahead of every page load so
+    // that waiting for it later never waits for those
+    more_ids = trow[min(w0 + 8 + lane, tmax)];
+    __builtin_amdgcn_sched_barrier(0);
+    // all of the above are issued before the first wait
+    asm volatile("" ::"s"(ids[0]), "s"(ids[1]), "s"(ids[2]), "s"(ids[3]), "s"(ids[4]),
+                 "s"(ids[5]), "s"(ids[6]), "s"(ids[7]), "s"(L));
+    n_hist = max(0, L - kSink - kRecent);
+    const int n_pages = (n_hist + kPage - 1) / kPage;
+    if (p0 >= n_pages) return;
+    const int p1 = min(p0 + p.pages_per_split, n_pages);
+    // pages of a shared prefix that cascade blocks took for this sequence are not this item's
+    const int cend = p.casc_chunks ? cascade_pages(p, n_hist, a.shared_pages[b]) : 0;
+    if (p1 <= cend) return;
+    w1 = min(w0 + qw, p1);   // w1 <= w0: a wave without pages (it still combines)
+    wa = max(w0, cend);
+  }
 
   // ---- key operands of the query (registers, the same for every page) and, per lane, the sums
   // of q'' of its head in each tile (head 4 ht + gq; a head the group does not have gets -inf
   // logits); loaded after the first pages' loads are issued (see the pair loop)
-  const int64_t op0 = (static_cast<int64_t>(b) * p.hkv + kv) * NA;
+  int64_t op0 = (static_cast<int64_t>(b) * p.hkv + kv) * NA;
   v8i aq[NA];
   int sq[NA];
   float sig[NT][NG], hbias[NT];
@@ -223,6 +242,21 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   for (int ht = 0; ht < NB; ++ht)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) accb[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int ht = 0; ht < NT; ++ht) {
+      m_ref[ht] = -INFINITY;
+      l_run[ht] = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) z_run[ht][g] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ht = 0; ht < NB; ++ht)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) accb[ht][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  };
 
   // One page's operands, fetched with 16-byte loads from the tiled block (one chunk row = 64 lanes
   // x 16 bytes): key chunk row j holds this lane's words of sub-tiles 2j and 2j + 1, value chunk
@@ -258,6 +292,20 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // gets a zero-length range, so its loads return zeros without touching memory and every round
   // still issues the same loads.
   auto load_page = [&](int pg, PageRegs& r) {
+    if constexpr (CASC) {
+      const uint8_t* blk = smem + S::STAGE + pg * BLK;
+      r.k[0] = *reinterpret_cast<const uint4*>(blk + kKCodesOff + lane * 16);
+      r.k[1] = *reinterpret_cast<const uint4*>(blk + kKCodesOff + 1024 + lane * 16);
+      r.v[0] = *reinterpret_cast<const uint4*>(blk + kVCodesOff + lane * 16);
+      r.v[1] = *reinterpret_cast<const uint4*>(blk + kVCodesOff + 1024 + lane * 16);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int w = 0; w < 2 * NG; ++w)
+          r.m[st][w] = reinterpret_cast<const uint32_t*>(blk + kMetaOff + n * 8 * NG +
+                                                         st * 16 * 8 * NG)[w];
+      return;
+    }
     const int pid = page_id(min(pg, w1 - 1));
     const uint8_t* blk = a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -287,15 +335,15 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       }
     }
   };
-  // pair q: pages w0 + 2 q and w0 + 2 q + 1
+  // pair q: pages wa + 2 q and wa + 2 q + 1
   auto load_pair = [&](int q, PageRegs* rr) {
-    load_page(w0 + 2 * q, rr[0]);
-    load_page(w0 + 2 * q + 1, rr[1]);
+    load_page(wa + 2 * q, rr[0]);
+    load_page(wa + 2 * q + 1, rr[1]);
   };
 
   // ---- one pair of pages
   auto process_pair = [&](int q, PageRegs* rr, bool first) {
-    const int pgs[2] = {w0 + 2 * q, w0 + 2 * q + 1};
+    const int pgs[2] = {wa + 2 * q, wa + 2 * q + 1};
     // a slot past the history (or a page past the wave's range) holds arbitrary bytes: its meta
     // becomes zero (no value contribution, finite products) and its logit -inf
     const bool tail = pgs[1] >= w1 || (pgs[1] + 1) * kPage > n_hist;
@@ -544,7 +592,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // one's, and the loop over full rounds has a single exit, so the wait counts stay exact.  The
   // query operands are loaded between the first two pairs' loads: the first pair waits on them
   // and on its own pages only.
-  const int npairs = w1 > w0 ? (w1 - w0 + 1) / 2 : 0;
+  const int npairs = w1 > wa ? (w1 - wa + 1) / 2 : 0;
   // Issue priority by the pairs a wave has left: two blocks share a compute unit, and the arbiter
   // otherwise favours the older one throughout, so the younger one would end its pages alone.
   auto set_prio = [&](int q) {
@@ -556,6 +604,61 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     else
       __builtin_amdgcn_s_setprio(1);
   };
+  float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
+  float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
+  if constexpr (CASC) {
+    // stage the chunk's page blocks of this KV head (cached loads: the other groups' blocks read
+    // the same pages)
+    constexpr int kChunks16 = BLK / 16;
+    for (int i = threadIdx.x; i < kCascPages * kChunks16; i += 256) {
+      const int pg = i / kChunks16, o = i - pg * kChunks16;
+      const int pid = a.prefix_ids[split * kCascPages + pg];
+      reinterpret_cast<uint4*>(smem + S::STAGE + pg * BLK)[o] = reinterpret_cast<const uint4*>(
+          a.pool + (static_cast<int64_t>(pid) * p.hkv + kv) * BLK)[o];
+    }
+    __syncthreads();
+    // wave w: sequences grp * kCascGroup + w + 4 i of the group for which the chunk is one of the
+    // cascade's (the chunk lies in their full history pages and their shared pages); each one's
+    // partial goes to slot `split` (the chunk) of its rows
+    for (int i = 0; i < kCascGroup / 4; ++i) {
+      b = grp * kCascGroup + wave + 4 * i;
+      if (b >= p.batch) break;
+      const int nh = max(0, a.seq_lens[b] + a.len_add - kSink - kRecent);
+      if (cascade_pages(p, nh, a.shared_pages[b]) < (split + 1) * kCascPages) continue;
+      head0 = b * p.hq + kv * G;
+      op0 = (static_cast<int64_t>(b) * p.hkv + kv) * NA;
+      reset_state();
+      load_query();
+      for (int q = 0; q < kCascPages / 2; ++q) {
+        PageRegs rr[2];
+        load_pair(q, rr);
+        process_pair(q, rr, q == 0);
+      }
+#pragma unroll
+      for (int ht = 0; ht < NT; ++ht) {
+        const int hd = 4 * ht + gq;
+        const float l = dev::row16_sum(l_run[ht]);
+        float zs[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) zs[g] = dev::row16_sum(z_run[ht][g]);
+        if (hd < G) {
+          const int64_t prow = static_cast<int64_t>(head0 + hd) * p.slots + split;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            float v = (acc[ht][nt][0] + acc[ht][nt][1]) + (acc[ht][nt][2] + acc[ht][nt][3]);
+            if constexpr (CB) {
+              const float h =
+                  (accb[ht][nt][0] + accb[ht][nt][1]) + (accb[ht][nt][2] + accb[ht][nt][3]);
+              v = fmaf(cbv_d, h, cbv_b * v);
+            }
+            pacc[prow * kHeadDim + 16 * nt + n] = v + zs[NG == 2 ? nt / 4 : 0];
+          }
+          if (n == 0) reinterpret_cast<float2*>(ml)[prow] = make_float2(m_ref[ht], l);
+        }
+      }
+    }
+    return;
+  }
   if (npairs > 0) {
     PageRegs r0[2], r1[2];
     set_prio(0);
@@ -618,8 +721,6 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // acc'[h][ch] = sum_w f_w acc_w[h][ch] with f_w = 2^(m_w - m).  Every wave has written its rows
   // (a wave without pages: m = -inf, l = 0, zero rows, so f_w = 0), and every LDS read below is
   // issued before the first one is used.
-  float* ml = reinterpret_cast<float*>(a.workspace + p.off_int2_ml);
-  float* pacc = reinterpret_cast<float*>(a.workspace + p.off_int2_acc);
   // thread i: head i / 32, channels 4 (i % 32) .. 4 (i % 32) + 3 (one 16-byte store)
   static_assert(G * kHeadDim / 4 <= 256, "one round of outputs");
   if (threadIdx.x < G * kHeadDim / 4) {
@@ -632,7 +733,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       lw[w] = red_l[w][h];
       aw[w] = reinterpret_cast<const float4*>(red_acc + (w * G + h) * kHeadDim)[jq];
     }
-    const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));   // finite: wave 0 has a page
+    const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));   // finite: a wave has pages
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float l = 0.f;
 #pragma unroll
@@ -644,7 +745,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       s4.w = fmaf(aw[w].w, f, s4.w);
       l = fmaf(lw[w], f, l);
     }
-    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
+    const int64_t prow = static_cast<int64_t>(head0 + h) * p.slots + p.casc_chunks + split;
     reinterpret_cast<float4*>(pacc + prow * kHeadDim)[jq] = s4;
     if (jq == 0) reinterpret_cast<float2*>(ml)[prow] = make_float2(mm, l);
   }
@@ -794,11 +895,35 @@ constexpr int attn_lds_bytes() {
   return i2 > Bf16Lds<G>::TOTAL ? i2 : Bf16Lds<G>::TOTAL;
 }
 
-template <int G, int NG, bool STREAM, bool CB>
-__global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p,
-                                                                    float scale_log2, int x0) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[attn_lds_bytes<G, NG>()];
-  const int x = x0 + static_cast<int>(blockIdx.x) / p.hkv, kv = blockIdx.x % p.hkv, b = blockIdx.z;
+// CASC: the launch also holds the shared-prefix cascade blocks, one per (prefix chunk, KV head,
+// group of kCascGroup sequences): casc_z z-slices of the grid, every casc_step-th slice from the
+// first, so that the chip runs them (arithmetic on staged pages) beside the segment blocks
+// (streams of private pages) instead of after them.  A cascade block of slice k is number
+// k * gridDim.x + blockIdx.x, taken KV head fastest, then group, then chunk: the groups of one
+// (chunk, KV head), which read the same pages, are dispatched hkv blocks apart -- with eight KV
+// heads, to one XCD and its L2 (workgroups go to the eight XCDs in turn).
+template <int G, int NG, bool STREAM, bool CB, bool CASC = false>
+__global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
+                                                      int x0, int casc_z, int casc_step) {
+  constexpr int kLds = CASC && Int2Lds<G, 1>::CASC_TOTAL > attn_lds_bytes<G, NG>()
+                           ? Int2Lds<G, 1>::CASC_TOTAL
+                           : attn_lds_bytes<G, NG>();
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  const int x = x0 + static_cast<int>(blockIdx.x) / p.hkv, kv = blockIdx.x % p.hkv;
+  int b = blockIdx.z;
+  if constexpr (CASC) {
+    static_assert(NG == 1 && !CB && !STREAM, "cascade blocks: single-group pass, no codebooks");
+    const int k = b / casc_step;
+    if (b % casc_step == 0 && k < casc_z) {
+      const int ci = k * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
+      if (ci >= p.casc_chunks * p.hkv * p.casc_groups) return;
+      const int rest = ci / p.hkv;
+      int2_block<G, 1, false, false, true>(a, p, rest / p.casc_groups, ci % p.hkv,
+                                           rest % p.casc_groups, smem);
+      return;
+    }
+    b -= min(k + 1, casc_z);
+  }
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
   else if constexpr (int2_fp8_pass(G, NG))
@@ -845,9 +970,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = dev::lane_id();
   const float2* iml = reinterpret_cast<const float2*>(a.workspace + p.off_int2_ml) +
-                      static_cast<int64_t>(row) * p.num_splits;
+                      static_cast<int64_t>(row) * p.slots;
   const float4* iacc = reinterpret_cast<const float4*>(a.workspace + p.off_int2_acc) +
-                       static_cast<int64_t>(row) * p.num_splits * (kHeadDim / 4);
+                       static_cast<int64_t>(row) * p.slots * (kHeadDim / 4);
   const float* bml = reinterpret_cast<const float*>(a.workspace + p.off_bf16_ml) +
                      static_cast<int64_t>(row) * kBf16Chunks * 2;
   const float* bacc = reinterpret_cast<const float*>(a.workspace + p.off_bf16_acc) +
@@ -861,7 +986,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
 #pragma unroll
   for (int i = 0; i < kMergePrefetch; ++i) {
     const int s = sr + 8 * i;
-    const bool in = s < p.num_splits;
+    const bool in = s < p.slots;
     st[i] = in ? iml[s] : make_float2(-INFINITY, 0.f);
     pa[i] = in ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
                : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -887,6 +1012,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int n_hist = max(0, L - kSink - kRecent);
   const int n_pages = (n_hist + kPage - 1) / kPage;
   const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
+  // slots of the row's partials: cascade chunks [0, casc_chunks) (those its history wholly holds
+  // were written), then splits (those holding a page past the cascade's pages and within the
+  // history: none when the cascade took every page)
+  const int cend = p.casc_chunks ? cascade_pages(p, n_hist, a.shared_pages[b]) : 0;
+  const int c_b = cend / kCascPages;
+  const int s_end = p.casc_chunks + n_valid;
+  const int s_first = cend < n_pages ? p.casc_chunks + cend / p.pages_per_split : s_end;
+  auto valid = [&](int s) { return s < c_b || (s >= s_first && s < s_end); };
 
   // ---- (1) this thread's splits (those the sequence reaches), with its own maximum
   float m_loc = -INFINITY, l_loc = 0.f;
@@ -894,7 +1027,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   auto absorb = [&](const float2* ml, const float4* v, int s0, int n) {
     float mb = -INFINITY;
     for (int i = 0; i < n; ++i)
-      if (s0 + 8 * i < n_valid) mb = fmaxf(mb, ml[i].x);
+      if (valid(s0 + 8 * i)) mb = fmaxf(mb, ml[i].x);
     if (mb == -INFINITY) return;
     const float mn = fmaxf(m_loc, mb);
     const float al = exp2f(m_loc - mn);   // 0 while nothing is held yet
@@ -905,7 +1038,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     s4.w *= al;
     m_loc = mn;
     for (int i = 0; i < n; ++i) {
-      if (s0 + 8 * i >= n_valid) continue;
+      if (!valid(s0 + 8 * i)) continue;
       const float f = exp2f(ml[i].x - mn);
       l_loc = fmaf(ml[i].y, f, l_loc);
       s4.x = fmaf(v[i].x, f, s4.x);
@@ -915,16 +1048,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
     }
   };
   absorb(st, pa, sr, kMergePrefetch);
-  // splits past the prefetch (more than 96 per row): rounds of four
-  for (int s0 = sr + 8 * kMergePrefetch; s0 < n_valid; s0 += 32) {
+  // slots past the prefetch (more than 96 per row): rounds of four
+  for (int s0 = sr + 8 * kMergePrefetch; s0 < s_end; s0 += 32) {
     float2 ml4[4];
     float4 v4[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int s = s0 + 8 * k;
-      ml4[k] = s < n_valid ? iml[s] : make_float2(-INFINITY, 0.f);
-      v4[k] = s < n_valid ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      ml4[k] = s < s_end ? iml[s] : make_float2(-INFINITY, 0.f);
+      v4[k] = s < s_end ? iacc[static_cast<int64_t>(s) * (kHeadDim / 4) + cq]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     absorb(ml4, v4, s0, 4);
   }
@@ -1032,7 +1165,25 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
   const int x0 = (stages & OSCAR_STAGE_BF16) ? 0 : kBf16Chunks;
   const int x1 = kBf16Chunks + ((stages & OSCAR_STAGE_INT2) ? p.num_splits : 0);
   bool cb_done = false;
-  if (x1 > x0) {
+  if ((stages & OSCAR_STAGE_INT2) && p.casc_chunks > 0) {
+    // the host admits a cascade on the four-head single-group pass only, without codebooks;
+    // its blocks share the segment launch (x1 > x0 here)
+    if constexpr (int2_fp8_pass(G, 1)) {
+      if (p.n_groups != 1 || a.cb_k != nullptr || a.prefix_ids == nullptr ||
+          a.shared_pages == nullptr)
+        return hipErrorInvalidValue;
+      const int gx = (x1 - x0) * p.hkv;
+      const int blocks = p.casc_chunks * p.hkv * p.casc_groups;
+      const int cz = (blocks + gx - 1) / gx;
+      const int step = (p.batch + cz) / cz;   // >= 1
+      hipLaunchKernelGGL((attn_kernel<G, 1, false, false, true>), dim3(gx, 1, p.batch + cz),
+                         dim3(256), 0, stream, a, p, scale_log2, x0, cz, step);
+      cb_done = true;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (x1 > x0 && !cb_done) {
     dim3 grid((x1 - x0) * p.hkv, 1, p.batch);
     const bool one = p.batch == 1;
     // a codebook history (cb_k / cb_v) runs on the fp8 pass; the host admits it only there
@@ -1041,10 +1192,10 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
       if (cb && p.n_groups == 1) {
         if (one)
           hipLaunchKernelGGL((attn_kernel<G, 1, true, true>), grid, dim3(256), 0, stream, a, p,
-                             scale_log2, x0);
+                             scale_log2, x0, 0, 1);
         else
           hipLaunchKernelGGL((attn_kernel<G, 1, false, true>), grid, dim3(256), 0, stream, a, p,
-                             scale_log2, x0);
+                             scale_log2, x0, 0, 1);
         cb_done = true;
       }
     }
@@ -1054,16 +1205,16 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
       return hipErrorInvalidValue;
     else if (p.n_groups == 1 && one)
       hipLaunchKernelGGL((attn_kernel<G, 1, true, false>), grid, dim3(256), 0, stream, a, p,
-                         scale_log2, x0);
+                         scale_log2, x0, 0, 1);
     else if (p.n_groups == 1)
       hipLaunchKernelGGL((attn_kernel<G, 1, false, false>), grid, dim3(256), 0, stream, a, p,
-                         scale_log2, x0);
+                         scale_log2, x0, 0, 1);
     else if (one)
       hipLaunchKernelGGL((attn_kernel<G, 2, true, false>), grid, dim3(256), 0, stream, a, p,
-                         scale_log2, x0);
+                         scale_log2, x0, 0, 1);
     else
       hipLaunchKernelGGL((attn_kernel<G, 2, false, false>), grid, dim3(256), 0, stream, a, p,
-                         scale_log2, x0);
+                         scale_log2, x0, 0, 1);
   }
   if (stages & OSCAR_STAGE_MERGE) {
     const int rows = p.batch * p.hq;

@@ -544,7 +544,7 @@ __device__ __forceinline__ void int2_block_i8(const DecodeArgs& a, const Plan& p
       s4.w = fmaf(aw[w].w, f, s4.w);
       l = fmaf(lw[w], f, l);
     }
-    const int64_t prow = static_cast<int64_t>(head0 + h) * p.num_splits + split;
+    const int64_t prow = static_cast<int64_t>(head0 + h) * p.slots + p.casc_chunks + split;
     reinterpret_cast<float4*>(pacc + prow * kHeadDim)[jq] = s4;
     if (jq == 0) reinterpret_cast<float2*>(ml)[prow] = make_float2(mm, l);
   }

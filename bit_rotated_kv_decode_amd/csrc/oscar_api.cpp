@@ -77,7 +77,7 @@ oscar_status hip_status(hipError_t e, const char* what) {
 
 namespace oscar {
 
-Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
+Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_pages) {
   Plan p;
   p.batch = batch;
   p.hq = lay.num_q_heads;
@@ -97,6 +97,12 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
+  // whole cascade chunks of the shared prefix (the cascade runs on the four-head single-group pass)
+  if (prefix_pages > 0 && int2_fp8_pass(p.gqa, p.n_groups)) {
+    p.casc_chunks = std::min(prefix_pages, p.max_pages) / kCascPages;
+    p.casc_groups = p.casc_chunks ? (batch + kCascGroup - 1) / kCascGroup : 0;
+  }
+  p.slots = p.casc_chunks + p.num_splits;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(batch) * p.hq;
   size_t off = 0;
@@ -110,9 +116,9 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.off_sigma = off;
   off = al(off + rows * 4 * 4);
   p.off_int2_ml = off;
-  off = al(off + rows * std::max(p.num_splits, 1) * 2 * 4);
+  off = al(off + rows * std::max(p.slots, 1) * 2 * 4);
   p.off_int2_acc = off;
-  off = al(off + rows * std::max(p.num_splits, 1) * kHeadDim * 4);
+  off = al(off + rows * std::max(p.slots, 1) * kHeadDim * 4);
   p.off_bf16_ml = off;
   off = al(off + rows * kBf16Chunks * 2 * 4);
   p.off_bf16_acc = off;
@@ -201,13 +207,27 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
                               const float* u_v, float sm_scale, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, int32_t batch,
                               int32_t max_seq_len, oscar::DecodeArgs& a, oscar::QueryArgs& qa,
-                              oscar::Plan& plan) {
+                              oscar::Plan& plan, const int32_t* prefix_ids = nullptr,
+                              const int32_t* shared_pages = nullptr, int32_t prefix_pages = 0) {
   oscar_status st = check_layout(l);
   if (st != OSCAR_OK) return st;
   if (batch < 0) return fail(OSCAR_ERR_RANGE, "negative batch");
+  if (prefix_pages < 0) return fail(OSCAR_ERR_RANGE, "negative prefix_pages");
+  if (prefix_pages > 0) {
+    if (prefix_ids == nullptr || shared_pages == nullptr)
+      return fail(OSCAR_ERR_NULL, "decode: a shared prefix needs prefix_ids and shared_pages");
+    if (!aligned(prefix_ids, 4) || !aligned(shared_pages, 4))
+      return fail(OSCAR_ERR_ALIGN, "decode: misaligned prefix_ids or shared_pages");
+    if (prefix_pages > l->num_pages || prefix_pages > l->max_pages_per_seq)
+      return fail(OSCAR_ERR_RANGE, "prefix_pages %d exceeds the pool or the page-table rows",
+                  prefix_pages);
+    if (l->levels_kind != 0)
+      return fail(OSCAR_ERR_SHAPE, "decode: the shared-prefix cascade runs on histories without "
+                  "symmetric codebooks (levels_kind 0)");
+  }
   if (batch == 0) return ok();
   if (max_seq_len < 1) return fail(OSCAR_ERR_RANGE, "max_seq_len %d < 1", max_seq_len);
-  plan = oscar::make_plan(*l, batch, max_seq_len);
+  plan = oscar::make_plan(*l, batch, max_seq_len, prefix_pages);
   if (plan.max_pages > l->max_pages_per_seq)
     return fail(OSCAR_ERR_RANGE, "max_seq_len %d needs %d pages > max_pages_per_seq %d",
                 max_seq_len, plan.max_pages, l->max_pages_per_seq);
@@ -247,6 +267,8 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   a.len_add = 0;
   a.cb_k = nullptr;
   a.cb_v = nullptr;
+  a.prefix_ids = plan.casc_chunks > 0 ? prefix_ids : nullptr;
+  a.shared_pages = plan.casc_chunks > 0 ? shared_pages : nullptr;
   qa.q = a.q;
   qa.u_k = u_k;
   qa.batch = batch;
@@ -485,7 +507,8 @@ oscar_status decode_attn_impl(const oscar_layout* l, const void* pool, const int
                               const float* u_v, const float* cb_k, const float* cb_v,
                               float sm_scale, float* out, float* lse, void* workspace,
                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
-                              uint32_t stages, void* stream) {
+                              uint32_t stages, void* stream, const int32_t* prefix_ids = nullptr,
+                              const int32_t* shared_pages = nullptr, int32_t prefix_pages = 0) {
   if (stages == 0 || (stages & ~OSCAR_STAGE_ALL) != 0)
     return fail(OSCAR_ERR_RANGE, "stage mask 0x%x invalid", stages);
   oscar::DecodeArgs a;
@@ -494,7 +517,8 @@ oscar_status decode_attn_impl(const oscar_layout* l, const void* pool, const int
   const oscar_status st = make_decode_args(l, pool, page_table, sink_k, sink_v, recent_k,
                                            recent_v, seq_slot, seq_lens, q, u_k, u_v, sm_scale,
                                            out, lse, workspace, workspace_bytes, batch,
-                                           max_seq_len, a, qa, plan);
+                                           max_seq_len, a, qa, plan, prefix_ids, shared_pages,
+                                           prefix_pages);
   if (st != OSCAR_OK || batch == 0) return st;
   a.cb_k = cb_k;
   a.cb_v = cb_v;
@@ -544,15 +568,18 @@ oscar_status oscar_decode_attn_codebook(const oscar_layout* l, const void* pool,
                           stages, stream);
 }
 
-oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t* page_table,
-                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
-                               const float* u_k, const float* u_v, const float* clip_k,
-                               const float* clip_v, const float* levels_k,
-                               const float* levels_v, const void* k_new, const void* v_new,
-                               const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
-                               float sm_scale, float* out, float* lse, void* workspace,
-                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
-                               void* stream) {
+namespace {
+
+oscar_status decode_step_impl(const oscar_layout* l, void* pool, const int32_t* page_table,
+                              void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                              const float* u_k, const float* u_v, const float* clip_k,
+                              const float* clip_v, const float* levels_k,
+                              const float* levels_v, const void* k_new, const void* v_new,
+                              const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
+                              float sm_scale, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                              void* stream, const int32_t* prefix_ids,
+                              const int32_t* shared_pages, int32_t prefix_pages) {
   oscar::AppendArgs ap;
   oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
                                      u_k, u_v, clip_k, clip_v, levels_k, levels_v, k_new, v_new,
@@ -563,7 +590,7 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
   oscar::Plan plan;
   st = make_decode_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot, seq_pos,
                         q, u_k, u_v, sm_scale, out, lse, workspace, workspace_bytes, batch,
-                        max_seq_len, a, qa, plan);
+                        max_seq_len, a, qa, plan, prefix_ids, shared_pages, prefix_pages);
   if (st != OSCAR_OK || batch == 0) return st;
   st = check_codebook_attention(l, levels_k, levels_v, "oscar_decode_step");
   if (st != OSCAR_OK) return st;
@@ -578,6 +605,96 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
   return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
                                                       OSCAR_STAGE_MERGE, s),
                     "oscar_decode_step");
+}
+
+}  // namespace
+
+oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t* page_table,
+                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
+                               const float* u_k, const float* u_v, const float* clip_k,
+                               const float* clip_v, const float* levels_k,
+                               const float* levels_v, const void* k_new, const void* v_new,
+                               const int32_t* seq_slot, const int32_t* seq_pos, const void* q,
+                               float sm_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                               void* stream) {
+  return decode_step_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
+                          clip_k, clip_v, levels_k, levels_v, k_new, v_new, seq_slot, seq_pos, q,
+                          sm_scale, out, lse, workspace, workspace_bytes, batch, max_seq_len,
+                          stream, nullptr, nullptr, 0);
+}
+
+oscar_status oscar_decode_step_prefix(const oscar_layout* l, void* pool,
+                                      const int32_t* page_table, void* sink_k, void* sink_v,
+                                      void* recent_k, void* recent_v, const float* u_k,
+                                      const float* u_v, const float* clip_k, const float* clip_v,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* seq_slot, const int32_t* seq_pos,
+                                      const void* q, const int32_t* prefix_ids,
+                                      const int32_t* shared_pages, int32_t prefix_pages,
+                                      float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                                      void* stream) {
+  if (l != nullptr && l->levels_kind != 0)
+    return fail(OSCAR_ERR_SHAPE, "oscar_decode_step_prefix: the shared-prefix path takes layouts "
+                "with levels_kind 0 only");
+  return decode_step_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
+                          clip_k, clip_v, nullptr, nullptr, k_new, v_new, seq_slot, seq_pos, q,
+                          sm_scale, out, lse, workspace, workspace_bytes, batch, max_seq_len,
+                          stream, prefix_ids, shared_pages, prefix_pages);
+}
+
+oscar_status oscar_decode_attn_prefix(const oscar_layout* l, const void* pool,
+                                      const int32_t* page_table, const void* sink_k,
+                                      const void* sink_v, const void* recent_k,
+                                      const void* recent_v, const int32_t* seq_slot,
+                                      const int32_t* seq_lens, const void* q, const float* u_k,
+                                      const float* u_v, const int32_t* prefix_ids,
+                                      const int32_t* shared_pages, int32_t prefix_pages,
+                                      float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                                      uint32_t stages, void* stream) {
+  if (l != nullptr && l->levels_kind != 0)
+    return fail(OSCAR_ERR_SHAPE, "oscar_decode_attn_prefix: the shared-prefix path takes layouts "
+                "with levels_kind 0 only");
+  return decode_attn_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, seq_slot,
+                          seq_lens, q, u_k, u_v, nullptr, nullptr, sm_scale, out, lse, workspace,
+                          workspace_bytes, batch, max_seq_len, stages, stream, prefix_ids,
+                          shared_pages, prefix_pages);
+}
+
+size_t oscar_decode_workspace_bytes_prefix(const oscar_layout* l, int32_t batch,
+                                           int32_t max_seq_len, int32_t prefix_pages) {
+  if (check_layout(l) != OSCAR_OK || batch < 0 || max_seq_len < 0 || prefix_pages < 0) return 0;
+  return oscar::make_plan(*l, batch, max_seq_len, prefix_pages).total;
+}
+
+oscar_status oscar_check_shared_prefix(const oscar_layout* l, const int32_t* page_table,
+                                       int32_t batch, const int32_t* prefix_ids,
+                                       const int32_t* shared_pages, int32_t prefix_pages) {
+  oscar_status st = check_layout(l);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || prefix_pages < 0 || prefix_pages > l->max_pages_per_seq)
+    return fail(OSCAR_ERR_RANGE, "check_shared_prefix: batch %d or prefix_pages %d out of range",
+                batch, prefix_pages);
+  if ((batch > 0 && (!page_table || !shared_pages)) || (prefix_pages > 0 && !prefix_ids))
+    return fail(OSCAR_ERR_NULL, "check_shared_prefix: NULL pointer");
+  for (int j = 0; j < prefix_pages; ++j)
+    if (prefix_ids[j] < 0 || prefix_ids[j] >= l->num_pages)
+      return fail(OSCAR_ERR_RANGE, "prefix page %d has id %d outside [0, %d)", j, prefix_ids[j],
+                  l->num_pages);
+  for (int b = 0; b < batch; ++b) {
+    const int n = shared_pages[b];
+    if (n < 0 || n > prefix_pages)
+      return fail(OSCAR_ERR_RANGE, "sequence %d: shared_pages %d outside [0, %d]", b, n,
+                  prefix_pages);
+    const int32_t* row = page_table + static_cast<int64_t>(b) * l->max_pages_per_seq;
+    for (int j = 0; j < n; ++j)
+      if (row[j] != prefix_ids[j])
+        return fail(OSCAR_ERR_SHAPE, "sequence %d: page %d is %d, not the shared prefix's %d", b,
+                    j, row[j], prefix_ids[j]);
+  }
+  return ok();
 }
 
 oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,

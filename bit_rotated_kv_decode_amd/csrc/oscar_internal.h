@@ -18,6 +18,10 @@ constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
 constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
+// Shared-prefix cascade: a cascade block takes kCascPages pages of the shared prefix of one KV head
+// (staged in LDS) for a group of kCascGroup sequences, four waves taking kCascGroup / 4 each.
+constexpr int kCascPages = 12;
+constexpr int kCascGroup = 16;
 // The INT2 pass a (query heads per KV head, groups per head) shape takes: the fp8 x FP4 pass for
 // tiles of up to four heads and one group, the int8 / bf16 pass otherwise.  The preparation
 // launch writes the query operand that pass reads.
@@ -58,18 +62,32 @@ struct Plan {
   int max_pages = 0;         // history pages of the longest sequence
   int pages_per_split = 1;   // history pages per INT2 work item
   int num_splits = 0;        // work items per (sequence, KV head)
+  int casc_chunks = 0;       // shared-prefix chunks of kCascPages pages taken by cascade blocks
+  int casc_groups = 0;       // sequence groups of kCascGroup per cascade chunk
+  int slots = 0;             // INT2 partials per (sequence, query head): casc_chunks + num_splits
   size_t off_qrot = 0;       // int8 [B][Hq][2][128] rotated queries, hi / lo parts (int8 pass)
   size_t off_qops = 0;       // fp8 key operands [B][Hkv][tiles][groups][64 lanes][32 B]
   size_t off_qscale = 0;     // int32 E8M0 row scales [B][Hkv][tiles][groups][64 lanes]
   size_t off_sigma = 0;      // fp32 [B][Hq][4] per-group sums of the rotated, scaled query
-  size_t off_int2_ml = 0;    // fp32 [B][Hq][S][2] (m, l) of INT2 partials (log2 domain)
-  size_t off_int2_acc = 0;   // fp32 [B][Hq][S][128] rotated-space accumulators
+  size_t off_int2_ml = 0;    // fp32 [B][Hq][slots][2] (m, l) of INT2 partials (log2 domain):
+                             // cascade chunks first, then the splits
+  size_t off_int2_acc = 0;   // fp32 [B][Hq][slots][128] rotated-space accumulators
   size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]
   size_t off_bf16_acc = 0;   // fp32 [B][Hq][5][128]
   size_t total = 0;
 };
 
-Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len);
+// prefix_pages: pages of a shared prefix a cascade may take (0: none).
+Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_pages = 0);
+
+// History pages of a sequence that the cascade chunks of plan p take: the whole chunks within
+// both its full history pages (n_hist tokens) and its first `shared` pages (those of its
+// page-table row that are the shared prefix's).
+__host__ __device__ inline int cascade_pages(const Plan& p, int n_hist, int shared) {
+  const int held = n_hist / kPage < shared ? n_hist / kPage : shared;
+  const int chunks = held / kCascPages;
+  return kCascPages * (chunks < p.casc_chunks ? chunks : p.casc_chunks);
+}
 
 struct DemoteArgs {
   uint8_t* pool;
@@ -138,6 +156,10 @@ struct DecodeArgs {
   // (l0, l1, 3 - l1, 3 - l0)), or NULL for the grid {0, 1, 2, 3}
   const float* cb_k;
   const float* cb_v;
+  // physical ids of the shared prefix's pages (plan.casc_chunks * kCascPages of them are read) and,
+  // per sequence, how many leading pages of its page-table row are those; NULL without a cascade
+  const int32_t* prefix_ids;
+  const int32_t* shared_pages;
 };
 
 struct QueryArgs {

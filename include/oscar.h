@@ -14,6 +14,9 @@
  *        oldest recent token by a fused rotate / clip / quantise / pack step, 4 two-bit codes per
  *        byte, INT2 decode with scale / zero-point dequantisation and float accumulation, a
  *        separate BF16 sink / recent pass, an online-softmax merge, paged-KV compatibility.
+ *   [W3] the repost of [W1] on m.kljzs.com (article 2026060659440) -- keeps the evaluation part:
+ *        the 100k-context system figures (Fig. 5: prefix-cache-hit decode, batch throughput) and
+ *        the prefix-cache hit-rate frontier (Fig. 6), and the closing comparison with TurboQuant.
  *   [P]  "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization",
  *        ModelScope paper page of arXiv 2605.17757, "摘要" and "Abstract" -- an INT2 attention
  *        kernel that stays compatible with paged KV caches and fused decode pipelines.
@@ -84,7 +87,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 6u
+#define OSCAR_ABI_VERSION 7u
 
 typedef int32_t oscar_status;
 
@@ -156,6 +159,22 @@ int32_t oscar_decode_splits(const oscar_layout* layout, int32_t batch, int32_t m
 oscar_status oscar_check_page_table(const oscar_layout* layout, const int32_t* host_page_table,
                                     const int32_t* host_seq_lens, int32_t batch,
                                     int32_t extra_tokens);
+
+/* Device workspace oscar_decode_attn_prefix / oscar_decode_step_prefix need for `batch`
+ * sequences of at most `max_seq_len` tokens over a shared prefix of `prefix_pages` history pages
+ * (0 for invalid arguments).  With prefix_pages 0 it is oscar_decode_workspace_bytes. */
+size_t oscar_decode_workspace_bytes_prefix(const oscar_layout* layout, int32_t batch,
+                                           int32_t max_seq_len, int32_t prefix_pages);
+
+/* Host-side check of the shared-prefix description oscar_decode_attn_prefix takes, against a host
+ * copy of the page table: prefix_ids[0 .. prefix_pages) in [0, num_pages), prefix_pages at most
+ * max_pages_per_seq, and for every sequence b, shared_pages[b] in [0, prefix_pages] with
+ * page_table[b][j] == prefix_ids[j] for every j < shared_pages[b].  All pointers are host memory
+ * (page_table and shared_pages may be NULL when batch is 0).  Touches no device memory.
+ * Returns OSCAR_OK, or NULL / SHAPE / RANGE. */
+oscar_status oscar_check_shared_prefix(const oscar_layout* layout, const int32_t* host_page_table,
+                                       int32_t batch, const int32_t* host_prefix_ids,
+                                       const int32_t* host_shared_pages, int32_t prefix_pages);
 
 /* Demotion into the INT2 history ([W1] OSCAR 的设计: the oldest recent tokens are rotated,
  * clipped, quantised and packed into the history; four 2-bit codes per byte).
@@ -284,6 +303,38 @@ oscar_status oscar_decode_attn_codebook(const oscar_layout* layout, const void* 
                                         int32_t batch, int32_t max_seq_len, uint32_t stages,
                                         void* stream);
 
+/* oscar_decode_attn_stages for a batch whose sequences share a prefix through the page table
+ * ([W1] OSCAR 的设计 and [W3] Fig. 5 / Fig. 6: the paged INT2 pool works with a radix prefix
+ * cache, whose hits alias one physical copy of a prefix's pages in many sequences' rows).  The
+ * result is that of oscar_decode_attn_stages on the same arguments; only the work differs: the
+ * INT2 pass reads each whole chunk of 12 shared pages of a KV head once for a group of 16
+ * sequences (a cascade block stages the chunk in LDS and runs every sequence of the group against
+ * it), and the split-KV items take each sequence's remaining pages.
+ *   prefix_ids    device int32 [prefix_pages]: physical page ids of the shared prefix, in order.
+ *   shared_pages  device int32 [batch]: how many leading pages of sequence b's page-table row are
+ *                 prefix_ids[0 ..) (0 .. prefix_pages; a short sequence, or one whose prefix
+ *                 diverges, shares fewer).  Both arrays 4-byte aligned and trusted like the page
+ *                 table; oscar_check_shared_prefix checks host copies.
+ *   prefix_pages  0 .. min(num_pages, max_pages_per_seq); 0 (with NULL arrays) is
+ *                 oscar_decode_attn_stages.  Pages of the prefix past max_seq_len's history and a
+ *                 trailing part of fewer than 12 pages are taken by the split items as usual.
+ * workspace: oscar_decode_workspace_bytes_prefix(layout, batch, max_seq_len, prefix_pages) bytes.
+ * The cascade runs on layouts with up to four query heads per KV head, group_size 128 and
+ * levels_kind 0; other layouts take the split items alone (the same result).  A layout with
+ * levels_kind 1 is refused (SHAPE).  Stage OSCAR_STAGE_INT2 launches the
+ * cascade blocks ahead of the split items on the same stream.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
+oscar_status oscar_decode_attn_prefix(const oscar_layout* layout, const void* pool,
+                                      const int32_t* page_table, const void* sink_k,
+                                      const void* sink_v, const void* recent_k,
+                                      const void* recent_v, const int32_t* seq_slot,
+                                      const int32_t* seq_lens, const void* q, const float* u_k,
+                                      const float* u_v, const int32_t* prefix_ids,
+                                      const int32_t* shared_pages, int32_t prefix_pages,
+                                      float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                                      uint32_t stages, void* stream);
+
 /* One whole decode step of a layer ([W1] OSCAR 的设计: a new token enters the recent window, the
  * token it displaces is demoted into the INT2 history, then attention runs over the three
  * segments): the same result as
@@ -304,6 +355,25 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
                                float sm_scale, float* out, float* lse, void* workspace,
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                                void* stream);
+
+/* oscar_decode_step over a shared prefix: oscar_append followed by oscar_decode_attn_prefix
+ * (seq_lens = seq_pos + 1), in three launches as oscar_decode_step, plus the cascade launch.
+ * The new tokens' demotions must not land in a shared page (oscar_check_page_table with
+ * extra_tokens); a layout with levels_kind 1 is refused (SHAPE).  Arguments
+ * are those of oscar_decode_step and oscar_decode_attn_prefix, with the same requirements;
+ * workspace: oscar_decode_workspace_bytes_prefix bytes.
+ * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
+oscar_status oscar_decode_step_prefix(const oscar_layout* layout, void* pool,
+                                      const int32_t* page_table, void* sink_k, void* sink_v,
+                                      void* recent_k, void* recent_v, const float* u_k,
+                                      const float* u_v, const float* clip_k, const float* clip_v,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* seq_slot, const int32_t* seq_pos,
+                                      const void* q, const int32_t* prefix_ids,
+                                      const int32_t* shared_pages, int32_t prefix_pages,
+                                      float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
+                                      void* stream);
 
 /* oscar_decode_step for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, and harnesses that forbid hipMalloc.  The same step, with the

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 6
+    assert lib.oscar_abi_version() == 7
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -476,6 +476,96 @@ def _call_step_noalloc(lay, **over):
         ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
         a["uv"], a["ck"], a["cv"], a["lk"], a["lv"], a["kn"], a["vn"], a["slot"], a["pos"],
         a["q"], 0.0, a["out"], a["lse"], a["batch"], a["maxlen"], None)
+
+
+def _call_decode_prefix(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, slot=4096, lens=4096,
+             q=4096, uk=4096, uv=4096, ids=4096, shared=4096, npre=3, out=4096, lse=None,
+             ws=4096, wsb=1 << 30, batch=1, maxlen=600, stages=ok.STAGE_ALL)
+    a.update(over)
+    return ok.lib().oscar_decode_attn_prefix(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["slot"],
+        a["lens"], a["q"], a["uk"], a["uv"], a["ids"], a["shared"], a["npre"], 0.0, a["out"],
+        a["lse"], a["ws"], a["wsb"], a["batch"], a["maxlen"], a["stages"], None)
+
+
+def _call_step_prefix(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, uk=4096, uv=4096, ck=4096,
+             cv=4096, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, ids=4096, shared=4096,
+             npre=3, out=4096, lse=None, ws=4096, wsb=1 << 30, batch=1, maxlen=600)
+    a.update(over)
+    return ok.lib().oscar_decode_step_prefix(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
+        a["uv"], a["ck"], a["cv"], a["kn"], a["vn"], a["slot"], a["pos"], a["q"], a["ids"],
+        a["shared"], a["npre"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"], a["batch"],
+        a["maxlen"], None)
+
+
+def test_prefix_validation_happens_before_launch():
+    lay = _lay()
+    for call in (_call_decode_prefix, _call_step_prefix):
+        assert call(lay, ids=None) == -1                  # a prefix needs its page ids
+        assert call(lay, shared=None) == -1
+        assert call(lay, ids=4098) == -3
+        assert call(lay, shared=4097) == -3
+        assert call(lay, npre=-1) == -4
+        assert call(lay, npre=11) == -4                   # more pages than the pool holds
+        assert call(lay, npre=6) == -4                    # longer than a page-table row
+        assert call(_lay(levels_kind=1)) == -2            # no cascade over symmetric codebooks
+        assert "levels_kind" in ok.lib().oscar_last_error().decode()
+        assert call(lay, q=None) == -1                    # the checks of the plain call still run
+        assert call(lay, ws=None) == -5
+        assert call(lay, maxlen=100000) == -4
+        # without a prefix the arrays are not needed, and nothing to do is OK
+        assert call(lay, npre=0, ids=None, shared=None, q=None) == -1
+        assert call(lay, batch=0, q=None, ids=None, shared=None, npre=0) == 0
+    assert _call_step_prefix(lay, kn=None) == -1
+    assert _call_step_prefix(lay, ck=4096 + 2) == -3
+    assert _call_decode_prefix(lay, stages=0) == -4
+
+
+def test_prefix_workspace_grows_by_the_cascade_slots():
+    big = _lay(num_pages=4000, max_pages_per_seq=2100, max_seqs=64)
+    for batch, maxlen in ((64, 131072), (1, 100000), (3, 40000)):
+        base = ok.decode_workspace_bytes(big, batch, maxlen)
+        assert ok.decode_workspace_bytes_prefix(big, batch, maxlen, 0) == base
+        w = ok.decode_workspace_bytes_prefix(big, batch, maxlen, 511)
+        # 42 whole chunks of 12 pages: 42 more partial slots of (m, l) and 128 accumulators per
+        # (sequence, query head) row, each region rounded up to 256 bytes
+        rows = batch * 32
+        extra = w - base
+        assert rows * 42 * (128 + 2) * 4 <= extra <= rows * 42 * (128 + 2) * 4 + 512
+        # a prefix shorter than one chunk adds nothing
+        assert ok.decode_workspace_bytes_prefix(big, batch, maxlen, 11) == base
+    # layouts on the int8 / bf16 pass take no cascade: the plan is the plain one
+    gqa8 = _lay(num_q_heads=64, num_pages=4000, max_pages_per_seq=2100, max_seqs=64)
+    assert (ok.decode_workspace_bytes_prefix(gqa8, 64, 131072, 511) ==
+            ok.decode_workspace_bytes(gqa8, 64, 131072))
+    assert ok.decode_workspace_bytes_prefix(big, 64, 131072, -1) == 0
+
+
+def test_check_shared_prefix():
+    import workloads
+    wl = workloads.scaled(workloads.get("qwen3_8b_b64_prefix"), batch=8)
+    lens = workloads.context_lengths(wl)
+    table, num_pages = workloads.page_tables(wl, lens, spare_tokens=10)
+    lay = _lay(num_pages=num_pages, max_pages_per_seq=table.shape[1], max_seqs=8)
+    ids, shared = workloads.shared_prefix(wl, table, lens, spare_tokens=10)
+    assert len(ids) == max(shared) and len(ids) <= 511
+    ok.check_shared_prefix(lay, table, ids, shared)
+    # the description may claim fewer shared pages than the table has, never more
+    ok.check_shared_prefix(lay, table, ids, [max(0, n - 5) for n in shared])
+    with pytest.raises(ok.OscarError, match="shared prefix"):
+        bad = list(shared)
+        bad[int(np.argmin(shared))] += 1
+        ok.check_shared_prefix(lay, table, ids, bad)
+    with pytest.raises(ok.OscarError, match="outside"):
+        ok.check_shared_prefix(lay, table, ids, [len(ids) + 1] * len(shared))
+    with pytest.raises(ok.OscarError, match="outside"):
+        bad_ids = np.array(ids, np.int32)
+        bad_ids[3] = num_pages
+        ok.check_shared_prefix(lay, table, bad_ids, shared)
+    ok.check_shared_prefix(lay, table, [], [0] * len(shared))
 
 
 def test_step_noalloc_validation_happens_before_launch():

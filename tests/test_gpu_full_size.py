@@ -30,7 +30,8 @@ def _note(msg):
 class FullLayer:
     """One layer of a workload at full size on the GPU after one decode step."""
 
-    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None, levels=None, codebook=None):
+    def __init__(self, wl, layer=0, u=None, clip=None, lengths=None, levels=None, codebook=None,
+                 prefix=False):
         self.wl, self.layer = wl, layer
         self.lengths = list(workloads.context_lengths(wl) if lengths is None else lengths)
         self.B = len(self.lengths)
@@ -90,13 +91,25 @@ class FullLayer:
         pos = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
         slots = torch.arange(self.B, dtype=torch.int32, device=dev)
         mx = max(self.lengths) + 1
-        ws = torch.empty(ok.decode_workspace_bytes(self.lay, self.B, mx), dtype=torch.uint8,
-                         device=dev)
         out = torch.empty((self.B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
-        ok.decode_step(self.lay, cache.pool, table, cache.sink_k, cache.sink_v, cache.recent_k,
-                       cache.recent_v, uk, uv, ck, cv, self.k_new, self.v_new, slots, pos,
-                       self.q, out, ws, mx, levels_k=lk, levels_v=lv)
+        if prefix:
+            # the shared prefix handed to the cascade (the benchmark's configuration)
+            ids, shared = workloads.shared_prefix(wl, self.table, self.lengths, spare_tokens=1)
+            ok.check_shared_prefix(self.lay, self.table, ids, shared)
+            self.prefix = (torch.from_numpy(ids).to(dev), torch.from_numpy(shared).to(dev))
+            ws = torch.empty(ok.decode_workspace_bytes_prefix(self.lay, self.B, mx, len(ids)),
+                             dtype=torch.uint8, device=dev)
+            ok.decode_step_prefix(self.lay, cache.pool, table, cache.sink_k, cache.sink_v,
+                                  cache.recent_k, cache.recent_v, uk, uv, ck, cv, self.k_new,
+                                  self.v_new, slots, pos, self.q, *self.prefix, out, ws, mx)
+        else:
+            ws = torch.empty(ok.decode_workspace_bytes(self.lay, self.B, mx), dtype=torch.uint8,
+                             device=dev)
+            ok.decode_step(self.lay, cache.pool, table, cache.sink_k, cache.sink_v,
+                           cache.recent_k, cache.recent_v, uk, uv, ck, cv, self.k_new, self.v_new,
+                           slots, pos, self.q, out, ws, mx, levels_k=lk, levels_v=lv)
         torch.cuda.synchronize()
+        self.gpu = dict(table=table, uk=uk, uv=uv, slots=slots, mx=mx)
         self.cache = cache
         self.out = out.cpu().numpy()
         self.blocks = cache.pool.view(self.num_pages, hkv, self.geom.block_bytes)
@@ -275,12 +288,30 @@ def test_full_size_qwen3_8b_100k_symmetric_codebook():
 
 
 def test_full_size_qwen3_8b_b64_shared_prefix():
+    # the step runs with the shared-prefix cascade, as the benchmark times it; the plain attention
+    # over the cache the step left must agree with it to the fp8 parts' resolution and fp32
+    # summation order (1e-4 of each row's largest output: pages pair up from other starting
+    # pages in the two paths), and sampled rows must agree with the oracle
     wl = workloads.get("qwen3_8b_b64_prefix")
-    layer = FullLayer(wl, layer=0)
+    layer = FullLayer(wl, layer=0, prefix=True)
     lens = layer.lengths
-    _note(f"qwen3_8b_b64_prefix: 64 sequences, lengths {min(lens)}..{max(lens)}")
+    _note(f"qwen3_8b_b64_prefix: 64 sequences, lengths {min(lens)}..{max(lens)}, prefix "
+          f"{layer.prefix[0].numel()} pages")
     rng = np.random.default_rng(32)
     _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
+    c, gi = layer.cache, layer.gpu
+    plain = torch.empty((layer.B, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ok.decode_workspace_bytes(layer.lay, layer.B, gi["mx"]), dtype=torch.uint8,
+                     device="cuda")
+    lens1 = torch.tensor(lens, dtype=torch.int32, device="cuda") + 1
+    ok.decode_attn(layer.lay, c.pool, gi["table"], c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                   gi["slots"], lens1, layer.q, gi["uk"], gi["uv"], plain, ws, gi["mx"])
+    torch.cuda.synchronize()
+    plain = plain.cpu().numpy()
+    scale = np.maximum(np.abs(plain).max(axis=-1, keepdims=True), 1e-30)
+    d = float(np.max(np.abs(layer.out - plain) / scale))
+    _note(f"  cascade step vs plain attention: {d:.2e}")
+    assert d <= 1e-4
     order = np.argsort(lens)
     for b, kv in ((int(order[-1]), 3), (int(order[0]), 6), (int(order[32]), 0)):
         layer.check_attention(b, kv)

@@ -179,6 +179,16 @@ def page_tables(wl: Workload, lengths: Sequence[int], layer: int = 0, spare_toke
     return table, max(num_pages, 1)
 
 
+def shared_prefix(wl: Workload, table: np.ndarray, lengths: Sequence[int], spare_tokens: int = 0,
+                  sink: int = 64, recent: int = 256, page: int = 64):
+    """The shared prefix of ``page_tables``' table as the cascade takes it: (physical page ids of
+    the prefix, int32 [P]; per sequence, how many leading pages of its row are those)."""
+    share = [shared_pages(wl, L, spare_tokens, sink, recent, page) for L in lengths]
+    n = max(share) if share else 0
+    ids = table[int(np.argmax(share)), :n].astype(np.int32) if n else np.zeros(0, np.int32)
+    return ids, np.asarray(share, np.int32)
+
+
 # ----------------------------------------------------------------------------------------------
 # keys and values
 
