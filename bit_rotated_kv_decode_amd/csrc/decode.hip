@@ -106,6 +106,12 @@ struct Int2Lds {
   static constexpr int CASC_TOTAL = STAGE + kCascPages * (kMetaOff + kPage * 8 * NG);
 };
 
+// Whether a page pair may be a wave's last one (a compile-time flag of the pair step).
+template <bool B>
+struct PairKind {
+  static constexpr bool value = B;
+};
+
 // STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
 // sequence, so no page is read twice in it; with several sequences pages may be shared (a prefix
 // cache), and cached loads let the second reader hit.
@@ -341,12 +347,13 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     load_page(wa + 2 * q + 1, rr[1]);
   };
 
-  // ---- one pair of pages
-  auto process_pair = [&](int q, PageRegs* rr, bool first) {
+  // ---- one pair of pages.  `last` (a PairKind): only a wave's last pair can hold a slot past
+  // the history or a page past the wave's range, so only that pair carries the checks.
+  auto process_pair = [&](int q, PageRegs* rr, bool first, auto last) {
     const int pgs[2] = {wa + 2 * q, wa + 2 * q + 1};
     // a slot past the history (or a page past the wave's range) holds arbitrary bytes: its meta
     // becomes zero (no value contribution, finite products) and its logit -inf
-    const bool tail = pgs[1] >= w1 || (pgs[1] + 1) * kPage > n_hist;
+    const bool tail = decltype(last)::value && (pgs[1] >= w1 || (pgs[1] + 1) * kPage > n_hist);
     if (tail) {
 #pragma unroll
       for (int P = 0; P < 2; ++P)
@@ -536,7 +543,10 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
               for (int st = 0; st < 4; ++st) in[st] = r[st];
             }
             const float div = pt <= 1 ? 1.f : pt == 2 ? 0.0625f : 0.00390625f;
-            v2s w01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, in[0], in[1], div, false);
+            // both halves of the dword are written: the first conversion's other half may be any
+            v2s w00;
+            w00 = __builtin_nondeterministic_value(w00);
+            v2s w01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w00, in[0], in[1], div, false);
             const v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w01, in[2], in[3], div, true);
             uint32_t pk;
             __builtin_memcpy(&pk, &w, 4);
@@ -586,13 +596,14 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Pairs of this wave: pages w0 + 2 q and + 1.  Two register sets used in turn: while one pair
-  // is processed, the next pair's loads are in flight.  Every round issues the same loads
-  // (slots past the wave's pages read nothing), so the wait before a pair never covers a later
-  // one's, and the loop over full rounds has a single exit, so the wait counts stay exact.  The
-  // query operands are loaded between the first two pairs' loads: the first pair waits on them
-  // and on its own pages only.
+  // Pairs of this wave: pages wa + 2 q and + 1.  Two register sets used in turn: while one pair
+  // is processed, the next pair's loads are in flight.  Every load of a round is issued whether
+  // or not its page is the wave's (slots past the wave's pages read nothing), so the wait before
+  // a pair never covers a later one's.  The query operands are loaded between the first two
+  // pairs' loads: the first pair waits on them and on its own pages only.
   const int npairs = w1 > wa ? (w1 - wa + 1) / 2 : 0;
+  // pairs before a wave's last one skip the checks
+  using Inner = PairKind<false>;
   // Issue priority by the pairs a wave has left: two blocks share a compute unit, and the arbiter
   // otherwise favours the older one throughout, so the younger one would end its pages alone.
   auto set_prio = [&](int q) {
@@ -632,7 +643,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
       for (int q = 0; q < kCascPages / 2; ++q) {
         PageRegs rr[2];
         load_pair(q, rr);
-        process_pair(q, rr, q == 0);
+        process_pair(q, rr, q == 0, PairKind<false>{});   // staged pages: all history
       }
 #pragma unroll
       for (int ht = 0; ht < NT; ++ht) {
@@ -668,23 +679,59 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     __builtin_amdgcn_sched_barrier(0);
     load_pair(1, r1);
     __builtin_amdgcn_sched_barrier(0);
-    process_pair(0, r0, true);
+    if constexpr (CB) {
+      // one pair step with the checks throughout (the codebook pass's registers are at the
+      // limit; more inlined steps spill)
+      process_pair(0, r0, true, PairKind<true>{});
+      int q = 1, rest = npairs - 1;
+      for (; rest >= 2; rest -= 2) {
+        set_prio(q);
+        load_pair(q + 1, r0);
+        process_pair(q, r1, false, PairKind<true>{});
+        ++q;
+        __builtin_amdgcn_sched_barrier(0);
+        set_prio(q);
+        load_pair(q + 1, r1);
+        process_pair(q, r0, false, PairKind<true>{});
+        ++q;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (rest == 1) {
+        set_prio(q);
+        process_pair(q, r1, false, PairKind<true>{});
+      }
+    } else {
+    if (npairs == 1)
+      process_pair(0, r0, true, PairKind<true>{});
+    else
+      process_pair(0, r0, true, Inner{});
     int q = 1, rest = npairs - 1;
-    for (; rest >= 2; rest -= 2) {
+    // rounds of two pairs while a later pair remains; the wave's last pair (the only one with
+    // checks) in the round or single pair after the loop
+    for (; rest >= 3; rest -= 2) {
       set_prio(q);
       load_pair(q + 1, r0);
-      process_pair(q, r1, false);
+      process_pair(q, r1, false, Inner{});
       ++q;
       __builtin_amdgcn_sched_barrier(0);
       set_prio(q);
       load_pair(q + 1, r1);
-      process_pair(q, r0, false);
+      process_pair(q, r0, false, Inner{});
       ++q;
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (rest == 1) {
+    if (rest == 2) {
       set_prio(q);
-      process_pair(q, r1, false);
+      load_pair(q + 1, r0);
+      process_pair(q, r1, false, Inner{});
+      ++q;
+      __builtin_amdgcn_sched_barrier(0);
+      set_prio(q);
+      process_pair(q, r0, false, PairKind<true>{});
+    } else if (rest == 1) {
+      set_prio(q);
+      process_pair(q, r1, false, PairKind<true>{});
+    }
     }
     __builtin_amdgcn_s_setprio(0);
   }
