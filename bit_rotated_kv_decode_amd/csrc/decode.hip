@@ -393,18 +393,34 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
 
     // ---- logits of head 4 ht + gq for token 16 st + n of page P
     float lg[NT][2][4];
+    // without codebooks, a page's four sub-tile contractions are issued back to back (four
+    // independent results) before their sums are read
+    v4f dk[4][NT * NG];
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
+    for (int P = 0; P < 2; ++P) {
+      if constexpr (!CB) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const v8i bk = fp4_operand(kword(rr[P], st, 0), kword(rr[P], st, 1));
+#pragma unroll
+          for (int i = 0; i < NT * NG; ++i)
+            dk[st][i] = mfma_f8_f4(aq[i], bk, v4f{0.f, 0.f, 0.f, 0.f}, sq[i]);
+        }
+      }
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const uint32_t kw0 = kword(rr[P], st, 0), kw1 = kword(rr[P], st, 1);
-        const v8i bk = fp4_operand(kw0, kw1);
         float sc[NT][NG];
 #pragma unroll
         for (int ht = 0; ht < NT; ++ht)
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            const v4f d = mfma_f8_f4(aq[ht * NG + g], bk, v4f{0.f, 0.f, 0.f, 0.f}, sq[ht * NG + g]);
+            v4f d;
+            if constexpr (CB)
+              d = mfma_f8_f4(aq[ht * NG + g], fp4_operand(kw0, kw1), v4f{0.f, 0.f, 0.f, 0.f},
+                             sq[ht * NG + g]);
+            else
+              d = dk[st][ht * NG + g];
             sc[ht][g] = (d[0] + d[1]) + (d[2] + d[3]);
           }
         if constexpr (CB) {
@@ -431,6 +447,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
           lg[ht][P][st] = t;
         }
       }
+    }
     if (tail) {
 #pragma unroll
       for (int P = 0; P < 2; ++P)
