@@ -120,7 +120,8 @@ struct PairKind {
 // chunk's pages are staged in LDS once; each wave then takes its sequences in turn (those whose
 // history wholly holds the chunk), runs the same page-pair arithmetic as a split block against
 // the staged pages and writes the sequence's partial for the chunk itself.
-template <int G, int NG, bool STREAM, bool CB, bool CASC = false>
+// PCASC: the plan has cascade chunks (a split block then skips the pages they took).
+template <int G, int NG, bool STREAM, bool CB, bool CASC = false, bool PCASC = CASC>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
                                            int grp, unsigned char* smem) {
   using S = Int2Lds<G, NG>;
@@ -166,7 +167,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     if (p0 >= n_pages) return;
     const int p1 = min(p0 + p.pages_per_split, n_pages);
     // pages of a shared prefix that cascade blocks took for this sequence are not this item's
-    const int cend = p.casc_chunks ? cascade_pages(p, n_hist, a.shared_pages[b]) : 0;
+    int cend = 0;
+    if constexpr (PCASC) cend = cascade_pages(p, n_hist, a.shared_pages[b]);
     if (p1 <= cend) return;
     w1 = min(w0 + qw, p1);   // w1 <= w0: a wave without pages (it still combines)
     wa = max(w0, cend);
@@ -982,8 +984,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, floa
       const int ci = k * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
       if (ci >= p.casc_chunks * p.hkv * p.casc_groups) return;
       const int rest = ci / p.hkv;
-      int2_block<G, 1, false, false, true>(a, p, rest / p.casc_groups, ci % p.hkv,
-                                           rest % p.casc_groups, smem);
+      int2_block<G, 1, false, false, true, true>(a, p, rest / p.casc_groups, ci % p.hkv,
+                                                 rest % p.casc_groups, smem);
       return;
     }
     b -= min(k + 1, casc_z);
@@ -991,7 +993,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, floa
   if (x < kBf16Chunks)
     bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
   else if constexpr (int2_fp8_pass(G, NG))
-    int2_block<G, NG, STREAM, CB>(a, p, x - kBf16Chunks, kv, b, smem);
+    int2_block<G, NG, STREAM, CB, false, CASC>(a, p, x - kBf16Chunks, kv, b, smem);
   else
     int2_block_i8<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
 }
@@ -1018,7 +1020,8 @@ constexpr int kMergeCols = kHeadDim / kMergeQuarters;
 // repeat less of the per-row work (the split loads and merges of steps 1 and 2).
 constexpr int kMergeRowsOneBlock = 512;
 
-template <int PARTS>
+// CASC: the plan has cascade chunks (their slots come first in each row).
+template <int PARTS, bool CASC>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   __shared__ __attribute__((aligned(16))) float part[8][kHeadDim];
   __shared__ float part_m[8], part_l[8];
@@ -1078,12 +1081,21 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, Plan p) {
   const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
   // slots of the row's partials: cascade chunks [0, casc_chunks) (those its history wholly holds
   // were written), then splits (those holding a page past the cascade's pages and within the
-  // history: none when the cascade took every page)
-  const int cend = p.casc_chunks ? cascade_pages(p, n_hist, a.shared_pages[b]) : 0;
-  const int c_b = cend / kCascPages;
-  const int s_end = p.casc_chunks + n_valid;
-  const int s_first = cend < n_pages ? p.casc_chunks + cend / p.pages_per_split : s_end;
-  auto valid = [&](int s) { return s < c_b || (s >= s_first && s < s_end); };
+  // history: none when the cascade took every page); without a cascade, the splits [0, n_valid)
+  int c_b = 0, s_first = 0, s_end = n_valid;
+  if constexpr (CASC) {
+    const int cend = cascade_pages(p, n_hist, a.shared_pages[b]);
+    c_b = cend / kCascPages;
+    s_end = p.casc_chunks + n_valid;
+    s_first = cend < n_pages ? p.casc_chunks + cend / p.pages_per_split : s_end;
+  }
+  // (no short-circuit: one compare per slot, not a branch)
+  auto valid = [&](int s) {
+    if constexpr (CASC)
+      return (s < c_b) | ((s >= s_first) & (s < s_end));
+    else
+      return s < s_end;
+  };
 
   // ---- (1) this thread's splits (those the sequence reaches), with its own maximum
   float m_loc = -INFINITY, l_loc = 0.f;
@@ -1282,11 +1294,19 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
   }
   if (stages & OSCAR_STAGE_MERGE) {
     const int rows = p.batch * p.hq;
-    if (rows >= kMergeRowsOneBlock)
-      hipLaunchKernelGGL(merge_kernel<1>, dim3(rows), dim3(256), 0, stream, a, p);
-    else
-      hipLaunchKernelGGL(merge_kernel<kMergeQuarters>, dim3(rows * kMergeQuarters), dim3(256), 0,
-                         stream, a, p);
+    const bool casc = p.casc_chunks > 0;
+    if (rows >= kMergeRowsOneBlock) {
+      if (casc)
+        hipLaunchKernelGGL((merge_kernel<1, true>), dim3(rows), dim3(256), 0, stream, a, p);
+      else
+        hipLaunchKernelGGL((merge_kernel<1, false>), dim3(rows), dim3(256), 0, stream, a, p);
+    } else if (casc) {
+      hipLaunchKernelGGL((merge_kernel<kMergeQuarters, true>), dim3(rows * kMergeQuarters),
+                         dim3(256), 0, stream, a, p);
+    } else {
+      hipLaunchKernelGGL((merge_kernel<kMergeQuarters, false>), dim3(rows * kMergeQuarters),
+                         dim3(256), 0, stream, a, p);
+    }
   }
   return hipGetLastError();
 }

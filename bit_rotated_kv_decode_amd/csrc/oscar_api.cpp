@@ -96,6 +96,17 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   long long pps = std::max<long long>(4, (items + target - 1) / target);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
+  // On the four-head single-group pass a wave takes pages two at a time: a multiple of eight pages
+  // per item gives every wave whole pairs (no pair step spent on one page; measured at 100k
+  // tokens: 32 pages per item 14.40 us against 27 pages 14.77 us, 24 pages 17.3 us -- a second
+  // round of blocks).  Rounding up keeps the grid within one round; it is taken while the grid
+  // keeps at least three quarters of its blocks.
+  if (int2_fp8_pass(p.gqa, p.n_groups) && items > 0) {
+    const long long up = std::min<long long>(kMaxPagesPerSplit, (p.pages_per_split + 7) / 8 * 8);
+    if (4 * ((items + up - 1) / up) >= 3 * std::min(target, (items + p.pages_per_split - 1) /
+                                                               p.pages_per_split))
+      p.pages_per_split = static_cast<int>(up);
+  }
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
   // whole cascade chunks of the shared prefix (the cascade runs on the four-head single-group pass)
   if (prefix_pages > 0 && int2_fp8_pass(p.gqa, p.n_groups)) {
