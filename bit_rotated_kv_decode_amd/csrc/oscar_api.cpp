@@ -96,16 +96,25 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   long long pps = std::max<long long>(4, (items + target - 1) / target);
   pps = std::max<long long>(pps, (p.max_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = static_cast<int>(std::min<long long>(pps, kMaxPagesPerSplit));
-  // On the four-head single-group pass a wave takes pages two at a time: a multiple of eight pages
-  // per item gives every wave whole pairs (no pair step spent on one page; measured at 100k
-  // tokens: 32 pages per item 14.40 us against 27 pages 14.77 us, 24 pages 17.3 us -- a second
-  // round of blocks).  Rounding up keeps the grid within one round; it is taken while the grid
-  // keeps at least three quarters of its blocks.
+  // The four-head single-group pass takes a wave's pages two at a time, so items get a multiple of
+  // eight pages (whole pairs per wave: a pair step costs the same with one page) while the grid
+  // keeps three quarters of its blocks.  Then one INT2 block per compute unit (each wave alone on
+  // its SIMD) replaces the two per unit when a wave gets at least four pairs that way, or when
+  // two per unit leave a wave less than one pair.  Measured on MI355X: 100k tokens, Hkv 8: 56
+  // pages per item (224 blocks) 13.6 us against 14.5 us at 32 pages (392 blocks); Hkv 1: 8 pages
+  // 7.0 us against 8.8 us at 4; 32k tokens, Hkv 8: 9 pages (456 blocks) 8.8 us against 16 pages
+  // (254 blocks) 9.1 us.  A grid that leaves some units two INT2 blocks and others one runs at the
+  // slower units' pace (48 pages at 100k: 264 blocks, 16.4 us).
   if (int2_fp8_pass(p.gqa, p.n_groups) && items > 0) {
     const long long up = std::min<long long>(kMaxPagesPerSplit, (p.pages_per_split + 7) / 8 * 8);
     if (4 * ((items + up - 1) / up) >= 3 * std::min(target, (items + p.pages_per_split - 1) /
-                                                               p.pages_per_split))
+                                                             p.pages_per_split))
       p.pages_per_split = static_cast<int>(up);
+    const long long one = std::min<long long>(
+        kMaxPagesPerSplit, ((items + kComputeUnits - 1) / kComputeUnits + 7) / 8 * 8);
+    if ((items + one - 1) / one <= kComputeUnits && one >= p.pages_per_split &&
+        (one >= 32 || p.pages_per_split < 8))
+      p.pages_per_split = static_cast<int>(one);
   }
   p.num_splits = p.max_pages ? (p.max_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
   // whole cascade chunks of the shared prefix (the cascade runs on the four-head single-group pass)

@@ -18,6 +18,7 @@ constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
 constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
+constexpr int kComputeUnits = 256;        // compute units of an MI355X (gfx950)
 // Shared-prefix cascade: a cascade block takes kCascPages pages of the shared prefix of one KV head
 // (staged in LDS) for a group of kCascGroup sequences, four waves taking kCascGroup / 4 each.
 constexpr int kCascPages = 12;

@@ -434,17 +434,24 @@ def test_binding_rejects_undersized_buffers(wrong, name):
 
 def test_decode_splits_query():
     # the plan aims at one round of two blocks per compute unit (512 blocks with the BF16 chunk
-    # blocks), at least 4 pages per split; on the four-head single-group pass the pages per split
-    # round up to a multiple of 8 (whole page pairs per wave) while the grid keeps 3/4 of its blocks
+    # blocks), at least 4 pages per split; on the four-head single-group pass, whole page pairs
+    # per wave (multiples of 8 pages while the grid keeps 3/4 of its blocks), then one block per
+    # compute unit (256) when that gives a wave four pairs or more, or two per unit give it less
+    # than one
     lay = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2000)
-    # 1558 pages x 8 heads / 472 blocks -> 27 pages, rounded to 32 (392 blocks >= 3/4 of 462)
-    assert ok.decode_splits(lay, 1, 100000) == (49, 32)
-    assert ok.decode_splits(lay, 1, 32768) == (57, 9)         # 16 would leave 256 of 456 blocks
+    # 1558 pages x 8 heads: 27 -> 32 pages (392 blocks), then 49 -> 56 pages: 224 blocks
+    assert ok.decode_splits(lay, 1, 100000) == (28, 56)
+    # 507 x 8: 9 pages (16 would leave 254 of 456 blocks; one per unit would give 2 pairs)
+    assert ok.decode_splits(lay, 1, 32768) == (57, 9)
     assert ok.decode_splits(lay, 1, 320) == (0, 4)
     one = _lay(num_kv_heads=1, num_q_heads=4, max_pages_per_seq=2000)
-    assert ok.decode_splits(one, 1, 100000) == (390, 4)       # 8 would halve the grid
+    assert ok.decode_splits(one, 1, 100000) == (195, 8)       # 4 pages = half a pair per wave
+    two = _lay(num_kv_heads=2, num_q_heads=8, max_pages_per_seq=2000)
+    assert ok.decode_splits(two, 1, 100000) == (195, 8)       # 7 -> 8 pages, one pair per wave
     gqa8 = _lay(num_kv_heads=8, num_q_heads=64, max_pages_per_seq=2000)
-    assert ok.decode_splits(gqa8, 1, 100000) == (58, 27)      # the int8 / bf16 pass: no rounding
+    assert ok.decode_splits(gqa8, 1, 100000) == (58, 27)      # the int8 / bf16 pass: as planned
+    big = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2100, max_seqs=64)
+    assert ok.decode_splits(big, 64, 130009) == (8, 256)      # the per-item page limit
     with pytest.raises(ok.OscarError):
         ok.decode_splits(lay, -1, 10)
 
