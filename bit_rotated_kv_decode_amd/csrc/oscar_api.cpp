@@ -104,8 +104,10 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   // pages per item (224 blocks) 13.6 us against 14.5 us at 32 pages (392 blocks); Hkv 1: 8 pages
   // 7.0 us against 8.8 us at 4; 32k tokens, Hkv 8: 9 pages (456 blocks) 8.8 us against 16 pages
   // (254 blocks) 9.1 us.  A grid that leaves some units two INT2 blocks and others one runs at the
-  // slower units' pace (48 pages at 100k: 264 blocks, 16.4 us).
-  if (int2_fp8_pass(p.gqa, p.n_groups) && items > 0) {
+  // slower units' pace (48 pages at 100k: 264 blocks, 16.4 us).  Histories with symmetric codebooks
+  // keep the plan above: their pass holds more registers (two value accumulators per tile) and ran
+  // slower with one block per unit (100k: 22.9 us at 56 pages against 20.0 us at 27).
+  if (int2_fp8_pass(p.gqa, p.n_groups) && lay.levels_kind == 0 && items > 0) {
     const long long up = std::min<long long>(kMaxPagesPerSplit, (p.pages_per_split + 7) / 8 * 8);
     if (4 * ((items + up - 1) / up) >= 3 * std::min(target, (items + p.pages_per_split - 1) /
                                                              p.pages_per_split))

@@ -450,6 +450,8 @@ def test_decode_splits_query():
     assert ok.decode_splits(two, 1, 100000) == (195, 8)       # 7 -> 8 pages, one pair per wave
     gqa8 = _lay(num_kv_heads=8, num_q_heads=64, max_pages_per_seq=2000)
     assert ok.decode_splits(gqa8, 1, 100000) == (58, 27)      # the int8 / bf16 pass: as planned
+    sym = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2000, levels_kind=1)
+    assert ok.decode_splits(sym, 1, 100000) == (58, 27)       # symmetric codebooks: as planned
     big = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2100, max_seqs=64)
     assert ok.decode_splits(big, 64, 130009) == (8, 256)      # the per-item page limit
     with pytest.raises(ok.OscarError):
