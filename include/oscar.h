@@ -321,8 +321,8 @@ oscar_status oscar_decode_attn_codebook(const oscar_layout* layout, const void* 
  * workspace: oscar_decode_workspace_bytes_prefix(layout, batch, max_seq_len, prefix_pages) bytes.
  * The cascade runs on layouts with up to four query heads per KV head, group_size 128 and
  * levels_kind 0; other layouts take the split items alone (the same result).  A layout with
- * levels_kind 1 is refused (SHAPE).  Stage OSCAR_STAGE_INT2 launches the
- * cascade blocks ahead of the split items on the same stream.
+ * levels_kind 1 is refused (SHAPE).  The cascade blocks run in the segment launch (stage
+ * OSCAR_STAGE_INT2), beside the split items.
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
 oscar_status oscar_decode_attn_prefix(const oscar_layout* layout, const void* pool,
                                       const int32_t* page_table, const void* sink_k,
@@ -357,7 +357,7 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
                                void* stream);
 
 /* oscar_decode_step over a shared prefix: oscar_append followed by oscar_decode_attn_prefix
- * (seq_lens = seq_pos + 1), in three launches as oscar_decode_step, plus the cascade launch.
+ * (seq_lens = seq_pos + 1), in three launches as oscar_decode_step.
  * The new tokens' demotions must not land in a shared page (oscar_check_page_table with
  * extra_tokens); a layout with levels_kind 1 is refused (SHAPE).  Arguments
  * are those of oscar_decode_step and oscar_decode_attn_prefix, with the same requirements;
