@@ -93,7 +93,7 @@ class FullLayer:
         mx = max(self.lengths) + 1
         out = torch.empty((self.B, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
         if prefix:
-            # the shared prefix handed to the cascade (the benchmark's configuration)
+            # the shared prefix handed to the cascade, as the benchmark hands it
             ids, shared = workloads.shared_prefix(wl, self.table, self.lengths, spare_tokens=1)
             ok.check_shared_prefix(self.lay, self.table, ids, shared)
             self.prefix = (torch.from_numpy(ids).to(dev), torch.from_numpy(shared).to(dev))
@@ -288,10 +288,10 @@ def test_full_size_qwen3_8b_100k_symmetric_codebook():
 
 
 def test_full_size_qwen3_8b_b64_shared_prefix():
-    # the step runs with the shared-prefix cascade, as the benchmark times it; the plain attention
-    # over the cache the step left must agree with it to the fp8 parts' resolution and fp32
-    # summation order (1e-4 of each row's largest output: pages pair up from other starting
-    # pages in the two paths), and sampled rows must agree with the oracle
+    # the step runs with the shared-prefix cascade (the benchmark times it beside the plain
+    # step); the plain attention over the cache the step left must agree with it to the fp8
+    # parts' resolution and fp32 summation order (1e-4 of each row's largest output: pages pair
+    # up from other starting pages in the two paths), and sampled rows must agree with the oracle
     wl = workloads.get("qwen3_8b_b64_prefix")
     layer = FullLayer(wl, layer=0, prefix=True)
     lens = layer.lengths
