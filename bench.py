@@ -330,7 +330,7 @@ def main():
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     max_len = max(lengths) + total_steps + 4
     n_prefix = layers[0].prefix_ids.numel() if both else 0
-    ws = torch.empty(ok.decode_workspace_bytes_prefix(layers[0].lay, B, max_len, n_prefix),
+    ws = torch.zeros(ok.decode_workspace_bytes_prefix(layers[0].lay, B, max_len, n_prefix),
                      dtype=torch.uint8, device=dev)
 
     def plain_step():
@@ -404,50 +404,67 @@ def main():
         del other_graph
 
     # ---- timed region 2: the segment-pass kernel (INT2 history + BF16 sink / recent blocks in
-    # one launch) exactly as a step launches it, once per layer pool: a graph of n_layers launches
-    # (the pools repeated in turn up to at least 8 launches, so that one graph launch's overhead
-    # is spread) replayed args.steps times, HIP events around each replay on the launch stream.
-    # Each layer gets its own workspace holding its rotated query.
+    # one launch) exactly as a step launches it -- on the fp8 pass without codebooks or a cascade
+    # the launch also appends the token and rotates the query (oscar_decode_step_stages) -- once
+    # per layer pool: a graph of n_layers launches (the pools repeated in turn up to at least 8
+    # launches, so that one graph launch's overhead is spread) replayed args.steps times, HIP
+    # events around each replay on the launch stream.  Each layer gets its own workspace.  The
+    # repeated launches append again each time (the caches are not read after this).  Then the
+    # same for the segment launch of oscar_decode_attn, which takes an already rotated query.
     lens = pos + 1
     seg = ok.STAGE_INT2 | ok.STAGE_BF16
-    wss = [torch.empty_like(ws) for _ in layers]
-
-    def seg_args(i):
-        Lr = layers[i]
-        c = Lr.cache
-        return (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v, slots, lens,
-                Lr.q, Lr.u_k, Lr.u_v, Lr.out, wss[i], max_len)
+    wss = [torch.zeros_like(ws) for _ in layers]
 
     def attn(i, stages):
-        a = seg_args(i)
+        Lr = layers[i]
+        c = Lr.cache
+        a = (Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v, slots, lens,
+             Lr.q, Lr.u_k, Lr.u_v, Lr.out, wss[i], max_len)
         if cascade:
-            ok.decode_attn_prefix(*a[:12], layers[i].prefix_ids, layers[i].shared_pages,
-                                  *a[12:], stages=stages)
-        elif layers[i].lay.levels_kind == ok.LEVELS_SYMMETRIC:
-            ok.decode_attn_codebook(*a[:12], layers[i].levels, layers[i].levels, *a[12:],
-                                    stages=stages)
+            ok.decode_attn_prefix(*a[:12], Lr.prefix_ids, Lr.shared_pages, *a[12:],
+                                  stages=stages)
+        elif Lr.lay.levels_kind == ok.LEVELS_SYMMETRIC:
+            ok.decode_attn_codebook(*a[:12], Lr.levels, Lr.levels, *a[12:], stages=stages)
         else:
             ok.decode_attn(*a, stages=stages)
 
-    for i in range(len(layers)):
-        attn(i, ok.STAGE_QUERY)
+    def step_part(i, stages):
+        Lr = layers[i]
+        c = Lr.cache
+        ok.decode_step(Lr.lay, c.pool, Lr.table, c.sink_k, c.sink_v, c.recent_k, c.recent_v,
+                       Lr.u_k, Lr.u_v, Lr.clip_k, Lr.clip_v, Lr.k_new, Lr.v_new, slots, pos,
+                       Lr.q, Lr.out, wss[i], max_len, levels_k=Lr.levels, levels_v=Lr.levels,
+                       stages=stages)
 
     seg_reps = -(-8 // len(layers))
 
-    def seg_launches():
-        for _ in range(seg_reps):
-            for i in range(len(layers)):
-                attn(i, seg)
+    def time_launches(launch):
+        def launches():
+            for _ in range(seg_reps):
+                for i in range(len(layers)):
+                    launch(i, seg)
 
-    seg_graph = capture(seg_launches)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    seg_us = []
-    for _ in range(args.steps):
-        e0.record()
-        seg_graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        seg_us.append(e0.elapsed_time(e1) * 1e3 / (seg_reps * len(layers)))
+        g_seg = capture(launches)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        us = []
+        for _ in range(args.steps):
+            e0.record()
+            g_seg.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / (seg_reps * len(layers)))
+        return us
+
+    # the step's own segment launch (the cascade step's is oscar_decode_attn_prefix's)
+    seg_launch = attn if cascade else step_part
+    for i in range(len(layers)):
+        seg_launch(i, ok.STAGE_QUERY)
+    seg_us = time_launches(seg_launch)
+    attn_us = None
+    if not cascade:
+        for i in range(len(layers)):
+            attn(i, ok.STAGE_QUERY)
+        attn_us = time_launches(attn)
 
     # algorithmic bytes of the timed steps: attention (as the segment launch counts them, plus
     # the bf16 query in and the fp32 output) and the append (new K/V rows in, the displaced row
@@ -461,14 +478,25 @@ def main():
         append = B * (hkv * 128 * 2 * 2 * 3 + hkv * bpt)
         att_bytes += n_layers * (att + append)
     seg_lengths = [int(x) for x in lens.tolist()]
-    # the segment launch also reads the rotated int8 query (INT2 blocks) and the bf16 query;
-    # pages shared by several sequences count once (logical bytes reported alongside)
-    seg_bytes = history_bytes(wl, seg_lengths, layers[0].table_np) + B * hq * (256 + 128 * 2)
-    seg_logical = history_bytes(wl, seg_lengths) + B * hq * (256 + 128 * 2)
+    # the segment launch of oscar_decode_attn also reads the rotated query operand (INT2 blocks)
+    # and the bf16 query; pages shared by several sequences count once (logical bytes reported
+    # alongside).  The step's own segment launch, when it prepares the step itself, reads the
+    # bf16 query, U_k and U_v (once per KV head) and does the append's reads and writes instead
+    # of reading a rotated query.
+    fused = not cascade and ok.decode_step_launches(layers[0].lay, B, max_len) == 2
+    attn_extra = B * hq * (256 + 128 * 2)
+    step_extra = (B * hq * 128 * 2 + 2 * hkv * 128 * 128 * 4 +
+                  B * (hkv * 128 * 2 * 2 * 3 + hkv * bpt))
+    attn_bytes = history_bytes(wl, seg_lengths, layers[0].table_np) + attn_extra
+    seg_bytes = attn_bytes - attn_extra + (step_extra if fused else attn_extra)
+    seg_logical = history_bytes(wl, seg_lengths) + (step_extra if fused else attn_extra)
     step_bytes = att_bytes / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     seg_us_avg = float(np.mean(seg_us))
     achieved = seg_bytes / (seg_us_avg * 1e-6) / 1e9
+    # what the step's segment launch reads besides: the step's preparation (U_k, the new rows,
+    # and for a demotion the displaced rows and U_v) -- L2-resident after the first block, so
+    # not counted in the algorithmic bytes above
 
     ctx = (f"context {lengths[0]}" if len(set(lengths)) == 1 else
            f"contexts {min(lengths)}..{max(lengths)}")
@@ -525,6 +553,19 @@ def main():
                                f"{seg_reps * n_layers} launches ({seg_reps} per layer pool), "
                                f"per-launch mean"},
     }
+    if fused:
+        result["roofline"]["kernel"] = (
+            "attn_kernel of the decode step (INT2 split-KV history + BF16 sink/recent blocks; "
+            "the INT2 blocks rotate the query, one BF16 block per KV head demotes the displaced "
+            "token)")
+    if attn_us is not None:
+        a_us = float(np.mean(attn_us))
+        result["attention_only"] = {
+            "kernel": "attn_kernel as oscar_decode_attn launches it (query rotated beforehand)",
+            "avg_launch_us": round(a_us, 3), "launch_us": distribution(attn_us, 3),
+            "bytes_per_launch": int(attn_bytes),
+            "achieved": round(attn_bytes / (a_us * 1e-6) / 1e9, 1),
+            "frac": round(attn_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if both:
         casc_ms, plain_ms = (ms_per_step, other_ms) if cascade else (other_ms, ms_per_step)
         result["cascade"] = {

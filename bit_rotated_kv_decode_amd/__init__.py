@@ -24,6 +24,7 @@ __all__ = [
     "OscarError", "Layout", "LIB_PATH", "lib", "make_layout", "page_block_bytes", "page_bytes",
     "pool_bytes", "sink_bytes", "recent_bytes", "decode_workspace_bytes", "decode_splits",
     "check_page_table", "decode_workspace_bytes_prefix", "check_shared_prefix",
+    "decode_step_launches",
     "demote", "append", "decode_attn", "decode_attn_codebook", "decode_attn_prefix",
     "decode_step", "decode_step_prefix", "decode_step_noalloc", "Cache",
     "STAGE_QUERY", "STAGE_INT2", "STAGE_BF16", "STAGE_MERGE", "STAGE_ALL", "HEAD_DIM", "PAGE_TOKENS", "SINK_TOKENS",
@@ -90,6 +91,10 @@ _SIGNATURES = {
                                                        ctypes.c_size_t, _i32, _i32, _vp]),
     "oscar_decode_step_noalloc": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _i32,
                                                                _i32, _vp]),
+    "oscar_decode_step_launches": (_i32, [_LP, _i32, _i32]),
+    "oscar_decode_step_stages": (_i32, [_LP] + [_vp] * 17 + [ctypes.c_float, _vp, _vp, _vp,
+                                                              ctypes.c_size_t, _i32, _i32,
+                                                              ctypes.c_uint32, _vp]),
     "oscar_decode_workspace_bytes_prefix": (ctypes.c_size_t, [_LP, _i32, _i32, _i32]),
     "oscar_check_shared_prefix": (_i32, [_LP, _vp, _i32, _vp, _vp, _i32]),
     "oscar_decode_attn_prefix": (_i32, [_LP] + [_vp] * 13 + [_i32, ctypes.c_float, _vp, _vp,
@@ -177,6 +182,12 @@ def decode_workspace_bytes_prefix(lay: Layout, batch: int, max_seq_len: int,
                                   prefix_pages: int) -> int:
     return lib().oscar_decode_workspace_bytes_prefix(ctypes.byref(lay), batch, max_seq_len,
                                                      prefix_pages)
+
+
+def decode_step_launches(lay: Layout, batch: int, max_seq_len: int) -> int:
+    """Launches of one oscar_decode_step: 2 when the segment launch appends and rotates the query
+    itself, else 3 (0: invalid layout or shape)."""
+    return lib().oscar_decode_step_launches(ctypes.byref(lay), batch, max_seq_len)
 
 
 def decode_splits(lay: Layout, batch: int, max_seq_len: int):
@@ -444,9 +455,10 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
                 q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
                 lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0,
                 levels_k: Optional[torch.Tensor] = None,
-                levels_v: Optional[torch.Tensor] = None) -> None:
-    """append(k_new, v_new at seq_pos) then decode_attn(q) over seq_pos + 1 tokens, in three
-    launches (oscar_decode_step); the caller advances seq_pos afterwards."""
+                levels_v: Optional[torch.Tensor] = None, stages: Optional[int] = None) -> None:
+    """append(k_new, v_new at seq_pos) then decode_attn(q) over seq_pos + 1 tokens
+    (oscar_decode_step, or oscar_decode_step_stages with the launches `stages` selects); the
+    caller advances seq_pos afterwards.  The workspace must be zero-filled before its first use."""
     bsz = seq_pos.numel()
     if tuple(k_new.shape) != (bsz, lay.num_kv_heads, HEAD_DIM) or k_new.shape != v_new.shape:
         raise TypeError("k_new / v_new must be [batch, Hkv, 128]")
@@ -456,7 +468,8 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
                      u_k, u_v, lse)
     _shape(clip_k, "clip_k", (lay.num_kv_heads,))
     _shape(clip_v, "clip_v", (lay.num_kv_heads,))
-    _check(lib().oscar_decode_step(
+    fn = lib().oscar_decode_step if stages is None else lib().oscar_decode_step_stages
+    _check(fn(
         ctypes.byref(lay), _contig(pool, "pool", torch.uint8),
         _contig(page_table, "page_table", torch.int32), _contig(sink_k, "sink_k", torch.bfloat16),
         _contig(sink_v, "sink_v", torch.bfloat16), _contig(recent_k, "recent_k", torch.bfloat16),
@@ -469,7 +482,7 @@ def decode_step(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_
         float(sm_scale), _contig(out, "out", torch.float32),
         None if lse is None else _contig(lse, "lse", torch.float32),
         _contig(workspace, "workspace", torch.uint8), workspace.numel(), bsz, int(max_seq_len),
-        _stream()), "decode_step")
+        *(() if stages is None else (ctypes.c_uint32(stages),)), _stream()), "decode_step")
 
 
 def decode_step_prefix(lay: Layout, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k,

@@ -15,6 +15,7 @@
 //                    the BF16 partials, normalisation.
 // Softmax statistics are kept in the log2 domain: scores are scaled by sm_scale * log2(e).
 #include "device_common.h"
+#include "encode_common.h"
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -104,6 +105,15 @@ struct Int2Lds {
   // cascade blocks: the chunk's kCascPages page blocks of one KV head, staged once for all waves
   static constexpr int STAGE = (TOTAL + 15) & ~15;
   static constexpr int CASC_TOTAL = STAGE + kCascPages * (kMetaOff + kPage * 8 * NG);
+  // a decode step's own query rotation (step_prologue), apart from everything the page loop
+  // uses: the G query rows (fp32 [G][128]), their rotation partials (fp64 [G][8][128]) and the
+  // query operands the block builds: NA tiles, their E8M0 row scales and the per-head sums
+  static constexpr int FX = (TOTAL + 15) & ~15;
+  static constexpr int FRED = FX + G * kHeadDim * 4;
+  static constexpr int FOPS = FRED + G * dev::kRotGroups * kHeadDim * 8;
+  static constexpr int FSC = FOPS + NA * 2048;
+  static constexpr int FSIG = FSC + NA * 64 * 4;
+  static constexpr int FUSED_TOTAL = FSIG + G * 4 * 4;
 };
 
 // Whether a page pair may be a wave's last one (a compile-time flag of the pair step).
@@ -111,6 +121,161 @@ template <bool B>
 struct PairKind {
   static constexpr bool value = B;
 };
+
+// ------------------------------------------------------------------------------------------
+// A decode step's own preparation inside the segment launch (fp8 pass, one group, no codebooks),
+// with the arithmetic of the preparation launch (encode.hip) in the same order, so both give the
+// same bytes:
+//  - every INT2 split block rotates the G query rows of its KV head and builds their key operands
+//    in LDS (step_prologue);
+//  - once the new token at position pos >= 320 displaces the ring row of position pos - 256
+//    (history index pos - 320, in the history's last page), the BF16 block of the sink chunk of
+//    that (sequence, KV head) moves the row into its page slot -- rotation, quantiser, store --
+//    gives the ring slot to the new token and then sets the pair's flag to pos + 1
+//    (displace_token);
+//  - the one wave that reads that page waits for the flag before it loads its last page pair,
+//    and clears it.  The BF16 block has the lower workgroup number, so it is dispatched first and
+//    never waits for anything; the wait is bounded all the same, and a wave that gives up poisons
+//    its partial (the output turns NaN).
+constexpr int kFlagSpins = 1 << 19;   // polls of about 0.2 us each
+// The BF16 chunk whose block demotes: the last one.  The launch's workgroups beyond one per
+// compute unit (the last INT2 splits) share units with the first ones, the sink chunks; the
+// demoting block is better off alone on its unit, and so are they.
+constexpr int kDisplaceChunk = kBf16Chunks - 1;
+
+// step_prologue: every thread of the block; on return the query operands are in LDS.  U_k's
+// slices and the query rows are requested first, `prefetch0` (the first page pair's loads) once
+// they have arrived -- issued earlier, the page loads would queue ahead of them at the memory and
+// hold up the whole preparation -- and `prefetch1` (the second pair's) once U_k's registers are
+// free.  One pass over U_k's slices serves all rows (thread t: the partial
+// sums over rows 16 (t / 32) .. + 15 of U for columns 4 (t % 32) .. + 3); wave w then sums the
+// eight partials of row w in order and applies the Hadamard transform and the operand split.
+template <int G, typename Prefetch0, typename Prefetch1>
+__device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p, int b, int kv,
+                                              unsigned char* smem, Prefetch0&& prefetch0,
+                                              Prefetch1&& prefetch1) {
+  using S = Int2Lds<G, 1>;
+  float* xs = reinterpret_cast<float*>(smem + S::FX);
+  double (*red)[dev::kRotGroups][kHeadDim] =
+      reinterpret_cast<double (*)[dev::kRotGroups][kHeadDim]>(smem + S::FRED);
+  const int tid = threadIdx.x;
+  constexpr int kQ = (G * kHeadDim + 255) / 256;   // query values per thread
+  dev::URows uk;
+  dev::load_u_rows(a.u_k + static_cast<int64_t>(kv) * kHeadDim * kHeadDim, uk);
+  const uint16_t* qrow = a.q + static_cast<int64_t>(b * p.hq + kv * G) * kHeadDim;
+  uint16_t qv[kQ];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) qv[j] = tid + 256 * j < G * kHeadDim ? qrow[tid + 256 * j] : 0;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+    if (tid + 256 * j < G * kHeadDim) xs[tid + 256 * j] = dev::bf16_to_f32(qv[j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) asm volatile("" ::"v"(uk.v[k].x));
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch0();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();   // query rows staged
+  const int g = tid >> 5, c = tid & 31;
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    double y[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const double xi = static_cast<double>(xs[r * kHeadDim + 16 * g + k]);
+      y[0] = fma(xi, static_cast<double>(uk.v[k].x), y[0]);
+      y[1] = fma(xi, static_cast<double>(uk.v[k].y), y[1]);
+      y[2] = fma(xi, static_cast<double>(uk.v[k].z), y[2]);
+      y[3] = fma(xi, static_cast<double>(uk.v[k].w), y[3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[r][g][4 * c + e] = y[e];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch1();   // U_k's registers are free again
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  const int wave = tid >> 6;
+  if (wave < G) {
+    const int lane = dev::lane_id();
+    double y0 = red[wave][0][lane], y1 = red[wave][0][lane + 64];
+#pragma unroll
+    for (int j = 1; j < dev::kRotGroups; ++j) {
+      y0 += red[wave][j][lane];
+      y1 += red[wave][j][lane + 64];
+    }
+    double o0, o1;
+    dev::hadamard_bitrev(y0, y1, o0, o1);
+    enc::query_operands(o0, o1, 1, G, wave, a.sm_scale * kLog2e, smem + S::FOPS,
+                        reinterpret_cast<int32_t*>(smem + S::FSC),
+                        reinterpret_cast<float*>(smem + S::FSIG) + 4 * wave);
+  }
+  __syncthreads();   // the query operands
+}
+
+// displace_token: the whole BF16 block of the sink chunk, before its own work, in the first
+// 9 KiB of its LDS (every read of them is done when it returns).  Per tensor (K, then V) the rotation of the preparation launch's append: the
+// block's fp64 partial sums, wave 0 adding them and quantising (one group, the equally spaced
+// levels of levels_kind 0) and storing the token.  Wave 0 then makes its stores visible at agent
+// scope before it sets the flag.
+__device__ __forceinline__ void displace_token(const DecodeArgs& a, const Plan& p, int b, int kv,
+                                               int pos, int64_t slot, unsigned char* lds) {
+  const AppendArgs& ap = a.ap;
+  int32_t* flag = reinterpret_cast<int32_t*>(a.workspace + p.off_flags) + b * p.hkv + kv;
+  // cleared first (the reader waits for this call's value, which is written last)
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* x = reinterpret_cast<float*>(lds);                                // [2][128]
+  double (*red)[kHeadDim] = reinterpret_cast<double (*)[kHeadDim]>(lds + 2 * kHeadDim * 4);
+  const int tid = threadIdx.x;
+  constexpr int64_t kU = kHeadDim * kHeadDim;
+  dev::URows ur;
+  dev::load_u_rows(ap.u_k + kv * kU, ur);
+  // thread t < 128: key channel t, else value channel t - 128
+  const int tensor = tid >> 7, ch = tid & (kHeadDim - 1);
+  uint16_t* ring = (tensor == 0 ? ap.recent_k : ap.recent_v) +
+                   ((slot * p.hkv + kv) * kRecent + pos % kRecent) * kHeadDim + ch;
+  const uint16_t nw =
+      (tensor == 0 ? ap.k_new : ap.v_new)[(static_cast<int64_t>(b) * p.hkv + kv) * kHeadDim + ch];
+  x[tensor * kHeadDim + ch] = dev::bf16_to_f32(*ring);
+  const int idx = pos - kSink - kRecent;
+  uint8_t* blk = enc::page_block(ap.pool, ap.page_table, ap.max_pages_per_seq, b, idx, p.hkv,
+                                 kv, block_bytes(1));
+  __syncthreads();   // the displaced rows are staged: their ring slot takes the new token
+  *ring = nw;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t == 1) dev::load_u_rows(ap.u_v + kv * kU, ur);
+    double r0, r1;
+    if (dev::rotate1_block(x + t * kHeadDim, ur, red, r0, r1)) {
+      const float* lvp = t == 0 ? ap.levels_k : ap.levels_v;
+      const float lv_lo = lvp ? lvp[2 * kv] : 0.0f;
+      const float lv_step = lvp ? lvp[2 * kv + 1] : 1.0f;
+      const enc::LaneCodes q = enc::quantize_lane(r0, r1, (t == 0 ? ap.clip_k : ap.clip_v)[kv],
+                                                  1, lv_lo, lv_step, 0);
+      enc::store_token(blk, t, idx % kPage, 1, q);
+    }
+    __syncthreads();   // wave 0 has read the partials before they are written again
+  }
+  if ((tid >> 6) == 0) {
+    __threadfence();
+    if (tid == 0) __hip_atomic_store(flag, pos + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The reader's side: wait (bounded) until the flag of (b, kv) reads pos + 1, then clear it.
+// Returns false if it never did.
+__device__ __forceinline__ bool wait_displaced(const DecodeArgs& a, const Plan& p, int b, int kv,
+                                               int pos) {
+  int32_t* flag = reinterpret_cast<int32_t*>(a.workspace + p.off_flags) + b * p.hkv + kv;
+  bool seen = false;
+  for (int it = 0; it < kFlagSpins && !seen; ++it) {
+    seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == pos + 1;
+    if (!seen) __builtin_amdgcn_s_sleep(8);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (dev::lane_id() == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return seen;
+}
 
 // STREAM: history pages are fetched with non-temporal loads.  Chosen when the launch holds one
 // sequence, so no page is read twice in it; with several sequences pages may be shared (a prefix
@@ -121,9 +286,13 @@ struct PairKind {
 // history wholly holds the chunk), runs the same page-pair arithmetic as a split block against
 // the staged pages and writes the sequence's partial for the chunk itself.
 // PCASC: the plan has cascade chunks (a split block then skips the pages they took).
-template <int G, int NG, bool STREAM, bool CB, bool CASC = false, bool PCASC = CASC>
+// FUSE: a decode step whose preparation the block runs itself (step_prologue); the query operands
+// then come from LDS.
+template <int G, int NG, bool STREAM, bool CB, bool CASC = false, bool PCASC = CASC,
+          bool FUSE = false>
 __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, int split, int kv,
                                            int grp, unsigned char* smem) {
+  static_assert(!FUSE || (NG == 1 && !CB && !CASC && !PCASC), "fp8 pass without extras");
   using S = Int2Lds<G, NG>;
   constexpr int NT = S::NT, NA = S::NA;
   constexpr int BLK = kMetaOff + kPage * 8 * NG;
@@ -144,6 +313,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // chunk: local indices 0 .. kCascPages - 1, all of them history.
   static_assert((kMaxPagesPerSplit + 3) / 4 <= 8 + 64, "eight scalar ids and one per lane");
   int w0 = 0, w1 = kCascPages, wa = 0, n_hist = 1 << 30;
+  bool demote = false;   // FUSE: the split holds the page the displaced token goes to,
+  int owner = -1;        // which wave `owner` reads
   int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int more_ids = 0;
   if constexpr (!CASC) {
@@ -166,6 +337,10 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     const int n_pages = (n_hist + kPage - 1) / kPage;
     if (p0 >= n_pages) return;
     const int p1 = min(p0 + p.pages_per_split, n_pages);
+    if constexpr (FUSE) {
+      demote = p1 == n_pages;
+      owner = (n_pages - 1 - p0) / qw;
+    }
     // pages of a shared prefix that cascade blocks took for this sequence are not this item's
     int cend = 0;
     if constexpr (PCASC) cend = cascade_pages(p, n_hist, a.shared_pages[b]);
@@ -184,19 +359,24 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   auto load_query = [&]() {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.workspace + p.off_qops +
-                                                        (op0 + i) * 2048 + lane * 32);
+      const uint4* src =
+          FUSE ? reinterpret_cast<const uint4*>(smem + S::FOPS + i * 2048 + lane * 32)
+               : reinterpret_cast<const uint4*>(a.workspace + p.off_qops + (op0 + i) * 2048 +
+                                                lane * 32);
       const uint4 x = src[0], y = src[1];
       aq[i] = v8i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z),
                   static_cast<int>(x.w), static_cast<int>(y.x), static_cast<int>(y.y),
                   static_cast<int>(y.z), static_cast<int>(y.w)};
-      sq[i] = reinterpret_cast<const int32_t*>(a.workspace + p.off_qscale)[(op0 + i) * 64 + lane];
+      sq[i] = FUSE ? reinterpret_cast<const int32_t*>(smem + S::FSC)[i * 64 + lane]
+                   : reinterpret_cast<const int32_t*>(a.workspace +
+                                                      p.off_qscale)[(op0 + i) * 64 + lane];
     }
     const float* qmeta = reinterpret_cast<const float*>(a.workspace + p.off_sigma);
 #pragma unroll
     for (int ht = 0; ht < NT; ++ht) {
       const int hd = 4 * ht + gq;
-      const float* m = qmeta + static_cast<int64_t>(head0 + min(hd, G - 1)) * 4;
+      const float* m = FUSE ? reinterpret_cast<const float*>(smem + S::FSIG) + min(hd, G - 1) * 4
+                            : qmeta + static_cast<int64_t>(head0 + min(hd, G - 1)) * 4;
 #pragma unroll
       for (int g = 0; g < NG; ++g) sig[ht][g] = hd < G ? m[g] : 0.f;
       hbias[ht] = hd < G ? 0.f : -INFINITY;
@@ -621,12 +801,16 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // a pair never covers a later one's.  The query operands are loaded between the first two
   // pairs' loads: the first pair waits on them and on its own pages only.
   const int npairs = w1 > wa ? (w1 - wa + 1) / 2 : 0;
+  // FUSE: the wave that reads the displaced token's page takes its last pair after the loop,
+  // once the token is there (the same pairs as without FUSE, so the same arithmetic)
+  const bool last_apart = FUSE && demote && wave == owner;
+  const int nl = last_apart ? npairs - 1 : npairs;   // pairs of the loop
   // pairs before a wave's last one skip the checks
   using Inner = PairKind<false>;
   // Issue priority by the pairs a wave has left: two blocks share a compute unit, and the arbiter
   // otherwise favours the older one throughout, so the younger one would end its pages alone.
   auto set_prio = [&](int q) {
-    const int rem = npairs - q;
+    const int rem = nl - q;
     if (rem >= 3)
       __builtin_amdgcn_s_setprio(3);
     else if (rem >= 2)
@@ -689,14 +873,20 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     }
     return;
   }
-  if (npairs > 0) {
-    PageRegs r0[2], r1[2];
+  PageRegs r0[2], r1[2];
+  // FUSE: the first pair's loads are in flight during the query rotation
+  if constexpr (FUSE) step_prologue<G>(a, p, b, kv, smem, [&]() {
+      if (nl > 0) load_pair(0, r0);
+    }, [&]() {
+      if (nl > 1) load_pair(1, r1);
+    });
+  if (nl > 0) {
     set_prio(0);
-    load_pair(0, r0);
+    if (!FUSE) load_pair(0, r0);
     __builtin_amdgcn_sched_barrier(0);
     load_query();
     __builtin_amdgcn_sched_barrier(0);
-    load_pair(1, r1);
+    if (!FUSE) load_pair(1, r1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (CB) {
       // one pair step with the checks throughout (the codebook pass's registers are at the
@@ -720,11 +910,11 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
         process_pair(q, r1, false, PairKind<true>{});
       }
     } else {
-    if (npairs == 1)
+    if (nl == 1)
       process_pair(0, r0, true, PairKind<true>{});
     else
       process_pair(0, r0, true, Inner{});
-    int q = 1, rest = npairs - 1;
+    int q = 1, rest = nl - 1;
     // rounds of two pairs while a later pair remains; the wave's last pair (the only one with
     // checks) in the round or single pair after the loop
     for (; rest >= 3; rest -= 2) {
@@ -753,6 +943,18 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
     }
     }
     __builtin_amdgcn_s_setprio(0);
+  }
+  if constexpr (FUSE) {
+    if (last_apart) {
+      // the displaced token's page is read once the sink chunk's block has stored the token
+      const bool ok = wait_displaced(a, p, b, kv, n_hist + kSink + kRecent - 1);
+      if (nl == 0) load_query();
+      PageRegs rr[2];
+      load_pair(nl, rr);
+      process_pair(nl, rr, nl == 0, PairKind<true>{});
+#pragma unroll
+      for (int ht = 0; ht < NT; ++ht) l_run[ht] = ok ? l_run[ht] : NAN;
+    }
   }
 
   // ---- finish the wave: l and z summed over the 16 lanes of each head; each accumulator row as
@@ -838,7 +1040,11 @@ struct Bf16Lds {
   static constexpr int TOTAL = RACC + 4 * G * kHeadDim * 4;
 };
 
-template <int G>
+// FUSE: a decode step whose append the segment launch runs: the new token's key and value rows
+// are read from k_new / v_new in place of their row of the sink or ring, and the chunk that holds
+// that row writes them there unless the token displaces a ring row (position >= 320: the sink
+// chunk's block, which demotes the displaced row first, writes the slot after reading it).
+template <int G, bool FUSE = false>
 __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, float scale_log2,
                                            int chunk, int kv, int b, unsigned char* smem) {
   using S = Bf16Lds<G>;
@@ -851,6 +1057,10 @@ __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, f
   const int wave = tid >> 6, lane = dev::lane_id();
   const int L = a.seq_lens[b] + a.len_add;
   const int64_t slot = a.seq_slot[b];
+  if constexpr (FUSE) {
+    if (chunk == kDisplaceChunk && L - 1 >= kSink + kRecent)
+      displace_token(a, p, b, kv, L - 1, slot, smem);   // done with its LDS on return
+  }
   const int head0 = b * p.hq + kv * G;
   const int64_t row0 = chunk == 0 ? (slot * p.hkv + kv) * kSink
                                    : (slot * p.hkv + kv) * kRecent + (chunk - 1) * 64;
@@ -864,22 +1074,49 @@ __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, f
     const int posr = start + (((r - start) % kRecent) + kRecent) % kRecent;
     return n_recent > 0 && posr < L;
   };
+  // FUSE: the chunk row of the new token (position L - 1), or -1
+  int new_row = -1;
+  const uint16_t* knew = nullptr;
+  const uint16_t* vnew = nullptr;
+  if constexpr (FUSE) {
+    const int pos = L - 1;
+    if (chunk == (pos < kSink ? 0 : 1 + (pos % kRecent) / kPage))
+      new_row = pos < kSink ? pos : pos % kPage;
+    knew = a.ap.k_new + (static_cast<int64_t>(b) * p.hkv + kv) * kHeadDim;
+    vnew = a.ap.v_new + (static_cast<int64_t>(b) * p.hkv + kv) * kHeadDim;
+  }
+  auto key_row = [&](int r) {
+    return FUSE && r == new_row ? knew : krows + static_cast<int64_t>(r) * kHeadDim;
+  };
+  auto value_row = [&](int r) {
+    return FUSE && r == new_row ? vnew : vrows + static_cast<int64_t>(r) * kHeadDim;
+  };
   // ---- loads: key quarter rows, value pairs, query
   const int t = tid >> 2, qq = tid & 3;
   const bool kvalid = row_valid(t);
   uint4 kr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    kr[i] = kvalid ? reinterpret_cast<const uint4*>(krows + static_cast<int64_t>(t) * kHeadDim +
-                                                    32 * qq)[i]
+    kr[i] = kvalid ? reinterpret_cast<const uint4*>(key_row(t) + 32 * qq)[i]
                    : make_uint4(0, 0, 0, 0);
   uint32_t vr[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int tv = 16 * wave + i;
-    vr[i] = row_valid(tv) ? reinterpret_cast<const uint32_t*>(vrows + static_cast<int64_t>(tv) *
-                                                                         kHeadDim)[lane]
-                          : 0u;
+    vr[i] = row_valid(tv) ? reinterpret_cast<const uint32_t*>(value_row(tv))[lane] : 0u;
+  }
+  if constexpr (FUSE) {
+    if (new_row >= 0 && L - 1 < kSink + kRecent) {
+      const int64_t o = row0 * kHeadDim + static_cast<int64_t>(new_row) * kHeadDim;
+      uint16_t* kdst = (chunk == 0 ? a.ap.sink_k : a.ap.recent_k) + o;
+      uint16_t* vdst = (chunk == 0 ? a.ap.sink_v : a.ap.recent_v) + o;
+      if (t == new_row)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(kdst + 32 * qq)[i] = kr[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (16 * wave + i == new_row) reinterpret_cast<uint32_t*>(vdst)[lane] = vr[i];
+    }
   }
   for (int i = tid; i < G * kHeadDim; i += 256)
     q_s[i / kHeadDim][i % kHeadDim] =
@@ -968,12 +1205,17 @@ constexpr int attn_lds_bytes() {
 // k * gridDim.x + blockIdx.x, taken KV head fastest, then group, then chunk: the groups of one
 // (chunk, KV head), which read the same pages, are dispatched hkv blocks apart -- with eight KV
 // heads, to one XCD and its L2 (workgroups go to the eight XCDs in turn).
-template <int G, int NG, bool STREAM, bool CB, bool CASC = false>
+// FUSE: a decode step that appends and rotates the query in this launch (see step_prologue).
+template <int G, int NG, bool STREAM, bool CB, bool CASC = false, bool FUSE = false>
 __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, float scale_log2,
                                                       int x0, int casc_z, int casc_step) {
-  constexpr int kLds = CASC && Int2Lds<G, 1>::CASC_TOTAL > attn_lds_bytes<G, NG>()
-                           ? Int2Lds<G, 1>::CASC_TOTAL
-                           : attn_lds_bytes<G, NG>();
+  constexpr int kBase = CASC && Int2Lds<G, 1>::CASC_TOTAL > attn_lds_bytes<G, NG>()
+                            ? Int2Lds<G, 1>::CASC_TOTAL
+                            : attn_lds_bytes<G, NG>();
+  constexpr int kLds = FUSE && Int2Lds<G, 1>::FUSED_TOTAL > kBase ? Int2Lds<G, 1>::FUSED_TOTAL
+                                                                  : kBase;
+  static_assert(!FUSE || kLds >= 2 * kHeadDim * 4 + dev::kRotGroups * kHeadDim * 8,
+                "displace_token's rows and partials");
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const int x = x0 + static_cast<int>(blockIdx.x) / p.hkv, kv = blockIdx.x % p.hkv;
   int b = blockIdx.z;
@@ -991,9 +1233,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, floa
     b -= min(k + 1, casc_z);
   }
   if (x < kBf16Chunks)
-    bf16_block<G>(a, p, scale_log2, x, kv, b, smem);
+    bf16_block<G, FUSE>(a, p, scale_log2, x, kv, b, smem);
   else if constexpr (int2_fp8_pass(G, NG))
-    int2_block<G, NG, STREAM, CB, false, CASC>(a, p, x - kBf16Chunks, kv, b, smem);
+    int2_block<G, NG, STREAM, CB, false, CASC, FUSE>(a, p, x - kBf16Chunks, kv, b, smem);
   else
     int2_block_i8<G, NG, STREAM>(a, p, x - kBf16Chunks, kv, b, smem);
 }
@@ -1254,6 +1496,25 @@ hipError_t launch_g(const DecodeArgs& a, const Plan& p, uint32_t stages, hipStre
       const int step = (p.batch + cz) / cz;   // >= 1
       hipLaunchKernelGGL((attn_kernel<G, 1, false, false, true>), dim3(gx, 1, p.batch + cz),
                          dim3(256), 0, stream, a, p, scale_log2, x0, cz, step);
+      cb_done = true;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (a.fuse && x1 > x0) {
+    // a decode step with its preparation in this launch: every segment block, the fp8 pass
+    // without codebooks or a cascade (the host admits no other)
+    if constexpr (int2_fp8_pass(G, 1)) {
+      if (x0 != 0 || x1 != kBf16Chunks + p.num_splits || p.n_groups != 1 ||
+          a.cb_k != nullptr || p.casc_chunks != 0)
+        return hipErrorInvalidValue;
+      dim3 grid((x1 - x0) * p.hkv, 1, p.batch);
+      if (p.batch == 1)
+        hipLaunchKernelGGL((attn_kernel<G, 1, true, false, false, true>), grid, dim3(256), 0,
+                           stream, a, p, scale_log2, x0, 0, 1);
+      else
+        hipLaunchKernelGGL((attn_kernel<G, 1, false, false, false, true>), grid, dim3(256), 0,
+                           stream, a, p, scale_log2, x0, 0, 1);
       cb_done = true;
     } else {
       return hipErrorInvalidValue;

@@ -145,6 +145,8 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   off = al(off + rows * kBf16Chunks * 2 * 4);
   p.off_bf16_acc = off;
   off = al(off + rows * kBf16Chunks * kHeadDim * 4);
+  p.off_flags = off;
+  off = al(off + static_cast<size_t>(batch) * p.hkv * 4);
   p.total = off;
   return p;
 }
@@ -291,6 +293,8 @@ oscar_status make_decode_args(const oscar_layout* l, const void* pool, const int
   a.cb_v = nullptr;
   a.prefix_ids = plan.casc_chunks > 0 ? prefix_ids : nullptr;
   a.shared_pages = plan.casc_chunks > 0 ? shared_pages : nullptr;
+  a.fuse = 0;
+  a.ap = oscar::AppendArgs{};
   qa.q = a.q;
   qa.u_k = u_k;
   qa.batch = batch;
@@ -592,6 +596,29 @@ oscar_status oscar_decode_attn_codebook(const oscar_layout* l, const void* pool,
 
 namespace {
 
+// Whether a decode step's segment launch appends the token and rotates the query itself: the
+// fp8 pass (at most four query heads per KV head, one group) without codebooks or a cascade.
+bool step_fused(const oscar::Plan& plan, int levels_kind) {
+  return oscar::int2_fp8_pass(plan.gqa, plan.n_groups) && plan.casc_chunks == 0 &&
+         levels_kind == 0;
+}
+
+// The launches of one decode step (those `stages` selects): fused, the segment launch and the
+// merge; otherwise the preparation launch (OSCAR_STAGE_QUERY), the segment launch and the merge.
+hipError_t launch_step(oscar::DecodeArgs& a, const oscar::QueryArgs& qa,
+                       const oscar::AppendArgs& ap, const oscar::Plan& plan, uint32_t stages,
+                       hipStream_t s) {
+  const uint32_t rest = stages & (OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 | OSCAR_STAGE_MERGE);
+  if (step_fused(plan, ap.levels_kind)) {
+    a.fuse = 1;
+    a.ap = ap;
+  } else if (stages & OSCAR_STAGE_QUERY) {
+    const hipError_t e = oscar::launch_prep(&ap, &qa, s);
+    if (e != hipSuccess) return e;
+  }
+  return rest ? oscar::launch_decode(a, plan, rest, s) : hipSuccess;
+}
+
 oscar_status decode_step_impl(const oscar_layout* l, void* pool, const int32_t* page_table,
                               void* sink_k, void* sink_v, void* recent_k, void* recent_v,
                               const float* u_k, const float* u_v, const float* clip_k,
@@ -601,7 +628,10 @@ oscar_status decode_step_impl(const oscar_layout* l, void* pool, const int32_t* 
                               float sm_scale, float* out, float* lse, void* workspace,
                               size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                               void* stream, const int32_t* prefix_ids,
-                              const int32_t* shared_pages, int32_t prefix_pages) {
+                              const int32_t* shared_pages, int32_t prefix_pages,
+                              uint32_t stages = OSCAR_STAGE_ALL) {
+  if (stages == 0 || (stages & ~OSCAR_STAGE_ALL) != 0)
+    return fail(OSCAR_ERR_RANGE, "oscar_decode_step: stage mask 0x%x invalid", stages);
   oscar::AppendArgs ap;
   oscar_status st = make_append_args(l, pool, page_table, sink_k, sink_v, recent_k, recent_v,
                                      u_k, u_v, clip_k, clip_v, levels_k, levels_v, k_new, v_new,
@@ -621,11 +651,11 @@ oscar_status decode_step_impl(const oscar_layout* l, void* pool, const int32_t* 
     a.cb_v = levels_v;
   }
   a.len_add = 1;   // attention sees the appended token
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = oscar::launch_prep(&ap, &qa, s);
-  if (e != hipSuccess) return hip_status(e, "oscar_decode_step");
-  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
-                                                      OSCAR_STAGE_MERGE, s),
+  constexpr uint32_t kSeg = OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16;
+  if (step_fused(plan, l->levels_kind) && (stages & kSeg) != 0 && (stages & kSeg) != kSeg)
+    return fail(OSCAR_ERR_RANGE, "oscar_decode_step: this step's segment launch also appends; "
+                "stages INT2 and BF16 go together (mask 0x%x)", stages);
+  return hip_status(launch_step(a, qa, ap, plan, stages, static_cast<hipStream_t>(stream)),
                     "oscar_decode_step");
 }
 
@@ -644,6 +674,27 @@ oscar_status oscar_decode_step(const oscar_layout* l, void* pool, const int32_t*
                           clip_k, clip_v, levels_k, levels_v, k_new, v_new, seq_slot, seq_pos, q,
                           sm_scale, out, lse, workspace, workspace_bytes, batch, max_seq_len,
                           stream, nullptr, nullptr, 0);
+}
+
+int32_t oscar_decode_step_launches(const oscar_layout* l, int32_t batch, int32_t max_seq_len) {
+  if (check_layout(l) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
+  return step_fused(oscar::make_plan(*l, batch, max_seq_len), l->levels_kind) ? 2 : 3;
+}
+
+oscar_status oscar_decode_step_stages(const oscar_layout* l, void* pool,
+                                      const int32_t* page_table, void* sink_k, void* sink_v,
+                                      void* recent_k, void* recent_v, const float* u_k,
+                                      const float* u_v, const float* clip_k, const float* clip_v,
+                                      const float* levels_k, const float* levels_v,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* seq_slot, const int32_t* seq_pos,
+                                      const void* q, float sm_scale, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, int32_t batch,
+                                      int32_t max_seq_len, uint32_t stages, void* stream) {
+  return decode_step_impl(l, pool, page_table, sink_k, sink_v, recent_k, recent_v, u_k, u_v,
+                          clip_k, clip_v, levels_k, levels_v, k_new, v_new, seq_slot, seq_pos, q,
+                          sm_scale, out, lse, workspace, workspace_bytes, batch, max_seq_len,
+                          stream, nullptr, nullptr, 0, stages);
 }
 
 oscar_status oscar_decode_step_prefix(const oscar_layout* l, void* pool,
@@ -765,11 +816,8 @@ oscar_status oscar_decode_step_noalloc(const oscar_layout* l, void* pool,
     a.cb_v = levels_v;
   }
   a.len_add = 1;   // attention sees the appended token
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  e = oscar::launch_prep(&ap, &qa, s);
-  if (e != hipSuccess) return hip_status(e, "oscar_decode_step_noalloc");
-  return hip_status(oscar::launch_decode(a, plan, OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 |
-                                                      OSCAR_STAGE_MERGE, s),
+  return hip_status(launch_step(a, qa, ap, plan, OSCAR_STAGE_ALL,
+                                static_cast<hipStream_t>(stream)),
                     "oscar_decode_step_noalloc");
 }
 

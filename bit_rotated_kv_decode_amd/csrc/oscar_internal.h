@@ -75,6 +75,8 @@ struct Plan {
   size_t off_int2_acc = 0;   // fp32 [B][Hq][slots][128] rotated-space accumulators
   size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]
   size_t off_bf16_acc = 0;   // fp32 [B][Hq][5][128]
+  size_t off_flags = 0;      // int32 [B][Hkv]: a fused decode step's displaced-token flags, zero
+                             // between calls
   size_t total = 0;
 };
 
@@ -161,6 +163,11 @@ struct DecodeArgs {
   // per sequence, how many leading pages of its page-table row are those; NULL without a cascade
   const int32_t* prefix_ids;
   const int32_t* shared_pages;
+  // fuse != 0: a decode step whose append and query rotation run inside the segment launch (the
+  // fp8 pass without codebooks or a cascade); `ap` holds the step's append arguments and
+  // seq_lens[b] the new token's position (len_add 1)
+  int fuse;
+  AppendArgs ap;
 };
 
 struct QueryArgs {

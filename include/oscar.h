@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 7u
+#define OSCAR_ABI_VERSION 8u
 
 typedef int32_t oscar_status;
 
@@ -340,10 +340,15 @@ oscar_status oscar_decode_attn_prefix(const oscar_layout* layout, const void* po
  * segments): the same result as
  *   oscar_append(..., seq_slot, seq_pos, ...)  followed by
  *   oscar_decode_attn(..., seq_lens = seq_pos + 1, ...)
- * (oscar_decode_attn_codebook with the same levels for a layout with levels_kind 1),
- * in three launches: the append and the query rotation share the first.
+ * (oscar_decode_attn_codebook with the same levels for a layout with levels_kind 1).
+ * With at most four query heads per KV head, one group per vector and levels_kind 0, two
+ * launches: the segment launch also rotates the query (in each INT2 block) and appends the token
+ * (one BF16 block per (sequence, KV head) demotes the displaced token and signals the one wave
+ * that reads its page through a flag word per (sequence, KV head) in the workspace); otherwise
+ * three, the append and the query rotation sharing the first.  Both give the same bytes.
  * seq_pos[b] = position of the new token = tokens cached before the step; seq_pos[b] + 1 must be
- * in [1, max_seq_len].  Arguments are those of the two calls, with the same requirements.
+ * in [1, max_seq_len].  Arguments are those of the two calls, with the same requirements; the
+ * workspace must be zero-filled before its first use (every call leaves the flag words zero).
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP; nothing is launched
  * unless every argument check passes. */
 oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int32_t* page_table,
@@ -356,8 +361,31 @@ oscar_status oscar_decode_step(const oscar_layout* layout, void* pool, const int
                                size_t workspace_bytes, int32_t batch, int32_t max_seq_len,
                                void* stream);
 
+/* How many launches oscar_decode_step makes for this layout and shape: 2 when the segment launch
+ * appends and rotates the query itself (at most four query heads per KV head, one group per
+ * vector, levels_kind 0), else 3; 0 for an invalid layout or shape.  (oscar_decode_step_prefix
+ * always makes 3.) */
+int32_t oscar_decode_step_launches(const oscar_layout* layout, int32_t batch, int32_t max_seq_len);
+
+/* The launches of oscar_decode_step that `stages` selects (a mask as in oscar_decode_attn_stages):
+ * OSCAR_STAGE_QUERY the preparation launch (append + query rotation; nothing when the segment
+ * launch does both), OSCAR_STAGE_INT2 | OSCAR_STAGE_BF16 the segment launch (when it appends, the
+ * two go together: RANGE otherwise), OSCAR_STAGE_MERGE the merge.  Selected in that order, over
+ * calls, they make one step; one launch alone, repeated (to time it), appends again each time.
+ * Arguments and results otherwise as oscar_decode_step. */
+oscar_status oscar_decode_step_stages(const oscar_layout* layout, void* pool,
+                                      const int32_t* page_table, void* sink_k, void* sink_v,
+                                      void* recent_k, void* recent_v, const float* u_k,
+                                      const float* u_v, const float* clip_k, const float* clip_v,
+                                      const float* levels_k, const float* levels_v,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* seq_slot, const int32_t* seq_pos,
+                                      const void* q, float sm_scale, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, int32_t batch,
+                                      int32_t max_seq_len, uint32_t stages, void* stream);
+
 /* oscar_decode_step over a shared prefix: oscar_append followed by oscar_decode_attn_prefix
- * (seq_lens = seq_pos + 1), in three launches as oscar_decode_step.
+ * (seq_lens = seq_pos + 1), in three launches (the append and the query rotation share the first).
  * The new tokens' demotions must not land in a shared page (oscar_check_page_table with
  * extra_tokens); a layout with levels_kind 1 is refused (SHAPE).  Arguments
  * are those of oscar_decode_step and oscar_decode_attn_prefix, with the same requirements;
@@ -382,9 +410,10 @@ oscar_status oscar_decode_step_prefix(const oscar_layout* layout, void* pool,
  * call on each device).  Calls whose plan needs more than 16 MiB of workspace (as reported by
  * oscar_decode_workspace_bytes) are rejected with OSCAR_ERR_WORKSPACE before anything is
  * launched.  The call allocates and frees nothing.  Every call on one GPU uses that GPU's one
- * array, whose contents on entry do not matter (each call writes every byte it reads before
- * reading it): calls that overlap on one GPU -- on different streams without ordering between
- * them, or from several host threads -- race on it and give wrong results.
+ * array, zero when the library is loaded; each call writes every byte it reads before reading it,
+ * apart from the step's flag words, which it leaves zero: calls that overlap on one GPU -- on
+ * different streams without ordering between them, or from several host threads -- race on it
+ * and give wrong results.
  * Returns OSCAR_OK, or NULL / SHAPE / ALIGN / RANGE / WORKSPACE / HIP. */
 oscar_status oscar_decode_step_noalloc(const oscar_layout* layout, void* pool,
                                        const int32_t* page_table, void* sink_k, void* sink_v,

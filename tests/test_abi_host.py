@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ok.lib()
-    assert lib.oscar_abi_version() == 7
+    assert lib.oscar_abi_version() == 8
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.oscar_status_string(s)
 
@@ -600,3 +600,38 @@ def test_step_noalloc_validation_happens_before_launch():
     assert "scratch" in ok.lib().oscar_last_error().decode()
     # the same plan with a caller workspace gets past that check (and fails on the fake pool)
     assert ok.decode_workspace_bytes(_lay(), 1, 600) <= (16 << 20)
+
+
+def _call_step_stages(lay, **over):
+    a = dict(pool=4096, pt=4096, sk=4096, sv=4096, rk=4096, rv=4096, uk=4096, uv=4096, ck=4096,
+             cv=4096, lk=None, lv=None, kn=4096, vn=4096, slot=4096, pos=4096, q=4096, out=4096,
+             lse=None, ws=4096, wsb=1 << 30, batch=1, maxlen=600, stages=ok.STAGE_ALL)
+    a.update(over)
+    return ok.lib().oscar_decode_step_stages(
+        ctypes.byref(lay), a["pool"], a["pt"], a["sk"], a["sv"], a["rk"], a["rv"], a["uk"],
+        a["uv"], a["ck"], a["cv"], a["lk"], a["lv"], a["kn"], a["vn"], a["slot"], a["pos"],
+        a["q"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"], a["batch"], a["maxlen"],
+        a["stages"], None)
+
+
+def test_step_stages_validation_happens_before_launch():
+    lay = _lay()                  # four heads per KV head, one group: the segment launch appends
+    assert _call_step_stages(lay, stages=0) == -4
+    assert _call_step_stages(lay, stages=16) == -4
+    for part in (ok.STAGE_INT2, ok.STAGE_BF16, ok.STAGE_QUERY | ok.STAGE_BF16 | ok.STAGE_MERGE):
+        assert _call_step_stages(lay, stages=part) == -4
+        assert "together" in ok.lib().oscar_last_error().decode()
+    assert _call_step_stages(lay, q=None) == -1            # the plain call's checks still run
+    assert _call_step_stages(lay, wsb=16) == -5
+
+
+def test_step_launch_count():
+    # the segment launch appends and rotates the query on the fp8 pass (at most four query heads
+    # per KV head, one group per vector) without codebooks; otherwise a preparation launch first
+    assert ok.decode_step_launches(_lay(), 1, 100000) == 2
+    assert ok.decode_step_launches(_lay(num_q_heads=8, num_kv_heads=8), 4, 600) == 2
+    assert ok.decode_step_launches(_lay(num_q_heads=64), 1, 600) == 3        # eight per KV head
+    assert ok.decode_step_launches(_lay(group_size=64), 1, 600) == 3         # two groups
+    assert ok.decode_step_launches(_lay(levels_kind=1), 1, 600) == 3         # symmetric levels
+    assert ok.decode_step_launches(_lay(), 0, 600) == 0
+    assert ok.decode_step_launches(_lay(head_dim=64), 1, 600) == 0

@@ -192,9 +192,9 @@ def test_decode_step_prefix_matches_decode_step():
     lay = case.layout
     ca, cb = case.gpu_cache(g), case.gpu_cache(g)
     mx = max(final)
-    ws_a = torch.empty(ok.decode_workspace_bytes_prefix(lay, 4, mx, ids.numel()),
+    ws_a = torch.zeros(ok.decode_workspace_bytes_prefix(lay, 4, mx, ids.numel()),
                        dtype=torch.uint8, device="cuda")
-    ws_b = torch.empty(ok.decode_workspace_bytes(lay, 4, mx), dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros(ok.decode_workspace_bytes(lay, 4, mx), dtype=torch.uint8, device="cuda")
     out_a = torch.empty((4, 8, 128), dtype=torch.float32, device="cuda")
     out_b = torch.empty_like(out_a)
     worst = 0.0

@@ -97,13 +97,13 @@ class FullLayer:
             ids, shared = workloads.shared_prefix(wl, self.table, self.lengths, spare_tokens=1)
             ok.check_shared_prefix(self.lay, self.table, ids, shared)
             self.prefix = (torch.from_numpy(ids).to(dev), torch.from_numpy(shared).to(dev))
-            ws = torch.empty(ok.decode_workspace_bytes_prefix(self.lay, self.B, mx, len(ids)),
+            ws = torch.zeros(ok.decode_workspace_bytes_prefix(self.lay, self.B, mx, len(ids)),
                              dtype=torch.uint8, device=dev)
             ok.decode_step_prefix(self.lay, cache.pool, table, cache.sink_k, cache.sink_v,
                                   cache.recent_k, cache.recent_v, uk, uv, ck, cv, self.k_new,
                                   self.v_new, slots, pos, self.q, *self.prefix, out, ws, mx)
         else:
-            ws = torch.empty(ok.decode_workspace_bytes(self.lay, self.B, mx), dtype=torch.uint8,
+            ws = torch.zeros(ok.decode_workspace_bytes(self.lay, self.B, mx), dtype=torch.uint8,
                              device=dev)
             ok.decode_step(self.lay, cache.pool, table, cache.sink_k, cache.sink_v,
                            cache.recent_k, cache.recent_v, uk, uv, ck, cv, self.k_new, self.v_new,
@@ -301,7 +301,7 @@ def test_full_size_qwen3_8b_b64_shared_prefix():
     _note(f"  demotion flips: {layer.check_demotion(_samples(rng, layer, 96))}")
     c, gi = layer.cache, layer.gpu
     plain = torch.empty((layer.B, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(ok.decode_workspace_bytes(layer.lay, layer.B, gi["mx"]), dtype=torch.uint8,
+    ws = torch.zeros(ok.decode_workspace_bytes(layer.lay, layer.B, gi["mx"]), dtype=torch.uint8,
                      device="cuda")
     lens1 = torch.tensor(lens, dtype=torch.int32, device="cuda") + 1
     ok.decode_attn(layer.lay, c.pool, gi["table"], c.sink_k, c.sink_v, c.recent_k, c.recent_v,

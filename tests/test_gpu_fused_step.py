@@ -1,0 +1,75 @@
+"""oscar_decode_step on the fp8 pass (at most four query heads per KV head, one group), where the
+segment launch appends the new token and rotates the query itself, against the two-launch path
+(oscar_append, then oscar_decode_attn over the appended cache): outputs, log-sum-exp and every
+cache byte equal at each step, and the final attention against the oracle.
+
+The steps cross the sink's end (position 64), the full-ring threshold (320, where the appended
+token first displaces a ring row into the history), a value-word group (16) and a history page
+boundary (64); batch 1 runs the non-temporal page loads, larger batches the cached ones."""
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_decode_amd as ok
+import workloads
+from oscar_cases import ATTN_TOL, Case, attention_error
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("hq,hkv,start,steps", [
+    (8, 2, [315], 8),                  # four heads per KV head, one sequence
+    (8, 2, [58, 317, 1019, 700], 9),   # ragged batch
+    (8, 4, [60, 318, 1020], 7),        # two heads per KV head
+    (4, 4, [62, 316], 6),              # one head per KV head
+    (4, 4, [1021], 5),
+])
+def test_fused_step_matches_two_launches(hq, hkv, start, steps):
+    wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
+    case = Case(wl, [s + steps for s in start], spare=200)
+    final = list(case.lengths)
+    case.lengths = list(start)
+    g = case.gpu_inputs()
+    lay = case.layout
+    B = len(start)
+    ca, cb = case.gpu_cache(g), case.gpu_cache(g)
+    mx = max(final) + 200   # splits past every sequence's pages exist and return at once
+    ws_a = torch.zeros(ok.decode_workspace_bytes(lay, B, mx), dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros_like(ws_a)
+    out_a = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    out_b = torch.empty_like(out_a)
+    lse_a = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    gen = torch.Generator().manual_seed(hq * 7 + hkv + B)
+    for s in range(steps):
+        pos = [p + s for p in start]
+        _note(f"fused step hq={hq} hkv={hkv} step {s}: positions {pos}")
+        k_new = torch.stack([case.k[b][pos[b]] for b in range(B)]).to("cuda")
+        v_new = torch.stack([case.v[b][pos[b]] for b in range(B)]).to("cuda")
+        pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        q_s = torch.randn(g["q"].shape, generator=gen).to(torch.bfloat16).to("cuda")
+        ok.decode_step(lay, ca.pool, g["table"], ca.sink_k, ca.sink_v, ca.recent_k, ca.recent_v,
+                       g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"],
+                       pos_t, q_s, out_a, ws_a, mx, lse=lse_a)
+        ok.append(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t)
+        ok.decode_attn(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                       g["slots"], pos_t + 1, q_s, g["u_k"], g["u_v"], out_b, ws_b, mx,
+                       lse=lse_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), s
+        assert torch.equal(lse_a, lse_b), s
+        assert torch.equal(ca.pool, cb.pool), s
+        assert torch.equal(ca.sink_k, cb.sink_k) and torch.equal(ca.sink_v, cb.sink_v), s
+        assert torch.equal(ca.recent_k, cb.recent_k) and torch.equal(ca.recent_v, cb.recent_v), s
+    case.lengths = final
+    case.q = q_s.cpu()
+    ref, ref_lse = case.oracle_attention(case.oracle_pool())
+    err = attention_error(out_a.cpu().numpy(), ref)
+    _note(f"fused step final max row error {err:.3e}")
+    assert err <= ATTN_TOL
+    assert np.allclose(lse_a.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)

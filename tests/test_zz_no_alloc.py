@@ -36,7 +36,7 @@ def _step(case, g, cache, lengths, noalloc):
     if noalloc:
         ok.decode_step_noalloc(*args, mx, lse=lse)
     else:
-        ws = torch.empty(ok.decode_workspace_bytes(case.layout, b, mx), dtype=torch.uint8,
+        ws = torch.zeros(ok.decode_workspace_bytes(case.layout, b, mx), dtype=torch.uint8,
                          device="cuda")
         ok.decode_step(*args, ws, mx, lse=lse)
     torch.cuda.synchronize()
