@@ -4,7 +4,9 @@
 // section OSCAR 的设计: the INT2 history and the BF16 segments are processed separately and then
 // combined with an online-softmax merge.  Launch order on one stream (after the preparation
 // launch of encode.hip, which rotates the query and writes it as the fp8 operand of the key
-// contraction, q'' = q' * sm_scale * log2(e) in four parts, plus its per-group sums):
+// contraction, q'' = q' * sm_scale * log2(e) in four parts, plus its per-group sums -- or, for a
+// decode step on the fp8 pass, with that preparation and the step's append inside attn_kernel:
+// see step_prologue and displace_token):
 //   1. attn_kernel   both segment passes in one grid:
 //                    INT2 blocks: split-KV over history pages on the matrix cores, the codes as
 //                    FP4 operands: scores s (q'' . codes) + z sum(q''), a softmax reference per
@@ -129,18 +131,19 @@ struct PairKind {
 //  - every INT2 split block rotates the G query rows of its KV head and builds their key operands
 //    in LDS (step_prologue);
 //  - once the new token at position pos >= 320 displaces the ring row of position pos - 256
-//    (history index pos - 320, in the history's last page), the BF16 block of the sink chunk of
-//    that (sequence, KV head) moves the row into its page slot -- rotation, quantiser, store --
-//    gives the ring slot to the new token and then sets the pair's flag to pos + 1
-//    (displace_token);
+//    (history index pos - 320, in the history's last page), one BF16 block of that (sequence,
+//    KV head), that of chunk kDisplaceChunk, moves the row into its page slot -- rotation,
+//    quantiser, store -- gives the ring slot to the new token and then sets the pair's flag to
+//    pos + 1 (displace_token);
 //  - the one wave that reads that page waits for the flag before it loads its last page pair,
 //    and clears it.  The BF16 block has the lower workgroup number, so it is dispatched first and
 //    never waits for anything; the wait is bounded all the same, and a wave that gives up poisons
 //    its partial (the output turns NaN).
 constexpr int kFlagSpins = 1 << 19;   // polls of about 0.2 us each
 // The BF16 chunk whose block demotes: the last one.  The launch's workgroups beyond one per
-// compute unit (the last INT2 splits) share units with the first ones, the sink chunks; the
-// demoting block is better off alone on its unit, and so are they.
+// compute unit (the last INT2 splits, which hold the demoted tokens' pages) share units with the
+// first ones, the sink chunks; measured at 100k tokens, Hkv 8, with the sink chunk demoting, the
+// demoting blocks and the last splits slowed each other (1.5 us longer preparations).
 constexpr int kDisplaceChunk = kBf16Chunks - 1;
 
 // step_prologue: every thread of the block; on return the query operands are in LDS.  U_k's
@@ -213,8 +216,8 @@ __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p
   __syncthreads();   // the query operands
 }
 
-// displace_token: the whole BF16 block of the sink chunk, before its own work, in the first
-// 9 KiB of its LDS (every read of them is done when it returns).  Per tensor (K, then V) the rotation of the preparation launch's append: the
+// displace_token: the whole BF16 block of chunk kDisplaceChunk, before its own work, in the
+// first 9 KiB of its LDS (every read of them is done when it returns).  Per tensor (K, then V) the rotation of the preparation launch's append: the
 // block's fp64 partial sums, wave 0 adding them and quantising (one group, the equally spaced
 // levels of levels_kind 0) and storing the token.  Wave 0 then makes its stores visible at agent
 // scope before it sets the flag.
@@ -946,7 +949,7 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   }
   if constexpr (FUSE) {
     if (last_apart) {
-      // the displaced token's page is read once the sink chunk's block has stored the token
+      // the displaced token's page is read once the demoting BF16 block has stored the token
       const bool ok = wait_displaced(a, p, b, kv, n_hist + kSink + kRecent - 1);
       if (nl == 0) load_query();
       PageRegs rr[2];

@@ -75,8 +75,8 @@ struct Plan {
   size_t off_int2_acc = 0;   // fp32 [B][Hq][slots][128] rotated-space accumulators
   size_t off_bf16_ml = 0;    // fp32 [B][Hq][5][2]
   size_t off_bf16_acc = 0;   // fp32 [B][Hq][5][128]
-  size_t off_flags = 0;      // int32 [B][Hkv]: a fused decode step's displaced-token flags, zero
-                             // between calls
+  size_t off_flags = 0;      // int32 [B][Hkv] at offset 0: a fused decode step's displaced-token
+                             // flags, zero between calls
   size_t total = 0;
 };
 

@@ -615,23 +615,31 @@ def _call_step_stages(lay, **over):
 
 
 def test_step_stages_validation_happens_before_launch():
-    lay = _lay()                  # four heads per KV head, one group: the segment launch appends
-    assert _call_step_stages(lay, stages=0) == -4
-    assert _call_step_stages(lay, stages=16) == -4
+    lay = _lay(max_pages_per_seq=1600)
+    long = dict(maxlen=100000)    # 224 INT2 blocks of 56 pages: the segment launch appends
+    assert ok.decode_step_launches(lay, 1, 100000) == 2
+    assert _call_step_stages(lay, stages=0, **long) == -4
+    assert _call_step_stages(lay, stages=16, **long) == -4
     for part in (ok.STAGE_INT2, ok.STAGE_BF16, ok.STAGE_QUERY | ok.STAGE_BF16 | ok.STAGE_MERGE):
-        assert _call_step_stages(lay, stages=part) == -4
+        assert _call_step_stages(lay, stages=part, **long) == -4
         assert "together" in ok.lib().oscar_last_error().decode()
-    assert _call_step_stages(lay, q=None) == -1            # the plain call's checks still run
-    assert _call_step_stages(lay, wsb=16) == -5
+    assert _call_step_stages(lay, q=None, **long) == -1    # the plain call's checks still run
+    assert _call_step_stages(lay, wsb=16, **long) == -5
 
 
 def test_step_launch_count():
     # the segment launch appends and rotates the query on the fp8 pass (at most four query heads
-    # per KV head, one group per vector) without codebooks; otherwise a preparation launch first
-    assert ok.decode_step_launches(_lay(), 1, 100000) == 2
-    assert ok.decode_step_launches(_lay(num_q_heads=8, num_kv_heads=8), 4, 600) == 2
-    assert ok.decode_step_launches(_lay(num_q_heads=64), 1, 600) == 3        # eight per KV head
-    assert ok.decode_step_launches(_lay(group_size=64), 1, 600) == 3         # two groups
-    assert ok.decode_step_launches(_lay(levels_kind=1), 1, 600) == 3         # symmetric levels
+    # per KV head, one group per vector) without codebooks, when its INT2 blocks all run at once
+    # with at least 32 pages each; otherwise a preparation launch first
+    assert ok.decode_splits(_lay(), 1, 100000) == (28, 56)
+    assert ok.decode_step_launches(_lay(), 1, 100000) == 2                   # 224 blocks
+    assert ok.decode_step_launches(_lay(num_q_heads=8, num_kv_heads=2), 4, 100000) == 2
+    assert ok.decode_step_launches(_lay(num_q_heads=4, num_kv_heads=4), 2, 100000) == 2
+    assert ok.decode_step_launches(_lay(), 1, 600) == 3                      # 4 pages per block
+    assert ok.decode_step_launches(_lay(num_q_heads=4, num_kv_heads=1), 1, 100000) == 3
+    assert ok.decode_step_launches(_lay(), 64, 32768) == 3                   # several rounds
+    assert ok.decode_step_launches(_lay(num_q_heads=64), 1, 100000) == 3     # eight per KV head
+    assert ok.decode_step_launches(_lay(group_size=64), 1, 100000) == 3      # two groups
+    assert ok.decode_step_launches(_lay(levels_kind=1), 1, 100000) == 3      # symmetric levels
     assert ok.decode_step_launches(_lay(), 0, 600) == 0
     assert ok.decode_step_launches(_lay(head_dim=64), 1, 600) == 0

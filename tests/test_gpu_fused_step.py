@@ -1,7 +1,9 @@
-"""oscar_decode_step on the fp8 pass (at most four query heads per KV head, one group), where the
-segment launch appends the new token and rotates the query itself, against the two-launch path
-(oscar_append, then oscar_decode_attn over the appended cache): outputs, log-sum-exp and every
-cache byte equal at each step, and the final attention against the oracle.
+"""oscar_decode_step where the segment launch appends the new token and rotates the query itself
+(the fp8 pass -- at most four query heads per KV head, one group -- with its INT2 blocks all
+running at once on at least 32 pages each: the plan of a long max_seq_len, here 100k or 200k
+tokens over short sequences, whose split blocks past a sequence's pages return at once), against
+the two-launch path (oscar_append, then oscar_decode_attn over the appended cache): outputs,
+log-sum-exp and every cache byte equal at each step, and the final attention against the oracle.
 
 The steps cross the sink's end (position 64), the full-ring threshold (320, where the appended
 token first displaces a ring row into the history), a value-word group (16) and a history page
@@ -21,23 +23,23 @@ def _note(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("hq,hkv,start,steps", [
-    (8, 2, [315], 8),                  # four heads per KV head, one sequence
-    (8, 2, [58, 317, 1019, 700], 9),   # ragged batch
-    (8, 4, [60, 318, 1020], 7),        # two heads per KV head
-    (4, 4, [62, 316], 6),              # one head per KV head
-    (4, 4, [1021], 5),
+@pytest.mark.parametrize("hq,hkv,start,steps,mx", [
+    (8, 2, [315], 8, 200000),                  # four heads per KV head, one sequence
+    (8, 2, [58, 317, 1019, 700], 9, 100000),   # ragged batch
+    (8, 4, [60, 318, 1020], 7, 100000),        # two heads per KV head
+    (4, 4, [62, 316], 6, 100000),              # one head per KV head
+    (4, 4, [1021], 5, 100000),
 ])
-def test_fused_step_matches_two_launches(hq, hkv, start, steps):
+def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx):
     wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
-    case = Case(wl, [s + steps for s in start], spare=200)
+    case = Case(wl, [s + steps for s in start], spare=mx)
     final = list(case.lengths)
     case.lengths = list(start)
     g = case.gpu_inputs()
     lay = case.layout
     B = len(start)
     ca, cb = case.gpu_cache(g), case.gpu_cache(g)
-    mx = max(final) + 200   # splits past every sequence's pages exist and return at once
+    assert ok.decode_step_launches(lay, B, mx) == 2
     ws_a = torch.zeros(ok.decode_workspace_bytes(lay, B, mx), dtype=torch.uint8, device="cuda")
     ws_b = torch.zeros_like(ws_a)
     out_a = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
