@@ -603,7 +603,8 @@ namespace {
 // its INT2 blocks all run at once (at most one per compute unit) with at least kFusePages pages
 // each.  Every such block then repeats the query rotation (about 4.5 us of dependent loads and
 // fp64 arithmetic before its pages stream), which pays only where a wave's pages take long enough
-// to hide it.  Measured on MI355X (steps/s, fused against three launches): 100k tokens, Hkv 8
+// to hide it.  Measured on MI355X (steps/s, fused against three launches): Hkv 8 at 64k tokens
+// (256 blocks of 32 pages) 1,328 against 1,294, at 80k (40 pages) 1,275 against 1,228, at 100k
 // (224 blocks of 56 pages) 1,283 against 1,232; 100k, Hkv 1 (8 pages) 1,383 against 1,458;
 // batch 64 at 32k (4,096 blocks) 71.9 against 76.1; 32k, Hkv 8 (9 pages) 27,921 against 28,412.
 constexpr int kFusePages = 32;
