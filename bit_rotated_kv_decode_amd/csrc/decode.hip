@@ -150,9 +150,9 @@ constexpr int kDisplaceChunk = kBf16Chunks - 1;
 // slices and the query rows are requested first, `prefetch0` (the first page pair's loads) once
 // they have arrived -- issued earlier, the page loads would queue ahead of them at the memory and
 // hold up the whole preparation -- and `prefetch1` (the second pair's) once U_k's registers are
-// free.  One pass over U_k's slices serves all rows (thread t: the partial
-// sums over rows 16 (t / 32) .. + 15 of U for columns 4 (t % 32) .. + 3); wave w then sums the
-// eight partials of row w in order and applies the Hadamard transform and the operand split.
+// free.  One pass over U_k's slices serves all rows (thread t: the partial sums over rows
+// 16 (t / 32) .. + 15 of U for columns 4 (t % 32) .. + 3); wave w then sums the eight partials of
+// row w in order and applies the Hadamard transform and the operand split.
 template <int G, typename Prefetch0, typename Prefetch1>
 __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p, int b, int kv,
                                               unsigned char* smem, Prefetch0&& prefetch0,
@@ -217,10 +217,10 @@ __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p
 }
 
 // displace_token: the whole BF16 block of chunk kDisplaceChunk, before its own work, in the
-// first 9 KiB of its LDS (every read of them is done when it returns).  Per tensor (K, then V) the rotation of the preparation launch's append: the
-// block's fp64 partial sums, wave 0 adding them and quantising (one group, the equally spaced
-// levels of levels_kind 0) and storing the token.  Wave 0 then makes its stores visible at agent
-// scope before it sets the flag.
+// first 9 KiB of its LDS (every read of them is done when it returns).  Per tensor (K, then V)
+// the rotation of the preparation launch's append: the block's fp64 partial sums, wave 0 adding
+// them and quantising (one group, the equally spaced levels of levels_kind 0) and storing the
+// token.  Wave 0 then makes its stores visible at agent scope before it sets the flag.
 __device__ __forceinline__ void displace_token(const DecodeArgs& a, const Plan& p, int b, int kv,
                                                int pos, int64_t slot, unsigned char* lds) {
   const AppendArgs& ap = a.ap;
@@ -316,8 +316,8 @@ __device__ __forceinline__ void int2_block(const DecodeArgs& a, const Plan& p, i
   // chunk: local indices 0 .. kCascPages - 1, all of them history.
   static_assert((kMaxPagesPerSplit + 3) / 4 <= 8 + 64, "eight scalar ids and one per lane");
   int w0 = 0, w1 = kCascPages, wa = 0, n_hist = 1 << 30;
-  bool demote = false;   // FUSE: the split holds the page the displaced token goes to,
-  int owner = -1;        // which wave `owner` reads
+  bool demote = false;   // FUSE: the split holds the page the displaced token goes to
+  int owner = -1;        // FUSE: the wave whose pages include it
   int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int more_ids = 0;
   if constexpr (!CASC) {
@@ -1045,8 +1045,9 @@ struct Bf16Lds {
 
 // FUSE: a decode step whose append the segment launch runs: the new token's key and value rows
 // are read from k_new / v_new in place of their row of the sink or ring, and the chunk that holds
-// that row writes them there unless the token displaces a ring row (position >= 320: the sink
-// chunk's block, which demotes the displaced row first, writes the slot after reading it).
+// that row writes them there unless the token displaces a ring row (position >= 320: the block
+// of chunk kDisplaceChunk, which demotes the displaced row first, writes the slot after reading
+// it).
 template <int G, bool FUSE = false>
 __device__ __forceinline__ void bf16_block(const DecodeArgs& a, const Plan& p, float scale_log2,
                                            int chunk, int kv, int b, unsigned char* smem) {

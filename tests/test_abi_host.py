@@ -637,7 +637,7 @@ def test_step_launch_count():
     assert ok.decode_step_launches(_lay(num_q_heads=4, num_kv_heads=4), 2, 100000) == 2
     assert ok.decode_step_launches(_lay(), 1, 600) == 3                      # 4 pages per block
     assert ok.decode_step_launches(_lay(num_q_heads=4, num_kv_heads=1), 1, 100000) == 3
-    assert ok.decode_step_launches(_lay(), 64, 32768) == 3                   # several rounds
+    assert ok.decode_step_launches(_lay(), 64, 32768) == 3                   # > one block per unit
     assert ok.decode_step_launches(_lay(num_q_heads=64), 1, 100000) == 3     # eight per KV head
     assert ok.decode_step_launches(_lay(group_size=64), 1, 100000) == 3      # two groups
     assert ok.decode_step_launches(_lay(levels_kind=1), 1, 100000) == 3      # symmetric levels
