@@ -23,16 +23,25 @@ def _note(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("hq,hkv,start,steps,mx", [
-    (8, 2, [315], 8, 200000),                  # four heads per KV head, one sequence
-    (8, 2, [58, 317, 1019, 700], 9, 100000),   # ragged batch
-    (8, 4, [60, 318, 1020], 7, 100000),        # two heads per KV head
-    (4, 4, [62, 316], 6, 100000),              # one head per KV head
-    (4, 4, [1021], 5, 100000),
+def _levels(hkv):
+    """Equally spaced codebooks (lo, step) per KV head for keys and values, one per head."""
+    lo = np.linspace(0.3, 0.6, hkv, dtype=np.float32)
+    lv = np.stack([lo, (3 - 2 * lo) / 3], -1).astype(np.float32)
+    return lv, lv[::-1].copy()
+
+
+@pytest.mark.parametrize("hq,hkv,start,steps,mx,levels", [
+    (8, 2, [315], 8, 200000, False),                  # four heads per KV head, one sequence
+    (8, 2, [58, 317, 1019, 700], 9, 100000, False),   # ragged batch
+    (8, 4, [60, 318, 1020], 7, 100000, False),        # two heads per KV head
+    (4, 4, [62, 316], 6, 100000, False),              # one head per KV head
+    (4, 4, [1021], 5, 100000, False),
+    (8, 2, [317, 1020], 6, 100000, True),             # equally spaced codebook levels
 ])
-def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx):
+def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx, levels):
     wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
-    case = Case(wl, [s + steps for s in start], spare=mx)
+    case = Case(wl, [s + steps for s in start], spare=mx,
+                levels=_levels(hkv) if levels else None)
     final = list(case.lengths)
     case.lengths = list(start)
     g = case.gpu_inputs()
@@ -56,9 +65,11 @@ def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx):
         q_s = torch.randn(g["q"].shape, generator=gen).to(torch.bfloat16).to("cuda")
         ok.decode_step(lay, ca.pool, g["table"], ca.sink_k, ca.sink_v, ca.recent_k, ca.recent_v,
                        g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"],
-                       pos_t, q_s, out_a, ws_a, mx, lse=lse_a)
+                       pos_t, q_s, out_a, ws_a, mx, lse=lse_a, levels_k=g["levels_k"],
+                       levels_v=g["levels_v"])
         ok.append(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
-                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t)
+                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t,
+                  levels_k=g["levels_k"], levels_v=g["levels_v"])
         ok.decode_attn(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
                        g["slots"], pos_t + 1, q_s, g["u_k"], g["u_v"], out_b, ws_b, mx,
                        lse=lse_b)
