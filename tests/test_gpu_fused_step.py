@@ -37,6 +37,7 @@ def _levels(hkv):
     (4, 4, [62, 316], 6, 100000, False),              # one head per KV head
     (4, 4, [1021], 5, 100000, False),
     (8, 2, [317, 1020], 6, 100000, True),             # equally spaced codebook levels
+    (4, 4, [1300, 2250], 4, 100000, False),           # the page read by waves 1 and 2
 ])
 def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx, levels):
     wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
