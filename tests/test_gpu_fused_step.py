@@ -87,3 +87,62 @@ def test_fused_step_matches_two_launches(hq, hkv, start, steps, mx, levels):
     _note(f"fused step final max row error {err:.3e}")
     assert err <= ATTN_TOL
     assert np.allclose(lse_a.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def _draw(seed):
+    """A seeded shape for the two-launch step: batch 1-4, one, two or four query heads per KV
+    head, positions from the sink to a few thousand, some exactly at a boundary."""
+    rng = np.random.default_rng(1000 + seed)
+    gqa = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.choice([1, 2, 4])) if gqa < 4 else int(rng.choice([1, 2]))
+    batch = int(rng.integers(1, 5))
+    edges = [63, 64, 319, 320, 383, 384, 399, 400, 447, 448]
+    start = [int(rng.choice(edges)) - 1 if rng.random() < 0.4 else int(rng.integers(0, 3000))
+             for _ in range(batch)]
+    return gqa * hkv, hkv, [max(0, s) for s in start]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fused_step_sweep(seed):
+    hq, hkv, start = _draw(seed)
+    B, steps = len(start), 3
+    wl = workloads.scaled(workloads.get("tiny_gqa4_1k"), num_q_heads=hq, num_kv_heads=hkv)
+    # the shortest max_seq_len from 100k up whose plan fuses the step
+    mx = next(m for m in range(100000, 400001, 20000)
+              if ok.decode_step_launches(ok.make_layout(hq, hkv, 10, B, (m + 63) // 64, 128),
+                                         B, m) == 2)
+    case = Case(wl, [s + steps for s in start], spare=mx)
+    final = list(case.lengths)
+    case.lengths = list(start)
+    g = case.gpu_inputs()
+    lay = case.layout
+    assert ok.decode_step_launches(lay, B, mx) == 2
+    _note(f"fused sweep {seed}: hq={hq} hkv={hkv} start={start} max_seq_len={mx}")
+    ca, cb = case.gpu_cache(g), case.gpu_cache(g)
+    ws_a = torch.zeros(ok.decode_workspace_bytes(lay, B, mx), dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros_like(ws_a)
+    out_a = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    out_b = torch.empty_like(out_a)
+    gen = torch.Generator().manual_seed(seed)
+    for s in range(steps):
+        pos = [p + s for p in start]
+        k_new = torch.stack([case.k[b][pos[b]] for b in range(B)]).to("cuda")
+        v_new = torch.stack([case.v[b][pos[b]] for b in range(B)]).to("cuda")
+        pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        q_s = torch.randn(g["q"].shape, generator=gen).to(torch.bfloat16).to("cuda")
+        ok.decode_step(lay, ca.pool, g["table"], ca.sink_k, ca.sink_v, ca.recent_k, ca.recent_v,
+                       g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"],
+                       pos_t, q_s, out_a, ws_a, mx)
+        ok.append(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                  g["u_k"], g["u_v"], g["clip_k"], g["clip_v"], k_new, v_new, g["slots"], pos_t)
+        ok.decode_attn(lay, cb.pool, g["table"], cb.sink_k, cb.sink_v, cb.recent_k, cb.recent_v,
+                       g["slots"], pos_t + 1, q_s, g["u_k"], g["u_v"], out_b, ws_b, mx)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), s
+        assert torch.equal(ca.pool, cb.pool), s
+        assert torch.equal(ca.sink_k, cb.sink_k) and torch.equal(ca.sink_v, cb.sink_v), s
+        assert torch.equal(ca.recent_k, cb.recent_k) and torch.equal(ca.recent_v, cb.recent_v), s
+    case.lengths = final
+    case.q = q_s.cpu()
+    ref, _ = case.oracle_attention(case.oracle_pool())
+    assert attention_error(out_a.cpu().numpy(), ref) <= ATTN_TOL
