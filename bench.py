@@ -529,6 +529,8 @@ def main():
                    "batch": B, "context": lengths[0] if len(set(lengths)) == 1 else
                    [min(lengths), max(lengths)], "layers": n_layers,
                    "launch": "hip-graph" if graph is not None else "eager",
+                   "step_launches": 3 if cascade else ok.decode_step_launches(layers[0].lay, B,
+                                                                               max_len),
                    **({} if not levels else
                       {"codebook": {"symmetric_l0_l1": list(levels)}} if kind else
                       {"codebook": {"lo": levels[0], "step": levels[1]}})},
