@@ -606,7 +606,8 @@ namespace {
 // to hide it.  Measured on MI355X (steps/s, fused against three launches): Hkv 8 at 64k tokens
 // (256 blocks of 32 pages) 1,328 against 1,294, at 80k (40 pages) 1,275 against 1,228, at 100k
 // (224 blocks of 56 pages) 1,283 against 1,232; 100k, Hkv 1 (8 pages) 1,383 against 1,458;
-// batch 64 at 32k (4,096 blocks) 71.9 against 76.1; 32k, Hkv 8 (9 pages) 27,921 against 28,412.
+// batch 64 at 8k-128k tokens (4,096 blocks) 71.9 against 76.1; 32k, Hkv 8 (9 pages) 27,921
+// against 28,412.
 constexpr int kFusePages = 32;
 
 bool step_fused(const oscar::Plan& plan, int levels_kind) {
