@@ -108,11 +108,11 @@ struct Int2Lds {
   static constexpr int STAGE = (TOTAL + 15) & ~15;
   static constexpr int CASC_TOTAL = STAGE + kCascPages * (kMetaOff + kPage * 8 * NG);
   // a decode step's own query rotation (step_prologue), apart from everything the page loop
-  // uses: the G query rows (fp32 [G][128]), their rotation partials (fp64 [G][8][128]) and the
+  // uses: the G query rows (fp32 [G][128]), their rotation partials (fp32 [G][8][128]) and the
   // query operands the block builds: NA tiles, their E8M0 row scales and the per-head sums
   static constexpr int FX = (TOTAL + 15) & ~15;
   static constexpr int FRED = FX + G * kHeadDim * 4;
-  static constexpr int FOPS = FRED + G * dev::kRotGroups * kHeadDim * 8;
+  static constexpr int FOPS = FRED + G * dev::kRotGroups * kHeadDim * 4;
   static constexpr int FSC = FOPS + NA * 2048;
   static constexpr int FSIG = FSC + NA * 64 * 4;
   static constexpr int FUSED_TOTAL = FSIG + G * 4 * 4;
@@ -159,8 +159,8 @@ __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p
                                               Prefetch1&& prefetch1) {
   using S = Int2Lds<G, 1>;
   float* xs = reinterpret_cast<float*>(smem + S::FX);
-  double (*red)[dev::kRotGroups][kHeadDim] =
-      reinterpret_cast<double (*)[dev::kRotGroups][kHeadDim]>(smem + S::FRED);
+  float (*red)[dev::kRotGroups][kHeadDim] =
+      reinterpret_cast<float (*)[dev::kRotGroups][kHeadDim]>(smem + S::FRED);
   const int tid = threadIdx.x;
   constexpr int kQ = (G * kHeadDim + 255) / 256;   // query values per thread
   dev::URows uk;
@@ -182,15 +182,8 @@ __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p
   const int g = tid >> 5, c = tid & 31;
 #pragma unroll
   for (int r = 0; r < G; ++r) {
-    double y[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const double xi = static_cast<double>(xs[r * kHeadDim + 16 * g + k]);
-      y[0] = fma(xi, static_cast<double>(uk.v[k].x), y[0]);
-      y[1] = fma(xi, static_cast<double>(uk.v[k].y), y[1]);
-      y[2] = fma(xi, static_cast<double>(uk.v[k].z), y[2]);
-      y[3] = fma(xi, static_cast<double>(uk.v[k].w), y[3]);
-    }
+    float y[4];
+    dev::query_partials(xs + r * kHeadDim, uk, y);
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[r][g][4 * c + e] = y[e];
   }
@@ -200,15 +193,8 @@ __device__ __forceinline__ void step_prologue(const DecodeArgs& a, const Plan& p
   __syncthreads();
   const int wave = tid >> 6;
   if (wave < G) {
-    const int lane = dev::lane_id();
-    double y0 = red[wave][0][lane], y1 = red[wave][0][lane + 64];
-#pragma unroll
-    for (int j = 1; j < dev::kRotGroups; ++j) {
-      y0 += red[wave][j][lane];
-      y1 += red[wave][j][lane + 64];
-    }
-    double o0, o1;
-    dev::hadamard_bitrev(y0, y1, o0, o1);
+    float o0, o1;
+    dev::query_finish(red[wave], o0, o1);
     enc::query_operands(o0, o1, 1, G, wave, a.sm_scale * kLog2e, smem + S::FOPS,
                         reinterpret_cast<int32_t*>(smem + S::FSC),
                         reinterpret_cast<float*>(smem + S::FSIG) + 4 * wave);

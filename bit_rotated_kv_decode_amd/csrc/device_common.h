@@ -273,6 +273,64 @@ __device__ __forceinline__ bool rotate1_block(const float* x, const URows& ur,
   return true;
 }
 
+// The query's rotation, in fp32 (the query feeds score operands good to about 2^-16 of its
+// largest element, far above fp32's rounding; the history's rotation, which decides codes, stays
+// fp64).  Partial sums as in rotate1_block -- thread (g, c) = (t / 32, t % 32) sums rows
+// 16 g .. 16 g + 15 of x U for columns 4 c .. 4 c + 3, one fmaf chain from zero over the rows in
+// order -- then the eight partial vectors added in order of g, the Hadamard butterflies and the
+// bit-reversal gather in fp32, and the scaling by 1/sqrt(128) last.  query_partials is one
+// thread's part (y[e] for column 4 c + e); query_finish is a wave's: `red` rows [g][128] of one
+// vector in, lane l out holding rotated channels l (o0) and l + 64 (o1).
+__device__ __forceinline__ void query_partials(const float* x, const URows& ur, float (&y)[4]) {
+  const int g = threadIdx.x >> 5;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float xi = x[16 * g + k];
+    y[0] = fmaf(xi, ur.v[k].x, y[0]);
+    y[1] = fmaf(xi, ur.v[k].y, y[1]);
+    y[2] = fmaf(xi, ur.v[k].z, y[2]);
+    y[3] = fmaf(xi, ur.v[k].w, y[3]);
+  }
+}
+
+__device__ __forceinline__ void query_finish(const float (*red)[128], float& o0, float& o1) {
+  const int lane = lane_id();
+  float y0 = red[0][lane], y1 = red[0][lane + 64];
+#pragma unroll
+  for (int r = 1; r < kRotGroups; ++r) {
+    y0 += red[r][lane];
+    y1 += red[r][lane + 64];
+  }
+  {
+    const float a = y0 + y1, b = y0 - y1;
+    y0 = a;
+    y1 = b;
+  }
+  y0 = butterfly<32>(y0);
+  y1 = butterfly<32>(y1);
+  y0 = butterfly<16>(y0);
+  y1 = butterfly<16>(y1);
+  y0 = butterfly<8>(y0);
+  y1 = butterfly<8>(y1);
+  y0 = butterfly<4>(y0);
+  y1 = butterfly<4>(y1);
+  y0 = butterfly<2>(y0);
+  y1 = butterfly<2>(y1);
+  y0 = butterfly<1>(y0);
+  y1 = butterfly<1>(y1);
+  // as in hadamard_bitrev: x'_j = z_rev(j), z[r] in lane r & 63 (slot r >> 6), z[r + 1] next lane
+  const int r = bitrev7(lane);
+  const int src = r & 63;
+  const bool hi = (r >> 6) != 0;
+  const float a0 = __shfl(y0, src), a1 = __shfl(y1, src);
+  const float b0 = __shfl(y0, src + 1), b1 = __shfl(y1, src + 1);
+  const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
+  o0 = (hi ? a1 : a0) * inv_sqrt_d;
+  o1 = (hi ? b1 : b0) * inv_sqrt_d;
+}
+
 // Rotation of TPW row vectors x (fp32, staged in LDS as [TPW][128]) by R = U H P / sqrt(128)
 // in fp64.  Lane l returns rotated channels l and l+64 of each vector in out[t][0], out[t][1].
 // U is fp32 [128][128] row-major in global memory; x U is accumulated in fp64 over i = 0..127,

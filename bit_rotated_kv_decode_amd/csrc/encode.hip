@@ -7,10 +7,12 @@
 // bit-reversal, clipped, quantised with a per-group scale and zero point and packed four 2-bit
 // codes to a byte; the query is rotated by the same R_k so that scores can be taken against the
 // stored rotated keys.  One 64-lane wave encodes one (token, KV head, K|V) vector: lane l owns
-// rotated channels l and l + 64.  The rotation runs in fp64 (x U as a matrix-vector product, the
-// Hadamard as cross-lane butterflies), the rotated vector is rounded once to fp32 and every step
-// that decides a code (clip, group min / max, (max - min) / 3, fp16 rounding, (x - z) / s, rint)
-// runs in IEEE fp32.
+// rotated channels l and l + 64.  The history's rotation runs in fp64 (x U as a matrix-vector
+// product, the Hadamard as cross-lane butterflies), the rotated vector is rounded once to fp32 and
+// every step that decides a code (clip, group min / max, (max - min) / 3, fp16 rounding,
+// (x - z) / s, rint) runs in IEEE fp32.  The query's rotation for the four-head pass runs in fp32
+// (it decides no code; dev::query_partials / query_finish, shared with the decode step's segment
+// launch, which repeats it); the other passes' query rotation is the fp64 one.
 #include "device_common.h"
 #include "encode_common.h"
 #include "oscar_internal.h"
@@ -192,16 +194,26 @@ __device__ __forceinline__ void query_item(const QueryArgs& a, int row, unsigned
   if (threadIdx.x < kHeadDim)
     x[threadIdx.x] = dev::bf16_to_f32(a.q[static_cast<int64_t>(row) * kHeadDim + threadIdx.x]);
   __syncthreads();
-  double r0, r1;
-  if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
   if (!int2_fp8_pass(a.gqa, a.n_groups)) {
+    double r0, r1;
+    if (!dev::rotate1_block(x, ur, red, r0, r1)) return;
     split_query(r0, r1, a.n_groups, a.scale_log2, a.qpack + static_cast<int64_t>(row) * 256,
                 a.qmeta + static_cast<int64_t>(row) * 4);
     return;
   }
+  // the fp8 pass: the fp32 rotation the segment launch of a fused decode step also runs
+  float (*redf)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(smem + 4 * kHeadDim);
+  float y[4];
+  dev::query_partials(x, ur, y);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) redf[threadIdx.x >> 5][4 * (threadIdx.x & 31) + e] = y[e];
+  __syncthreads();
+  if ((threadIdx.x >> 6) != 0) return;
+  float o0, o1;
+  dev::query_finish(redf, o0, o1);
   const int b = row / a.hq, hd = (row % a.hq) % a.gqa;
   const int64_t op = (static_cast<int64_t>(b) * a.hkv + kv) * key_tiles(a.gqa) * a.n_groups;
-  query_operands(r0, r1, a.n_groups, a.gqa, hd, a.scale_log2, a.qops + op * 2048,
+  query_operands(o0, o1, a.n_groups, a.gqa, hd, a.scale_log2, a.qops + op * 2048,
                  a.qscales + op * 64, a.qmeta + static_cast<int64_t>(row) * 4);
 }
 
