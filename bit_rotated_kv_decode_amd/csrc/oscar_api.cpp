@@ -84,8 +84,8 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   p.hkv = lay.num_kv_heads;
   p.gqa = p.hq / p.hkv;
   p.n_groups = kHeadDim / lay.group_size;
-  const int n_hist = std::max(0, max_seq_len - kSink - kRecent);
-  p.max_pages = (n_hist + kPage - 1) / kPage;
+  const int64_t n_hist = std::max<int64_t>(0, int64_t{max_seq_len} - kSink - kRecent);
+  p.max_pages = static_cast<int>((n_hist + kPage - 1) / kPage);
   // Aim for one round of two blocks per compute unit: a grid that leaves some units a third
   // block finishes when those do.  The INT2 work items share the launch with the BF16 chunk
   // blocks.  At least one page per wave, within the per-item page and per-head item limits.
@@ -122,7 +122,8 @@ Plan make_plan(const oscar_layout& lay, int batch, int max_seq_len, int prefix_p
   // whole cascade chunks of the shared prefix (the cascade runs on the four-head single-group pass)
   if (prefix_pages > 0 && int2_fp8_pass(p.gqa, p.n_groups)) {
     p.casc_chunks = std::min(prefix_pages, p.max_pages) / kCascPages;
-    p.casc_groups = p.casc_chunks ? (batch + kCascGroup - 1) / kCascGroup : 0;
+    p.casc_groups =
+        p.casc_chunks ? static_cast<int>((int64_t{batch} + kCascGroup - 1) / kCascGroup) : 0;
   }
   p.slots = p.casc_chunks + p.num_splits;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -159,7 +160,7 @@ Bf16Plan make_bf16_plan(const oscar_layout& lay, int batch, int max_seq_len) {
   p.hq = lay.num_q_heads;
   p.hkv = lay.num_kv_heads;
   p.gqa = p.hq / p.hkv;
-  p.max_pages = (std::max(0, max_seq_len) + kPage - 1) / kPage;
+  p.max_pages = static_cast<int>((std::max<int64_t>(0, max_seq_len) + kPage - 1) / kPage);
   // one round of two blocks per compute unit, as for the INT2 pass; at least one page per wave
   const long long items = static_cast<long long>(p.max_pages) * batch * p.hkv;
   long long pps = std::max<long long>(4, (items + kInt2Items - 1) / kInt2Items);
