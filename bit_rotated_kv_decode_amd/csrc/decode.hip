@@ -1245,6 +1245,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(DecodeArgs a, Plan p, floa
 //   (3) times U_v^T: eight threads per output channel, 16 inputs each, summed across the lanes;
 //   (4) merge with the BF16 chunk partials and normalise.
 constexpr int kMergePrefetch = 12;   // splits per thread loaded up front (96 splits per row)
+static_assert(kMergePrefetch * 8 == kMergeSplits, "the plan caps the splits at what one round takes");
 constexpr int kMergeQuarters = 4;    // output-channel quarters of a row (32 channels each)
 constexpr int kMergeCols = kHeadDim / kMergeQuarters;
 // Rows (sequence, query head) from which a launch gives each row one block that takes all four

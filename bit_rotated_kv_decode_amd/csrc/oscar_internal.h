@@ -17,6 +17,7 @@ constexpr int kBf16Chunks = (kSink + kRecent) / 64;  // 64-token chunks of the B
 constexpr int kMaxGqa = 8;
 constexpr int kMaxPagesPerSplit = 256;    // history pages one INT2 work item may cover
 constexpr int kMaxSplits = 1024;          // INT2 work items per (sequence, KV head)
+constexpr int kMergeSplits = 96;          // splits per row the merge loads at once
 constexpr int kInt2Items = 512;           // blocks per launch the plan aims at (2 per compute unit)
 constexpr int kComputeUnits = 256;        // compute units of an MI355X (gfx950)
 // Shared-prefix cascade: a cascade block takes kCascPages pages of the shared prefix of one KV head

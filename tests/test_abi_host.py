@@ -444,10 +444,11 @@ def test_decode_splits_query():
     # 507 x 8: 9 pages (16 would leave 254 of 456 blocks; one per unit would give 2 pairs)
     assert ok.decode_splits(lay, 1, 32768) == (57, 9)
     assert ok.decode_splits(lay, 1, 320) == (0, 4)
+    # at most 96 splits per row (what the merge loads at once): 1558 / 96 -> 17 -> 24 pages
     one = _lay(num_kv_heads=1, num_q_heads=4, max_pages_per_seq=2000)
-    assert ok.decode_splits(one, 1, 100000) == (195, 8)       # 4 pages = half a pair per wave
+    assert ok.decode_splits(one, 1, 100000) == (65, 24)
     two = _lay(num_kv_heads=2, num_q_heads=8, max_pages_per_seq=2000)
-    assert ok.decode_splits(two, 1, 100000) == (195, 8)       # 7 -> 8 pages, one pair per wave
+    assert ok.decode_splits(two, 1, 100000) == (65, 24)
     gqa8 = _lay(num_kv_heads=8, num_q_heads=64, max_pages_per_seq=2000)
     assert ok.decode_splits(gqa8, 1, 100000) == (58, 27)      # the int8 / bf16 pass: as planned
     sym = _lay(num_kv_heads=8, num_q_heads=32, max_pages_per_seq=2000, levels_kind=1)
